@@ -36,7 +36,9 @@ Readings taken where the pages leave a step open:
     printed objective carries a 1/2 on the data term only; Sigma_i as printed
     governs, because the whole algorithm is built on it);
   * rho_i is the exact solution (explicit Cholesky), not a CG iterate;
-    ``cg_solve`` gives the CG iterate under the stop rule below separately.
+    ``cg_solve`` gives the CG iterate under the stop rule below separately,
+    on the pages' system or on the same system expanded around the weighted
+    key mean (``centred_moments``), which has the same exact solution.
   * CG ([LLA] 2.2: matrix-free CG on Sigma_i rho_i = mu_i; the stop rule is
     not printed): x0 = 0, r0 = p0 = mu_i; a query stops at the first k with
     ||r_k|| <= tol * ||r_0|| (recurrence residual), on breakdown
@@ -59,6 +61,8 @@ __all__ = [
     "cholesky_solve",
     "cg_solve",
     "intercept_from_rho",
+    "centred_moments",
+    "centred_intercept",
     "oracle_row",
     "oracle_head",
     "ridge_bruteforce",
@@ -153,19 +157,56 @@ def intercept_from_rho(w, Z, V_prefix, omega, mu, rho):
     return s @ V_prefix, s, schur
 
 
+def centred_moments(q_i, K_prefix, w, lam):
+    """The same local fit expanded around the weighted key mean
+    kbar_i = sum_j w_ij k_j / omega_i instead of q_i, with explicit pairwise
+    differences k_j - kbar_i:
+        Sigma_c = sum_j w_ij (k_j - kbar_i)(k_j - kbar_i)^T + lam I.
+    By the parallel-axis identity Sigma_i = Sigma_c + omega_i u u^T with
+    u = kbar_i - q_i, and mu_i = omega_i u ([LLA] 2.1, Eqs. (6)-(7) rewritten).
+    Returns Zc, omega, kbar, mu, Sigma_c."""
+    omega = float(np.sum(w))
+    kbar = (K_prefix.T @ w) / omega
+    Zc = K_prefix - kbar[None, :]
+    mu = omega * (kbar - q_i)
+    Sigma_c = (Zc * w[:, None]).T @ Zc + lam * np.eye(K_prefix.shape[1])
+    return Zc, omega, kbar, mu, Sigma_c
+
+
+def centred_intercept(w, Zc, V_prefix, rho_c):
+    """Output for a solution rho_c of Sigma_c rho_c = mu_i: with
+    a_ij = w_ij (1 - (k_j - kbar_i)^T rho_c), b_i = sum_j a_ij v_j / sum_j a_ij.
+    For the exact rho_c this is [LLA] Eq. (8) exactly (Sherman-Morrison on the
+    rank-one term above; sum_j a_ij = omega_i because sum_j w_ij (k_j - kbar_i)
+    = 0); the pages' rho_i = rho_c / (1 + (kbar_i - q_i)^T rho_c)."""
+    a = w * (1.0 - Zc @ rho_c)
+    den = float(np.sum(a))
+    return (a @ V_prefix) / den, a / den, den
+
+
 def oracle_row(q_i, K_prefix, V_prefix, lam, scale=None, solver="cholesky",
                cg_max_iters=0, cg_rel_tol=0.0) -> RowResult:
     """One row of causal LLA in float64.
 
     ``solver="cholesky"``: exact rho_i (the definition).
-    ``solver="cg"``: rho_i is the CG iterate of ``cg_solve`` (same stop rule
-    as the GPU), the output is then Eq. (8) with that rho_i.
+    ``solver="cg"``: rho_i is the CG iterate of ``cg_solve`` on the pages'
+    system Sigma_i rho_i = mu_i; the output is then Eq. (8) with that rho_i.
+    ``solver="cg_centred"``: CG (same stop rule) on Sigma_c rho_c = mu_i, the
+    system centred at the weighted key mean (``centred_moments``); output by
+    ``centred_intercept``; ``rho`` is reported as the pages' rho_i.
     ``solver="zero"``: rho_i = 0, the local-constant (softmax) limit."""
     q_i = np.asarray(q_i, dtype=np.float64)
     K_prefix = np.asarray(K_prefix, dtype=np.float64)
     V_prefix = np.asarray(V_prefix, dtype=np.float64)
     c = _scale(q_i.shape[0], scale)
     _, m, w = causal_weights(q_i, K_prefix, c)
+    if solver == "cg_centred":
+        Zc, omega, kbar, mu, Sigma_c = centred_moments(q_i, K_prefix, w, lam)
+        rho_c, iters, resid = cg_solve(Sigma_c, mu, cg_max_iters, cg_rel_tol)
+        b, s, _ = centred_intercept(w, Zc, V_prefix, rho_c)
+        rho = rho_c / (1.0 + (kbar - q_i) @ rho_c)
+        schur = float(omega - mu @ rho)
+        return RowResult(b, omega, mu, rho, m, schur, s, w, Sigma_c, iters, resid)
     Z, omega, mu, Sigma = pairwise_moments(q_i, K_prefix, w, lam)
     iters, resid = -1, 0.0
     if solver == "cholesky":

@@ -323,3 +323,53 @@ def test_workloads_recipes():
     assert got[4] == -197 / 128 * 2.0**-9
     r = make_random(1, 1, 10, 16, "bf16", qk_scale=None)
     assert r.k.shape == (1, 1, 10, 16)
+
+
+# --- the mean-centred system: same exact answer --------------------------------
+
+@pytest.mark.parametrize("name", ["tiny", "piecewise"])
+def test_centred_system_exact_solution_equals_definition(name):
+    """Solving Sigma_c rho_c = mu_i exactly and forming the centred output gives
+    [LLA] Eq. (8) with the exact rho_i; the Sherman-Morrison map gives rho_i."""
+    w = make_workload(name)
+    q, k, v = _head(w)
+    d = q.shape[1]
+    for i in (0, 1, 5, 63, 64, 200, q.shape[0] - 1):
+        r = O.oracle_row(q[i], k[:i + 1], v[:i + 1], w.lam)
+        _, _, wt = O.causal_weights(q[i], k[:i + 1], 1 / np.sqrt(d))
+        Zc, om, kbar, mu, Sc = O.centred_moments(q[i], k[:i + 1], wt, w.lam)
+        # parallel-axis identity against the explicit pairwise Sigma_i
+        u = kbar - q[i]
+        np.testing.assert_allclose(Sc + om * np.outer(u, u), r.Sigma, rtol=0,
+                                   atol=1e-11 * np.abs(r.Sigma).max())
+        rho_c = np.linalg.solve(Sc, mu)
+        b, _, den = O.centred_intercept(wt, Zc, v[:i + 1], rho_c)
+        assert abs(den - om) <= 1e-9 * om
+        np.testing.assert_allclose(b, r.b, rtol=0, atol=1e-9 * max(1, np.abs(r.b).max()))
+        np.testing.assert_allclose(rho_c / (1 + u @ rho_c), r.rho, rtol=1e-8, atol=1e-12)
+
+
+def test_centred_cg_converges_to_definition():
+    w = make_workload("piecewise")
+    q, k, v = _head(w)
+    for i in (3, 100, 700):
+        r = O.oracle_row(q[i], k[:i + 1], v[:i + 1], w.lam)
+        g = O.oracle_row(q[i], k[:i + 1], v[:i + 1], w.lam, solver="cg_centred",
+                         cg_max_iters=400, cg_rel_tol=1e-13)
+        assert g.cg_resid <= 1e-13
+        np.testing.assert_allclose(g.b, r.b, rtol=0, atol=1e-8 * max(1, np.abs(r.b).max()))
+        np.testing.assert_allclose(g.rho, r.rho, rtol=1e-6, atol=1e-10)
+        assert abs(g.omega - r.omega) <= 1e-12 * r.omega
+
+
+def test_centred_output_weights_sum_to_one_any_rho():
+    """sum_j a_ij / sum_j a_ij = 1 trivially; the content is den = omega_i for
+    any rho_c, because the centred differences have zero weighted mean."""
+    q, k, v = _tiny_inputs(30, 6, 12, 2.0)
+    rng = np.random.default_rng(0)
+    i = 29
+    _, _, wt = O.causal_weights(q[i], k[:i + 1], 1 / np.sqrt(6))
+    Zc, om, kbar, mu, Sc = O.centred_moments(q[i], k[:i + 1], wt, 0.5)
+    for _ in range(3):
+        _, _, den = O.centred_intercept(wt, Zc, v[:i + 1], rng.standard_normal(6) * 10)
+        assert abs(den - om) <= 1e-10 * om
