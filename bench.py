@@ -1,0 +1,211 @@
+#!/usr/bin/env python3
+"""Throughput of the causal LLA forward on one MI355X.
+
+One step = one full forward (all three phases: moment scan, CG, output scan)
+over one batch of the synthetic workload, inputs resident in HBM. Prints one
+JSON line: queries/s (one query = one (batch, head, position) row solved),
+TFLOP/s of the algorithmic FLOP count, the dominant kernel's roofline
+fraction, and the float64 CPU oracle timed on a bounded sample of the same
+workload on this host's cores.
+
+Algorithmic FLOPs per causal pair (i, j <= i), d = head dim: 4d for the
+moment scan (q.k and w k), 6d per CG iteration (q.k, p.k and U k), 6d for the
+output scan (q.k, rho.k and a v). F = d * sum_i (i+1) (10 + 6 T_i), with T_i
+the CG iterations query i took.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK = {  # MI355X published dense peaks
+    "mfma_fp16": 2500.0,   # TFLOP/s, fp16/bf16 matrix
+    "valu_fp32": 157.3,    # TFLOP/s, fp32 vector
+    "hbm": 8000.0,         # GB/s
+}
+
+
+def algorithmic_flops(n: int, d: int, iters: np.ndarray) -> float:
+    """iters: [B, H, n] CG iterations per query."""
+    pairs = np.arange(1, n + 1, dtype=np.float64)
+    return float(d * np.sum(pairs[None, None, :] * (10.0 + 6.0 * iters.astype(np.float64))))
+
+
+def _oracle_sample_job(args):
+    q, k, v, lam, rows = args
+    from threadpoolctl import threadpool_limits
+    from oracle import lla_oracle as O
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        O.oracle_head(q, k, v, lam, rows=rows)
+        return time.perf_counter() - t0, len(rows)
+
+
+def cpu_baseline(wl, target_rows: int, seed: int = 0):
+    """Time the float64 oracle (Cholesky per row, as written) on a seeded
+    uniform sample of (b, h, i) rows of the workload, one worker per core."""
+    from concurrent.futures import ProcessPoolExecutor
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    rng = np.random.default_rng(seed)
+    B, H, n = wl.B, wl.H, wl.n
+    flat = rng.choice(B * H * n, size=min(target_rows, B * H * n), replace=False)
+    by_head = {}
+    for f in flat:
+        bh, i = divmod(int(f), n)
+        by_head.setdefault(bh, []).append(i)
+    jobs = []
+    for bh, rows in by_head.items():
+        b, h = divmod(bh, H)
+        rows = sorted(rows)
+        # split long row lists so every worker gets a share
+        for c in range(0, len(rows), 64):
+            part = rows[c:c + 64]
+            kmax = part[-1] + 1
+            jobs.append((wl.q[b, h, :kmax], wl.k[b, h, :kmax], wl.v[b, h, :kmax], wl.lam, part))
+    t0 = time.perf_counter()
+    with ProcessPoolExecutor(max_workers=cores) as ex:
+        res = list(ex.map(_oracle_sample_job, jobs))
+    wall = time.perf_counter() - t0
+    cpu_s = sum(r[0] for r in res)
+    nrows = sum(r[1] for r in res)
+    return {
+        "value": nrows / wall, "unit": "queries/s", "cores": cores, "kind": "oracle",
+        "sample": (f"{nrows} rows drawn uniformly (seed {seed}) from the {B}x{H}x{n} rows of "
+                   f"the workload; float64 Cholesky per row; {cpu_s:.1f} CPU-s over "
+                   f"{wall:.1f} s wall"),
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="standard",
+                    choices=["tiny", "piecewise", "standard", "long", "recall"])
+    ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--split-u", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=3072,
+                    help="rows in the CPU-oracle sample (0 = skip)")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON file with measured HBM bytes per launch of the main kernel")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "the forward shards by (batch, head) with no communication, so the "
+              "whole-job rate is the per-GPU rate times the GPU count.", file=sys.stderr)
+        return 2
+
+    import torch
+    import local_linear_attention_flashlla_amd as lla
+    from local_linear_attention_flashlla_amd.workloads import make_workload
+    if not os.path.exists(lla._lib.LIB_PATH):
+        from local_linear_attention_flashlla_amd import build as _b
+        _b.build()
+    assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    dev = torch.device("cuda:0")
+
+    wl = make_workload(args.workload)
+    if wl.dtype == "f32":
+        q, k, v = (torch.from_numpy(a).to(dev) for a in (wl.q_dev, wl.k_dev, wl.v_dev))
+    else:
+        q, k, v = (torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+                   for a in (wl.q_dev, wl.k_dev, wl.v_dev))
+    kernel = {"auto": lla.LLA_KERNEL_AUTO, "valu": lla.LLA_KERNEL_VALU,
+              "mfma": lla.LLA_KERNEL_MFMA}[args.kernel]
+    flags = lla.LLA_FLAG_SPLIT_U if args.split_u else 0
+    B, H, n, d = wl.B, wl.H, wl.n, wl.d
+    out = torch.empty((B, H, n, d), dtype=torch.float32, device=dev)
+    ws_bytes = lla.workspace_bytes(B, H, n, d, wl.dtype, kernel)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    kernel_used = kernel
+    if kernel == lla.LLA_KERNEL_AUTO:
+        kernel_used = lla.LLA_KERNEL_MFMA if ws_bytes > 0 else lla.LLA_KERNEL_VALU
+
+    def step(events=None):
+        lla.forward(q, k, v, wl.lam, wl.cg_max_iters, wl.cg_rel_tol, out=out, workspace=ws,
+                    kernel=kernel, flags=flags, events=events)
+
+    # iteration counts for the algorithmic FLOP count (untimed)
+    iters = torch.empty((B, H, n), dtype=torch.int32, device=dev)
+    lla.forward(q, k, v, wl.lam, wl.cg_max_iters, wl.cg_rel_tol, out=out, workspace=ws,
+                kernel=kernel, flags=flags, cg_iters=iters)
+    torch.cuda.synchronize()
+    iters_np = iters.cpu().numpy()
+    flops = algorithmic_flops(n, d, iters_np)
+    flops_nom = algorithmic_flops(n, d, np.full_like(iters_np, wl.cg_max_iters))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events=ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    queries = B * H * n
+    value = queries / (ms_step * 1e-3)
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    if kernel_used == lla.LLA_KERNEL_MFMA:
+        bound, peak, unit = "mfma", PEAK["mfma_fp16"], "TFLOP/s"
+    else:
+        bound, peak, unit = "alu", PEAK["valu_fp32"], "TFLOP/s"
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            traffic = json.load(f).get("bytes_per_launch")
+
+    cpu = None
+    if args.cpu_rows > 0:
+        cpu = cpu_baseline(wl, args.cpu_rows)
+
+    rec = {
+        "metric": "LLA fwd queries/s + TFLOP/s (% MFMA peak) at n=4096,d=128, 1 MI355X",
+        "value": value,
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "H": H, "n": n, "d": d,
+                   "lambda": wl.lam, "cg_max_iters": wl.cg_max_iters,
+                   "cg_rel_tol": wl.cg_rel_tol,
+                   "kernel": {lla.LLA_KERNEL_MFMA: "mfma", lla.LLA_KERNEL_VALU: "valu"}[kernel_used],
+                   "split_u": bool(args.split_u)},
+        "tflops": tflops,
+        "flops_per_step": flops,
+        "flops_nominal": flops_nom,
+        "cg_iters_mean": float(iters_np.mean()),
+        "cg_iters_max": int(iters_np.max()),
+        "main_kernel_ms": kern_ms,
+        "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+                     "frac": achieved / peak, "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,164 @@
+/*
+ * lla.h -- C ABI of the causal Local Linear Attention (LLA) forward library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (per batch b, head h and query row i; j runs over the
+ * causal prefix 0..i, diagonal included). Source: "Local Linear Attention:
+ * reading notes" on arXiv:2510.01450 (Zuo et al.), section 2.1, Eqs. (6)-(8):
+ *
+ *   s_ij    = c q_i . k_j,   c = 1/sqrt(d)
+ *   w_ij    = exp(s_ij - max_{l<=i} s_il)           (largest weight is 1)
+ *   z_ij    = k_j - q_i
+ *   omega_i = sum_j w_ij,   mu_i = sum_j w_ij z_ij
+ *   Sigma_i = sum_j w_ij z_ij z_ij^T + lambda I,   rho_i = Sigma_i^{-1} mu_i
+ *   out_i   = sum_j w_ij (1 - z_ij^T rho_i) v_j / (omega_i - mu_i^T rho_i)
+ *
+ * i.e. the intercept of a kernel-weighted ridge regression of v on k around
+ * q_i. How it is computed follows the blocked three-phase scheme of section
+ * 2.2 (Algorithm 1) of the same page: per block of queries, (1) one scan over
+ * the key blocks with an online row max accumulates omega_i and
+ * mu~_i = sum_j w_ij k_j (Eqs. (10)-(11)); (2) matrix-free conjugate gradient,
+ * each iteration re-scanning the key blocks to form a Gram-matrix product
+ * (Eq. (12)); (3) a scan over the key/value blocks accumulates the output.
+ * The n x n weights are never stored; working memory is linear in n.
+ *
+ * The CG of phase (2) runs on the system centred at the weighted key mean
+ * kbar_i = mu~_i / omega_i instead of at q_i:
+ *     Sigma_c = sum_j w_ij (k_j - kbar_i)(k_j - kbar_i)^T + lambda I
+ *             = Sigma~_i - mu~_i mu~_i^T / omega_i,      Sigma_c rho_c = mu_i,
+ *     out_i   = sum_j w_ij (1 - (k_j - kbar_i)^T rho_c) v_j / omega_i.
+ * Since Sigma_i = Sigma_c + omega_i (kbar_i - q_i)(kbar_i - q_i)^T and
+ * mu_i = omega_i (kbar_i - q_i), this is the same output exactly (Sherman-
+ * Morrison), with rho_i = rho_c / (1 + (kbar_i - q_i)^T rho_c); it avoids the
+ * division by the Schur complement omega_i - mu_i^T rho_i, which amplifies
+ * any error in an unconverged CG iterate by omega_i / (omega_i - mu_i^T rho_i).
+ *
+ * CG policy (the pages leave it to an appendix that is not reproduced): x0 = 0,
+ * r0 = p0 = mu_i; a query stops at the first k with ||r_k|| <= tol ||r_0||
+ * (recurrence residual), on breakdown (p^T Sigma_c p <= 0 or r = 0), or at
+ * k = cg_max_iters. cg_rel_tol = 0 runs exactly cg_max_iters steps;
+ * cg_max_iters = 0 gives rho = 0, i.e. causal softmax attention. A stopped
+ * query freezes while the rest of its block continues. Non-convergence is not
+ * an error: it is reported through cg_iters / cg_resid.
+ *
+ * Conventions common to every entry point:
+ *  - Tensors are DEVICE pointers, contiguous row-major [B][H][n][d] (d
+ *    fastest), 16-byte aligned; value dimension = key dimension = d.
+ *  - Inputs are never written. `out` (fp32) and every non-NULL optional
+ *    output are fully written. The library keeps no pointer after the call
+ *    and no state between calls; calls are reentrant and thread safe.
+ *  - Asynchronous: the call returns after enqueueing work on `stream`
+ *    (NULL = the default stream); the caller synchronises. Device faults
+ *    surface at that synchronisation.
+ *  - Validation runs on the host before any device work; on failure nothing
+ *    is enqueued or written and a negative status is returned, with detail in
+ *    lla_last_error().
+ *  - NaN/Inf inputs are not checked; they propagate to the affected rows.
+ */
+#ifndef LLA_H
+#define LLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LLA_VERSION 100 /* 1.0.0 */
+
+/* Status codes. */
+enum {
+  LLA_OK = 0,
+  LLA_ERR_INVALID_ARG = -1, /* NULL required pointer, B/H/n < 1, lambda not
+                               finite or <= 0, cg_max_iters < 0 or > 100000,
+                               cg_rel_tol < 0 or NaN, out overlapping an
+                               input, misaligned pointer, unknown dtype,
+                               kernel or flag */
+  LLA_ERR_UNSUPPORTED = -2, /* d not in {16, 32, 64, 128}; sizes too large;
+                               a kernel choice not available for the dtype/d */
+  LLA_ERR_HIP = -3,         /* a HIP launch or allocation failed */
+  LLA_ERR_WORKSPACE = -4    /* caller workspace smaller than required */
+};
+
+/* Element type of q, k, v. */
+enum { LLA_DTYPE_F32 = 0, LLA_DTYPE_BF16 = 1 };
+
+/* Kernel selection for lla_forward_ex. */
+enum {
+  LLA_KERNEL_AUTO = 0, /* fp32 inputs: VALU; bf16 inputs with d in {64,128}:
+                          MFMA; otherwise VALU */
+  LLA_KERNEL_VALU = 1, /* fp32 vector-ALU kernel, any supported d/dtype */
+  LLA_KERNEL_MFMA = 2  /* fp16 matrix-core kernel; bf16 inputs, d in {64,128} */
+};
+
+/* Flags for lla_forward_ex (bitwise OR). */
+enum {
+  LLA_FLAG_SPLIT_U = 1 /* MFMA kernel: carry the CG tile W*(K p) as two fp16
+                          terms (hi + lo) instead of one; slower, more exact */
+};
+
+/* Full argument block of lla_forward_ex. Zero-initialise, then fill. */
+typedef struct lla_fwd_args {
+  int dtype;          /* LLA_DTYPE_F32 or LLA_DTYPE_BF16 */
+  const void* q;      /* [B][H][n][d] dtype, device */
+  const void* k;      /* [B][H][n][d] dtype, device */
+  const void* v;      /* [B][H][n][d] dtype, device */
+  float* out;         /* [B][H][n][d] fp32, device, written */
+  int B, H, n, d;
+  float lambda;       /* ridge on the local slope; > 0 */
+  int cg_max_iters;   /* >= 0 */
+  float cg_rel_tol;   /* >= 0; 0 = run exactly cg_max_iters steps */
+  /* optional outputs, NULL = not wanted (device pointers) */
+  float* omega;       /* [B][H][n]    omega_i */
+  float* rho;         /* [B][H][n][d] rho_i = Sigma_i^{-1} mu_i (pages' rho) */
+  float* rowmax;      /* [B][H][n]    max_{l<=i} c q_i . k_l */
+  int32_t* cg_iters;  /* [B][H][n]    CG steps taken by the query */
+  float* cg_resid;    /* [B][H][n]    ||r_k|| / ||r_0|| at exit (0 if r_0 = 0) */
+  /* optional caller workspace (device); NULL = the library allocates and
+     frees it stream-ordered on `stream` */
+  void* workspace;
+  size_t workspace_bytes;
+  int kernel;         /* LLA_KERNEL_* */
+  int flags;          /* LLA_FLAG_* */
+  /* optional timing events (created by the caller, NULL = none): recorded on
+     `stream` immediately before and after the call's main kernel, the one
+     that runs the three phases (any set-up kernel falls outside them) */
+  hipEvent_t ev_main_begin;
+  hipEvent_t ev_main_end;
+} lla_fwd_args;
+
+/* out = LLA(q, k, v) for fp32 inputs. Arguments as in lla_fwd_args;
+   returns LLA_OK or a negative status. Kernel: AUTO. */
+int lla_forward_f32(const float* q, const float* k, const float* v, float* out,
+                    int B, int H, int n, int d, float lambda, int cg_max_iters,
+                    float cg_rel_tol, hipStream_t stream);
+
+/* Same for bfloat16 inputs, passed as their 16-bit patterns. */
+int lla_forward_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                     float* out, int B, int H, int n, int d, float lambda,
+                     int cg_max_iters, float cg_rel_tol, hipStream_t stream);
+
+/* Full form: dtype, kernel choice, optional outputs, optional workspace. */
+int lla_forward_ex(const lla_fwd_args* args, hipStream_t stream);
+
+/* Device workspace bytes lla_forward_ex needs for these sizes and this
+   kernel choice (0 if none). Returns 0 for invalid sizes too. */
+size_t lla_workspace_bytes(int B, int H, int n, int d, int dtype, int kernel);
+
+/* Static, human-readable name of a status code. */
+const char* lla_status_string(int status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* lla_last_error(void);
+
+/* LLA_VERSION of the loaded library. */
+int lla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LLA_H */

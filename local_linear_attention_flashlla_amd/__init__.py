@@ -1,0 +1,103 @@
+"""Causal Local Linear Attention (LLA) forward for AMD Instinct MI355X.
+
+The computation runs in liblla.so (hand-written HIP kernels for gfx950
+behind the C ABI of include/lla.h); this package is a thin binding over it.
+``forward`` takes torch tensors on the GPU and calls the library on torch's
+current stream. There is no CPU fallback: without the built library or a GPU
+the call raises.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+from . import _lib
+from ._lib import (LLA_DTYPE_BF16, LLA_DTYPE_F32, LLA_FLAG_SPLIT_U, LLA_KERNEL_AUTO,
+                   LLA_KERNEL_MFMA, LLA_KERNEL_VALU, LlaError)
+
+__all__ = ["forward", "workspace_bytes", "LlaError", "LLA_KERNEL_AUTO", "LLA_KERNEL_VALU",
+           "LLA_KERNEL_MFMA", "LLA_FLAG_SPLIT_U", "version"]
+
+
+def version() -> int:
+    return _lib.load().lla_version()
+
+
+def workspace_bytes(B: int, H: int, n: int, d: int, dtype: str = "bf16",
+                    kernel: int = LLA_KERNEL_AUTO) -> int:
+    dt = LLA_DTYPE_BF16 if dtype == "bf16" else LLA_DTYPE_F32
+    return int(_lib.load().lla_workspace_bytes(B, H, n, d, dt, kernel))
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def forward(q, k, v, lam: float, cg_max_iters: int, cg_rel_tol: float, *,
+            out=None, omega=None, rho=None, rowmax=None, cg_iters=None, cg_resid=None,
+            workspace=None, kernel: int = LLA_KERNEL_AUTO, flags: int = 0, stream=None,
+            events=None):
+    """Causal LLA forward on the GPU.
+
+    q, k, v: contiguous [B, H, n, d] tensors on a HIP device, all float32 or all
+    bfloat16. Returns ``out`` ([B, H, n, d] float32). Optional outputs are
+    filled when given: omega/rowmax/cg_resid [B, H, n] float32, rho
+    [B, H, n, d] float32, cg_iters [B, H, n] int32. ``workspace`` is an
+    optional uint8 device tensor of at least ``workspace_bytes(...)`` bytes.
+    The call is asynchronous on ``stream`` (default: torch's current stream).
+    ``events``: optional (begin, end) pair of ``torch.cuda.Event`` that the
+    library records around its main kernel.
+    """
+    import torch
+
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share one [B, H, n, d] shape")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share one dtype")
+    if q.dtype == torch.float32:
+        dtype = LLA_DTYPE_F32
+    elif q.dtype == torch.bfloat16:
+        dtype = LLA_DTYPE_BF16
+    else:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    B, H, n, d = (int(s) for s in q.shape)
+    if out is None:
+        out = torch.empty((B, H, n, d), dtype=torch.float32, device=q.device)
+    for name, t, dt, shape in (("out", out, torch.float32, (B, H, n, d)),
+                               ("omega", omega, torch.float32, (B, H, n)),
+                               ("rho", rho, torch.float32, (B, H, n, d)),
+                               ("rowmax", rowmax, torch.float32, (B, H, n)),
+                               ("cg_iters", cg_iters, torch.int32, (B, H, n)),
+                               ("cg_resid", cg_resid, torch.float32, (B, H, n))):
+        if t is None:
+            continue
+        if t.dtype != dt or tuple(t.shape) != shape or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous {dt} GPU tensor of shape {shape}")
+    a = _lib.LlaFwdArgs()
+    a.dtype = dtype
+    a.q, a.k, a.v, a.out = _ptr(q), _ptr(k), _ptr(v), _ptr(out)
+    a.B, a.H, a.n, a.d = B, H, n, d
+    a.lambda_ = float(lam)
+    a.cg_max_iters = int(cg_max_iters)
+    a.cg_rel_tol = float(cg_rel_tol)
+    a.omega, a.rho, a.rowmax = _ptr(omega), _ptr(rho), _ptr(rowmax)
+    a.cg_iters, a.cg_resid = _ptr(cg_iters), _ptr(cg_resid)
+    if workspace is not None:
+        a.workspace = _ptr(workspace)
+        a.workspace_bytes = int(workspace.numel() * workspace.element_size())
+    a.kernel = int(kernel)
+    a.flags = int(flags)
+    if events is not None:
+        ev0, ev1 = events
+        ev0.record()  # makes torch create the underlying HIP events
+        ev1.record()
+        a.ev_main_begin, a.ev_main_end = int(ev0.cuda_event), int(ev1.cuda_event)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    import ctypes
+    st = _lib.load().lla_forward_ex(ctypes.byref(a), ctypes.c_void_p(handle))
+    _lib.check(st)
+    return out

@@ -1,0 +1,210 @@
+// Host side of liblla.so: argument validation, kernel dispatch, workspace
+// handling and status reporting for the C ABI declared in include/lla.h.
+//
+// Validation is pure host arithmetic on the arguments (no device call), so a
+// rejected call enqueues nothing and writes nothing.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/lla.h"
+#include "lla_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [a, a + na) and [b, b + nb) overlap (byte ranges).
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+bool d_supported(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+// Resolve LLA_KERNEL_AUTO and check the choice. Returns LLA_OK or a status.
+int resolve_kernel(int dtype, int d, int requested, int* chosen) {
+  if (requested == LLA_KERNEL_AUTO) {
+    *chosen = lla::mfma_supported(dtype, d) ? LLA_KERNEL_MFMA : LLA_KERNEL_VALU;
+    return LLA_OK;
+  }
+  if (requested == LLA_KERNEL_VALU) {
+    *chosen = LLA_KERNEL_VALU;
+    return LLA_OK;
+  }
+  if (requested == LLA_KERNEL_MFMA) {
+    if (!lla::mfma_supported(dtype, d))
+      return fail(LLA_ERR_UNSUPPORTED, "MFMA kernel needs bf16 inputs and d in {64,128} (dtype=%d d=%d)",
+                  dtype, d);
+    *chosen = LLA_KERNEL_MFMA;
+    return LLA_OK;
+  }
+  return fail(LLA_ERR_INVALID_ARG, "unknown kernel choice %d", requested);
+}
+
+int validate(const lla_fwd_args* a) {
+  if (!a) return fail(LLA_ERR_INVALID_ARG, "args is NULL");
+  if (a->dtype != LLA_DTYPE_F32 && a->dtype != LLA_DTYPE_BF16)
+    return fail(LLA_ERR_INVALID_ARG, "unknown dtype %d", a->dtype);
+  if (!a->q || !a->k || !a->v || !a->out)
+    return fail(LLA_ERR_INVALID_ARG, "q, k, v and out must be non-NULL");
+  if (a->B < 1 || a->H < 1 || a->n < 1)
+    return fail(LLA_ERR_INVALID_ARG, "B, H, n must be >= 1 (B=%d H=%d n=%d)", a->B, a->H, a->n);
+  if (!d_supported(a->d)) return fail(LLA_ERR_UNSUPPORTED, "d=%d not in {16,32,64,128}", a->d);
+  if (!std::isfinite(a->lambda) || !(a->lambda > 0.f))
+    return fail(LLA_ERR_INVALID_ARG, "lambda must be finite and > 0 (got %g)", (double)a->lambda);
+  if (a->cg_max_iters < 0 || a->cg_max_iters > 100000)
+    return fail(LLA_ERR_INVALID_ARG, "cg_max_iters must be in [0, 100000] (got %d)", a->cg_max_iters);
+  if (!(a->cg_rel_tol >= 0.f) || !std::isfinite(a->cg_rel_tol))
+    return fail(LLA_ERR_INVALID_ARG, "cg_rel_tol must be finite and >= 0 (got %g)", (double)a->cg_rel_tol);
+  if (a->flags & ~LLA_FLAG_SPLIT_U) return fail(LLA_ERR_INVALID_ARG, "unknown flags 0x%x", a->flags);
+  // sizes: every element count must fit comfortably in 64-bit and the grid in 2^31
+  const unsigned long long bh = (unsigned long long)a->B * (unsigned long long)a->H;
+  if (bh > 0x7fffffffULL) return fail(LLA_ERR_UNSUPPORTED, "B*H too large");
+  const unsigned long long rows = bh * (unsigned long long)a->n;
+  if (rows > (1ULL << 40)) return fail(LLA_ERR_UNSUPPORTED, "B*H*n too large");
+  const unsigned long long grid = bh * (unsigned long long)((a->n + 31) / 32);
+  if (grid > 0x7fffffffULL) return fail(LLA_ERR_UNSUPPORTED, "grid too large");
+  const size_t esz = a->dtype == LLA_DTYPE_F32 ? 4 : 2;
+  const size_t nin = (size_t)(rows * (unsigned long long)a->d) * esz;
+  const size_t nout = (size_t)(rows * (unsigned long long)a->d) * 4;
+  const size_t nrow = (size_t)rows * 4;
+  const void* ins[3] = {a->q, a->k, a->v};
+  for (const void* in : ins) {
+    if (!aligned16(in)) return fail(LLA_ERR_INVALID_ARG, "input pointer %p not 16-byte aligned", in);
+  }
+  struct Out { const void* p; size_t bytes; const char* name; };
+  const Out outs[6] = {{a->out, nout, "out"},           {a->rho, nout, "rho"},
+                       {a->omega, nrow, "omega"},       {a->rowmax, nrow, "rowmax"},
+                       {a->cg_iters, nrow, "cg_iters"}, {a->cg_resid, nrow, "cg_resid"}};
+  for (int i = 0; i < 6; ++i) {
+    if (!outs[i].p) continue;
+    if (!aligned16(outs[i].p))
+      return fail(LLA_ERR_INVALID_ARG, "%s pointer %p not 16-byte aligned", outs[i].name, outs[i].p);
+    for (const void* in : ins)
+      if (overlap(outs[i].p, outs[i].bytes, in, nin))
+        return fail(LLA_ERR_INVALID_ARG, "%s overlaps an input", outs[i].name);
+    for (int j = 0; j < i; ++j)
+      if (overlap(outs[i].p, outs[i].bytes, outs[j].p, outs[j].bytes))
+        return fail(LLA_ERR_INVALID_ARG, "%s overlaps %s", outs[i].name, outs[j].name);
+  }
+  if (a->workspace && !aligned16(a->workspace))
+    return fail(LLA_ERR_INVALID_ARG, "workspace pointer not 16-byte aligned");
+  return LLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lla_status_string(int status) {
+  switch (status) {
+    case LLA_OK: return "LLA_OK";
+    case LLA_ERR_INVALID_ARG: return "LLA_ERR_INVALID_ARG";
+    case LLA_ERR_UNSUPPORTED: return "LLA_ERR_UNSUPPORTED";
+    case LLA_ERR_HIP: return "LLA_ERR_HIP";
+    case LLA_ERR_WORKSPACE: return "LLA_ERR_WORKSPACE";
+    default: return "LLA_ERR_UNKNOWN";
+  }
+}
+
+const char* lla_last_error(void) { return g_last_error; }
+
+int lla_version(void) { return LLA_VERSION; }
+
+size_t lla_workspace_bytes(int B, int H, int n, int d, int dtype, int kernel) {
+  if (B < 1 || H < 1 || n < 1 || !d_supported(d)) return 0;
+  if (dtype != LLA_DTYPE_F32 && dtype != LLA_DTYPE_BF16) return 0;
+  int chosen = 0;
+  char saved[sizeof(g_last_error)];
+  memcpy(saved, g_last_error, sizeof(saved));
+  const int st = resolve_kernel(dtype, d, kernel, &chosen);
+  memcpy(g_last_error, saved, sizeof(saved));
+  if (st != LLA_OK) return 0;
+  if (chosen == LLA_KERNEL_MFMA) return lla::mfma_workspace_bytes(B * H, n, d);
+  return 0;
+}
+
+int lla_forward_ex(const lla_fwd_args* a, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  int st = validate(a);
+  if (st != LLA_OK) return st;
+  int kernel = 0;
+  st = resolve_kernel(a->dtype, a->d, a->kernel, &kernel);
+  if (st != LLA_OK) return st;
+  lla::FwdParams p{};
+  p.q = a->q; p.k = a->k; p.v = a->v; p.out = a->out;
+  p.omega = a->omega; p.rho = a->rho; p.rowmax = a->rowmax;
+  p.cg_iters = a->cg_iters; p.cg_resid = a->cg_resid;
+  p.BH = a->B * a->H; p.n = a->n; p.d = a->d; p.dtype = a->dtype;
+  p.lambda = a->lambda; p.cg_max_iters = a->cg_max_iters; p.cg_rel_tol = a->cg_rel_tol;
+  p.flags = a->flags;
+  p.ev_main_begin = a->ev_main_begin;
+  p.ev_main_end = a->ev_main_end;
+  if (kernel == LLA_KERNEL_VALU) {
+    const hipError_t e = lla::launch_valu(p, stream);
+    if (e != hipSuccess) return fail(LLA_ERR_HIP, "VALU launch: %s", hipGetErrorString(e));
+    return LLA_OK;
+  }
+  // MFMA: needs a workspace
+  const size_t need = lla::mfma_workspace_bytes(p.BH, p.n, p.d);
+  void* ws = a->workspace;
+  bool owned = false;
+  if (ws) {
+    if (a->workspace_bytes < need)
+      return fail(LLA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", a->workspace_bytes, need);
+  } else if (need > 0) {
+    const hipError_t e = hipMallocAsync(&ws, need, stream);
+    if (e != hipSuccess) return fail(LLA_ERR_HIP, "workspace allocation of %zu bytes: %s", need,
+                                     hipGetErrorString(e));
+    owned = true;
+  }
+  p.workspace = ws;
+  p.workspace_bytes = owned ? need : a->workspace_bytes;
+  const hipError_t e = lla::launch_mfma(p, stream);
+  if (owned) {
+    const hipError_t f = hipFreeAsync(ws, stream);
+    if (e == hipSuccess && f != hipSuccess)
+      return fail(LLA_ERR_HIP, "workspace free: %s", hipGetErrorString(f));
+  }
+  if (e != hipSuccess) return fail(LLA_ERR_HIP, "MFMA launch: %s", hipGetErrorString(e));
+  return LLA_OK;
+}
+
+int lla_forward_f32(const float* q, const float* k, const float* v, float* out, int B, int H, int n,
+                    int d, float lambda, int cg_max_iters, float cg_rel_tol, hipStream_t stream) {
+  lla_fwd_args a{};
+  a.dtype = LLA_DTYPE_F32;
+  a.q = q; a.k = k; a.v = v; a.out = out;
+  a.B = B; a.H = H; a.n = n; a.d = d;
+  a.lambda = lambda; a.cg_max_iters = cg_max_iters; a.cg_rel_tol = cg_rel_tol;
+  return lla_forward_ex(&a, stream);
+}
+
+int lla_forward_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, float* out, int B, int H,
+                     int n, int d, float lambda, int cg_max_iters, float cg_rel_tol,
+                     hipStream_t stream) {
+  lla_fwd_args a{};
+  a.dtype = LLA_DTYPE_BF16;
+  a.q = q; a.k = k; a.v = v; a.out = out;
+  a.B = B; a.H = H; a.n = n; a.d = d;
+  a.lambda = lambda; a.cg_max_iters = cg_max_iters; a.cg_rel_tol = cg_rel_tol;
+  return lla_forward_ex(&a, stream);
+}
+
+}  // extern "C"

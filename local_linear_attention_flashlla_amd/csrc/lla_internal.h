@@ -1,0 +1,44 @@
+// Internal declarations shared by the host API and the kernel translation
+// units of liblla.so. Not part of the public ABI (see include/lla.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lla {
+
+// Everything a forward launch needs, already validated by the host API.
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* out;
+  float* omega;      // optional [BH][n]
+  float* rho;        // optional [BH][n][d]
+  float* rowmax;     // optional [BH][n]
+  int32_t* cg_iters; // optional [BH][n]
+  float* cg_resid;   // optional [BH][n]
+  int BH;            // B * H
+  int n;
+  int d;
+  int dtype;         // LLA_DTYPE_*
+  float lambda;
+  int cg_max_iters;
+  float cg_rel_tol;
+  int flags;
+  void* workspace;   // device scratch (kernel specific), may be NULL
+  size_t workspace_bytes;
+  hipEvent_t ev_main_begin;  // optional, recorded around the main kernel
+  hipEvent_t ev_main_end;
+};
+
+// fp32 vector-ALU kernel (any d in {16,32,64,128}, fp32 or bf16 inputs).
+hipError_t launch_valu(const FwdParams& p, hipStream_t stream);
+
+// fp16 matrix-core kernel (bf16 inputs, d in {64,128}).
+size_t mfma_workspace_bytes(int BH, int n, int d);
+bool mfma_supported(int dtype, int d);
+hipError_t launch_mfma(const FwdParams& p, hipStream_t stream);
+
+}  // namespace lla

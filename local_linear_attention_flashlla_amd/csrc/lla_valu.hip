@@ -1,0 +1,388 @@
+// fp32 vector-ALU kernel for the causal LLA forward pass.
+//
+// One workgroup of 256 threads owns a block of VQ = 32 consecutive query rows
+// of one (batch, head) and runs all three phases of the blocked forward of
+// "Local Linear Attention: reading notes" (section 2.2, Algorithm 1) for it:
+//   1. scan key tiles with an online row max -> omega_i, mu~_i (Eqs. (10)-(11))
+//   2. matrix-free CG, one key-tile sweep per iteration for the Gram product
+//      (Eq. (12), centred at kbar_i = mu~_i / omega_i; see include/lla.h)
+//   3. scan key/value tiles -> out_i = sum_j w_ij (1 - (k_j - kbar_i)^T rho) v_j
+//      / sum_j w_ij (1 - (k_j - kbar_i)^T rho)
+// Per-query CG state lives in registers (x, r, kbar, accumulators) and LDS
+// (q, p); the weights exist only as a VQ x VK tile in LDS.
+//
+// Thread roles: thread t serves query row t >> 3 together with the 7 other
+// threads of its group of 8 lanes (row reductions are 3 xor-shuffles). For
+// score tiles it computes keys (t & 7) and (t & 7) + 8 of the tile; for
+// d-vectors it owns the float4 chunks (t & 7) + 8 u of the row.
+//
+// This kernel is the fp32 path (fp32 inputs must not be rounded to a 16-bit
+// matrix type) and the reference GPU path for bf16 inputs.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "lla_internal.h"
+#include "../../include/lla.h"
+
+namespace lla {
+namespace {
+
+constexpr int VQ = 32;   // queries per workgroup
+constexpr int VK = 16;   // keys per tile
+constexpr int VT = 256;  // threads per workgroup
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float load_elem(const float* p, size_t i) { return p[i]; }
+__device__ __forceinline__ float load_elem(const uint16_t* p, size_t i) {
+  return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
+}
+
+__device__ __forceinline__ float4 load4(const float* p, size_t i) {
+  return *reinterpret_cast<const float4*>(p + i);
+}
+__device__ __forceinline__ float4 load4(const uint16_t* p, size_t i) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p + i);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+}
+
+__device__ __forceinline__ float row_sum8(float v) {
+  v += __shfl_xor(v, 1);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 4);
+  return v;
+}
+__device__ __forceinline__ float row_max8(float v) {
+  v = fmaxf(v, __shfl_xor(v, 1));
+  v = fmaxf(v, __shfl_xor(v, 2));
+  v = fmaxf(v, __shfl_xor(v, 4));
+  return v;
+}
+__device__ __forceinline__ float dot4(float4 a, float4 b) {
+  return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+}
+__device__ __forceinline__ float4 fma4(float s, float4 a, float4 c) {
+  return make_float4(fmaf(s, a.x, c.x), fmaf(s, a.y, c.y), fmaf(s, a.z, c.z), fmaf(s, a.w, c.w));
+}
+
+// Load rows [r0, r0 + rows) of a [n][D] matrix into LDS (row stride LD
+// floats), zero-filling rows at or beyond `rend`.
+template <int D, int LD, typename Tin>
+__device__ __forceinline__ void stage_rows(float* dst, const Tin* src, int r0, int rows,
+                                           int rend) {
+  constexpr int NC = D / 4;
+  for (int e = threadIdx.x; e < rows * NC; e += VT) {
+    const int r = e / NC, c = (e % NC) * 4;
+    float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (r0 + r < rend) val = load4(src, static_cast<size_t>(r0 + r) * D + c);
+    *reinterpret_cast<float4*>(dst + r * LD + c) = val;
+  }
+}
+
+template <int D, typename Tin>
+__global__ __launch_bounds__(VT) void lla_valu_kernel(FwdParams P) {
+  constexpr int LD = D + 4;           // padded LDS row stride (floats)
+  constexpr int NC = D / 4;           // float4 chunks per row
+  constexpr int YC = (NC + 7) / 8;    // chunks owned per thread
+  __shared__ __align__(16) float sQ[VQ * LD];  // q rows of the block
+  __shared__ __align__(16) float sP[VQ * LD];  // p (phase 2) / rho (phase 3)
+  __shared__ __align__(16) float sK[VK * LD];  // key tile
+  __shared__ __align__(16) float sV[VK * LD];  // value tile (phase 3)
+  __shared__ float sW[VQ * (VK + 1)];          // weight-derived tile
+  __shared__ int sAny;
+
+  const int tid = threadIdx.x;
+  const int row = tid >> 3;
+  const int l8 = tid & 7;
+  const int nqb = (P.n + VQ - 1) / VQ;
+  const int blk = blockIdx.x;
+  const int qb = nqb - 1 - blk / P.BH;  // longest causal prefix first
+  const int bh = blk % P.BH;
+  const int i0 = qb * VQ;
+  const int nq = min(VQ, P.n - i0);
+  const int kend = i0 + nq;           // keys 0 .. kend-1 are visible to the block
+  const int qi = i0 + row;            // this thread's query row
+  const bool valid = row < nq;
+  const size_t base = static_cast<size_t>(bh) * P.n * D;
+  const Tin* Q = static_cast<const Tin*>(P.q) + base;
+  const Tin* K = static_cast<const Tin*>(P.k) + base;
+  const Tin* V = static_cast<const Tin*>(P.v) + base;
+  const float sc2 = kLog2e / sqrtf(static_cast<float>(D));  // scores in log2 units
+  const float lam = P.lambda;
+
+  stage_rows<D, LD>(sQ, Q, i0, VQ, kend);
+
+  // ---------------- phase 1: online max, omega, mu~ ----------------
+  float m2 = -INFINITY;  // running row max (log2 units)
+  float om = 0.f;
+  float4 acc[YC];
+  for (int u = 0; u < YC; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+
+  for (int kt = 0; kt < kend; kt += VK) {
+    __syncthreads();
+    stage_rows<D, LD>(sK, K, kt, VK, kend);
+    __syncthreads();
+    float s[2];
+    float tmax = -INFINITY;
+    for (int u = 0; u < 2; ++u) {
+      const int kc = l8 + 8 * u;
+      const int j = kt + kc;
+      float dsum = 0.f;
+      for (int c = 0; c < D; c += 4)
+        dsum += dot4(*reinterpret_cast<const float4*>(sQ + row * LD + c),
+                     *reinterpret_cast<const float4*>(sK + kc * LD + c));
+      s[u] = (valid && j <= qi) ? dsum * sc2 : -INFINITY;
+      tmax = fmaxf(tmax, s[u]);
+    }
+    tmax = row_max8(tmax);
+    const float mnew = fmaxf(m2, tmax);
+    const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(m2 - mnew);
+    float psum = 0.f;
+    for (int u = 0; u < 2; ++u) {
+      const float w = (s[u] == -INFINITY) ? 0.f : exp2f(s[u] - mnew);
+      sW[row * (VK + 1) + l8 + 8 * u] = w;
+      psum += w;
+    }
+    om = om * alpha + row_sum8(psum);
+    m2 = mnew;
+    for (int u = 0; u < YC; ++u) {
+      acc[u].x *= alpha; acc[u].y *= alpha; acc[u].z *= alpha; acc[u].w *= alpha;
+    }
+    __syncthreads();
+    for (int u = 0; u < YC; ++u) {
+      const int c = (l8 + 8 * u) * 4;
+      if (c < D) {
+        float4 a = acc[u];
+        for (int kk = 0; kk < VK; ++kk)
+          a = fma4(sW[row * (VK + 1) + kk], *reinterpret_cast<const float4*>(sK + kk * LD + c), a);
+        acc[u] = a;
+      }
+    }
+  }
+
+  // ------------- CG set-up on the mean-centred system ----------------
+  // kbar = mu~ / omega; mu = mu~ - omega q = omega (kbar - q); x0 = 0, r0 = p0 = mu.
+  float4 kb[YC], x[YC], r[YC];
+  float rr = 0.f, kp = 0.f;
+  const float inv_om = valid ? 1.f / om : 0.f;
+  for (int u = 0; u < YC; ++u) {
+    const int c = (l8 + 8 * u) * 4;
+    kb[u] = x[u] = r[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c < D && valid) {
+      const float4 qv = *reinterpret_cast<const float4*>(sQ + row * LD + c);
+      const float4 a = acc[u];
+      kb[u] = make_float4(a.x * inv_om, a.y * inv_om, a.z * inv_om, a.w * inv_om);
+      r[u] = make_float4(a.x - om * qv.x, a.y - om * qv.y, a.z - om * qv.z, a.w - om * qv.w);
+      rr += dot4(r[u], r[u]);
+      kp += dot4(kb[u], r[u]);
+    }
+  }
+  __syncthreads();  // sP is free (phase 1 never touched it) but keep LDS phases apart
+  for (int u = 0; u < YC; ++u) {
+    const int c = (l8 + 8 * u) * 4;
+    if (c < D) *reinterpret_cast<float4*>(sP + row * LD + c) = r[u];
+  }
+  rr = row_sum8(rr);
+  kp = row_sum8(kp);
+  const float r0 = sqrtf(rr);
+  const float stop_at = P.cg_rel_tol * r0;
+  bool active = valid && rr > 0.f && P.cg_max_iters > 0;
+  int iters = 0;
+
+  // ---------------- phase 2: matrix-free CG ----------------
+  for (int it = 0; it < P.cg_max_iters; ++it) {
+    if (tid == 0) sAny = 0;
+    __syncthreads();
+    if (active && l8 == 0) sAny = 1;
+    __syncthreads();
+    if (!sAny) break;
+    // Y = sum_j w_ij k_j ((k_j - kbar) . p) over the causal prefix
+    float usum = 0.f;
+    for (int u = 0; u < YC; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int kt = 0; kt < kend; kt += VK) {
+      __syncthreads();
+      stage_rows<D, LD>(sK, K, kt, VK, kend);
+      __syncthreads();
+      for (int u = 0; u < 2; ++u) {
+        const int kc = l8 + 8 * u;
+        const int j = kt + kc;
+        float ds = 0.f, dt = 0.f;
+        for (int c = 0; c < D; c += 4) {
+          const float4 kv = *reinterpret_cast<const float4*>(sK + kc * LD + c);
+          ds += dot4(*reinterpret_cast<const float4*>(sQ + row * LD + c), kv);
+          dt += dot4(*reinterpret_cast<const float4*>(sP + row * LD + c), kv);
+        }
+        float U = 0.f;
+        if (valid && j <= qi) U = exp2f(ds * sc2 - m2) * (dt - kp);
+        sW[row * (VK + 1) + kc] = U;
+        usum += U;
+      }
+      __syncthreads();
+      for (int u = 0; u < YC; ++u) {
+        const int c = (l8 + 8 * u) * 4;
+        if (c < D) {
+          float4 a = acc[u];
+          for (int kk = 0; kk < VK; ++kk)
+            a = fma4(sW[row * (VK + 1) + kk], *reinterpret_cast<const float4*>(sK + kk * LD + c), a);
+          acc[u] = a;
+        }
+      }
+    }
+    usum = row_sum8(usum);
+    // Sigma_c p = Y - (sum_j U_ij) kbar + lambda p; then the CG step.
+    float pAp = 0.f;
+    float4 Ap[YC], pv[YC];
+    for (int u = 0; u < YC; ++u) {
+      const int c = (l8 + 8 * u) * 4;
+      pv[u] = Ap[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (c < D) {
+        pv[u] = *reinterpret_cast<const float4*>(sP + row * LD + c);
+        const float4 a = acc[u];
+        Ap[u] = make_float4(a.x - usum * kb[u].x + lam * pv[u].x, a.y - usum * kb[u].y + lam * pv[u].y,
+                            a.z - usum * kb[u].z + lam * pv[u].z, a.w - usum * kb[u].w + lam * pv[u].w);
+        pAp += dot4(pv[u], Ap[u]);
+      }
+    }
+    pAp = row_sum8(pAp);
+    bool step = active && pAp > 0.f;
+    if (active && !step) active = false;  // breakdown
+    float rrn = 0.f;
+    const float al = step ? rr / pAp : 0.f;
+    for (int u = 0; u < YC; ++u) {
+      if (step) {
+        x[u] = fma4(al, pv[u], x[u]);
+        r[u] = fma4(-al, Ap[u], r[u]);
+      }
+      rrn += dot4(r[u], r[u]);
+    }
+    rrn = row_sum8(rrn);
+    float kpn = 0.f;
+    if (step) {
+      ++iters;
+      if (sqrtf(rrn) <= stop_at || rrn == 0.f) {
+        active = false;
+      } else {
+        const float be = rrn / rr;
+        for (int u = 0; u < YC; ++u) {
+          const int c = (l8 + 8 * u) * 4;
+          pv[u] = fma4(be, pv[u], r[u]);
+          if (c < D) *reinterpret_cast<float4*>(sP + row * LD + c) = pv[u];
+          kpn += dot4(kb[u], pv[u]);
+        }
+      }
+      rr = rrn;
+    }
+    kpn = row_sum8(kpn);
+    if (active) kp = kpn;
+    __syncthreads();
+  }
+
+  // ---------------- phase 3: output scan ----------------
+  // a_ij = w_ij (1 - (k_j - kbar) . rho_c); out_i = sum_j a_ij v_j / sum_j a_ij
+  __syncthreads();
+  float kr = 0.f, qr = 0.f;
+  for (int u = 0; u < YC; ++u) {
+    const int c = (l8 + 8 * u) * 4;
+    if (c < D) {
+      *reinterpret_cast<float4*>(sP + row * LD + c) = x[u];
+      kr += dot4(kb[u], x[u]);
+      qr += dot4(*reinterpret_cast<const float4*>(sQ + row * LD + c), x[u]);
+    }
+    acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  kr = row_sum8(kr);
+  qr = row_sum8(qr);
+  float den = 0.f;
+  for (int kt = 0; kt < kend; kt += VK) {
+    __syncthreads();
+    stage_rows<D, LD>(sK, K, kt, VK, kend);
+    stage_rows<D, LD>(sV, V, kt, VK, kend);
+    __syncthreads();
+    for (int u = 0; u < 2; ++u) {
+      const int kc = l8 + 8 * u;
+      const int j = kt + kc;
+      float ds = 0.f, dr = 0.f;
+      for (int c = 0; c < D; c += 4) {
+        const float4 kv = *reinterpret_cast<const float4*>(sK + kc * LD + c);
+        ds += dot4(*reinterpret_cast<const float4*>(sQ + row * LD + c), kv);
+        dr += dot4(*reinterpret_cast<const float4*>(sP + row * LD + c), kv);
+      }
+      float a = 0.f;
+      if (valid && j <= qi) a = exp2f(ds * sc2 - m2) * (1.f - (dr - kr));
+      sW[row * (VK + 1) + kc] = a;
+      den += a;
+    }
+    __syncthreads();
+    for (int u = 0; u < YC; ++u) {
+      const int c = (l8 + 8 * u) * 4;
+      if (c < D) {
+        float4 o = acc[u];
+        for (int kk = 0; kk < VK; ++kk)
+          o = fma4(sW[row * (VK + 1) + kk], *reinterpret_cast<const float4*>(sV + kk * LD + c), o);
+        acc[u] = o;
+      }
+    }
+  }
+  den = row_sum8(den);
+  if (!valid) return;
+  const size_t orow = static_cast<size_t>(bh) * P.n + qi;
+  const float inv_den = 1.f / den;
+  // the pages' rho_i = Sigma_i^{-1} mu_i = rho_c / (1 + (kbar - q) . rho_c)
+  const float rs = 1.f / (1.f + (kr - qr));
+  for (int u = 0; u < YC; ++u) {
+    const int c = (l8 + 8 * u) * 4;
+    if (c < D) {
+      const float4 o = acc[u];
+      *reinterpret_cast<float4*>(P.out + orow * D + c) =
+          make_float4(o.x * inv_den, o.y * inv_den, o.z * inv_den, o.w * inv_den);
+      if (P.rho)
+        *reinterpret_cast<float4*>(P.rho + orow * D + c) =
+            make_float4(x[u].x * rs, x[u].y * rs, x[u].z * rs, x[u].w * rs);
+    }
+  }
+  if (l8 == 0) {
+    if (P.omega) P.omega[orow] = om;
+    if (P.rowmax) P.rowmax[orow] = m2 * kLn2;
+    if (P.cg_iters) P.cg_iters[orow] = iters;
+    if (P.cg_resid) P.cg_resid[orow] = r0 > 0.f ? sqrtf(rr) / r0 : 0.f;
+  }
+}
+
+template <int D, typename Tin>
+hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
+  const int nqb = (p.n + VQ - 1) / VQ;
+  const long long blocks = static_cast<long long>(nqb) * p.BH;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (p.ev_main_begin) {
+    const hipError_t e = hipEventRecord(p.ev_main_begin, stream);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((lla_valu_kernel<D, Tin>), dim3(static_cast<unsigned>(blocks)), dim3(VT), 0,
+                     stream, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.ev_main_end) return hipEventRecord(p.ev_main_end, stream);
+  return hipSuccess;
+}
+
+template <typename Tin>
+hipError_t launch_t(const FwdParams& p, hipStream_t stream) {
+  switch (p.d) {
+    case 16: return launch_d<16, Tin>(p, stream);
+    case 32: return launch_d<32, Tin>(p, stream);
+    case 64: return launch_d<64, Tin>(p, stream);
+    case 128: return launch_d<128, Tin>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_valu(const FwdParams& p, hipStream_t stream) {
+  if (p.dtype == LLA_DTYPE_F32) return launch_t<float>(p, stream);
+  return launch_t<uint16_t>(p, stream);
+}
+
+}  // namespace lla

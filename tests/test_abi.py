@@ -1,0 +1,160 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects invalid arguments before any device work (these
+calls never reach a kernel, so they run without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from tests._support import ensure_built, ROOT
+from local_linear_attention_flashlla_amd import _lib
+
+HEADER = os.path.join(ROOT, "include", "lla.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ensure_built()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lla_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_symbols():
+    assert _declared_functions() == sorted(_lib.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_matches_header(lib):
+    m = re.search(r"#define LLA_VERSION (\d+)", open(HEADER).read())
+    assert lib.lla_version() == int(m.group(1))
+
+
+def test_status_strings(lib):
+    assert _lib.status_string(0) == "LLA_OK"
+    assert _lib.status_string(-1) == "LLA_ERR_INVALID_ARG"
+    assert _lib.status_string(-2) == "LLA_ERR_UNSUPPORTED"
+    assert _lib.status_string(-3) == "LLA_ERR_HIP"
+    assert _lib.status_string(-4) == "LLA_ERR_WORKSPACE"
+    assert _lib.status_string(7) == "LLA_ERR_UNKNOWN"
+
+
+def test_struct_layout_matches_header():
+    # 4 ints/ptrs ... the struct must be what the C compiler lays out; check
+    # offsets of a few fields that follow padding.
+    A = _lib.LlaFwdArgs
+    assert A.q.offset == 8 and A.out.offset == 32 and A.B.offset == 40
+    assert A.omega.offset == 72 and A.workspace_bytes.offset == 120 and A.kernel.offset == 128
+    assert A.ev_main_end.offset == 144 and ctypes.sizeof(A) == 152
+
+
+# Fake, well-aligned device addresses: validation only does pointer arithmetic.
+BASE = 0x7F0000000000
+GAP = 1 << 32
+
+
+def _args(**kw):
+    a = _lib.LlaFwdArgs()
+    a.dtype = kw.get("dtype", _lib.LLA_DTYPE_BF16)
+    a.q, a.k, a.v, a.out = BASE, BASE + GAP, BASE + 2 * GAP, BASE + 3 * GAP
+    a.B, a.H, a.n, a.d = 2, 3, 100, 64
+    a.lambda_ = 1.0
+    a.cg_max_iters = 8
+    a.cg_rel_tol = 1e-4
+    for key, val in kw.items():
+        setattr(a, key, val)
+    return a
+
+
+def _call(lib, a):
+    return lib.lla_forward_ex(ctypes.byref(a), None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("q", 0, -1), ("k", 0, -1), ("v", 0, -1), ("out", 0, -1),
+    ("B", 0, -1), ("H", -1, -1), ("n", 0, -1),
+    ("d", 48, -2), ("d", 256, -2), ("d", 0, -2),
+    ("lambda_", 0.0, -1), ("lambda_", -1.0, -1), ("lambda_", float("nan"), -1),
+    ("lambda_", float("inf"), -1),
+    ("cg_max_iters", -1, -1), ("cg_max_iters", 100001, -1),
+    ("cg_rel_tol", -1e-3, -1), ("cg_rel_tol", float("nan"), -1), ("cg_rel_tol", float("inf"), -1),
+    ("dtype", 7, -1), ("kernel", 9, -1), ("flags", 8, -1),
+    ("q", BASE + 8, -1),                 # misaligned
+    ("out", BASE + GAP + 64, -1),        # overlaps k
+    ("rho", BASE + 3 * GAP + 4096, -1),  # overlaps out
+    ("omega", BASE + 4 * GAP + 4, -1),   # misaligned optional output
+])
+def test_invalid_arguments_are_rejected_on_the_host(lib, field, value, status):
+    a = _args(**{field: value})
+    assert _call(lib, a) == status
+    assert _lib.last_error() != ""
+
+
+def test_null_args_pointer(lib):
+    assert lib.lla_forward_ex(None, None) == -1
+
+
+def test_mfma_kernel_needs_bf16(lib):
+    a = _args(dtype=_lib.LLA_DTYPE_F32, kernel=_lib.LLA_KERNEL_MFMA)
+    assert _call(lib, a) == -2
+
+
+def test_too_small_workspace_is_reported(lib):
+    need = lib.lla_workspace_bytes(2, 3, 100, 64, _lib.LLA_DTYPE_BF16, _lib.LLA_KERNEL_MFMA)
+    if need == 0:
+        pytest.skip("MFMA kernel not available in this build")
+    a = _args(kernel=_lib.LLA_KERNEL_MFMA, workspace=BASE + 5 * GAP, workspace_bytes=need - 16)
+    assert _call(lib, a) == -4
+
+
+def test_workspace_sizes(lib):
+    # the VALU kernel keeps its state on chip
+    assert lib.lla_workspace_bytes(1, 1, 256, 16, _lib.LLA_DTYPE_F32, _lib.LLA_KERNEL_VALU) == 0
+    assert lib.lla_workspace_bytes(0, 1, 256, 16, _lib.LLA_DTYPE_F32, 0) == 0
+    assert lib.lla_workspace_bytes(1, 1, 256, 48, _lib.LLA_DTYPE_F32, 0) == 0
+    # when the MFMA kernel is present its workspace grows linearly in n
+    sizes = [lib.lla_workspace_bytes(1, 16, n, 128, _lib.LLA_DTYPE_BF16, _lib.LLA_KERNEL_MFMA)
+             for n in (1024, 2048, 4096, 8192, 16384)]
+    if sizes[0] == 0:
+        pytest.skip("MFMA kernel not available in this build")
+    diffs = [b - a for a, b in zip(sizes, sizes[1:])]
+    # linear: doubling n adds twice the previous increment
+    assert diffs[1] == 2 * diffs[0] and diffs[2] == 2 * diffs[1] and diffs[3] == 2 * diffs[2]
+
+
+def test_rejected_call_leaves_no_stale_error_after_success_path(lib):
+    a = _args(B=0)
+    assert _call(lib, a) == -1
+    assert "B, H, n" in _lib.last_error()
+
+
+def test_struct_layout_matches_c_compiler(tmp_path):
+    """Compile a tiny C program against include/lla.h with the host compiler
+    and compare offsetof() of every field with the ctypes mirror."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    fields = [f[0] for f in _lib.LlaFwdArgs._fields_]
+    cfields = ["lambda" if f == "lambda_" else f for f in fields]
+    src = tmp_path / "layout.c"
+    body = "\n".join(f'  printf("%zu\\n", offsetof(lla_fwd_args, {f}));' for f in cfields)
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "lla.h"\nint main(void){\n'
+                   + body + '\n  printf("%zu\\n", sizeof(lla_fwd_args));\n  return 0;\n}\n')
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                    "-I", "/opt/rocm/include", str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True,
+                                          text=True).stdout.split()]
+    want = [getattr(_lib.LlaFwdArgs, f).offset for f in fields] + [ctypes.sizeof(_lib.LlaFwdArgs)]
+    assert got == want
