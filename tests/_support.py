@@ -63,3 +63,44 @@ def oracle_rows(wl, heads_rows, solver="cholesky", T=0, tol=0.0, lam=None, worke
         return [_oracle_job(j) for j in jobs]
     with ProcessPoolExecutor(max_workers=workers) as ex:
         return list(ex.map(_oracle_job, jobs))
+
+
+def check_parity(wl, out, heads_rows, tol, T=None, cg_tol=None, lam=None, label="",
+                 factor=3.0):
+    """Compare GPU rows with the float64 oracle.
+
+    e_gpu = row error of the GPU output against the exact (Cholesky) oracle;
+    e_cg  = row error of the oracle's own float64 CG run (same system, same
+            iteration cap and stop rule) against the same exact answer.
+    Every row must satisfy e_gpu <= tol + factor * e_cg: where the configured
+    CG budget converges (e_cg ~ 0) this is the plain tolerance; where it does
+    not even in float64, the GPU may not be more than `factor` times further
+    from the exact answer than float64 arithmetic running the same algorithm.
+    Returns a dict of statistics (also printed)."""
+    T = wl.cg_max_iters if T is None else T
+    cg_tol = wl.cg_rel_tol if cg_tol is None else cg_tol
+    exact = oracle_rows(wl, heads_rows, lam=lam)
+    cg = oracle_rows(wl, heads_rows, solver="cg_centred", T=T, tol=cg_tol, lam=lam)
+    e_gpu, e_cg = [], []
+    for ((b, h), rows), ex, c in zip(heads_rows, exact, cg):
+        rows = list(rows)
+        e_gpu.append(row_errors(out[b, h, rows], ex["b"]))
+        e_cg.append(row_errors(c["b"], ex["b"]))
+    e_gpu = np.concatenate(e_gpu)
+    e_cg = np.concatenate(e_cg)
+    bound = tol + factor * e_cg
+    strict = e_gpu <= tol
+    stats = {
+        "rows": int(e_gpu.size), "max": float(e_gpu.max()), "p50": float(np.median(e_gpu)),
+        "p99": float(np.quantile(e_gpu, 0.99)), "strict_pass_frac": float(strict.mean()),
+        "cg64_max": float(e_cg.max()), "cg64_trunc_rows": int((e_cg > tol / 2).sum()),
+        "worst_over_bound": float((e_gpu / bound).max()),
+    }
+    print(f"[parity] {label} rows={stats['rows']} max={stats['max']:.3e} p50={stats['p50']:.2e} "
+          f"p99={stats['p99']:.2e} strict<={tol}: {stats['strict_pass_frac']*100:.2f}% | "
+          f"float64-CG vs exact: max={stats['cg64_max']:.2e}, truncated rows={stats['cg64_trunc_rows']} "
+          f"| worst e_gpu/(tol+{factor}e_cg)={stats['worst_over_bound']:.2f}", flush=True)
+    assert np.all(e_gpu <= bound), (
+        f"{label}: {int((e_gpu > bound).sum())} rows exceed tol + {factor} x float64-CG error; "
+        f"worst ratio {stats['worst_over_bound']:.2f}")
+    return stats
