@@ -89,7 +89,10 @@ def test_optional_outputs(torch):
         b, h = bh
         np.testing.assert_allclose(res["omega"][b, h], x["omega"], rtol=2e-3)
         np.testing.assert_allclose(res["rowmax"][b, h], x["m"], rtol=0, atol=1e-4)
-        assert np.all(res["cg_iters"][b, h] == wl.cg_max_iters)  # tol 0: fixed count
+        # tol 0 runs the full count except where the residual is exactly zero or
+        # the step breaks down (row 0, whose system is lambda I, is one such row)
+        it = res["cg_iters"][b, h]
+        assert it.max() <= wl.cg_max_iters and np.mean(it[1:] == wl.cg_max_iters) > 0.99
         rho_err = row_errors(res["rho"][b, h], x["rho"])
         print(f"[rho] head {h} max rel {rho_err.max():.2e} p50 {np.median(rho_err):.2e}", flush=True)
         # rho itself is the ill-conditioned quantity; compare loosely with the
@@ -99,17 +102,35 @@ def test_optional_outputs(torch):
     assert np.all(res["cg_resid"] >= 0)
 
 
+# The recall workload (lambda = 1e-3 against unit-scale keys) is ill-conditioned
+# by construction; its CG tile needs the two-term fp16 U (LLA_FLAG_SPLIT_U).
+# The other workloads run with the default single fp16 U.
+FLAGS = {"standard": 0, "long": 0, "recall": lla.LLA_FLAG_SPLIT_U}
+
+
 @pytest.mark.parametrize("name", ["standard", "long", "recall"])
 def test_small_recipes(torch, name):
     wl = make_workload(name, B=1, H=2, n=300)
-    a = run(torch, wl)
+    a = run(torch, wl, flags=FLAGS[name])
     check_parity(wl, a["out"], all_rows(wl), BF16_TOL, label=f"mfma {name}-300")
 
 
-def test_split_u_flag(torch):
-    wl = make_workload("recall", B=1, H=2, n=300)
+def test_split_u_on_well_conditioned_workload(torch):
+    wl = make_workload("standard", B=1, H=2, n=300)
     a = run(torch, wl, flags=lla.LLA_FLAG_SPLIT_U)
-    check_parity(wl, a["out"], all_rows(wl), BF16_TOL, label="mfma split-U recall-300")
+    check_parity(wl, a["out"], all_rows(wl), BF16_TOL, label="mfma split-U standard-300")
+
+
+@pytest.mark.parametrize("name,T,tol", [("recall", 400, 1e-7), ("standard", 64, 0.0)])
+def test_converging_budget_matches_exact_answer(torch, name, T, tol):
+    """With a CG budget under which float64 CG reaches the exact answer on every
+    row, the kernel must match the exact (Cholesky) oracle on every row: the
+    arithmetic is not what limits parity at the configured budgets."""
+    wl = make_workload(name, B=1, H=2, n=300)
+    res = run(torch, wl, T=T, tol=tol, flags=FLAGS[name])
+    st = check_parity(wl, res["out"], all_rows(wl), BF16_TOL, T=T, cg_tol=tol,
+                      label=f"mfma {name}-300 T={T}")
+    assert st["truncation_rows"] == 0 and st["max"] <= BF16_TOL
 
 
 def test_deterministic(torch):
@@ -143,7 +164,7 @@ FULL = {"standard": [(0, 0), (1, 3), (3, 7)],
 @pytest.mark.parametrize("name", ["standard", "long", "recall"])
 def test_full_size_sampled_rows(torch, name):
     wl = make_workload(name)
-    res = run(torch, wl, extras=True)
+    res = run(torch, wl, extras=True, flags=FLAGS[name])
     heads_rows = [((b, h), O.sample_rows(wl.n, seed=17 * b + h)) for b, h in FULL[name]]
     stats = check_parity(wl, res["out"], heads_rows, BF16_TOL, label=f"full {name}")
     it = res["cg_iters"]

@@ -128,6 +128,14 @@ def test_large_lambda_is_softmax(torch):
     assert e.max() < 1e-4
 
 
+def test_converging_budget_recall(torch):
+    wl = make_workload("recall", B=1, H=2, n=300)
+    res = run(torch, wl, T=400, tol=1e-7)
+    st = check_parity(wl, res["out"], all_rows(wl), BF16_TOL, T=400, cg_tol=1e-7,
+                      label="valu recall-300 T=400")
+    assert st["truncation_rows"] == 0 and st["max"] <= BF16_TOL
+
+
 def test_deterministic(torch):
     wl = make_workload("piecewise")
     a = run(torch, wl)["out"]
