@@ -98,6 +98,9 @@ def main(argv=None):
                     help="rows in the CPU-oracle sample (0 = skip)")
     ap.add_argument("--traffic", default=None,
                     help="JSON file with measured HBM bytes per launch of the main kernel")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB (a "
+                         "reference kernel of known traffic for hardware byte counters)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -170,6 +173,15 @@ def main(argv=None):
     if args.traffic and os.path.exists(args.traffic):
         with open(args.traffic) as f:
             traffic = json.load(f).get("bytes_per_launch")
+
+    if args.calib_copy_mb > 0:
+        nbytes = args.calib_copy_mb << 20
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if args.cpu_rows > 0:

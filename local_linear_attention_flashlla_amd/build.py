@@ -25,6 +25,10 @@ HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",
     # keep the compiler from emitting packed fp32 VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in the architectural VGPR file: the CG state
+    # that the vector ALU reads between key sweeps then never has to be copied
+    # between the accumulation and architectural register files in the loop
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
 ]
 

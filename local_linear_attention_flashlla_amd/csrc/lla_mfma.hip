@@ -42,6 +42,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <type_traits>
+
 #include "lla_internal.h"
 #include "../../include/lla.h"
 
@@ -91,6 +93,20 @@ __device__ __forceinline__ floatx16 mfma(half8 a, half8 b, floatx16 c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// round two floats to fp16 (nearest even) and add their rounded values to acc
+// with one packed dot product against (1, 1): acc + h0 + h1 exactly in fp32
+__device__ __forceinline__ half2v pack_sum(float a, float b, float& acc) {
+  half2v h;
+  h[0] = static_cast<_Float16>(a);
+  h[1] = static_cast<_Float16>(b);
+  const half2v one = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
+  acc = __builtin_amdgcn_fdot2(h, one, acc, false);
+  return h;
+}
+
 __device__ __forceinline__ float pair_sum(float v) { return v + __shfl_xor(v, 32); }
 __device__ __forceinline__ float pair_max(float v) { return fmaxf(v, __shfl_xor(v, 32)); }
 
@@ -99,6 +115,8 @@ struct Workspace {
   _Float16* kr;     // [BH][npad][D]      s k, d index permuted by swz16
   _Float16* kt;     // [BH][npad/32][D][32] s k transposed, key index permuted
   _Float16* vt;     // [BH][npad/32][D][32] sv v transposed, key index permuted
+  float* xs;        // CG iterates: per workgroup BQ x D fp32, lane-contiguous
+  float* kbs;       // fp32 kbar, same layout
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -116,6 +134,12 @@ Workspace carve(void* base, int BH, int n, int d) {
   w.kt = reinterpret_cast<_Float16*>(p);
   p += t;
   w.vt = reinterpret_cast<_Float16*>(p);
+  p += t;
+  const size_t nqb = static_cast<size_t>((n + BQ - 1) / BQ);
+  const size_t sl = align256(static_cast<size_t>(BH) * nqb * BQ * d * sizeof(float));
+  w.xs = reinterpret_cast<float*>(p);
+  p += sl;
+  w.kbs = reinterpret_cast<float*>(p);
   return w;
 }
 
@@ -245,61 +269,85 @@ struct MainParams {
   const _Float16* kr;
   const _Float16* kt;
   const _Float16* vt;
+  float* xs;         // CG iterate slab, [blocks][4 waves][d/8 float4 chunks][64 lanes]
+  float* kbs;        // fp32 kbar slab, same layout
   int BH, n, nchunk, nblk;
   float lambda;
   int cg_max_iters;
   float cg_rel_tol;
 };
 
+// LDS tiles. The K-row tile holds BK rows of D fp16 (the d index already
+// permuted by swz16 within 16-element chunks); the transposed tile holds D
+// rows of BK fp16 keys. Neither is padded: the 16-byte chunk c of a row sits
+// at chunk position c ^ chunk_xor(row) instead, which spreads the rows that one
+// 16-lane group reads in the same operand step over distinct LDS banks.
 template <int D>
-struct TileLoader {
-  static constexpr int KRS = D + 8;        // LDS row stride of the K-row tile (halves)
-  static constexpr int KTS = BK + 8;       // LDS row stride of the transposed tiles (halves)
-  static constexpr int NR = BK * D / 8 / NT;  // 16-byte chunks per thread, row tile
-  static constexpr int NTR = D * BK / 8 / NT; // 16-byte chunks per thread, transposed tile
-  u32x4 r[NR];
-  u32x4 t[NTR];
+__device__ __forceinline__ int kr_chunk_xor(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+__device__ __forceinline__ int kt_chunk_xor(int row) { return (row >> 2) & 3; }
 
-  __device__ __forceinline__ void load(const _Float16* kr_head, const _Float16* t_head, int kt) {
-    const int tid = threadIdx.x;
-    #pragma unroll
-    for (int u = 0; u < NR; ++u) {
-      const int e = tid + NT * u;
-      const int row = e / (D / 8), c8 = e % (D / 8);
-      r[u] = *reinterpret_cast<const u32x4*>(kr_head + (static_cast<size_t>(kt) * BK + row) * D + c8 * 8);
-    }
-    #pragma unroll
-    for (int u = 0; u < NTR; ++u) {
-      const int e = tid + NT * u;
-      t[u] = *reinterpret_cast<const u32x4*>(t_head + static_cast<size_t>(kt) * D * BK + e * 8);
-    }
+// Copy key tile `kt` of this head straight from global memory into the LDS
+// tiles (global_load_lds: each wave instruction fills 1 KiB of LDS, lane l
+// its l-th 16 bytes; the source address of each lane applies the chunk
+// permutation). Completion is awaited by the next __syncthreads().
+template <int D>
+__device__ __forceinline__ void load_tile_to_lds(const _Float16* kr_head, const _Float16* t_head,
+                                                 int kt, _Float16* sKr, _Float16* sKt, int wave,
+                                                 int lane) {
+  constexpr int CPR = D / 8;          // 16-byte chunks per K row
+  constexpr int RPI = 64 / CPR;       // K rows per wave instruction
+  constexpr int NI = D / 64;          // instructions per wave for each tile
+  #pragma unroll
+  for (int u = 0; u < NI; ++u) {
+    const int inst = wave * NI + u;
+    const int row = inst * RPI + lane / CPR;
+    const int c = (lane % CPR) ^ kr_chunk_xor<D>(row);
+    const _Float16* src = kr_head + (static_cast<size_t>(kt) * BK + row) * D + c * 8;
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void*)(src),
+        (__attribute__((address_space(3))) void*)(sKr + inst * 512), 16, 0, 0);
   }
-  __device__ __forceinline__ void store(_Float16* sKr, _Float16* sKt) const {
-    const int tid = threadIdx.x;
-    #pragma unroll
-    for (int u = 0; u < NR; ++u) {
-      const int e = tid + NT * u;
-      const int row = e / (D / 8), c8 = e % (D / 8);
-      *reinterpret_cast<u32x4*>(sKr + row * KRS + c8 * 8) = r[u];
-    }
-    #pragma unroll
-    for (int u = 0; u < NTR; ++u) {
-      const int e = tid + NT * u;
-      const int row = e / (BK / 8), c = e % (BK / 8);
-      *reinterpret_cast<u32x4*>(sKt + row * KTS + c * 8) = t[u];
-    }
+  #pragma unroll
+  for (int u = 0; u < NI; ++u) {
+    const int inst = wave * NI + u;
+    const int row = inst * 16 + lane / 4;
+    const int c = (lane % 4) ^ kt_chunk_xor(row);
+    const _Float16* src = t_head + static_cast<size_t>(kt) * D * BK + row * BK + c * 8;
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void*)(src),
+        (__attribute__((address_space(3))) void*)(sKt + inst * 512), 16, 0, 0);
   }
-};
+}
+
+// Work order. Workgroups are handed to the eight XCDs (each with its own L2)
+// in turn: block b runs on XCD b % 8. When the head count divides by 8, each
+// XCD gets its own heads and walks them one after the other, every head's
+// query blocks longest causal prefix first, so the key tiles that an XCD's
+// workgroups stream are those of about one head at a time and stay in its L2.
+// Otherwise the order is longest prefix first across all heads.
+constexpr int kXcds = 8;
+__device__ __forceinline__ void block_coords(int b, int BH, int nqb, int* qb, int* bh) {
+  if (BH % kXcds == 0) {
+    const int xcd = b % kXcds, j = b / kXcds;
+    const int heads_per_xcd = BH / kXcds;
+    *bh = xcd * heads_per_xcd + j / nqb;
+    *qb = nqb - 1 - j % nqb;
+  } else {
+    *qb = nqb - 1 - b / BH;
+    *bh = b % BH;
+  }
+}
 
 template <int D, bool SPLIT_U>
 __global__ __launch_bounds__(NT) void lla_mfma_main(MainParams P) {
   constexpr int NKS = D / 16;  // k-steps over d
   constexpr int NMB = D / 32;  // 32-row blocks over d
-  using TL = TileLoader<D>;
-  constexpr int KRS = TL::KRS, KTS = TL::KTS;
-  __shared__ __align__(16) _Float16 sKr[2][BK * KRS];
-  __shared__ __align__(16) _Float16 sKt[2][D * KTS];
-  __shared__ __align__(16) floatx4 sKb[NT / 64][NMB * 4][64];
+  __shared__ __align__(16) _Float16 sKr[2][BK * D];
+  __shared__ __align__(16) _Float16 sKt[2][D * BK];
+  __shared__ __align__(16) half8 sKb[NT / 64][NKS][64];     // kbar, fp16, operand order
+  __shared__ __align__(16) floatx4 sR[NT / 64][NMB * 4][64];  // CG residual r, fp32
   __shared__ float sScale[2];
 
   const int tid = threadIdx.x;
@@ -307,8 +355,8 @@ __global__ __launch_bounds__(NT) void lla_mfma_main(MainParams P) {
   const int ql = lane & 31, g = lane >> 5;
   const int n = P.n;
   const int nqb = (n + BQ - 1) / BQ;
-  const int qb = nqb - 1 - static_cast<int>(blockIdx.x) / P.BH;  // longest prefix first
-  const int bh = static_cast<int>(blockIdx.x) % P.BH;
+  int qb, bh;
+  block_coords(static_cast<int>(blockIdx.x), P.BH, nqb, &qb, &bh);
   const int i0 = qb * BQ;
   const int kend = min(n, i0 + BQ);
   const int ntiles = (kend + BK - 1) / BK;
@@ -352,17 +400,23 @@ __global__ __launch_bounds__(NT) void lla_mfma_main(MainParams P) {
   // The key sweep: tiles 0 .. ntiles-1 of this head, double-buffered through
   // LDS; `tile(kt, buf)` runs on the waves whose queries see tile kt.
   auto sweep = [&](const _Float16* t_head, auto&& tile, bool wave_busy) __attribute__((always_inline)) {
-    TL ld;
-    ld.load(kr_head, t_head, 0);
-    ld.store(sKr[0], sKt[0]);
+    load_tile_to_lds<D>(kr_head, t_head, 0, sKr[0], sKt[0], wave, lane);
     __syncthreads();
     for (int kt = 0; kt < ntiles; ++kt) {
       const int buf = kt & 1;
-      if (kt + 1 < ntiles) ld.load(kr_head, t_head, kt + 1);
+      if (kt + 1 < ntiles) load_tile_to_lds<D>(kr_head, t_head, kt + 1, sKr[buf ^ 1], sKt[buf ^ 1], wave, lane);
       if (wave_busy && kt <= wlast) tile(kt, buf);
-      if (kt + 1 < ntiles) ld.store(sKr[buf ^ 1], sKt[buf ^ 1]);
       __syncthreads();
     }
+  };
+
+  // this lane's operand fragments in the LDS tiles
+  const int krx = kr_chunk_xor<D>(ql), ktx = kt_chunk_xor(ql);
+  auto kr_frag = [&](int buf, int t) __attribute__((always_inline)) {
+    return *reinterpret_cast<const half8*>(sKr[buf] + ql * D + 8 * ((2 * t + g) ^ krx));
+  };
+  auto kt_frag = [&](int buf, int mb, int h) __attribute__((always_inline)) {
+    return *reinterpret_cast<const half8*>(sKt[buf] + (32 * mb + ql) * BK + 8 * ((2 * h + g) ^ ktx));
   };
 
   // key index (within the tile) of accumulator register r of this lane
@@ -378,73 +432,99 @@ __global__ __launch_bounds__(NT) void lla_mfma_main(MainParams P) {
   float m2 = -INFINITY;  // running row max of the log2-scaled scores
   float om = 0.f;        // partial row sum (this half of the keys)
   sweep(kt_head, [&](int kt, int buf) __attribute__((always_inline)) {
-    floatx16 sacc;
+    half8 kf[NKS], tf[2 * NMB];
     #pragma unroll
-    for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
-    const _Float16* a_row = sKr[buf] + ql * KRS + 8 * g;
-    #pragma unroll
-    for (int t = 0; t < NKS; ++t)
-      sacc = mfma(*reinterpret_cast<const half8*>(a_row + 16 * t), qop[t], sacc);
-    const bool full = wave_full && kt < wlast;
-    float sc[16];
-    float tmax = -INFINITY;
-    #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float x = sacc[r] * c2s;
-      if (!full && kt * BK + key_of(r) > kmax) x = -INFINITY;
-      sc[r] = x;
-      tmax = fmaxf(tmax, x);
-    }
-    tmax = pair_max(tmax);
-    const float mnew = fmaxf(m2, tmax);
-    const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(m2 - mnew);
-    half8 wb[2];
-    float wsum = 0.f;
-    #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float w = (sc[r] == -INFINITY) ? 0.f : fast_exp2(sc[r] - mnew);
-      const _Float16 wh = static_cast<_Float16>(w);
-      wb[r >> 3][r & 7] = wh;
-      wsum += static_cast<float>(wh);
-    }
-    om = om * alpha + wsum;
-    m2 = mnew;
-    if (alpha != 1.f)
-      #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb) acc[mb] *= alpha;
-    const _Float16* t_row = sKt[buf] + ql * KTS + 8 * g;
+    for (int t = 0; t < NKS; ++t) kf[t] = kr_frag(buf, t);
     #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
       #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        acc[mb] = mfma(*reinterpret_cast<const half8*>(t_row + 32 * mb * KTS + 16 * h), wb[h], acc[mb]);
+      for (int h = 0; h < 2; ++h) tf[2 * mb + h] = kt_frag(buf, mb, h);
+    floatx16 sacc = mfma(kf[0], qop[0], floatx16{});
+    #pragma unroll
+    for (int t = 1; t < NKS; ++t) sacc = mfma(kf[t], qop[t], sacc);
+    const int lim = kmax - kt * BK;  // keys <= lim are visible
+    half8 wb[2];
+    auto body = [&](auto masked) __attribute__((always_inline)) {
+      float sc[16];
+      float tmax = -INFINITY;
+      #pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = sacc[r] * c2s;
+        if constexpr (decltype(masked)::value) {
+          if (key_of(r) > lim) x = -INFINITY;
+        }
+        sc[r] = x;
+        tmax = fmaxf(tmax, x);
+      }
+      tmax = pair_max(tmax);
+      const float mnew = fmaxf(m2, tmax);
+      // a query with every key so far masked (only queries past the end) keeps
+      // its running max at -inf; then nothing is accumulated for it
+      const float mref = (mnew == -INFINITY) ? 0.f : mnew;
+      const float alpha = fast_exp2(m2 - mref);
+      float wsum = 0.f;
+      #pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const half2v hw = pack_sum(fast_exp2(sc[r] - mref), fast_exp2(sc[r + 1] - mref), wsum);
+        wb[r >> 3][r & 7] = hw[0];
+        wb[r >> 3][(r & 7) + 1] = hw[1];
+      }
+      om = om * alpha + wsum;
+      m2 = mnew;
+      if (alpha != 1.f)
+        #pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) acc[mb] *= alpha;
+    };
+    if (wave_full && kt < wlast)
+      body(std::false_type{});
+    else
+      body(std::true_type{});
+    #pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+      #pragma unroll
+      for (int h = 0; h < 2; ++h) acc[mb] = mfma(tf[2 * mb + h], wb[h], acc[mb]);
   }, wave_any);
   om = pair_sum(om);
   if (!qvalid) m2 = 0.f;
 
   // --------------------------- CG set-up -------------------------------
-  // kbar = mu~ / omega (kept in LDS), r0 = mu = mu~ - omega q, x0 = 0.
-  float xr[NMB][16], rv[NMB][16];
+  // Per query: kbar = mu~ / omega, r0 = mu = mu~ - omega q, x0 = 0. Nothing
+  // large stays in registers across a key sweep: r lives in LDS (fp32), x and
+  // the fp32 kbar in lane-contiguous workspace slabs, and the CG matvec uses
+  // kbar rounded to fp16 from LDS as its expansion point. The matvec is exact
+  // for any expansion point c used consistently in U = w (K d - c.d) and in
+  // the correction -(sum U) c (the shift of c.d cancels through sum U), so
+  // rounding kbar only moves the centre: Sigma_c becomes
+  // Sigma_c + omega (kbar - c)(kbar - c)^T, a rank-one change of relative size
+  // 2^-24. Phase 3 uses the fp32 kbar.
+  const size_t slab = (static_cast<size_t>(blockIdx.x) * (NT / 64) + wave) * (NMB * 4 * 64);
+  floatx4* xs = reinterpret_cast<floatx4*>(P.xs) + slab;
+  floatx4* kbs = reinterpret_cast<floatx4*>(P.kbs) + slab;
   float rr = 0.f;
   {
     const float inv_om = qvalid ? 1.f / om : 0.f;
+    half8 kb16[NKS];
     #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
       #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        floatx4 kb;
+        floatx4 kb, rc;
         #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const int r = 4 * a + b;
           const float mt = acc[mb][r];
           const float qv = static_cast<float>(qop[2 * mb + (r >> 3)][r & 7]);
           kb[b] = mt * inv_om;
-          rv[mb][r] = qvalid ? mt - om * qv : 0.f;
-          xr[mb][r] = 0.f;
-          rr += rv[mb][r] * rv[mb][r];
+          kb16[2 * mb + (r >> 3)][r & 7] = static_cast<_Float16>(kb[b]);
+          rc[b] = qvalid ? mt - om * qv : 0.f;
+          rr += rc[b] * rc[b];
         }
-        sKb[wave][mb * 4 + a][lane] = kb;
+        kbs[(mb * 4 + a) * 64 + lane] = kb;
+        xs[(mb * 4 + a) * 64 + lane] = floatx4{0.f, 0.f, 0.f, 0.f};
+        sR[wave][mb * 4 + a][lane] = rc;
       }
+    #pragma unroll
+    for (int t = 0; t < NKS; ++t) sKb[wave][t][lane] = kb16[t];
   }
   rr = pair_sum(rr);
   const float r0n = sqrtf(rr);
@@ -452,38 +532,42 @@ __global__ __launch_bounds__(NT) void lla_mfma_main(MainParams P) {
   bool active = qvalid && rr > 0.f && P.cg_max_iters > 0;
   int iters = 0;
 
+  // fp16 kbar . op for an operand-ordered fp16 vector
+  auto kbar_dot = [&](const half8 (&op)[NKS]) __attribute__((always_inline)) {
+    float acc_ = 0.f;
+    #pragma unroll
+    for (int t = 0; t < NKS; ++t) {
+      const half8 kb = sKb[wave][t][lane];
+      #pragma unroll
+      for (int c = 0; c < 8; ++c) acc_ += static_cast<float>(kb[c]) * static_cast<float>(op[t][c]);
+    }
+    return pair_sum(acc_);
+  };
+
   // direction d = fp16(p / sp), sp a power of two with |p / sp| <= 1
   half8 dop[NKS];
   float sp = 1.f;
-  auto set_direction = [&](const float (&p)[NMB][16]) {
+  {
+    float rv[NMB][16];
     float mx = 0.f;
     #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
       #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fabsf(p[mb][r]));
+      for (int a = 0; a < 4; ++a) {
+        const floatx4 rc = sR[wave][mb * 4 + a][lane];
+        #pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          rv[mb][4 * a + b] = rc[b];
+          mx = fmaxf(mx, fabsf(rc[b]));
+        }
+      }
     sp = pow2_ceil(pair_max(mx));
     const float inv = 1.f / sp;
     #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
       #pragma unroll
-      for (int r = 0; r < 16; ++r) dop[2 * mb + (r >> 3)][r & 7] = static_cast<_Float16>(p[mb][r] * inv);
-  };
-  auto kbar_dot = [&](const half8 (&op)[NKS]) {
-    float acc_ = 0.f;
-    #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
-      #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const floatx4 kb = sKb[wave][mb * 4 + a][lane];
-        #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int r = 4 * a + b;
-          acc_ += kb[b] * static_cast<float>(op[2 * mb + (r >> 3)][r & 7]);
-        }
-      }
-    return pair_sum(acc_);
-  };
-  set_direction(rv);
+      for (int r = 0; r < 16; ++r) dop[2 * mb + (r >> 3)][r & 7] = static_cast<_Float16>(rv[mb][r] * inv);
+  }
   float kbd = kbar_dot(dop);
 
   // ------------------------------ phase 2 ------------------------------
@@ -495,61 +579,91 @@ __global__ __launch_bounds__(NT) void lla_mfma_main(MainParams P) {
       #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
     float usum = 0.f;
+    floatx16 tinit;
+    #pragma unroll
+    for (int r = 0; r < 16; ++r) tinit[r] = -kbd;
     sweep(kt_head, [&](int kt, int buf) __attribute__((always_inline)) {
-      floatx16 sacc, tacc;
+      half8 kf[NKS], tf[2 * NMB];
       #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[r] = tacc[r] = 0.f;
-      const _Float16* a_row = sKr[buf] + ql * KRS + 8 * g;
+      for (int t = 0; t < NKS; ++t) kf[t] = kr_frag(buf, t);
       #pragma unroll
-      for (int t = 0; t < NKS; ++t) {
-        const half8 a = *reinterpret_cast<const half8*>(a_row + 16 * t);
-        sacc = mfma(a, qop[t], sacc);
-        tacc = mfma(a, dop[t], tacc);
+      for (int mb = 0; mb < NMB; ++mb)
+        #pragma unroll
+        for (int h = 0; h < 2; ++h) tf[2 * mb + h] = kt_frag(buf, mb, h);
+      // S = K Q^T; T = K d^T - kbar.d (the shift enters as the accumulator's
+      // initial value, so U = w T needs one multiply per element)
+      floatx16 sacc = mfma(kf[0], qop[0], floatx16{});
+      floatx16 tacc = mfma(kf[0], dop[0], tinit);
+      #pragma unroll
+      for (int t = 1; t < NKS; ++t) {
+        sacc = mfma(kf[t], qop[t], sacc);
+        tacc = mfma(kf[t], dop[t], tacc);
       }
-      const bool full = wave_full && kt < wlast;
       half8 ub[2], ul[2];
-      #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float w = fast_exp2(sacc[r] * c2s - m2);
-        if (!full && kt * BK + key_of(r) > kmax) w = 0.f;
-        const float u = w * (tacc[r] - kbd);
-        const _Float16 uh = static_cast<_Float16>(u);
-        ub[r >> 3][r & 7] = uh;
-        usum += static_cast<float>(uh);
-        if constexpr (SPLIT_U) {
-          const _Float16 lo = static_cast<_Float16>(u - static_cast<float>(uh));
-          ul[r >> 3][r & 7] = lo;
-          usum += static_cast<float>(lo);
+      const int lim = kmax - kt * BK;  // keys <= lim are visible
+      auto make_u = [&](auto masked) __attribute__((always_inline)) {
+        #pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          float w0 = fast_exp2(fmaf(sacc[r], c2s, -m2));
+          float w1 = fast_exp2(fmaf(sacc[r + 1], c2s, -m2));
+          if constexpr (decltype(masked)::value) {
+            if (key_of(r) > lim) w0 = 0.f;
+            if (key_of(r + 1) > lim) w1 = 0.f;
+          }
+          const float u0 = w0 * tacc[r], u1 = w1 * tacc[r + 1];
+          const half2v hu = pack_sum(u0, u1, usum);
+          ub[r >> 3][r & 7] = hu[0];
+          ub[r >> 3][(r & 7) + 1] = hu[1];
+          if constexpr (SPLIT_U) {
+            const half2v lo = pack_sum(u0 - static_cast<float>(hu[0]),
+                                       u1 - static_cast<float>(hu[1]), usum);
+            ul[r >> 3][r & 7] = lo[0];
+            ul[r >> 3][(r & 7) + 1] = lo[1];
+          }
         }
-      }
-      const _Float16* t_row = sKt[buf] + ql * KTS + 8 * g;
+      };
+      // the causal mask only bites on the wave's diagonal tile (wave-uniform)
+      if (wave_full && kt < wlast)
+        make_u(std::false_type{});
+      else
+        make_u(std::true_type{});
       #pragma unroll
       for (int mb = 0; mb < NMB; ++mb)
         #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const half8 a = *reinterpret_cast<const half8*>(t_row + 32 * mb * KTS + 16 * h);
-          acc[mb] = mfma(a, ub[h], acc[mb]);
-          if constexpr (SPLIT_U) acc[mb] = mfma(a, ul[h], acc[mb]);
+          acc[mb] = mfma(tf[2 * mb + h], ub[h], acc[mb]);
+          if constexpr (SPLIT_U) acc[mb] = mfma(tf[2 * mb + h], ul[h], acc[mb]);
         }
     }, wave_busy);
     usum = pair_sum(usum);
-    // Sigma_c d = Y - (sum U) kbar + lambda d; exact line search along d.
+
+    // CG step (registers only in this stretch): Sigma_c d = Y - (sum U) c +
+    // lambda d with c the fp16 kbar; exact line search along d; then the next
+    // direction p = r + beta sp d, renormalised and rounded to fp16.
+    float rv[NMB][16], ad[NMB][16];
     float dAd = 0.f, rd = 0.f;
     #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
+    for (int mb = 0; mb < NMB; ++mb) {
       #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const floatx4 kb = sKb[wave][mb * 4 + a][lane];
+        const floatx4 rc = sR[wave][mb * 4 + a][lane];
         #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int r = 4 * a + b;
-          const float dv = static_cast<float>(dop[2 * mb + (r >> 3)][r & 7]);
-          const float ad = acc[mb][r] - usum * kb[b] + lam_s * dv;
-          acc[mb][r] = ad;
-          dAd += dv * ad;
+        for (int b = 0; b < 4; ++b) rv[mb][4 * a + b] = rc[b];
+      }
+      #pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const half8 kb = sKb[wave][2 * mb + h][lane];
+        #pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const int r = 8 * h + c;
+          const float dv = static_cast<float>(dop[2 * mb + h][c]);
+          const float v = acc[mb][r] - usum * static_cast<float>(kb[c]) + lam_s * dv;
+          ad[mb][r] = v;
+          dAd += dv * v;
           rd += rv[mb][r] * dv;
         }
       }
+    }
     dAd = pair_sum(dAd);
     rd = pair_sum(rd);
     const bool step = active && dAd > 0.f;
@@ -559,22 +673,33 @@ __global__ __launch_bounds__(NT) void lla_mfma_main(MainParams P) {
     for (int mb = 0; mb < NMB; ++mb)
       #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float dv = static_cast<float>(dop[2 * mb + (r >> 3)][r & 7]);
-        if (step) {
-          xr[mb][r] += al * dv;
-          rv[mb][r] -= al * acc[mb][r];
-        }
+        if (step) rv[mb][r] -= al * ad[mb][r];
         rrn += rv[mb][r] * rv[mb][r];
       }
+    if (step) {
+      #pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+        #pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          floatx4 xc = xs[(mb * 4 + a) * 64 + lane];
+          floatx4 rc;
+          #pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const int r = 4 * a + b;
+            xc[b] += al * static_cast<float>(dop[2 * mb + (r >> 3)][r & 7]);
+            rc[b] = rv[mb][r];
+          }
+          xs[(mb * 4 + a) * 64 + lane] = xc;
+          sR[wave][mb * 4 + a][lane] = rc;
+        }
+    }
     rrn = pair_sum(rrn);
     bool cont = false;
     if (step) {
       ++iters;
       cont = !(sqrtf(rrn) <= thr || rrn == 0.f);
     }
-    // next direction p = r + beta p_prev with p_prev = sp d, normalised to a
-    // power of two and rounded to fp16; lanes that stopped keep their state.
-    // The pair exchanges run in every lane.
+    // lanes that stopped keep their state; the pair exchanges run in every lane
     const float be = (step && rr > 0.f) ? rrn / rr * sp : 0.f;
     float mx = 0.f;
     #pragma unroll
@@ -604,13 +729,19 @@ __global__ __launch_bounds__(NT) void lla_mfma_main(MainParams P) {
   half8 rhi[NKS], rlo[NKS];
   float srho, kr_dot, inv_sA;
   {
+    float xv[NMB][16];
     float mx = 0.f, nn = 0.f;
     #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
       #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        mx = fmaxf(mx, fabsf(xr[mb][r]));
-        nn += xr[mb][r] * xr[mb][r];
+      for (int a = 0; a < 4; ++a) {
+        const floatx4 xc = xs[(mb * 4 + a) * 64 + lane];
+        #pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          xv[mb][4 * a + b] = xc[b];
+          mx = fmaxf(mx, fabsf(xc[b]));
+          nn += xc[b] * xc[b];
+        }
       }
     srho = pow2_ceil(pair_max(mx));
     nn = pair_sum(nn);
@@ -619,17 +750,17 @@ __global__ __launch_bounds__(NT) void lla_mfma_main(MainParams P) {
     for (int mb = 0; mb < NMB; ++mb)
       #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float xs = xr[mb][r] * inv;
-        const _Float16 h = static_cast<_Float16>(xs);
+        const float xsc = xv[mb][r] * inv;
+        const _Float16 h = static_cast<_Float16>(xsc);
         rhi[2 * mb + (r >> 3)][r & 7] = h;
-        rlo[2 * mb + (r >> 3)][r & 7] = static_cast<_Float16>(xs - static_cast<float>(h));
+        rlo[2 * mb + (r >> 3)][r & 7] = static_cast<_Float16>(xsc - static_cast<float>(h));
       }
     float kd = 0.f;
     #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
       #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const floatx4 kb = sKb[wave][mb * 4 + a][lane];
+        const floatx4 kb = kbs[(mb * 4 + a) * 64 + lane];
         #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const int r = 4 * a + b;
@@ -641,65 +772,68 @@ __global__ __launch_bounds__(NT) void lla_mfma_main(MainParams P) {
     // |(k - kbar).rho'| <= 2 * 128 * ||rho'||, so a / sA stays within [-1, 1]
     inv_sA = 1.f / pow2_ceil(1.f + 2.f * kRowNormCap * sqrtf(nn));
   }
+  // racc starts at -kbar.rho' / srho (srho is a power of two: exact), so
+  // (k - kbar).rho' = srho racc and a / sA = w (inv_sA - srho inv_sA racc)
+  const float a_slope = -srho * inv_sA;
+  floatx16 rinit;
+  #pragma unroll
+  for (int r = 0; r < 16; ++r) rinit[r] = -kr_dot / srho;
   #pragma unroll
   for (int mb = 0; mb < NMB; ++mb)
     #pragma unroll
     for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
   float den = 0.f;
   sweep(vt_head, [&](int kt, int buf) __attribute__((always_inline)) {
-    floatx16 sacc, racc;
+    half8 kf[NKS], tf[2 * NMB];
     #pragma unroll
-    for (int r = 0; r < 16; ++r) sacc[r] = racc[r] = 0.f;
-    const _Float16* a_row = sKr[buf] + ql * KRS + 8 * g;
-    #pragma unroll
-    for (int t = 0; t < NKS; ++t) {
-      const half8 a = *reinterpret_cast<const half8*>(a_row + 16 * t);
-      sacc = mfma(a, qop[t], sacc);
-      racc = mfma(a, rhi[t], racc);
-      racc = mfma(a, rlo[t], racc);
-    }
-    const bool full = wave_full && kt < wlast;
-    half8 ab[2];
-    #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float w = fast_exp2(sacc[r] * c2s - m2);
-      if (!full && kt * BK + key_of(r) > kmax) w = 0.f;
-      const float av = w * (1.f - (racc[r] * srho - kr_dot)) * inv_sA;
-      const _Float16 ah = static_cast<_Float16>(av);
-      ab[r >> 3][r & 7] = ah;
-      den += static_cast<float>(ah);
-    }
-    const _Float16* t_row = sKt[buf] + ql * KTS + 8 * g;
+    for (int t = 0; t < NKS; ++t) kf[t] = kr_frag(buf, t);
     #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
       #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        acc[mb] = mfma(*reinterpret_cast<const half8*>(t_row + 32 * mb * KTS + 16 * h), ab[h], acc[mb]);
+      for (int h = 0; h < 2; ++h) tf[2 * mb + h] = kt_frag(buf, mb, h);
+    // S = K Q^T; R = K (hi + lo)^T - kbar.rho' / srho, the shift entering as
+    // the accumulator's initial value; then a = w (1 - srho R) / sA
+    floatx16 sacc = mfma(kf[0], qop[0], floatx16{});
+    floatx16 racc = mfma(kf[0], rhi[0], rinit);
+    racc = mfma(kf[0], rlo[0], racc);
+    #pragma unroll
+    for (int t = 1; t < NKS; ++t) {
+      sacc = mfma(kf[t], qop[t], sacc);
+      racc = mfma(kf[t], rhi[t], racc);
+      racc = mfma(kf[t], rlo[t], racc);
+    }
+    const int lim = kmax - kt * BK;
+    half8 ab[2];
+    auto body = [&](auto masked) __attribute__((always_inline)) {
+      #pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float w0 = fast_exp2(fmaf(sacc[r], c2s, -m2));
+        float w1 = fast_exp2(fmaf(sacc[r + 1], c2s, -m2));
+        if constexpr (decltype(masked)::value) {
+          if (key_of(r) > lim) w0 = 0.f;
+          if (key_of(r + 1) > lim) w1 = 0.f;
+        }
+        const float a0 = w0 * fmaf(racc[r], a_slope, inv_sA);
+        const float a1 = w1 * fmaf(racc[r + 1], a_slope, inv_sA);
+        const half2v ha = pack_sum(a0, a1, den);
+        ab[r >> 3][r & 7] = ha[0];
+        ab[r >> 3][(r & 7) + 1] = ha[1];
+      }
+    };
+    if (wave_full && kt < wlast)
+      body(std::false_type{});
+    else
+      body(std::true_type{});
+    #pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+      #pragma unroll
+      for (int h = 0; h < 2; ++h) acc[mb] = mfma(tf[2 * mb + h], ab[h], acc[mb]);
   }, wave_any);
   den = pair_sum(den);
 
   if (!qvalid) return;
   const size_t orow = static_cast<size_t>(bh) * n + qi;
   const float ob = 1.f / (den * sv);
-  float qx = 0.f, kx = 0.f;
-  if (P.rho) {
-    #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
-      #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const floatx4 kb = sKb[wave][mb * 4 + a][lane];
-        #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int r = 4 * a + b;
-          qx += static_cast<float>(qop[2 * mb + (r >> 3)][r & 7]) * xr[mb][r];
-          kx += kb[b] * xr[mb][r];
-        }
-      }
-  }
-  // (both lanes of the pair are valid here, so the exchange is well defined)
-  qx = pair_sum(qx);
-  kx = pair_sum(kx);
-  const float rs = s / (1.f + (kx - qx));  // the pages' rho_i in input units
   #pragma unroll
   for (int mb = 0; mb < NMB; ++mb)
     #pragma unroll
@@ -711,15 +845,37 @@ __global__ __launch_bounds__(NT) void lla_mfma_main(MainParams P) {
       o.z = acc[mb][4 * a + 2] * ob;
       o.w = acc[mb][4 * a + 3] * ob;
       *reinterpret_cast<float4*>(P.out + orow * D + dim) = o;
-      if (P.rho) {
-        float4 p4;
-        p4.x = xr[mb][4 * a + 0] * rs;
-        p4.y = xr[mb][4 * a + 1] * rs;
-        p4.z = xr[mb][4 * a + 2] * rs;
-        p4.w = xr[mb][4 * a + 3] * rs;
-        *reinterpret_cast<float4*>(P.rho + orow * D + dim) = p4;
-      }
     }
+  if (P.rho) {
+    // the pages' rho_i = rho_c / (1 + (kbar - q).rho_c), in input units
+    float qx = 0.f, kx = 0.f;
+    #pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+      #pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const floatx4 kb = kbs[(mb * 4 + a) * 64 + lane];
+        const floatx4 xc = xs[(mb * 4 + a) * 64 + lane];
+        #pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int r = 4 * a + b;
+          qx += static_cast<float>(qop[2 * mb + (r >> 3)][r & 7]) * xc[b];
+          kx += kb[b] * xc[b];
+        }
+      }
+    // (both lanes of the pair are valid here, so the exchange is well defined)
+    qx = pair_sum(qx);
+    kx = pair_sum(kx);
+    const float rs = s / (1.f + (kx - qx));
+    #pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+      #pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const floatx4 xc = xs[(mb * 4 + a) * 64 + lane];
+        const int dim = 32 * mb + 8 * a + 4 * g;
+        *reinterpret_cast<float4*>(P.rho + orow * D + dim) =
+            make_float4(xc[0] * rs, xc[1] * rs, xc[2] * rs, xc[3] * rs);
+      }
+  }
   if (g == 0) {
     if (P.omega) P.omega[orow] = om;
     if (P.rowmax) P.rowmax[orow] = m2 * kLn2;
@@ -757,6 +913,8 @@ hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
   m.kr = w.kr;
   m.kt = w.kt;
   m.vt = w.vt;
+  m.xs = w.xs;
+  m.kbs = w.kbs;
   m.BH = p.BH;
   m.n = n;
   m.nchunk = nchunk;
@@ -788,8 +946,10 @@ bool mfma_supported(int dtype, int d) { return dtype == LLA_DTYPE_BF16 && (d == 
 size_t mfma_workspace_bytes(int BH, int n, int d) {
   const int nchunk = (n + NORM_ROWS - 1) / NORM_ROWS;
   const size_t npad = static_cast<size_t>((n + BK - 1) / BK) * BK;
+  const size_t nqb = static_cast<size_t>((n + BQ - 1) / BQ);
   return align256(static_cast<size_t>(BH) * nchunk * 2 * sizeof(float)) +
-         3 * align256(static_cast<size_t>(BH) * npad * d * sizeof(_Float16));
+         3 * align256(static_cast<size_t>(BH) * npad * d * sizeof(_Float16)) +
+         2 * align256(static_cast<size_t>(BH) * nqb * BQ * d * sizeof(float));
 }
 
 hipError_t launch_mfma(const FwdParams& p, hipStream_t stream) {
