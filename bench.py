@@ -40,6 +40,26 @@ def algorithmic_flops(n: int, d: int, iters: np.ndarray) -> float:
     return float(d * np.sum(pairs[None, None, :] * (10.0 + 6.0 * iters.astype(np.float64))))
 
 
+def measured_traffic(path: str):
+    """HBM bytes (calibrated FETCH_SIZE + WRITE_SIZE) of one launch of the main
+    kernel, from a rocprofv3 summary, or None when the summary is missing or was
+    taken on another version of the kernel source."""
+    import hashlib
+    if not os.path.exists(path):
+        return None
+    src = os.path.join(ROOT, "local_linear_attention_flashlla_amd", "csrc", "lla_mfma.hip")
+    with open(src, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    found_sha, value = None, None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("lla_mfma.hip sha256:"):
+                found_sha = line.split(":", 1)[1].strip()
+            elif line.startswith("bytes_per_launch lla_mfma_main:"):
+                value = float(line.split(":", 1)[1])
+    return value if found_sha == sha else None
+
+
 def _oracle_sample_job(args):
     q, k, v, lam, rows = args
     from threadpoolctl import threadpool_limits
@@ -94,10 +114,11 @@ def main(argv=None):
                     choices=["tiny", "piecewise", "standard", "long", "recall"])
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--split-u", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=3072,
+    ap.add_argument("--cpu-rows", type=int, default=8192,
                     help="rows in the CPU-oracle sample (0 = skip)")
     ap.add_argument("--traffic", default=None,
-                    help="JSON file with measured HBM bytes per launch of the main kernel")
+                    help="byte-counter summary to read the main kernel's HBM bytes per launch "
+                         "from (default: the one under profiles/ for this workload)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a "
                          "reference kernel of known traffic for hardware byte counters)")
@@ -169,10 +190,9 @@ def main(argv=None):
     else:
         bound, peak, unit = "alu", PEAK["valu_fp32"], "TFLOP/s"
     achieved = flops / (kern_ms * 1e-3) / 1e12
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            traffic = json.load(f).get("bytes_per_launch")
+    traffic = measured_traffic(args.traffic or os.path.join(
+        ROOT, "profiles", f"lla_mfma_main_{wl.name}_hbm_bytes.txt")) \
+        if kernel_used == lla.LLA_KERNEL_MFMA and not args.split_u else None
 
     if args.calib_copy_mb > 0:
         nbytes = args.calib_copy_mb << 20
