@@ -124,8 +124,10 @@ typedef struct lla_fwd_args {
   int kernel;         /* LLA_KERNEL_* */
   int flags;          /* LLA_FLAG_* */
   /* optional timing events (created by the caller, NULL = none): recorded on
-     `stream` immediately before and after the call's main kernel, the one
-     that runs the three phases (any set-up kernel falls outside them) */
+     `stream` immediately before and after the call's dominant kernel -- the
+     conjugate-gradient kernel of the matrix-core path, the single fused
+     kernel of the vector-ALU path; set-up kernels and the moment and output
+     kernels of the matrix-core path fall outside them */
   hipEvent_t ev_main_begin;
   hipEvent_t ev_main_end;
 } lla_fwd_args;

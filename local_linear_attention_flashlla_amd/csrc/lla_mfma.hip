@@ -55,7 +55,9 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BQ = 128;     // queries per workgroup
+constexpr int kNW13 = 4;    // waves per workgroup of the moment and output kernels
+constexpr int kNW2 = 4;     // waves per workgroup of the CG kernel
+constexpr int kMaxBQ = 32 * (kNW13 > kNW2 ? kNW13 : kNW2);  // slab padding of the query axis
 constexpr int BK = 32;      // keys per tile
 constexpr int NT = 256;     // threads per workgroup (4 waves)
 constexpr int NORM_ROWS = 256;
@@ -117,6 +119,8 @@ struct Workspace {
   _Float16* vt;     // [BH][npad/32][D][32] sv v transposed, key index permuted
   float* xs;        // CG iterates: per workgroup BQ x D fp32, lane-contiguous
   float* kbs;       // fp32 kbar, same layout
+  float* rs;        // CG residuals, same layout
+  float* qs;        // per query row max and omega: [blocks][4 waves][2][64 lanes]
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -135,11 +139,15 @@ Workspace carve(void* base, int BH, int n, int d) {
   p += t;
   w.vt = reinterpret_cast<_Float16*>(p);
   p += t;
-  const size_t nqb = static_cast<size_t>((n + BQ - 1) / BQ);
-  const size_t sl = align256(static_cast<size_t>(BH) * nqb * BQ * d * sizeof(float));
+  const size_t nqpad = static_cast<size_t>((n + kMaxBQ - 1) / kMaxBQ) * kMaxBQ;
+  const size_t sl = align256(static_cast<size_t>(BH) * nqpad * d * sizeof(float));
   w.xs = reinterpret_cast<float*>(p);
   p += sl;
   w.kbs = reinterpret_cast<float*>(p);
+  p += sl;
+  w.rs = reinterpret_cast<float*>(p);
+  p += sl;
+  w.qs = reinterpret_cast<float*>(p);
   return w;
 }
 
@@ -211,8 +219,13 @@ __global__ __launch_bounds__(NT) void prep_norms(const uint16_t* __restrict__ q,
   }
 }
 
-// Prepass 2: per (head, 32-key block) write s k in fp16 as permuted rows and
-// as a permuted transposed tile, and sv v as a permuted transposed tile.
+// Prepass 2: per (head, 32-key block) write s k in fp16 as a tile of
+// permuted rows and as a permuted transposed tile, and sv v as a permuted
+// transposed tile. Tiles are stored chunk-major (all rows' first 16-byte
+// chunk, then all rows' second, ...): an MFMA operand fragment of a lane is
+// one chunk of one row, so the 16 lanes that LDS serves together read 256
+// consecutive bytes (no bank conflicts) and the fragments of one lane sit at
+// fixed offsets from each other.
 template <int D>
 __global__ __launch_bounds__(NT) void prep_convert(const uint16_t* __restrict__ k,
                                                    const uint16_t* __restrict__ v, int n,
@@ -241,18 +254,20 @@ __global__ __launch_bounds__(NT) void prep_convert(const uint16_t* __restrict__ 
     sV[r][c] = b;
   }
   __syncthreads();
-  const size_t npad = static_cast<size_t>(nblk) * BK;
+  // both tiles chunk-major: 16-byte chunk c of every row, rows consecutive
+  const size_t tb = (static_cast<size_t>(bh) * nblk + kb) * BK * D;
   for (int e = threadIdx.x; e < BK * D; e += NT) {
-    const int r = e / D, pos = e % D;
+    // K rows: [chunk c < D/8][row r < 32][8], d positions 8c..8c+7 permuted
+    const int c = e / (8 * BK), r = (e / 8) % BK, pos = 8 * c + e % 8;
     const int src = (pos & ~15) | swz16(pos & 15);
-    kr[(static_cast<size_t>(bh) * npad + kb * BK + r) * D + pos] = static_cast<_Float16>(sK[r][src]);
+    kr[tb + e] = static_cast<_Float16>(sK[r][src]);
   }
-  const size_t tb = (static_cast<size_t>(bh) * nblk + kb) * D;
   for (int e = threadIdx.x; e < BK * D; e += NT) {
-    const int dim = e / BK, pos = e % BK;
+    // transposed: [chunk c < 4][dim < D][8], key positions 8c..8c+7 permuted
+    const int c = e / (8 * D), dim = (e / 8) % D, pos = 8 * c + e % 8;
     const int key = (pos & 16) | swz16(pos & 15);
-    kt[(tb + dim) * BK + pos] = static_cast<_Float16>(sK[key][dim]);
-    vt[(tb + dim) * BK + pos] = static_cast<_Float16>(sV[key][dim]);
+    kt[tb + e] = static_cast<_Float16>(sK[key][dim]);
+    vt[tb + e] = static_cast<_Float16>(sV[key][dim]);
   }
 }
 
@@ -271,54 +286,76 @@ struct MainParams {
   const _Float16* vt;
   float* xs;         // CG iterate slab, [blocks][4 waves][d/8 float4 chunks][64 lanes]
   float* kbs;        // fp32 kbar slab, same layout
+  float* rs;         // CG residual slab, same layout
+  float* qs;         // per-query state slab: row max, omega
   int BH, n, nchunk, nblk;
+  int nq32;          // 32-query groups per head in the state slabs
   float lambda;
   int cg_max_iters;
   float cg_rel_tol;
 };
 
-// LDS tiles. The K-row tile holds BK rows of D fp16 (the d index already
-// permuted by swz16 within 16-element chunks); the transposed tile holds D
-// rows of BK fp16 keys. Neither is padded: the 16-byte chunk c of a row sits
-// at chunk position c ^ chunk_xor(row) instead, which spreads the rows that one
-// 16-lane group reads in the same operand step over distinct LDS banks.
-template <int D>
-__device__ __forceinline__ int kr_chunk_xor(int row) {
-  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+// Copy key tile `kt` of this head (rows or transposed, both BK x D fp16,
+// contiguous in global memory) into an LDS tile with global_load_lds: each
+// wave instruction moves 1 KiB, lane l its l-th 16 bytes; the four waves
+// together copy the tile. Completion is awaited by a later barrier.
+// Buffer resource over `bytes` bytes at `base` (raw, untyped; reads past the
+// end return zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
 }
-__device__ __forceinline__ int kt_chunk_xor(int row) { return (row >> 2) & 3; }
 
-// Copy key tile `kt` of this head straight from global memory into the LDS
-// tiles (global_load_lds: each wave instruction fills 1 KiB of LDS, lane l
-// its l-th 16 bytes; the source address of each lane applies the chunk
-// permutation). Completion is awaited by the next __syncthreads().
-template <int D>
-__device__ __forceinline__ void load_tile_to_lds(const _Float16* kr_head, const _Float16* t_head,
-                                                 int kt, _Float16* sKr, _Float16* sKt, int wave,
-                                                 int lane) {
-  constexpr int CPR = D / 8;          // 16-byte chunks per K row
-  constexpr int RPI = 64 / CPR;       // K rows per wave instruction
-  constexpr int NI = D / 64;          // instructions per wave for each tile
+// 16-byte chunk `chunk` of lane `lane` in a lane-contiguous state slab
+// ([chunk][64 lanes] x 16 bytes)
+__device__ __forceinline__ floatx4 slab_ld(__amdgpu_buffer_rsrc_t r, int chunk, int lane) {
+  return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, chunk * 1024, 0));
+}
+__device__ __forceinline__ void slab_st(__amdgpu_buffer_rsrc_t r, int chunk, int lane, floatx4 x) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, lane * 16, chunk * 1024, 0);
+}
+
+template <int D, int NW>
+__device__ __forceinline__ void load_kr_to_lds(__amdgpu_buffer_rsrc_t head, int kt, _Float16* buf,
+                                               int wave, int lane) {
+  constexpr int NI = D / 16;  // 1 KiB instructions per tile
+  const int tile_off = kt * (BK * D * 2);  // bytes, wave-uniform
   #pragma unroll
-  for (int u = 0; u < NI; ++u) {
-    const int inst = wave * NI + u;
-    const int row = inst * RPI + lane / CPR;
-    const int c = (lane % CPR) ^ kr_chunk_xor<D>(row);
-    const _Float16* src = kr_head + (static_cast<size_t>(kt) * BK + row) * D + c * 8;
-    __builtin_amdgcn_global_load_lds(
-        (const __attribute__((address_space(1))) void*)(src),
-        (__attribute__((address_space(3))) void*)(sKr + inst * 512), 16, 0, 0);
+  for (int u = 0; u < (NI + NW - 1) / NW; ++u) {
+    const int inst = u * NW + wave;
+    if (NI % NW == 0 || inst < NI)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          head, (__attribute__((address_space(3))) void*)(buf + inst * 512), 16,
+          inst * 1024 + lane * 16, tile_off, 0, 0);
   }
-  #pragma unroll
-  for (int u = 0; u < NI; ++u) {
-    const int inst = wave * NI + u;
-    const int row = inst * 16 + lane / 4;
-    const int c = (lane % 4) ^ kt_chunk_xor(row);
-    const _Float16* src = t_head + static_cast<size_t>(kt) * D * BK + row * BK + c * 8;
-    __builtin_amdgcn_global_load_lds(
-        (const __attribute__((address_space(1))) void*)(src),
-        (__attribute__((address_space(3))) void*)(sKt + inst * 512), 16, 0, 0);
-  }
+}
+template <int D, int NW>
+__device__ __forceinline__ void load_kt_to_lds(__amdgpu_buffer_rsrc_t head, int kt, _Float16* buf,
+                                               int wave, int lane) {
+  load_kr_to_lds<D, NW>(head, kt, buf, wave, lane);
+}
+template <int D, int NW>
+__device__ __forceinline__ void load_tile_to_lds(__amdgpu_buffer_rsrc_t kr_head,
+                                                 __amdgpu_buffer_rsrc_t t_head, int kt,
+                                                 _Float16* sKr, _Float16* sKt, int wave, int lane) {
+  load_kr_to_lds<D, NW>(kr_head, kt, sKr, wave, lane);
+  load_kt_to_lds<D, NW>(t_head, kt, sKt, wave, lane);
+}
+
+// End of a step of the pipelined CG sweep: wait until at most the copies of
+// the last two steps (rows and transposed tile, ceil(D/16 / NW) instructions
+// each per wave) are still in flight, i.e. this wave's copies of two steps
+// ago have landed, and all LDS reads of this step are done; then a barrier,
+// after which every wave's copies of two steps ago are visible. The asm
+// statement is also a compiler memory barrier: no memory access moves across.
+template <int D, int NW>
+__device__ __forceinline__ void step_barrier() {
+  constexpr int per_step = 2 * ((D / 16 + NW - 1) / NW);
+  static_assert(per_step == 2 || per_step == 4, "vmcnt below assumes 1 or 2 copies per tile");
+  if constexpr (per_step == 4)
+    asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Work order. Workgroups are handed to the eight XCDs (each with its own L2)
@@ -340,25 +377,29 @@ __device__ __forceinline__ void block_coords(int b, int BH, int nqb, int* qb, in
   }
 }
 
-template <int D, bool SPLIT_U>
-__global__ __launch_bounds__(NT) void lla_mfma_main(MainParams P) {
+template <int D, int PHASE, bool SPLIT_U, int NW>
+__global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
   constexpr int NKS = D / 16;  // k-steps over d
   constexpr int NMB = D / 32;  // 32-row blocks over d
-  __shared__ __align__(16) _Float16 sKr[2][BK * D];
-  __shared__ __align__(16) _Float16 sKt[2][D * BK];
-  __shared__ __align__(16) half8 sKb[NT / 64][NKS][64];     // kbar, fp16, operand order
-  __shared__ __align__(16) floatx4 sR[NT / 64][NMB * 4][64];  // CG residual r, fp32
+  constexpr int BQW = 32 * NW; // queries per workgroup (32 per wave)
+  // key tiles: in the CG sweep tile t lives in sKr<t % 4> (rows) and
+  // sKt<t % 4> (transposed); separate arrays so that every buffer choice there
+  // is static. The other sweeps double-buffer through buffers 0 and 1.
+  __shared__ __align__(16) _Float16 sKr0[BK * D], sKr1[BK * D], sKr2[BK * D], sKr3[BK * D];
+  __shared__ __align__(16) _Float16 sKt0[D * BK], sKt1[D * BK], sKt2[D * BK], sKt3[D * BK];
+  __shared__ __align__(16) half8 sKb[NW][NKS][64];  // kbar, fp16, operand order
   __shared__ float sScale[2];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int ql = lane & 31, g = lane >> 5;
   const int n = P.n;
-  const int nqb = (n + BQ - 1) / BQ;
+  const int nqb = (n + BQW - 1) / BQW;
   int qb, bh;
   block_coords(static_cast<int>(blockIdx.x), P.BH, nqb, &qb, &bh);
-  const int i0 = qb * BQ;
-  const int kend = min(n, i0 + BQ);
+  const int i0 = qb * BQW;
+  const int kend = min(n, i0 + BQW);
   const int ntiles = (kend + BK - 1) / BK;
   const int qi = i0 + 32 * wave + ql;
   const bool qvalid = qi < n;
@@ -374,9 +415,12 @@ __global__ __launch_bounds__(NT) void lla_mfma_main(MainParams P) {
   const float c2s = kLog2e / sqrtf(static_cast<float>(D)) / (s * s);
   const float lam_s = P.lambda * s * s;
 
-  const _Float16* kr_head = P.kr + static_cast<size_t>(bh) * P.nblk * BK * D;
-  const _Float16* kt_head = P.kt + static_cast<size_t>(bh) * P.nblk * BK * D;
-  const _Float16* vt_head = P.vt + static_cast<size_t>(bh) * P.nblk * BK * D;
+  // buffer resources over this head's key tiles (rows, transposed) and value tiles
+  const size_t head_elems = static_cast<size_t>(P.nblk) * BK * D;
+  const uint32_t head_bytes = static_cast<uint32_t>(head_elems * sizeof(_Float16));
+  const __amdgpu_buffer_rsrc_t kr_head = make_rsrc(P.kr + bh * head_elems, head_bytes);
+  const __amdgpu_buffer_rsrc_t kt_head = make_rsrc(P.kt + bh * head_elems, head_bytes);
+  const __amdgpu_buffer_rsrc_t vt_head = make_rsrc(P.vt + bh * head_elems, head_bytes);
 
   // Q operand of this lane's query: slot (t, c) holds s q[16 t + 8 (c >> 2) + 4 g + (c & 3)]
   half8 qop[NKS];
@@ -399,28 +443,58 @@ __global__ __launch_bounds__(NT) void lla_mfma_main(MainParams P) {
 
   // The key sweep: tiles 0 .. ntiles-1 of this head, double-buffered through
   // LDS; `tile(kt, buf)` runs on the waves whose queries see tile kt.
-  auto sweep = [&](const _Float16* t_head, auto&& tile, bool wave_busy) __attribute__((always_inline)) {
-    load_tile_to_lds<D>(kr_head, t_head, 0, sKr[0], sKt[0], wave, lane);
+  auto krbuf = [&](int buf) __attribute__((always_inline)) { return buf ? sKr1 : sKr0; };
+  auto ktbuf = [&](int buf) __attribute__((always_inline)) { return buf ? sKt1 : sKt0; };
+  auto sweep = [&](__amdgpu_buffer_rsrc_t t_head, auto&& tile, bool wave_busy) __attribute__((always_inline)) {
+    load_tile_to_lds<D, NW>(kr_head, t_head, 0, sKr0, sKt0, wave, lane);
     __syncthreads();
     for (int kt = 0; kt < ntiles; ++kt) {
       const int buf = kt & 1;
-      if (kt + 1 < ntiles) load_tile_to_lds<D>(kr_head, t_head, kt + 1, sKr[buf ^ 1], sKt[buf ^ 1], wave, lane);
+      if (kt + 1 < ntiles) load_tile_to_lds<D, NW>(kr_head, t_head, kt + 1, krbuf(buf ^ 1), ktbuf(buf ^ 1), wave, lane);
       if (wave_busy && kt <= wlast) tile(kt, buf);
       __syncthreads();
     }
   };
 
   // this lane's operand fragments in the LDS tiles
-  const int krx = kr_chunk_xor<D>(ql), ktx = kt_chunk_xor(ql);
-  auto kr_frag = [&](int buf, int t) __attribute__((always_inline)) {
-    return *reinterpret_cast<const half8*>(sKr[buf] + ql * D + 8 * ((2 * t + g) ^ krx));
+  auto kr_frag_at = [&](const _Float16* b, int t) __attribute__((always_inline)) {
+    return *reinterpret_cast<const half8*>(b + ((2 * t + g) * BK + ql) * 8);
   };
+  auto kt_frag_at = [&](const _Float16* b, int mb, int h) __attribute__((always_inline)) {
+    return *reinterpret_cast<const half8*>(b + ((2 * h + g) * D + 32 * mb + ql) * 8);
+  };
+  auto kr_frag = [&](int buf, int t) __attribute__((always_inline)) { return kr_frag_at(krbuf(buf), t); };
   auto kt_frag = [&](int buf, int mb, int h) __attribute__((always_inline)) {
-    return *reinterpret_cast<const half8*>(sKt[buf] + (32 * mb + ql) * BK + 8 * ((2 * h + g) ^ ktx));
+    return kt_frag_at(ktbuf(buf), mb, h);
+  };
+  // static buffer choice for the CG sweep
+  auto KR = [&](auto I) __attribute__((always_inline)) -> _Float16* {
+    constexpr int i = decltype(I)::value % 4;
+    if constexpr (i == 0) return sKr0;
+    else if constexpr (i == 1) return sKr1;
+    else if constexpr (i == 2) return sKr2;
+    else return sKr3;
+  };
+  auto KT = [&](auto I) __attribute__((always_inline)) -> _Float16* {
+    constexpr int i = decltype(I)::value % 4;
+    if constexpr (i == 0) return sKt0;
+    else if constexpr (i == 1) return sKt1;
+    else if constexpr (i == 2) return sKt2;
+    else return sKt3;
   };
 
   // key index (within the tile) of accumulator register r of this lane
   auto key_of = [&](int r) __attribute__((always_inline)) { return 8 * (r >> 2) + 4 * g + (r & 3); };
+
+  // per-wave slabs of per-query state, shared by the three phase kernels
+  // (indexed by the wave's 32-query group, whatever the workgroup size)
+  const size_t wslot = static_cast<size_t>(bh) * (P.nq32) + (i0 >> 5) + wave;
+  // (buffer resources: scalar base, lane offset, chunk offset in a scalar)
+  const __amdgpu_buffer_rsrc_t xs = make_rsrc(P.xs + wslot * (32 * D), 32 * D * 4);
+  const __amdgpu_buffer_rsrc_t kbs = make_rsrc(P.kbs + wslot * (32 * D), 32 * D * 4);
+  const __amdgpu_buffer_rsrc_t rsl = make_rsrc(P.rs + wslot * (32 * D), 32 * D * 4);
+  float* qst = P.qs + wslot * 128;  // [0, 64): row max m2; [64, 128): omega
+  const size_t orow = static_cast<size_t>(bh) * n + (qvalid ? qi : 0);
 
   floatx16 acc[NMB];
   #pragma unroll
@@ -428,6 +502,7 @@ __global__ __launch_bounds__(NT) void lla_mfma_main(MainParams P) {
     #pragma unroll
     for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
 
+  if constexpr (PHASE == 1) {
   // ------------------------------ phase 1 ------------------------------
   float m2 = -INFINITY;  // running row max of the log2-scaled scores
   float om = 0.f;        // partial row sum (this half of the keys)
@@ -487,23 +562,10 @@ __global__ __launch_bounds__(NT) void lla_mfma_main(MainParams P) {
   om = pair_sum(om);
   if (!qvalid) m2 = 0.f;
 
-  // --------------------------- CG set-up -------------------------------
-  // Per query: kbar = mu~ / omega, r0 = mu = mu~ - omega q, x0 = 0. Nothing
-  // large stays in registers across a key sweep: r lives in LDS (fp32), x and
-  // the fp32 kbar in lane-contiguous workspace slabs, and the CG matvec uses
-  // kbar rounded to fp16 from LDS as its expansion point. The matvec is exact
-  // for any expansion point c used consistently in U = w (K d - c.d) and in
-  // the correction -(sum U) c (the shift of c.d cancels through sum U), so
-  // rounding kbar only moves the centre: Sigma_c becomes
-  // Sigma_c + omega (kbar - c)(kbar - c)^T, a rank-one change of relative size
-  // 2^-24. Phase 3 uses the fp32 kbar.
-  const size_t slab = (static_cast<size_t>(blockIdx.x) * (NT / 64) + wave) * (NMB * 4 * 64);
-  floatx4* xs = reinterpret_cast<floatx4*>(P.xs) + slab;
-  floatx4* kbs = reinterpret_cast<floatx4*>(P.kbs) + slab;
-  float rr = 0.f;
+  // Per query: kbar = mu~ / omega, r0 = mu = mu~ - omega q, x0 = 0, into the
+  // lane-contiguous workspace slabs; the row max and omega into the state slab.
   {
     const float inv_om = qvalid ? 1.f / om : 0.f;
-    half8 kb16[NKS];
     #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
       #pragma unroll
@@ -515,16 +577,54 @@ __global__ __launch_bounds__(NT) void lla_mfma_main(MainParams P) {
           const float mt = acc[mb][r];
           const float qv = static_cast<float>(qop[2 * mb + (r >> 3)][r & 7]);
           kb[b] = mt * inv_om;
-          kb16[2 * mb + (r >> 3)][r & 7] = static_cast<_Float16>(kb[b]);
           rc[b] = qvalid ? mt - om * qv : 0.f;
-          rr += rc[b] * rc[b];
         }
-        kbs[(mb * 4 + a) * 64 + lane] = kb;
-        xs[(mb * 4 + a) * 64 + lane] = floatx4{0.f, 0.f, 0.f, 0.f};
-        sR[wave][mb * 4 + a][lane] = rc;
+        slab_st(kbs, mb * 4 + a, lane, kb);
+        slab_st(xs, mb * 4 + a, lane, floatx4{0.f, 0.f, 0.f, 0.f});
+        slab_st(rsl, mb * 4 + a, lane, rc);
+      }
+  }
+  qst[lane] = m2;
+  qst[64 + lane] = om;
+  if (qvalid && g == 0) {
+    if (P.omega) P.omega[orow] = om;
+    if (P.rowmax) P.rowmax[orow] = m2 * kLn2;
+  }
+  } else if constexpr (PHASE == 2) {
+  // --------------------------- CG set-up -------------------------------
+  // The CG matvec uses kbar rounded to fp16 (kept in LDS) as its expansion
+  // point. The matvec is exact for any expansion point c used consistently in
+  // U = w (K d - c.d) and in the correction -(sum U) c (the shift of c.d
+  // cancels through sum U), so rounding kbar only moves the centre: Sigma_c
+  // becomes Sigma_c + omega (kbar - c)(kbar - c)^T, a rank-one change of
+  // relative size 2^-24. The output phase uses the fp32 kbar.
+  const float m2 = qst[lane];
+  {
+    half8 kb16[NKS];
+    #pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+      #pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const floatx4 kb = slab_ld(kbs, mb * 4 + a, lane);
+        #pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int r = 4 * a + b;
+          kb16[2 * mb + (r >> 3)][r & 7] = static_cast<_Float16>(kb[b]);
+        }
       }
     #pragma unroll
     for (int t = 0; t < NKS; ++t) sKb[wave][t][lane] = kb16[t];
+  }
+  // CG state in registers: residual r and iterate x (fp32, accumulator
+  // layout); between updates they are parked in the accumulation registers
+  floatx4 rv4[NMB * 4], xv4[NMB * 4];
+  float rr = 0.f;
+  #pragma unroll
+  for (int c = 0; c < NMB * 4; ++c) {
+    rv4[c] = slab_ld(rsl, c, lane);
+    xv4[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+    for (int b = 0; b < 4; ++b) rr += rv4[c][b] * rv4[c][b];
   }
   rr = pair_sum(rr);
   const float r0n = sqrtf(rr);
@@ -548,108 +648,206 @@ __global__ __launch_bounds__(NT) void lla_mfma_main(MainParams P) {
   half8 dop[NKS];
   float sp = 1.f;
   {
-    float rv[NMB][16];
     float mx = 0.f;
     #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
+    for (int c = 0; c < NMB * 4; ++c)
       #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const floatx4 rc = sR[wave][mb * 4 + a][lane];
-        #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          rv[mb][4 * a + b] = rc[b];
-          mx = fmaxf(mx, fabsf(rc[b]));
-        }
-      }
+      for (int b = 0; b < 4; ++b) mx = fmaxf(mx, fabsf(rv4[c][b]));
     sp = pow2_ceil(pair_max(mx));
     const float inv = 1.f / sp;
     #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
+    for (int c = 0; c < NMB * 4; ++c)
       #pragma unroll
-      for (int r = 0; r < 16; ++r) dop[2 * mb + (r >> 3)][r & 7] = static_cast<_Float16>(rv[mb][r] * inv);
+      for (int b = 0; b < 4; ++b) {
+        const int r = 4 * (c & 3) + b, mb = c >> 2;
+        dop[2 * mb + (r >> 3)][r & 7] = static_cast<_Float16>(rv4[c][b] * inv);
+      }
   }
   float kbd = kbar_dot(dop);
+  // Operands and state that the key sweep does not touch with vector
+  // instructions wait in the accumulation registers (MFMA takes its B
+  // operand from there directly): q, the direction, r and x.
+  auto park = [&]() __attribute__((always_inline)) {
+    #pragma unroll
+    for (int t = 0; t < NKS; ++t) {
+      asm volatile("" : "+a"(qop[t]));
+      asm volatile("" : "+a"(dop[t]));
+    }
+    #pragma unroll
+    for (int c = 0; c < NMB * 4; ++c) {
+      asm volatile("" : "+a"(rv4[c]));
+      asm volatile("" : "+a"(xv4[c]));
+    }
+  };
+  park();
 
   // ------------------------------ phase 2 ------------------------------
+  // The first tiles of every sweep (rows of tiles 0..3, transposed tiles 0
+  // and 1, and tile 0 again into sKt3) are copied before the sweep's first
+  // barrier: for the first iteration here, for later ones before the CG
+  // update of the previous iteration, which hides the copy latency.
+  auto start_sweep_copies = [&]() __attribute__((always_inline)) {
+    const int tl = ntiles - 1;
+    load_kr_to_lds<D, NW>(kr_head, 0, sKr0, wave, lane);
+    load_kr_to_lds<D, NW>(kr_head, min(1, tl), sKr1, wave, lane);
+    load_kr_to_lds<D, NW>(kr_head, min(2, tl), sKr2, wave, lane);
+    load_kr_to_lds<D, NW>(kr_head, min(3, tl), sKr3, wave, lane);
+    load_kt_to_lds<D, NW>(kt_head, 0, sKt0, wave, lane);
+    load_kt_to_lds<D, NW>(kt_head, min(1, tl), sKt1, wave, lane);
+    load_kt_to_lds<D, NW>(kt_head, 0, sKt3, wave, lane);
+  };
+  start_sweep_copies();
   for (int it = 0; it < P.cg_max_iters; ++it) {
     if (!__syncthreads_or(active ? 1 : 0)) break;
-    const bool wave_busy = __any(active ? 1 : 0);
     #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
       #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
     float usum = 0.f;
-    floatx16 tinit;
-    #pragma unroll
-    for (int r = 0; r < 16; ++r) tinit[r] = -kbd;
-    sweep(kt_head, [&](int kt, int buf) __attribute__((always_inline)) {
-      half8 kf[NKS], tf[2 * NMB];
-      #pragma unroll
-      for (int t = 0; t < NKS; ++t) kf[t] = kr_frag(buf, t);
-      #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb)
-        #pragma unroll
-        for (int h = 0; h < 2; ++h) tf[2 * mb + h] = kt_frag(buf, mb, h);
-      // S = K Q^T; T = K d^T - kbar.d (the shift enters as the accumulator's
-      // initial value, so U = w T needs one multiply per element)
-      floatx16 sacc = mfma(kf[0], qop[0], floatx16{});
-      floatx16 tacc = mfma(kf[0], dop[0], tinit);
+
+    // S = K Q^T and K d^T for the key tile in `kbuf`
+    auto st_tile = [&](const _Float16* kbuf, floatx16& so, floatx16& to) __attribute__((always_inline)) {
+      half8 kf = kr_frag_at(kbuf, 0);
+      so = mfma(kf, qop[0], floatx16{});
+      to = mfma(kf, dop[0], floatx16{});
       #pragma unroll
       for (int t = 1; t < NKS; ++t) {
-        sacc = mfma(kf[t], qop[t], sacc);
-        tacc = mfma(kf[t], dop[t], tacc);
+        kf = kr_frag_at(kbuf, t);
+        so = mfma(kf, qop[t], so);
+        to = mfma(kf, dop[t], to);
       }
-      half8 ub[2], ul[2];
-      const int lim = kmax - kt * BK;  // keys <= lim are visible
-      auto make_u = [&](auto masked) __attribute__((always_inline)) {
-        #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          float w0 = fast_exp2(fmaf(sacc[r], c2s, -m2));
-          float w1 = fast_exp2(fmaf(sacc[r + 1], c2s, -m2));
-          if constexpr (decltype(masked)::value) {
-            if (key_of(r) > lim) w0 = 0.f;
-            if (key_of(r + 1) > lim) w1 = 0.f;
-          }
-          const float u0 = w0 * tacc[r], u1 = w1 * tacc[r + 1];
-          const half2v hu = pack_sum(u0, u1, usum);
-          ub[r >> 3][r & 7] = hu[0];
-          ub[r >> 3][(r & 7) + 1] = hu[1];
-          if constexpr (SPLIT_U) {
-            const half2v lo = pack_sum(u0 - static_cast<float>(hu[0]),
-                                       u1 - static_cast<float>(hu[1]), usum);
-            ul[r >> 3][r & 7] = lo[0];
-            ul[r >> 3][(r & 7) + 1] = lo[1];
-          }
-        }
+    };
+    // Software-pipelined sweep over tiles 0 .. 4 qb + 3 of this head: every
+    // query of the block sees the whole of tiles 0 .. 4 qb - 1; the last four
+    // tiles hold the block's diagonal and are masked (tiles past the end of
+    // the head are clamped copies of its last tile, masked out entirely).
+    // Step j, all waves in lockstep:
+    //   start copying rows of tile j + 4 and the transposed tile j + 2;
+    //   Y += Kt(j-1)^T U(j-1)            matrix cores, U from step j - 1
+    //   [S; T](j+1) = K(j+1) [Q; D]^T    matrix cores
+    //   U(j) = w(S(j)) T(j)              vector ALU, independent of both
+    // so the vector work of one tile overlaps the matrix work of its
+    // neighbours, and every copy has two steps to land. Tile t sits in
+    // sKr<t % 4> and sKt<t % 4>: step j overwrites the rows of tile j (last
+    // read in step j - 1) and the transposed tile j - 2 (last read in step
+    // j - 1). A step ends by waiting for this wave's copies issued two steps
+    // earlier (the ones the next step reads), then a barrier.
+    const int nsteps = NW * (qb + 1);  // the last NW tiles hold the diagonal
+    const int tlast = ntiles - 1;
+    half8 ua[2], ub[2], ula[2], ulb[2];
+    floatx16 sa, ta, sb, tb;
+    // One step, written out in issue order: the tile copies, PF fragment
+    // reads ahead, then for each of the NF matrix products of the step (the
+    // NY of Y, then the NKS of [S; T]) its MFMA(s), the fragment read PF
+    // products ahead and EPS elements of U(j). The sched_barrier fences keep
+    // that order, so the vector work and LDS latency hide under the MFMAs.
+    constexpr int NY = 2 * NMB, NF = NY + NKS, PF = 4, EPS = 16 / NF;
+    static_assert(NF * EPS == 16, "U elements must spread evenly");
+    auto pstep = [&](auto JM, auto masked, int j, const floatx16& sc, const floatx16& tc,
+                     floatx16& sn, floatx16& tn, const half8 (&up)[2], const half8 (&ulp)[2],
+                     half8 (&uc)[2], half8 (&ulc)[2]) __attribute__((always_inline)) {
+      constexpr int jm = decltype(JM)::value;
+      const _Float16* kbn = KR(std::integral_constant<int, jm + 1>{});
+      const _Float16* tbp = KT(std::integral_constant<int, jm + 3>{});
+      load_kr_to_lds<D, NW>(kr_head, min(j + 4, tlast), KR(std::integral_constant<int, jm>{}), wave, lane);
+      load_kt_to_lds<D, NW>(kt_head, min(j + 2, tlast), KT(std::integral_constant<int, jm + 2>{}), wave, lane);
+      auto frag = [&](int k) __attribute__((always_inline)) {
+        // Y products cycle through the accumulators (no two dependent MFMAs
+        // back to back): product k uses row block k % NMB and key half k / NMB
+        return k < NY ? kt_frag_at(tbp, k % NMB, k / NMB) : kr_frag_at(kbn, k - NY);
       };
-      // the causal mask only bites on the wave's diagonal tile (wave-uniform)
-      if (wave_full && kt < wlast)
-        make_u(std::false_type{});
-      else
-        make_u(std::true_type{});
+      half8 fr[PF];
       #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb)
-        #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          acc[mb] = mfma(tf[2 * mb + h], ub[h], acc[mb]);
-          if constexpr (SPLIT_U) acc[mb] = mfma(tf[2 * mb + h], ul[h], acc[mb]);
+      for (int k = 0; k < PF; ++k) fr[k] = frag(k);
+      const int lim = kmax - j * BK;  // keys <= lim are visible
+      float uv[16];
+      __builtin_amdgcn_sched_barrier(0);
+      #pragma unroll
+      for (int k = 0; k < NF; ++k) {
+        const half8 f = fr[k % PF];
+        if (k < NY) {
+          acc[k % NMB] = mfma(f, up[k / NMB], acc[k % NMB]);
+          if constexpr (SPLIT_U) acc[k % NMB] = mfma(f, ulp[k / NMB], acc[k % NMB]);
+        } else {
+          const int t = k - NY;
+          sn = mfma(f, qop[t], t == 0 ? floatx16{} : sn);
+          tn = mfma(f, dop[t], t == 0 ? floatx16{} : tn);
         }
-    }, wave_busy);
+        if (k + PF < NF) fr[k % PF] = frag(k + PF);
+        #pragma unroll
+        for (int e = 0; e < EPS; ++e) {
+          const int r = k * EPS + e;
+          float w = fast_exp2(fmaf(sc[r], c2s, -m2));
+          if constexpr (decltype(masked)::value) {
+            if (key_of(r) > lim) w = 0.f;
+          }
+          uv[r] = w * (tc[r] - kbd);
+          if (r & 1) {
+            const half2v hu = pack_sum(uv[r - 1], uv[r], usum);
+            uc[r >> 3][(r - 1) & 7] = hu[0];
+            uc[r >> 3][r & 7] = hu[1];
+            if constexpr (SPLIT_U) {
+              const half2v lo = pack_sum(uv[r - 1] - static_cast<float>(hu[0]),
+                                         uv[r] - static_cast<float>(hu[1]), usum);
+              ulc[r >> 3][(r - 1) & 7] = lo[0];
+              ulc[r >> 3][r & 7] = lo[1];
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      step_barrier<D, NW>();
+    };
+    // prologue (the copies were started before the previous update, see
+    // start_sweep_copies): S/T(0) formed; the empty product Y(-1) of step 0
+    // multiplies U = 0 with tile 0 copied into sKt3 (any finite operand would
+    // do)
+    #pragma unroll
+    for (int h = 0; h < 2; ++h)
+      #pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        ub[h][c] = static_cast<_Float16>(0.f);
+        ulb[h][c] = static_cast<_Float16>(0.f);
+      }
+    __syncthreads();
+    st_tile(sKr0, sa, ta);
+    __syncthreads();
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    static_assert(NW % 4 == 0, "the sweep is unrolled by four steps");
+    for (int j0 = 0; j0 < nsteps - NW; j0 += 4) {
+      pstep(I0{}, std::false_type{}, j0 + 0, sa, ta, sb, tb, ub, ulb, ua, ula);
+      pstep(I1{}, std::false_type{}, j0 + 1, sb, tb, sa, ta, ua, ula, ub, ulb);
+      pstep(I2{}, std::false_type{}, j0 + 2, sa, ta, sb, tb, ub, ulb, ua, ula);
+      pstep(I3{}, std::false_type{}, j0 + 3, sb, tb, sa, ta, ua, ula, ub, ulb);
+    }
+    for (int j0 = nsteps - NW; j0 < nsteps; j0 += 4) {
+      pstep(I0{}, std::true_type{}, j0 + 0, sa, ta, sb, tb, ub, ulb, ua, ula);
+      pstep(I1{}, std::true_type{}, j0 + 1, sb, tb, sa, ta, ua, ula, ub, ulb);
+      pstep(I2{}, std::true_type{}, j0 + 2, sa, ta, sb, tb, ub, ulb, ua, ula);
+      pstep(I3{}, std::true_type{}, j0 + 3, sb, tb, sa, ta, ua, ula, ub, ulb);
+    }
+    // Y += Kt^T U of the last tile (sKt3)
+    #pragma unroll
+    for (int k = 0; k < NY; ++k) {
+      const half8 f = kt_frag_at(sKt3, k >> 1, k & 1);
+      acc[k >> 1] = mfma(f, ub[k & 1], acc[k >> 1]);
+      if constexpr (SPLIT_U) acc[k >> 1] = mfma(f, ulb[k & 1], acc[k >> 1]);
+    }
     usum = pair_sum(usum);
+    // every wave is done with the tiles: start the next sweep's first copies
+    __syncthreads();
+    start_sweep_copies();
 
-    // CG step (registers only in this stretch): Sigma_c d = Y - (sum U) c +
-    // lambda d with c the fp16 kbar; exact line search along d; then the next
-    // direction p = r + beta sp d, renormalised and rounded to fp16.
-    float rv[NMB][16], ad[NMB][16];
+    // CG step: Sigma_c d = Y - (sum U) c + lambda d with c the fp16 kbar
+    // (recomputed where needed rather than kept); exact line search along d;
+    // then the next direction p = r + beta sp d, renormalised and rounded to
+    // fp16.
     float dAd = 0.f, rd = 0.f;
     #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) {
-      #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const floatx4 rc = sR[wave][mb * 4 + a][lane];
-        #pragma unroll
-        for (int b = 0; b < 4; ++b) rv[mb][4 * a + b] = rc[b];
-      }
+    for (int mb = 0; mb < NMB; ++mb)
       #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const half8 kb = sKb[wave][2 * mb + h][lane];
@@ -658,12 +856,10 @@ __global__ __launch_bounds__(NT) void lla_mfma_main(MainParams P) {
           const int r = 8 * h + c;
           const float dv = static_cast<float>(dop[2 * mb + h][c]);
           const float v = acc[mb][r] - usum * static_cast<float>(kb[c]) + lam_s * dv;
-          ad[mb][r] = v;
           dAd += dv * v;
-          rd += rv[mb][r] * dv;
+          rd += rv4[mb * 4 + (r >> 2)][r & 3] * dv;
         }
       }
-    }
     dAd = pair_sum(dAd);
     rd = pair_sum(rd);
     const bool step = active && dAd > 0.f;
@@ -672,27 +868,20 @@ __global__ __launch_bounds__(NT) void lla_mfma_main(MainParams P) {
     #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
       #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (step) rv[mb][r] -= al * ad[mb][r];
-        rrn += rv[mb][r] * rv[mb][r];
-      }
-    if (step) {
-      #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb)
+      for (int h = 0; h < 2; ++h) {
+        const half8 kb = sKb[wave][2 * mb + h][lane];
         #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          floatx4 xc = xs[(mb * 4 + a) * 64 + lane];
-          floatx4 rc;
-          #pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const int r = 4 * a + b;
-            xc[b] += al * static_cast<float>(dop[2 * mb + (r >> 3)][r & 7]);
-            rc[b] = rv[mb][r];
-          }
-          xs[(mb * 4 + a) * 64 + lane] = xc;
-          sR[wave][mb * 4 + a][lane] = rc;
+        for (int c = 0; c < 8; ++c) {
+          const int r = 8 * h + c;
+          const float dv = static_cast<float>(dop[2 * mb + h][c]);
+          const float v = acc[mb][r] - usum * static_cast<float>(kb[c]) + lam_s * dv;
+          // al = 0 leaves a stopped query's state as it is
+          const int ci = mb * 4 + (r >> 2), bi = r & 3;
+          rv4[ci][bi] = rv4[ci][bi] - al * v;
+          xv4[ci][bi] = xv4[ci][bi] + al * dv;
+          rrn += rv4[ci][bi] * rv4[ci][bi];
         }
-    }
+      }
     rrn = pair_sum(rrn);
     bool cont = false;
     if (step) {
@@ -706,7 +895,7 @@ __global__ __launch_bounds__(NT) void lla_mfma_main(MainParams P) {
     for (int mb = 0; mb < NMB; ++mb)
       #pragma unroll
       for (int r = 0; r < 16; ++r)
-        mx = fmaxf(mx, fabsf(rv[mb][r] + be * static_cast<float>(dop[2 * mb + (r >> 3)][r & 7])));
+        mx = fmaxf(mx, fabsf(rv4[mb * 4 + (r >> 2)][r & 3] + be * static_cast<float>(dop[2 * mb + (r >> 3)][r & 7])));
     const float sp_new = pow2_ceil(pair_max(mx));
     const float inv_sp = 1.f / sp_new;
     #pragma unroll
@@ -714,7 +903,7 @@ __global__ __launch_bounds__(NT) void lla_mfma_main(MainParams P) {
       #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int t = 2 * mb + (r >> 3), c = r & 7;
-        const float pv = rv[mb][r] + be * static_cast<float>(dop[t][c]);
+        const float pv = rv4[mb * 4 + (r >> 2)][r & 3] + be * static_cast<float>(dop[t][c]);
         if (cont) dop[t][c] = static_cast<_Float16>(pv * inv_sp);
       }
     if (cont) sp = sp_new;
@@ -722,9 +911,19 @@ __global__ __launch_bounds__(NT) void lla_mfma_main(MainParams P) {
     if (cont) kbd = kbdn;
     if (step) rr = rrn;
     active = cont;
+    park();
   }
+  __syncthreads();  // no tile copy may still be in flight when the kernel ends
+  #pragma unroll
+  for (int c = 0; c < NMB * 4; ++c) slab_st(xs, c, lane, xv4[c]);
 
+  if (qvalid && g == 0) {
+    if (P.cg_iters) P.cg_iters[orow] = iters;
+    if (P.cg_resid) P.cg_resid[orow] = r0n > 0.f ? sqrtf(rr) / r0n : 0.f;
+  }
+  } else {
   // ------------------------------ phase 3 ------------------------------
+  const float m2 = qst[lane];
   // rho' = x as two fp16 terms: x = srho (hi + lo)
   half8 rhi[NKS], rlo[NKS];
   float srho, kr_dot, inv_sA;
@@ -735,7 +934,7 @@ __global__ __launch_bounds__(NT) void lla_mfma_main(MainParams P) {
     for (int mb = 0; mb < NMB; ++mb)
       #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const floatx4 xc = xs[(mb * 4 + a) * 64 + lane];
+        const floatx4 xc = slab_ld(xs, mb * 4 + a, lane);
         #pragma unroll
         for (int b = 0; b < 4; ++b) {
           xv[mb][4 * a + b] = xc[b];
@@ -760,7 +959,7 @@ __global__ __launch_bounds__(NT) void lla_mfma_main(MainParams P) {
     for (int mb = 0; mb < NMB; ++mb)
       #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const floatx4 kb = kbs[(mb * 4 + a) * 64 + lane];
+        const floatx4 kb = slab_ld(kbs, mb * 4 + a, lane);
         #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const int r = 4 * a + b;
@@ -832,7 +1031,6 @@ __global__ __launch_bounds__(NT) void lla_mfma_main(MainParams P) {
   den = pair_sum(den);
 
   if (!qvalid) return;
-  const size_t orow = static_cast<size_t>(bh) * n + qi;
   const float ob = 1.f / (den * sv);
   #pragma unroll
   for (int mb = 0; mb < NMB; ++mb)
@@ -853,8 +1051,8 @@ __global__ __launch_bounds__(NT) void lla_mfma_main(MainParams P) {
     for (int mb = 0; mb < NMB; ++mb)
       #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const floatx4 kb = kbs[(mb * 4 + a) * 64 + lane];
-        const floatx4 xc = xs[(mb * 4 + a) * 64 + lane];
+        const floatx4 kb = slab_ld(kbs, mb * 4 + a, lane);
+        const floatx4 xc = slab_ld(xs, mb * 4 + a, lane);
         #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const int r = 4 * a + b;
@@ -870,17 +1068,12 @@ __global__ __launch_bounds__(NT) void lla_mfma_main(MainParams P) {
     for (int mb = 0; mb < NMB; ++mb)
       #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const floatx4 xc = xs[(mb * 4 + a) * 64 + lane];
+        const floatx4 xc = slab_ld(xs, mb * 4 + a, lane);
         const int dim = 32 * mb + 8 * a + 4 * g;
         *reinterpret_cast<float4*>(P.rho + orow * D + dim) =
             make_float4(xc[0] * rs, xc[1] * rs, xc[2] * rs, xc[3] * rs);
       }
   }
-  if (g == 0) {
-    if (P.omega) P.omega[orow] = om;
-    if (P.rowmax) P.rowmax[orow] = m2 * kLn2;
-    if (P.cg_iters) P.cg_iters[orow] = iters;
-    if (P.cg_resid) P.cg_resid[orow] = r0n > 0.f ? sqrtf(rr) / r0n : 0.f;
   }
 }
 
@@ -915,6 +1108,8 @@ hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
   m.vt = w.vt;
   m.xs = w.xs;
   m.kbs = w.kbs;
+  m.rs = w.rs;
+  m.qs = w.qs;
   m.BH = p.BH;
   m.n = n;
   m.nchunk = nchunk;
@@ -922,21 +1117,30 @@ hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
   m.lambda = p.lambda;
   m.cg_max_iters = p.cg_max_iters;
   m.cg_rel_tol = p.cg_rel_tol;
-  const long long blocks = static_cast<long long>((n + BQ - 1) / BQ) * p.BH;
+  m.nq32 = (n + kMaxBQ - 1) / kMaxBQ * (kMaxBQ / 32);
+  const dim3 grid1(static_cast<unsigned>(static_cast<long long>((n + 32 * kNW13 - 1) / (32 * kNW13)) * p.BH));
+  const dim3 grid2(static_cast<unsigned>(static_cast<long long>((n + 32 * kNW2 - 1) / (32 * kNW2)) * p.BH));
+  // three kernels, one per phase, sharing the block order and per-query state
+  // slabs: moments, conjugate gradient (timed by the optional events), output
+  hipLaunchKernelGGL((lla_mfma_phase<D, 1, false, kNW13>), grid1, dim3(64 * kNW13), 0, stream, m);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   if (p.ev_main_begin) {
     e = hipEventRecord(p.ev_main_begin, stream);
     if (e != hipSuccess) return e;
   }
   if (p.flags & LLA_FLAG_SPLIT_U)
-    hipLaunchKernelGGL((lla_mfma_main<D, true>), dim3(static_cast<unsigned>(blocks)), dim3(NT), 0,
-                       stream, m);
+    hipLaunchKernelGGL((lla_mfma_phase<D, 2, true, kNW2>), grid2, dim3(64 * kNW2), 0, stream, m);
   else
-    hipLaunchKernelGGL((lla_mfma_main<D, false>), dim3(static_cast<unsigned>(blocks)), dim3(NT), 0,
-                       stream, m);
+    hipLaunchKernelGGL((lla_mfma_phase<D, 2, false, kNW2>), grid2, dim3(64 * kNW2), 0, stream, m);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (p.ev_main_end) return hipEventRecord(p.ev_main_end, stream);
-  return hipSuccess;
+  if (p.ev_main_end) {
+    e = hipEventRecord(p.ev_main_end, stream);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((lla_mfma_phase<D, 3, false, kNW13>), grid1, dim3(64 * kNW13), 0, stream, m);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -946,10 +1150,11 @@ bool mfma_supported(int dtype, int d) { return dtype == LLA_DTYPE_BF16 && (d == 
 size_t mfma_workspace_bytes(int BH, int n, int d) {
   const int nchunk = (n + NORM_ROWS - 1) / NORM_ROWS;
   const size_t npad = static_cast<size_t>((n + BK - 1) / BK) * BK;
-  const size_t nqb = static_cast<size_t>((n + BQ - 1) / BQ);
+  const size_t nqpad = static_cast<size_t>((n + kMaxBQ - 1) / kMaxBQ) * kMaxBQ;
   return align256(static_cast<size_t>(BH) * nchunk * 2 * sizeof(float)) +
          3 * align256(static_cast<size_t>(BH) * npad * d * sizeof(_Float16)) +
-         2 * align256(static_cast<size_t>(BH) * nqb * BQ * d * sizeof(float));
+         3 * align256(static_cast<size_t>(BH) * nqpad * d * sizeof(float)) +
+         align256(static_cast<size_t>(BH) * nqpad * 4 * sizeof(float));
 }
 
 hipError_t launch_mfma(const FwdParams& p, hipStream_t stream) {
