@@ -109,8 +109,17 @@ __device__ __forceinline__ half2v pack_sum(float a, float b, float& acc) {
   return h;
 }
 
-__device__ __forceinline__ float pair_sum(float v) { return v + __shfl_xor(v, 32); }
-__device__ __forceinline__ float pair_max(float v) { return fmaxf(v, __shfl_xor(v, 32)); }
+// The two lanes l and l ^ 32 of a query combine their halves with one
+// v_permlane32_swap (no LDS round trip): it returns the lower half of v in
+// both halves of r[0] and the upper half in both halves of r[1].
+__device__ __forceinline__ float pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
 struct Workspace {
   float* partial;   // [BH][nchunk][2]: max row ||.||^2 of q and k; of v
@@ -389,6 +398,7 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
   __shared__ __align__(16) _Float16 sKt0[D * BK], sKt1[D * BK], sKt2[D * BK], sKt3[D * BK];
   __shared__ __align__(16) half8 sKb[NW][NKS][64];  // kbar, fp16, operand order
   __shared__ float sScale[2];
+  __shared__ int sFlag[NW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -698,7 +708,15 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
   };
   start_sweep_copies();
   for (int it = 0; it < P.cg_max_iters; ++it) {
-    if (!__syncthreads_or(active ? 1 : 0)) break;
+    // one barrier both publishes which waves still iterate and (its fence
+    // waits for this wave's copies) makes the sweep's first tiles visible
+    const bool wave_active = __any(active ? 1 : 0);
+    if (lane == 0) sFlag[wave] = wave_active ? 1 : 0;
+    __syncthreads();
+    int any_active = 0;
+    #pragma unroll
+    for (int w = 0; w < NW; ++w) any_active |= sFlag[w];
+    if (!any_active) break;
     #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
       #pragma unroll
@@ -809,7 +827,6 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
         ub[h][c] = static_cast<_Float16>(0.f);
         ulb[h][c] = static_cast<_Float16>(0.f);
       }
-    __syncthreads();
     st_tile(sKr0, sa, ta);
     __syncthreads();
     using I0 = std::integral_constant<int, 0>;
