@@ -48,9 +48,9 @@ def cg_flops(n: int, d: int, iters: np.ndarray) -> float:
 
 
 def measured_traffic(path: str):
-    """HBM bytes (calibrated FETCH_SIZE + WRITE_SIZE) of one launch of the main
-    kernel, from a rocprofv3 summary, or None when the summary is missing or was
-    taken on another version of the kernel source."""
+    """HBM bytes (calibrated FETCH_SIZE + WRITE_SIZE) of one launch of the
+    conjugate-gradient kernel, from a rocprofv3 summary, or None when the summary
+    is missing or was taken on another version of the kernel source."""
     import hashlib
     if not os.path.exists(path):
         return None
@@ -62,7 +62,7 @@ def measured_traffic(path: str):
         for line in f:
             if line.startswith("lla_mfma.hip sha256:"):
                 found_sha = line.split(":", 1)[1].strip()
-            elif line.startswith("bytes_per_launch lla_mfma_main:"):
+            elif line.startswith("bytes_per_launch cg_kernel:"):
                 value = float(line.split(":", 1)[1])
     return value if found_sha == sha else None
 
@@ -201,7 +201,7 @@ def main(argv=None):
     # the single fused kernel on the vector path
     achieved = (flops_cg if kernel_used == lla.LLA_KERNEL_MFMA else flops) / (kern_ms * 1e-3) / 1e12
     traffic = measured_traffic(args.traffic or os.path.join(
-        ROOT, "profiles", f"lla_mfma_main_{wl.name}_hbm_bytes.txt")) \
+        ROOT, "profiles", f"lla_cg_kernel_{wl.name}_hbm_bytes.txt")) \
         if kernel_used == lla.LLA_KERNEL_MFMA and not args.split_u else None
 
     if args.calib_copy_mb > 0:

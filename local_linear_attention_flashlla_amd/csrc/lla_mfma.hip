@@ -181,18 +181,24 @@ __global__ __launch_bounds__(NT) void prep_norms(const uint16_t* __restrict__ q,
                                                  const uint16_t* __restrict__ k,
                                                  const uint16_t* __restrict__ v, int n, int nchunk,
                                                  float* __restrict__ partial) {
+  // D / 8 consecutive lanes read one row (16 bytes each), so every wave
+  // instruction reads whole rows contiguously
+  constexpr int LPR = D / 8;               // lanes per row
+  constexpr int RPI = NT / LPR;            // rows per workgroup pass
   const int bh = blockIdx.x, chunk = blockIdx.y;
-  const int i = chunk * NORM_ROWS + threadIdx.x;
+  const int sub = threadIdx.x % LPR, rofs = threadIdx.x / LPR;
   float mqk = 0.f, mv = 0.f;
-  if (i < n) {
-    const size_t off = (static_cast<size_t>(bh) * n + i) * D;
+  for (int r0 = 0; r0 < NORM_ROWS; r0 += RPI) {
+    const int i = chunk * NORM_ROWS + r0 + rofs;
     float sq = 0.f, sk = 0.f, sw = 0.f;
-    for (int c = 0; c < D; c += 8) {
-      const uint4 a = *reinterpret_cast<const uint4*>(q + off + c);
-      const uint4 b = *reinterpret_cast<const uint4*>(k + off + c);
-      const uint4 e = *reinterpret_cast<const uint4*>(v + off + c);
+    if (i < n) {
+      const size_t off = (static_cast<size_t>(bh) * n + i) * D + sub * 8;
+      const uint4 a = *reinterpret_cast<const uint4*>(q + off);
+      const uint4 b = *reinterpret_cast<const uint4*>(k + off);
+      const uint4 e = *reinterpret_cast<const uint4*>(v + off);
       const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w},
                      ev[4] = {e.x, e.y, e.z, e.w};
+      #pragma unroll
       for (int u = 0; u < 4; ++u) {
         float x0 = bf16_to_f(av[u] & 0xffffu), x1 = bf16_to_f(av[u] >> 16);
         sq += x0 * x0 + x1 * x1;
@@ -202,8 +208,15 @@ __global__ __launch_bounds__(NT) void prep_norms(const uint16_t* __restrict__ q,
         sw += x0 * x0 + x1 * x1;
       }
     }
-    mqk = fmaxf(sq, sk);
-    mv = sw;
+    // the row's sums: add across its LPR lanes
+    #pragma unroll
+    for (int o = LPR / 2; o > 0; o >>= 1) {
+      sq += __shfl_xor(sq, o);
+      sk += __shfl_xor(sk, o);
+      sw += __shfl_xor(sw, o);
+    }
+    mqk = fmaxf(mqk, fmaxf(sq, sk));
+    mv = fmaxf(mv, sw);
   }
   for (int o = 32; o > 0; o >>= 1) {
     mqk = fmaxf(mqk, __shfl_xor(mqk, o));
