@@ -736,11 +736,16 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
       for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
     float usum = 0.f;
 
-    // S = K Q^T and K d^T for the key tile in `kbuf`
+    // S = K Q^T and T = K d^T - kbar.d for the key tile in `kbuf` (the shift
+    // enters as the accumulator's initial value, so U = w T needs one
+    // multiply per element)
+    floatx16 tinit;
+    #pragma unroll
+    for (int r = 0; r < 16; ++r) tinit[r] = -kbd;
     auto st_tile = [&](const _Float16* kbuf, floatx16& so, floatx16& to) __attribute__((always_inline)) {
       half8 kf = kr_frag_at(kbuf, 0);
       so = mfma(kf, qop[0], floatx16{});
-      to = mfma(kf, dop[0], floatx16{});
+      to = mfma(kf, dop[0], tinit);
       #pragma unroll
       for (int t = 1; t < NKS; ++t) {
         kf = kr_frag_at(kbuf, t);
@@ -802,7 +807,7 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
         } else {
           const int t = k - NY;
           sn = mfma(f, qop[t], t == 0 ? floatx16{} : sn);
-          tn = mfma(f, dop[t], t == 0 ? floatx16{} : tn);
+          tn = mfma(f, dop[t], t == 0 ? tinit : tn);
         }
         if (k + PF < NF) fr[k % PF] = frag(k + PF);
         #pragma unroll
@@ -812,7 +817,7 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
           if constexpr (decltype(masked)::value) {
             if (key_of(r) > lim) w = 0.f;
           }
-          uv[r] = w * (tc[r] - kbd);
+          uv[r] = w * tc[r];
           if (r & 1) {
             const half2v hu = pack_sum(uv[r - 1], uv[r], usum);
             uc[r >> 3][(r - 1) & 7] = hu[0];
