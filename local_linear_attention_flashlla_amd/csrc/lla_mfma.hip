@@ -109,6 +109,19 @@ __device__ __forceinline__ half2v pack_sum(float a, float b, float& acc) {
   return h;
 }
 
+// fp16(a0 b0), fp16(a1 b1) packed, their rounded values added to acc as in
+// pack_sum. v_fma_mixlo/mixhi_f16 form the fp32 product and round it to fp16
+// in one instruction each (the same rounding as a multiply then a convert).
+__device__ __forceinline__ half2v mul_pack_sum(float a0, float b0, float a1, float b1, float& acc) {
+  uint32_t u;
+  asm volatile("v_fma_mixlo_f16 %0, %1, %2, 0" : "=v"(u) : "v"(a0), "v"(b0));
+  asm volatile("v_fma_mixhi_f16 %0, %1, %2, 0" : "+v"(u) : "v"(a1), "v"(b1));
+  const half2v h = __builtin_bit_cast(half2v, u);
+  const half2v one = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
+  acc = __builtin_amdgcn_fdot2(h, one, acc, false);
+  return h;
+}
+
 // The two lanes l and l ^ 32 of a query combine their halves with one
 // v_permlane32_swap (no LDS round trip): it returns the lower half of v in
 // both halves of r[0] and the upper half in both halves of r[1].
@@ -435,7 +448,10 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
   if (tid == 0) head_scales(P.partial, bh, P.nchunk, &sScale[0], &sScale[1]);
   __syncthreads();
   const float s = sScale[0], sv = sScale[1];
-  const float c2s = kLog2e / sqrtf(static_cast<float>(D)) / (s * s);
+  // The Q operand carries log2(e) / sqrt(d) / s, so that with the s-scaled
+  // keys a score tile comes out of the matrix cores in log2 units (no
+  // per-element multiply before the exponential)
+  const float qsc = kLog2e / sqrtf(static_cast<float>(D)) / s;
   const float lam_s = P.lambda * s * s;
 
   // buffer resources over this head's key tiles (rows, transposed) and value tiles
@@ -445,10 +461,17 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
   const __amdgpu_buffer_rsrc_t kt_head = make_rsrc(P.kt + bh * head_elems, head_bytes);
   const __amdgpu_buffer_rsrc_t vt_head = make_rsrc(P.vt + bh * head_elems, head_bytes);
 
-  // Q operand of this lane's query: slot (t, c) holds s q[16 t + 8 (c >> 2) + 4 g + (c & 3)]
+  // Q operand of this lane's query: slot (t, c) holds qsc q[16 t + 8 (c >> 2) + 4 g + (c & 3)]
+  // (subnormal fp16 values included: the matrix cores do not flush them)
+  const uint16_t* qrow = P.q + (static_cast<size_t>(bh) * n + (qvalid ? qi : 0)) * D;
+  // s q at dims 32 mb + 8 a + 4 g + (0..3): the accumulator layout's slot (mb, 4 a + b)
+  auto q_acc = [&](int mb, int a) __attribute__((always_inline)) {
+    const uint2 w2 = *reinterpret_cast<const uint2*>(qrow + 32 * mb + 8 * a + 4 * g);
+    return floatx4{bf16_to_f(w2.x & 0xffffu) * s, bf16_to_f(w2.x >> 16) * s,
+                   bf16_to_f(w2.y & 0xffffu) * s, bf16_to_f(w2.y >> 16) * s};
+  };
   half8 qop[NKS];
   {
-    const uint16_t* qrow = P.q + (static_cast<size_t>(bh) * n + (qvalid ? qi : 0)) * D;
     #pragma unroll
     for (int t = 0; t < NKS; ++t) {
       const uint2 lo = *reinterpret_cast<const uint2*>(qrow + 16 * t + 4 * g);
@@ -456,8 +479,8 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
       const uint32_t w4[4] = {lo.x, lo.y, hi.x, hi.y};
       #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const float a = qvalid ? bf16_to_f(w4[u] & 0xffffu) * s : 0.f;
-        const float b = qvalid ? bf16_to_f(w4[u] >> 16) * s : 0.f;
+        const float a = qvalid ? bf16_to_f(w4[u] & 0xffffu) * qsc : 0.f;
+        const float b = qvalid ? bf16_to_f(w4[u] >> 16) * qsc : 0.f;
         qop[t][2 * u] = static_cast<_Float16>(a);
         qop[t][2 * u + 1] = static_cast<_Float16>(b);
       }
@@ -547,7 +570,7 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
       float tmax = -INFINITY;
       #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float x = sacc[r] * c2s;
+        float x = sacc[r];
         if constexpr (decltype(masked)::value) {
           if (key_of(r) > lim) x = -INFINITY;
         }
@@ -594,13 +617,12 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
       #pragma unroll
       for (int a = 0; a < 4; ++a) {
         floatx4 kb, rc;
+        const floatx4 qv = q_acc(mb, a);
         #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          const int r = 4 * a + b;
-          const float mt = acc[mb][r];
-          const float qv = static_cast<float>(qop[2 * mb + (r >> 3)][r & 7]);
+          const float mt = acc[mb][4 * a + b];
           kb[b] = mt * inv_om;
-          rc[b] = qvalid ? mt - om * qv : 0.f;
+          rc[b] = qvalid ? mt - om * qv[b] : 0.f;
         }
         slab_st(kbs, mb * 4 + a, lane, kb);
         slab_st(xs, mb * 4 + a, lane, floatx4{0.f, 0.f, 0.f, 0.f});
@@ -736,15 +758,18 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
       for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
     float usum = 0.f;
 
-    // S = K Q^T and T = K d^T - kbar.d for the key tile in `kbuf` (the shift
-    // enters as the accumulator's initial value, so U = w T needs one
-    // multiply per element)
-    floatx16 tinit;
+    // S = K Q^T - m2 (log2 units) and T = K d^T - kbar.d for the key tile in
+    // `kbuf`; both shifts enter as the accumulators' initial values, so
+    // U = exp2(S) T needs an exponential and a multiply per element
+    floatx16 sinit, tinit;
     #pragma unroll
-    for (int r = 0; r < 16; ++r) tinit[r] = -kbd;
+    for (int r = 0; r < 16; ++r) {
+      sinit[r] = -m2;
+      tinit[r] = -kbd;
+    }
     auto st_tile = [&](const _Float16* kbuf, floatx16& so, floatx16& to) __attribute__((always_inline)) {
       half8 kf = kr_frag_at(kbuf, 0);
-      so = mfma(kf, qop[0], floatx16{});
+      so = mfma(kf, qop[0], sinit);
       to = mfma(kf, dop[0], tinit);
       #pragma unroll
       for (int t = 1; t < NKS; ++t) {
@@ -796,7 +821,7 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
       #pragma unroll
       for (int k = 0; k < PF; ++k) fr[k] = frag(k);
       const int lim = kmax - j * BK;  // keys <= lim are visible
-      float uv[16];
+      float wv[16];
       __builtin_amdgcn_sched_barrier(0);
       #pragma unroll
       for (int k = 0; k < NF; ++k) {
@@ -806,27 +831,31 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
           if constexpr (SPLIT_U) acc[k % NMB] = mfma(f, ulp[k / NMB], acc[k % NMB]);
         } else {
           const int t = k - NY;
-          sn = mfma(f, qop[t], t == 0 ? floatx16{} : sn);
+          sn = mfma(f, qop[t], t == 0 ? sinit : sn);
           tn = mfma(f, dop[t], t == 0 ? tinit : tn);
         }
         if (k + PF < NF) fr[k % PF] = frag(k + PF);
         #pragma unroll
         for (int e = 0; e < EPS; ++e) {
           const int r = k * EPS + e;
-          float w = fast_exp2(fmaf(sc[r], c2s, -m2));
+          float w = fast_exp2(sc[r]);
           if constexpr (decltype(masked)::value) {
             if (key_of(r) > lim) w = 0.f;
           }
-          uv[r] = w * tc[r];
+          wv[r] = w;
           if (r & 1) {
-            const half2v hu = pack_sum(uv[r - 1], uv[r], usum);
-            uc[r >> 3][(r - 1) & 7] = hu[0];
-            uc[r >> 3][r & 7] = hu[1];
             if constexpr (SPLIT_U) {
-              const half2v lo = pack_sum(uv[r - 1] - static_cast<float>(hu[0]),
-                                         uv[r] - static_cast<float>(hu[1]), usum);
+              const float u0 = wv[r - 1] * tc[r - 1], u1 = w * tc[r];
+              const half2v hu = pack_sum(u0, u1, usum);
+              const half2v lo = pack_sum(u0 - static_cast<float>(hu[0]), u1 - static_cast<float>(hu[1]), usum);
+              uc[r >> 3][(r - 1) & 7] = hu[0];
+              uc[r >> 3][r & 7] = hu[1];
               ulc[r >> 3][(r - 1) & 7] = lo[0];
               ulc[r >> 3][r & 7] = lo[1];
+            } else {
+              const half2v hu = mul_pack_sum(wv[r - 1], tc[r - 1], w, tc[r], usum);
+              uc[r >> 3][(r - 1) & 7] = hu[0];
+              uc[r >> 3][r & 7] = hu[1];
             }
           }
         }
@@ -1012,6 +1041,9 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
   floatx16 rinit;
   #pragma unroll
   for (int r = 0; r < 16; ++r) rinit[r] = -kr_dot / srho;
+  floatx16 sinit;
+  #pragma unroll
+  for (int r = 0; r < 16; ++r) sinit[r] = -m2;
   #pragma unroll
   for (int mb = 0; mb < NMB; ++mb)
     #pragma unroll
@@ -1025,9 +1057,10 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
     for (int mb = 0; mb < NMB; ++mb)
       #pragma unroll
       for (int h = 0; h < 2; ++h) tf[2 * mb + h] = kt_frag(buf, mb, h);
-    // S = K Q^T; R = K (hi + lo)^T - kbar.rho' / srho, the shift entering as
-    // the accumulator's initial value; then a = w (1 - srho R) / sA
-    floatx16 sacc = mfma(kf[0], qop[0], floatx16{});
+    // S = K Q^T - m2 (log2 units); R = K (hi + lo)^T - kbar.rho' / srho, the
+    // shifts entering as the accumulators' initial values; then
+    // a = exp2(S) (1 - srho R) / sA
+    floatx16 sacc = mfma(kf[0], qop[0], sinit);
     floatx16 racc = mfma(kf[0], rhi[0], rinit);
     racc = mfma(kf[0], rlo[0], racc);
     #pragma unroll
@@ -1041,15 +1074,14 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
     auto body = [&](auto masked) __attribute__((always_inline)) {
       #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        float w0 = fast_exp2(fmaf(sacc[r], c2s, -m2));
-        float w1 = fast_exp2(fmaf(sacc[r + 1], c2s, -m2));
+        float w0 = fast_exp2(sacc[r]);
+        float w1 = fast_exp2(sacc[r + 1]);
         if constexpr (decltype(masked)::value) {
           if (key_of(r) > lim) w0 = 0.f;
           if (key_of(r + 1) > lim) w1 = 0.f;
         }
-        const float a0 = w0 * fmaf(racc[r], a_slope, inv_sA);
-        const float a1 = w1 * fmaf(racc[r + 1], a_slope, inv_sA);
-        const half2v ha = pack_sum(a0, a1, den);
+        const half2v ha = mul_pack_sum(w0, fmaf(racc[r], a_slope, inv_sA), w1,
+                                       fmaf(racc[r + 1], a_slope, inv_sA), den);
         ab[r >> 3][r & 7] = ha[0];
         ab[r >> 3][(r & 7) + 1] = ha[1];
       }
@@ -1088,10 +1120,10 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
       for (int a = 0; a < 4; ++a) {
         const floatx4 kb = slab_ld(kbs, mb * 4 + a, lane);
         const floatx4 xc = slab_ld(xs, mb * 4 + a, lane);
+        const floatx4 qv = q_acc(mb, a);
         #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          const int r = 4 * a + b;
-          qx += static_cast<float>(qop[2 * mb + (r >> 3)][r & 7]) * xc[b];
+          qx += qv[b] * xc[b];
           kx += kb[b] * xc[b];
         }
       }
