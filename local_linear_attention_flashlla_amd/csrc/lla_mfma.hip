@@ -364,6 +364,17 @@ __device__ __forceinline__ void load_kr_to_lds(__amdgpu_buffer_rsrc_t head, int 
           inst * 1024 + lane * 16, tile_off, 0, 0);
   }
 }
+// Copy instruction u (of ceil(D/16 / NW)) of this wave's share of a tile.
+template <int D, int NW>
+__device__ __forceinline__ void load_chunk_to_lds(__amdgpu_buffer_rsrc_t head, int kt, _Float16* buf,
+                                                  int wave, int lane, int u) {
+  constexpr int NI = D / 16;
+  const int inst = u * NW + wave;
+  if (NI % NW == 0 || inst < NI)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        head, (__attribute__((address_space(3))) void*)(buf + inst * 512), 16,
+        inst * 1024 + lane * 16, kt * (BK * D * 2), 0, 0);
+}
 template <int D, int NW>
 __device__ __forceinline__ void load_kt_to_lds(__amdgpu_buffer_rsrc_t head, int kt, _Float16* buf,
                                                int wave, int lane) {
@@ -810,8 +821,21 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
       constexpr int jm = decltype(JM)::value;
       const _Float16* kbn = KR(std::integral_constant<int, jm + 1>{});
       const _Float16* tbp = KT(std::integral_constant<int, jm + 3>{});
-      load_kr_to_lds<D, NW>(kr_head, min(j + 4, tlast), KR(std::integral_constant<int, jm>{}), wave, lane);
-      load_kt_to_lds<D, NW>(kt_head, min(j + 2, tlast), KT(std::integral_constant<int, jm + 2>{}), wave, lane);
+      // this step's copies (rows of tile j + 4, transposed tile j + 2), spread
+      // over the step so that their LDS writes do not arrive in one burst
+      constexpr int NCP = (D / 16 + NW - 1) / NW;  // copy instructions per tile and wave
+      const int tr = min(j + 4, tlast), tt = min(j + 2, tlast);
+      auto copy_at = [&](int k) __attribute__((always_inline)) {
+        #pragma unroll
+        for (int u = 0; u < 2 * NCP; ++u)
+          if (k == u * NF / (2 * NCP)) {
+            if (u < NCP)
+              load_chunk_to_lds<D, NW>(kr_head, tr, KR(std::integral_constant<int, jm>{}), wave, lane, u);
+            else
+              load_chunk_to_lds<D, NW>(kt_head, tt, KT(std::integral_constant<int, jm + 2>{}), wave, lane,
+                                       u - NCP);
+          }
+      };
       auto frag = [&](int k) __attribute__((always_inline)) {
         // Y products cycle through the accumulators (no two dependent MFMAs
         // back to back): product k uses row block k % NMB and key half k / NMB
@@ -825,6 +849,7 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
       __builtin_amdgcn_sched_barrier(0);
       #pragma unroll
       for (int k = 0; k < NF; ++k) {
+        copy_at(k);
         const half8 f = fr[k % PF];
         if (k < NY) {
           acc[k % NMB] = mfma(f, up[k / NMB], acc[k % NMB]);
