@@ -388,20 +388,22 @@ __device__ __forceinline__ void load_tile_to_lds(__amdgpu_buffer_rsrc_t kr_head,
   load_kt_to_lds<D, NW>(t_head, kt, sKt, wave, lane);
 }
 
-// End of a step of the pipelined CG sweep: wait until at most the copies of
-// the last two steps (rows and transposed tile, ceil(D/16 / NW) instructions
-// each per wave) are still in flight, i.e. this wave's copies of two steps
-// ago have landed, and all LDS reads of this step are done; then a barrier,
-// after which every wave's copies of two steps ago are visible. The asm
-// statement is also a compiler memory barrier: no memory access moves across.
-template <int D, int NW>
+// End of a step of a pipelined sweep: wait until at most the copies of the
+// last two steps (NS tiles per step, ceil(D/16 / NW) instructions each per
+// wave) are still in flight, i.e. this wave's copies of two steps ago have
+// landed, and all LDS reads of this step are done; then a barrier, after
+// which every wave's copies of two steps ago are visible. The asm statement
+// is also a compiler memory barrier: no memory access moves across.
+template <int D, int NW, int NS = 2>
 __device__ __forceinline__ void step_barrier() {
-  constexpr int per_step = 2 * ((D / 16 + NW - 1) / NW);
-  static_assert(per_step == 2 || per_step == 4, "vmcnt below assumes 1 or 2 copies per tile");
+  constexpr int per_step = NS * ((D / 16 + NW - 1) / NW);
+  static_assert(per_step == 1 || per_step == 2 || per_step == 4, "vmcnt below");
   if constexpr (per_step == 4)
     asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else
+  else if constexpr (per_step == 2)
     asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Work order. Workgroups are handed to the eight XCDs (each with its own L2)
@@ -428,9 +430,9 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
   constexpr int NKS = D / 16;  // k-steps over d
   constexpr int NMB = D / 32;  // 32-row blocks over d
   constexpr int BQW = 32 * NW; // queries per workgroup (32 per wave)
-  // key tiles: in the CG sweep tile t lives in sKr<t % 4> (rows) and
-  // sKt<t % 4> (transposed); separate arrays so that every buffer choice there
-  // is static. The other sweeps double-buffer through buffers 0 and 1.
+  // key tiles: in every sweep tile t lives in sKr<t % 4> (rows) and
+  // sKt<t % 4> (transposed keys, or values in the output phase); separate
+  // arrays so that every buffer choice is static.
   __shared__ __align__(16) _Float16 sKr0[BK * D], sKr1[BK * D], sKr2[BK * D], sKr3[BK * D];
   __shared__ __align__(16) _Float16 sKt0[D * BK], sKt1[D * BK], sKt2[D * BK], sKt3[D * BK];
   __shared__ __align__(16) half8 sKb[NW][NKS][64];  // kbar, fp16, operand order
@@ -498,31 +500,12 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
     }
   }
 
-  // The key sweep: tiles 0 .. ntiles-1 of this head, double-buffered through
-  // LDS; `tile(kt, buf)` runs on the waves whose queries see tile kt.
-  auto krbuf = [&](int buf) __attribute__((always_inline)) { return buf ? sKr1 : sKr0; };
-  auto ktbuf = [&](int buf) __attribute__((always_inline)) { return buf ? sKt1 : sKt0; };
-  auto sweep = [&](__amdgpu_buffer_rsrc_t t_head, auto&& tile, bool wave_busy) __attribute__((always_inline)) {
-    load_tile_to_lds<D, NW>(kr_head, t_head, 0, sKr0, sKt0, wave, lane);
-    __syncthreads();
-    for (int kt = 0; kt < ntiles; ++kt) {
-      const int buf = kt & 1;
-      if (kt + 1 < ntiles) load_tile_to_lds<D, NW>(kr_head, t_head, kt + 1, krbuf(buf ^ 1), ktbuf(buf ^ 1), wave, lane);
-      if (wave_busy && kt <= wlast) tile(kt, buf);
-      __syncthreads();
-    }
-  };
-
   // this lane's operand fragments in the LDS tiles
   auto kr_frag_at = [&](const _Float16* b, int t) __attribute__((always_inline)) {
     return *reinterpret_cast<const half8*>(b + ((2 * t + g) * BK + ql) * 8);
   };
   auto kt_frag_at = [&](const _Float16* b, int mb, int h) __attribute__((always_inline)) {
     return *reinterpret_cast<const half8*>(b + ((2 * h + g) * D + 32 * mb + ql) * 8);
-  };
-  auto kr_frag = [&](int buf, int t) __attribute__((always_inline)) { return kr_frag_at(krbuf(buf), t); };
-  auto kt_frag = [&](int buf, int mb, int h) __attribute__((always_inline)) {
-    return kt_frag_at(ktbuf(buf), mb, h);
   };
   // static buffer choice for the CG sweep
   auto KR = [&](auto I) __attribute__((always_inline)) -> _Float16* {
@@ -559,65 +542,200 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
     #pragma unroll
     for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
 
+  // --------- pipelined sweeps of the moment and output phases ---------
+  // Step j of a sweep over the block's tiles 0 .. NW (qb + 1) - 1, all waves
+  // in lockstep: copy the rows of tile j + 4 (and, for a sweep with a second
+  // operand, its transposed or value tile j + 2) into the static buffers,
+  // spread over the step; the "back" products of tile j - 1 with the second
+  // operand; the "front" products of tile j + 1 with the rows; the vector work
+  // of tile j, independent of both. Tile t sits in sKr<t % 4> / sKt<t % 4>.
+  // The last NW tiles hold the block's diagonal: there keys past a query are
+  // masked, and a wave skips the products and vector work of tiles past its
+  // last query (tiles past the end of the head are clamped copies of its last
+  // tile, masked out entirely).
+  constexpr int NCP = (D / 16 + NW - 1) / NW;  // copy instructions per tile and wave
+  const int ps_steps = NW * (qb + 1);
+  const int ps_tlast = ntiles - 1;
+  auto ps_start_copies = [&](auto WITH_T, __amdgpu_buffer_rsrc_t t_head) __attribute__((always_inline)) {
+    load_kr_to_lds<D, NW>(kr_head, 0, sKr0, wave, lane);
+    load_kr_to_lds<D, NW>(kr_head, min(1, ps_tlast), sKr1, wave, lane);
+    load_kr_to_lds<D, NW>(kr_head, min(2, ps_tlast), sKr2, wave, lane);
+    load_kr_to_lds<D, NW>(kr_head, min(3, ps_tlast), sKr3, wave, lane);
+    if constexpr (decltype(WITH_T)::value) {
+      load_kt_to_lds<D, NW>(t_head, 0, sKt0, wave, lane);
+      load_kt_to_lds<D, NW>(t_head, min(1, ps_tlast), sKt1, wave, lane);
+      load_kt_to_lds<D, NW>(t_head, 0, sKt3, wave, lane);  // for the empty product of step 0
+    }
+  };
+  // copy instruction u of step j (rows for u < NCP, then the second operand)
+  auto ps_copy = [&](auto JM, __amdgpu_buffer_rsrc_t t_head, int j, int u) __attribute__((always_inline)) {
+    constexpr int jm = decltype(JM)::value;
+    if (u < NCP)
+      load_chunk_to_lds<D, NW>(kr_head, min(j + 4, ps_tlast), KR(std::integral_constant<int, jm>{}), wave,
+                               lane, u);
+    else
+      load_chunk_to_lds<D, NW>(t_head, min(j + 2, ps_tlast), KT(std::integral_constant<int, jm + 2>{}),
+                               wave, lane, u - NCP);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  static_assert(NW % 4 == 0, "the pipelined sweeps are unrolled by four steps");
+
   if constexpr (PHASE == 1) {
   // ------------------------------ phase 1 ------------------------------
-  float m2 = -INFINITY;  // running row max of the log2-scaled scores
-  float om = 0.f;        // partial row sum (this half of the keys)
-  sweep(kt_head, [&](int kt, int buf) __attribute__((always_inline)) {
-    half8 kf[NKS], tf[2 * NMB];
+  // One pipelined sweep accumulates omega = sum_j w_j and mu~ = sum_j w_j k_j
+  // with w_j = exp2(S_j - mref) against a reference mref: the max of the first
+  // tile, raised (and the sums rescaled) only when a score would exceed it by
+  // more than 2^15 in weight, which fp16 still holds. The exact row max m2 is
+  // tracked alongside; at the end both sums are scaled by exp2(mref - m2),
+  // which gives the max-normalised moments.
+  constexpr int NY = 2 * NMB, NF = NY + NKS, PF = 4;
+  constexpr int EH = 32 / NF;  // elements per stage: max in the first half, weights in the second
+  static_assert(NY == NKS && EH * NF == 32, "vector work must spread evenly");
+  constexpr float kHead = 15.f;  // log2 of the largest weight allowed against mref
+  float om = 0.f;      // row sum of the fp16 weights (this lane's half of the keys)
+  float mref, m2;      // reference, exact running max (log2 units)
+  ps_start_copies(std::true_type{}, kt_head);
+  __syncthreads();
+  floatx16 sa, sb;
+  {
+    half8 kf = kr_frag_at(sKr0, 0);
+    sa = mfma(kf, qop[0], floatx16{});
     #pragma unroll
-    for (int t = 0; t < NKS; ++t) kf[t] = kr_frag(buf, t);
+    for (int t = 1; t < NKS; ++t) {
+      kf = kr_frag_at(sKr0, t);
+      sa = mfma(kf, qop[t], sa);
+    }
+    // mref = max of the first tile (every query of the block sees some of it)
+    float mx = -INFINITY;
     #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
-      #pragma unroll
-      for (int h = 0; h < 2; ++h) tf[2 * mb + h] = kt_frag(buf, mb, h);
-    floatx16 sacc = mfma(kf[0], qop[0], floatx16{});
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, key_of(r) > kmax ? -INFINITY : sa[r]);
+    mx = pair_max(mx);
+    mref = (mx == -INFINITY) ? 0.f : mx;  // (only a query past the end sees no key)
+    m2 = mref;
     #pragma unroll
-    for (int t = 1; t < NKS; ++t) sacc = mfma(kf[t], qop[t], sacc);
-    const int lim = kmax - kt * BK;  // keys <= lim are visible
-    half8 wb[2];
-    auto body = [&](auto masked) __attribute__((always_inline)) {
-      float sc[16];
-      float tmax = -INFINITY;
-      #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = sacc[r];
-        if constexpr (decltype(masked)::value) {
-          if (key_of(r) > lim) x = -INFINITY;
-        }
-        sc[r] = x;
-        tmax = fmaxf(tmax, x);
-      }
-      tmax = pair_max(tmax);
-      const float mnew = fmaxf(m2, tmax);
-      // a query with every key so far masked (only queries past the end) keeps
-      // its running max at -inf; then nothing is accumulated for it
-      const float mref = (mnew == -INFINITY) ? 0.f : mnew;
-      const float alpha = fast_exp2(m2 - mref);
-      float wsum = 0.f;
-      #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const half2v hw = pack_sum(fast_exp2(sc[r] - mref), fast_exp2(sc[r + 1] - mref), wsum);
-        wb[r >> 3][r & 7] = hw[0];
-        wb[r >> 3][(r & 7) + 1] = hw[1];
-      }
-      om = om * alpha + wsum;
-      m2 = mnew;
-      if (alpha != 1.f)
-        #pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) acc[mb] *= alpha;
+    for (int r = 0; r < 16; ++r) sa[r] -= mref;
+  }
+  floatx16 sinit;  // -mref, the initial value of the score accumulators
+  #pragma unroll
+  for (int r = 0; r < 16; ++r) sinit[r] = -mref;
+  half8 wa[2], wb[2];
+  #pragma unroll
+  for (int h = 0; h < 2; ++h)
+    #pragma unroll
+    for (int c = 0; c < 8; ++c) wb[h][c] = static_cast<_Float16>(0.f);
+  // step j: Y += Kt(j-1) W(j-1); S(j+1) - mref; the max of S(j) over the first
+  // half of the step, then (rarely) a new reference, then W(j) = exp2(S(j) - mref)
+  auto wstep = [&](auto JM, auto masked, int j, floatx16& sc, floatx16& sn, const half8 (&up)[2],
+                   half8 (&uc)[2]) __attribute__((always_inline)) {
+    constexpr int jm = decltype(JM)::value;
+    constexpr bool MASKED = decltype(masked)::value;
+    const _Float16* kbn = KR(std::integral_constant<int, jm + 1>{});
+    const _Float16* tbp = KT(std::integral_constant<int, jm + 3>{});
+    const bool doY = !MASKED || j - 1 <= wlast;
+    const bool doF = !MASKED || j + 1 <= wlast;
+    const bool doV = !MASKED || j <= wlast;
+    const int lim = kmax - j * BK;
+    auto frag = [&](int k) __attribute__((always_inline)) {
+      return k < NY ? kt_frag_at(tbp, k % NMB, k / NMB) : kr_frag_at(kbn, k - NY);
     };
-    if (wave_full && kt < wlast)
-      body(std::false_type{});
-    else
-      body(std::true_type{});
+    half8 fr[PF];
     #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
+    for (int k = 0; k < PF; ++k) fr[k] = frag(k);
+    float tm = -INFINITY, wv[16];
+    __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+    for (int k = 0; k < NF; ++k) {
       #pragma unroll
-      for (int h = 0; h < 2; ++h) acc[mb] = mfma(tf[2 * mb + h], wb[h], acc[mb]);
-  }, wave_any);
+      for (int u = 0; u < 2 * NCP; ++u)
+        if (k == u * NF / (2 * NCP)) ps_copy(JM, kt_head, j, u);
+      if (k == NY && doV) {
+        // the Y products of this step are issued: a new reference may rescale
+        // the sums (and the scores of tile j + 1 have not been started)
+        tm = pair_max(tm);
+        m2 = fmaxf(m2, tm + mref);
+        const bool lift = tm > kHead;
+        if (__any(lift ? 1 : 0)) {
+          const float nref = lift ? mref + tm : mref;
+          const float alpha = fast_exp2(mref - nref);
+          #pragma unroll
+          for (int mb = 0; mb < NMB; ++mb) acc[mb] *= alpha;
+          om *= alpha;
+          #pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            sc[r] -= nref - mref;
+            sinit[r] = -nref;
+          }
+          mref = nref;
+        }
+      }
+      const half8 f = fr[k % PF];
+      if (k < NY) {
+        if (doY) acc[k % NMB] = mfma(f, up[k / NMB], acc[k % NMB]);
+      } else {
+        const int t = k - NY;
+        if (doF) {
+          sn = mfma(f, qop[t], t == 0 ? sinit : sn);
+        }
+      }
+      if (k + PF < NF) fr[k % PF] = frag(k + PF);
+      if (doV) {
+        #pragma unroll
+        for (int e = 0; e < EH; ++e) {
+          if (k < NY) {
+            const int r = k * EH + e;
+            float x = sc[r];
+            if constexpr (MASKED) {
+              if (key_of(r) > lim) x = -INFINITY;
+            }
+            tm = fmaxf(tm, x);
+          } else {
+            const int r = (k - NY) * EH + e;
+            float w = fast_exp2(sc[r]);
+            if constexpr (MASKED) {
+              if (key_of(r) > lim) w = 0.f;
+            }
+            wv[r] = w;
+            if (r & 1) {
+              const half2v hw = pack_sum(wv[r - 1], w, om);
+              uc[r >> 3][(r - 1) & 7] = hw[0];
+              uc[r >> 3][r & 7] = hw[1];
+            }
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    step_barrier<D, NW, 2>();
+  };
+  for (int j0 = 0; j0 < ps_steps - NW; j0 += 4) {
+    wstep(I0{}, std::false_type{}, j0 + 0, sa, sb, wb, wa);
+    wstep(I1{}, std::false_type{}, j0 + 1, sb, sa, wa, wb);
+    wstep(I2{}, std::false_type{}, j0 + 2, sa, sb, wb, wa);
+    wstep(I3{}, std::false_type{}, j0 + 3, sb, sa, wa, wb);
+  }
+  for (int j0 = ps_steps - NW; j0 < ps_steps; j0 += 4) {
+    wstep(I0{}, std::true_type{}, j0 + 0, sa, sb, wb, wa);
+    wstep(I1{}, std::true_type{}, j0 + 1, sb, sa, wa, wb);
+    wstep(I2{}, std::true_type{}, j0 + 2, sa, sb, wb, wa);
+    wstep(I3{}, std::true_type{}, j0 + 3, sb, sa, wa, wb);
+  }
+  // Y += Kt^T W of the last tile (sKt3)
+  if (ps_steps - 1 <= wlast) {
+    #pragma unroll
+    for (int k = 0; k < NY; ++k) acc[k % NMB] = mfma(kt_frag_at(sKt3, k % NMB, k / NMB), wb[k / NMB], acc[k % NMB]);
+  }
+  __syncthreads();  // no tile copy may still be in flight when the kernel ends
+  {
+    // moments against the exact max
+    const float beta = fast_exp2(mref - m2);
+    #pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) acc[mb] *= beta;
+    om *= beta;
+  }
   om = pair_sum(om);
-  if (!qvalid) m2 = 0.f;
 
   // Per query: kbar = mu~ / omega, r0 = mu = mu~ - omega q, x0 = 0, into the
   // lane-contiguous workspace slabs; the row max and omega into the state slab.
@@ -901,11 +1019,6 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
       }
     st_tile(sKr0, sa, ta);
     __syncthreads();
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    using I3 = std::integral_constant<int, 3>;
-    static_assert(NW % 4 == 0, "the sweep is unrolled by four steps");
     for (int j0 = 0; j0 < nsteps - NW; j0 += 4) {
       pstep(I0{}, std::false_type{}, j0 + 0, sa, ta, sb, tb, ub, ulb, ua, ula);
       pstep(I1{}, std::false_type{}, j0 + 1, sb, tb, sa, ta, ua, ula, ub, ulb);
@@ -1074,52 +1187,106 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
     #pragma unroll
     for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
   float den = 0.f;
-  sweep(vt_head, [&](int kt, int buf) __attribute__((always_inline)) {
-    half8 kf[NKS], tf[2 * NMB];
-    #pragma unroll
-    for (int t = 0; t < NKS; ++t) kf[t] = kr_frag(buf, t);
-    #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
+  {
+    // Y += Vt(j-1) A(j-1); [S - m2; R](j+1); A(j) = exp2(S(j)) (1 - srho R(j)) / sA
+    constexpr int NY = 2 * NMB, NF = NY + NKS, PF = 4, EPS = 16 / NF;
+    static_assert(NF * EPS == 16, "vector work must spread evenly");
+    ps_start_copies(std::true_type{}, vt_head);
+    __syncthreads();
+    floatx16 sa, ra, sb, rb;
+    {
+      half8 kf = kr_frag_at(sKr0, 0);
+      sa = mfma(kf, qop[0], sinit);
+      ra = mfma(kf, rhi[0], rinit);
+      ra = mfma(kf, rlo[0], ra);
       #pragma unroll
-      for (int h = 0; h < 2; ++h) tf[2 * mb + h] = kt_frag(buf, mb, h);
-    // S = K Q^T - m2 (log2 units); R = K (hi + lo)^T - kbar.rho' / srho, the
-    // shifts entering as the accumulators' initial values; then
-    // a = exp2(S) (1 - srho R) / sA
-    floatx16 sacc = mfma(kf[0], qop[0], sinit);
-    floatx16 racc = mfma(kf[0], rhi[0], rinit);
-    racc = mfma(kf[0], rlo[0], racc);
-    #pragma unroll
-    for (int t = 1; t < NKS; ++t) {
-      sacc = mfma(kf[t], qop[t], sacc);
-      racc = mfma(kf[t], rhi[t], racc);
-      racc = mfma(kf[t], rlo[t], racc);
-    }
-    const int lim = kmax - kt * BK;
-    half8 ab[2];
-    auto body = [&](auto masked) __attribute__((always_inline)) {
-      #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float w0 = fast_exp2(sacc[r]);
-        float w1 = fast_exp2(sacc[r + 1]);
-        if constexpr (decltype(masked)::value) {
-          if (key_of(r) > lim) w0 = 0.f;
-          if (key_of(r + 1) > lim) w1 = 0.f;
-        }
-        const half2v ha = mul_pack_sum(w0, fmaf(racc[r], a_slope, inv_sA), w1,
-                                       fmaf(racc[r + 1], a_slope, inv_sA), den);
-        ab[r >> 3][r & 7] = ha[0];
-        ab[r >> 3][(r & 7) + 1] = ha[1];
+      for (int t = 1; t < NKS; ++t) {
+        kf = kr_frag_at(sKr0, t);
+        sa = mfma(kf, qop[t], sa);
+        ra = mfma(kf, rhi[t], ra);
+        ra = mfma(kf, rlo[t], ra);
       }
-    };
-    if (wave_full && kt < wlast)
-      body(std::false_type{});
-    else
-      body(std::true_type{});
+    }
+    half8 aa[2], ab[2];
     #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
+    for (int h = 0; h < 2; ++h)
       #pragma unroll
-      for (int h = 0; h < 2; ++h) acc[mb] = mfma(tf[2 * mb + h], ab[h], acc[mb]);
-  }, wave_any);
+      for (int c = 0; c < 8; ++c) ab[h][c] = static_cast<_Float16>(0.f);
+    auto ostep = [&](auto JM, auto masked, int j, const floatx16& sc, const floatx16& rc, floatx16& sn,
+                     floatx16& rn, const half8 (&up)[2], half8 (&uc)[2]) __attribute__((always_inline)) {
+      constexpr int jm = decltype(JM)::value;
+      constexpr bool MASKED = decltype(masked)::value;
+      const _Float16* kbn = KR(std::integral_constant<int, jm + 1>{});
+      const _Float16* tbp = KT(std::integral_constant<int, jm + 3>{});
+      const bool doY = !MASKED || j - 1 <= wlast;
+      const bool doF = !MASKED || j + 1 <= wlast;
+      const bool doV = !MASKED || j <= wlast;
+      const int lim = kmax - j * BK;
+      auto frag = [&](int k) __attribute__((always_inline)) {
+        return k < NY ? kt_frag_at(tbp, k % NMB, k / NMB) : kr_frag_at(kbn, k - NY);
+      };
+      half8 fr[PF];
+      #pragma unroll
+      for (int k = 0; k < PF; ++k) fr[k] = frag(k);
+      float wv[16];
+      __builtin_amdgcn_sched_barrier(0);
+      #pragma unroll
+      for (int k = 0; k < NF; ++k) {
+        #pragma unroll
+        for (int u = 0; u < 2 * NCP; ++u)
+          if (k == u * NF / (2 * NCP)) ps_copy(JM, vt_head, j, u);
+        const half8 f = fr[k % PF];
+        if (k < NY) {
+          if (doY) acc[k % NMB] = mfma(f, up[k / NMB], acc[k % NMB]);
+        } else {
+          const int t = k - NY;
+          if (doF) {
+            sn = mfma(f, qop[t], t == 0 ? sinit : sn);
+            rn = mfma(f, rhi[t], t == 0 ? rinit : rn);
+            rn = mfma(f, rlo[t], rn);
+          }
+        }
+        if (k + PF < NF) fr[k % PF] = frag(k + PF);
+        if (doV) {
+          #pragma unroll
+          for (int e = 0; e < EPS; ++e) {
+            const int r = k * EPS + e;
+            float w = fast_exp2(sc[r]);
+            if constexpr (MASKED) {
+              if (key_of(r) > lim) w = 0.f;
+            }
+            wv[r] = w;
+            if (r & 1) {
+              const half2v ha = mul_pack_sum(wv[r - 1], fmaf(rc[r - 1], a_slope, inv_sA), w,
+                                             fmaf(rc[r], a_slope, inv_sA), den);
+              uc[r >> 3][(r - 1) & 7] = ha[0];
+              uc[r >> 3][r & 7] = ha[1];
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      step_barrier<D, NW, 2>();
+    };
+    for (int j0 = 0; j0 < ps_steps - NW; j0 += 4) {
+      ostep(I0{}, std::false_type{}, j0 + 0, sa, ra, sb, rb, ab, aa);
+      ostep(I1{}, std::false_type{}, j0 + 1, sb, rb, sa, ra, aa, ab);
+      ostep(I2{}, std::false_type{}, j0 + 2, sa, ra, sb, rb, ab, aa);
+      ostep(I3{}, std::false_type{}, j0 + 3, sb, rb, sa, ra, aa, ab);
+    }
+    for (int j0 = ps_steps - NW; j0 < ps_steps; j0 += 4) {
+      ostep(I0{}, std::true_type{}, j0 + 0, sa, ra, sb, rb, ab, aa);
+      ostep(I1{}, std::true_type{}, j0 + 1, sb, rb, sa, ra, aa, ab);
+      ostep(I2{}, std::true_type{}, j0 + 2, sa, ra, sb, rb, ab, aa);
+      ostep(I3{}, std::true_type{}, j0 + 3, sb, rb, sa, ra, aa, ab);
+    }
+    // Y += Vt^T A of the last tile (sKt3)
+    if (ps_steps - 1 <= wlast) {
+      #pragma unroll
+      for (int k = 0; k < NY; ++k) acc[k % NMB] = mfma(kt_frag_at(sKt3, k % NMB, k / NMB), ab[k / NMB], acc[k % NMB]);
+    }
+    __syncthreads();  // no tile copy may still be in flight when the kernel ends
+  }
   den = pair_sum(den);
 
   if (!qvalid) return;
