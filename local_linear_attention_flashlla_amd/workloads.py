@@ -201,16 +201,24 @@ def make_workload(name: str, seed: int = 0, B: Optional[int] = None,
 
 
 def make_random(B: int, H: int, n: int, d: int, dtype: str = "f32",
-                seed: int = 0, qk_scale: Optional[float] = 1.0) -> Workload:
+                seed: int = 0, qk_scale: Optional[float] = 1.0,
+                key_ramp: Optional[float] = None) -> Workload:
     """Gaussian q,k,v of any shape (q,k unit rows times ``qk_scale``, or raw
-    Gaussian when ``qk_scale`` is None), for edge-case tests."""
+    Gaussian when ``qk_scale`` is None), for edge-case tests. With
+    ``key_ramp`` the key of position j is further scaled by
+    1 + key_ramp * j / (n - 1), so that scores grow along the sequence."""
     rng = np.random.default_rng(seed)
     q = np.empty((B, H, n, d))
     k = np.empty((B, H, n, d))
     v = np.empty((B, H, n, d))
+    ramp = None
+    if key_ramp is not None:
+        ramp = 1.0 + key_ramp * np.arange(n) / max(n - 1, 1)
     for b in range(B):
         for h in range(H):
             q[b, h], k[b, h], v[b, h] = _head_gaussian(rng, n, d, qk_scale)
+            if ramp is not None:
+                k[b, h] *= ramp[:, None]
     spec = Spec("random", B, H, n, d, dtype, 1.0, 16, 0.0)
     if dtype == "f32":
         dev = [x.astype(np.float32) for x in (q, k, v)]

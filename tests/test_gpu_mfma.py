@@ -71,6 +71,32 @@ def test_no_cg_is_causal_softmax(torch, d):
     assert e.max() < 2e-3
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_rising_scores_move_the_moment_reference(torch, d):
+    # Key norms grow 10-20 fold along the sequence, so many rows' max score lies
+    # far above the first tile's: the moment phase must raise its reference
+    # weight (and rescale its sums) on the way. omega, the row max and the
+    # output are checked against the exact oracle.
+    wl = make_random(1, 2, 512, d, "bf16", seed=40 + d, qk_scale=8.0, key_ramp={64: 9.0, 128: 19.0}[d])
+    lam = 1e3
+    s = np.einsum("bhid,bhjd->bhij", wl.q, wl.k) / np.sqrt(d)
+    causal = np.tril(np.ones((wl.n, wl.n), dtype=bool))
+    s = np.where(causal, s, -np.inf)
+    climb = (s.max(-1) - s[..., :32].max(-1)) / np.log(2)
+    print(f"[rising] rows whose max lies > 15 binades above the first tile's: "
+          f"{np.mean(climb > 15):.2f}", flush=True)
+    assert np.mean(climb > 15) > 0.3
+    res = run(torch, wl, T=16, tol=0.0, lam=lam, extras=True)
+    hr = all_rows(wl)
+    ex = oracle_rows(wl, hr, lam=lam)
+    for (bh, _), x in zip(hr, ex):
+        b, h = bh
+        np.testing.assert_allclose(res["rowmax"][b, h], x["m"], rtol=1e-3, atol=1e-3)
+        np.testing.assert_allclose(res["omega"][b, h], x["omega"], rtol=5e-3)
+    check_parity(wl, res["out"], hr, BF16_TOL, T=16, cg_tol=0.0, lam=lam,
+                 label=f"rising scores d={d}")
+
+
 def test_large_lambda_is_softmax(torch):
     wl = make_random(1, 2, 300, 128, "bf16", seed=8, qk_scale=4.0)
     res = run(torch, wl, T=16, tol=0.0, lam=1e7)
