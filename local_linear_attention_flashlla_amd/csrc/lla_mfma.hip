@@ -963,6 +963,12 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
       #pragma unroll
       for (int k = 0; k < PF; ++k) fr[k] = frag(k);
       const int lim = kmax - j * BK;  // keys <= lim are visible
+      // on the diagonal a wave skips what concerns tiles past its last query
+      // (their weights are all zero)
+      constexpr bool MASKED = decltype(masked)::value;
+      const bool doY = !MASKED || j - 1 <= wlast;
+      const bool doF = !MASKED || j + 1 <= wlast;
+      const bool doV = !MASKED || j <= wlast;
       float wv[16];
       __builtin_amdgcn_sched_barrier(0);
       #pragma unroll
@@ -970,14 +976,19 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
         copy_at(k);
         const half8 f = fr[k % PF];
         if (k < NY) {
-          acc[k % NMB] = mfma(f, up[k / NMB], acc[k % NMB]);
-          if constexpr (SPLIT_U) acc[k % NMB] = mfma(f, ulp[k / NMB], acc[k % NMB]);
+          if (doY) {
+            acc[k % NMB] = mfma(f, up[k / NMB], acc[k % NMB]);
+            if constexpr (SPLIT_U) acc[k % NMB] = mfma(f, ulp[k / NMB], acc[k % NMB]);
+          }
         } else {
           const int t = k - NY;
-          sn = mfma(f, qop[t], t == 0 ? sinit : sn);
-          tn = mfma(f, dop[t], t == 0 ? tinit : tn);
+          if (doF) {
+            sn = mfma(f, qop[t], t == 0 ? sinit : sn);
+            tn = mfma(f, dop[t], t == 0 ? tinit : tn);
+          }
         }
         if (k + PF < NF) fr[k % PF] = frag(k + PF);
+        if (doV)
         #pragma unroll
         for (int e = 0; e < EPS; ++e) {
           const int r = k * EPS + e;
@@ -1032,11 +1043,13 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
       pstep(I3{}, std::true_type{}, j0 + 3, sb, tb, sa, ta, ua, ula, ub, ulb);
     }
     // Y += Kt^T U of the last tile (sKt3)
-    #pragma unroll
-    for (int k = 0; k < NY; ++k) {
-      const half8 f = kt_frag_at(sKt3, k >> 1, k & 1);
-      acc[k >> 1] = mfma(f, ub[k & 1], acc[k >> 1]);
-      if constexpr (SPLIT_U) acc[k >> 1] = mfma(f, ulb[k & 1], acc[k >> 1]);
+    if (nsteps - 1 <= wlast) {
+      #pragma unroll
+      for (int k = 0; k < NY; ++k) {
+        const half8 f = kt_frag_at(sKt3, k >> 1, k & 1);
+        acc[k >> 1] = mfma(f, ub[k & 1], acc[k >> 1]);
+        if constexpr (SPLIT_U) acc[k >> 1] = mfma(f, ulb[k & 1], acc[k >> 1]);
+      }
     }
     usum = pair_sum(usum);
     // every wave is done with the tiles: start the next sweep's first copies
