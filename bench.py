@@ -112,6 +112,46 @@ def cpu_baseline(wl, target_rows: int, seed: int = 0):
     }
 
 
+def memory_curve(torch, lla, dev, ns=(1024, 2048, 4096, 8192, 16384), B=1, H=16, d=128):
+    """Peak device memory of one forward at the long-sequence shape (B=1, H=16,
+    d=128, bf16) for n = 1k .. 16k: inputs, output and workspace, all allocated
+    here through torch (the library allocates nothing when it is handed a
+    workspace). Working memory linear in n shows as a constant peak per row."""
+    rows = []
+    for n in ns:
+        torch.cuda.synchronize(dev)
+        torch.cuda.empty_cache()
+        base = torch.cuda.memory_allocated(dev)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(n)
+        qkv = []
+        for _ in range(3):
+            x = torch.randn((B, H, n, d), device=dev, generator=gen, dtype=torch.float32)
+            qkv.append(x.to(torch.bfloat16))
+            del x
+        q, k, v = qkv
+        q /= q.float().norm(dim=-1, keepdim=True).to(torch.bfloat16)
+        k /= k.float().norm(dim=-1, keepdim=True).to(torch.bfloat16)
+        torch.cuda.synchronize(dev)
+        torch.cuda.reset_peak_memory_stats(dev)
+        ws_bytes = lla.workspace_bytes(B, H, n, d, "bf16", lla.LLA_KERNEL_MFMA)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        out = torch.empty((B, H, n, d), dtype=torch.float32, device=dev)
+        lla.forward(q, k, v, 1.0, 2, 0.0, out=out, workspace=ws, kernel=lla.LLA_KERNEL_MFMA)
+        torch.cuda.synchronize(dev)
+        peak = torch.cuda.max_memory_allocated(dev) - base
+        io = 3 * B * H * n * d * 2 + B * H * n * d * 4
+        rows.append({"n": n, "peak_bytes": int(peak), "workspace_bytes": int(ws_bytes),
+                     "inputs_outputs_bytes": int(io),
+                     "peak_bytes_per_row": peak / (B * H * n),
+                     "workspace_bytes_per_row": ws_bytes / (B * H * n)})
+        del q, k, v, ws, out, qkv
+    return {"metric": "peak device memory of one forward vs n", "unit": "bytes",
+            "config": {"workload": "long-sequence shape", "B": B, "H": H, "d": d,
+                       "dtype": "bf16", "kernel": "mfma"},
+            "data": "synthetic", "rows": rows}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -129,6 +169,9 @@ def main(argv=None):
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a "
                          "reference kernel of known traffic for hardware byte counters)")
+    ap.add_argument("--memory-curve", action="store_true",
+                    help="instead of timing, print the peak device memory of one forward at "
+                         "n = 1k .. 16k (B=1, H=16, d=128) as one JSON line")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -145,6 +188,9 @@ def main(argv=None):
         _b.build()
     assert torch.cuda.is_available(), "bench.py needs a HIP device"
     dev = torch.device("cuda:0")
+    if args.memory_curve:
+        print(json.dumps(memory_curve(torch, lla, dev)), flush=True)
+        return 0
 
     wl = make_workload(args.workload)
     if wl.dtype == "f32":
