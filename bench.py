@@ -152,6 +152,56 @@ def memory_curve(torch, lla, dev, ns=(1024, 2048, 4096, 8192, 16384), B=1, H=16,
             "data": "synthetic", "rows": rows}
 
 
+def bench_given_rho(args, torch, lla, wl, q, k, v, out, ws, kernel, kernel_used):
+    """Throughput of the output given rho: the moment and output scans of the
+    forward with the CG solve replaced by a supplied rho (here the forward's own
+    rho for this workload, computed untimed). 10d FLOPs per causal pair: 4d for
+    the moment scan, 6d for the output scan; the timed kernel is the output
+    scan."""
+    B, H, n, d = wl.B, wl.H, wl.n, wl.d
+    rho = torch.empty((B, H, n, d), dtype=torch.float32, device=q.device)
+    lla.forward(q, k, v, wl.lam, wl.cg_max_iters, wl.cg_rel_tol, out=out, workspace=ws,
+                kernel=kernel, rho=rho)
+    torch.cuda.synchronize()
+
+    def step(events=None):
+        lla.forward(q, k, v, wl.lam, 0, 0.0, out=out, workspace=ws, kernel=kernel, events=events,
+                    rho_in=rho)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events=ev[i])
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    pairs = B * H * n * (n + 1) / 2.0
+    flops = 10.0 * d * pairs
+    mfma = kernel_used == lla.LLA_KERNEL_MFMA
+    achieved = (6.0 * d * pairs if mfma else flops) / (kern_ms * 1e-3) / 1e12
+    peak = PEAK["mfma_fp16"] if mfma else PEAK["valu_fp32"]
+    rec = {
+        "metric": "LLA output given rho: queries/s + TFLOP/s, 1 MI355X",
+        "value": B * H * n / (ms_step * 1e-3), "unit": "queries/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "H": H, "n": n, "d": d, "lambda": wl.lam,
+                   "kernel": "mfma" if mfma else "valu", "rho": "the forward's own rho"},
+        "tflops": flops / (ms_step * 1e-3) / 1e12, "flops_per_step": flops,
+        "main_kernel_ms": kern_ms,
+        "main_kernel": "output scan (phase 3)" if mfma else "fused kernel",
+        "roofline": {"bound": "mfma" if mfma else "alu", "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None},
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -169,6 +219,9 @@ def main(argv=None):
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a "
                          "reference kernel of known traffic for hardware byte counters)")
+    ap.add_argument("--given-rho", action="store_true",
+                    help="time lla_output_given_rho (moment and output scans, the CG solve "
+                         "replaced by a supplied rho) instead of the full forward")
     ap.add_argument("--memory-curve", action="store_true",
                     help="instead of timing, print the peak device memory of one forward at "
                          "n = 1k .. 16k (B=1, H=16, d=128) as one JSON line")
@@ -212,6 +265,9 @@ def main(argv=None):
     def step(events=None):
         lla.forward(q, k, v, wl.lam, wl.cg_max_iters, wl.cg_rel_tol, out=out, workspace=ws,
                     kernel=kernel, flags=flags, events=events)
+
+    if args.given_rho:
+        return bench_given_rho(args, torch, lla, wl, q, k, v, out, ws, kernel, kernel_used)
 
     # iteration counts for the algorithmic FLOP count (untimed)
     iters = torch.empty((B, H, n), dtype=torch.int32, device=dev)

@@ -146,8 +146,28 @@ int lla_forward_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 /* Full form: dtype, kernel choice, optional outputs, optional workspace. */
 int lla_forward_ex(const lla_fwd_args* args, hipStream_t stream);
 
-/* Device workspace bytes lla_forward_ex needs for these sizes and this
-   kernel choice (0 if none). Returns 0 for invalid sizes too. */
+/* out = Eq. (8) of the reading notes' section 2.1 for a SUPPLIED rho_i
+   instead of the solved one:
+     out_i = sum_j w_ij (1 - (k_j - q_i)^T rho_i) v_j / (omega_i - mu_i^T rho_i)
+   (the denominator formed as sum_j w_ij (1 - (k_j - q_i)^T rho_i), equal to it
+   for every rho). This is the forward's moment and output scans with the CG
+   solve left out, so the solve and the output can be run and timed apart; it
+   is also the covariance form of the Parallax summary,
+   out_i = vbar_i - eta_i C_i rho_i, written out.
+   rho_in: [B][H][n][d] fp32, device, 16-byte aligned, read only; rho_i = 0
+   gives causal softmax attention. args: as for lla_forward_ex;
+   cg_max_iters, cg_rel_tol and LLA_FLAG_SPLIT_U have no effect; cg_iters and
+   cg_resid (if requested) are written 0; rho (if requested) receives rho_in;
+   the events bracket the output kernel of the matrix-core path. No output
+   may overlap rho_in. Returns LLA_OK or a negative status, as lla_forward_ex.
+   Unlike the forward, which works on the system centred at the weighted key
+   mean, this follows the printed form, whose denominator can be small for a
+   rho far from the solution. */
+int lla_output_given_rho(const lla_fwd_args* args, const float* rho_in, hipStream_t stream);
+
+/* Device workspace bytes lla_forward_ex (or lla_output_given_rho) needs for
+   these sizes and this kernel choice (0 if none). Returns 0 for invalid sizes
+   too. */
 size_t lla_workspace_bytes(int B, int H, int n, int d, int dtype, int kernel);
 
 /* Static, human-readable name of a status code. */

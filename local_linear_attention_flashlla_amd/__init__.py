@@ -35,7 +35,7 @@ def _ptr(t) -> int:
 def forward(q, k, v, lam: float, cg_max_iters: int, cg_rel_tol: float, *,
             out=None, omega=None, rho=None, rowmax=None, cg_iters=None, cg_resid=None,
             workspace=None, kernel: int = LLA_KERNEL_AUTO, flags: int = 0, stream=None,
-            events=None):
+            events=None, rho_in=None):
     """Causal LLA forward on the GPU.
 
     q, k, v: contiguous [B, H, n, d] tensors on a HIP device, all float32 or all
@@ -46,6 +46,10 @@ def forward(q, k, v, lam: float, cg_max_iters: int, cg_rel_tol: float, *,
     The call is asynchronous on ``stream`` (default: torch's current stream).
     ``events``: optional (begin, end) pair of ``torch.cuda.Event`` that the
     library records around its main kernel.
+    ``rho_in``: optional [B, H, n, d] float32 GPU tensor; when given, the CG
+    solve is skipped and ``out`` is Eq. (8) with this rho_i
+    (``lla_output_given_rho``); ``lam``, ``cg_max_iters`` and ``cg_rel_tol``
+    are then passed through but do not change the result.
     """
     import torch
 
@@ -98,6 +102,13 @@ def forward(q, k, v, lam: float, cg_max_iters: int, cg_rel_tol: float, *,
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     import ctypes
-    st = _lib.load().lla_forward_ex(ctypes.byref(a), ctypes.c_void_p(handle))
+    if rho_in is not None:
+        if (rho_in.dtype != torch.float32 or tuple(rho_in.shape) != (B, H, n, d)
+                or not rho_in.is_contiguous() or not rho_in.is_cuda):
+            raise ValueError(f"rho_in must be a contiguous float32 GPU tensor of shape {(B, H, n, d)}")
+        st = _lib.load().lla_output_given_rho(ctypes.byref(a), ctypes.c_void_p(_ptr(rho_in)),
+                                             ctypes.c_void_p(handle))
+    else:
+        st = _lib.load().lla_forward_ex(ctypes.byref(a), ctypes.c_void_p(handle))
     _lib.check(st)
     return out

@@ -30,7 +30,8 @@ LLA_FLAG_SPLIT_U = 1
 
 # Every symbol include/lla.h declares.
 EXPORTED_SYMBOLS = (
-    "lla_forward_f32", "lla_forward_bf16", "lla_forward_ex", "lla_workspace_bytes",
+    "lla_forward_f32", "lla_forward_bf16", "lla_forward_ex", "lla_output_given_rho",
+    "lla_workspace_bytes",
     "lla_status_string", "lla_last_error", "lla_version",
 )
 
@@ -91,6 +92,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.lla_forward_bf16.restype = ci
     lib.lla_forward_ex.argtypes = [ctypes.POINTER(LlaFwdArgs), vp]
     lib.lla_forward_ex.restype = ci
+    lib.lla_output_given_rho.argtypes = [ctypes.POINTER(LlaFwdArgs), vp, vp]
+    lib.lla_output_given_rho.restype = ci
     lib.lla_workspace_bytes.argtypes = [ci, ci, ci, ci, ci, ci]
     lib.lla_workspace_bytes.restype = cz
     lib.lla_status_string.argtypes = [ci]

@@ -140,8 +140,7 @@ size_t lla_workspace_bytes(int B, int H, int n, int d, int dtype, int kernel) {
   return 0;
 }
 
-int lla_forward_ex(const lla_fwd_args* a, hipStream_t stream) {
-  g_last_error[0] = '\0';
+static int forward_impl(const lla_fwd_args* a, const float* rho_in, hipStream_t stream) {
   int st = validate(a);
   if (st != LLA_OK) return st;
   int kernel = 0;
@@ -151,6 +150,7 @@ int lla_forward_ex(const lla_fwd_args* a, hipStream_t stream) {
   p.q = a->q; p.k = a->k; p.v = a->v; p.out = a->out;
   p.omega = a->omega; p.rho = a->rho; p.rowmax = a->rowmax;
   p.cg_iters = a->cg_iters; p.cg_resid = a->cg_resid;
+  p.rho_in = rho_in;
   p.BH = a->B * a->H; p.n = a->n; p.d = a->d; p.dtype = a->dtype;
   p.lambda = a->lambda; p.cg_max_iters = a->cg_max_iters; p.cg_rel_tol = a->cg_rel_tol;
   p.flags = a->flags;
@@ -184,6 +184,31 @@ int lla_forward_ex(const lla_fwd_args* a, hipStream_t stream) {
   }
   if (e != hipSuccess) return fail(LLA_ERR_HIP, "MFMA launch: %s", hipGetErrorString(e));
   return LLA_OK;
+}
+
+int lla_forward_ex(const lla_fwd_args* a, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  return forward_impl(a, nullptr, stream);
+}
+
+int lla_output_given_rho(const lla_fwd_args* a, const float* rho_in, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  const int st = validate(a);  // (sizes are checked before they are multiplied below)
+  if (st != LLA_OK) return st;
+  if (!rho_in) return fail(LLA_ERR_INVALID_ARG, "rho_in is NULL");
+  if (!aligned16(rho_in)) return fail(LLA_ERR_INVALID_ARG, "rho_in pointer not 16-byte aligned");
+  {
+    const size_t nrho = (size_t)a->B * a->H * a->n * a->d * sizeof(float);
+    const size_t nrow = (size_t)a->B * a->H * a->n * sizeof(float);
+    struct Out { const void* p; size_t bytes; const char* name; };
+    const Out outs[6] = {{a->out, nrho, "out"},           {a->rho, nrho, "rho"},
+                         {a->omega, nrow, "omega"},       {a->rowmax, nrow, "rowmax"},
+                         {a->cg_iters, nrow, "cg_iters"}, {a->cg_resid, nrow, "cg_resid"}};
+    for (const Out& o : outs)
+      if (o.p && overlap(o.p, o.bytes, rho_in, nrho))
+        return fail(LLA_ERR_INVALID_ARG, "%s overlaps rho_in", o.name);
+  }
+  return forward_impl(a, rho_in, stream);
 }
 
 int lla_forward_f32(const float* q, const float* k, const float* v, float* out, int B, int H, int n,

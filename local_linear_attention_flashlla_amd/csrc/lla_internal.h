@@ -19,6 +19,7 @@ struct FwdParams {
   float* rowmax;     // optional [BH][n]
   int32_t* cg_iters; // optional [BH][n]
   float* cg_resid;   // optional [BH][n]
+  const float* rho_in;  // supplied rho_i [BH][n][d] (skips the CG solve), or NULL
   int BH;            // B * H
   int n;
   int d;

@@ -323,6 +323,7 @@ struct MainParams {
   float* kbs;        // fp32 kbar slab, same layout
   float* rs;         // CG residual slab, same layout
   float* qs;         // per-query state slab: row max, omega
+  const float* rho_in;  // supplied rho_i [BH][n][d] (no CG solve), or NULL
   int BH, n, nchunk, nblk;
   int nq32;          // 32-query groups per head in the state slabs
   float lambda;
@@ -739,13 +740,15 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
 
   // Per query: kbar = mu~ / omega, r0 = mu = mu~ - omega q, x0 = 0, into the
   // lane-contiguous workspace slabs; the row max and omega into the state slab.
+  // With a supplied rho (no CG solve) the output phase is centred at q
+  // instead, which is Eq. (8) as printed: the slabs then hold s q and rho / s.
   {
     const float inv_om = qvalid ? 1.f / om : 0.f;
     #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
       #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        floatx4 kb, rc;
+        floatx4 kb, rc, x0 = {0.f, 0.f, 0.f, 0.f};
         const floatx4 qv = q_acc(mb, a);
         #pragma unroll
         for (int b = 0; b < 4; ++b) {
@@ -753,8 +756,16 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
           kb[b] = mt * inv_om;
           rc[b] = qvalid ? mt - om * qv[b] : 0.f;
         }
+        if (P.rho_in) {
+          kb = qvalid ? qv : floatx4{0.f, 0.f, 0.f, 0.f};
+          if (qvalid) {
+            const float4 rv = *reinterpret_cast<const float4*>(P.rho_in + orow * D + 32 * mb + 8 * a + 4 * g);
+            const float inv_s = 1.f / s;
+            x0 = floatx4{rv.x * inv_s, rv.y * inv_s, rv.z * inv_s, rv.w * inv_s};
+          }
+        }
         slab_st(kbs, mb * 4 + a, lane, kb);
-        slab_st(xs, mb * 4 + a, lane, floatx4{0.f, 0.f, 0.f, 0.f});
+        slab_st(xs, mb * 4 + a, lane, x0);
         slab_st(rsl, mb * 4 + a, lane, rc);
       }
   }
@@ -762,6 +773,10 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
   qst[64 + lane] = om;
   if (qvalid && g == 0) {
     if (P.omega) P.omega[orow] = om;
+    if (P.rho_in) {  // no CG solve in this mode
+      if (P.cg_iters) P.cg_iters[orow] = 0;
+      if (P.cg_resid) P.cg_resid[orow] = 0.f;
+    }
     if (P.rowmax) P.rowmax[orow] = m2 * kLn2;
   }
   } else if constexpr (PHASE == 2) {
@@ -1382,6 +1397,7 @@ hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
   m.kbs = w.kbs;
   m.rs = w.rs;
   m.qs = w.qs;
+  m.rho_in = p.rho_in;
   m.BH = p.BH;
   m.n = n;
   m.nchunk = nchunk;
@@ -1397,6 +1413,18 @@ hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((lla_mfma_phase<D, 1, false, kNW13>), grid1, dim3(64 * kNW13), 0, stream, m);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (p.rho_in) {
+    // rho supplied: no CG kernel; the events bracket the output kernel
+    if (p.ev_main_begin) {
+      e = hipEventRecord(p.ev_main_begin, stream);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((lla_mfma_phase<D, 3, false, kNW13>), grid1, dim3(64 * kNW13), 0, stream, m);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (p.ev_main_end) e = hipEventRecord(p.ev_main_end, stream);
+    return e;
+  }
   if (p.ev_main_begin) {
     e = hipEventRecord(p.ev_main_begin, stream);
     if (e != hipSuccess) return e;

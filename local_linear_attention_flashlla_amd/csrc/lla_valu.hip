@@ -173,6 +173,13 @@ __global__ __launch_bounds__(VT) void lla_valu_kernel(FwdParams P) {
     if (c < D && valid) {
       const float4 qv = *reinterpret_cast<const float4*>(sQ + row * LD + c);
       const float4 a = acc[u];
+      if (P.rho_in) {
+        // rho supplied: no solve; the output scan is centred at q, which is
+        // Eq. (8) as printed
+        kb[u] = qv;
+        x[u] = *reinterpret_cast<const float4*>(P.rho_in + (static_cast<size_t>(bh) * P.n + qi) * D + c);
+        continue;
+      }
       kb[u] = make_float4(a.x * inv_om, a.y * inv_om, a.z * inv_om, a.w * inv_om);
       r[u] = make_float4(a.x - om * qv.x, a.y - om * qv.y, a.z - om * qv.z, a.w - om * qv.w);
       rr += dot4(r[u], r[u]);

@@ -65,6 +65,23 @@ def oracle_rows(wl, heads_rows, solver="cholesky", T=0, tol=0.0, lam=None, worke
         return list(ex.map(_oracle_job, jobs))
 
 
+def oracle_given_rho(wl, heads_rows, rho, lam=None):
+    """Eq. (8) rows for a supplied rho (float64 copy of what the GPU read):
+    rho is [B, H, n, d]; returns a list of [len(rows), d] arrays."""
+    lam = wl.lam if lam is None else lam
+    res = []
+    for (b, h), rows in heads_rows:
+        out = []
+        for i in rows:
+            q_i, K, V = wl.q[b, h, i], wl.k[b, h, :i + 1], wl.v[b, h, :i + 1]
+            _, _, w = O.causal_weights(q_i, K, 1.0 / np.sqrt(wl.d))
+            Z, omega, mu, _ = O.pairwise_moments(q_i, K, w, lam)
+            bi, _, _ = O.intercept_from_rho(w, Z, V, omega, mu, np.asarray(rho[b, h, i], np.float64))
+            out.append(bi)
+        res.append(np.array(out))
+    return res
+
+
 def check_parity(wl, out, heads_rows, tol, T=None, cg_tol=None, lam=None, label="",
                  factor=4.0):
     """Compare GPU rows with the float64 oracle.

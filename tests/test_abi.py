@@ -99,6 +99,20 @@ def test_invalid_arguments_are_rejected_on_the_host(lib, field, value, status):
     assert _lib.last_error() != ""
 
 
+@pytest.mark.parametrize("rho_in,kw,status", [
+    (0, {}, -1),                                  # NULL rho_in
+    (BASE + 5 * GAP + 4, {}, -1),                 # misaligned rho_in
+    (BASE + 3 * GAP + 64, {}, -1),                # rho_in overlaps out
+    (BASE + 5 * GAP, {"omega": BASE + 5 * GAP + 1024}, -1),  # an output overlaps rho_in
+    (BASE + 5 * GAP, {"B": 0}, -1),               # the forward's own checks run too
+    (BASE + 5 * GAP, {"d": 48}, -2),
+])
+def test_output_given_rho_rejects_invalid_arguments(lib, rho_in, kw, status):
+    a = _args(**kw)
+    assert lib.lla_output_given_rho(ctypes.byref(a), ctypes.c_void_p(rho_in), None) == status
+    assert _lib.last_error() != ""
+
+
 def test_null_args_pointer(lib):
     assert lib.lla_forward_ex(None, None) == -1
 

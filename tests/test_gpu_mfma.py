@@ -4,7 +4,8 @@ rows), in the same launch configuration bench.py times."""
 import numpy as np
 import pytest
 
-from tests._support import check_parity, ensure_built, oracle_rows, row_errors, to_device
+from tests._support import (check_parity, ensure_built, oracle_given_rho, oracle_rows,
+                            row_errors, to_device)
 from local_linear_attention_flashlla_amd.workloads import make_workload, make_random
 from oracle import lla_oracle as O
 import local_linear_attention_flashlla_amd as lla
@@ -47,6 +48,45 @@ def run(torch, wl, kernel=MFMA, T=None, tol=None, lam=None, extras=False, flags=
 
 def all_rows(wl):
     return [((b, h), range(wl.n)) for b in range(wl.B) for h in range(wl.H)]
+
+
+def given_rho_cases(torch, wl, kernel, tol_rel, label):
+    """Eq. (8) for supplied rho against the oracle's Eq. (8) with the same rho:
+    the exact rho (then also the exact output), rho = 0 (softmax) and a rho
+    halfway to zero with noise (any rho; the denominator stays away from 0)."""
+    hr = all_rows(wl)
+    lam = wl.lam
+    ex = oracle_rows(wl, hr, lam=lam)
+    shape = (wl.B, wl.H, wl.n, wl.d)
+    rho_exact = np.zeros(shape, np.float32)
+    for ((b, h), _), x in zip(hr, ex):
+        rho_exact[b, h] = x["rho"]
+    rng = np.random.default_rng(11)
+    noise = rng.standard_normal(shape) * np.abs(rho_exact).mean(axis=-1, keepdims=True)
+    cases = {"exact": rho_exact, "zero": np.zeros(shape, np.float32),
+             "other": (0.5 * rho_exact + 0.1 * noise).astype(np.float32)}
+    q, k, v = to_device(wl)
+    for name, rho in cases.items():
+        print(f"\n[case] given rho ({name}) {label} kernel={kernel}", flush=True)
+        rho_t = torch.from_numpy(rho).cuda()
+        rho_o = torch.empty(shape, device="cuda")
+        it_o = torch.full(shape[:3], -1, dtype=torch.int32, device="cuda")
+        out = lla.forward(q, k, v, lam, 16, 0.0, kernel=kernel, rho_in=rho_t, rho=rho_o,
+                          cg_iters=it_o)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().astype(np.float64)
+        ref = oracle_given_rho(wl, hr, rho.astype(np.float64), lam)
+        e = np.concatenate([row_errors(got[b, h], r) for ((b, h), _), r in zip(hr, ref)])
+        print(f"[parity] given rho ({name}) {label} rows={e.size} max={e.max():.3e} "
+              f"p50={np.median(e):.2e}", flush=True)
+        assert e.max() <= tol_rel
+        if name == "exact":
+            ee = np.concatenate([row_errors(got[b, h], x["b"]) for ((b, h), _), x in zip(hr, ex)])
+            assert ee.max() <= tol_rel
+        # rho comes back (up to the rounding of a factor 1 / (1 + (q - q).rho)),
+        # and no CG step is taken
+        np.testing.assert_allclose(rho_o.cpu().numpy(), rho, rtol=1e-6, atol=0)
+        assert np.all(it_o.cpu().numpy() == 0)
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -200,3 +240,12 @@ def test_full_size_sampled_rows(torch, name):
     assert it.max() <= wl.cg_max_iters
     assert np.isfinite(res["out"]).all()
     assert stats["rows"] > 0
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_output_given_rho(torch, d):
+    if d == 128:
+        wl = make_workload("standard", B=1, H=2, n=300)
+    else:
+        wl = make_random(1, 2, 200, 64, "bf16", seed=12, qk_scale=4.0)
+    given_rho_cases(torch, wl, MFMA, BF16_TOL, f"mfma d={d}")
