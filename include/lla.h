@@ -170,6 +170,49 @@ int lla_output_given_rho(const lla_fwd_args* args, const float* rho_in, hipStrea
    too. */
 size_t lla_workspace_bytes(int B, int H, int n, int d, int dtype, int kernel);
 
+/* ------------------------------------------------------------------------
+ * Decode: one new query per (batch, head) against a cache of n keys and
+ * values, every one of them visible -- the last row of the causal forward
+ * whose query sits at position n - 1 (q_{n-1} = q). Same estimator, same
+ * mean-centred CG system and the same CG policy as lla_forward_ex.
+ * The centred Gram matrix sum_j w_j (k_j - kbar)(k_j - kbar)^T of the query
+ * (d x d) is formed once on the matrix cores, its operands carried as two
+ * fp16 terms each, and CG runs on it plus lambda I in fp32: the cache is read
+ * three times whatever the iteration count, and working memory is n + O(d^2)
+ * floats per head. In exact arithmetic the iterates are those of the
+ * matrix-free CG.
+ * ------------------------------------------------------------------------ */
+typedef struct lla_decode_args {
+  int dtype;          /* LLA_DTYPE_F32 or LLA_DTYPE_BF16 */
+  const void* q;      /* [B][H][d] dtype, device: the new query of each head */
+  const void* k;      /* [B][H][n][d] dtype, device: key cache (the new key included) */
+  const void* v;      /* [B][H][n][d] dtype, device: value cache */
+  float* out;         /* [B][H][d] fp32, device, written */
+  int B, H, n, d;     /* d in {64, 128} */
+  float lambda;       /* > 0 */
+  int cg_max_iters;   /* >= 0 */
+  float cg_rel_tol;   /* >= 0 */
+  /* optional outputs, NULL = not wanted (device pointers) */
+  float* omega;       /* [B][H]    */
+  float* rho;         /* [B][H][d] the pages' rho */
+  float* rowmax;      /* [B][H]    max_l c q . k_l */
+  int32_t* cg_iters;  /* [B][H]    */
+  float* cg_resid;    /* [B][H]    ||r_k|| / ||r_0|| at exit */
+  void* workspace;    /* optional caller workspace (device), as for lla_forward_ex */
+  size_t workspace_bytes;
+  hipEvent_t ev_main_begin; /* optional: recorded around the Gram kernel */
+  hipEvent_t ev_main_end;
+} lla_decode_args;
+
+/* out = LLA(q; k, v) for one query per head. Conventions, validation and
+   status codes as for lla_forward_ex (LLA_ERR_UNSUPPORTED for d outside
+   {64, 128}). */
+int lla_decode_ex(const lla_decode_args* args, hipStream_t stream);
+
+/* Device workspace bytes lla_decode_ex needs for these sizes (0 for invalid
+   sizes). Linear in n. */
+size_t lla_decode_workspace_bytes(int B, int H, int n, int d, int dtype);
+
 /* Static, human-readable name of a status code. */
 const char* lla_status_string(int status);
 

@@ -14,7 +14,7 @@ from . import _lib
 from ._lib import (LLA_DTYPE_BF16, LLA_DTYPE_F32, LLA_FLAG_SPLIT_U, LLA_KERNEL_AUTO,
                    LLA_KERNEL_MFMA, LLA_KERNEL_VALU, LlaError)
 
-__all__ = ["forward", "workspace_bytes", "LlaError", "LLA_KERNEL_AUTO", "LLA_KERNEL_VALU",
+__all__ = ["forward", "decode", "decode_workspace_bytes", "workspace_bytes", "LlaError", "LLA_KERNEL_AUTO", "LLA_KERNEL_VALU",
            "LLA_KERNEL_MFMA", "LLA_FLAG_SPLIT_U", "version"]
 
 
@@ -111,4 +111,75 @@ def forward(q, k, v, lam: float, cg_max_iters: int, cg_rel_tol: float, *,
     else:
         st = _lib.load().lla_forward_ex(ctypes.byref(a), ctypes.c_void_p(handle))
     _lib.check(st)
+    return out
+
+
+def decode_workspace_bytes(B: int, H: int, n: int, d: int, dtype: str = "bf16") -> int:
+    dt = LLA_DTYPE_BF16 if dtype == "bf16" else LLA_DTYPE_F32
+    return int(_lib.load().lla_decode_workspace_bytes(B, H, n, d, dt))
+
+
+def decode(q, k, v, lam: float, cg_max_iters: int, cg_rel_tol: float, *, out=None, omega=None,
+           rho=None, rowmax=None, cg_iters=None, cg_resid=None, workspace=None, stream=None,
+           events=None):
+    """Decode-shaped LLA forward on the GPU: one new query per (batch, head).
+
+    q: [B, H, d]; k, v: [B, H, n, d] key and value caches (the new key and
+    value included), contiguous GPU tensors, all float32 or all bfloat16.
+    Returns ``out`` ([B, H, d] float32), the last row of the causal forward
+    whose query is q. Optional outputs: omega/rowmax/cg_resid [B, H] float32,
+    rho [B, H, d] float32, cg_iters [B, H] int32. ``events``: optional
+    (begin, end) pair recorded around the Gram kernel.
+    """
+    import ctypes
+    import torch
+
+    if q.dim() != 3 or k.dim() != 4 or k.shape != v.shape or tuple(q.shape) != (
+            k.shape[0], k.shape[1], k.shape[3]):
+        raise ValueError("q must be [B, H, d] and k, v [B, H, n, d]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share one dtype")
+    if q.dtype == torch.float32:
+        dtype = LLA_DTYPE_F32
+    elif q.dtype == torch.bfloat16:
+        dtype = LLA_DTYPE_BF16
+    else:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    B, H, n, d = (int(s) for s in k.shape)
+    if out is None:
+        out = torch.empty((B, H, d), dtype=torch.float32, device=q.device)
+    for name, t, dt, shape in (("out", out, torch.float32, (B, H, d)),
+                               ("omega", omega, torch.float32, (B, H)),
+                               ("rho", rho, torch.float32, (B, H, d)),
+                               ("rowmax", rowmax, torch.float32, (B, H)),
+                               ("cg_iters", cg_iters, torch.int32, (B, H)),
+                               ("cg_resid", cg_resid, torch.float32, (B, H))):
+        if t is None:
+            continue
+        if t.dtype != dt or tuple(t.shape) != shape or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous {dt} GPU tensor of shape {shape}")
+    a = _lib.LlaDecodeArgs()
+    a.dtype = dtype
+    a.q, a.k, a.v, a.out = _ptr(q), _ptr(k), _ptr(v), _ptr(out)
+    a.B, a.H, a.n, a.d = B, H, n, d
+    a.lambda_ = float(lam)
+    a.cg_max_iters = int(cg_max_iters)
+    a.cg_rel_tol = float(cg_rel_tol)
+    a.omega, a.rho, a.rowmax = _ptr(omega), _ptr(rho), _ptr(rowmax)
+    a.cg_iters, a.cg_resid = _ptr(cg_iters), _ptr(cg_resid)
+    if workspace is not None:
+        a.workspace = _ptr(workspace)
+        a.workspace_bytes = int(workspace.numel() * workspace.element_size())
+    if events is not None:
+        ev0, ev1 = events
+        ev0.record()
+        ev1.record()
+        a.ev_main_begin, a.ev_main_end = int(ev0.cuda_event), int(ev1.cuda_event)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    _lib.check(_lib.load().lla_decode_ex(ctypes.byref(a), ctypes.c_void_p(handle)))
     return out

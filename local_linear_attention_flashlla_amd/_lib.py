@@ -31,7 +31,7 @@ LLA_FLAG_SPLIT_U = 1
 # Every symbol include/lla.h declares.
 EXPORTED_SYMBOLS = (
     "lla_forward_f32", "lla_forward_bf16", "lla_forward_ex", "lla_output_given_rho",
-    "lla_workspace_bytes",
+    "lla_workspace_bytes", "lla_decode_ex", "lla_decode_workspace_bytes",
     "lla_status_string", "lla_last_error", "lla_version",
 )
 
@@ -60,6 +60,33 @@ class LlaFwdArgs(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t),
         ("kernel", ctypes.c_int),
         ("flags", ctypes.c_int),
+        ("ev_main_begin", ctypes.c_void_p),
+        ("ev_main_end", ctypes.c_void_p),
+    ]
+
+
+class LlaDecodeArgs(ctypes.Structure):
+    """Mirror of ``lla_decode_args``."""
+    _fields_ = [
+        ("dtype", ctypes.c_int),
+        ("q", ctypes.c_void_p),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
+        ("B", ctypes.c_int),
+        ("H", ctypes.c_int),
+        ("n", ctypes.c_int),
+        ("d", ctypes.c_int),
+        ("lambda_", ctypes.c_float),
+        ("cg_max_iters", ctypes.c_int),
+        ("cg_rel_tol", ctypes.c_float),
+        ("omega", ctypes.c_void_p),
+        ("rho", ctypes.c_void_p),
+        ("rowmax", ctypes.c_void_p),
+        ("cg_iters", ctypes.c_void_p),
+        ("cg_resid", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
         ("ev_main_begin", ctypes.c_void_p),
         ("ev_main_end", ctypes.c_void_p),
     ]
@@ -94,6 +121,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.lla_forward_ex.restype = ci
     lib.lla_output_given_rho.argtypes = [ctypes.POINTER(LlaFwdArgs), vp, vp]
     lib.lla_output_given_rho.restype = ci
+    lib.lla_decode_ex.argtypes = [ctypes.POINTER(LlaDecodeArgs), vp]
+    lib.lla_decode_ex.restype = ci
+    lib.lla_decode_workspace_bytes.argtypes = [ci, ci, ci, ci, ci]
+    lib.lla_decode_workspace_bytes.restype = cz
     lib.lla_workspace_bytes.argtypes = [ci, ci, ci, ci, ci, ci]
     lib.lla_workspace_bytes.restype = cz
     lib.lla_status_string.argtypes = [ci]

@@ -211,6 +211,90 @@ int lla_output_given_rho(const lla_fwd_args* a, const float* rho_in, hipStream_t
   return forward_impl(a, rho_in, stream);
 }
 
+int lla_decode_ex(const lla_decode_args* a, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (!a) return fail(LLA_ERR_INVALID_ARG, "args is NULL");
+  if (a->dtype != LLA_DTYPE_F32 && a->dtype != LLA_DTYPE_BF16)
+    return fail(LLA_ERR_INVALID_ARG, "unknown dtype %d", a->dtype);
+  if (!a->q || !a->k || !a->v || !a->out)
+    return fail(LLA_ERR_INVALID_ARG, "q, k, v and out must be non-NULL");
+  if (a->B < 1 || a->H < 1 || a->n < 1)
+    return fail(LLA_ERR_INVALID_ARG, "B, H, n must be >= 1 (B=%d H=%d n=%d)", a->B, a->H, a->n);
+  if (!lla::decode_supported(a->d)) return fail(LLA_ERR_UNSUPPORTED, "decode: d=%d not in {64,128}", a->d);
+  if (!std::isfinite(a->lambda) || !(a->lambda > 0.f))
+    return fail(LLA_ERR_INVALID_ARG, "lambda must be finite and > 0 (got %g)", (double)a->lambda);
+  if (a->cg_max_iters < 0 || a->cg_max_iters > 100000)
+    return fail(LLA_ERR_INVALID_ARG, "cg_max_iters must be in [0, 100000] (got %d)", a->cg_max_iters);
+  if (!(a->cg_rel_tol >= 0.f) || !std::isfinite(a->cg_rel_tol))
+    return fail(LLA_ERR_INVALID_ARG, "cg_rel_tol must be finite and >= 0 (got %g)", (double)a->cg_rel_tol);
+  const unsigned long long bh = (unsigned long long)a->B * (unsigned long long)a->H;
+  if (bh > 65535ULL) return fail(LLA_ERR_UNSUPPORTED, "decode: B*H = %llu > 65535", bh);
+  const unsigned long long keys = bh * (unsigned long long)a->n;
+  if (keys > (1ULL << 36)) return fail(LLA_ERR_UNSUPPORTED, "B*H*n too large");
+  const size_t esz = a->dtype == LLA_DTYPE_F32 ? 4 : 2;
+  const size_t nq = (size_t)bh * a->d * esz, nkv = (size_t)keys * a->d * esz;
+  const size_t nout = (size_t)bh * a->d * 4, nrow = (size_t)bh * 4;
+  struct In { const void* p; size_t bytes; };
+  const In ins[3] = {{a->q, nq}, {a->k, nkv}, {a->v, nkv}};
+  for (const In& in : ins)
+    if (!aligned16(in.p)) return fail(LLA_ERR_INVALID_ARG, "input pointer %p not 16-byte aligned", in.p);
+  struct Out { const void* p; size_t bytes; const char* name; };
+  const Out outs[6] = {{a->out, nout, "out"},           {a->rho, nout, "rho"},
+                       {a->omega, nrow, "omega"},       {a->rowmax, nrow, "rowmax"},
+                       {a->cg_iters, nrow, "cg_iters"}, {a->cg_resid, nrow, "cg_resid"}};
+  for (int i = 0; i < 6; ++i) {
+    if (!outs[i].p) continue;
+    if (!aligned16(outs[i].p))
+      return fail(LLA_ERR_INVALID_ARG, "%s pointer %p not 16-byte aligned", outs[i].name, outs[i].p);
+    for (const In& in : ins)
+      if (overlap(outs[i].p, outs[i].bytes, in.p, in.bytes))
+        return fail(LLA_ERR_INVALID_ARG, "%s overlaps an input", outs[i].name);
+    for (int j = 0; j < i; ++j)
+      if (overlap(outs[i].p, outs[i].bytes, outs[j].p, outs[j].bytes))
+        return fail(LLA_ERR_INVALID_ARG, "%s overlaps %s", outs[i].name, outs[j].name);
+  }
+  if (a->workspace && !aligned16(a->workspace))
+    return fail(LLA_ERR_INVALID_ARG, "workspace pointer not 16-byte aligned");
+  lla::DecodeParams p{};
+  p.q = a->q; p.k = a->k; p.v = a->v; p.out = a->out;
+  p.omega = a->omega; p.rho = a->rho; p.rowmax = a->rowmax;
+  p.cg_iters = a->cg_iters; p.cg_resid = a->cg_resid;
+  p.BH = (int)bh; p.n = a->n; p.d = a->d; p.dtype = a->dtype;
+  p.lambda = a->lambda; p.cg_max_iters = a->cg_max_iters; p.cg_rel_tol = a->cg_rel_tol;
+  p.ev_main_begin = a->ev_main_begin;
+  p.ev_main_end = a->ev_main_end;
+  const size_t need = lla::decode_workspace_bytes(p.BH, p.n, p.d);
+  void* ws = a->workspace;
+  bool owned = false;
+  if (ws) {
+    if (a->workspace_bytes < need)
+      return fail(LLA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", a->workspace_bytes, need);
+  } else {
+    const hipError_t e = hipMallocAsync(&ws, need, stream);
+    if (e != hipSuccess) return fail(LLA_ERR_HIP, "workspace allocation of %zu bytes: %s", need,
+                                     hipGetErrorString(e));
+    owned = true;
+  }
+  p.workspace = ws;
+  p.workspace_bytes = owned ? need : a->workspace_bytes;
+  const hipError_t e = lla::launch_decode(p, stream);
+  if (owned) {
+    const hipError_t f = hipFreeAsync(ws, stream);
+    if (e == hipSuccess && f != hipSuccess)
+      return fail(LLA_ERR_HIP, "workspace free: %s", hipGetErrorString(f));
+  }
+  if (e != hipSuccess) return fail(LLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  return LLA_OK;
+}
+
+size_t lla_decode_workspace_bytes(int B, int H, int n, int d, int dtype) {
+  if (B < 1 || H < 1 || n < 1 || !lla::decode_supported(d)) return 0;
+  if (dtype != LLA_DTYPE_F32 && dtype != LLA_DTYPE_BF16) return 0;
+  const unsigned long long bh = (unsigned long long)B * (unsigned long long)H;
+  if (bh > 65535ULL || bh * (unsigned long long)n > (1ULL << 36)) return 0;
+  return lla::decode_workspace_bytes((int)bh, n, d);
+}
+
 int lla_forward_f32(const float* q, const float* k, const float* v, float* out, int B, int H, int n,
                     int d, float lambda, int cg_max_iters, float cg_rel_tol, hipStream_t stream) {
   lla_fwd_args a{};

@@ -1,0 +1,482 @@
+// Decode-shaped LLA forward: one new query per (batch, head) against a cache
+// of n keys and values, all of them visible (the last row of a causal forward
+// whose query sits at position n - 1). Same estimator and CG policy as the
+// blocked forward ("Local Linear Attention: reading notes", section 2.1,
+// Eqs. (6)-(8); the CG of section 2.2 on the system centred at the weighted key
+// mean, as described in include/lla.h).
+//
+// With a single query per head the matrix-free CG of the blocked forward has
+// nothing to share a key fragment with: each iteration would re-read the whole
+// cache for 2d multiply-adds per key on the vector ALU. Here the centred Gram
+// matrix of the one query,
+//     G = sum_j w_j (k_j - kbar)(k_j - kbar)^T        (d x d, independent of n),
+// is formed once, as a dense product on the matrix cores split over the keys,
+// and the CG iterations run on G + lambda I held in LDS: d^2 multiply-adds per
+// iteration instead of 2 n d, and the cache is read three times in all (scores
+// and moments, Gram, output) whatever the iteration count. In exact arithmetic
+// the CG iterates are those of the matrix-free CG on the same system.
+//
+// Five kernels, the keys of each head split into S chunks of L:
+//   dec_moments  (S x BH)  scores c q.k_j (kept, log2 units), chunk max, omega
+//                          and mu~ partials;
+//   dec_gram     (S x BH)  combines the partials into m, omega, kbar; the chunk's
+//                          contribution to G on v_mfma_f32_32x32x16_f16, each
+//                          operand carried as two fp16 terms (hi + lo, ~22
+//                          bits): hi.hi + hi.lo + lo.hi;
+//   dec_solve    (BH)      sums the chunk Grams, adds lambda I, runs CG on
+//                          G rho_c = mu = omega (kbar - q);
+//   dec_output   (S x BH)  a_j = w_j (1 - (k_j - kbar).rho_c): partial sums of
+//                          a_j v_j and a_j;
+//   dec_finish   (BH)      out = sum a_j v_j / sum a_j.
+// No workgroup waits on another inside a kernel.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include <algorithm>
+
+#include "lla_internal.h"
+#include "../../include/lla.h"
+
+namespace lla {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int DT = 256;        // threads per workgroup (four waves)
+constexpr int GK = 32;         // keys per Gram tile
+constexpr int GLD = GK + 8;    // LDS row stride (halfs) of the transposed Gram operands
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct DecParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* out;
+  float* omega;
+  float* rho;
+  float* rowmax;
+  int32_t* cg_iters;
+  float* cg_resid;
+  float* s;      // [BH][n] scores c q.k_j in log2 units
+  float* p1;     // [BH][S][2 + d] chunk max, omega, mu~ (relative to the chunk max)
+  float* gram;   // [BH][S][d][d] chunk Grams
+  float* st;     // [BH][2 d + 2] rho_c, kbar, m, omega
+  float* p4;     // [BH][S][d + 1] sum a_j v_j, sum a_j
+  int BH, n, S, L;
+  float lambda;
+  int cg_max_iters;
+  float cg_rel_tol;
+};
+
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
+
+// the EPL = d / 64 consecutive elements of a row that lane `lane` owns
+template <int D, typename T>
+__device__ __forceinline__ void load_lane(const T* row, int lane, float (&x)[D / 64]) {
+  #pragma unroll
+  for (int e = 0; e < D / 64; ++e) x[e] = to_f(row[lane * (D / 64) + e]);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  #pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// m (log2 units), omega and kbar of head bh from the S chunk partials:
+// m = max_c m_c, omega = sum_c omega_c 2^(m_c - m), mu~ likewise, kbar = mu~ / omega.
+// Threads t < D write kbar[t]; thread 0 writes mo[0] = m, mo[1] = omega.
+template <int D>
+__device__ __forceinline__ void combine_moments(const DecParams& P, int bh, float* kbar, float* mo) {
+  const float* base = P.p1 + static_cast<size_t>(bh) * P.S * (D + 2);
+  float m = -INFINITY;
+  for (int c = 0; c < P.S; ++c) m = fmaxf(m, base[c * (D + 2)]);
+  float om = 0.f, mu = 0.f;
+  const int t = threadIdx.x;
+  for (int c = 0; c < P.S; ++c) {
+    const float* pc = base + c * (D + 2);
+    if (pc[0] == -INFINITY) continue;
+    const float a = exp2f(pc[0] - m);
+    om += pc[1] * a;
+    if (t < D) mu += pc[2 + t] * a;
+  }
+  if (t < D) kbar[t] = mu / om;
+  if (t == 0) {
+    mo[0] = m;
+    mo[1] = om;
+  }
+}
+
+// --------------------------- scores and moments ----------------------------
+template <int D, typename T>
+__global__ __launch_bounds__(DT) void dec_moments(DecParams P) {
+  constexpr int EPL = D / 64;
+  __shared__ float sm[DT / 64], som[DT / 64];
+  __shared__ float smu[DT / 64][D];
+  const int sp = blockIdx.x, bh = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c0 = sp * P.L, c1 = min(P.n, c0 + P.L);
+  const T* K = static_cast<const T*>(P.k) + static_cast<size_t>(bh) * P.n * D;
+  float qd[EPL];
+  load_lane<D>(static_cast<const T*>(P.q) + static_cast<size_t>(bh) * D, lane, qd);
+  const float cs = kLog2e / sqrtf(static_cast<float>(D));
+  float m = -INFINITY, om = 0.f, mu[EPL];
+  #pragma unroll
+  for (int e = 0; e < EPL; ++e) mu[e] = 0.f;
+  for (int j = c0 + wave; j < c1; j += DT / 64) {
+    float kd[EPL];
+    load_lane<D>(K + static_cast<size_t>(j) * D, lane, kd);
+    float part = 0.f;
+    #pragma unroll
+    for (int e = 0; e < EPL; ++e) part += qd[e] * kd[e];
+    const float sj = wave_sum(part) * cs;  // the same in every lane
+    if (lane == 0) P.s[static_cast<size_t>(bh) * P.n + j] = sj;
+    if (sj > m) {  // wave-uniform; exp2(-inf) = 0 on the first key
+      const float a = exp2f(m - sj);
+      om *= a;
+      #pragma unroll
+      for (int e = 0; e < EPL; ++e) mu[e] *= a;
+      m = sj;
+    }
+    const float w = exp2f(sj - m);
+    om += w;
+    #pragma unroll
+    for (int e = 0; e < EPL; ++e) mu[e] += w * kd[e];
+  }
+  if (lane == 0) {
+    sm[wave] = m;
+    som[wave] = om;
+  }
+  #pragma unroll
+  for (int e = 0; e < EPL; ++e) smu[wave][lane * EPL + e] = mu[e];
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < D) {
+    float mc = -INFINITY;
+    #pragma unroll
+    for (int w = 0; w < DT / 64; ++w) mc = fmaxf(mc, sm[w]);
+    float o = 0.f, u = 0.f;
+    #pragma unroll
+    for (int w = 0; w < DT / 64; ++w) {
+      if (sm[w] == -INFINITY) continue;
+      const float a = exp2f(sm[w] - mc);
+      o += som[w] * a;
+      u += smu[w][t] * a;
+    }
+    float* dst = P.p1 + (static_cast<size_t>(bh) * P.S + sp) * (D + 2);
+    if (t == 0) {
+      dst[0] = mc;
+      dst[1] = o;
+    }
+    dst[2 + t] = u;
+  }
+}
+
+// ------------------------------ chunk Gram ---------------------------------
+template <int D, typename T>
+__global__ __launch_bounds__(DT) void dec_gram(DecParams P) {
+  constexpr int NB = D / 32;              // 32-row blocks of G
+  constexpr int TPW = NB * NB / (DT / 64);  // output tiles per wave
+  static_assert(TPW >= 1 && NB * NB % (DT / 64) == 0, "tiles must spread over the waves");
+  __shared__ __align__(16) _Float16 cHi[D * GLD], cLo[D * GLD], wHi[D * GLD], wLo[D * GLD];
+  __shared__ float skb[D];
+  __shared__ float sw[GK];
+  __shared__ float smo[2];
+  const int sp = blockIdx.x, bh = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, ql = lane & 31, g = lane >> 5;
+  combine_moments<D>(P, bh, skb, smo);
+  __syncthreads();
+  const float m = smo[0];
+  const int c0 = sp * P.L, c1 = min(P.n, c0 + P.L);
+  const T* K = static_cast<const T*>(P.k) + static_cast<size_t>(bh) * P.n * D;
+  const float* S = P.s + static_cast<size_t>(bh) * P.n;
+  floatx16 acc[TPW];
+  #pragma unroll
+  for (int u = 0; u < TPW; ++u)
+    #pragma unroll
+    for (int r = 0; r < 16; ++r) acc[u][r] = 0.f;
+  for (int t0 = c0; t0 < c1; t0 += GK) {
+    if (tid < GK) sw[tid] = (t0 + tid < c1) ? exp2f(S[t0 + tid] - m) : 0.f;
+    __syncthreads();
+    // transposed operands: row d holds keys t0 .. t0 + 31 of c = k - kbar and of
+    // w c, each as fp16 hi + lo; a work item is one d and 8 consecutive keys
+    for (int it = tid; it < D * (GK / 8); it += DT) {
+      const int d = it % D, kg = it / D;
+      half8 ch, cl, wh, wl;
+      #pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int kk = 8 * kg + e, j = t0 + kk;
+        const float c = j < c1 ? to_f(K[static_cast<size_t>(j) * D + d]) - skb[d] : 0.f;
+        const float wc = sw[kk] * c;
+        ch[e] = static_cast<_Float16>(c);
+        cl[e] = static_cast<_Float16>(c - static_cast<float>(ch[e]));
+        wh[e] = static_cast<_Float16>(wc);
+        wl[e] = static_cast<_Float16>(wc - static_cast<float>(wh[e]));
+      }
+      *reinterpret_cast<half8*>(cHi + d * GLD + 8 * kg) = ch;
+      *reinterpret_cast<half8*>(cLo + d * GLD + 8 * kg) = cl;
+      *reinterpret_cast<half8*>(wHi + d * GLD + 8 * kg) = wh;
+      *reinterpret_cast<half8*>(wLo + d * GLD + 8 * kg) = wl;
+    }
+    __syncthreads();
+    #pragma unroll
+    for (int ks = 0; ks < GK / 16; ++ks)
+      #pragma unroll
+      for (int u = 0; u < TPW; ++u) {
+        const int ti = wave + (DT / 64) * u, I = ti / NB, J = ti % NB;
+        const int ao = (32 * I + ql) * GLD + 16 * ks + 8 * g;
+        const int bo = (32 * J + ql) * GLD + 16 * ks + 8 * g;
+        const half8 ah = *reinterpret_cast<const half8*>(cHi + ao);
+        const half8 al = *reinterpret_cast<const half8*>(cLo + ao);
+        const half8 bhv = *reinterpret_cast<const half8*>(wHi + bo);
+        const half8 blv = *reinterpret_cast<const half8*>(wLo + bo);
+        acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bhv, acc[u], 0, 0, 0);
+        acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, blv, acc[u], 0, 0, 0);
+        acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bhv, acc[u], 0, 0, 0);
+      }
+    __syncthreads();  // the next tile overwrites the operands
+  }
+  // accumulator register r of lane (ql, g) holds row 8 (r / 4) + 4 g + r % 4,
+  // column ql of its 32 x 32 tile
+  float* G = P.gram + (static_cast<size_t>(bh) * P.S + sp) * D * D;
+  #pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int ti = wave + (DT / 64) * u, I = ti / NB, J = ti % NB;
+    #pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = 32 * I + 8 * (r >> 2) + 4 * g + (r & 3);
+      G[i * D + 32 * J + ql] = acc[u][r];
+    }
+  }
+}
+
+// ---------------------------------- solve ----------------------------------
+// Block-wide sum of one value per thread of the first D threads (the others
+// pass 0); every thread gets the total.
+template <int D>
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = wave_sum(v);
+  __syncthreads();  // red may still be read by the previous call
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float s = 0.f;
+  #pragma unroll
+  for (int w = 0; w < DT / 64; ++w) s += red[w];
+  return s;
+}
+
+template <int D, typename T>
+__global__ __launch_bounds__(DT) void dec_solve(DecParams P) {
+  constexpr int LG = D + 1;          // row stride of G in LDS
+  constexpr int NP = DT / D;         // column parts of the matrix-vector product
+  __shared__ float sG[D * LG];
+  __shared__ float skb[D], sp_[D], spart[NP][D];
+  __shared__ float smo[2], red[DT / 64];
+  const int bh = blockIdx.x, t = threadIdx.x;
+  combine_moments<D>(P, bh, skb, smo);
+  // G + lambda I from the chunk Grams (coalesced over the d^2 entries)
+  const float* Gc = P.gram + static_cast<size_t>(bh) * P.S * D * D;
+  for (int idx = t; idx < D * D; idx += DT) {
+    float a = 0.f;
+    for (int c = 0; c < P.S; ++c) a += Gc[static_cast<size_t>(c) * D * D + idx];
+    const int i = idx / D, j = idx % D;
+    sG[i * LG + j] = a + (i == j ? P.lambda : 0.f);
+  }
+  __syncthreads();
+  const float m = smo[0], om = smo[1];
+  // CG on (G + lambda I) x = mu = omega (kbar - q): thread t < D owns element t
+  const bool own = t < D;
+  float qv = 0.f, kb = 0.f, x = 0.f, r = 0.f, p = 0.f;
+  if (own) {
+    qv = to_f(static_cast<const T*>(P.q)[static_cast<size_t>(bh) * D + t]);
+    kb = skb[t];
+    r = om * (kb - qv);
+    p = r;
+  }
+  float rr = block_sum<D>(own ? r * r : 0.f, red);
+  const float r0 = sqrtf(rr);
+  const float thr = P.cg_rel_tol * r0;
+  bool active = rr > 0.f && P.cg_max_iters > 0;
+  int iters = 0;
+  const int row = t % D, part = t / D;
+  for (int it = 0; it < P.cg_max_iters && active; ++it) {  // `active` is block-uniform
+    if (own) sp_[t] = p;
+    __syncthreads();
+    float ap = 0.f;
+    #pragma unroll 8
+    for (int c = part * (D / NP); c < (part + 1) * (D / NP); ++c) ap += sG[row * LG + c] * sp_[c];
+    spart[part][row] = ap;
+    __syncthreads();
+    float Ap = 0.f;
+    if (own) {
+      #pragma unroll
+      for (int h = 0; h < NP; ++h) Ap += spart[h][t];
+    }
+    const float pAp = block_sum<D>(own ? p * Ap : 0.f, red);
+    if (!(pAp > 0.f)) break;  // breakdown: keep the iterate
+    const float al = rr / pAp;
+    x += al * p;
+    r -= al * Ap;
+    const float rrn = block_sum<D>(own ? r * r : 0.f, red);
+    ++iters;
+    if (sqrtf(rrn) <= thr || rrn == 0.f) {
+      rr = rrn;
+      break;
+    }
+    p = r + (rrn / rr) * p;
+    rr = rrn;
+  }
+  // state for the output scan; the pages' rho_i = rho_c / (1 + (kbar - q).rho_c)
+  const float kq = block_sum<D>(own ? (kb - qv) * x : 0.f, red);
+  if (own) {
+    float* st = P.st + static_cast<size_t>(bh) * (2 * D + 2);
+    st[t] = x;
+    st[D + t] = kb;
+    if (t == 0) {
+      st[2 * D] = m;
+      st[2 * D + 1] = om;
+    }
+    if (P.rho) P.rho[static_cast<size_t>(bh) * D + t] = x / (1.f + kq);
+  }
+  if (t == 0) {
+    if (P.omega) P.omega[bh] = om;
+    if (P.rowmax) P.rowmax[bh] = m * kLn2;
+    if (P.cg_iters) P.cg_iters[bh] = iters;
+    if (P.cg_resid) P.cg_resid[bh] = r0 > 0.f ? sqrtf(rr) / r0 : 0.f;
+  }
+}
+
+// ---------------------------------- output ---------------------------------
+template <int D, typename T>
+__global__ __launch_bounds__(DT) void dec_output(DecParams P) {
+  constexpr int EPL = D / 64;
+  __shared__ float sden[DT / 64];
+  __shared__ float so[DT / 64][D];
+  const int sp = blockIdx.x, bh = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c0 = sp * P.L, c1 = min(P.n, c0 + P.L);
+  const float* st = P.st + static_cast<size_t>(bh) * (2 * D + 2);
+  float xr[EPL], kr = 0.f;
+  #pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    xr[e] = st[lane * EPL + e];
+    kr += st[D + lane * EPL + e] * xr[e];
+  }
+  kr = wave_sum(kr);
+  const float m = st[2 * D];
+  const T* K = static_cast<const T*>(P.k) + static_cast<size_t>(bh) * P.n * D;
+  const T* V = static_cast<const T*>(P.v) + static_cast<size_t>(bh) * P.n * D;
+  const float* S = P.s + static_cast<size_t>(bh) * P.n;
+  float o[EPL], den = 0.f;
+  #pragma unroll
+  for (int e = 0; e < EPL; ++e) o[e] = 0.f;
+  for (int j = c0 + wave; j < c1; j += DT / 64) {
+    float kd[EPL], vd[EPL];
+    load_lane<D>(K + static_cast<size_t>(j) * D, lane, kd);
+    load_lane<D>(V + static_cast<size_t>(j) * D, lane, vd);
+    float part = 0.f;
+    #pragma unroll
+    for (int e = 0; e < EPL; ++e) part += kd[e] * xr[e];
+    const float a = exp2f(S[j] - m) * (1.f - (wave_sum(part) - kr));
+    den += a;
+    #pragma unroll
+    for (int e = 0; e < EPL; ++e) o[e] += a * vd[e];
+  }
+  if (lane == 0) sden[wave] = den;
+  #pragma unroll
+  for (int e = 0; e < EPL; ++e) so[wave][lane * EPL + e] = o[e];
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t <= D) {
+    float a = 0.f;
+    #pragma unroll
+    for (int w = 0; w < DT / 64; ++w) a += t < D ? so[w][t] : sden[w];
+    P.p4[(static_cast<size_t>(bh) * P.S + sp) * (D + 1) + t] = a;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(DT) void dec_finish(DecParams P) {
+  const int bh = blockIdx.x, t = threadIdx.x;
+  if (t >= D) return;
+  const float* p4 = P.p4 + static_cast<size_t>(bh) * P.S * (D + 1);
+  float o = 0.f, den = 0.f;
+  for (int c = 0; c < P.S; ++c) {
+    o += p4[c * (D + 1) + t];
+    den += p4[c * (D + 1) + D];
+  }
+  P.out[static_cast<size_t>(bh) * D + t] = o / den;
+}
+
+size_t al256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+struct DecLayout {
+  int S, L;
+  size_t s, p1, gram, st, p4, total;  // byte offsets
+};
+
+DecLayout dec_layout(int BH, int n, int d) {
+  DecLayout o{};
+  // about two workgroups per compute unit, at least 64 keys per chunk
+  int S = (512 + BH - 1) / BH;
+  S = std::max(1, std::min(S, std::min(64, (n + 63) / 64)));
+  o.L = (n + S - 1) / S;
+  o.S = (n + o.L - 1) / o.L;  // every chunk non-empty
+  size_t off = 0;
+  o.s = off;    off += al256(static_cast<size_t>(BH) * n * sizeof(float));
+  o.p1 = off;   off += al256(static_cast<size_t>(BH) * o.S * (d + 2) * sizeof(float));
+  o.gram = off; off += al256(static_cast<size_t>(BH) * o.S * d * d * sizeof(float));
+  o.st = off;   off += al256(static_cast<size_t>(BH) * (2 * d + 2) * sizeof(float));
+  o.p4 = off;   off += al256(static_cast<size_t>(BH) * o.S * (d + 1) * sizeof(float));
+  o.total = off;
+  return o;
+}
+
+template <int D, typename T>
+hipError_t launch_dec(const DecodeParams& p, hipStream_t stream) {
+  const DecLayout ly = dec_layout(p.BH, p.n, D);
+  char* ws = static_cast<char*>(p.workspace);
+  DecParams P{};
+  P.q = p.q; P.k = p.k; P.v = p.v; P.out = p.out;
+  P.omega = p.omega; P.rho = p.rho; P.rowmax = p.rowmax; P.cg_iters = p.cg_iters; P.cg_resid = p.cg_resid;
+  P.s = reinterpret_cast<float*>(ws + ly.s);
+  P.p1 = reinterpret_cast<float*>(ws + ly.p1);
+  P.gram = reinterpret_cast<float*>(ws + ly.gram);
+  P.st = reinterpret_cast<float*>(ws + ly.st);
+  P.p4 = reinterpret_cast<float*>(ws + ly.p4);
+  P.BH = p.BH; P.n = p.n; P.S = ly.S; P.L = ly.L;
+  P.lambda = p.lambda; P.cg_max_iters = p.cg_max_iters; P.cg_rel_tol = p.cg_rel_tol;
+  const dim3 gs(ly.S, p.BH), gh(p.BH);
+  hipLaunchKernelGGL((dec_moments<D, T>), gs, dim3(DT), 0, stream, P);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.ev_main_begin && (e = hipEventRecord(p.ev_main_begin, stream)) != hipSuccess) return e;
+  hipLaunchKernelGGL((dec_gram<D, T>), gs, dim3(DT), 0, stream, P);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (p.ev_main_end && (e = hipEventRecord(p.ev_main_end, stream)) != hipSuccess) return e;
+  hipLaunchKernelGGL((dec_solve<D, T>), gh, dim3(DT), 0, stream, P);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((dec_output<D, T>), gs, dim3(DT), 0, stream, P);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((dec_finish<D>), gh, dim3(DT), 0, stream, P);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool decode_supported(int d) { return d == 64 || d == 128; }
+
+size_t decode_workspace_bytes(int BH, int n, int d) { return dec_layout(BH, n, d).total; }
+
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
+  if (p.dtype == LLA_DTYPE_BF16)
+    return p.d == 128 ? launch_dec<128, uint16_t>(p, stream) : launch_dec<64, uint16_t>(p, stream);
+  return p.d == 128 ? launch_dec<128, float>(p, stream) : launch_dec<64, float>(p, stream);
+}
+
+}  // namespace lla

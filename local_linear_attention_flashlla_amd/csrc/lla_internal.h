@@ -34,6 +34,33 @@ struct FwdParams {
   hipEvent_t ev_main_end;
 };
 
+// Everything a decode launch needs, already validated by the host API.
+struct DecodeParams {
+  const void* q;     // [BH][d]
+  const void* k;     // [BH][n][d]
+  const void* v;     // [BH][n][d]
+  float* out;        // [BH][d]
+  float* omega;      // optional [BH]
+  float* rho;        // optional [BH][d]
+  float* rowmax;     // optional [BH]
+  int32_t* cg_iters; // optional [BH]
+  float* cg_resid;   // optional [BH]
+  int BH, n, d, dtype;
+  float lambda;
+  int cg_max_iters;
+  float cg_rel_tol;
+  void* workspace;
+  size_t workspace_bytes;
+  hipEvent_t ev_main_begin;  // optional, recorded around the Gram kernel
+  hipEvent_t ev_main_end;
+};
+
+// decode-shaped forward (one query per head against n keys): d in {64,128},
+// fp32 or bf16 inputs
+bool decode_supported(int d);
+size_t decode_workspace_bytes(int BH, int n, int d);
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+
 // fp32 vector-ALU kernel (any d in {16,32,64,128}, fp32 or bf16 inputs).
 hipError_t launch_valu(const FwdParams& p, hipStream_t stream);
 

@@ -456,7 +456,6 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
   const int kmax = qvalid ? qi : -1;      // last key this lane's query sees
   const int wfirst = i0 + 32 * wave;      // first query of the wave
   const bool wave_any = wfirst < n;
-  const bool wave_full = wfirst + 31 < n;
   const int wlast = wave_any ? min(ntiles - 1, (wfirst + 31) / BK) : -1;  // last tile of the wave
 
   if (tid == 0) head_scales(P.partial, bh, P.nchunk, &sScale[0], &sScale[1]);

@@ -113,6 +113,43 @@ def test_output_given_rho_rejects_invalid_arguments(lib, rho_in, kw, status):
     assert _lib.last_error() != ""
 
 
+def _dargs(**kw):
+    a = _lib.LlaDecodeArgs()
+    a.dtype = kw.get("dtype", _lib.LLA_DTYPE_BF16)
+    a.q, a.k, a.v, a.out = BASE, BASE + GAP, BASE + 2 * GAP, BASE + 3 * GAP
+    a.B, a.H, a.n, a.d = 2, 3, 100, 128
+    a.lambda_ = 1.0
+    a.cg_max_iters = 8
+    a.cg_rel_tol = 0.0
+    for key, val in kw.items():
+        setattr(a, key, val)
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("q", 0, -1), ("k", 0, -1), ("v", 0, -1), ("out", 0, -1),
+    ("B", 0, -1), ("n", 0, -1), ("d", 32, -2), ("d", 16, -2),
+    ("lambda_", 0.0, -1), ("cg_max_iters", -1, -1), ("cg_rel_tol", float("nan"), -1),
+    ("dtype", 5, -1), ("H", 70000, -2),
+    ("k", BASE + GAP + 8, -1),            # misaligned
+    ("out", BASE + GAP + 512, -1),        # overlaps k
+    ("rho", BASE + 3 * GAP + 256, -1),    # overlaps out ([B][H][d] fp32 = 3 KiB)
+])
+def test_decode_invalid_arguments_are_rejected_on_the_host(lib, field, value, status):
+    a = _dargs(**{field: value})
+    assert lib.lla_decode_ex(ctypes.byref(a), None) == status
+    assert _lib.last_error() != ""
+
+
+def test_decode_workspace_is_linear_in_n(lib):
+    assert lib.lla_decode_workspace_bytes(1, 1, 100, 32, _lib.LLA_DTYPE_BF16) == 0
+    sizes = [lib.lla_decode_workspace_bytes(4, 8, n, 128, _lib.LLA_DTYPE_BF16)
+             for n in (4096, 8192, 16384)]
+    assert all(s > 0 for s in sizes)
+    # the score buffer grows with n; the Gram partials do not
+    assert sizes[1] - sizes[0] >= 4 * 8 * 4096 * 4 and sizes[2] - sizes[1] >= 4 * 8 * 8192 * 4
+
+
 def test_null_args_pointer(lib):
     assert lib.lla_forward_ex(None, None) == -1
 
@@ -151,7 +188,9 @@ def test_rejected_call_leaves_no_stale_error_after_success_path(lib):
     assert "B, H, n" in _lib.last_error()
 
 
-def test_struct_layout_matches_c_compiler(tmp_path):
+@pytest.mark.parametrize("cname,mirror", [("lla_fwd_args", "LlaFwdArgs"),
+                                           ("lla_decode_args", "LlaDecodeArgs")])
+def test_struct_layout_matches_c_compiler(tmp_path, cname, mirror):
     """Compile a tiny C program against include/lla.h with the host compiler
     and compare offsetof() of every field with the ctypes mirror."""
     import shutil
@@ -159,16 +198,17 @@ def test_struct_layout_matches_c_compiler(tmp_path):
     cc = shutil.which("gcc") or shutil.which("cc")
     if cc is None:
         pytest.skip("no host C compiler")
-    fields = [f[0] for f in _lib.LlaFwdArgs._fields_]
+    M = getattr(_lib, mirror)
+    fields = [f[0] for f in M._fields_]
     cfields = ["lambda" if f == "lambda_" else f for f in fields]
     src = tmp_path / "layout.c"
-    body = "\n".join(f'  printf("%zu\\n", offsetof(lla_fwd_args, {f}));' for f in cfields)
+    body = "\n".join(f'  printf("%zu\\n", offsetof({cname}, {f}));' for f in cfields)
     src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "lla.h"\nint main(void){\n'
-                   + body + '\n  printf("%zu\\n", sizeof(lla_fwd_args));\n  return 0;\n}\n')
+                   + body + f'\n  printf("%zu\\n", sizeof({cname}));\n  return 0;\n}}\n')
     exe = tmp_path / "layout"
     subprocess.run([cc, "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
                     "-I", "/opt/rocm/include", str(src), "-o", str(exe)], check=True)
     got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True,
                                           text=True).stdout.split()]
-    want = [getattr(_lib.LlaFwdArgs, f).offset for f in fields] + [ctypes.sizeof(_lib.LlaFwdArgs)]
+    want = [getattr(M, f).offset for f in fields] + [ctypes.sizeof(M)]
     assert got == want
