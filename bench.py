@@ -202,6 +202,74 @@ def bench_given_rho(args, torch, lla, wl, q, k, v, out, ws, kernel, kernel_used)
     return 0
 
 
+def bench_decode(args, torch, lla, dev):
+    """Decode throughput: one new query per (batch, head) against n-key caches
+    of the workload's shape (the workload's generator for one batch element,
+    tiled over --decode-batch). Queries/s = heads answered per second. The
+    cache is read three times per call (scores, Gram, output) plus V once;
+    the roofline line is the Gram kernel (2 n d^2 FLOPs per head, fp16 MFMA,
+    three products per key block for the two-term operands)."""
+    from local_linear_attention_flashlla_amd.workloads import make_workload
+    wl = make_workload(args.workload, B=1)
+    B = args.decode_batch if args.decode_batch > 0 else {"standard": 4, "long": 1, "recall": 8}.get(
+        args.workload, 1)
+    H, n, d = wl.H, wl.n, wl.d
+    if wl.dtype == "f32":
+        up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    else:
+        up = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    k1, v1 = up(wl.k_dev), up(wl.v_dev)
+    q1 = up(wl.q_dev[:, :, n - 1])
+    k = k1.expand(B, H, n, d).contiguous()
+    v = v1.expand(B, H, n, d).contiguous()
+    q = q1.expand(B, H, d).contiguous()
+    out = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(lla.decode_workspace_bytes(B, H, n, d, wl.dtype), 16), dtype=torch.uint8,
+                     device=dev)
+    iters = torch.empty((B, H), dtype=torch.int32, device=dev)
+    lla.decode(q, k, v, wl.lam, wl.cg_max_iters, wl.cg_rel_tol, out=out, workspace=ws,
+               cg_iters=iters)
+    torch.cuda.synchronize()
+
+    def step(events=None):
+        lla.decode(q, k, v, wl.lam, wl.cg_max_iters, wl.cg_rel_tol, out=out, workspace=ws,
+                   events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    steps = max(args.steps, 20)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events=ev[i])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    gram_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    esz = 2 if wl.dtype == "bf16" else 4
+    cache = B * H * n * d * esz
+    gram_flops = 2.0 * B * H * n * d * d
+    rec = {
+        "metric": "LLA decode queries/s (one new query per head), 1 MI355X",
+        "value": B * H / (ms * 1e-3), "unit": "queries/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": f"decode over the {wl.name} caches", "B": B, "H": H, "n": n, "d": d,
+                   "lambda": wl.lam, "cg_max_iters": wl.cg_max_iters, "cg_rel_tol": wl.cg_rel_tol},
+        "cg_iters_mean": float(iters.float().mean().item()),
+        "cache_bytes_k_plus_v": 2 * cache,
+        "cache_read_rate_GBps": (4 * cache) / (ms * 1e-3) / 1e9,
+        "main_kernel": "Gram kernel", "main_kernel_ms": gram_ms,
+        "roofline": {"bound": "mfma", "achieved": gram_flops / (gram_ms * 1e-3) / 1e12,
+                     "peak": PEAK["mfma_fp16"], "unit": "TFLOP/s",
+                     "frac": gram_flops / (gram_ms * 1e-3) / 1e12 / PEAK["mfma_fp16"],
+                     "traffic": None},
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -222,6 +290,11 @@ def main(argv=None):
     ap.add_argument("--given-rho", action="store_true",
                     help="time lla_output_given_rho (moment and output scans, the CG solve "
                          "replaced by a supplied rho) instead of the full forward")
+    ap.add_argument("--decode", action="store_true",
+                    help="time lla_decode_ex: one new query per head against the workload's "
+                         "key and value caches (its last row)")
+    ap.add_argument("--decode-batch", type=int, default=0,
+                    help="with --decode: batch size B (default: the workload's)")
     ap.add_argument("--memory-curve", action="store_true",
                     help="instead of timing, print the peak device memory of one forward at "
                          "n = 1k .. 16k (B=1, H=16, d=128) as one JSON line")
@@ -244,6 +317,9 @@ def main(argv=None):
     if args.memory_curve:
         print(json.dumps(memory_curve(torch, lla, dev)), flush=True)
         return 0
+
+    if args.decode:
+        return bench_decode(args, torch, lla, dev)
 
     wl = make_workload(args.workload)
     if wl.dtype == "f32":

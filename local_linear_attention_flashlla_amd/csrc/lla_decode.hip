@@ -19,7 +19,7 @@
 // Five kernels, the keys of each head split into S chunks of L:
 //   dec_moments  (S x BH)  scores c q.k_j (kept, log2 units), chunk max, omega
 //                          and mu~ partials;
-//   dec_gram     (S x BH)  combines the partials into m, omega, kbar; the chunk's
+//   dec_gram     (SG x BH) combines the partials into m, omega, kbar; the chunk's
 //                          contribution to G on v_mfma_f32_32x32x16_f16, each
 //                          operand carried as two fp16 terms (hi + lo, ~22
 //                          bits): hi.hi + hi.lo + lo.hi;
@@ -62,10 +62,11 @@ struct DecParams {
   float* cg_resid;
   float* s;      // [BH][n] scores c q.k_j in log2 units
   float* p1;     // [BH][S][2 + d] chunk max, omega, mu~ (relative to the chunk max)
-  float* gram;   // [BH][S][d][d] chunk Grams
+  float* gram;   // [BH][SG][d][d] chunk Grams
   float* st;     // [BH][2 d + 2] rho_c, kbar, m, omega
   float* p4;     // [BH][S][d + 1] sum a_j v_j, sum a_j
-  int BH, n, S, L;
+  int BH, n, S, L;     // key chunks of the score, moment and output kernels
+  int SG, LG;          // key chunks of the Gram kernel (fewer: each writes d^2 floats)
   float lambda;
   int cg_max_iters;
   float cg_rel_tol;
@@ -81,10 +82,23 @@ __device__ __forceinline__ void load_lane(const T* row, int lane, float (&x)[D /
   for (int e = 0; e < D / 64; ++e) x[e] = to_f(row[lane * (D / 64) + e]);
 }
 
+// Sum over the 64 lanes, the result in every lane, without the LDS crossbar:
+// DPP quad permutations (partners l ^ 1, l ^ 2), row half-mirror and mirror
+// (8- and 16-lane groups), then v_permlane16_swap and v_permlane32_swap,
+// which exchange 16- and 32-lane halves.
+template <int CTRL>
+__device__ __forceinline__ float dpp_partner(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-  #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += dpp_partner<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp_partner<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp_partner<0x141>(v);  // row_half_mirror
+  v += dpp_partner<0x140>(v);  // row_mirror
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // m (log2 units), omega and kbar of head bh from the S chunk partials:
@@ -127,25 +141,43 @@ __global__ __launch_bounds__(DT) void dec_moments(DecParams P) {
   float m = -INFINITY, om = 0.f, mu[EPL];
   #pragma unroll
   for (int e = 0; e < EPL; ++e) mu[e] = 0.f;
-  for (int j = c0 + wave; j < c1; j += DT / 64) {
-    float kd[EPL];
-    load_lane<D>(K + static_cast<size_t>(j) * D, lane, kd);
-    float part = 0.f;
+  // each wave takes batches of U consecutive keys: U rows in flight at once,
+  // U interleaved lane reductions
+  constexpr int U = 16;
+  for (int jb = c0 + wave * U; jb < c1; jb += (DT / 64) * U) {
+    float kd[U][EPL], part[U];
     #pragma unroll
-    for (int e = 0; e < EPL; ++e) part += qd[e] * kd[e];
-    const float sj = wave_sum(part) * cs;  // the same in every lane
-    if (lane == 0) P.s[static_cast<size_t>(bh) * P.n + j] = sj;
-    if (sj > m) {  // wave-uniform; exp2(-inf) = 0 on the first key
-      const float a = exp2f(m - sj);
-      om *= a;
+    for (int u = 0; u < U; ++u) {
+      if (jb + u < c1) {
+        load_lane<D>(K + static_cast<size_t>(jb + u) * D, lane, kd[u]);
+      } else {
+        #pragma unroll
+        for (int e = 0; e < EPL; ++e) kd[u][e] = 0.f;
+      }
+      part[u] = 0.f;
       #pragma unroll
-      for (int e = 0; e < EPL; ++e) mu[e] *= a;
-      m = sj;
+      for (int e = 0; e < EPL; ++e) part[u] += qd[e] * kd[u][e];
     }
-    const float w = exp2f(sj - m);
-    om += w;
     #pragma unroll
-    for (int e = 0; e < EPL; ++e) mu[e] += w * kd[e];
+    for (int u = 0; u < U; ++u) part[u] = wave_sum(part[u]);
+    #pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = jb + u;
+      if (j >= c1) break;  // wave-uniform
+      const float sj = part[u] * cs;  // the same in every lane
+      if (lane == u) P.s[static_cast<size_t>(bh) * P.n + j] = sj;
+      if (sj > m) {  // wave-uniform; exp2(-inf) = 0 on the first key
+        const float a = exp2f(m - sj);
+        om *= a;
+        #pragma unroll
+        for (int e = 0; e < EPL; ++e) mu[e] *= a;
+        m = sj;
+      }
+      const float w = exp2f(sj - m);
+      om += w;
+      #pragma unroll
+      for (int e = 0; e < EPL; ++e) mu[e] += w * kd[u][e];
+    }
   }
   if (lane == 0) {
     sm[wave] = m;
@@ -191,7 +223,7 @@ __global__ __launch_bounds__(DT) void dec_gram(DecParams P) {
   combine_moments<D>(P, bh, skb, smo);
   __syncthreads();
   const float m = smo[0];
-  const int c0 = sp * P.L, c1 = min(P.n, c0 + P.L);
+  const int c0 = sp * P.LG, c1 = min(P.n, c0 + P.LG);
   const T* K = static_cast<const T*>(P.k) + static_cast<size_t>(bh) * P.n * D;
   const float* S = P.s + static_cast<size_t>(bh) * P.n;
   floatx16 acc[TPW];
@@ -199,18 +231,38 @@ __global__ __launch_bounds__(DT) void dec_gram(DecParams P) {
   for (int u = 0; u < TPW; ++u)
     #pragma unroll
     for (int r = 0; r < 16; ++r) acc[u][r] = 0.f;
+  // a staging work item is one d and 8 consecutive keys of the tile; the
+  // items of the next tile are loaded into registers while this one computes
+  constexpr int IPT = D * (GK / 8) / DT;
+  static_assert(IPT * DT == D * (GK / 8), "items must spread evenly");
+  float cur[IPT][8], nxt[IPT][8], scur = 0.f, snxt = 0.f;
+  auto load_tile = [&](int tb, float (&buf)[IPT][8], float& sv) __attribute__((always_inline)) {
+    #pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      const int it = tid + DT * i, d = it % D, kg = it / D;
+      #pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = tb + 8 * kg + e;
+        buf[i][e] = j < c1 ? to_f(K[static_cast<size_t>(j) * D + d]) : 0.f;
+      }
+    }
+    if (tid < GK) sv = tb + tid < c1 ? S[tb + tid] : 0.f;
+  };
+  load_tile(c0, cur, scur);
   for (int t0 = c0; t0 < c1; t0 += GK) {
-    if (tid < GK) sw[tid] = (t0 + tid < c1) ? exp2f(S[t0 + tid] - m) : 0.f;
-    __syncthreads();
+    if (t0 + GK < c1) load_tile(t0 + GK, nxt, snxt);
+    if (tid < GK) sw[tid] = (t0 + tid < c1) ? exp2f(scur - m) : 0.f;
+    __syncthreads();  // sw ready; every wave is done with the previous tile's operands
     // transposed operands: row d holds keys t0 .. t0 + 31 of c = k - kbar and of
-    // w c, each as fp16 hi + lo; a work item is one d and 8 consecutive keys
-    for (int it = tid; it < D * (GK / 8); it += DT) {
-      const int d = it % D, kg = it / D;
+    // w c, each as fp16 hi + lo
+    #pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      const int it = tid + DT * i, d = it % D, kg = it / D;
       half8 ch, cl, wh, wl;
       #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int kk = 8 * kg + e, j = t0 + kk;
-        const float c = j < c1 ? to_f(K[static_cast<size_t>(j) * D + d]) - skb[d] : 0.f;
+        const float c = j < c1 ? cur[i][e] - skb[d] : 0.f;
         const float wc = sw[kk] * c;
         ch[e] = static_cast<_Float16>(c);
         cl[e] = static_cast<_Float16>(c - static_cast<float>(ch[e]));
@@ -238,11 +290,15 @@ __global__ __launch_bounds__(DT) void dec_gram(DecParams P) {
         acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, blv, acc[u], 0, 0, 0);
         acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bhv, acc[u], 0, 0, 0);
       }
-    __syncthreads();  // the next tile overwrites the operands
+    #pragma unroll
+    for (int i = 0; i < IPT; ++i)
+      #pragma unroll
+      for (int e = 0; e < 8; ++e) cur[i][e] = nxt[i][e];
+    scur = snxt;
   }
   // accumulator register r of lane (ql, g) holds row 8 (r / 4) + 4 g + r % 4,
   // column ql of its 32 x 32 tile
-  float* G = P.gram + (static_cast<size_t>(bh) * P.S + sp) * D * D;
+  float* G = P.gram + (static_cast<size_t>(bh) * P.SG + sp) * D * D;
   #pragma unroll
   for (int u = 0; u < TPW; ++u) {
     const int ti = wave + (DT / 64) * u, I = ti / NB, J = ti % NB;
@@ -280,10 +336,10 @@ __global__ __launch_bounds__(DT) void dec_solve(DecParams P) {
   const int bh = blockIdx.x, t = threadIdx.x;
   combine_moments<D>(P, bh, skb, smo);
   // G + lambda I from the chunk Grams (coalesced over the d^2 entries)
-  const float* Gc = P.gram + static_cast<size_t>(bh) * P.S * D * D;
+  const float* Gc = P.gram + static_cast<size_t>(bh) * P.SG * D * D;
   for (int idx = t; idx < D * D; idx += DT) {
     float a = 0.f;
-    for (int c = 0; c < P.S; ++c) a += Gc[static_cast<size_t>(c) * D * D + idx];
+    for (int c = 0; c < P.SG; ++c) a += Gc[static_cast<size_t>(c) * D * D + idx];
     const int i = idx / D, j = idx % D;
     sG[i * LG + j] = a + (i == j ? P.lambda : 0.f);
   }
@@ -375,17 +431,35 @@ __global__ __launch_bounds__(DT) void dec_output(DecParams P) {
   float o[EPL], den = 0.f;
   #pragma unroll
   for (int e = 0; e < EPL; ++e) o[e] = 0.f;
-  for (int j = c0 + wave; j < c1; j += DT / 64) {
-    float kd[EPL], vd[EPL];
-    load_lane<D>(K + static_cast<size_t>(j) * D, lane, kd);
-    load_lane<D>(V + static_cast<size_t>(j) * D, lane, vd);
-    float part = 0.f;
+  constexpr int U = 8;  // keys per batch per wave (rows of K and V in flight)
+  for (int jb = c0 + wave * U; jb < c1; jb += (DT / 64) * U) {
+    float vd[U][EPL], part[U], sv[U];
     #pragma unroll
-    for (int e = 0; e < EPL; ++e) part += kd[e] * xr[e];
-    const float a = exp2f(S[j] - m) * (1.f - (wave_sum(part) - kr));
-    den += a;
+    for (int u = 0; u < U; ++u) {
+      float kd[EPL];
+      const bool in = jb + u < c1;
+      if (in) {
+        load_lane<D>(K + static_cast<size_t>(jb + u) * D, lane, kd);
+        load_lane<D>(V + static_cast<size_t>(jb + u) * D, lane, vd[u]);
+      } else {
+        #pragma unroll
+        for (int e = 0; e < EPL; ++e) kd[e] = vd[u][e] = 0.f;
+      }
+      sv[u] = in ? S[jb + u] : -INFINITY;
+      part[u] = 0.f;
+      #pragma unroll
+      for (int e = 0; e < EPL; ++e) part[u] += kd[e] * xr[e];
+    }
     #pragma unroll
-    for (int e = 0; e < EPL; ++e) o[e] += a * vd[e];
+    for (int u = 0; u < U; ++u) part[u] = wave_sum(part[u]);
+    #pragma unroll
+    for (int u = 0; u < U; ++u) {
+      // keys past the chunk: exp2(-inf) = 0
+      const float a = exp2f(sv[u] - m) * (1.f - (part[u] - kr));
+      den += a;
+      #pragma unroll
+      for (int e = 0; e < EPL; ++e) o[e] += a * vd[u][e];
+    }
   }
   if (lane == 0) sden[wave] = den;
   #pragma unroll
@@ -416,21 +490,29 @@ __global__ __launch_bounds__(DT) void dec_finish(DecParams P) {
 size_t al256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
 struct DecLayout {
-  int S, L;
+  int S, L, SG, LG;
   size_t s, p1, gram, st, p4, total;  // byte offsets
 };
 
 DecLayout dec_layout(int BH, int n, int d) {
   DecLayout o{};
-  // about two workgroups per compute unit, at least 64 keys per chunk
-  int S = (512 + BH - 1) / BH;
+  // score, moment and output kernels: about eight workgroups per compute
+  // unit, at least 64 keys per chunk
+  int S = (2048 + BH - 1) / BH;
   S = std::max(1, std::min(S, std::min(64, (n + 63) / 64)));
   o.L = (n + S - 1) / S;
   o.S = (n + o.L - 1) / o.L;  // every chunk non-empty
+  // Gram kernel: about two workgroups per compute unit, but each chunk Gram
+  // (d^2 floats written, then read by the solve) no larger than a quarter of
+  // the chunk's keys (L d values)
+  int SG = (512 + BH - 1) / BH;
+  SG = std::max(1, std::min(SG, std::min(64, n / (4 * d))));
+  o.LG = (n + SG - 1) / SG;
+  o.SG = (n + o.LG - 1) / o.LG;
   size_t off = 0;
   o.s = off;    off += al256(static_cast<size_t>(BH) * n * sizeof(float));
   o.p1 = off;   off += al256(static_cast<size_t>(BH) * o.S * (d + 2) * sizeof(float));
-  o.gram = off; off += al256(static_cast<size_t>(BH) * o.S * d * d * sizeof(float));
+  o.gram = off; off += al256(static_cast<size_t>(BH) * o.SG * d * d * sizeof(float));
   o.st = off;   off += al256(static_cast<size_t>(BH) * (2 * d + 2) * sizeof(float));
   o.p4 = off;   off += al256(static_cast<size_t>(BH) * o.S * (d + 1) * sizeof(float));
   o.total = off;
@@ -449,14 +531,14 @@ hipError_t launch_dec(const DecodeParams& p, hipStream_t stream) {
   P.gram = reinterpret_cast<float*>(ws + ly.gram);
   P.st = reinterpret_cast<float*>(ws + ly.st);
   P.p4 = reinterpret_cast<float*>(ws + ly.p4);
-  P.BH = p.BH; P.n = p.n; P.S = ly.S; P.L = ly.L;
+  P.BH = p.BH; P.n = p.n; P.S = ly.S; P.L = ly.L; P.SG = ly.SG; P.LG = ly.LG;
   P.lambda = p.lambda; P.cg_max_iters = p.cg_max_iters; P.cg_rel_tol = p.cg_rel_tol;
-  const dim3 gs(ly.S, p.BH), gh(p.BH);
+  const dim3 gs(ly.S, p.BH), gg(ly.SG, p.BH), gh(p.BH);
   hipLaunchKernelGGL((dec_moments<D, T>), gs, dim3(DT), 0, stream, P);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.ev_main_begin && (e = hipEventRecord(p.ev_main_begin, stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL((dec_gram<D, T>), gs, dim3(DT), 0, stream, P);
+  hipLaunchKernelGGL((dec_gram<D, T>), gg, dim3(DT), 0, stream, P);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (p.ev_main_end && (e = hipEventRecord(p.ev_main_end, stream)) != hipSuccess) return e;
   hipLaunchKernelGGL((dec_solve<D, T>), gh, dim3(DT), 0, stream, P);
