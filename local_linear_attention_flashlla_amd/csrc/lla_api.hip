@@ -232,6 +232,8 @@ int lla_decode_ex(const lla_decode_args* a, hipStream_t stream) {
   const unsigned long long keys = bh * (unsigned long long)a->n;
   if (keys > (1ULL << 36)) return fail(LLA_ERR_UNSUPPORTED, "B*H*n too large");
   const size_t esz = a->dtype == LLA_DTYPE_F32 ? 4 : 2;
+  if ((unsigned long long)a->n * a->d * esz >= (1ULL << 31))
+    return fail(LLA_ERR_UNSUPPORTED, "decode: one head's cache (n*d elements) must stay under 2 GiB");
   const size_t nq = (size_t)bh * a->d * esz, nkv = (size_t)keys * a->d * esz;
   const size_t nout = (size_t)bh * a->d * 4, nrow = (size_t)bh * 4;
   struct In { const void* p; size_t bytes; };

@@ -34,6 +34,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "lla_internal.h"
 #include "../../include/lla.h"
@@ -101,6 +102,48 @@ __device__ __forceinline__ float wave_sum(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Buffer resource over `bytes` bytes at `base` (reads past the end return 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+
+// The 32-key tiles of a chunk stream through four static LDS buffers: tile t
+// (32 rows of the cache, contiguous in memory) is copied with
+// buffer_load ... lds, 1 KiB per wave instruction, three steps before it is
+// used, into buffer t % 4. Separate arrays keep every buffer choice static,
+// so the compiler never waits on a copy it does not need.
+template <int D, typename T>
+struct Tiles {
+  static constexpr int kBytes = GK * D * static_cast<int>(sizeof(T));
+  static constexpr int kChunks = kBytes / 1024;
+  static constexpr int kPerWave = kChunks / (DT / 64);  // copy instructions per wave and tile
+  static_assert(kChunks % (DT / 64) == 0, "chunks must spread over the waves");
+};
+template <int D, typename T>
+__device__ __forceinline__ void copy_tile(__amdgpu_buffer_rsrc_t r, uint32_t tile_off, T* buf, int wave,
+                                          int lane) {
+  #pragma unroll
+  for (int u = 0; u < Tiles<D, T>::kPerWave; ++u) {
+    const int ch = u * (DT / 64) + wave;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void*)(reinterpret_cast<char*>(buf) + ch * 1024), 16,
+        ch * 1024 + lane * 16, tile_off, 0, 0);
+  }
+}
+// Wait until at most N of this wave's copies are in flight and its LDS reads
+// are done, then a barrier: every wave's older copies are then visible and no
+// wave still reads a buffer that the next copy overwrites.
+template <int N>
+__device__ __forceinline__ void wait_copies_barrier() {
+  static_assert(N == 2 || N == 4 || N == 8 || N == 16, "vmcnt below");
+  if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+template <int I> using IC = std::integral_constant<int, I>;
+
 // m (log2 units), omega and kbar of head bh from the S chunk partials:
 // m = max_c m_c, omega = sum_c omega_c 2^(m_c - m), mu~ likewise, kbar = mu~ / omega.
 // Threads t < D write kbar[t]; thread 0 writes mo[0] = m, mo[1] = omega.
@@ -129,39 +172,56 @@ __device__ __forceinline__ void combine_moments(const DecParams& P, int bh, floa
 template <int D, typename T>
 __global__ __launch_bounds__(DT) void dec_moments(DecParams P) {
   constexpr int EPL = D / 64;
+  constexpr int KPW = GK / (DT / 64);  // keys of a tile per wave
+  __shared__ __align__(16) T b0[GK * D], b1[GK * D], b2[GK * D], b3[GK * D];
   __shared__ float sm[DT / 64], som[DT / 64];
   __shared__ float smu[DT / 64][D];
+  auto BUF = [&](auto I) __attribute__((always_inline)) -> T* {
+    constexpr int i = decltype(I)::value % 4;
+    if constexpr (i == 0) return b0;
+    else if constexpr (i == 1) return b1;
+    else if constexpr (i == 2) return b2;
+    else return b3;
+  };
   const int sp = blockIdx.x, bh = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c0 = sp * P.L, c1 = min(P.n, c0 + P.L);
-  const T* K = static_cast<const T*>(P.k) + static_cast<size_t>(bh) * P.n * D;
+  const int ntl = (c1 - c0 + GK - 1) / GK;
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(static_cast<const T*>(P.k) + static_cast<size_t>(bh) * P.n * D,
+                                              static_cast<uint32_t>(static_cast<size_t>(P.n) * D * sizeof(T)));
+  auto toff = [&](int t) __attribute__((always_inline)) {
+    return static_cast<uint32_t>((c0 + min(t, ntl - 1) * GK) * D * static_cast<int>(sizeof(T)));
+  };
   float qd[EPL];
   load_lane<D>(static_cast<const T*>(P.q) + static_cast<size_t>(bh) * D, lane, qd);
   const float cs = kLog2e / sqrtf(static_cast<float>(D));
   float m = -INFINITY, om = 0.f, mu[EPL];
   #pragma unroll
   for (int e = 0; e < EPL; ++e) mu[e] = 0.f;
-  // each wave takes batches of U consecutive keys: U rows in flight at once,
-  // U interleaved lane reductions
-  constexpr int U = 16;
-  for (int jb = c0 + wave * U; jb < c1; jb += (DT / 64) * U) {
-    float kd[U][EPL], part[U];
+  copy_tile<D>(kr, toff(0), b0, wave, lane);
+  copy_tile<D>(kr, toff(1), b1, wave, lane);
+  copy_tile<D>(kr, toff(2), b2, wave, lane);
+  // step t: tile t has landed; copy tile t + 3 (clamped: every step issues the
+  // same number of copies); this wave's KPW keys of tile t
+  auto step = [&](auto JM, int t) __attribute__((always_inline)) {
+    wait_copies_barrier<2 * Tiles<D, T>::kPerWave>();
+    copy_tile<D>(kr, toff(t + 3), BUF(IC<decltype(JM)::value + 3>{}), wave, lane);
+    if (t >= ntl) return;  // block-uniform
+    const T* buf = BUF(JM);
+    float kd[KPW][EPL], part[KPW];
     #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (jb + u < c1) {
-        load_lane<D>(K + static_cast<size_t>(jb + u) * D, lane, kd[u]);
-      } else {
-        #pragma unroll
-        for (int e = 0; e < EPL; ++e) kd[u][e] = 0.f;
-      }
+    for (int u = 0; u < KPW; ++u) {
+      load_lane<D>(buf + (KPW * wave + u) * D, lane, kd[u]);
       part[u] = 0.f;
       #pragma unroll
       for (int e = 0; e < EPL; ++e) part[u] += qd[e] * kd[u][e];
     }
     #pragma unroll
-    for (int u = 0; u < U; ++u) part[u] = wave_sum(part[u]);
+    for (int u = 0; u < KPW; ++u) part[u] = wave_sum(part[u]);
+    const int jb = c0 + t * GK + KPW * wave;
     #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < KPW; ++u) {
       const int j = jb + u;
       if (j >= c1) break;  // wave-uniform
       const float sj = part[u] * cs;  // the same in every lane
@@ -178,6 +238,12 @@ __global__ __launch_bounds__(DT) void dec_moments(DecParams P) {
       #pragma unroll
       for (int e = 0; e < EPL; ++e) mu[e] += w * kd[u][e];
     }
+  };
+  for (int t0 = 0; t0 < ntl; t0 += 4) {
+    step(IC<0>{}, t0);
+    step(IC<1>{}, t0 + 1);
+    step(IC<2>{}, t0 + 2);
+    step(IC<3>{}, t0 + 3);
   }
   if (lane == 0) {
     sm[wave] = m;
@@ -185,7 +251,7 @@ __global__ __launch_bounds__(DT) void dec_moments(DecParams P) {
   }
   #pragma unroll
   for (int e = 0; e < EPL; ++e) smu[wave][lane * EPL + e] = mu[e];
-  __syncthreads();
+  __syncthreads();  // (also: no tile copy is still in flight past this point)
   const int t = threadIdx.x;
   if (t < D) {
     float mc = -INFINITY;
@@ -211,59 +277,77 @@ __global__ __launch_bounds__(DT) void dec_moments(DecParams P) {
 // ------------------------------ chunk Gram ---------------------------------
 template <int D, typename T>
 __global__ __launch_bounds__(DT) void dec_gram(DecParams P) {
-  constexpr int NB = D / 32;              // 32-row blocks of G
+  constexpr int NB = D / 32;                // 32-row blocks of G
   constexpr int TPW = NB * NB / (DT / 64);  // output tiles per wave
   static_assert(TPW >= 1 && NB * NB % (DT / 64) == 0, "tiles must spread over the waves");
+  constexpr int IPT = D * (GK / 8) / DT;    // staging items (one d, 8 keys) per thread
+  static_assert(IPT * DT == D * (GK / 8), "items must spread evenly");
+  __shared__ __align__(16) T r0[GK * D], r1[GK * D], r2[GK * D], r3[GK * D];
   __shared__ __align__(16) _Float16 cHi[D * GLD], cLo[D * GLD], wHi[D * GLD], wLo[D * GLD];
   __shared__ float skb[D];
-  __shared__ float sw[GK];
+  __shared__ float sw[2][GK];
   __shared__ float smo[2];
+  auto RB = [&](auto I) __attribute__((always_inline)) -> T* {
+    constexpr int i = decltype(I)::value % 4;
+    if constexpr (i == 0) return r0;
+    else if constexpr (i == 1) return r1;
+    else if constexpr (i == 2) return r2;
+    else return r3;
+  };
   const int sp = blockIdx.x, bh = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, ql = lane & 31, g = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, ql = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c0 = sp * P.LG, c1 = min(P.n, c0 + P.LG);
+  const int ntl = (c1 - c0 + GK - 1) / GK;
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(static_cast<const T*>(P.k) + static_cast<size_t>(bh) * P.n * D,
+                                              static_cast<uint32_t>(static_cast<size_t>(P.n) * D * sizeof(T)));
+  auto toff = [&](int t) __attribute__((always_inline)) {
+    return static_cast<uint32_t>((c0 + min(t, ntl - 1) * GK) * D * static_cast<int>(sizeof(T)));
+  };
+  copy_tile<D>(kr, toff(0), r0, wave, lane);
+  copy_tile<D>(kr, toff(1), r1, wave, lane);
+  copy_tile<D>(kr, toff(2), r2, wave, lane);
   combine_moments<D>(P, bh, skb, smo);
   __syncthreads();
   const float m = smo[0];
-  const int c0 = sp * P.LG, c1 = min(P.n, c0 + P.LG);
-  const T* K = static_cast<const T*>(P.k) + static_cast<size_t>(bh) * P.n * D;
   const float* S = P.s + static_cast<size_t>(bh) * P.n;
+  // scores of key tid of tiles t .. t + 3 in a ring (threads tid < GK); the
+  // weights of tile t + 1 are written to LDS during step t
+  float sR[4] = {0.f, 0.f, 0.f, 0.f};
+  auto load_s = [&](int t) __attribute__((always_inline)) {
+    const int j = c0 + t * GK + tid;
+    return (tid < GK && j < c1) ? S[j] : -INFINITY;
+  };
+  sR[0] = load_s(0);
+  sR[1] = load_s(1);
+  sR[2] = load_s(2);
+  if (tid < GK) sw[0][tid] = exp2f(sR[0] - m);  // keys past the chunk: weight 0
   floatx16 acc[TPW];
   #pragma unroll
   for (int u = 0; u < TPW; ++u)
     #pragma unroll
     for (int r = 0; r < 16; ++r) acc[u][r] = 0.f;
-  // a staging work item is one d and 8 consecutive keys of the tile; the
-  // items of the next tile are loaded into registers while this one computes
-  constexpr int IPT = D * (GK / 8) / DT;
-  static_assert(IPT * DT == D * (GK / 8), "items must spread evenly");
-  float cur[IPT][8], nxt[IPT][8], scur = 0.f, snxt = 0.f;
-  auto load_tile = [&](int tb, float (&buf)[IPT][8], float& sv) __attribute__((always_inline)) {
-    #pragma unroll
-    for (int i = 0; i < IPT; ++i) {
-      const int it = tid + DT * i, d = it % D, kg = it / D;
-      #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = tb + 8 * kg + e;
-        buf[i][e] = j < c1 ? to_f(K[static_cast<size_t>(j) * D + d]) : 0.f;
-      }
-    }
-    if (tid < GK) sv = tb + tid < c1 ? S[tb + tid] : 0.f;
-  };
-  load_tile(c0, cur, scur);
-  for (int t0 = c0; t0 < c1; t0 += GK) {
-    if (t0 + GK < c1) load_tile(t0 + GK, nxt, snxt);
-    if (tid < GK) sw[tid] = (t0 + tid < c1) ? exp2f(scur - m) : 0.f;
-    __syncthreads();  // sw ready; every wave is done with the previous tile's operands
-    // transposed operands: row d holds keys t0 .. t0 + 31 of c = k - kbar and of
+  auto step = [&](auto JM, int t) __attribute__((always_inline)) {
+    constexpr int jm = decltype(JM)::value;
+    // raw tile t has landed; every wave is done with the operands of tile t - 1
+    wait_copies_barrier<2 * Tiles<D, T>::kPerWave>();
+    copy_tile<D>(kr, toff(t + 3), RB(IC<jm + 3>{}), wave, lane);
+    if (t >= ntl) return;  // block-uniform
+    if (tid < GK) sw[(jm + 1) & 1][tid] = exp2f(sR[(jm + 1) % 4] - m);
+    sR[(jm + 3) % 4] = load_s(t + 3);
+    // transposed operands: row d holds the tile's keys of c = k - kbar and of
     // w c, each as fp16 hi + lo
+    const T* raw = RB(JM);
+    const float* w = sw[jm & 1];
     #pragma unroll
     for (int i = 0; i < IPT; ++i) {
       const int it = tid + DT * i, d = it % D, kg = it / D;
       half8 ch, cl, wh, wl;
       #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int kk = 8 * kg + e, j = t0 + kk;
-        const float c = j < c1 ? cur[i][e] - skb[d] : 0.f;
-        const float wc = sw[kk] * c;
+        const int kk = 8 * kg + e;
+        const float c = c0 + t * GK + kk < c1 ? to_f(raw[kk * D + d]) - skb[d] : 0.f;
+        const float wc = w[kk] * c;
         ch[e] = static_cast<_Float16>(c);
         cl[e] = static_cast<_Float16>(c - static_cast<float>(ch[e]));
         wh[e] = static_cast<_Float16>(wc);
@@ -290,12 +374,14 @@ __global__ __launch_bounds__(DT) void dec_gram(DecParams P) {
         acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, blv, acc[u], 0, 0, 0);
         acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bhv, acc[u], 0, 0, 0);
       }
-    #pragma unroll
-    for (int i = 0; i < IPT; ++i)
-      #pragma unroll
-      for (int e = 0; e < 8; ++e) cur[i][e] = nxt[i][e];
-    scur = snxt;
+  };
+  for (int t0 = 0; t0 < ntl; t0 += 4) {
+    step(IC<0>{}, t0);
+    step(IC<1>{}, t0 + 1);
+    step(IC<2>{}, t0 + 2);
+    step(IC<3>{}, t0 + 3);
   }
+  __syncthreads();  // no tile copy may still be in flight when the kernel ends
   // accumulator register r of lane (ql, g) holds row 8 (r / 4) + 4 g + r % 4,
   // column ql of its 32 x 32 tile
   float* G = P.gram + (static_cast<size_t>(bh) * P.SG + sp) * D * D;
@@ -411,60 +497,106 @@ __global__ __launch_bounds__(DT) void dec_solve(DecParams P) {
 template <int D, typename T>
 __global__ __launch_bounds__(DT) void dec_output(DecParams P) {
   constexpr int EPL = D / 64;
+  constexpr int KPW = GK / (DT / 64);
+  __shared__ __align__(16) T k0[GK * D], k1[GK * D], k2[GK * D], k3[GK * D];
+  __shared__ __align__(16) T v0[GK * D], v1[GK * D], v2[GK * D], v3[GK * D];
   __shared__ float sden[DT / 64];
   __shared__ float so[DT / 64][D];
+  auto KB = [&](auto I) __attribute__((always_inline)) -> T* {
+    constexpr int i = decltype(I)::value % 4;
+    if constexpr (i == 0) return k0;
+    else if constexpr (i == 1) return k1;
+    else if constexpr (i == 2) return k2;
+    else return k3;
+  };
+  auto VB = [&](auto I) __attribute__((always_inline)) -> T* {
+    constexpr int i = decltype(I)::value % 4;
+    if constexpr (i == 0) return v0;
+    else if constexpr (i == 1) return v1;
+    else if constexpr (i == 2) return v2;
+    else return v3;
+  };
   const int sp = blockIdx.x, bh = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c0 = sp * P.L, c1 = min(P.n, c0 + P.L);
+  const int ntl = (c1 - c0 + GK - 1) / GK;
+  const uint32_t head_bytes = static_cast<uint32_t>(static_cast<size_t>(P.n) * D * sizeof(T));
+  const __amdgpu_buffer_rsrc_t kr =
+      make_rsrc(static_cast<const T*>(P.k) + static_cast<size_t>(bh) * P.n * D, head_bytes);
+  const __amdgpu_buffer_rsrc_t vr =
+      make_rsrc(static_cast<const T*>(P.v) + static_cast<size_t>(bh) * P.n * D, head_bytes);
+  auto toff = [&](int t) __attribute__((always_inline)) {
+    return static_cast<uint32_t>((c0 + min(t, ntl - 1) * GK) * D * static_cast<int>(sizeof(T)));
+  };
   const float* st = P.st + static_cast<size_t>(bh) * (2 * D + 2);
-  float xr[EPL], kr = 0.f;
+  float xr[EPL], kr_dot = 0.f;
   #pragma unroll
   for (int e = 0; e < EPL; ++e) {
     xr[e] = st[lane * EPL + e];
-    kr += st[D + lane * EPL + e] * xr[e];
+    kr_dot += st[D + lane * EPL + e] * xr[e];
   }
-  kr = wave_sum(kr);
+  kr_dot = wave_sum(kr_dot);
   const float m = st[2 * D];
-  const T* K = static_cast<const T*>(P.k) + static_cast<size_t>(bh) * P.n * D;
-  const T* V = static_cast<const T*>(P.v) + static_cast<size_t>(bh) * P.n * D;
   const float* S = P.s + static_cast<size_t>(bh) * P.n;
   float o[EPL], den = 0.f;
   #pragma unroll
   for (int e = 0; e < EPL; ++e) o[e] = 0.f;
-  constexpr int U = 8;  // keys per batch per wave (rows of K and V in flight)
-  for (int jb = c0 + wave * U; jb < c1; jb += (DT / 64) * U) {
-    float vd[U][EPL], part[U], sv[U];
+  // scores of this wave's keys, loaded two steps ahead into a ring of four
+  float sreg[4][KPW];
+  auto load_s = [&](int t, float (&dst)[KPW]) __attribute__((always_inline)) {
+    const int jb = c0 + t * GK + KPW * wave;
     #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < KPW; ++u) dst[u] = jb + u < c1 ? S[jb + u] : -INFINITY;  // past the chunk: weight 0
+  };
+  load_s(0, sreg[0]);
+  load_s(1, sreg[1]);
+  copy_tile<D>(kr, toff(0), k0, wave, lane);
+  copy_tile<D>(vr, toff(0), v0, wave, lane);
+  copy_tile<D>(kr, toff(1), k1, wave, lane);
+  copy_tile<D>(vr, toff(1), v1, wave, lane);
+  copy_tile<D>(kr, toff(2), k2, wave, lane);
+  copy_tile<D>(vr, toff(2), v2, wave, lane);
+  auto step = [&](auto JM, int t) __attribute__((always_inline)) {
+    wait_copies_barrier<4 * Tiles<D, T>::kPerWave>();
+    copy_tile<D>(kr, toff(t + 3), KB(IC<decltype(JM)::value + 3>{}), wave, lane);
+    copy_tile<D>(vr, toff(t + 3), VB(IC<decltype(JM)::value + 3>{}), wave, lane);
+    if (t >= ntl) return;  // block-uniform
+    constexpr int jm = decltype(JM)::value;
+    load_s(t + 2, sreg[(jm + 2) % 4]);
+    const T* kb = KB(JM);
+    const T* vb = VB(JM);
+    float vd[KPW][EPL], part[KPW];
+    const float (&sv)[KPW] = sreg[jm];
+    #pragma unroll
+    for (int u = 0; u < KPW; ++u) {
       float kd[EPL];
-      const bool in = jb + u < c1;
-      if (in) {
-        load_lane<D>(K + static_cast<size_t>(jb + u) * D, lane, kd);
-        load_lane<D>(V + static_cast<size_t>(jb + u) * D, lane, vd[u]);
-      } else {
-        #pragma unroll
-        for (int e = 0; e < EPL; ++e) kd[e] = vd[u][e] = 0.f;
-      }
-      sv[u] = in ? S[jb + u] : -INFINITY;
+      load_lane<D>(kb + (KPW * wave + u) * D, lane, kd);
+      load_lane<D>(vb + (KPW * wave + u) * D, lane, vd[u]);
       part[u] = 0.f;
       #pragma unroll
       for (int e = 0; e < EPL; ++e) part[u] += kd[e] * xr[e];
     }
     #pragma unroll
-    for (int u = 0; u < U; ++u) part[u] = wave_sum(part[u]);
+    for (int u = 0; u < KPW; ++u) part[u] = wave_sum(part[u]);
     #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      // keys past the chunk: exp2(-inf) = 0
-      const float a = exp2f(sv[u] - m) * (1.f - (part[u] - kr));
+    for (int u = 0; u < KPW; ++u) {
+      const float a = exp2f(sv[u] - m) * (1.f - (part[u] - kr_dot));
       den += a;
       #pragma unroll
       for (int e = 0; e < EPL; ++e) o[e] += a * vd[u][e];
     }
+  };
+  for (int t0 = 0; t0 < ntl; t0 += 4) {
+    step(IC<0>{}, t0);
+    step(IC<1>{}, t0 + 1);
+    step(IC<2>{}, t0 + 2);
+    step(IC<3>{}, t0 + 3);
   }
   if (lane == 0) sden[wave] = den;
   #pragma unroll
   for (int e = 0; e < EPL; ++e) so[wave][lane * EPL + e] = o[e];
-  __syncthreads();
+  __syncthreads();  // (also: no tile copy is still in flight past this point)
   const int t = threadIdx.x;
   if (t <= D) {
     float a = 0.f;
