@@ -189,7 +189,7 @@ def bench_given_rho(args, torch, lla, wl, q, k, v, out, ws, kernel, kernel_used)
         "value": B * H * n / (ms_step * 1e-3), "unit": "queries/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if wl.dtype == "bf16" else "f32", "data": "synthetic",
+        "dtype": "fp16" if mfma else "f32", "data": "synthetic",
         "config": {"workload": wl.name, "B": B, "H": H, "n": n, "d": d, "lambda": wl.lam,
                    "kernel": "mfma" if mfma else "valu", "rho": "the forward's own rho"},
         "tflops": flops / (ms_step * 1e-3) / 1e12, "flops_per_step": flops,
@@ -254,8 +254,11 @@ def bench_decode(args, torch, lla, dev):
         "metric": "LLA decode queries/s (one new query per head), 1 MI355X",
         "value": B * H / (ms * 1e-3), "unit": "queries/s", "n_gpus": 1, "steps": steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        # the Gram kernel multiplies fp16 x fp16 into fp32 (operands in two
+        # fp16 terms); scores, CG and output run in fp32 on the vector ALU
+        "vs_baseline": None, "dtype": "fp16", "data": "synthetic",
         "config": {"workload": f"decode over the {wl.name} caches", "B": B, "H": H, "n": n, "d": d,
+                   "input_dtype": wl.dtype,
                    "lambda": wl.lam, "cg_max_iters": wl.cg_max_iters, "cg_rel_tol": wl.cg_rel_tol},
         "cg_iters_mean": float(iters.float().mean().item()),
         "cache_bytes_k_plus_v": 2 * cache,
@@ -406,11 +409,14 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        # the arithmetic type: bf16 inputs convert exactly to fp16, and the
+        # matrix cores multiply fp16 x fp16 into fp32; the fp32 path is fp32
+        "dtype": ("fp16" if kernel_used == lla.LLA_KERNEL_MFMA else "f32"),
         "data": "synthetic",
         "config": {"workload": wl.name, "B": B, "H": H, "n": n, "d": d,
                    "lambda": wl.lam, "cg_max_iters": wl.cg_max_iters,
                    "cg_rel_tol": wl.cg_rel_tol,
+                   "input_dtype": wl.dtype, "accumulate": "f32",
                    "kernel": {lla.LLA_KERNEL_MFMA: "mfma", lla.LLA_KERNEL_VALU: "valu"}[kernel_used],
                    "split_u": bool(args.split_u)},
         "tflops": tflops,
