@@ -5,3 +5,4 @@ import this package; the HIP library and its binding never do.
 """
 from .lla_oracle import *  # noqa: F401,F403
 from .lla_oracle import sample_rows  # noqa: F401
+from . import lla_oracle_bwd  # noqa: F401  (the gradient of the forward above)
