@@ -130,6 +130,12 @@ typedef struct lla_fwd_args {
      kernels of the matrix-core path fall outside them */
   hipEvent_t ev_main_begin;
   hipEvent_t ev_main_end;
+  /* optional output, NULL = not wanted: [B][H][n][d] fp32, device -- the
+     solution the forward solved for, rho_c = Sigma_c^{-1} omega_i (kbar_i -
+     q_i) with Sigma_c centred at the weighted key mean kbar_i (the pages'
+     rho_i = rho_c / (1 + (kbar_i - q_i) . rho_c)); the input of
+     lla_backward_ex. Not available with lla_output_given_rho. */
+  float* rho_c;
 } lla_fwd_args;
 
 /* out = LLA(q, k, v) for fp32 inputs. Arguments as in lla_fwd_args;
@@ -212,6 +218,64 @@ int lla_decode_ex(const lla_decode_args* args, hipStream_t stream);
 /* Device workspace bytes lla_decode_ex needs for these sizes (0 for invalid
    sizes). Linear in n. */
 size_t lla_decode_workspace_bytes(int B, int H, int n, int d, int dtype);
+
+/* ------------------------------------------------------------------------
+ * Backward: the gradient of L = sum_i dout_i . out_i with respect to q, k and
+ * v for the causal forward computed by the matrix-core path (bf16 inputs,
+ * d in {64, 128}). "Local Linear Attention: reading notes" (section 2.2, on
+ * training; appendix D) states that the backward needs further linear
+ * systems per query but prints none; the gradient is implicit
+ * differentiation of Eqs. (6)-(8) in the form the forward solves (centred at
+ * the weighted key mean), with one adjoint CG solve per query on the same
+ * matrix Sigma_c and the same CG policy as the forward:
+ *   Sigma_c y_i = C_i^T dout_i,  C_i = sum_j (w_ij / omega_i) v_j (k_j - kbar_i)^T,
+ * and the max-normalisation's share of the gradient routed to the key that
+ * attains the row max (weights are max-normalised, and lambda makes the fit
+ * depend on their scale). Working memory is linear in n.
+ * ------------------------------------------------------------------------ */
+typedef struct lla_bwd_args {
+  int dtype;          /* LLA_DTYPE_BF16 (LLA_ERR_UNSUPPORTED otherwise) */
+  const void* q;      /* [B][H][n][d] bf16, device: the forward's inputs */
+  const void* k;
+  const void* v;
+  const float* out;   /* [B][H][n][d] fp32, device: the forward's output */
+  const float* dout;  /* [B][H][n][d] fp32, device: dL/dout */
+  const float* rho_c; /* [B][H][n][d] fp32, device: the forward's rho_c output
+                         (kept rather than rho: where (kbar - q) . rho_c is large
+                         the pages' rho no longer fixes its scale in fp32) */
+  float* dq;          /* [B][H][n][d] fp32, device, written */
+  float* dk;
+  float* dv;
+  int B, H, n, d;     /* d in {64, 128} */
+  float lambda;       /* > 0, as in the forward */
+  int cg_max_iters;   /* >= 0: adjoint solve, same policy as the forward */
+  float cg_rel_tol;   /* >= 0 */
+  /* optional outputs, NULL = not wanted (device pointers) */
+  int32_t* adj_iters; /* [B][H][n] CG steps of the adjoint solve */
+  float* adj_resid;   /* [B][H][n] ||r_k|| / ||r_0|| of the adjoint solve at exit */
+  void* workspace;    /* optional caller workspace (device), as for lla_forward_ex */
+  size_t workspace_bytes;
+  hipEvent_t ev_main_begin; /* optional: recorded around the adjoint CG kernel */
+  hipEvent_t ev_main_end;
+  int flags;          /* LLA_FLAG_SPLIT_U: the adjoint's right-hand side and CG
+                         products carry w * (...) as two fp16 terms (slower,
+                         more exact; see lla_backward_ex) */
+} lla_bwd_args;
+
+/* dq, dk, dv for the forward lla_forward_ex computed with the same q, k, v,
+   lambda and CG policy (kernel LLA_KERNEL_MFMA or AUTO), given its out and
+   rho_c outputs. Every element of dq, dk and dv is written; the inputs are not.
+   Conventions as for lla_forward_ex: device pointers, 16-byte aligned, no
+   output may overlap an input or another output; validation on the host
+   before any device work (nothing is written on failure); asynchronous on
+   `stream`. Returns LLA_OK, LLA_ERR_INVALID_ARG, LLA_ERR_UNSUPPORTED (dtype
+   other than bf16, d outside {64, 128}, sizes too large), LLA_ERR_WORKSPACE
+   or LLA_ERR_HIP. */
+int lla_backward_ex(const lla_bwd_args* args, hipStream_t stream);
+
+/* Device workspace bytes lla_backward_ex needs for these sizes (0 for
+   invalid or unsupported ones). Linear in n. */
+size_t lla_backward_workspace_bytes(int B, int H, int n, int d, int dtype);
 
 /* Static, human-readable name of a status code. */
 const char* lla_status_string(int status);

@@ -33,15 +33,17 @@ def _ptr(t) -> int:
 
 
 def forward(q, k, v, lam: float, cg_max_iters: int, cg_rel_tol: float, *,
-            out=None, omega=None, rho=None, rowmax=None, cg_iters=None, cg_resid=None,
+            out=None, omega=None, rho=None, rowmax=None, cg_iters=None, cg_resid=None, rho_c=None,
             workspace=None, kernel: int = LLA_KERNEL_AUTO, flags: int = 0, stream=None,
             events=None, rho_in=None):
     """Causal LLA forward on the GPU.
 
     q, k, v: contiguous [B, H, n, d] tensors on a HIP device, all float32 or all
     bfloat16. Returns ``out`` ([B, H, n, d] float32). Optional outputs are
-    filled when given: omega/rowmax/cg_resid [B, H, n] float32, rho
-    [B, H, n, d] float32, cg_iters [B, H, n] int32. ``workspace`` is an
+    filled when given: omega/rowmax/cg_resid [B, H, n] float32, rho and rho_c
+    [B, H, n, d] float32 (the pages' rho_i and the solution of the system
+    centred at the weighted key mean, which ``backward`` takes), cg_iters
+    [B, H, n] int32. ``workspace`` is an
     optional uint8 device tensor of at least ``workspace_bytes(...)`` bytes.
     The call is asynchronous on ``stream`` (default: torch's current stream).
     ``events``: optional (begin, end) pair of ``torch.cuda.Event`` that the
@@ -74,12 +76,14 @@ def forward(q, k, v, lam: float, cg_max_iters: int, cg_rel_tol: float, *,
                                ("rho", rho, torch.float32, (B, H, n, d)),
                                ("rowmax", rowmax, torch.float32, (B, H, n)),
                                ("cg_iters", cg_iters, torch.int32, (B, H, n)),
-                               ("cg_resid", cg_resid, torch.float32, (B, H, n))):
+                               ("cg_resid", cg_resid, torch.float32, (B, H, n)),
+                               ("rho_c", rho_c, torch.float32, (B, H, n, d))):
         if t is None:
             continue
         if t.dtype != dt or tuple(t.shape) != shape or not t.is_contiguous() or not t.is_cuda:
             raise ValueError(f"{name} must be a contiguous {dt} GPU tensor of shape {shape}")
     a = _lib.LlaFwdArgs()
+    a.rho_c = _ptr(rho_c)
     a.dtype = dtype
     a.q, a.k, a.v, a.out = _ptr(q), _ptr(k), _ptr(v), _ptr(out)
     a.B, a.H, a.n, a.d = B, H, n, d
@@ -183,3 +187,75 @@ def decode(q, k, v, lam: float, cg_max_iters: int, cg_rel_tol: float, *, out=Non
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     _lib.check(_lib.load().lla_decode_ex(ctypes.byref(a), ctypes.c_void_p(handle)))
     return out
+
+
+def backward_workspace_bytes(B: int, H: int, n: int, d: int, dtype: str = "bf16") -> int:
+    dt = LLA_DTYPE_BF16 if dtype == "bf16" else LLA_DTYPE_F32
+    return int(_lib.load().lla_backward_workspace_bytes(B, H, n, d, dt))
+
+
+def backward(q, k, v, out, dout, rho_c, lam: float, cg_max_iters: int, cg_rel_tol: float, *,
+             dq=None, dk=None, dv=None, adj_iters=None, adj_resid=None, workspace=None,
+             stream=None, events=None, flags=0):
+    """Gradient of sum(dout * out) for the causal LLA forward on the GPU.
+
+    q, k, v: [B, H, n, d] bfloat16 (d in {64, 128}), the forward's inputs;
+    out, rho_c: the forward's output and its ``rho_c`` output ([B, H, n, d]
+    float32, from ``forward(..., rho_c=...)`` with the same lam and CG
+    policy);
+    dout: [B, H, n, d] float32. Returns (dq, dk, dv), float32 [B, H, n, d].
+    Optional: adj_iters [B, H, n] int32 and adj_resid [B, H, n] float32 (the
+    adjoint CG's steps and final relative residual); ``events``: a (begin,
+    end) pair recorded around the adjoint CG kernel.
+    """
+    import ctypes
+    import torch
+
+    if q.dtype != torch.bfloat16 or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("backward: q, k, v must be bfloat16")
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share one [B, H, n, d] shape")
+    B, H, n, d = (int(s) for s in q.shape)
+    shape = (B, H, n, d)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if dq is None:
+        dq = torch.empty(shape, dtype=torch.float32, device=q.device)
+    if dk is None:
+        dk = torch.empty(shape, dtype=torch.float32, device=q.device)
+    if dv is None:
+        dv = torch.empty(shape, dtype=torch.float32, device=q.device)
+    for name, t, dt, shp in (("out", out, torch.float32, shape), ("dout", dout, torch.float32, shape),
+                             ("rho_c", rho_c, torch.float32, shape), ("dq", dq, torch.float32, shape),
+                             ("dk", dk, torch.float32, shape), ("dv", dv, torch.float32, shape),
+                             ("adj_iters", adj_iters, torch.int32, shape[:3]),
+                             ("adj_resid", adj_resid, torch.float32, shape[:3])):
+        if t is None:
+            continue
+        if t.dtype != dt or tuple(t.shape) != shp or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous {dt} GPU tensor of shape {shp}")
+    a = _lib.LlaBwdArgs()
+    a.dtype = LLA_DTYPE_BF16
+    a.q, a.k, a.v = _ptr(q), _ptr(k), _ptr(v)
+    a.out, a.dout, a.rho_c = _ptr(out), _ptr(dout), _ptr(rho_c)
+    a.dq, a.dk, a.dv = _ptr(dq), _ptr(dk), _ptr(dv)
+    a.B, a.H, a.n, a.d = B, H, n, d
+    a.lambda_ = float(lam)
+    a.cg_max_iters = int(cg_max_iters)
+    a.cg_rel_tol = float(cg_rel_tol)
+    a.adj_iters, a.adj_resid = _ptr(adj_iters), _ptr(adj_resid)
+    a.flags = int(flags)
+    if workspace is not None:
+        a.workspace = _ptr(workspace)
+        a.workspace_bytes = int(workspace.numel() * workspace.element_size())
+    if events is not None:
+        ev0, ev1 = events
+        ev0.record()
+        ev1.record()
+        a.ev_main_begin, a.ev_main_end = int(ev0.cuda_event), int(ev1.cuda_event)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    _lib.check(_lib.load().lla_backward_ex(ctypes.byref(a), ctypes.c_void_p(handle)))
+    return dq, dk, dv

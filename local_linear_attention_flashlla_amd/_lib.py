@@ -32,7 +32,7 @@ LLA_FLAG_SPLIT_U = 1
 EXPORTED_SYMBOLS = (
     "lla_forward_f32", "lla_forward_bf16", "lla_forward_ex", "lla_output_given_rho",
     "lla_workspace_bytes", "lla_decode_ex", "lla_decode_workspace_bytes",
-    "lla_status_string", "lla_last_error", "lla_version",
+    "lla_backward_ex", "lla_backward_workspace_bytes", "lla_status_string", "lla_last_error", "lla_version",
 )
 
 
@@ -62,6 +62,7 @@ class LlaFwdArgs(ctypes.Structure):
         ("flags", ctypes.c_int),
         ("ev_main_begin", ctypes.c_void_p),
         ("ev_main_end", ctypes.c_void_p),
+        ("rho_c", ctypes.c_void_p),
     ]
 
 
@@ -89,6 +90,36 @@ class LlaDecodeArgs(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t),
         ("ev_main_begin", ctypes.c_void_p),
         ("ev_main_end", ctypes.c_void_p),
+    ]
+
+
+class LlaBwdArgs(ctypes.Structure):
+    """Mirror of ``lla_bwd_args``."""
+    _fields_ = [
+        ("dtype", ctypes.c_int),
+        ("q", ctypes.c_void_p),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
+        ("dout", ctypes.c_void_p),
+        ("rho_c", ctypes.c_void_p),
+        ("dq", ctypes.c_void_p),
+        ("dk", ctypes.c_void_p),
+        ("dv", ctypes.c_void_p),
+        ("B", ctypes.c_int),
+        ("H", ctypes.c_int),
+        ("n", ctypes.c_int),
+        ("d", ctypes.c_int),
+        ("lambda_", ctypes.c_float),
+        ("cg_max_iters", ctypes.c_int),
+        ("cg_rel_tol", ctypes.c_float),
+        ("adj_iters", ctypes.c_void_p),
+        ("adj_resid", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("ev_main_begin", ctypes.c_void_p),
+        ("ev_main_end", ctypes.c_void_p),
+        ("flags", ctypes.c_int),
     ]
 
 
@@ -125,6 +156,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.lla_decode_ex.restype = ci
     lib.lla_decode_workspace_bytes.argtypes = [ci, ci, ci, ci, ci]
     lib.lla_decode_workspace_bytes.restype = cz
+    lib.lla_backward_ex.argtypes = [ctypes.POINTER(LlaBwdArgs), vp]
+    lib.lla_backward_ex.restype = ci
+    lib.lla_backward_workspace_bytes.argtypes = [ci, ci, ci, ci, ci]
+    lib.lla_backward_workspace_bytes.restype = cz
     lib.lla_workspace_bytes.argtypes = [ci, ci, ci, ci, ci, ci]
     lib.lla_workspace_bytes.restype = cz
     lib.lla_status_string.argtypes = [ci]

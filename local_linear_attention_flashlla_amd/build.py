@@ -18,7 +18,7 @@ LIB_NAME = "liblla.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 ARCH = os.environ.get("LLA_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["lla_api.hip", "lla_valu.hip", "lla_mfma.hip", "lla_decode.hip"]
+SOURCES = ["lla_api.hip", "lla_valu.hip", "lla_mfma.hip", "lla_decode.hip", "lla_bwd.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -89,10 +89,11 @@ int validate(const lla_fwd_args* a) {
     if (!aligned16(in)) return fail(LLA_ERR_INVALID_ARG, "input pointer %p not 16-byte aligned", in);
   }
   struct Out { const void* p; size_t bytes; const char* name; };
-  const Out outs[6] = {{a->out, nout, "out"},           {a->rho, nout, "rho"},
+  const Out outs[7] = {{a->out, nout, "out"},           {a->rho, nout, "rho"},
                        {a->omega, nrow, "omega"},       {a->rowmax, nrow, "rowmax"},
-                       {a->cg_iters, nrow, "cg_iters"}, {a->cg_resid, nrow, "cg_resid"}};
-  for (int i = 0; i < 6; ++i) {
+                       {a->cg_iters, nrow, "cg_iters"}, {a->cg_resid, nrow, "cg_resid"},
+                       {a->rho_c, nout, "rho_c"}};
+  for (int i = 0; i < 7; ++i) {
     if (!outs[i].p) continue;
     if (!aligned16(outs[i].p))
       return fail(LLA_ERR_INVALID_ARG, "%s pointer %p not 16-byte aligned", outs[i].name, outs[i].p);
@@ -151,6 +152,7 @@ static int forward_impl(const lla_fwd_args* a, const float* rho_in, hipStream_t 
   p.omega = a->omega; p.rho = a->rho; p.rowmax = a->rowmax;
   p.cg_iters = a->cg_iters; p.cg_resid = a->cg_resid;
   p.rho_in = rho_in;
+  p.rho_c = a->rho_c;
   p.BH = a->B * a->H; p.n = a->n; p.d = a->d; p.dtype = a->dtype;
   p.lambda = a->lambda; p.cg_max_iters = a->cg_max_iters; p.cg_rel_tol = a->cg_rel_tol;
   p.flags = a->flags;
@@ -196,6 +198,7 @@ int lla_output_given_rho(const lla_fwd_args* a, const float* rho_in, hipStream_t
   const int st = validate(a);  // (sizes are checked before they are multiplied below)
   if (st != LLA_OK) return st;
   if (!rho_in) return fail(LLA_ERR_INVALID_ARG, "rho_in is NULL");
+  if (a->rho_c) return fail(LLA_ERR_INVALID_ARG, "rho_c is not defined when rho is supplied");
   if (!aligned16(rho_in)) return fail(LLA_ERR_INVALID_ARG, "rho_in pointer not 16-byte aligned");
   {
     const size_t nrho = (size_t)a->B * a->H * a->n * a->d * sizeof(float);
@@ -295,6 +298,93 @@ size_t lla_decode_workspace_bytes(int B, int H, int n, int d, int dtype) {
   const unsigned long long bh = (unsigned long long)B * (unsigned long long)H;
   if (bh > 65535ULL || bh * (unsigned long long)n > (1ULL << 36)) return 0;
   return lla::decode_workspace_bytes((int)bh, n, d);
+}
+
+int lla_backward_ex(const lla_bwd_args* a, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (!a) return fail(LLA_ERR_INVALID_ARG, "args is NULL");
+  if (a->dtype != LLA_DTYPE_F32 && a->dtype != LLA_DTYPE_BF16)
+    return fail(LLA_ERR_INVALID_ARG, "unknown dtype %d", a->dtype);
+  if (!a->q || !a->k || !a->v || !a->out || !a->dout || !a->rho_c || !a->dq || !a->dk || !a->dv)
+    return fail(LLA_ERR_INVALID_ARG, "q, k, v, out, dout, rho_c, dq, dk and dv must be non-NULL");
+  if (a->B < 1 || a->H < 1 || a->n < 1)
+    return fail(LLA_ERR_INVALID_ARG, "B, H, n must be >= 1 (B=%d H=%d n=%d)", a->B, a->H, a->n);
+  if (!lla::mfma_supported(a->dtype, a->d))
+    return fail(LLA_ERR_UNSUPPORTED, "backward: needs bf16 inputs and d in {64,128} (dtype=%d d=%d)",
+                a->dtype, a->d);
+  if (!std::isfinite(a->lambda) || !(a->lambda > 0.f))
+    return fail(LLA_ERR_INVALID_ARG, "lambda must be finite and > 0 (got %g)", (double)a->lambda);
+  if (a->cg_max_iters < 0 || a->cg_max_iters > 100000)
+    return fail(LLA_ERR_INVALID_ARG, "cg_max_iters must be in [0, 100000] (got %d)", a->cg_max_iters);
+  if (!(a->cg_rel_tol >= 0.f) || !std::isfinite(a->cg_rel_tol))
+    return fail(LLA_ERR_INVALID_ARG, "cg_rel_tol must be finite and >= 0 (got %g)", (double)a->cg_rel_tol);
+  const unsigned long long bh = (unsigned long long)a->B * (unsigned long long)a->H;
+  if (bh > 0x7fffffffULL) return fail(LLA_ERR_UNSUPPORTED, "B*H too large");
+  if (a->n > (1 << 21)) return fail(LLA_ERR_UNSUPPORTED, "backward: n=%d > 2^21", a->n);
+  const unsigned long long rows = bh * (unsigned long long)a->n;
+  if (rows > (1ULL << 40) || bh * (unsigned long long)((a->n + 127) / 128) > 0x7fffffffULL)
+    return fail(LLA_ERR_UNSUPPORTED, "B*H*n too large");
+  const size_t nin = (size_t)rows * a->d * 2, nf = (size_t)rows * a->d * 4, nrow = (size_t)rows * 4;
+  struct Buf { const void* p; size_t bytes; const char* name; };
+  const Buf ins[6] = {{a->q, nin, "q"},     {a->k, nin, "k"},       {a->v, nin, "v"},
+                      {a->out, nf, "out"},  {a->dout, nf, "dout"},  {a->rho_c, nf, "rho_c"}};
+  for (const Buf& in : ins)
+    if (!aligned16(in.p)) return fail(LLA_ERR_INVALID_ARG, "%s pointer %p not 16-byte aligned", in.name, in.p);
+  const Buf outs[5] = {{a->dq, nf, "dq"}, {a->dk, nf, "dk"}, {a->dv, nf, "dv"},
+                       {a->adj_iters, nrow, "adj_iters"}, {a->adj_resid, nrow, "adj_resid"}};
+  for (int i = 0; i < 5; ++i) {
+    if (!outs[i].p) continue;
+    if (!aligned16(outs[i].p))
+      return fail(LLA_ERR_INVALID_ARG, "%s pointer %p not 16-byte aligned", outs[i].name, outs[i].p);
+    for (const Buf& in : ins)
+      if (overlap(outs[i].p, outs[i].bytes, in.p, in.bytes))
+        return fail(LLA_ERR_INVALID_ARG, "%s overlaps %s", outs[i].name, in.name);
+    for (int j = 0; j < i; ++j)
+      if (overlap(outs[i].p, outs[i].bytes, outs[j].p, outs[j].bytes))
+        return fail(LLA_ERR_INVALID_ARG, "%s overlaps %s", outs[i].name, outs[j].name);
+  }
+  if (a->workspace && !aligned16(a->workspace))
+    return fail(LLA_ERR_INVALID_ARG, "workspace pointer not 16-byte aligned");
+  if (a->flags & ~LLA_FLAG_SPLIT_U) return fail(LLA_ERR_INVALID_ARG, "unknown flags 0x%x", a->flags);
+  lla::BwdParams p{};
+  p.q = a->q; p.k = a->k; p.v = a->v;
+  p.out = a->out; p.dout = a->dout; p.rho_c = a->rho_c;
+  p.dq = a->dq; p.dk = a->dk; p.dv = a->dv;
+  p.adj_iters = a->adj_iters; p.adj_resid = a->adj_resid;
+  p.BH = (int)bh; p.n = a->n; p.d = a->d; p.dtype = a->dtype;
+  p.lambda = a->lambda; p.cg_max_iters = a->cg_max_iters; p.cg_rel_tol = a->cg_rel_tol;
+  p.flags = a->flags;
+  p.ev_main_begin = a->ev_main_begin;
+  p.ev_main_end = a->ev_main_end;
+  const size_t need = lla::bwd_workspace_bytes(p.BH, p.n, p.d);
+  void* ws = a->workspace;
+  bool owned = false;
+  if (ws) {
+    if (a->workspace_bytes < need)
+      return fail(LLA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", a->workspace_bytes, need);
+  } else {
+    const hipError_t e = hipMallocAsync(&ws, need, stream);
+    if (e != hipSuccess) return fail(LLA_ERR_HIP, "workspace allocation of %zu bytes: %s", need,
+                                     hipGetErrorString(e));
+    owned = true;
+  }
+  p.workspace = ws;
+  p.workspace_bytes = owned ? need : a->workspace_bytes;
+  const hipError_t e = lla::launch_bwd(p, stream);
+  if (owned) {
+    const hipError_t f = hipFreeAsync(ws, stream);
+    if (e == hipSuccess && f != hipSuccess)
+      return fail(LLA_ERR_HIP, "workspace free: %s", hipGetErrorString(f));
+  }
+  if (e != hipSuccess) return fail(LLA_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
+  return LLA_OK;
+}
+
+size_t lla_backward_workspace_bytes(int B, int H, int n, int d, int dtype) {
+  if (B < 1 || H < 1 || n < 1 || n > (1 << 21) || !lla::mfma_supported(dtype, d)) return 0;
+  const unsigned long long bh = (unsigned long long)B * (unsigned long long)H;
+  if (bh > 0x7fffffffULL || bh * (unsigned long long)n > (1ULL << 40)) return 0;
+  return lla::bwd_workspace_bytes((int)bh, n, d);
 }
 
 int lla_forward_f32(const float* q, const float* k, const float* v, float* out, int B, int H, int n,

@@ -20,6 +20,7 @@ struct FwdParams {
   int32_t* cg_iters; // optional [BH][n]
   float* cg_resid;   // optional [BH][n]
   const float* rho_in;  // supplied rho_i [BH][n][d] (skips the CG solve), or NULL
+  float* rho_c;      // optional [BH][n][d]: the centred system's solution
   int BH;            // B * H
   int n;
   int d;
@@ -68,5 +69,39 @@ hipError_t launch_valu(const FwdParams& p, hipStream_t stream);
 size_t mfma_workspace_bytes(int BH, int n, int d);
 bool mfma_supported(int dtype, int d);
 hipError_t launch_mfma(const FwdParams& p, hipStream_t stream);
+// Pieces of the matrix-core forward that its gradient reuses on the same
+// workspace: the prepasses and the moment kernel (per-query kbar, omega, row
+// max; the residual slab set to mu), and the CG kernel alone, which solves
+// Sigma_c x = r for whatever right-hand side r the residual slab holds.
+hipError_t mfma_moments(const FwdParams& p, hipStream_t stream);
+hipError_t mfma_cg(const FwdParams& p, hipStream_t stream);
+
+// Everything a backward launch needs, already validated by the host API.
+struct BwdParams {
+  const void* q;      // bf16 [BH][n][d]
+  const void* k;
+  const void* v;
+  const float* out;   // the forward output b [BH][n][d]
+  const float* dout;  // dL/db [BH][n][d]
+  const float* rho_c; // the forward's centred solution [BH][n][d]
+  float* dq;          // [BH][n][d]
+  float* dk;
+  float* dv;
+  int32_t* adj_iters; // optional [BH][n]: CG steps of the adjoint solve
+  float* adj_resid;   // optional [BH][n]
+  int BH, n, d, dtype;
+  float lambda;
+  int cg_max_iters;
+  float cg_rel_tol;
+  int flags;         // LLA_FLAG_SPLIT_U: U of the adjoint products as two fp16 terms
+  void* workspace;
+  size_t workspace_bytes;
+  hipEvent_t ev_main_begin;  // optional, recorded around the adjoint CG kernel
+  hipEvent_t ev_main_end;
+};
+
+// gradient of the matrix-core forward (bf16 inputs, d in {64,128})
+size_t bwd_workspace_bytes(int BH, int n, int d);
+hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
 
 }  // namespace lla

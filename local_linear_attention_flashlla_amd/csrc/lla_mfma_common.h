@@ -1,0 +1,244 @@
+// Device helpers, constants and the workspace layout shared by the fp16
+// matrix-core kernels of the forward pass and of its gradient (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lla {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kNW13 = 4;    // waves per workgroup of the moment and output kernels
+constexpr int kNW2 = 4;     // waves per workgroup of the CG kernel
+constexpr int kMaxBQ = 32 * (kNW13 > kNW2 ? kNW13 : kNW2);  // slab padding of the query axis
+constexpr int BK = 32;      // keys per tile
+constexpr int NT = 256;     // threads per workgroup (4 waves)
+constexpr int NORM_ROWS = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRowNormCap = 128.f;
+
+// bits 2 and 3 of the index inside a 16-element chunk swapped (an involution)
+__host__ __device__ constexpr int swz16(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
+
+__device__ __forceinline__ float bf16_to_f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// smallest power of two >= m for m > 0 (1 for m <= 0 or NaN)
+__device__ __forceinline__ float pow2_ceil(float m) {
+  if (!(m > 0.f)) return 1.f;
+  uint32_t b = __float_as_uint(m);
+  uint32_t e = b >> 23;
+  if (e == 0) return 1.1754943508222875e-38f;
+  if (b & 0x7fffffu) e += 1;
+  if (e > 254) e = 254;
+  return __uint_as_float(e << 23);
+}
+
+// largest power of two <= m for m > 0
+__device__ __forceinline__ float pow2_floor(float m) {
+  uint32_t e = __float_as_uint(m) >> 23;
+  if (e == 0) e = 1;
+  if (e > 254) e = 254;
+  return __uint_as_float(e << 23);
+}
+
+__device__ __forceinline__ floatx16 mfma(half8 a, half8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// round two floats to fp16 (nearest even) and add their rounded values to acc
+// with one packed dot product against (1, 1): acc + h0 + h1 exactly in fp32
+__device__ __forceinline__ half2v pack_sum(float a, float b, float& acc) {
+  half2v h;
+  h[0] = static_cast<_Float16>(a);
+  h[1] = static_cast<_Float16>(b);
+  const half2v one = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
+  acc = __builtin_amdgcn_fdot2(h, one, acc, false);
+  return h;
+}
+
+// fp16(a0 b0), fp16(a1 b1) packed, their rounded values added to acc as in
+// pack_sum. v_fma_mixlo/mixhi_f16 form the fp32 product and round it to fp16
+// in one instruction each (the same rounding as a multiply then a convert).
+__device__ __forceinline__ half2v mul_pack_sum(float a0, float b0, float a1, float b1, float& acc) {
+  uint32_t u;
+  asm volatile("v_fma_mixlo_f16 %0, %1, %2, 0" : "=v"(u) : "v"(a0), "v"(b0));
+  asm volatile("v_fma_mixhi_f16 %0, %1, %2, 0" : "+v"(u) : "v"(a1), "v"(b1));
+  const half2v h = __builtin_bit_cast(half2v, u);
+  const half2v one = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
+  acc = __builtin_amdgcn_fdot2(h, one, acc, false);
+  return h;
+}
+
+// The two lanes l and l ^ 32 of a query combine their halves with one
+// v_permlane32_swap (no LDS round trip): it returns the lower half of v in
+// both halves of r[0] and the upper half in both halves of r[1].
+__device__ __forceinline__ float pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+struct Workspace {
+  float* partial;   // [BH][nchunk][2]: max row ||.||^2 of q and k; of v
+  _Float16* kr;     // [BH][npad][D]      s k, d index permuted by swz16
+  _Float16* kt;     // [BH][npad/32][D][32] s k transposed, key index permuted
+  _Float16* vt;     // [BH][npad/32][D][32] sv v transposed, key index permuted
+  float* xs;        // CG iterates: per workgroup BQ x D fp32, lane-contiguous
+  float* kbs;       // fp32 kbar, same layout
+  float* rs;        // CG residuals, same layout
+  float* qs;        // per query row max and omega: [blocks][4 waves][2][64 lanes]
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+Workspace carve(void* base, int BH, int n, int d) {
+  const int nchunk = (n + NORM_ROWS - 1) / NORM_ROWS;
+  const size_t npad = static_cast<size_t>((n + BK - 1) / BK) * BK;
+  char* p = static_cast<char*>(base);
+  Workspace w;
+  w.partial = reinterpret_cast<float*>(p);
+  p += align256(static_cast<size_t>(BH) * nchunk * 2 * sizeof(float));
+  const size_t t = align256(static_cast<size_t>(BH) * npad * d * sizeof(_Float16));
+  w.kr = reinterpret_cast<_Float16*>(p);
+  p += t;
+  w.kt = reinterpret_cast<_Float16*>(p);
+  p += t;
+  w.vt = reinterpret_cast<_Float16*>(p);
+  p += t;
+  const size_t nqpad = static_cast<size_t>((n + kMaxBQ - 1) / kMaxBQ) * kMaxBQ;
+  const size_t sl = align256(static_cast<size_t>(BH) * nqpad * d * sizeof(float));
+  w.xs = reinterpret_cast<float*>(p);
+  p += sl;
+  w.kbs = reinterpret_cast<float*>(p);
+  p += sl;
+  w.rs = reinterpret_cast<float*>(p);
+  p += sl;
+  w.qs = reinterpret_cast<float*>(p);
+  return w;
+}
+
+// The per-head power-of-two scales, from the row-norm partial maxima.
+__device__ __forceinline__ void head_scales(const float* partial, int bh, int nchunk, float* s,
+                                            float* sv) {
+  float mqk = 0.f, mv = 0.f;
+  for (int c = 0; c < nchunk; ++c) {
+    mqk = fmaxf(mqk, partial[(static_cast<size_t>(bh) * nchunk + c) * 2 + 0]);
+    mv = fmaxf(mv, partial[(static_cast<size_t>(bh) * nchunk + c) * 2 + 1]);
+  }
+  const float a = sqrtf(mqk), b = sqrtf(mv);
+  *s = a > 0.f ? fminf(fmaxf(pow2_floor(kRowNormCap / a), 0x1p-60f), 0x1p60f) : 1.f;
+  *sv = b > 0.f ? fminf(fmaxf(pow2_floor(kRowNormCap / b), 0x1p-60f), 0x1p60f) : 1.f;
+}
+
+// Buffer resource over `bytes` bytes at `base` (raw, untyped; reads past the
+// end return zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+
+// 16-byte chunk `chunk` of lane `lane` in a lane-contiguous state slab
+// ([chunk][64 lanes] x 16 bytes)
+__device__ __forceinline__ floatx4 slab_ld(__amdgpu_buffer_rsrc_t r, int chunk, int lane) {
+  return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, chunk * 1024, 0));
+}
+__device__ __forceinline__ void slab_st(__amdgpu_buffer_rsrc_t r, int chunk, int lane, floatx4 x) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, lane * 16, chunk * 1024, 0);
+}
+
+// Copy key tile `kt` of this head (rows or transposed, both BK x D fp16,
+// contiguous in global memory) into an LDS tile with global_load_lds: each
+// wave instruction moves 1 KiB, lane l its l-th 16 bytes; the four waves
+// together copy the tile. Completion is awaited by a later barrier.
+template <int D, int NW>
+__device__ __forceinline__ void load_kr_to_lds(__amdgpu_buffer_rsrc_t head, int kt, _Float16* buf,
+                                               int wave, int lane) {
+  constexpr int NI = D / 16;  // 1 KiB instructions per tile
+  const int tile_off = kt * (BK * D * 2);  // bytes, wave-uniform
+  #pragma unroll
+  for (int u = 0; u < (NI + NW - 1) / NW; ++u) {
+    const int inst = u * NW + wave;
+    if (NI % NW == 0 || inst < NI)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          head, (__attribute__((address_space(3))) void*)(buf + inst * 512), 16,
+          inst * 1024 + lane * 16, tile_off, 0, 0);
+  }
+}
+// Copy instruction u (of ceil(D/16 / NW)) of this wave's share of a tile.
+template <int D, int NW>
+__device__ __forceinline__ void load_chunk_to_lds(__amdgpu_buffer_rsrc_t head, int kt, _Float16* buf,
+                                                  int wave, int lane, int u) {
+  constexpr int NI = D / 16;
+  const int inst = u * NW + wave;
+  if (NI % NW == 0 || inst < NI)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        head, (__attribute__((address_space(3))) void*)(buf + inst * 512), 16,
+        inst * 1024 + lane * 16, kt * (BK * D * 2), 0, 0);
+}
+template <int D, int NW>
+__device__ __forceinline__ void load_kt_to_lds(__amdgpu_buffer_rsrc_t head, int kt, _Float16* buf,
+                                               int wave, int lane) {
+  load_kr_to_lds<D, NW>(head, kt, buf, wave, lane);
+}
+template <int D, int NW>
+__device__ __forceinline__ void load_tile_to_lds(__amdgpu_buffer_rsrc_t kr_head,
+                                                 __amdgpu_buffer_rsrc_t t_head, int kt,
+                                                 _Float16* sKr, _Float16* sKt, int wave, int lane) {
+  load_kr_to_lds<D, NW>(kr_head, kt, sKr, wave, lane);
+  load_kt_to_lds<D, NW>(t_head, kt, sKt, wave, lane);
+}
+
+// End of a step of a pipelined sweep: wait until at most the copies of the
+// last two steps (NS tiles per step, ceil(D/16 / NW) instructions each per
+// wave) are still in flight, i.e. this wave's copies of two steps ago have
+// landed, and all LDS reads of this step are done; then a barrier, after
+// which every wave's copies of two steps ago are visible. The asm statement
+// is also a compiler memory barrier: no memory access moves across.
+template <int D, int NW, int NS = 2>
+__device__ __forceinline__ void step_barrier() {
+  constexpr int per_step = NS * ((D / 16 + NW - 1) / NW);
+  static_assert(per_step == 1 || per_step == 2 || per_step == 4, "vmcnt below");
+  if constexpr (per_step == 4)
+    asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (per_step == 2)
+    asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Work order. Workgroups are handed to the eight XCDs (each with its own L2)
+// in turn: block b runs on XCD b % 8. When the head count divides by 8, each
+// XCD gets its own heads and walks them one after the other, every head's
+// query blocks longest causal prefix first, so the key tiles that an XCD's
+// workgroups stream are those of about one head at a time and stay in its L2.
+// Otherwise the order is longest prefix first across all heads.
+constexpr int kXcds = 8;
+__device__ __forceinline__ void block_coords(int b, int BH, int nqb, int* qb, int* bh) {
+  if (BH % kXcds == 0) {
+    const int xcd = b % kXcds, j = b / kXcds;
+    const int heads_per_xcd = BH / kXcds;
+    *bh = xcd * heads_per_xcd + j / nqb;
+    *qb = nqb - 1 - j % nqb;
+  } else {
+    *qb = nqb - 1 - b / BH;
+    *bh = b % BH;
+  }
+}
+}  // namespace
+}  // namespace lla

@@ -347,6 +347,7 @@ __global__ __launch_bounds__(VT) void lla_valu_kernel(FwdParams P) {
       if (P.rho)
         *reinterpret_cast<float4*>(P.rho + orow * D + c) =
             make_float4(x[u].x * rs, x[u].y * rs, x[u].z * rs, x[u].w * rs);
+      if (P.rho_c) *reinterpret_cast<float4*>(P.rho_c + orow * D + c) = x[u];
     }
   }
   if (l8 == 0) {

@@ -227,3 +227,12 @@ def make_random(B: int, H: int, n: int, d: int, dtype: str = "f32",
         dev = [f64_to_bf16_bits(x) for x in (q, k, v)]
         exact = [bf16_bits_to_f64(x) for x in dev]
     return Workload(spec, B, H, n, d, *exact, *dev)
+
+
+def make_cotangent(B: int, H: int, n: int, d: int, seed: int = 1) -> np.ndarray:
+    """A seeded upstream gradient dL/dout for the backward pass: N(0, 1)
+    entries, drawn in float64 from ``default_rng(seed)`` and rounded to
+    float32 (the float64 widening of those values is what both sides see).
+    Shape [B, H, n, d]."""
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((B, H, n, d)).astype(np.float32)

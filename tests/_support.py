@@ -16,6 +16,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 from oracle import lla_oracle as O  # noqa: E402
+from oracle import lla_oracle_bwd as OB  # noqa: E402
 
 
 def ensure_built():
@@ -132,3 +133,31 @@ def check_parity(wl, out, heads_rows, tol, T=None, cg_tol=None, lam=None, label=
         f"(worst ratio {stats['worst_ratio']:.2f})")
     assert stats["converged_max"] <= tol, f"{label}: a converged row exceeds {tol}"
     return stats
+
+
+def _grad_job(args):
+    q, k, v, g, lam, rows, form, solver, T, tol, jst = args
+    return OB.backward_head(q, k, v, g, lam, form=form, solver=solver, cg_max_iters=T,
+                            cg_rel_tol=tol, rows=rows, jstar=jst)
+
+
+def oracle_grads(wl, g, heads_rows, form="pages", solver="cholesky", T=0, tol=0.0, lam=None,
+                 jstar=None):
+    """Float64 gradients (dq, dk, dv) of sum(g * out) per head: heads_rows is a
+    list of ((b, h), rows); with rows a subset, dk and dv hold those rows'
+    share only (complete for keys at or after the first listed row when the
+    rows run to the end of the head). ``jstar``: optional {(b, h): [n] array}
+    of maximising keys. Runs heads in a process pool."""
+    lam = wl.lam if lam is None else lam
+    jobs = []
+    for (b, h), rows in heads_rows:
+        rows = list(rows)
+        m = max(rows) + 1
+        jst = None if jstar is None else np.asarray(jstar[(b, h)])[:m]
+        jobs.append((wl.q[b, h, :m], wl.k[b, h, :m], wl.v[b, h, :m], np.asarray(g[b, h, :m], np.float64),
+                     lam, rows, form, solver, T, tol, jst))
+    workers = min(len(jobs), max(1, min(16, len(os.sched_getaffinity(0)))))
+    if workers <= 1:
+        return [_grad_job(j) for j in jobs]
+    with ProcessPoolExecutor(max_workers=workers) as ex:
+        return list(ex.map(_grad_job, jobs))

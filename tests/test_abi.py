@@ -54,7 +54,7 @@ def test_struct_layout_matches_header():
     A = _lib.LlaFwdArgs
     assert A.q.offset == 8 and A.out.offset == 32 and A.B.offset == 40
     assert A.omega.offset == 72 and A.workspace_bytes.offset == 120 and A.kernel.offset == 128
-    assert A.ev_main_end.offset == 144 and ctypes.sizeof(A) == 152
+    assert A.ev_main_end.offset == 144 and A.rho_c.offset == 152 and ctypes.sizeof(A) == 160
 
 
 # Fake, well-aligned device addresses: validation only does pointer arithmetic.
@@ -91,6 +91,8 @@ def _call(lib, a):
     ("q", BASE + 8, -1),                 # misaligned
     ("out", BASE + GAP + 64, -1),        # overlaps k
     ("rho", BASE + 3 * GAP + 4096, -1),  # overlaps out
+    ("rho_c", BASE + 3 * GAP + 4096, -1),  # overlaps out
+    ("rho_c", BASE + 6 * GAP + 8, -1),     # misaligned
     ("omega", BASE + 4 * GAP + 4, -1),   # misaligned optional output
 ])
 def test_invalid_arguments_are_rejected_on_the_host(lib, field, value, status):
@@ -104,6 +106,7 @@ def test_invalid_arguments_are_rejected_on_the_host(lib, field, value, status):
     (BASE + 5 * GAP + 4, {}, -1),                 # misaligned rho_in
     (BASE + 3 * GAP + 64, {}, -1),                # rho_in overlaps out
     (BASE + 5 * GAP, {"omega": BASE + 5 * GAP + 1024}, -1),  # an output overlaps rho_in
+    (BASE + 5 * GAP, {"rho_c": BASE + 6 * GAP}, -1),          # rho_c has no meaning here
     (BASE + 5 * GAP, {"B": 0}, -1),               # the forward's own checks run too
     (BASE + 5 * GAP, {"d": 48}, -2),
 ])
@@ -188,8 +191,56 @@ def test_rejected_call_leaves_no_stale_error_after_success_path(lib):
     assert "B, H, n" in _lib.last_error()
 
 
+def _bargs(**kw):
+    a = _lib.LlaBwdArgs()
+    a.dtype = kw.get("dtype", _lib.LLA_DTYPE_BF16)
+    a.q, a.k, a.v = BASE, BASE + GAP, BASE + 2 * GAP
+    a.out, a.dout, a.rho_c = BASE + 3 * GAP, BASE + 4 * GAP, BASE + 5 * GAP
+    a.dq, a.dk, a.dv = BASE + 6 * GAP, BASE + 7 * GAP, BASE + 8 * GAP
+    a.B, a.H, a.n, a.d = 2, 3, 100, 128
+    a.lambda_ = 1.0
+    a.cg_max_iters = 8
+    a.cg_rel_tol = 0.0
+    for key, val in kw.items():
+        setattr(a, key, val)
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("q", 0, -1), ("dout", 0, -1), ("rho_c", 0, -1), ("dq", 0, -1), ("dk", 0, -1), ("dv", 0, -1),
+    ("B", 0, -1), ("n", 0, -1), ("d", 32, -2), ("dtype", _lib.LLA_DTYPE_F32, -2), ("dtype", 5, -1),
+    ("lambda_", float("inf"), -1), ("cg_max_iters", -1, -1), ("cg_rel_tol", -1.0, -1),
+    ("n", (1 << 21) + 1, -2),
+    ("rho_c", BASE + 5 * GAP + 4, -1),    # misaligned
+    ("dk", BASE + 6 * GAP + 1024, -1),    # overlaps dq
+    ("dv", BASE + 2 * GAP + 256, -1),     # overlaps v
+    ("adj_iters", BASE + 7 * GAP + 16, -1),  # overlaps dk
+])
+def test_backward_invalid_arguments_are_rejected_on_the_host(lib, field, value, status):
+    a = _bargs(**{field: value})
+    assert lib.lla_backward_ex(ctypes.byref(a), None) == status
+    assert _lib.last_error() != ""
+    assert lib.lla_backward_ex(None, None) == -1
+
+
+def test_backward_workspace_is_linear_in_n(lib):
+    assert lib.lla_backward_workspace_bytes(1, 1, 100, 32, _lib.LLA_DTYPE_BF16) == 0
+    assert lib.lla_backward_workspace_bytes(1, 1, 100, 64, _lib.LLA_DTYPE_F32) == 0
+    sizes = [lib.lla_backward_workspace_bytes(1, 16, n, 128, _lib.LLA_DTYPE_BF16)
+             for n in (1024, 2048, 4096, 8192)]
+    assert all(s > 0 for s in sizes)
+    diffs = [b - a for a, b in zip(sizes, sizes[1:])]
+    assert diffs[1] == 2 * diffs[0] and diffs[2] == 2 * diffs[1]
+    # and it holds the forward's workspace
+    assert sizes[0] > lib.lla_workspace_bytes(1, 16, 1024, 128, _lib.LLA_DTYPE_BF16, _lib.LLA_KERNEL_MFMA)
+    a = _bargs(workspace=BASE + 9 * GAP,
+               workspace_bytes=lib.lla_backward_workspace_bytes(2, 3, 100, 128, _lib.LLA_DTYPE_BF16) - 16)
+    assert lib.lla_backward_ex(ctypes.byref(a), None) == -4
+
+
 @pytest.mark.parametrize("cname,mirror", [("lla_fwd_args", "LlaFwdArgs"),
-                                           ("lla_decode_args", "LlaDecodeArgs")])
+                                           ("lla_decode_args", "LlaDecodeArgs"),
+                                           ("lla_bwd_args", "LlaBwdArgs")])
 def test_struct_layout_matches_c_compiler(tmp_path, cname, mirror):
     """Compile a tiny C program against include/lla.h with the host compiler
     and compare offsetof() of every field with the ctypes mirror."""
