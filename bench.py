@@ -12,6 +12,10 @@ Algorithmic FLOPs per causal pair (i, j <= i), d = head dim: 4d for the
 moment scan (q.k and w k), 6d per CG iteration (q.k, p.k and U k), 6d for the
 output scan (q.k, rho.k and a v). F = d * sum_i (i+1) (10 + 6 T_i), with T_i
 the CG iterations query i took.
+
+--backward times lla_backward_ex instead (its own JSON line and FLOP count,
+see backward_flops); --decode, --given-rho and --memory-curve time the other
+entry points.
 """
 from __future__ import annotations
 
@@ -273,6 +277,94 @@ def bench_decode(args, torch, lla, dev):
     return 0
 
 
+def backward_flops(n: int, d: int, iters: np.ndarray) -> float:
+    """Algorithmic FLOPs of one backward: per causal pair 4d for the moment
+    scan it repeats (q.k, w k), 6d for the sweep that forms the adjoint
+    right-hand side (q.k, g.v, U k), 6d per adjoint CG iteration (q.k, p.k,
+    U k), 10d for the dq sweep (q.k, rho_c.k, y.k, g.v, dL/ds k) and 16d for
+    the dk/dv sweep (the same four score products, then dL/ds q, w A y,
+    w e rho_c, w A g): d (36 + 6 T_i) per pair, T_i the adjoint iterations of
+    query i. Operands carried as two terms count once."""
+    pairs = np.arange(1, n + 1, dtype=np.float64)
+    return float(d * np.sum(pairs[None, None, :] * (36.0 + 6.0 * iters.astype(np.float64))))
+
+
+def bench_backward(args, torch, lla, wl, q, k, v, dev):
+    """Throughput of lla_backward_ex on the workload: one step = one full
+    backward (dq, dk, dv of sum(dout * out)) given the forward's out and rho_c,
+    all inputs resident. Queries/s = rows whose gradient contributions are
+    formed per second. The roofline line is the adjoint CG kernel (the
+    forward's CG kernel on the adjoint right-hand side)."""
+    from local_linear_attention_flashlla_amd.workloads import make_cotangent
+    B, H, n, d = wl.B, wl.H, wl.n, wl.d
+    shape = (B, H, n, d)
+    out = torch.empty(shape, dtype=torch.float32, device=dev)
+    rho_c = torch.empty(shape, dtype=torch.float32, device=dev)
+    fws = torch.empty(max(lla.workspace_bytes(B, H, n, d, wl.dtype, lla.LLA_KERNEL_MFMA), 16),
+                      dtype=torch.uint8, device=dev)
+    lla.forward(q, k, v, wl.lam, wl.cg_max_iters, wl.cg_rel_tol, out=out, rho_c=rho_c,
+                workspace=fws, kernel=lla.LLA_KERNEL_MFMA)
+    dout = torch.from_numpy(make_cotangent(B, H, n, d, seed=1)).to(dev)
+    dq, dk, dv = (torch.empty(shape, dtype=torch.float32, device=dev) for _ in range(3))
+    bws = torch.empty(lla.backward_workspace_bytes(B, H, n, d), dtype=torch.uint8, device=dev)
+    iters = torch.empty((B, H, n), dtype=torch.int32, device=dev)
+    lla.backward(q, k, v, out, dout, rho_c, wl.lam, wl.cg_max_iters, wl.cg_rel_tol, dq=dq, dk=dk,
+                 dv=dv, adj_iters=iters, workspace=bws, flags=lla.LLA_FLAG_SPLIT_U if args.split_u else 0)
+    torch.cuda.synchronize()
+    iters_np = iters.cpu().numpy()
+    flops = backward_flops(n, d, iters_np)
+    flops_cg = cg_flops(n, d, iters_np)
+
+    def step(events=None):
+        lla.backward(q, k, v, out, dout, rho_c, wl.lam, wl.cg_max_iters, wl.cg_rel_tol, dq=dq, dk=dk,
+                     dv=dv, workspace=bws, events=events,
+                     flags=lla.LLA_FLAG_SPLIT_U if args.split_u else 0)
+
+    def fwd():
+        lla.forward(q, k, v, wl.lam, wl.cg_max_iters, wl.cg_rel_tol, out=out, rho_c=rho_c,
+                    workspace=fws, kernel=lla.LLA_KERNEL_MFMA)
+
+    for _ in range(args.warmup):
+        step()
+        fwd()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events=ev[i])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    cg_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        fwd()
+    torch.cuda.synchronize()
+    fwd_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    achieved = flops_cg / (cg_ms * 1e-3) / 1e12
+    rec = {
+        "metric": "LLA backward queries/s + TFLOP/s (% MFMA peak) at n=4096,d=128, 1 MI355X",
+        "value": B * H * n / (ms * 1e-3), "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        # score-side products fp16 x fp16 (operands in one or two terms), the
+        # dk/dv products bf16 x bf16, all into fp32
+        "vs_baseline": None, "dtype": "fp16", "data": "synthetic",
+        "config": {"workload": f"backward of the {wl.name} forward", "B": B, "H": H, "n": n, "d": d,
+                   "lambda": wl.lam, "cg_max_iters": wl.cg_max_iters, "cg_rel_tol": wl.cg_rel_tol,
+                   "input_dtype": wl.dtype, "accumulate": "f32", "dk_dv_products": "bf16",
+                   "split_u": bool(args.split_u)},
+        "tflops": flops / (ms * 1e-3) / 1e12, "flops_per_step": flops,
+        "adj_iters_mean": float(iters_np.mean()),
+        "forward_ms_same_run": fwd_ms,
+        "main_kernel": "adjoint conjugate-gradient kernel", "main_kernel_ms": cg_ms,
+        "main_kernel_flops": flops_cg,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK["mfma_fp16"], "unit": "TFLOP/s",
+                     "frac": achieved / PEAK["mfma_fp16"], "traffic": None},
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -298,6 +390,9 @@ def main(argv=None):
                          "key and value caches (its last row)")
     ap.add_argument("--decode-batch", type=int, default=0,
                     help="with --decode: batch size B (default: the workload's)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time lla_backward_ex (dq, dk, dv given the forward's out and rho_c) "
+                         "instead of the forward")
     ap.add_argument("--memory-curve", action="store_true",
                     help="instead of timing, print the peak device memory of one forward at "
                          "n = 1k .. 16k (B=1, H=16, d=128) as one JSON line")
@@ -347,6 +442,8 @@ def main(argv=None):
 
     if args.given_rho:
         return bench_given_rho(args, torch, lla, wl, q, k, v, out, ws, kernel, kernel_used)
+    if args.backward:
+        return bench_backward(args, torch, lla, wl, q, k, v, dev)
 
     # iteration counts for the algorithmic FLOP count (untimed)
     iters = torch.empty((B, H, n), dtype=torch.int32, device=dev)
