@@ -181,16 +181,23 @@ struct SweepParams {
 };
 
 // Query-major sweep over the key tiles of each block of 128 queries (four
-// waves of 32; the query along lanes as in the forward's kernels), tiles
-// double-buffered in LDS with one barrier per tile.
+// waves of 32; the query along lanes as in the forward's kernels), tiles in
+// three LDS buffers with one barrier per tile.
 //   MODE 0: the adjoint right-hand side and the maximising key;
 //   MODE 1: dq.
 template <int D, int MODE, bool SPLIT = false>
 __global__ __launch_bounds__(NT) void bwd_sweep(SweepParams P) {
   constexpr int NKS = D / 16, NMB = D / 32, NW = NT / 64, BQW = 32 * NW;
-  __shared__ __align__(16) _Float16 sKr[2][BK * D];
-  __shared__ __align__(16) _Float16 sVr[2][BK * D];
-  __shared__ __align__(16) _Float16 sKt[2][BK * D];
+  // The dq sweep runs a two-stage pipeline over three tile buffers; the
+  // right-hand-side sweep keeps two workgroups per CU instead (its second
+  // accumulator set would cost the second one) and runs the stages in turn.
+  constexpr bool PIPE = MODE == 1;
+  constexpr int NB = PIPE ? 3 : 2;
+  constexpr int NCPT = 3 * ((D / 16 + NW - 1) / NW);  // copy instructions per tile and wave
+  static_assert(NCPT == 6 || NCPT == 3, "vmcnt below");
+  __shared__ __align__(16) _Float16 sKr[NB][BK * D];
+  __shared__ __align__(16) _Float16 sVr[NB][BK * D];
+  __shared__ __align__(16) _Float16 sKt[NB][BK * D];
   __shared__ float sScale[2];
 
   const int tid = threadIdx.x;
@@ -236,7 +243,9 @@ __global__ __launch_bounds__(NT) void bwd_sweep(SweepParams P) {
 
   // per-query operands (B operands of the score products) and constants
   half8 qop[NKS], gop[NKS], glo[NKS];
-  half8 rh[MODE == 1 ? NKS : 1], rl[MODE == 1 ? NKS : 1], yop[MODE == 1 ? NKS : 1], ylo[MODE == 1 ? NKS : 1];
+  // (dq takes y as one fp16 term: its error there stays at the 1e-4 level even
+  // where the fit nearly interpolates; dk needs two, see bwd_keys)
+  half8 rh[MODE == 1 ? NKS : 1], rl[MODE == 1 ? NKS : 1], yop[MODE == 1 ? NKS : 1];
   float sinit_v = 0.f, ginit_v = 0.f;
   float sg = 1.f, om = 0.f;
   float c_rinit = 0.f, c_rslope = 0.f, c_yinit = 0.f, c_eg = 0.f, c_ey = 0.f, c_tau = 0.f,
@@ -302,7 +311,6 @@ __global__ __launch_bounds__(NT) void bwd_sweep(SweepParams P) {
         rh[t] = rfrag(T_RH, t);
         rl[t] = rfrag(T_RL, t);
         yop[t] = rfrag(T_YH, t);
-        ylo[t] = rfrag(T_YL, t);
         gop[t] = rfrag(T_GH, t);
         glo[t] = rfrag(T_GL, t);
       }
@@ -324,8 +332,7 @@ __global__ __launch_bounds__(NT) void bwd_sweep(SweepParams P) {
       for (int t = 0; t < NKS; ++t)
         #pragma unroll
         for (int c = 0; c < 8; ++c) {
-          qop[t][c] = rh[t][c] = rl[t][c] = yop[t][c] = ylo[t][c] = gop[t][c] = glo[t][c] =
-              static_cast<_Float16>(0.f);
+          qop[t][c] = rh[t][c] = rl[t][c] = yop[t][c] = gop[t][c] = glo[t][c] = static_cast<_Float16>(0.f);
         }
     }
   }
@@ -344,38 +351,43 @@ __global__ __launch_bounds__(NT) void bwd_sweep(SweepParams P) {
     load_kr_to_lds<D, NW>(vr_head, j, sVr[b], wave, lane);
     load_kr_to_lds<D, NW>(kt_head, j, sKt[b], wave, lane);
   };
-  copy_tile(0, 0);
-  for (int j = 0; j < ntiles; ++j) {
-    const int b = j & 1;
-    // tile j has landed everywhere and tile j - 1 is no longer read
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (j + 1 < ntiles) copy_tile(j + 1, b ^ 1);
-    if (j > wlast) continue;
-    const _Float16* kb_ = sKr[b];
-    const _Float16* vb_ = sVr[b];
-    const _Float16* tb_ = sKt[b];
-    floatx16 sacc, gacc, racc, yacc;
+  // Two-stage pipeline over the key tiles: step j issues the score products
+  // of tile j + 1 (into the other accumulator set), then the vector work of
+  // tile j, which does not depend on them and runs while they execute, then
+  // tile j's products into acc. Tile t sits in buffer t % NB: in step j the
+  // waves read tiles j and j + 1 while tile j + 2 is copied into the buffer
+  // of tile j - 1.
+  // X[0] = S (scores, log2 units, less the row max), X[1] = G, X[2] = R, X[3] = Yp
+  auto front = [&](int j, floatx16 (&X)[4]) __attribute__((always_inline)) {
+    const _Float16* kb_ = sKr[j % NB];
+    const _Float16* vb_ = sVr[j % NB];
     #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      sacc[r] = sinit_v;
-      gacc[r] = ginit_v;
-      racc[r] = c_rinit;
-      yacc[r] = c_yinit;
+      X[0][r] = sinit_v;
+      X[1][r] = ginit_v;
+      X[2][r] = c_rinit;
+      X[3][r] = c_yinit;
     }
+    // (consecutive products write different accumulators: a dependent
+    // matrix instruction would wait for its predecessor's result)
     #pragma unroll
     for (int t = 0; t < NKS; ++t) {
       const half8 kf = kr_frag_at(kb_, t);
-      sacc = mfma(kf, qop[t], sacc);
-      if constexpr (MODE == 1) {
-        racc = mfma(kf, rh[t], racc);
-        racc = mfma(kf, rl[t], racc);
-        yacc = mfma(kf, yop[t], yacc);
-        yacc = mfma(kf, ylo[t], yacc);
-      }
       const half8 vf = kr_frag_at(vb_, t);
-      gacc = mfma(vf, gop[t], gacc);
-      gacc = mfma(vf, glo[t], gacc);
+      X[0] = mfma(kf, qop[t], X[0]);
+      X[1] = mfma(vf, gop[t], X[1]);
+      if constexpr (MODE == 1) {
+        X[2] = mfma(kf, rh[t], X[2]);
+        X[3] = mfma(kf, yop[t], X[3]);
+        X[1] = mfma(vf, glo[t], X[1]);
+        X[2] = mfma(kf, rl[t], X[2]);
+      } else {
+        X[1] = mfma(vf, glo[t], X[1]);
+      }
     }
+  };
+  auto back = [&](int j, const floatx16 (&X)[4]) __attribute__((always_inline)) {
+    const _Float16* tb_ = sKt[j % NB];
     const bool diag = (j == wlast);
     const int lim = qi - j * BK;  // keys <= lim are visible
     half8 U[2], Ul[2];
@@ -384,7 +396,7 @@ __global__ __launch_bounds__(NT) void bwd_sweep(SweepParams P) {
     for (int r = 0; r < 16; ++r) {
       const int key = key_of(r);
       const bool vis = qvalid && (!diag || key <= lim);
-      const float x = sacc[r];
+      const float x = X[0][r];
       const float w = vis ? fast_exp2(x) : 0.f;
       if constexpr (MODE == 0) {
         const int kj = j * BK + key;
@@ -395,7 +407,7 @@ __global__ __launch_bounds__(NT) void bwd_sweep(SweepParams P) {
         wv[r] = w;
         if (r & 1) {
           if constexpr (SPLIT) {
-            const float u0 = wv[r - 1] * gacc[r - 1], u1 = w * gacc[r];
+            const float u0 = wv[r - 1] * X[1][r - 1], u1 = w * X[1][r];
             const half2v hu = pack_sum(u0, u1, usum);
             const half2v lo = pack_sum(u0 - static_cast<float>(hu[0]), u1 - static_cast<float>(hu[1]), usum);
             U[r >> 3][(r - 1) & 7] = hu[0];
@@ -403,14 +415,14 @@ __global__ __launch_bounds__(NT) void bwd_sweep(SweepParams P) {
             Ul[r >> 3][(r - 1) & 7] = lo[0];
             Ul[r >> 3][r & 7] = lo[1];
           } else {
-            const half2v hu = mul_pack_sum(wv[r - 1], gacc[r - 1], w, gacc[r], usum);
+            const half2v hu = mul_pack_sum(wv[r - 1], X[1][r - 1], w, X[1][r], usum);
             U[r >> 3][(r - 1) & 7] = hu[0];
             U[r >> 3][r & 7] = hu[1];
           }
         }
       } else {
-        const float A = fmaf(c_rslope, racc[r], 1.f);
-        const float e = fmaf(gacc[r], c_eg, yacc[r] * c_ey);
+        const float A = fmaf(c_rslope, X[2][r], 1.f);
+        const float e = fmaf(X[1][r], c_eg, X[3][r] * c_ey);
         wv[r] = w * fmaf(A, e, c_tau) * c_f;
         if (r & 1) {
           const half2v hu = pack_sum(wv[r - 1], wv[r], usum);
@@ -420,13 +432,48 @@ __global__ __launch_bounds__(NT) void bwd_sweep(SweepParams P) {
       }
     }
     #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
+    for (int h = 0; h < 2; ++h)
       #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const half8 kt = kt_frag_at(tb_, mb, h);
-        acc[mb] = mfma(kt, U[h], acc[mb]);
-        if constexpr (SPLIT) acc[mb] = mfma(kt, Ul[h], acc[mb]);
-      }
+      for (int mb = 0; mb < NMB; ++mb) acc[mb] = mfma(kt_frag_at(tb_, mb, h), U[h], acc[mb]);
+    if constexpr (SPLIT)
+      #pragma unroll
+      for (int h = 0; h < 2; ++h)
+        #pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) acc[mb] = mfma(kt_frag_at(tb_, mb, h), Ul[h], acc[mb]);
+  };
+  // step j: tile j + 1 has landed everywhere (the only copy in flight), tile
+  // j - 1 is no longer read; start copying tile j + 2
+  auto step = [&](int j, const floatx16 (&Xc)[4], floatx16 (&Xn)[4]) __attribute__((always_inline)) {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (j + 2 < ntiles) copy_tile(j + 2, (j + 2) % NB);
+    if (j + 1 < ntiles && j + 1 <= wlast) front(j + 1, Xn);
+    if (j <= wlast) back(j, Xc);
+  };
+  floatx16 XA[4];
+  if constexpr (PIPE) {
+    floatx16 XB[4];
+    copy_tile(0, 0);
+    if (ntiles > 1) copy_tile(1, 1);
+    // tile 0 has landed (tile 1 may be in flight)
+    if constexpr (NCPT == 6)
+      asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (0 <= wlast) front(0, XA);
+    for (int j = 0; j < ntiles; j += 2) {
+      step(j, XA, XB);
+      if (j + 1 < ntiles) step(j + 1, XB, XA);
+    }
+  } else {
+    copy_tile(0, 0);
+    for (int j = 0; j < ntiles; ++j) {
+      // tile j has landed everywhere and tile j - 1 is no longer read
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (j + 1 < ntiles) copy_tile(j + 1, (j + 1) % NB);
+      if (j > wlast) continue;
+      front(j, XA);
+      back(j, XA);
+    }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no tile copy in flight at exit
 
@@ -816,14 +863,15 @@ __global__ __launch_bounds__(NT) void bwd_keys(KeyParams P) {
           gacc[4 * a + e] = g4[e];
         }
       }
+      // (consecutive products write different accumulators)
       #pragma unroll
       for (int t = 0; t < NKS; ++t) {
         sacc = mfma(rfrag(T_QR, t), kop[t], sacc);
         racc = mfma(rfrag(T_RH, t), kop[t], racc);
-        racc = mfma(rfrag(T_RL, t), kop[t], racc);
         yacc = mfma(rfrag(T_YH, t), kop[t], yacc);
-        yacc = mfma(rfrag(T_YL, t), kop[t], yacc);
         gacc = mfma(rfrag(T_GH, t), vop[t], gacc);
+        racc = mfma(rfrag(T_RL, t), kop[t], racc);
+        yacc = mfma(rfrag(T_YL, t), kop[t], yacc);
         gacc = mfma(rfrag(T_GL, t), vop[t], gacc);
       }
       #pragma unroll
@@ -859,15 +907,18 @@ __global__ __launch_bounds__(NT) void bwd_keys(KeyParams P) {
       auto tfrag = [&](int X, int mb, int h) __attribute__((always_inline)) {
         return *reinterpret_cast<const bf16x8*>(sT + X * TB + (((2 * h + g) * D + 32 * mb + ql) * 8) * 2);
       };
+      // product-major order: consecutive products write different accumulators
       #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb)
+      for (int h = 0; h < 2; ++h) {
         #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          dk[mb] = mfma_bf(tfrag(T_QT, mb, h), p1[h], dk[mb]);
-          dk[mb] = mfma_bf(tfrag(T_YT, mb, h), p2[h], dk[mb]);
-          dk[mb] = mfma_bf(tfrag(T_RT, mb, h), p3[h], dk[mb]);
-          dv[mb] = mfma_bf(tfrag(T_GT, mb, h), p2[h], dv[mb]);
-        }
+        for (int mb = 0; mb < NMB; ++mb) dk[mb] = mfma_bf(tfrag(T_QT, mb, h), p1[h], dk[mb]);
+        #pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) dv[mb] = mfma_bf(tfrag(T_GT, mb, h), p2[h], dv[mb]);
+        #pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) dk[mb] = mfma_bf(tfrag(T_YT, mb, h), p2[h], dk[mb]);
+        #pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) dk[mb] = mfma_bf(tfrag(T_RT, mb, h), p3[h], dk[mb]);
+      }
     }
     // every wave is done with the transposed tiles
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
