@@ -221,8 +221,10 @@ size_t lla_decode_workspace_bytes(int B, int H, int n, int d, int dtype);
 
 /* ------------------------------------------------------------------------
  * Backward: the gradient of L = sum_i dout_i . out_i with respect to q, k and
- * v for the causal forward computed by the matrix-core path (bf16 inputs,
- * d in {64, 128}). "Local Linear Attention: reading notes" (section 2.2, on
+ * v for the causal forward, on either path: the matrix cores (bf16 inputs,
+ * d in {64, 128}) or the fp32 vector ALU (fp32 or bf16 inputs, d in
+ * {16, 32, 64, 128}; dk and dv accumulated with fp32 atomics, so their last
+ * bits depend on the order of the additions). "Local Linear Attention: reading notes" (section 2.2, on
  * training; appendix D) states that the backward needs further linear
  * systems per query but prints none; the gradient is implicit
  * differentiation of Eqs. (6)-(8) in the form the forward solves (centred at
@@ -260,21 +262,24 @@ typedef struct lla_bwd_args {
   int flags;          /* LLA_FLAG_SPLIT_U: the adjoint's right-hand side and CG
                          products carry w * (...) as two fp16 terms (slower,
                          more exact; see lla_backward_ex) */
+  int kernel;         /* LLA_KERNEL_*: AUTO takes the matrix-core path for bf16
+                         inputs with d in {64, 128}, the vector path otherwise;
+                         use the forward's choice */
 } lla_bwd_args;
 
 /* dq, dk, dv for the forward lla_forward_ex computed with the same q, k, v,
-   lambda and CG policy (kernel LLA_KERNEL_MFMA or AUTO), given its out and
-   rho_c outputs. Every element of dq, dk and dv is written; the inputs are not.
+   lambda, CG policy and kernel choice, given its out and rho_c outputs. Every element of dq, dk and dv is written; the inputs are not.
    Conventions as for lla_forward_ex: device pointers, 16-byte aligned, no
    output may overlap an input or another output; validation on the host
    before any device work (nothing is written on failure); asynchronous on
    `stream`. Returns LLA_OK, LLA_ERR_INVALID_ARG, LLA_ERR_UNSUPPORTED (dtype
-   other than bf16, d outside {64, 128}, sizes too large), LLA_ERR_WORKSPACE
-   or LLA_ERR_HIP. */
+   other than bf16 or d outside {64, 128} with LLA_KERNEL_MFMA, d outside
+   {16, 32, 64, 128}, sizes too large), LLA_ERR_WORKSPACE or LLA_ERR_HIP. */
 int lla_backward_ex(const lla_bwd_args* args, hipStream_t stream);
 
-/* Device workspace bytes lla_backward_ex needs for these sizes (0 for
-   invalid or unsupported ones). Linear in n. */
+/* Device workspace bytes lla_backward_ex needs for these sizes with
+   LLA_KERNEL_AUTO (the matrix-core path; linear in n). 0 where the vector path
+   runs (it needs none) or for invalid sizes. */
 size_t lla_backward_workspace_bytes(int B, int H, int n, int d, int dtype);
 
 /* Static, human-readable name of a status code. */

@@ -196,10 +196,12 @@ def backward_workspace_bytes(B: int, H: int, n: int, d: int, dtype: str = "bf16"
 
 def backward(q, k, v, out, dout, rho_c, lam: float, cg_max_iters: int, cg_rel_tol: float, *,
              dq=None, dk=None, dv=None, adj_iters=None, adj_resid=None, workspace=None,
-             stream=None, events=None, flags=0):
+             stream=None, events=None, flags=0, kernel=LLA_KERNEL_AUTO):
     """Gradient of sum(dout * out) for the causal LLA forward on the GPU.
 
-    q, k, v: [B, H, n, d] bfloat16 (d in {64, 128}), the forward's inputs;
+    q, k, v: [B, H, n, d], the forward's inputs (float32 or bfloat16; the
+    matrix-core path takes bfloat16 with d in {64, 128}, the vector path any
+    d in {16, 32, 64, 128}; ``kernel`` as for ``forward``, the same choice);
     out, rho_c: the forward's output and its ``rho_c`` output ([B, H, n, d]
     float32, from ``forward(..., rho_c=...)`` with the same lam and CG
     policy);
@@ -211,8 +213,8 @@ def backward(q, k, v, out, dout, rho_c, lam: float, cg_max_iters: int, cg_rel_to
     import ctypes
     import torch
 
-    if q.dtype != torch.bfloat16 or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise ValueError("backward: q, k, v must be bfloat16")
+    if q.dtype not in (torch.bfloat16, torch.float32) or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("backward: q, k, v must share one dtype, float32 or bfloat16")
     if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
         raise ValueError("q, k, v must share one [B, H, n, d] shape")
     B, H, n, d = (int(s) for s in q.shape)
@@ -236,7 +238,8 @@ def backward(q, k, v, out, dout, rho_c, lam: float, cg_max_iters: int, cg_rel_to
         if t.dtype != dt or tuple(t.shape) != shp or not t.is_contiguous() or not t.is_cuda:
             raise ValueError(f"{name} must be a contiguous {dt} GPU tensor of shape {shp}")
     a = _lib.LlaBwdArgs()
-    a.dtype = LLA_DTYPE_BF16
+    a.dtype = LLA_DTYPE_BF16 if q.dtype == torch.bfloat16 else LLA_DTYPE_F32
+    a.kernel = int(kernel)
     a.q, a.k, a.v = _ptr(q), _ptr(k), _ptr(v)
     a.out, a.dout, a.rho_c = _ptr(out), _ptr(dout), _ptr(rho_c)
     a.dq, a.dk, a.dv = _ptr(dq), _ptr(dk), _ptr(dv)

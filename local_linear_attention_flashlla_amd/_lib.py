@@ -120,6 +120,7 @@ class LlaBwdArgs(ctypes.Structure):
         ("ev_main_begin", ctypes.c_void_p),
         ("ev_main_end", ctypes.c_void_p),
         ("flags", ctypes.c_int),
+        ("kernel", ctypes.c_int),
     ]
 
 

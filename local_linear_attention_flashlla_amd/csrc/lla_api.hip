@@ -309,9 +309,12 @@ int lla_backward_ex(const lla_bwd_args* a, hipStream_t stream) {
     return fail(LLA_ERR_INVALID_ARG, "q, k, v, out, dout, rho_c, dq, dk and dv must be non-NULL");
   if (a->B < 1 || a->H < 1 || a->n < 1)
     return fail(LLA_ERR_INVALID_ARG, "B, H, n must be >= 1 (B=%d H=%d n=%d)", a->B, a->H, a->n);
-  if (!lla::mfma_supported(a->dtype, a->d))
-    return fail(LLA_ERR_UNSUPPORTED, "backward: needs bf16 inputs and d in {64,128} (dtype=%d d=%d)",
-                a->dtype, a->d);
+  if (!d_supported(a->d)) return fail(LLA_ERR_UNSUPPORTED, "d=%d not in {16,32,64,128}", a->d);
+  int kernel = 0;
+  {
+    const int st = resolve_kernel(a->dtype, a->d, a->kernel, &kernel);
+    if (st != LLA_OK) return st;
+  }
   if (!std::isfinite(a->lambda) || !(a->lambda > 0.f))
     return fail(LLA_ERR_INVALID_ARG, "lambda must be finite and > 0 (got %g)", (double)a->lambda);
   if (a->cg_max_iters < 0 || a->cg_max_iters > 100000)
@@ -324,7 +327,8 @@ int lla_backward_ex(const lla_bwd_args* a, hipStream_t stream) {
   const unsigned long long rows = bh * (unsigned long long)a->n;
   if (rows > (1ULL << 40) || bh * (unsigned long long)((a->n + 127) / 128) > 0x7fffffffULL)
     return fail(LLA_ERR_UNSUPPORTED, "B*H*n too large");
-  const size_t nin = (size_t)rows * a->d * 2, nf = (size_t)rows * a->d * 4, nrow = (size_t)rows * 4;
+  const size_t nin = (size_t)rows * a->d * (a->dtype == LLA_DTYPE_F32 ? 4 : 2);
+  const size_t nf = (size_t)rows * a->d * 4, nrow = (size_t)rows * 4;
   struct Buf { const void* p; size_t bytes; const char* name; };
   const Buf ins[6] = {{a->q, nin, "q"},     {a->k, nin, "k"},       {a->v, nin, "v"},
                       {a->out, nf, "out"},  {a->dout, nf, "dout"},  {a->rho_c, nf, "rho_c"}};
@@ -356,6 +360,11 @@ int lla_backward_ex(const lla_bwd_args* a, hipStream_t stream) {
   p.flags = a->flags;
   p.ev_main_begin = a->ev_main_begin;
   p.ev_main_end = a->ev_main_end;
+  if (kernel == LLA_KERNEL_VALU) {
+    const hipError_t e = lla::launch_valu_bwd(p, stream);
+    if (e != hipSuccess) return fail(LLA_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
+    return LLA_OK;
+  }
   const size_t need = lla::bwd_workspace_bytes(p.BH, p.n, p.d);
   void* ws = a->workspace;
   bool owned = false;
@@ -381,7 +390,7 @@ int lla_backward_ex(const lla_bwd_args* a, hipStream_t stream) {
 }
 
 size_t lla_backward_workspace_bytes(int B, int H, int n, int d, int dtype) {
-  if (B < 1 || H < 1 || n < 1 || n > (1 << 21) || !lla::mfma_supported(dtype, d)) return 0;
+  if (B < 1 || H < 1 || n < 1 || n > (1 << 21) || !lla::mfma_supported(dtype, d)) return 0;  // (vector path: none)
   const unsigned long long bh = (unsigned long long)B * (unsigned long long)H;
   if (bh > 0x7fffffffULL || bh * (unsigned long long)n > (1ULL << 40)) return 0;
   return lla::bwd_workspace_bytes((int)bh, n, d);

@@ -103,5 +103,8 @@ struct BwdParams {
 // gradient of the matrix-core forward (bf16 inputs, d in {64,128})
 size_t bwd_workspace_bytes(int BH, int n, int d);
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
+// gradient of the vector-ALU forward (fp32 or bf16 inputs, d in {16,32,64,128});
+// no workspace; dk and dv are zero-filled and accumulated with atomics
+hipError_t launch_valu_bwd(const BwdParams& p, hipStream_t stream);
 
 }  // namespace lla

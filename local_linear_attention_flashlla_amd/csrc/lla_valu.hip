@@ -22,6 +22,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <algorithm>
+
 #include "lla_internal.h"
 #include "../../include/lla.h"
 
@@ -358,6 +360,439 @@ __global__ __launch_bounds__(VT) void lla_valu_kernel(FwdParams P) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Gradient of the forward above (fp32 arithmetic, any d in {16,32,64,128},
+// fp32 or bf16 inputs): dq, dk, dv of sum(dout * out). One workgroup per block
+// of VQ queries, the thread roles of the forward. The gradient is implicit
+// differentiation of Eqs. (6)-(8) of "Local Linear Attention: reading notes"
+// (section 2.1) in the form centred at kbar, as in the matrix-core backward:
+//   h = C^T g,  adjoint CG  Sigma_c y = h  (the forward's CG loop on h),
+//   e_j = (g.v_j - g.vbar)/omega - (k_j - kbar).y,  A_j = 1 - (k_j - kbar).rho_c,
+//   dL/ds_j = w_j (A_j e_j + tau),  tau = h.rho_c/omega - y.(kbar - q),
+//   and the max's share at the maximising key j* (its row sum, -lambda y.rho_c);
+//   dq = c sum_j dL/ds_j k_j + omega y;
+//   dk_j += c dL/ds_j q - w_j (A_j y + e_j rho_c);  dv_j += (w_j A_j / omega) g.
+// Phase 1 is the forward's, operation for operation, so the row max and kbar
+// (and with them the forward's rho_c) are reproduced exactly. dk and dv are
+// reduced over the block's queries in LDS per key tile and added to the
+// zero-filled outputs with fp32 atomics.
+template <int D, typename Tin>
+__global__ __launch_bounds__(VT) void lla_valu_bwd_kernel(BwdParams P) {
+  constexpr int LD = D + 4;
+  constexpr int NC = D / 4;
+  constexpr int YC = (NC + 7) / 8;
+  __shared__ __align__(16) float sQ[VQ * LD];   // q rows
+  __shared__ __align__(16) float sG[VQ * LD];   // dout rows
+  __shared__ __align__(16) float sP[VQ * LD];   // CG direction, then rho_c
+  __shared__ __align__(16) float sY[VQ * LD];   // y
+  __shared__ __align__(16) float sK[VK * LD];
+  __shared__ __align__(16) float sV[VK * LD];
+  __shared__ float sW[VQ * (VK + 1)];           // weight tile / dL/ds
+  __shared__ float sA[VQ * (VK + 1)];           // c dL/ds with the max's share (dk)
+  __shared__ float sB[VQ * (VK + 1)];           // -w A
+  __shared__ float sE[VQ * (VK + 1)];           // -w e
+  __shared__ float sOm[VQ];
+  __shared__ int sAny;
+
+  const int tid = threadIdx.x;
+  const int row = tid >> 3;
+  const int l8 = tid & 7;
+  const int nqb = (P.n + VQ - 1) / VQ;
+  const int blk = blockIdx.x;
+  const int qb = nqb - 1 - blk / P.BH;
+  const int bh = blk % P.BH;
+  const int i0 = qb * VQ;
+  const int nq = min(VQ, P.n - i0);
+  const int kend = i0 + nq;
+  const int qi = i0 + row;
+  const bool valid = row < nq;
+  const size_t base = static_cast<size_t>(bh) * P.n * D;
+  const Tin* Q = static_cast<const Tin*>(P.q) + base;
+  const Tin* K = static_cast<const Tin*>(P.k) + base;
+  const Tin* V = static_cast<const Tin*>(P.v) + base;
+  const float sc2 = kLog2e / sqrtf(static_cast<float>(D));
+  const float cs = 1.f / sqrtf(static_cast<float>(D));
+  const float lam = P.lambda;
+  const size_t orow = base + static_cast<size_t>(valid ? qi : i0) * D;
+
+  stage_rows<D, LD>(sQ, Q, i0, VQ, kend);
+  for (int e = tid; e < VQ * NC; e += VT) {
+    const int r = e / NC, c = (e % NC) * 4;
+    float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (r < nq) val = *reinterpret_cast<const float4*>(P.dout + base + static_cast<size_t>(i0 + r) * D + c);
+    *reinterpret_cast<float4*>(sG + r * LD + c) = val;
+  }
+
+  // ---------------- phase 1 (the forward's): row max, omega, mu~ ----------------
+  float m2 = -INFINITY;
+  float om = 0.f;
+  float4 acc[YC];
+  for (int u = 0; u < YC; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+  float bestv = -INFINITY;
+  int bestj = valid ? qi : 0;  // the maximising key (ties: the smaller index)
+  for (int kt = 0; kt < kend; kt += VK) {
+    __syncthreads();
+    stage_rows<D, LD>(sK, K, kt, VK, kend);
+    __syncthreads();
+    float s[2];
+    float tmax = -INFINITY;
+    for (int u = 0; u < 2; ++u) {
+      const int kc = l8 + 8 * u;
+      const int j = kt + kc;
+      float dsum = 0.f;
+      for (int c = 0; c < D; c += 4)
+        dsum += dot4(*reinterpret_cast<const float4*>(sQ + row * LD + c),
+                     *reinterpret_cast<const float4*>(sK + kc * LD + c));
+      s[u] = (valid && j <= qi) ? dsum * sc2 : -INFINITY;
+      tmax = fmaxf(tmax, s[u]);
+      if (s[u] > bestv || (s[u] == bestv && s[u] != -INFINITY && j < bestj)) {
+        bestv = s[u];
+        bestj = j;
+      }
+    }
+    tmax = row_max8(tmax);
+    const float mnew = fmaxf(m2, tmax);
+    const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(m2 - mnew);
+    float psum = 0.f;
+    for (int u = 0; u < 2; ++u) {
+      const float w = (s[u] == -INFINITY) ? 0.f : exp2f(s[u] - mnew);
+      sW[row * (VK + 1) + l8 + 8 * u] = w;
+      psum += w;
+    }
+    om = om * alpha + row_sum8(psum);
+    m2 = mnew;
+    for (int u = 0; u < YC; ++u) {
+      acc[u].x *= alpha; acc[u].y *= alpha; acc[u].z *= alpha; acc[u].w *= alpha;
+    }
+    __syncthreads();
+    for (int u = 0; u < YC; ++u) {
+      const int c = (l8 + 8 * u) * 4;
+      if (c < D) {
+        float4 a = acc[u];
+        for (int kk = 0; kk < VK; ++kk)
+          a = fma4(sW[row * (VK + 1) + kk], *reinterpret_cast<const float4*>(sK + kk * LD + c), a);
+        acc[u] = a;
+      }
+    }
+  }
+  // the row's maximising key: larger score, then smaller index, over the 8 lanes
+  for (int o = 1; o < 8; o <<= 1) {
+    const float ov = __shfl_xor(bestv, o);
+    const int oj = __shfl_xor(bestj, o);
+    if (ov > bestv || (ov == bestv && oj < bestj)) {
+      bestv = ov;
+      bestj = oj;
+    }
+  }
+  const float inv_om = valid ? 1.f / om : 0.f;
+  float4 kb[YC], qv[YC], gv4[YC];
+  float gb = 0.f;
+  for (int u = 0; u < YC; ++u) {
+    const int c = (l8 + 8 * u) * 4;
+    kb[u] = qv[u] = gv4[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c < D && valid) {
+      const float4 a = acc[u];
+      kb[u] = make_float4(a.x * inv_om, a.y * inv_om, a.z * inv_om, a.w * inv_om);
+      qv[u] = *reinterpret_cast<const float4*>(sQ + row * LD + c);
+      gv4[u] = *reinterpret_cast<const float4*>(sG + row * LD + c);
+      gb += dot4(gv4[u], *reinterpret_cast<const float4*>(P.out + orow + c));
+    }
+  }
+  gb = row_sum8(gb);
+
+  // ---------------- right-hand side h = C^T g ----------------
+  // U_j = w_j (g.v_j - g.out); h = (sum_j U_j k_j - (sum_j U_j) kbar) / omega
+  // (any constant in place of g.out gives the same h: sum_j w_j (k_j - kbar) = 0)
+  float usum = 0.f;
+  for (int u = 0; u < YC; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int kt = 0; kt < kend; kt += VK) {
+    __syncthreads();
+    stage_rows<D, LD>(sK, K, kt, VK, kend);
+    stage_rows<D, LD>(sV, V, kt, VK, kend);
+    __syncthreads();
+    for (int u = 0; u < 2; ++u) {
+      const int kc = l8 + 8 * u;
+      const int j = kt + kc;
+      float ds = 0.f, dg = 0.f;
+      for (int c = 0; c < D; c += 4) {
+        ds += dot4(*reinterpret_cast<const float4*>(sQ + row * LD + c),
+                   *reinterpret_cast<const float4*>(sK + kc * LD + c));
+        dg += dot4(*reinterpret_cast<const float4*>(sG + row * LD + c),
+                   *reinterpret_cast<const float4*>(sV + kc * LD + c));
+      }
+      float U = 0.f;
+      if (valid && j <= qi) U = exp2f(ds * sc2 - m2) * (dg - gb);
+      sW[row * (VK + 1) + kc] = U;
+      usum += U;
+    }
+    __syncthreads();
+    for (int u = 0; u < YC; ++u) {
+      const int c = (l8 + 8 * u) * 4;
+      if (c < D) {
+        float4 a = acc[u];
+        for (int kk = 0; kk < VK; ++kk)
+          a = fma4(sW[row * (VK + 1) + kk], *reinterpret_cast<const float4*>(sK + kk * LD + c), a);
+        acc[u] = a;
+      }
+    }
+  }
+  usum = row_sum8(usum);
+  float4 hv[YC], x[YC], r[YC];
+  float rr = 0.f, kp = 0.f;
+  for (int u = 0; u < YC; ++u) {
+    const float4 a = acc[u];
+    hv[u] = make_float4((a.x - usum * kb[u].x) * inv_om, (a.y - usum * kb[u].y) * inv_om,
+                        (a.z - usum * kb[u].z) * inv_om, (a.w - usum * kb[u].w) * inv_om);
+    x[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    r[u] = hv[u];
+    rr += dot4(r[u], r[u]);
+    kp += dot4(kb[u], r[u]);
+  }
+  __syncthreads();
+  for (int u = 0; u < YC; ++u) {
+    const int c = (l8 + 8 * u) * 4;
+    if (c < D) *reinterpret_cast<float4*>(sP + row * LD + c) = r[u];
+  }
+  rr = row_sum8(rr);
+  kp = row_sum8(kp);
+  const float r0 = sqrtf(rr);
+  const float stop_at = P.cg_rel_tol * r0;
+  bool active = valid && rr > 0.f && P.cg_max_iters > 0;
+  int iters = 0;
+
+  // ---------------- adjoint CG: Sigma_c y = h (the forward's loop) ----------------
+  for (int it = 0; it < P.cg_max_iters; ++it) {
+    if (tid == 0) sAny = 0;
+    __syncthreads();
+    if (active && l8 == 0) sAny = 1;
+    __syncthreads();
+    if (!sAny) break;
+    float us = 0.f;
+    for (int u = 0; u < YC; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int kt = 0; kt < kend; kt += VK) {
+      __syncthreads();
+      stage_rows<D, LD>(sK, K, kt, VK, kend);
+      __syncthreads();
+      for (int u = 0; u < 2; ++u) {
+        const int kc = l8 + 8 * u;
+        const int j = kt + kc;
+        float ds = 0.f, dt = 0.f;
+        for (int c = 0; c < D; c += 4) {
+          const float4 kv = *reinterpret_cast<const float4*>(sK + kc * LD + c);
+          ds += dot4(*reinterpret_cast<const float4*>(sQ + row * LD + c), kv);
+          dt += dot4(*reinterpret_cast<const float4*>(sP + row * LD + c), kv);
+        }
+        float U = 0.f;
+        if (valid && j <= qi) U = exp2f(ds * sc2 - m2) * (dt - kp);
+        sW[row * (VK + 1) + kc] = U;
+        us += U;
+      }
+      __syncthreads();
+      for (int u = 0; u < YC; ++u) {
+        const int c = (l8 + 8 * u) * 4;
+        if (c < D) {
+          float4 a = acc[u];
+          for (int kk = 0; kk < VK; ++kk)
+            a = fma4(sW[row * (VK + 1) + kk], *reinterpret_cast<const float4*>(sK + kk * LD + c), a);
+          acc[u] = a;
+        }
+      }
+    }
+    us = row_sum8(us);
+    float pAp = 0.f;
+    float4 Ap[YC], pv[YC];
+    for (int u = 0; u < YC; ++u) {
+      const int c = (l8 + 8 * u) * 4;
+      pv[u] = Ap[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (c < D) {
+        pv[u] = *reinterpret_cast<const float4*>(sP + row * LD + c);
+        const float4 a = acc[u];
+        Ap[u] = make_float4(a.x - us * kb[u].x + lam * pv[u].x, a.y - us * kb[u].y + lam * pv[u].y,
+                            a.z - us * kb[u].z + lam * pv[u].z, a.w - us * kb[u].w + lam * pv[u].w);
+        pAp += dot4(pv[u], Ap[u]);
+      }
+    }
+    pAp = row_sum8(pAp);
+    bool step = active && pAp > 0.f;
+    if (active && !step) active = false;
+    float rrn = 0.f;
+    const float al = step ? rr / pAp : 0.f;
+    for (int u = 0; u < YC; ++u) {
+      if (step) {
+        x[u] = fma4(al, pv[u], x[u]);
+        r[u] = fma4(-al, Ap[u], r[u]);
+      }
+      rrn += dot4(r[u], r[u]);
+    }
+    rrn = row_sum8(rrn);
+    float kpn = 0.f;
+    if (step) {
+      ++iters;
+      if (sqrtf(rrn) <= stop_at || rrn == 0.f) {
+        active = false;
+      } else {
+        const float be = rrn / rr;
+        for (int u = 0; u < YC; ++u) {
+          const int c = (l8 + 8 * u) * 4;
+          pv[u] = fma4(be, pv[u], r[u]);
+          if (c < D) *reinterpret_cast<float4*>(sP + row * LD + c) = pv[u];
+          kpn += dot4(kb[u], pv[u]);
+        }
+      }
+      rr = rrn;
+    }
+    kpn = row_sum8(kpn);
+    if (active) kp = kpn;
+    __syncthreads();
+  }
+  if (valid && l8 == 0) {
+    if (P.adj_iters) P.adj_iters[orow / D] = iters;
+    if (P.adj_resid) P.adj_resid[orow / D] = r0 > 0.f ? sqrtf(rr) / r0 : 0.f;
+  }
+
+  // ---------------- per-query constants ----------------
+  __syncthreads();
+  float4 rc[YC];
+  float kbx = 0.f, kby = 0.f, kap = 0.f, yu = 0.f, yr = 0.f;
+  for (int u = 0; u < YC; ++u) {
+    const int c = (l8 + 8 * u) * 4;
+    rc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c < D && valid) rc[u] = *reinterpret_cast<const float4*>(P.rho_c + orow + c);
+    if (c < D) {
+      *reinterpret_cast<float4*>(sP + row * LD + c) = rc[u];
+      *reinterpret_cast<float4*>(sY + row * LD + c) = x[u];
+    }
+    kbx += dot4(kb[u], rc[u]);
+    kby += dot4(kb[u], x[u]);
+    kap += dot4(hv[u], rc[u]);
+    yu += dot4(x[u], make_float4(kb[u].x - qv[u].x, kb[u].y - qv[u].y, kb[u].z - qv[u].z, kb[u].w - qv[u].w));
+    yr += dot4(x[u], rc[u]);
+  }
+  kbx = row_sum8(kbx);
+  kby = row_sum8(kby);
+  kap = row_sum8(kap);
+  yu = row_sum8(yu);
+  yr = row_sum8(yr);
+  const float tau = valid ? kap * inv_om - yu : 0.f;
+  const float msum = -lam * yr;
+  const float gvbar = gb + kap;
+  if (l8 == 0) sOm[row] = inv_om;
+
+  // ---------------- final sweep: dq, and dk, dv per key tile ----------------
+  float rsum = 0.f;
+  for (int u = 0; u < YC; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int kt = 0; kt < kend; kt += VK) {
+    __syncthreads();
+    stage_rows<D, LD>(sK, K, kt, VK, kend);
+    stage_rows<D, LD>(sV, V, kt, VK, kend);
+    __syncthreads();
+    for (int u = 0; u < 2; ++u) {
+      const int kc = l8 + 8 * u;
+      const int j = kt + kc;
+      float ds = 0.f, dr = 0.f, dy = 0.f, dg = 0.f;
+      for (int c = 0; c < D; c += 4) {
+        const float4 kv = *reinterpret_cast<const float4*>(sK + kc * LD + c);
+        ds += dot4(*reinterpret_cast<const float4*>(sQ + row * LD + c), kv);
+        dr += dot4(*reinterpret_cast<const float4*>(sP + row * LD + c), kv);
+        dy += dot4(*reinterpret_cast<const float4*>(sY + row * LD + c), kv);
+        dg += dot4(*reinterpret_cast<const float4*>(sG + row * LD + c),
+                   *reinterpret_cast<const float4*>(sV + kc * LD + c));
+      }
+      const bool vis = valid && j <= qi;
+      const float w = vis ? exp2f(ds * sc2 - m2) : 0.f;
+      const float A = 1.f - (dr - kbx);
+      const float ev = (dg - gvbar) * inv_om - (dy - kby);
+      const float sig = w * fmaf(A, ev, tau);
+      rsum += sig;
+      sW[row * (VK + 1) + kc] = sig;
+      sA[row * (VK + 1) + kc] = cs * ((vis && j == bestj) ? sig - msum : sig);
+      sB[row * (VK + 1) + kc] = -w * A;
+      sE[row * (VK + 1) + kc] = -w * ev;
+    }
+    __syncthreads();
+    for (int u = 0; u < YC; ++u) {
+      const int c = (l8 + 8 * u) * 4;
+      if (c < D) {
+        float4 a = acc[u];
+        for (int kk = 0; kk < VK; ++kk)
+          a = fma4(sW[row * (VK + 1) + kk], *reinterpret_cast<const float4*>(sK + kk * LD + c), a);
+        acc[u] = a;
+      }
+    }
+    // dk_j = sum_i [c dL/ds q_i - w A y_i - w e rho_c,i], dv_j = sum_i (w A / omega_i) g_i
+    for (int e = tid; e < VK * NC; e += VT) {
+      const int kk = e / NC, c = (e % NC) * 4;
+      const int j = kt + kk;
+      if (j >= kend) continue;
+      float4 dk = make_float4(0.f, 0.f, 0.f, 0.f), dv = dk;
+      for (int i = 0; i < nq; ++i) {
+        const float a1 = sA[i * (VK + 1) + kk], a2 = sB[i * (VK + 1) + kk], a3 = sE[i * (VK + 1) + kk];
+        dk = fma4(a1, *reinterpret_cast<const float4*>(sQ + i * LD + c), dk);
+        dk = fma4(a2, *reinterpret_cast<const float4*>(sY + i * LD + c), dk);
+        dk = fma4(a3, *reinterpret_cast<const float4*>(sP + i * LD + c), dk);
+        dv = fma4(-a2 * sOm[i], *reinterpret_cast<const float4*>(sG + i * LD + c), dv);
+      }
+      float* pk = P.dk + base + static_cast<size_t>(j) * D + c;
+      float* pvv = P.dv + base + static_cast<size_t>(j) * D + c;
+      atomicAdd(pk + 0, dk.x); atomicAdd(pk + 1, dk.y); atomicAdd(pk + 2, dk.z); atomicAdd(pk + 3, dk.w);
+      atomicAdd(pvv + 0, dv.x); atomicAdd(pvv + 1, dv.y); atomicAdd(pvv + 2, dv.z); atomicAdd(pvv + 3, dv.w);
+    }
+  }
+  rsum = row_sum8(rsum);
+  if (!valid) return;
+  // dq = c (sum_j dL/ds_j k_j - (sum_j dL/ds_j) k_j*) + omega y
+  for (int u = 0; u < YC; ++u) {
+    const int c = (l8 + 8 * u) * 4;
+    if (c < D) {
+      const float4 ks = load4(K, static_cast<size_t>(bestj) * D + c);
+      const float4 a = acc[u];
+      const float4 o = make_float4(cs * (a.x - rsum * ks.x) + om * x[u].x, cs * (a.y - rsum * ks.y) + om * x[u].y,
+                                   cs * (a.z - rsum * ks.z) + om * x[u].z, cs * (a.w - rsum * ks.w) + om * x[u].w);
+      *reinterpret_cast<float4*>(P.dq + orow + c) = o;
+    }
+  }
+}
+
+__global__ void zero_fill(float* __restrict__ a, float* __restrict__ b, size_t n4) {
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n4;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x) {
+    reinterpret_cast<float4*>(a)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    reinterpret_cast<float4*>(b)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
+template <int D, typename Tin>
+hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
+  const int nqb = (p.n + VQ - 1) / VQ;
+  const long long blocks = static_cast<long long>(nqb) * p.BH;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const size_t n4 = static_cast<size_t>(p.BH) * p.n * D / 4;
+  hipLaunchKernelGGL(zero_fill, dim3(static_cast<unsigned>(std::min<size_t>((n4 + 255) / 256, 65536))), dim3(256), 0,
+                     stream, p.dk, p.dv, n4);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.ev_main_begin) {
+    e = hipEventRecord(p.ev_main_begin, stream);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((lla_valu_bwd_kernel<D, Tin>), dim3(static_cast<unsigned>(blocks)), dim3(VT), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.ev_main_end) return hipEventRecord(p.ev_main_end, stream);
+  return hipSuccess;
+}
+
+template <typename Tin>
+hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
+  switch (p.d) {
+    case 16: return launch_bwd_d<16, Tin>(p, stream);
+    case 32: return launch_bwd_d<32, Tin>(p, stream);
+    case 64: return launch_bwd_d<64, Tin>(p, stream);
+    case 128: return launch_bwd_d<128, Tin>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <int D, typename Tin>
 hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
   const int nqb = (p.n + VQ - 1) / VQ;
@@ -391,6 +826,11 @@ hipError_t launch_t(const FwdParams& p, hipStream_t stream) {
 hipError_t launch_valu(const FwdParams& p, hipStream_t stream) {
   if (p.dtype == LLA_DTYPE_F32) return launch_t<float>(p, stream);
   return launch_t<uint16_t>(p, stream);
+}
+
+hipError_t launch_valu_bwd(const BwdParams& p, hipStream_t stream) {
+  if (p.dtype == LLA_DTYPE_F32) return launch_bwd_t<float>(p, stream);
+  return launch_bwd_t<uint16_t>(p, stream);
 }
 
 }  // namespace lla

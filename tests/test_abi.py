@@ -208,7 +208,7 @@ def _bargs(**kw):
 
 @pytest.mark.parametrize("field,value,status", [
     ("q", 0, -1), ("dout", 0, -1), ("rho_c", 0, -1), ("dq", 0, -1), ("dk", 0, -1), ("dv", 0, -1),
-    ("B", 0, -1), ("n", 0, -1), ("d", 32, -2), ("dtype", _lib.LLA_DTYPE_F32, -2), ("dtype", 5, -1),
+    ("B", 0, -1), ("n", 0, -1), ("d", 48, -2), ("dtype", 5, -1), ("kernel", 9, -1),
     ("lambda_", float("inf"), -1), ("cg_max_iters", -1, -1), ("cg_rel_tol", -1.0, -1),
     ("n", (1 << 21) + 1, -2),
     ("rho_c", BASE + 5 * GAP + 4, -1),    # misaligned
@@ -221,6 +221,13 @@ def test_backward_invalid_arguments_are_rejected_on_the_host(lib, field, value, 
     assert lib.lla_backward_ex(ctypes.byref(a), None) == status
     assert _lib.last_error() != ""
     assert lib.lla_backward_ex(None, None) == -1
+
+
+@pytest.mark.parametrize("kw", [dict(dtype=_lib.LLA_DTYPE_F32, kernel=_lib.LLA_KERNEL_MFMA),
+                                dict(d=32, kernel=_lib.LLA_KERNEL_MFMA)])
+def test_backward_matrix_core_path_needs_bf16_and_d_64_or_128(lib, kw):
+    a = _bargs(**kw)
+    assert lib.lla_backward_ex(ctypes.byref(a), None) == -2
 
 
 def test_backward_workspace_is_linear_in_n(lib):

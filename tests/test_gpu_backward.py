@@ -44,19 +44,19 @@ def torch():
     return _t
 
 
-def run(torch, wl, g, T, tol, lam, adj=False, flags=0):
-    print(f"\n[case] backward {wl.name} B={wl.B} H={wl.H} n={wl.n} d={wl.d} T={T} tol={tol} "
-          f"lam={lam}", flush=True)
+def run(torch, wl, g, T, tol, lam, adj=False, flags=0, kernel=MFMA):
+    print(f"\n[case] backward {wl.name} B={wl.B} H={wl.H} n={wl.n} d={wl.d} dtype={wl.dtype} "
+          f"kernel={kernel} T={T} tol={tol} lam={lam}", flush=True)
     q, k, v = to_device(wl)
     shape = (wl.B, wl.H, wl.n, wl.d)
     rho_c = torch.empty(shape, device="cuda")
-    out = lla.forward(q, k, v, lam, T, tol, kernel=MFMA, rho_c=rho_c)
+    out = lla.forward(q, k, v, lam, T, tol, kernel=kernel, rho_c=rho_c)
     dout = torch.from_numpy(np.ascontiguousarray(g)).cuda()
     kw = {}
     if adj:
         kw = dict(adj_iters=torch.full(shape[:3], -1, dtype=torch.int32, device="cuda"),
                   adj_resid=torch.full(shape[:3], -1.0, device="cuda"))
-    dq, dk, dv = lla.backward(q, k, v, out, dout, rho_c, lam, T, tol, flags=flags, **kw)
+    dq, dk, dv = lla.backward(q, k, v, out, dout, rho_c, lam, T, tol, flags=flags, kernel=kernel, **kw)
     torch.cuda.synchronize()
     res = {"dq": dq.cpu().numpy().astype(np.float64), "dk": dk.cpu().numpy().astype(np.float64),
            "dv": dv.cpu().numpy().astype(np.float64)}
@@ -83,9 +83,11 @@ def kernel_argmax(wl, b, h, rows):
     return js
 
 
-def interp_sensitivity(wl, g, b, h, rows, lam):
-    """S_j = 2^-11 sum_i w_ij |beta_ij / omega_i| |rho_c,i| over the listed
-    rows i (exact float64 quantities, from the oracle's own pieces)."""
+def interp_sensitivity(wl, g, b, h, rows, lam, eps=2.0 ** -11):
+    """S_j = eps sum_i w_ij |beta_ij / omega_i| |rho_c,i| over the listed
+    rows i (exact float64 quantities, from the oracle's own pieces); eps is
+    the rounding of the fit's weights: 2^-11 on the fp16 matrix-core path,
+    2^-24 on the fp32 vector path."""
     from oracle import lla_oracle as O
     c = 1.0 / np.sqrt(wl.d)
     S = np.zeros(wl.n)
@@ -96,18 +98,22 @@ def interp_sensitivity(wl, g, b, h, rows, lam):
         rho_c = O.cholesky_solve(Sc, mu)
         gi = np.asarray(g[b, h, i], np.float64)
         beta = V @ gi - gi @ ((V.T @ w) / omega)
-        S[:i + 1] += 2.0 ** -11 * w * np.abs(beta) / omega * np.linalg.norm(rho_c)
+        S[:i + 1] += eps * w * np.abs(beta) / omega * np.linalg.norm(rho_c)
     return S
 
 
-def check_grads(wl, g, res, heads, dq_rows, kv_from, T, tol, lam, label, factor=4.0):
+def check_grads(wl, g, res, heads, dq_rows, kv_from, T, tol, lam, label, factor=4.0, bar=None,
+                fp16_scores=True):
     """dq on rows dq_rows, dk/dv on keys kv_from..n-1 (the oracle then runs
-    rows kv_from..n-1, which hold every contribution to those keys)."""
+    rows kv_from..n-1, which hold every contribution to those keys). The
+    maximising key is decided on fp16 operands for the matrix-core path; the
+    vector path scores in fp32, where float64's decision is the same (ties
+    at the level of fp32 rounding aside)."""
     n = wl.n
     kv_rows = list(range(kv_from, n))
     rows = sorted(set(dq_rows) | set(kv_rows))
     hr = [((b, h), rows) for b, h in heads]
-    jst = {(b, h): kernel_argmax(wl, b, h, rows) for b, h in heads}
+    jst = {(b, h): kernel_argmax(wl, b, h, rows) for b, h in heads} if fp16_scores else None
     ex = oracle_grads(wl, g, hr, lam=lam, jstar=jst)
     cg = oracle_grads(wl, g, hr, form="centred", solver="cg", T=T, tol=tol, lam=lam, jstar=jst)
     worst = 0.0
@@ -117,12 +123,14 @@ def check_grads(wl, g, res, heads, dq_rows, kv_from, T, tol, lam, label, factor=
             e_gpu.append(row_errors(res[name][b, h, sel], x[idx][sel]))
             e_cg.append(row_errors(c[idx][sel], x[idx][sel]))
             if name == "dk":
-                S = interp_sensitivity(wl, g, b, h, rows, lam)[sel]
+                S = interp_sensitivity(wl, g, b, h, rows, lam,
+                                       eps=2.0 ** -11 if fp16_scores else 2.0 ** -24)[sel]
                 e_s.append(S / np.maximum(np.linalg.norm(x[idx][sel], axis=-1), 1e-30))
             else:
                 e_s.append(np.zeros(len(sel)))
         e_gpu, e_cg, e_s = np.concatenate(e_gpu), np.concatenate(e_cg), np.concatenate(e_s)
-        ratio = float((e_gpu / (tol_of(name) + factor * e_cg + factor * e_s)).max())
+        base = tol_of(name) if bar is None else bar
+        ratio = float((e_gpu / (base + factor * e_cg + factor * e_s)).max())
         worst = max(worst, ratio)
         print(f"[parity] {label} {name}: rows={e_gpu.size} max={e_gpu.max():.3e} "
               f"p50={np.median(e_gpu):.2e} p99={np.quantile(e_gpu, 0.99):.2e} | float64-CG err max "
@@ -266,3 +274,50 @@ def test_backward_split_u_flag(torch):
     g = make_cotangent(1, 2, 256, 128, seed=13)
     res = run(torch, wl, g, T=16, tol=0.0, lam=wl.lam, flags=lla.LLA_FLAG_SPLIT_U)
     check_grads(wl, g, res, [(0, 0), (0, 1)], range(256), 0, 16, 0.0, wl.lam, "split U")
+
+
+# --------------------------- the fp32 vector path ---------------------------
+F32_TOL = 1e-3
+VALU = lla.LLA_KERNEL_VALU
+
+
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("n", [1, 2, 17, 33, 100])
+def test_backward_valu_fp32_ragged(torch, n, d):
+    wl = make_random(1, 2, n, d, "f32", seed=500 + n + d, qk_scale=2.0)
+    g = make_cotangent(1, 2, n, d, seed=n + 3 * d)
+    res = run(torch, wl, g, T=2 * d, tol=1e-7, lam=1.0, kernel=VALU)
+    if n == 1:
+        assert np.abs(res["dq"]).max() <= 1e-6 and np.abs(res["dk"]).max() <= 1e-5
+        np.testing.assert_allclose(res["dv"], g, rtol=1e-5, atol=1e-6)
+        return
+    check_grads(wl, g, res, [(0, 0), (0, 1)], range(n), 0, 2 * d, 1e-7, 1.0,
+                f"valu f32 n={n} d={d}", bar=F32_TOL, fp16_scores=False)
+
+
+@pytest.mark.parametrize("name", ["tiny", "piecewise"])
+def test_backward_valu_fp32_workloads(torch, name):
+    """The fp32 workloads with their own CG policy (tiny: lambda 0.1, tol 1e-8,
+    at most 32 steps; piecewise: lambda 0.1, tol 1e-8, at most 64)."""
+    wl = make_workload(name, H=min(2, make_workload(name, n=8).H))
+    g = make_cotangent(wl.B, wl.H, wl.n, wl.d, seed=7)
+    res = run(torch, wl, g, T=wl.cg_max_iters, tol=wl.cg_rel_tol, lam=wl.lam, kernel=VALU, adj=True)
+    check_grads(wl, g, res, [(0, h) for h in range(wl.H)], range(wl.n), 0, wl.cg_max_iters,
+                wl.cg_rel_tol, wl.lam, f"valu {name}", bar=F32_TOL, fp16_scores=False)
+
+
+@pytest.mark.parametrize("d", [32, 128])
+def test_backward_valu_bf16(torch, d):
+    """bf16 inputs on the vector path (any d), and for d = 128 the same
+    gradient as the matrix-core path within the bf16 bar."""
+    wl = make_random(1, 2, 200, d, "bf16", seed=61 + d, qk_scale=2.0)
+    g = make_cotangent(1, 2, 200, d, seed=9)
+    res = run(torch, wl, g, T=d, tol=1e-6, lam=1.0, kernel=VALU)
+    check_grads(wl, g, res, [(0, 0), (0, 1)], range(200), 0, d, 1e-6, 1.0, f"valu bf16 d={d}",
+                bar=F32_TOL, fp16_scores=False)
+    if d == 128:
+        res2 = run(torch, wl, g, T=d, tol=1e-6, lam=1.0, kernel=MFMA)
+        for name in ("dq", "dk", "dv"):
+            e = row_errors(res2[name][0], res[name][0])
+            print(f"[paths] {name}: matrix-core vs vector max row difference {e.max():.2e}", flush=True)
+            assert e.max() <= BF16_TOL
