@@ -77,8 +77,13 @@ enum {
                                cg_rel_tol < 0 or NaN, out overlapping an
                                input, misaligned pointer, unknown dtype,
                                kernel or flag */
-  LLA_ERR_UNSUPPORTED = -2, /* d not in {16, 32, 64, 128}; sizes too large;
-                               a kernel choice not available for the dtype/d */
+  LLA_ERR_UNSUPPORTED = -2, /* d not in {16, 32, 64, 128}; a kernel choice
+                               not available for the dtype/d; sizes too
+                               large: B*H >= 2^31, B*H*n > 2^40, n > 2^23
+                               (forward, output given rho) or n > 2^21
+                               (backward); decode: B*H > 65535, B*H*n > 2^36
+                               or one head's cache (n*d elements) of 2 GiB
+                               or more */
   LLA_ERR_HIP = -3,         /* a HIP launch or allocation failed */
   LLA_ERR_WORKSPACE = -4    /* caller workspace smaller than required */
 };

@@ -37,6 +37,9 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 
 bool d_supported(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
+// Longest sequence the forward takes (see validate)
+constexpr int kMaxForwardN = 1 << 23;
+
 // Resolve LLA_KERNEL_AUTO and check the choice. Returns LLA_OK or a status.
 int resolve_kernel(int dtype, int d, int requested, int* chosen) {
   if (requested == LLA_KERNEL_AUTO) {
@@ -66,6 +69,9 @@ int validate(const lla_fwd_args* a) {
   if (a->B < 1 || a->H < 1 || a->n < 1)
     return fail(LLA_ERR_INVALID_ARG, "B, H, n must be >= 1 (B=%d H=%d n=%d)", a->B, a->H, a->n);
   if (!d_supported(a->d)) return fail(LLA_ERR_UNSUPPORTED, "d=%d not in {16,32,64,128}", a->d);
+  // one head's key tiles are addressed through buffer resources with a
+  // 32-bit byte range: n <= 2^23 keeps them at or under 2 GiB for every d
+  if (a->n > kMaxForwardN) return fail(LLA_ERR_UNSUPPORTED, "n=%d > 2^23", a->n);
   if (!std::isfinite(a->lambda) || !(a->lambda > 0.f))
     return fail(LLA_ERR_INVALID_ARG, "lambda must be finite and > 0 (got %g)", (double)a->lambda);
   if (a->cg_max_iters < 0 || a->cg_max_iters > 100000)
@@ -129,15 +135,17 @@ const char* lla_last_error(void) { return g_last_error; }
 int lla_version(void) { return LLA_VERSION; }
 
 size_t lla_workspace_bytes(int B, int H, int n, int d, int dtype, int kernel) {
-  if (B < 1 || H < 1 || n < 1 || !d_supported(d)) return 0;
+  if (B < 1 || H < 1 || n < 1 || n > kMaxForwardN || !d_supported(d)) return 0;
   if (dtype != LLA_DTYPE_F32 && dtype != LLA_DTYPE_BF16) return 0;
+  const unsigned long long bh = (unsigned long long)B * (unsigned long long)H;
+  if (bh > 0x7fffffffULL || bh * (unsigned long long)n > (1ULL << 40)) return 0;
   int chosen = 0;
   char saved[sizeof(g_last_error)];
   memcpy(saved, g_last_error, sizeof(saved));
   const int st = resolve_kernel(dtype, d, kernel, &chosen);
   memcpy(g_last_error, saved, sizeof(saved));
   if (st != LLA_OK) return 0;
-  if (chosen == LLA_KERNEL_MFMA) return lla::mfma_workspace_bytes(B * H, n, d);
+  if (chosen == LLA_KERNEL_MFMA) return lla::mfma_workspace_bytes(static_cast<int>(bh), n, d);
   return 0;
 }
 

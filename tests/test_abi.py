@@ -83,6 +83,7 @@ def _call(lib, a):
     ("q", 0, -1), ("k", 0, -1), ("v", 0, -1), ("out", 0, -1),
     ("B", 0, -1), ("H", -1, -1), ("n", 0, -1),
     ("d", 48, -2), ("d", 256, -2), ("d", 0, -2),
+    ("n", (1 << 23) + 1, -2),            # one head's key tiles would pass 2 GiB
     ("lambda_", 0.0, -1), ("lambda_", -1.0, -1), ("lambda_", float("nan"), -1),
     ("lambda_", float("inf"), -1),
     ("cg_max_iters", -1, -1), ("cg_max_iters", 100001, -1),
@@ -99,6 +100,20 @@ def test_invalid_arguments_are_rejected_on_the_host(lib, field, value, status):
     a = _args(**{field: value})
     assert _call(lib, a) == status
     assert _lib.last_error() != ""
+
+
+@pytest.mark.parametrize("B,H,n", [(1 << 16, 1 << 15, 1),     # B*H = 2^31
+                                   (1 << 15, 1 << 15, 1025)])  # B*H*n > 2^40
+def test_too_many_heads_or_rows_are_unsupported(lib, B, H, n):
+    assert _call(lib, _args(B=B, H=H, n=n)) == -2
+    assert lib.lla_workspace_bytes(B, H, n, 64, _lib.LLA_DTYPE_BF16, _lib.LLA_KERNEL_MFMA) == 0
+
+
+def test_workspace_query_respects_the_sequence_limit(lib):
+    ok = lib.lla_workspace_bytes(1, 1, 1 << 23, 128, _lib.LLA_DTYPE_BF16, _lib.LLA_KERNEL_MFMA)
+    assert ok > 0
+    assert lib.lla_workspace_bytes(1, 1, (1 << 23) + 1, 128, _lib.LLA_DTYPE_BF16,
+                                   _lib.LLA_KERNEL_MFMA) == 0
 
 
 @pytest.mark.parametrize("rho_in,kw,status", [
