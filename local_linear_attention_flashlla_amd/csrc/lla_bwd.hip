@@ -249,7 +249,7 @@ __global__ __launch_bounds__(NT) void bwd_sweep(SweepParams P) {
   float sinit_v = 0.f, ginit_v = 0.f;
   float sg = 1.f, om = 0.f;
   float c_rinit = 0.f, c_rslope = 0.f, c_yinit = 0.f, c_eg = 0.f, c_ey = 0.f, c_tau = 0.f,
-        c_msum = 0.f, c_f = 0.f, c_oms = 0.f, c_dqs = 0.f;
+        c_f = 0.f, c_oms = 0.f, c_dqs = 0.f;
   int jst = -1;
   if constexpr (MODE == 0) {
     const float qsc = kLog2e / sqrtf(static_cast<float>(D)) / s;
@@ -322,7 +322,6 @@ __global__ __launch_bounds__(NT) void bwd_sweep(SweepParams P) {
       c_eg = cst[C_EG * 32 + ql];
       c_ey = cst[C_EY * 32 + ql];
       c_tau = cst[C_TAU * 32 + ql];
-      c_msum = cst[C_MSUM * 32 + ql];
       jst = __float_as_int(cst[C_JSTAR * 32 + ql]);
       c_f = cst[C_F * 32 + ql];
       c_oms = cst[C_OMS * 32 + ql];

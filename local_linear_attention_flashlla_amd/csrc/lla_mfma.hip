@@ -714,11 +714,13 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
     floatx16 sa, ta, sb, tb;
     // One step, written out in issue order: the tile copies, PF fragment
     // reads ahead, then for each of the NF matrix products of the step (the
-    // NY of Y, then the NKS of [S; T]) its MFMA(s), the fragment read PF
-    // products ahead and EPS elements of U(j). The sched_barrier fences keep
-    // that order, so the vector work and LDS latency hide under the MFMAs.
+    // NY of Y alternating with the NKS of [S; T]) its MFMA(s), the fragment
+    // read PF products ahead and EPS elements of U(j). The sched_barrier
+    // fences keep that order, so the vector work and LDS latency hide under
+    // the MFMAs.
     constexpr int NY = 2 * NMB, NF = NY + NKS, PF = 4, EPS = 16 / NF;
     static_assert(NF * EPS == 16, "U elements must spread evenly");
+    static_assert(NY == NKS, "slots alternate between Y and front products");
     auto pstep = [&](auto JM, auto masked, int j, const floatx16& sc, const floatx16& tc,
                      floatx16& sn, floatx16& tn, const half8 (&up)[2], const half8 (&ulp)[2],
                      half8 (&uc)[2], half8 (&ulc)[2]) __attribute__((always_inline)) {
@@ -740,10 +742,12 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
                                        u - NCP);
           }
       };
+      // slot k holds Y product k / 2 (k even) or front product k / 2 (k
+      // odd): Y, S, T, Y, S, T, ... so that no accumulator is written by two
+      // matrix instructions fewer than three apart
       auto frag = [&](int k) __attribute__((always_inline)) {
-        // Y products cycle through the accumulators (no two dependent MFMAs
-        // back to back): product k uses row block k % NMB and key half k / NMB
-        return k < NY ? kt_frag_at(tbp, k % NMB, k / NMB) : kr_frag_at(kbn, k - NY);
+        const int p = k >> 1;
+        return (k & 1) == 0 ? kt_frag_at(tbp, p % NMB, p / NMB) : kr_frag_at(kbn, p);
       };
       half8 fr[PF];
       #pragma unroll
@@ -761,13 +765,14 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
       for (int k = 0; k < NF; ++k) {
         copy_at(k);
         const half8 f = fr[k % PF];
-        if (k < NY) {
+        if ((k & 1) == 0) {
+          const int p = k >> 1;
           if (doY) {
-            acc[k % NMB] = mfma(f, up[k / NMB], acc[k % NMB]);
-            if constexpr (SPLIT_U) acc[k % NMB] = mfma(f, ulp[k / NMB], acc[k % NMB]);
+            acc[p % NMB] = mfma(f, up[p / NMB], acc[p % NMB]);
+            if constexpr (SPLIT_U) acc[p % NMB] = mfma(f, ulp[p / NMB], acc[p % NMB]);
           }
         } else {
-          const int t = k - NY;
+          const int t = k >> 1;
           if (doF) {
             sn = mfma(f, qop[t], t == 0 ? sinit : sn);
             tn = mfma(f, dop[t], t == 0 ? tinit : tn);
