@@ -123,7 +123,9 @@ typedef struct lla_fwd_args {
   int32_t* cg_iters;  /* [B][H][n]    CG steps taken by the query */
   float* cg_resid;    /* [B][H][n]    ||r_k|| / ||r_0|| at exit (0 if r_0 = 0) */
   /* optional caller workspace (device); NULL = the library allocates and
-     frees it stream-ordered on `stream` */
+     frees it stream-ordered on `stream`. With a workspace (or where none is
+     needed) a call only launches kernels on `stream`: no allocation, memset
+     or synchronisation, so it can be captured into a HIP graph */
   void* workspace;
   size_t workspace_bytes;
   int kernel;         /* LLA_KERNEL_* */
