@@ -19,6 +19,39 @@ from oracle import lla_oracle as O  # noqa: E402
 from oracle import lla_oracle_bwd as OB  # noqa: E402
 
 
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def load_golden(name):
+    """Parse a fixture under tests/golden: 'key: v1 v2 ...' lines of integers
+    or fractions p/q, '#' comments. Returns {key: float64 array}."""
+    from fractions import Fraction
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                key, vals = line.split(":", 1)
+                out[key.strip()] = np.array([float(Fraction(x)) for x in vals.split()])
+    return out
+
+
+def pad(x, d):
+    """x zero-padded to length d."""
+    y = np.zeros(d)
+    y[:len(x)] = x
+    return y
+
+
+def worked_example_inputs(g, d):
+    """q, k, v ([n, d] float64, zero-padded) of the equal-scores worked example."""
+    n = sum(1 for key in g if key.startswith("k"))
+    q = np.stack([pad(g["q"], d)] * n)
+    k = np.stack([pad(g[f"k{j}"], d) for j in range(n)])
+    v = np.stack([pad(g[f"v{j}"], d) for j in range(n)])
+    return q, k, v
+
+
 def ensure_built():
     from local_linear_attention_flashlla_amd import _lib, build
     if not os.path.exists(_lib.LIB_PATH):

@@ -9,6 +9,7 @@ from scipy.special import softmax
 
 import oracle
 from oracle import lla_oracle as O
+from tests._support import load_golden, pad, worked_example_inputs
 from local_linear_attention_flashlla_amd.workloads import make_workload, make_random
 
 
@@ -185,6 +186,25 @@ def test_two_keys_in_one_dimension_is_linear_interpolation():
     r = O.oracle_row(q, k, v, 1e-12)
     expect = 2.0 + (-1.0 - 2.0) * (0.9 - 0.3) / (1.7 - 0.3)
     assert abs(r.b[0] - expect) < 1e-9
+
+
+@pytest.mark.parametrize("d", [3, 16])
+def test_equal_scores_worked_example(d):
+    """The hand-derived example in tests/golden (every weight exactly 1, exact
+    fractions from Eqs. (6)-(8)); zero-padding the head dimension changes
+    nothing."""
+    g = load_golden("equal_scores_worked_example.txt")
+    q, k, v = worked_example_inputs(g, d)
+    lam = g["lambda"][0]
+    for i in range(q.shape[0]):
+        r = O.oracle_row(q[i], k[:i + 1], v[:i + 1], lam)
+        np.testing.assert_allclose(r.w, 1.0, rtol=0, atol=1e-15)
+        assert abs(r.m - g["score"][0] / np.sqrt(d)) < 1e-15
+        assert abs(r.omega - g[f"omega{i}"][0]) < 1e-12
+        np.testing.assert_allclose(r.rho, pad(g[f"rho{i}"], d), rtol=0, atol=1e-12)
+        assert abs(r.schur - g[f"schur{i}"][0]) < 1e-12
+        np.testing.assert_allclose(r.s, g[f"s{i}"], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(r.b, pad(g[f"b{i}"], d), rtol=0, atol=1e-12)
 
 
 # --- [LLA] Eq. (9) and the [PLX] covariance form ------------------------------
