@@ -294,22 +294,28 @@ def bench_backward(args, torch, lla, wl, q, k, v, dev):
     backward (dq, dk, dv of sum(dout * out)) given the forward's out and rho_c,
     all inputs resident. Queries/s = rows whose gradient contributions are
     formed per second. The roofline line is the adjoint CG kernel (the
-    forward's CG kernel on the adjoint right-hand side)."""
+    forward's CG kernel on the adjoint right-hand side); on the fp32 vector
+    path (--kernel valu, or fp32 inputs) it is the one fused backward kernel."""
     from local_linear_attention_flashlla_amd.workloads import make_cotangent
     B, H, n, d = wl.B, wl.H, wl.n, wl.d
     shape = (B, H, n, d)
+    mfma = args.kernel == "mfma" or (
+        args.kernel == "auto" and lla.backward_workspace_bytes(B, H, n, d, wl.dtype) > 0)
+    kern = lla.LLA_KERNEL_MFMA if mfma else lla.LLA_KERNEL_VALU
     out = torch.empty(shape, dtype=torch.float32, device=dev)
     rho_c = torch.empty(shape, dtype=torch.float32, device=dev)
-    fws = torch.empty(max(lla.workspace_bytes(B, H, n, d, wl.dtype, lla.LLA_KERNEL_MFMA), 16),
+    fws = torch.empty(max(lla.workspace_bytes(B, H, n, d, wl.dtype, kern), 16),
                       dtype=torch.uint8, device=dev)
     lla.forward(q, k, v, wl.lam, wl.cg_max_iters, wl.cg_rel_tol, out=out, rho_c=rho_c,
-                workspace=fws, kernel=lla.LLA_KERNEL_MFMA)
+                workspace=fws, kernel=kern)
     dout = torch.from_numpy(make_cotangent(B, H, n, d, seed=1)).to(dev)
     dq, dk, dv = (torch.empty(shape, dtype=torch.float32, device=dev) for _ in range(3))
-    bws = torch.empty(lla.backward_workspace_bytes(B, H, n, d), dtype=torch.uint8, device=dev)
+    bws = torch.empty(max(lla.backward_workspace_bytes(B, H, n, d, wl.dtype) if mfma else 0, 16),
+                      dtype=torch.uint8, device=dev)
     iters = torch.empty((B, H, n), dtype=torch.int32, device=dev)
     lla.backward(q, k, v, out, dout, rho_c, wl.lam, wl.cg_max_iters, wl.cg_rel_tol, dq=dq, dk=dk,
-                 dv=dv, adj_iters=iters, workspace=bws, flags=lla.LLA_FLAG_SPLIT_U if args.split_u else 0)
+                 dv=dv, adj_iters=iters, workspace=bws, kernel=kern,
+                 flags=lla.LLA_FLAG_SPLIT_U if args.split_u else 0)
     torch.cuda.synchronize()
     iters_np = iters.cpu().numpy()
     flops = backward_flops(n, d, iters_np)
@@ -317,12 +323,12 @@ def bench_backward(args, torch, lla, wl, q, k, v, dev):
 
     def step(events=None):
         lla.backward(q, k, v, out, dout, rho_c, wl.lam, wl.cg_max_iters, wl.cg_rel_tol, dq=dq, dk=dk,
-                     dv=dv, workspace=bws, events=events,
+                     dv=dv, workspace=bws, events=events, kernel=kern,
                      flags=lla.LLA_FLAG_SPLIT_U if args.split_u else 0)
 
     def fwd():
         lla.forward(q, k, v, wl.lam, wl.cg_max_iters, wl.cg_rel_tol, out=out, rho_c=rho_c,
-                    workspace=fws, kernel=lla.LLA_KERNEL_MFMA)
+                    workspace=fws, kernel=kern)
 
     for _ in range(args.warmup):
         step()
@@ -341,25 +347,28 @@ def bench_backward(args, torch, lla, wl, q, k, v, dev):
         fwd()
     torch.cuda.synchronize()
     fwd_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    achieved = flops_cg / (cg_ms * 1e-3) / 1e12
+    # matrix cores: the adjoint CG kernel; vector path: the fused kernel (all of it)
+    achieved = (flops_cg if mfma else flops) / (cg_ms * 1e-3) / 1e12
+    peak = PEAK["mfma_fp16"] if mfma else PEAK["valu_fp32"]
     rec = {
         "metric": "LLA backward queries/s + TFLOP/s (% MFMA peak) at n=4096,d=128, 1 MI355X",
         "value": B * H * n / (ms * 1e-3), "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        # score-side products fp16 x fp16 (operands in one or two terms), the
-        # dk/dv products bf16 x bf16, all into fp32
-        "vs_baseline": None, "dtype": "fp16", "data": "synthetic",
+        # matrix cores: score-side products fp16 x fp16 (operands in one or
+        # two terms), the dk/dv products bf16 x bf16, all into fp32
+        "vs_baseline": None, "dtype": "fp16" if mfma else "f32", "data": "synthetic",
         "config": {"workload": f"backward of the {wl.name} forward", "B": B, "H": H, "n": n, "d": d,
                    "lambda": wl.lam, "cg_max_iters": wl.cg_max_iters, "cg_rel_tol": wl.cg_rel_tol,
-                   "input_dtype": wl.dtype, "accumulate": "f32", "dk_dv_products": "bf16",
-                   "split_u": bool(args.split_u)},
+                   "input_dtype": wl.dtype, "accumulate": "f32",
+                   "kernel": "mfma" if mfma else "valu",
+                   "dk_dv_products": "bf16" if mfma else "f32", "split_u": bool(args.split_u)},
         "tflops": flops / (ms * 1e-3) / 1e12, "flops_per_step": flops,
         "adj_iters_mean": float(iters_np.mean()),
         "forward_ms_same_run": fwd_ms,
-        "main_kernel": "adjoint conjugate-gradient kernel", "main_kernel_ms": cg_ms,
-        "main_kernel_flops": flops_cg,
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK["mfma_fp16"], "unit": "TFLOP/s",
-                     "frac": achieved / PEAK["mfma_fp16"], "traffic": None},
+        "main_kernel": "adjoint conjugate-gradient kernel" if mfma else "fused backward kernel",
+        "main_kernel_ms": cg_ms, "main_kernel_flops": flops_cg if mfma else flops,
+        "roofline": {"bound": "mfma" if mfma else "alu", "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None},
     }
     print(json.dumps(rec), flush=True)
     return 0
