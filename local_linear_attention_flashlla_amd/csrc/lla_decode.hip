@@ -101,6 +101,17 @@ __device__ __forceinline__ float wave_sum(float v) {
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
+// Maximum over the 64 lanes, the same exchanges as wave_sum.
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_partner<0xB1>(v));
+  v = fmaxf(v, dpp_partner<0x4E>(v));
+  v = fmaxf(v, dpp_partner<0x141>(v));
+  v = fmaxf(v, dpp_partner<0x140>(v));
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 
 // Buffer resource over `bytes` bytes at `base` (reads past the end return 0).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -144,27 +155,34 @@ __device__ __forceinline__ void wait_copies_barrier() {
 }
 template <int I> using IC = std::integral_constant<int, I>;
 
-// m (log2 units), omega and kbar of head bh from the S chunk partials:
+// m (log2 units), omega and kbar of head bh from the S <= 64 chunk partials:
 // m = max_c m_c, omega = sum_c omega_c 2^(m_c - m), mu~ likewise, kbar = mu~ / omega.
-// Threads t < D write kbar[t]; thread 0 writes mo[0] = m, mo[1] = omega.
+// The first wave reads one chunk per lane (all loads in flight at once) and
+// leaves the factors 2^(m_c - m) in sa[64]; threads t < D then sum their
+// element of mu~ over the chunks, eight loads at a time. Writes kbar[t]
+// (t < D), mo[0] = m, mo[1] = omega. Every thread of the block must call it.
 template <int D>
-__device__ __forceinline__ void combine_moments(const DecParams& P, int bh, float* kbar, float* mo) {
+__device__ __forceinline__ void combine_moments(const DecParams& P, int bh, float* kbar, float* mo, float* sa) {
   const float* base = P.p1 + static_cast<size_t>(bh) * P.S * (D + 2);
-  float m = -INFINITY;
-  for (int c = 0; c < P.S; ++c) m = fmaxf(m, base[c * (D + 2)]);
-  float om = 0.f, mu = 0.f;
   const int t = threadIdx.x;
-  for (int c = 0; c < P.S; ++c) {
-    const float* pc = base + c * (D + 2);
-    if (pc[0] == -INFINITY) continue;
-    const float a = exp2f(pc[0] - m);
-    om += pc[1] * a;
-    if (t < D) mu += pc[2 + t] * a;
+  if (t < 64) {
+    const float mc = t < P.S ? base[t * (D + 2)] : -INFINITY;
+    const float oc = t < P.S ? base[t * (D + 2) + 1] : 0.f;
+    const float m = wave_max(mc);
+    const float a = mc == -INFINITY ? 0.f : exp2f(mc - m);
+    const float om = wave_sum(oc * a);
+    sa[t] = a;
+    if (t == 0) {
+      mo[0] = m;
+      mo[1] = om;
+    }
   }
-  if (t < D) kbar[t] = mu / om;
-  if (t == 0) {
-    mo[0] = m;
-    mo[1] = om;
+  __syncthreads();
+  if (t < D) {
+    float mu = 0.f;
+    #pragma unroll 8
+    for (int c = 0; c < P.S; ++c) mu += base[c * (D + 2) + 2 + t] * sa[c];
+    kbar[t] = mu / mo[1];
   }
 }
 
@@ -286,7 +304,7 @@ __global__ __launch_bounds__(DT) void dec_gram(DecParams P) {
   __shared__ __align__(16) _Float16 cHi[D * GLD], cLo[D * GLD], wHi[D * GLD], wLo[D * GLD];
   __shared__ float skb[D];
   __shared__ float sw[2][GK];
-  __shared__ float smo[2];
+  __shared__ float smo[2], sca[64];
   auto RB = [&](auto I) __attribute__((always_inline)) -> T* {
     constexpr int i = decltype(I)::value % 4;
     if constexpr (i == 0) return r0;
@@ -307,7 +325,7 @@ __global__ __launch_bounds__(DT) void dec_gram(DecParams P) {
   copy_tile<D>(kr, toff(0), r0, wave, lane);
   copy_tile<D>(kr, toff(1), r1, wave, lane);
   copy_tile<D>(kr, toff(2), r2, wave, lane);
-  combine_moments<D>(P, bh, skb, smo);
+  combine_moments<D>(P, bh, skb, smo, sca);
   __syncthreads();
   const float m = smo[0];
   const float* S = P.s + static_cast<size_t>(bh) * P.n;
@@ -418,16 +436,31 @@ __global__ __launch_bounds__(DT) void dec_solve(DecParams P) {
   constexpr int NP = DT / D;         // column parts of the matrix-vector product
   __shared__ float sG[D * LG];
   __shared__ float skb[D], sp_[D], spart[NP][D];
-  __shared__ float smo[2], red[DT / 64];
+  __shared__ float smo[2], red[DT / 64], sca[64];
   const int bh = blockIdx.x, t = threadIdx.x;
-  combine_moments<D>(P, bh, skb, smo);
-  // G + lambda I from the chunk Grams (coalesced over the d^2 entries)
-  const float* Gc = P.gram + static_cast<size_t>(bh) * P.SG * D * D;
-  for (int idx = t; idx < D * D; idx += DT) {
-    float a = 0.f;
-    for (int c = 0; c < P.SG; ++c) a += Gc[static_cast<size_t>(c) * D * D + idx];
-    const int i = idx / D, j = idx % D;
-    sG[i * LG + j] = a + (i == j ? P.lambda : 0.f);
+  combine_moments<D>(P, bh, skb, smo, sca);
+  // G + lambda I from the chunk Grams: each thread sums its NG float4s of G
+  // over the chunks in order, all NG loads of a chunk in flight together
+  constexpr int NG = D * D / 4 / DT;
+  static_assert(NG * 4 * DT == D * D, "G must spread evenly over the threads");
+  const float4* Gc = reinterpret_cast<const float4*>(P.gram + static_cast<size_t>(bh) * P.SG * D * D);
+  float4 ga[NG];
+  #pragma unroll
+  for (int u = 0; u < NG; ++u) ga[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c = 0; c < P.SG; ++c) {
+    const float4* gc = Gc + static_cast<size_t>(c) * (D * D / 4);
+    #pragma unroll
+    for (int u = 0; u < NG; ++u) {
+      const float4 g = gc[t + DT * u];
+      ga[u].x += g.x; ga[u].y += g.y; ga[u].z += g.z; ga[u].w += g.w;
+    }
+  }
+  #pragma unroll
+  for (int u = 0; u < NG; ++u) {
+    const int idx = 4 * (t + DT * u), i = idx / D, j = idx % D;
+    const float e[4] = {ga[u].x, ga[u].y, ga[u].z, ga[u].w};
+    #pragma unroll
+    for (int q = 0; q < 4; ++q) sG[i * LG + j + q] = e[q] + (i == j + q ? P.lambda : 0.f);
   }
   __syncthreads();
   const float m = smo[0], om = smo[1];
@@ -612,6 +645,7 @@ __global__ __launch_bounds__(DT) void dec_finish(DecParams P) {
   if (t >= D) return;
   const float* p4 = P.p4 + static_cast<size_t>(bh) * P.S * (D + 1);
   float o = 0.f, den = 0.f;
+  #pragma unroll 8
   for (int c = 0; c < P.S; ++c) {
     o += p4[c * (D + 1) + t];
     den += p4[c * (D + 1) + D];
