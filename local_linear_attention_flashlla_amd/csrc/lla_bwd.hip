@@ -122,18 +122,6 @@ BwdWorkspace carve_bwd(void* base, int BH, int n, int d) {
   return w;
 }
 
-// largest row norms of q and k together, and of v, of one head
-__device__ __forceinline__ void head_norms(const float* partial, int bh, int nchunk, float* kmax,
-                                           float* vmax) {
-  float a = 0.f, b = 0.f;
-  for (int c = 0; c < nchunk; ++c) {
-    a = fmaxf(a, partial[(static_cast<size_t>(bh) * nchunk + c) * 2 + 0]);
-    b = fmaxf(b, partial[(static_cast<size_t>(bh) * nchunk + c) * 2 + 1]);
-  }
-  *kmax = sqrtf(a);
-  *vmax = sqrtf(b);
-}
-
 // ---------------------------------------------------------------------------
 // Value tiles in the row layout of the key tiles (for G = V g^T).
 template <int D>
@@ -143,7 +131,14 @@ __global__ __launch_bounds__(NT) void prep_vrows(const uint16_t* __restrict__ v,
   const int bh = blockIdx.x, kb = blockIdx.y;
   __shared__ float sV[BK][D + 1];
   __shared__ float sc[2];
-  if (threadIdx.x == 0) head_scales(partial, bh, nchunk, &sc[0], &sc[1]);
+  if (threadIdx.x < 64) {
+    float a, b;
+    head_scales(partial, bh, nchunk, threadIdx.x, &a, &b);
+    if (threadIdx.x == 0) {
+      sc[0] = a;
+      sc[1] = b;
+    }
+  }
   __syncthreads();
   const float sv = sc[1];
   for (int e = threadIdx.x; e < BK * D; e += NT) {
@@ -217,7 +212,14 @@ __global__ __launch_bounds__(NT) void bwd_sweep(SweepParams P) {
   const bool wave_any = wfirst < n;
   const int wlast = wave_any ? min(ntiles - 1, wfirst / BK) : -1;
 
-  if (tid == 0) head_scales(P.partial, bh, P.nchunk, &sScale[0], &sScale[1]);
+  if (tid < 64) {
+    float a, b;
+    head_scales(P.partial, bh, P.nchunk, tid, &a, &b);
+    if (tid == 0) {
+      sScale[0] = a;
+      sScale[1] = b;
+    }
+  }
   __syncthreads();
   const float s = sScale[0], sv = sScale[1];
 
@@ -562,9 +564,16 @@ __global__ __launch_bounds__(NT) void bwd_rows(RowsParams P) {
   const bool tvalid = T < P.nblk;
   const int qi = 32 * T + ql;
   const bool qvalid = qi < n;
-  if (tid == 0) {
-    head_scales(P.partial, bh, P.nchunk, &sScale[0], &sScale[1]);
-    head_norms(P.partial, bh, P.nchunk, &sScale[2], &sScale[3]);
+  if (tid < 64) {
+    float a, b, mqk, mv;
+    head_scales(P.partial, bh, P.nchunk, tid, &a, &b);
+    head_maxima(P.partial, bh, P.nchunk, tid, &mqk, &mv);
+    if (tid == 0) {
+      sScale[0] = a;
+      sScale[1] = b;
+      sScale[2] = sqrtf(mqk);  // largest row norm of q and k together
+      sScale[3] = sqrtf(mv);   // and of v
+    }
   }
   __syncthreads();
   const float s = sScale[0], sv = sScale[1], kmax = sScale[2], vmax = sScale[3];

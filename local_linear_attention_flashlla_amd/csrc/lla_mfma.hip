@@ -139,7 +139,14 @@ __global__ __launch_bounds__(NT) void prep_convert(const uint16_t* __restrict__ 
   __shared__ float sK[BK][D + 1];
   __shared__ float sV[BK][D + 1];
   __shared__ float sc[2];
-  if (threadIdx.x == 0) head_scales(partial, bh, nchunk, &sc[0], &sc[1]);
+  if (threadIdx.x < 64) {
+    float a, b;
+    head_scales(partial, bh, nchunk, threadIdx.x, &a, &b);
+    if (threadIdx.x == 0) {
+      sc[0] = a;
+      sc[1] = b;
+    }
+  }
   __syncthreads();
   const float s = sc[0], sv = sc[1];
   for (int e = threadIdx.x; e < BK * D; e += NT) {
@@ -230,7 +237,14 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
   const bool wave_any = wfirst < n;
   const int wlast = wave_any ? min(ntiles - 1, (wfirst + 31) / BK) : -1;  // last tile of the wave
 
-  if (tid == 0) head_scales(P.partial, bh, P.nchunk, &sScale[0], &sScale[1]);
+  if (tid < 64) {
+    float a, b;
+    head_scales(P.partial, bh, P.nchunk, tid, &a, &b);
+    if (tid == 0) {
+      sScale[0] = a;
+      sScale[1] = b;
+    }
+  }
   __syncthreads();
   const float s = sScale[0], sv = sScale[1];
   // The Q operand carries log2(e) / sqrt(d) / s, so that with the s-scaled

@@ -94,6 +94,24 @@ __device__ __forceinline__ float pair_max(float v) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Maximum over the 64 lanes, the result in every lane: DPP quad permutations
+// and row mirrors within 16-lane rows, then v_permlane16_swap and
+// v_permlane32_swap across rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_mov<0xB1>(v));   // quad_perm [1, 0, 3, 2]
+  v = fmaxf(v, dpp_mov<0x4E>(v));   // quad_perm [2, 3, 0, 1]
+  v = fmaxf(v, dpp_mov<0x141>(v));  // row_half_mirror
+  v = fmaxf(v, dpp_mov<0x140>(v));  // row_mirror
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 struct Workspace {
   float* partial;   // [BH][nchunk][2]: max row ||.||^2 of q and k; of v
   _Float16* kr;     // [BH][npad][D]      s k, d index permuted by swz16
@@ -133,14 +151,26 @@ Workspace carve(void* base, int BH, int n, int d) {
   return w;
 }
 
-// The per-head power-of-two scales, from the row-norm partial maxima.
-__device__ __forceinline__ void head_scales(const float* partial, int bh, int nchunk, float* s,
-                                            float* sv) {
-  float mqk = 0.f, mv = 0.f;
-  for (int c = 0; c < nchunk; ++c) {
-    mqk = fmaxf(mqk, partial[(static_cast<size_t>(bh) * nchunk + c) * 2 + 0]);
-    mv = fmaxf(mv, partial[(static_cast<size_t>(bh) * nchunk + c) * 2 + 1]);
+// Largest squared row norms of one head (q and k together, and v) from its
+// chunk partials. Called by every lane of one wave: each lane takes every
+// 64th chunk, then a 64-lane maximum; every lane gets the result.
+__device__ __forceinline__ void head_maxima(const float* partial, int bh, int nchunk, int lane,
+                                            float* mqk, float* mv) {
+  float a = 0.f, b = 0.f;
+  for (int c = lane; c < nchunk; c += 64) {
+    a = fmaxf(a, partial[(static_cast<size_t>(bh) * nchunk + c) * 2 + 0]);
+    b = fmaxf(b, partial[(static_cast<size_t>(bh) * nchunk + c) * 2 + 1]);
   }
+  *mqk = wave_max(a);
+  *mv = wave_max(b);
+}
+
+// Per-head power-of-two scales s (q, k) and sv (v) that bring the largest
+// row norm to at most kRowNormCap; called by every lane of one wave.
+__device__ __forceinline__ void head_scales(const float* partial, int bh, int nchunk, int lane,
+                                            float* s, float* sv) {
+  float mqk, mv;
+  head_maxima(partial, bh, nchunk, lane, &mqk, &mv);
   const float a = sqrtf(mqk), b = sqrtf(mv);
   *s = a > 0.f ? fminf(fmaxf(pow2_floor(kRowNormCap / a), 0x1p-60f), 0x1p60f) : 1.f;
   *sv = b > 0.f ? fminf(fmaxf(pow2_floor(kRowNormCap / b), 0x1p-60f), 0x1p60f) : 1.f;
