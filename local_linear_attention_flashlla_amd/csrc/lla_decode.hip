@@ -303,7 +303,7 @@ __global__ __launch_bounds__(DT) void dec_gram(DecParams P) {
   __shared__ __align__(16) T r0[GK * D], r1[GK * D], r2[GK * D], r3[GK * D];
   __shared__ __align__(16) _Float16 cHi[D * GLD], cLo[D * GLD], wHi[D * GLD], wLo[D * GLD];
   __shared__ float skb[D];
-  __shared__ float sw[2][GK];
+  __shared__ __align__(16) float sw[2][GK];
   __shared__ float smo[2], sca[64];
   auto RB = [&](auto I) __attribute__((always_inline)) -> T* {
     constexpr int i = decltype(I)::value % 4;
@@ -360,12 +360,20 @@ __global__ __launch_bounds__(DT) void dec_gram(DecParams P) {
     #pragma unroll
     for (int i = 0; i < IPT; ++i) {
       const int it = tid + DT * i, d = it % D, kg = it / D;
+      const float kbd = skb[d];
+      // every tile buffer holds GK copied rows (past the chunk: the next
+      // chunk's keys, or zeros past the cache), so every read is in bounds;
+      // keys past the chunk have weight 0, so their (finite) c meets a zero
+      // w c in every product and needs no mask
+      const float4 w0 = *reinterpret_cast<const float4*>(w + 8 * kg);
+      const float4 w1 = *reinterpret_cast<const float4*>(w + 8 * kg + 4);
+      const float we[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
       half8 ch, cl, wh, wl;
       #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int kk = 8 * kg + e;
-        const float c = c0 + t * GK + kk < c1 ? to_f(raw[kk * D + d]) - skb[d] : 0.f;
-        const float wc = w[kk] * c;
+        const float c = to_f(raw[kk * D + d]) - kbd;
+        const float wc = we[e] * c;
         ch[e] = static_cast<_Float16>(c);
         cl[e] = static_cast<_Float16>(c - static_cast<float>(ch[e]));
         wh[e] = static_cast<_Float16>(wc);
