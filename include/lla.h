@@ -53,7 +53,12 @@
  *  - Validation runs on the host before any device work; on failure nothing
  *    is enqueued or written and a negative status is returned, with detail in
  *    lla_last_error().
- *  - NaN/Inf inputs are not checked; they propagate to the affected rows.
+ *  - NaN/Inf inputs are not checked; they propagate, but never to another
+ *    head. Within a head, a NaN in q_i reaches output row i; a NaN in k_j or
+ *    v_j reaches the rows from 32*floor(j/32) on (the diagonal tile is
+ *    computed for 32 queries at once, and 0 * NaN is NaN). On the
+ *    matrix-core path an infinite input changes its head's power-of-two
+ *    scale, and with it the whole head.
  */
 #ifndef LLA_H
 #define LLA_H
