@@ -189,8 +189,10 @@ __device__ __forceinline__ void combine_moments(const DecParams& P, int bh, floa
 // --------------------------- scores and moments ----------------------------
 template <int D, typename T>
 __global__ __launch_bounds__(DT) void dec_moments(DecParams P) {
-  constexpr int EPL = D / 64;
   constexpr int KPW = GK / (DT / 64);  // keys of a tile per wave
+  constexpr int LPK = 64 / KPW;        // lanes per key
+  constexpr int DPL = D / LPK;         // dimensions of its key that a lane holds
+  static_assert(LPK == 8, "a key's score is an 8-lane butterfly");
   __shared__ __align__(16) T b0[GK * D], b1[GK * D], b2[GK * D], b3[GK * D];
   __shared__ float sm[DT / 64], som[DT / 64];
   __shared__ float smu[DT / 64][D];
@@ -204,6 +206,9 @@ __global__ __launch_bounds__(DT) void dec_moments(DecParams P) {
   const int sp = blockIdx.x, bh = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // lane = LPK * slot + part: key `slot` of the wave's KPW keys of a tile,
+  // dimensions [DPL part, DPL (part + 1)) of it
+  const int slot = lane / LPK, part = lane % LPK;
   const int c0 = sp * P.L, c1 = min(P.n, c0 + P.L);
   const int ntl = (c1 - c0 + GK - 1) / GK;
   const __amdgpu_buffer_rsrc_t kr = make_rsrc(static_cast<const T*>(P.k) + static_cast<size_t>(bh) * P.n * D,
@@ -211,51 +216,56 @@ __global__ __launch_bounds__(DT) void dec_moments(DecParams P) {
   auto toff = [&](int t) __attribute__((always_inline)) {
     return static_cast<uint32_t>((c0 + min(t, ntl - 1) * GK) * D * static_cast<int>(sizeof(T)));
   };
-  float qd[EPL];
-  load_lane<D>(static_cast<const T*>(P.q) + static_cast<size_t>(bh) * D, lane, qd);
+  float qd[DPL];
+  {
+    const T* qrow = static_cast<const T*>(P.q) + static_cast<size_t>(bh) * D + part * DPL;
+    #pragma unroll
+    for (int e = 0; e < DPL; ++e) qd[e] = to_f(qrow[e]);
+  }
   const float cs = kLog2e / sqrtf(static_cast<float>(D));
-  float m = -INFINITY, om = 0.f, mu[EPL];
+  // running max (the same in every lane), this lane's share of omega (lanes
+  // with part 0 count their key) and of mu~ (its key slot's keys, its dims)
+  float m = -INFINITY, om = 0.f, mu[DPL];
   #pragma unroll
-  for (int e = 0; e < EPL; ++e) mu[e] = 0.f;
+  for (int e = 0; e < DPL; ++e) mu[e] = 0.f;
   copy_tile<D>(kr, toff(0), b0, wave, lane);
   copy_tile<D>(kr, toff(1), b1, wave, lane);
   copy_tile<D>(kr, toff(2), b2, wave, lane);
   // step t: tile t has landed; copy tile t + 3 (clamped: every step issues the
-  // same number of copies); this wave's KPW keys of tile t
+  // same number of copies); this wave's KPW keys of tile t, one per 8 lanes
   auto step = [&](auto JM, int t) __attribute__((always_inline)) {
     wait_copies_barrier<2 * Tiles<D, T>::kPerWave>();
     copy_tile<D>(kr, toff(t + 3), BUF(IC<decltype(JM)::value + 3>{}), wave, lane);
     if (t >= ntl) return;  // block-uniform
-    const T* buf = BUF(JM);
-    float kd[KPW][EPL], part[KPW];
+    const T* row = BUF(JM) + (KPW * wave + slot) * D + part * DPL;
+    float kd[DPL];
+    float s = 0.f;
     #pragma unroll
-    for (int u = 0; u < KPW; ++u) {
-      load_lane<D>(buf + (KPW * wave + u) * D, lane, kd[u]);
-      part[u] = 0.f;
-      #pragma unroll
-      for (int e = 0; e < EPL; ++e) part[u] += qd[e] * kd[u][e];
+    for (int e = 0; e < DPL; ++e) {
+      kd[e] = to_f(row[e]);
+      s += qd[e] * kd[e];
     }
-    #pragma unroll
-    for (int u = 0; u < KPW; ++u) part[u] = wave_sum(part[u]);
-    const int jb = c0 + t * GK + KPW * wave;
-    #pragma unroll
-    for (int u = 0; u < KPW; ++u) {
-      const int j = jb + u;
-      if (j >= c1) break;  // wave-uniform
-      const float sj = part[u] * cs;  // the same in every lane
-      if (lane == u) P.s[static_cast<size_t>(bh) * P.n + j] = sj;
-      if (sj > m) {  // wave-uniform; exp2(-inf) = 0 on the first key
-        const float a = exp2f(m - sj);
-        om *= a;
-        #pragma unroll
-        for (int e = 0; e < EPL; ++e) mu[e] *= a;
-        m = sj;
-      }
-      const float w = exp2f(sj - m);
-      om += w;
+    // the key's 8 lanes: a butterfly of commutative adds, so all 8 hold the
+    // same sum
+    s += dpp_partner<0xB1>(s);   // quad_perm [1, 0, 3, 2]
+    s += dpp_partner<0x4E>(s);   // quad_perm [2, 3, 0, 1]
+    s += dpp_partner<0x141>(s);  // row_half_mirror
+    const int j = c0 + t * GK + KPW * wave + slot;
+    const bool in = j < c1;
+    const float sj = in ? s * cs : -INFINITY;
+    if (in && part == 0) P.s[static_cast<size_t>(bh) * P.n + j] = sj;
+    const float tmax = wave_max(sj);
+    if (tmax > m) {  // wave-uniform; exp2(-inf) = 0 on the first keys
+      const float a = exp2f(m - tmax);
+      om *= a;
       #pragma unroll
-      for (int e = 0; e < EPL; ++e) mu[e] += w * kd[u][e];
+      for (int e = 0; e < DPL; ++e) mu[e] *= a;
+      m = tmax;
     }
+    const float w = in ? exp2f(sj - m) : 0.f;  // (m is -inf while no key has been seen)
+    if (part == 0) om += w;
+    #pragma unroll
+    for (int e = 0; e < DPL; ++e) mu[e] += w * kd[e];
   };
   for (int t0 = 0; t0 < ntl; t0 += 4) {
     step(IC<0>{}, t0);
@@ -263,12 +273,23 @@ __global__ __launch_bounds__(DT) void dec_moments(DecParams P) {
     step(IC<2>{}, t0 + 2);
     step(IC<3>{}, t0 + 3);
   }
+  // the wave's totals: omega over all lanes, mu~ over the KPW key slots
+  // (lanes part, part + 8, ..., part + 56)
+  om = wave_sum(om);
+  #pragma unroll
+  for (int e = 0; e < DPL; ++e) {
+    mu[e] += __shfl_xor(mu[e], 8);
+    mu[e] += __shfl_xor(mu[e], 16);
+    mu[e] += __shfl_xor(mu[e], 32);
+  }
   if (lane == 0) {
     sm[wave] = m;
     som[wave] = om;
   }
-  #pragma unroll
-  for (int e = 0; e < EPL; ++e) smu[wave][lane * EPL + e] = mu[e];
+  if (slot == 0) {
+    #pragma unroll
+    for (int e = 0; e < DPL; ++e) smu[wave][part * DPL + e] = mu[e];
+  }
   __syncthreads();  // (also: no tile copy is still in flight past this point)
   const int t = threadIdx.x;
   if (t < D) {
