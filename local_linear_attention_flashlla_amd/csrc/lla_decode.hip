@@ -558,7 +558,6 @@ __global__ __launch_bounds__(DT) void dec_solve(DecParams P) {
 // ---------------------------------- output ---------------------------------
 template <int D, typename T>
 __global__ __launch_bounds__(DT) void dec_output(DecParams P) {
-  constexpr int EPL = D / 64;
   constexpr int KPW = GK / (DT / 64);
   __shared__ __align__(16) T k0[GK * D], k1[GK * D], k2[GK * D], k3[GK * D];
   __shared__ __align__(16) T v0[GK * D], v1[GK * D], v2[GK * D], v3[GK * D];
@@ -591,28 +590,35 @@ __global__ __launch_bounds__(DT) void dec_output(DecParams P) {
   auto toff = [&](int t) __attribute__((always_inline)) {
     return static_cast<uint32_t>((c0 + min(t, ntl - 1) * GK) * D * static_cast<int>(sizeof(T)));
   };
+  // lane = LPK * slot + part: key `slot` of the wave's KPW keys of a tile,
+  // dimensions [DPL part, DPL (part + 1)) of it
+  constexpr int LPK = 64 / KPW, DPL = D / LPK;
+  static_assert(LPK == 8, "a key's dot product is an 8-lane butterfly");
+  const int slot = lane / LPK, part = lane % LPK;
   const float* st = P.st + static_cast<size_t>(bh) * (2 * D + 2);
-  float xr[EPL], kr_dot = 0.f;
+  float xr[DPL], kr_dot = 0.f;
   #pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    xr[e] = st[lane * EPL + e];
-    kr_dot += st[D + lane * EPL + e] * xr[e];
+  for (int e = 0; e < DPL; ++e) {
+    xr[e] = st[part * DPL + e];
+    kr_dot += st[D + part * DPL + e] * xr[e];
   }
-  kr_dot = wave_sum(kr_dot);
+  // kbar . rho_c over the 8 parts (every key slot holds the same copy)
+  kr_dot += dpp_partner<0xB1>(kr_dot);
+  kr_dot += dpp_partner<0x4E>(kr_dot);
+  kr_dot += dpp_partner<0x141>(kr_dot);
   const float m = st[2 * D];
   const float* S = P.s + static_cast<size_t>(bh) * P.n;
-  float o[EPL], den = 0.f;
+  float o[DPL], den = 0.f;
   #pragma unroll
-  for (int e = 0; e < EPL; ++e) o[e] = 0.f;
-  // scores of this wave's keys, loaded two steps ahead into a ring of four
-  float sreg[4][KPW];
-  auto load_s = [&](int t, float (&dst)[KPW]) __attribute__((always_inline)) {
-    const int jb = c0 + t * GK + KPW * wave;
-    #pragma unroll
-    for (int u = 0; u < KPW; ++u) dst[u] = jb + u < c1 ? S[jb + u] : -INFINITY;  // past the chunk: weight 0
+  for (int e = 0; e < DPL; ++e) o[e] = 0.f;
+  // the score of this lane's key, loaded two steps ahead into a ring of four
+  float sreg[4];
+  auto load_s = [&](int t) __attribute__((always_inline)) {
+    const int j = c0 + t * GK + KPW * wave + slot;
+    return j < c1 ? S[j] : -INFINITY;  // past the chunk: weight 0
   };
-  load_s(0, sreg[0]);
-  load_s(1, sreg[1]);
+  sreg[0] = load_s(0);
+  sreg[1] = load_s(1);
   copy_tile<D>(kr, toff(0), k0, wave, lane);
   copy_tile<D>(vr, toff(0), v0, wave, lane);
   copy_tile<D>(kr, toff(1), k1, wave, lane);
@@ -625,29 +631,23 @@ __global__ __launch_bounds__(DT) void dec_output(DecParams P) {
     copy_tile<D>(vr, toff(t + 3), VB(IC<decltype(JM)::value + 3>{}), wave, lane);
     if (t >= ntl) return;  // block-uniform
     constexpr int jm = decltype(JM)::value;
-    load_s(t + 2, sreg[(jm + 2) % 4]);
-    const T* kb = KB(JM);
-    const T* vb = VB(JM);
-    float vd[KPW][EPL], part[KPW];
-    const float (&sv)[KPW] = sreg[jm];
+    sreg[(jm + 2) % 4] = load_s(t + 2);
+    const int ro = (KPW * wave + slot) * D + part * DPL;
+    const T* kb = KB(JM) + ro;
+    const T* vb = VB(JM) + ro;
+    float vd[DPL], dot = 0.f;
     #pragma unroll
-    for (int u = 0; u < KPW; ++u) {
-      float kd[EPL];
-      load_lane<D>(kb + (KPW * wave + u) * D, lane, kd);
-      load_lane<D>(vb + (KPW * wave + u) * D, lane, vd[u]);
-      part[u] = 0.f;
-      #pragma unroll
-      for (int e = 0; e < EPL; ++e) part[u] += kd[e] * xr[e];
+    for (int e = 0; e < DPL; ++e) {
+      dot += to_f(kb[e]) * xr[e];
+      vd[e] = to_f(vb[e]);
     }
+    dot += dpp_partner<0xB1>(dot);   // quad_perm [1, 0, 3, 2]
+    dot += dpp_partner<0x4E>(dot);   // quad_perm [2, 3, 0, 1]
+    dot += dpp_partner<0x141>(dot);  // row_half_mirror
+    const float a = exp2f(sreg[jm] - m) * (1.f - (dot - kr_dot));
+    if (part == 0) den += a;
     #pragma unroll
-    for (int u = 0; u < KPW; ++u) part[u] = wave_sum(part[u]);
-    #pragma unroll
-    for (int u = 0; u < KPW; ++u) {
-      const float a = exp2f(sv[u] - m) * (1.f - (part[u] - kr_dot));
-      den += a;
-      #pragma unroll
-      for (int e = 0; e < EPL; ++e) o[e] += a * vd[u][e];
-    }
+    for (int e = 0; e < DPL; ++e) o[e] += a * vd[e];
   };
   for (int t0 = 0; t0 < ntl; t0 += 4) {
     step(IC<0>{}, t0);
@@ -655,9 +655,19 @@ __global__ __launch_bounds__(DT) void dec_output(DecParams P) {
     step(IC<2>{}, t0 + 2);
     step(IC<3>{}, t0 + 3);
   }
-  if (lane == 0) sden[wave] = den;
+  // the wave's totals: den over all lanes, o over the KPW key slots
+  den = wave_sum(den);
   #pragma unroll
-  for (int e = 0; e < EPL; ++e) so[wave][lane * EPL + e] = o[e];
+  for (int e = 0; e < DPL; ++e) {
+    o[e] += __shfl_xor(o[e], 8);
+    o[e] += __shfl_xor(o[e], 16);
+    o[e] += __shfl_xor(o[e], 32);
+  }
+  if (lane == 0) sden[wave] = den;
+  if (slot == 0) {
+    #pragma unroll
+    for (int e = 0; e < DPL; ++e) so[wave][part * DPL + e] = o[e];
+  }
   __syncthreads();  // (also: no tile copy is still in flight past this point)
   const int t = threadIdx.x;
   if (t <= D) {
