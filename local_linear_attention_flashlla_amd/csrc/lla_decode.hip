@@ -20,9 +20,10 @@
 //   dec_moments  (S x BH)  scores c q.k_j (kept, log2 units), chunk max, omega
 //                          and mu~ partials;
 //   dec_gram     (SG x BH) combines the partials into m, omega, kbar; the chunk's
-//                          contribution to G on v_mfma_f32_32x32x16_f16, each
-//                          operand carried as two fp16 terms (hi + lo, ~22
-//                          bits): hi.hi + hi.lo + lo.hi;
+//                          contribution to G = sum_j u_j u_j^T with
+//                          u_j = sqrt(w_j) (k_j - kbar), on
+//                          v_mfma_f32_32x32x16_f16, u carried as two fp16
+//                          terms (hi + lo, ~22 bits): hi.hi + hi.lo + lo.hi;
 //   dec_solve    (BH)      sums the chunk Grams, adds lambda I, runs CG on
 //                          G rho_c = mu = omega (kbar - q);
 //   dec_output   (S x BH)  a_j = w_j (1 - (k_j - kbar).rho_c): partial sums of
@@ -322,7 +323,7 @@ __global__ __launch_bounds__(DT) void dec_gram(DecParams P) {
   constexpr int IPT = D * (GK / 8) / DT;    // staging items (one d, 8 keys) per thread
   static_assert(IPT * DT == D * (GK / 8), "items must spread evenly");
   __shared__ __align__(16) T r0[GK * D], r1[GK * D], r2[GK * D], r3[GK * D];
-  __shared__ __align__(16) _Float16 cHi[D * GLD], cLo[D * GLD], wHi[D * GLD], wLo[D * GLD];
+  __shared__ __align__(16) _Float16 uHi[D * GLD], uLo[D * GLD];
   __shared__ float skb[D];
   __shared__ __align__(16) float sw[2][GK];
   __shared__ float smo[2], sca[64];
@@ -360,7 +361,9 @@ __global__ __launch_bounds__(DT) void dec_gram(DecParams P) {
   sR[0] = load_s(0);
   sR[1] = load_s(1);
   sR[2] = load_s(2);
-  if (tid < GK) sw[0][tid] = exp2f(sR[0] - m);  // keys past the chunk: weight 0
+  // sw holds sqrt(w) = 2^((s - m) / 2): the chunk Gram is sum_j u_j u_j^T with
+  // u_j = sqrt(w_j) (k_j - kbar); keys past the chunk: 0
+  if (tid < GK) sw[0][tid] = exp2f(0.5f * (sR[0] - m));
   floatx16 acc[TPW];
   #pragma unroll
   for (int u = 0; u < TPW; ++u)
@@ -372,10 +375,10 @@ __global__ __launch_bounds__(DT) void dec_gram(DecParams P) {
     wait_copies_barrier<2 * Tiles<D, T>::kPerWave>();
     copy_tile<D>(kr, toff(t + 3), RB(IC<jm + 3>{}), wave, lane);
     if (t >= ntl) return;  // block-uniform
-    if (tid < GK) sw[(jm + 1) & 1][tid] = exp2f(sR[(jm + 1) % 4] - m);
+    if (tid < GK) sw[(jm + 1) & 1][tid] = exp2f(0.5f * (sR[(jm + 1) % 4] - m));
     sR[(jm + 3) % 4] = load_s(t + 3);
-    // transposed operands: row d holds the tile's keys of c = k - kbar and of
-    // w c, each as fp16 hi + lo
+    // transposed operand: row d holds the tile's keys of u = sqrt(w) (k - kbar)
+    // as fp16 hi + lo
     const T* raw = RB(JM);
     const float* w = sw[jm & 1];
     #pragma unroll
@@ -384,26 +387,21 @@ __global__ __launch_bounds__(DT) void dec_gram(DecParams P) {
       const float kbd = skb[d];
       // every tile buffer holds GK copied rows (past the chunk: the next
       // chunk's keys, or zeros past the cache), so every read is in bounds;
-      // keys past the chunk have weight 0, so their (finite) c meets a zero
-      // w c in every product and needs no mask
+      // keys past the chunk have sqrt(w) = 0, so their (finite) k - kbar
+      // gives u = 0 and needs no mask
       const float4 w0 = *reinterpret_cast<const float4*>(w + 8 * kg);
       const float4 w1 = *reinterpret_cast<const float4*>(w + 8 * kg + 4);
       const float we[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-      half8 ch, cl, wh, wl;
+      half8 uh, ul;
       #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int kk = 8 * kg + e;
-        const float c = to_f(raw[kk * D + d]) - kbd;
-        const float wc = we[e] * c;
-        ch[e] = static_cast<_Float16>(c);
-        cl[e] = static_cast<_Float16>(c - static_cast<float>(ch[e]));
-        wh[e] = static_cast<_Float16>(wc);
-        wl[e] = static_cast<_Float16>(wc - static_cast<float>(wh[e]));
+        const float u = we[e] * (to_f(raw[kk * D + d]) - kbd);
+        uh[e] = static_cast<_Float16>(u);
+        ul[e] = static_cast<_Float16>(u - static_cast<float>(uh[e]));
       }
-      *reinterpret_cast<half8*>(cHi + d * GLD + 8 * kg) = ch;
-      *reinterpret_cast<half8*>(cLo + d * GLD + 8 * kg) = cl;
-      *reinterpret_cast<half8*>(wHi + d * GLD + 8 * kg) = wh;
-      *reinterpret_cast<half8*>(wLo + d * GLD + 8 * kg) = wl;
+      *reinterpret_cast<half8*>(uHi + d * GLD + 8 * kg) = uh;
+      *reinterpret_cast<half8*>(uLo + d * GLD + 8 * kg) = ul;
     }
     __syncthreads();
     #pragma unroll
@@ -413,10 +411,10 @@ __global__ __launch_bounds__(DT) void dec_gram(DecParams P) {
         const int ti = wave + (DT / 64) * u, I = ti / NB, J = ti % NB;
         const int ao = (32 * I + ql) * GLD + 16 * ks + 8 * g;
         const int bo = (32 * J + ql) * GLD + 16 * ks + 8 * g;
-        const half8 ah = *reinterpret_cast<const half8*>(cHi + ao);
-        const half8 al = *reinterpret_cast<const half8*>(cLo + ao);
-        const half8 bhv = *reinterpret_cast<const half8*>(wHi + bo);
-        const half8 blv = *reinterpret_cast<const half8*>(wLo + bo);
+        const half8 ah = *reinterpret_cast<const half8*>(uHi + ao);
+        const half8 al = *reinterpret_cast<const half8*>(uLo + ao);
+        const half8 bhv = *reinterpret_cast<const half8*>(uHi + bo);
+        const half8 blv = *reinterpret_cast<const half8*>(uLo + bo);
         acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bhv, acc[u], 0, 0, 0);
         acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, blv, acc[u], 0, 0, 0);
         acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bhv, acc[u], 0, 0, 0);
