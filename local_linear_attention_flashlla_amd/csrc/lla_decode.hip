@@ -317,9 +317,20 @@ __global__ __launch_bounds__(DT) void dec_moments(DecParams P) {
 // ------------------------------ chunk Gram ---------------------------------
 template <int D, typename T>
 __global__ __launch_bounds__(DT) void dec_gram(DecParams P) {
-  constexpr int NB = D / 32;                // 32-row blocks of G
-  constexpr int TPW = NB * NB / (DT / 64);  // output tiles per wave
-  static_assert(TPW >= 1 && NB * NB % (DT / 64) == 0, "tiles must spread over the waves");
+  constexpr int NB = D / 32;                     // 32-row blocks of G
+  constexpr int NT = NB * (NB + 1) / 2;          // blocks on or above the diagonal (G is symmetric)
+  constexpr int TPW = (NT + DT / 64 - 1) / (DT / 64);  // output tiles per wave (the last may be empty)
+  // upper-triangle tile t -> block row I and column J >= I
+  auto tile_of = [](int t, int& I, int& J) __attribute__((always_inline)) {
+    I = 0;
+    #pragma unroll
+    for (int r = 0; r < NB; ++r)
+      if (t >= NB - I) {
+        t -= NB - I;
+        ++I;
+      }
+    J = I + t;
+  };
   constexpr int IPT = D * (GK / 8) / DT;    // staging items (one d, 8 keys) per thread
   static_assert(IPT * DT == D * (GK / 8), "items must spread evenly");
   __shared__ __align__(16) T r0[GK * D], r1[GK * D], r2[GK * D], r3[GK * D];
@@ -408,7 +419,10 @@ __global__ __launch_bounds__(DT) void dec_gram(DecParams P) {
     for (int ks = 0; ks < GK / 16; ++ks)
       #pragma unroll
       for (int u = 0; u < TPW; ++u) {
-        const int ti = wave + (DT / 64) * u, I = ti / NB, J = ti % NB;
+        const int ti = wave + (DT / 64) * u;
+        if (ti >= NT) continue;  // wave-uniform
+        int I, J;
+        tile_of(ti, I, J);
         const int ao = (32 * I + ql) * GLD + 16 * ks + 8 * g;
         const int bo = (32 * J + ql) * GLD + 16 * ks + 8 * g;
         const half8 ah = *reinterpret_cast<const half8*>(uHi + ao);
@@ -432,11 +446,15 @@ __global__ __launch_bounds__(DT) void dec_gram(DecParams P) {
   float* G = P.gram + (static_cast<size_t>(bh) * P.SG + sp) * D * D;
   #pragma unroll
   for (int u = 0; u < TPW; ++u) {
-    const int ti = wave + (DT / 64) * u, I = ti / NB, J = ti % NB;
+    const int ti = wave + (DT / 64) * u;
+    if (ti >= NT) continue;  // wave-uniform
+    int I, J;
+    tile_of(ti, I, J);
     #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int i = 32 * I + 8 * (r >> 2) + 4 * g + (r & 3);
       G[i * D + 32 * J + ql] = acc[u][r];
+      if (I != J) G[(32 * J + ql) * D + i] = acc[u][r];  // the mirror block
     }
   }
 }
