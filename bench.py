@@ -253,7 +253,10 @@ def bench_decode(args, torch, lla, dev):
     gram_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     esz = 2 if wl.dtype == "bf16" else 4
     cache = B * H * n * d * esz
-    gram_flops = 2.0 * B * H * n * d * d
+    # G = sum_j u_j u_j^T is symmetric: its d (d + 1) / 2 distinct entries
+    # take d (d + 1) FLOPs per key (a multiply and an add each), n d (d + 1)
+    # per head; the kernel forms only the blocks on or above the diagonal
+    gram_flops = 1.0 * B * H * n * d * (d + 1)
     rec = {
         "metric": "LLA decode queries/s (one new query per head), 1 MI355X",
         "value": B * H / (ms * 1e-3), "unit": "queries/s", "n_gpus": 1, "steps": steps,
