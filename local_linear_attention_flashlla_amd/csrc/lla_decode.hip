@@ -492,7 +492,24 @@ __global__ __launch_bounds__(DT) void dec_solve(DecParams P) {
   float4 ga[NG];
   #pragma unroll
   for (int u = 0; u < NG; ++u) ga[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int c = 0; c < P.SG; ++c) {
+  // two chunks per round trip (2 NG loads in flight), added in chunk order
+  int c = 0;
+  for (; c + 1 < P.SG; c += 2) {
+    const float4* g0 = Gc + static_cast<size_t>(c) * (D * D / 4);
+    const float4* g1 = g0 + D * D / 4;
+    float4 a0[NG], a1[NG];
+    #pragma unroll
+    for (int u = 0; u < NG; ++u) {
+      a0[u] = g0[t + DT * u];
+      a1[u] = g1[t + DT * u];
+    }
+    #pragma unroll
+    for (int u = 0; u < NG; ++u) {
+      ga[u].x += a0[u].x; ga[u].y += a0[u].y; ga[u].z += a0[u].z; ga[u].w += a0[u].w;
+      ga[u].x += a1[u].x; ga[u].y += a1[u].y; ga[u].z += a1[u].z; ga[u].w += a1[u].w;
+    }
+  }
+  if (c < P.SG) {
     const float4* gc = Gc + static_cast<size_t>(c) * (D * D / 4);
     #pragma unroll
     for (int u = 0; u < NG; ++u) {
