@@ -71,6 +71,23 @@ def measured_traffic(path: str):
     return value if found_sha == sha else None
 
 
+def calibration_kernels(torch, dev, mib: int):
+    """Kernels whose HBM traffic is known, run once each (after the timed
+    region) so that byte counters taken in the same run can be scaled: a fill
+    of N MiB (writes N), dst = src + 1 (reads N, writes N), a sum (reads N)."""
+    n = (mib << 20) // 4
+    src = torch.empty(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    src.fill_(1.0)
+    torch.cuda.synchronize()
+    torch.add(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    src.sum()
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def _oracle_sample_job(args):
     q, k, v, lam, rows = args
     from threadpoolctl import threadpool_limits
@@ -391,9 +408,11 @@ def main(argv=None):
     ap.add_argument("--traffic", default=None,
                     help="byte-counter summary to read the main kernel's HBM bytes per launch "
                          "from (default: the one under profiles/ for this workload)")
-    ap.add_argument("--calib-copy-mb", type=int, default=0,
-                    help="after timing, run one plain device copy of this many MiB (a "
-                         "reference kernel of known traffic for hardware byte counters)")
+    ap.add_argument("--calib-mb", type=int, default=0,
+                    help="after timing, run three kernels of known traffic on buffers of this "
+                         "many MiB, references for the hardware byte counters: a fill (writes "
+                         "N MiB), an elementwise copy dst = src + 1 (reads N, writes N) and a "
+                         "sum (reads N)")
     ap.add_argument("--given-rho", action="store_true",
                     help="time lla_output_given_rho (moment and output scans, the CG solve "
                          "replaced by a supplied rho) instead of the full forward")
@@ -422,6 +441,10 @@ def main(argv=None):
     if not os.path.exists(lla._lib.LIB_PATH):
         from local_linear_attention_flashlla_amd import build as _b
         _b.build()
+    if not lla._lib.is_current():
+        print(f"bench.py: {lla._lib.LIB_PATH} was built from other sources than this tree's; "
+              "rebuild it (python -m local_linear_attention_flashlla_amd.build)", file=sys.stderr)
+        return 3
     assert torch.cuda.is_available(), "bench.py needs a HIP device"
     dev = torch.device("cuda:0")
     if args.memory_curve:
@@ -494,14 +517,8 @@ def main(argv=None):
         ROOT, "profiles", f"lla_cg_kernel_{wl.name}_hbm_bytes.txt")) \
         if kernel_used == lla.LLA_KERNEL_MFMA and not args.split_u else None
 
-    if args.calib_copy_mb > 0:
-        nbytes = args.calib_copy_mb << 20
-        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    if args.calib_mb > 0:
+        calibration_kernels(torch, dev, args.calib_mb)
 
     cpu = None
     if args.cpu_rows > 0:

@@ -85,10 +85,12 @@ enum {
   LLA_ERR_UNSUPPORTED = -2, /* d not in {16, 32, 64, 128}; a kernel choice
                                not available for the dtype/d; sizes too
                                large: B*H >= 2^31, B*H*n > 2^40, n > 2^23
-                               (forward, output given rho) or n > 2^21
+                               (forward, output given rho), n > 2^21 with
+                               LLA_KERNEL_MFMA (forward) or on any path
                                (backward); decode: B*H > 65535, B*H*n > 2^36
                                or one head's cache (n*d elements) of 2 GiB
-                               or more */
+                               or more. Checked on the host before anything
+                               is allocated or enqueued */
   LLA_ERR_HIP = -3,         /* a HIP launch or allocation failed */
   LLA_ERR_WORKSPACE = -4    /* caller workspace smaller than required */
 };
@@ -98,10 +100,12 @@ enum { LLA_DTYPE_F32 = 0, LLA_DTYPE_BF16 = 1 };
 
 /* Kernel selection for lla_forward_ex. */
 enum {
-  LLA_KERNEL_AUTO = 0, /* fp32 inputs: VALU; bf16 inputs with d in {64,128}:
-                          MFMA; otherwise VALU */
-  LLA_KERNEL_VALU = 1, /* fp32 vector-ALU kernel, any supported d/dtype */
-  LLA_KERNEL_MFMA = 2  /* fp16 matrix-core kernel; bf16 inputs, d in {64,128} */
+  LLA_KERNEL_AUTO = 0, /* bf16 inputs with d in {64,128} and n <= 2^21: MFMA;
+                          otherwise (fp32 inputs, other d, longer n) VALU */
+  LLA_KERNEL_VALU = 1, /* fp32 vector-ALU kernel, any supported d/dtype,
+                          n <= 2^23 */
+  LLA_KERNEL_MFMA = 2  /* fp16 matrix-core kernel; bf16 inputs, d in {64,128},
+                          n <= 2^21 (LLA_ERR_UNSUPPORTED otherwise) */
 };
 
 /* Flags for lla_forward_ex (bitwise OR). */
@@ -184,8 +188,10 @@ int lla_forward_ex(const lla_fwd_args* args, hipStream_t stream);
 int lla_output_given_rho(const lla_fwd_args* args, const float* rho_in, hipStream_t stream);
 
 /* Device workspace bytes lla_forward_ex (or lla_output_given_rho) needs for
-   these sizes and this kernel choice (0 if none). Returns 0 for invalid sizes
-   too. */
+   these sizes and this kernel choice (LLA_KERNEL_*; the matrix-core path needs
+   a workspace linear in B*H*n, the vector path none, and AUTO resolves as in
+   the call). Returns 0 where no workspace is needed, and for sizes or a kernel
+   choice the call would reject (e.g. n > 2^21 with LLA_KERNEL_MFMA). */
 size_t lla_workspace_bytes(int B, int H, int n, int d, int dtype, int kernel);
 
 /* ------------------------------------------------------------------------
@@ -302,6 +308,12 @@ const char* lla_last_error(void);
 
 /* LLA_VERSION of the loaded library. */
 int lla_version(void);
+
+/* Lower-case hex SHA-256 of the source files and compiler flags the library
+   was built from, as the package's build script computes it ("unknown" for a
+   build without it), so a caller can tell a library that no longer matches
+   its sources. Static string. */
+const char* lla_source_hash(void);
 
 #ifdef __cplusplus
 }

@@ -33,6 +33,7 @@ EXPORTED_SYMBOLS = (
     "lla_forward_f32", "lla_forward_bf16", "lla_forward_ex", "lla_output_given_rho",
     "lla_workspace_bytes", "lla_decode_ex", "lla_decode_workspace_bytes",
     "lla_backward_ex", "lla_backward_workspace_bytes", "lla_status_string", "lla_last_error", "lla_version",
+    "lla_source_hash",
 )
 
 
@@ -169,9 +170,19 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.lla_last_error.restype = ctypes.c_char_p
     lib.lla_version.argtypes = []
     lib.lla_version.restype = ci
+    lib.lla_source_hash.argtypes = []
+    lib.lla_source_hash.restype = ctypes.c_char_p
     if path is None:
         _lib = lib
     return lib
+
+
+def is_current(lib: Optional[ctypes.CDLL] = None) -> bool:
+    """Whether the loaded library was built from the sources in this tree
+    (its lla_source_hash() equals the build script's hash of them)."""
+    from .build import source_hash
+    lib = lib or load()
+    return lib.lla_source_hash().decode() == source_hash()
 
 
 def status_string(status: int) -> str:

@@ -5,6 +5,7 @@ Run as ``python -m local_linear_attention_flashlla_amd.build`` or call
 """
 from __future__ import annotations
 
+import hashlib
 import os
 import shutil
 import subprocess
@@ -19,6 +20,9 @@ LIB_PATH = os.path.join(HERE, LIB_NAME)
 ARCH = os.environ.get("LLA_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["lla_api.hip", "lla_valu.hip", "lla_mfma.hip", "lla_decode.hip", "lla_bwd.hip"]
+# headers the sources include (part of the source hash)
+HEADERS = [os.path.join(CSRC, "lla_internal.h"), os.path.join(CSRC, "lla_mfma_common.h"),
+           os.path.join(ROOT, "include", "lla.h")]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -40,19 +44,41 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build liblla.so)")
 
 
+def source_hash() -> str:
+    """SHA-256 over the library's sources, headers and compiler flags: the
+    value the built library reports through lla_source_hash()."""
+    h = hashlib.sha256()
+    for path in [os.path.join(CSRC, s) for s in SOURCES] + HEADERS:
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode() + b"\0" + f.read() + b"\0")
+    h.update(" ".join(HIPCC_FLAGS).encode())
+    return h.hexdigest()
+
+
 def build(verbose: bool = False) -> str:
+    """Compile every source to an object in parallel, then link liblla.so."""
+    from concurrent.futures import ThreadPoolExecutor
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    fd, tmp = tempfile.mkstemp(prefix="liblla.", suffix=".so.tmp", dir=HERE)
-    os.close(fd)
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *srcs, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    try:
-        subprocess.run(cmd, check=True)
+    define = f"-DLLA_SOURCE_SHA256=\"{source_hash()}\""
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    with tempfile.TemporaryDirectory(prefix="lla_build.", dir=HERE) as tmpdir:
+        objs = [os.path.join(tmpdir, os.path.basename(s) + ".o") for s in srcs]
+        cmds = [[hipcc(), *compile_flags, define, "-I", os.path.join(ROOT, "include"), "-c", s, "-o", o]
+                for s, o in zip(srcs, objs)]
+        if verbose:
+            for c in cmds:
+                print(" ".join(c), flush=True)
+        with ThreadPoolExecutor(max_workers=min(len(cmds), max(1, os.cpu_count() or 1))) as ex:
+            for r in ex.map(lambda c: subprocess.run(c, capture_output=True, text=True), cmds):
+                if r.returncode != 0:
+                    sys.stderr.write(r.stderr)
+                    raise subprocess.CalledProcessError(r.returncode, r.args)
+        tmp = os.path.join(tmpdir, LIB_NAME)
+        link = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+        if verbose:
+            print(" ".join(link), flush=True)
+        subprocess.run(link, check=True)
         os.replace(tmp, LIB_PATH)
-    finally:
-        if os.path.exists(tmp):
-            os.unlink(tmp)
     return LIB_PATH
 
 

@@ -37,13 +37,19 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 
 bool d_supported(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
-// Longest sequence the forward takes (see validate)
+// Longest sequence the forward takes on the vector path (see validate). The
+// matrix-core path takes n <= lla::kMfmaMaxN (its key-tile offsets are 32-bit
+// byte counts formed in int arithmetic).
 constexpr int kMaxForwardN = 1 << 23;
 
-// Resolve LLA_KERNEL_AUTO and check the choice. Returns LLA_OK or a status.
-int resolve_kernel(int dtype, int d, int requested, int* chosen) {
+// Resolve LLA_KERNEL_AUTO and check the choice for this sequence length.
+// AUTO takes the matrix cores whenever they support the call (bf16, d in
+// {64, 128}, n within their limit), the vector path otherwise. Returns LLA_OK
+// or a status; nothing has been enqueued or allocated at this point.
+int resolve_kernel(int dtype, int d, int n, int requested, int* chosen) {
+  const bool mfma_ok = lla::mfma_supported(dtype, d) && n <= lla::kMfmaMaxN;
   if (requested == LLA_KERNEL_AUTO) {
-    *chosen = lla::mfma_supported(dtype, d) ? LLA_KERNEL_MFMA : LLA_KERNEL_VALU;
+    *chosen = mfma_ok ? LLA_KERNEL_MFMA : LLA_KERNEL_VALU;
     return LLA_OK;
   }
   if (requested == LLA_KERNEL_VALU) {
@@ -54,6 +60,8 @@ int resolve_kernel(int dtype, int d, int requested, int* chosen) {
     if (!lla::mfma_supported(dtype, d))
       return fail(LLA_ERR_UNSUPPORTED, "MFMA kernel needs bf16 inputs and d in {64,128} (dtype=%d d=%d)",
                   dtype, d);
+    if (n > lla::kMfmaMaxN)
+      return fail(LLA_ERR_UNSUPPORTED, "MFMA kernel takes n <= 2^21 (n=%d)", n);
     *chosen = LLA_KERNEL_MFMA;
     return LLA_OK;
   }
@@ -134,6 +142,12 @@ const char* lla_last_error(void) { return g_last_error; }
 
 int lla_version(void) { return LLA_VERSION; }
 
+// The build script passes the hash of the sources and flags it compiled.
+#ifndef LLA_SOURCE_SHA256
+#define LLA_SOURCE_SHA256 "unknown"
+#endif
+const char* lla_source_hash(void) { return LLA_SOURCE_SHA256; }
+
 size_t lla_workspace_bytes(int B, int H, int n, int d, int dtype, int kernel) {
   if (B < 1 || H < 1 || n < 1 || n > kMaxForwardN || !d_supported(d)) return 0;
   if (dtype != LLA_DTYPE_F32 && dtype != LLA_DTYPE_BF16) return 0;
@@ -142,7 +156,7 @@ size_t lla_workspace_bytes(int B, int H, int n, int d, int dtype, int kernel) {
   int chosen = 0;
   char saved[sizeof(g_last_error)];
   memcpy(saved, g_last_error, sizeof(saved));
-  const int st = resolve_kernel(dtype, d, kernel, &chosen);
+  const int st = resolve_kernel(dtype, d, n, kernel, &chosen);
   memcpy(g_last_error, saved, sizeof(saved));
   if (st != LLA_OK) return 0;
   if (chosen == LLA_KERNEL_MFMA) return lla::mfma_workspace_bytes(static_cast<int>(bh), n, d);
@@ -153,7 +167,7 @@ static int forward_impl(const lla_fwd_args* a, const float* rho_in, hipStream_t 
   int st = validate(a);
   if (st != LLA_OK) return st;
   int kernel = 0;
-  st = resolve_kernel(a->dtype, a->d, a->kernel, &kernel);
+  st = resolve_kernel(a->dtype, a->d, a->n, a->kernel, &kernel);
   if (st != LLA_OK) return st;
   lla::FwdParams p{};
   p.q = a->q; p.k = a->k; p.v = a->v; p.out = a->out;
@@ -320,7 +334,7 @@ int lla_backward_ex(const lla_bwd_args* a, hipStream_t stream) {
   if (!d_supported(a->d)) return fail(LLA_ERR_UNSUPPORTED, "d=%d not in {16,32,64,128}", a->d);
   int kernel = 0;
   {
-    const int st = resolve_kernel(a->dtype, a->d, a->kernel, &kernel);
+    const int st = resolve_kernel(a->dtype, a->d, a->n, a->kernel, &kernel);
     if (st != LLA_OK) return st;
   }
   if (!std::isfinite(a->lambda) || !(a->lambda > 0.f))
@@ -331,7 +345,7 @@ int lla_backward_ex(const lla_bwd_args* a, hipStream_t stream) {
     return fail(LLA_ERR_INVALID_ARG, "cg_rel_tol must be finite and >= 0 (got %g)", (double)a->cg_rel_tol);
   const unsigned long long bh = (unsigned long long)a->B * (unsigned long long)a->H;
   if (bh > 0x7fffffffULL) return fail(LLA_ERR_UNSUPPORTED, "B*H too large");
-  if (a->n > (1 << 21)) return fail(LLA_ERR_UNSUPPORTED, "backward: n=%d > 2^21", a->n);
+  if (a->n > lla::kMfmaMaxN) return fail(LLA_ERR_UNSUPPORTED, "backward: n=%d > 2^21", a->n);
   const unsigned long long rows = bh * (unsigned long long)a->n;
   if (rows > (1ULL << 40) || bh * (unsigned long long)((a->n + 127) / 128) > 0x7fffffffULL)
     return fail(LLA_ERR_UNSUPPORTED, "B*H*n too large");
@@ -398,7 +412,7 @@ int lla_backward_ex(const lla_bwd_args* a, hipStream_t stream) {
 }
 
 size_t lla_backward_workspace_bytes(int B, int H, int n, int d, int dtype) {
-  if (B < 1 || H < 1 || n < 1 || n > (1 << 21) || !lla::mfma_supported(dtype, d)) return 0;  // (vector path: none)
+  if (B < 1 || H < 1 || n < 1 || n > lla::kMfmaMaxN || !lla::mfma_supported(dtype, d)) return 0;  // (vector path: none)
   const unsigned long long bh = (unsigned long long)B * (unsigned long long)H;
   if (bh > 0x7fffffffULL || bh * (unsigned long long)n > (1ULL << 40)) return 0;
   return lla::bwd_workspace_bytes((int)bh, n, d);

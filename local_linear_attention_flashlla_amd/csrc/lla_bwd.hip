@@ -1064,7 +1064,7 @@ size_t bwd_workspace_bytes(int BH, int n, int d) {
 }
 
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
-  if (p.n > (1 << 21) || p.BH > 0x7fffffff) return hipErrorInvalidValue;
+  if (p.n > kMfmaMaxN || p.BH > 0x7fffffff) return hipErrorInvalidValue;
   if (p.d == 128) return bwd_d<128>(p, stream);
   if (p.d == 64) return bwd_d<64>(p, stream);
   return hipErrorInvalidValue;

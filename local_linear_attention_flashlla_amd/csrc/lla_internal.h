@@ -65,7 +65,10 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 // fp32 vector-ALU kernel (any d in {16,32,64,128}, fp32 or bf16 inputs).
 hipError_t launch_valu(const FwdParams& p, hipStream_t stream);
 
-// fp16 matrix-core kernel (bf16 inputs, d in {64,128}).
+// fp16 matrix-core kernel (bf16 inputs, d in {64,128}, n <= kMfmaMaxN: the
+// byte offset of a head's last key tile, formed in 32-bit int arithmetic,
+// stays below 2^31).
+constexpr int kMfmaMaxN = 1 << 21;
 size_t mfma_workspace_bytes(int BH, int n, int d);
 bool mfma_supported(int dtype, int d);
 hipError_t launch_mfma(const FwdParams& p, hipStream_t stream);

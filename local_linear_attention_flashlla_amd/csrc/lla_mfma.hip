@@ -1296,21 +1296,21 @@ size_t mfma_workspace_bytes(int BH, int n, int d) {
 }
 
 hipError_t launch_mfma(const FwdParams& p, hipStream_t stream) {
-  if (p.n > (1 << 21) || p.BH > 0x7fffffff) return hipErrorInvalidValue;
+  if (p.n > kMfmaMaxN || p.BH > 0x7fffffff) return hipErrorInvalidValue;
   if (p.d == 128) return launch_d<128>(p, stream);
   if (p.d == 64) return launch_d<64>(p, stream);
   return hipErrorInvalidValue;
 }
 
 hipError_t mfma_moments(const FwdParams& p, hipStream_t stream) {
-  if (p.n > (1 << 21) || p.BH > 0x7fffffff) return hipErrorInvalidValue;
+  if (p.n > kMfmaMaxN || p.BH > 0x7fffffff) return hipErrorInvalidValue;
   if (p.d == 128) return moments_d<128>(p, stream);
   if (p.d == 64) return moments_d<64>(p, stream);
   return hipErrorInvalidValue;
 }
 
 hipError_t mfma_cg(const FwdParams& p, hipStream_t stream) {
-  if (p.n > (1 << 21) || p.BH > 0x7fffffff) return hipErrorInvalidValue;
+  if (p.n > kMfmaMaxN || p.BH > 0x7fffffff) return hipErrorInvalidValue;
   if (p.d == 128) return cg_d<128>(p, stream);
   if (p.d == 64) return cg_d<64>(p, stream);
   return hipErrorInvalidValue;

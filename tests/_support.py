@@ -53,10 +53,23 @@ def worked_example_inputs(g, d):
 
 
 def ensure_built():
+    """The library, checked to be built from the sources in this tree. Without
+    a GPU (the host build check) a missing or stale library is rebuilt; on a
+    GPU machine a stale one is an error, so tests never pass on old code."""
     from local_linear_attention_flashlla_amd import _lib, build
     if not os.path.exists(_lib.LIB_PATH):
         build.build()
-    return _lib.load()
+    lib = _lib.load()
+    if not _lib.is_current(lib):
+        import torch
+        if torch.cuda.is_available():
+            raise RuntimeError(f"{_lib.LIB_PATH} was built from other sources than this tree's: "
+                               "rebuild it (python -m local_linear_attention_flashlla_amd.build)")
+        build.build()
+        lib = _lib.load(_lib.LIB_PATH)
+        _lib._lib = lib
+        assert _lib.is_current(lib)
+    return lib
 
 
 def to_device(wl, device="cuda"):
@@ -136,13 +149,23 @@ def check_parity(wl, out, heads_rows, tol, T=None, cg_tol=None, lam=None, label=
     cg_tol = wl.cg_rel_tol if cg_tol is None else cg_tol
     exact = oracle_rows(wl, heads_rows, lam=lam)
     cg = oracle_rows(wl, heads_rows, solver="cg_centred", T=T, tol=cg_tol, lam=lam)
-    e_gpu, e_cg = [], []
+    e_gpu, e_cg, idx = [], [], []
     for ((b, h), rows), ex, c in zip(heads_rows, exact, cg):
         rows = list(rows)
         e_gpu.append(row_errors(out[b, h, rows], ex["b"]))
         e_cg.append(row_errors(c["b"], ex["b"]))
+        idx.append(np.asarray(rows))
     e_gpu = np.concatenate(e_gpu)
     e_cg = np.concatenate(e_cg)
+    idx = np.concatenate(idx)
+    # errors by position: prefixes shorter than d (the fit nearly interpolates),
+    # between d and 2d, and longer
+    for name, sel in (("i<d", idx < wl.d), ("d<=i<2d", (idx >= wl.d) & (idx < 2 * wl.d)),
+                      ("i>=2d", idx >= 2 * wl.d)):
+        if sel.any():
+            print(f"[bucket] {label} {name}: rows={int(sel.sum())} gpu max={e_gpu[sel].max():.3e} "
+                  f"p50={np.median(e_gpu[sel]):.2e} | float64-CG max={e_cg[sel].max():.3e} | "
+                  f"gpu - float64-CG max={np.max(e_gpu[sel] - e_cg[sel]):.3e}", flush=True)
     bound = tol + factor * e_cg
     conv = e_cg <= 1e-3          # rows where float64 CG clearly reached the answer
     trunc = e_cg > tol / 2       # rows the CG budget leaves far from it

@@ -1,0 +1,191 @@
+"""A numpy model of the rounding in the matrix-core forward kernel.
+
+TEST INFRASTRUCTURE ONLY, and not the oracle: the oracle (``oracle/``) is the
+plain definition in float64. This module runs, per query, the algorithm the
+matrix-core kernel runs, as its header (include/lla.h) and comments describe
+it -- conjugate gradient on the system centred at the weighted key mean, with
+fp16 operands under power-of-two scales and fp32 accumulation -- and rounds
+where that description says the kernel rounds. It shares no code with the
+HIP library and imports nothing from it. Its one use is to say how far an
+honest fp16/fp32 implementation of the same CG lands from the float64 CG
+iterate, so that the GPU parity tests' allowance for unconverged rows and the
+CG-iterate tolerances are derived from data rather than chosen to pass.
+
+Rounding modelled (every other operation is exact, i.e. float64):
+  * keys, values: s k and sv v in fp16 (exact for bf16 inputs in range);
+  * the query operand: fp16(q log2(e) / (sqrt(d) s)), so scores come out in
+    log2 units; score sums rounded to fp32;
+  * moment phase: weights exp2(S - mref) rounded to fp16 against a reference
+    mref (the first 32-key tile's max, raised when a weight would pass 2^15),
+    then omega and mu~ scaled by exp2(mref - m) with m the exact row max;
+  * CG: direction d = fp16(p / sp) with sp a power of two, kbar rounded to
+    fp16 as the expansion point, T = K d - kbar.d in fp32, U = fp16(w T)
+    (or two fp16 terms), Y = sum U k and sum U in fp32; exact line search
+    along d, Fletcher-Reeves beta; r, x, p held in fp32; the stop rule of
+    lla.h;
+  * output phase: rho in two fp16 terms, a / sA = w (1 - (k - kbar).rho) / sA
+    rounded to fp16, sums in fp32.
+
+``exact=True`` turns every rounding off; the model then runs the float64
+CG of the oracle's ``cg_centred`` solver step for step (a CPU test pins it to
+that), which is what makes its rounded runs a measurement of rounding alone.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+LOG2E = 1.4426950408889634
+ROW_NORM_CAP = 128.0
+
+
+def _pow2_floor(x):
+    return 2.0 ** np.floor(np.log2(x))
+
+
+def _pow2_ceil(x):
+    return 1.0 if not x > 0 else 2.0 ** np.ceil(np.log2(x))
+
+
+class _R:
+    """Rounding helpers; identity when exact."""
+
+    def __init__(self, exact):
+        self.exact = exact
+
+    def h(self, x):      # to fp16 and back
+        return np.asarray(x, np.float64) if self.exact else np.asarray(x, np.float16).astype(np.float64)
+
+    def f(self, x):      # to fp32 and back
+        return np.asarray(x, np.float64) if self.exact else np.asarray(x, np.float32).astype(np.float64)
+
+
+def head_scales(q_head, k_head, v_head):
+    """Power-of-two scales s (q and k) and sv (v) that bring the head's largest
+    row norm to at most 128."""
+    a = max(np.linalg.norm(q_head, axis=-1).max(), np.linalg.norm(k_head, axis=-1).max())
+    b = np.linalg.norm(v_head, axis=-1).max()
+    s = _pow2_floor(ROW_NORM_CAP / a) if a > 0 else 1.0
+    sv = _pow2_floor(ROW_NORM_CAP / b) if b > 0 else 1.0
+    return float(s), float(sv)
+
+
+def _apply_two_term(R, M, r):
+    """z = M r with M and r each carried as two fp16 terms under power-of-two
+    scales (hi hi + hi lo + lo hi, fp32 accumulation)."""
+    if R.exact:
+        return M @ r
+    sm = _pow2_ceil(np.abs(M).max())
+    sr = _pow2_ceil(np.abs(r).max()) if np.any(r) else 1.0
+    mh = R.h(M / sm)
+    ml = R.h(M / sm - mh)
+    rh = R.h(r / sr)
+    rl = R.h(r / sr - rh)
+    return R.f((mh @ rh + mh @ rl + ml @ rh) * (sm * sr))
+
+
+def model_row(q_i, K, V, lam, cg_max_iters, cg_rel_tol, s, sv, split_u=False, exact=False,
+              precond=None):
+    """Row i of the causal forward (K, V: the prefix k_0..k_i, v_0..v_i) as
+    the kernel computes it. ``precond``: None (plain CG) or the preconditioner
+    matrix M (in input units, as the oracle defines it); it is rounded to fp32
+    and applied in two fp16 terms. Returns dict(b, rho_c, iters)."""
+    R = _R(exact)
+    d = q_i.shape[0]
+    ks = R.h(s * K)                                    # fp16 scaled keys
+    vs = R.h(sv * V)
+    qop = R.h(q_i * (LOG2E / np.sqrt(d) / s))          # log2-unit query operand
+    S = R.f(ks @ qop)                                  # scores, log2 units
+    m = float(S.max())
+    # moment phase against a reference raised only when needed
+    mref = float(S[:32].max())
+    om, mut = 0.0, np.zeros(d)
+    for t0 in range(0, S.size, 32):
+        st = S[t0:t0 + 32]
+        if st.max() - mref > 15.0:
+            nref = mref + (st.max() - mref)
+            om *= 2.0 ** (mref - nref)
+            mut = mut * 2.0 ** (mref - nref)
+            mref = nref
+        w16 = R.h(2.0 ** (st - mref))
+        om += w16.sum()
+        mut = mut + w16 @ ks[t0:t0 + 32]
+    beta = 2.0 ** (mref - m)
+    om, mut = float(R.f(om * beta)), R.f(mut * beta)
+    kbar = R.f(mut / om)
+    qs = s * q_i
+    r = R.f(mut - om * qs)                             # mu in scaled units
+    x = np.zeros(d)
+    w = R.f(2.0 ** (S - m))                            # CG weights, fp32
+    kb16 = R.h(kbar)
+    lam_s = lam * s * s
+    rr = float(r @ r)
+    r0 = np.sqrt(rr)
+    thr = cg_rel_tol * r0
+    active = rr > 0.0 and cg_max_iters > 0
+    iters = 0
+    Ms = None if precond is None else R.f(np.asarray(precond) / (s * s))   # scaled units
+    z = r if Ms is None else _apply_two_term(R, Ms, r)
+    rz = float(r @ z)
+    sp = _pow2_ceil(np.abs(z).max()) if rr > 0 else 1.0
+    dv = R.h(z / sp)
+    for _ in range(cg_max_iters):
+        if not active:
+            break
+        kbd = float(R.f(kb16 @ dv))
+        T = R.f(ks @ dv - kbd)
+        u = w * T
+        if split_u:
+            uh = R.h(u)
+            ul = R.h(u - uh)
+            U = uh + ul
+        else:
+            U = R.h(u)
+        Y = R.f(U @ ks)
+        usum = float(R.f(U.sum()))
+        Sd = R.f(Y - usum * kb16 + lam_s * dv)
+        dAd = float(dv @ Sd)
+        rd = float(r @ dv)
+        if not dAd > 0.0:
+            break
+        al = rd / dAd
+        r = R.f(r - al * Sd)
+        x = R.f(x + al * dv)
+        rrn = float(r @ r)
+        iters += 1
+        if np.sqrt(rrn) <= thr or rrn == 0.0:
+            rr = rrn
+            break
+        z = r if Ms is None else _apply_two_term(R, Ms, r)
+        rzn = float(r @ z)
+        be = rzn / rz * sp
+        p = R.f(z + be * dv)
+        sp = _pow2_ceil(np.abs(p).max())
+        dv = R.h(p / sp)
+        rr, rz = rrn, rzn
+    # output phase: rho in two fp16 terms around kbar (fp32)
+    srho = _pow2_ceil(np.abs(x).max()) if np.any(x) else 1.0
+    rhi = R.h(x / srho)
+    rlo = R.h(x / srho - rhi)
+    rho2 = (rhi + rlo) * srho
+    zr = R.f(ks @ rho2 - kbar @ rho2)                  # (k - kbar).rho
+    nn = float(np.sqrt(x @ x))
+    inv_sA = 1.0 / _pow2_ceil(1.0 + 2.0 * ROW_NORM_CAP * nn)
+    a = R.h(w * (1.0 - zr) * inv_sA)
+    den = float(R.f(a.sum()))
+    out = R.f(a @ vs) / (den * sv)
+    return {"b": out, "rho_c": x * s, "iters": iters}
+
+
+def model_head(q, k, v, lam, cg_max_iters, cg_rel_tol, rows=None, split_u=False, exact=False,
+               scales=None, precond=None):
+    """Rows of one head ([n, d] arrays, the values the GPU reads, in float64).
+    ``scales``: (s, sv) of the whole head (the kernel takes them over every
+    row of the head, including rows after the ones asked for). ``precond``:
+    None, or a function (i) -> preconditioner matrix of row i (or None)."""
+    n = q.shape[0]
+    rows = range(n) if rows is None else rows
+    s, sv = head_scales(q, k, v) if scales is None else scales
+    res = [model_row(q[i], k[:i + 1], v[:i + 1], lam, cg_max_iters, cg_rel_tol, s, sv,
+                     split_u=split_u, exact=exact,
+                     precond=None if precond is None else precond(i)) for i in rows]
+    return {key: np.array([r[key] for r in res]) for key in ("b", "rho_c", "iters")}

@@ -109,11 +109,33 @@ def test_too_many_heads_or_rows_are_unsupported(lib, B, H, n):
     assert lib.lla_workspace_bytes(B, H, n, 64, _lib.LLA_DTYPE_BF16, _lib.LLA_KERNEL_MFMA) == 0
 
 
-def test_workspace_query_respects_the_sequence_limit(lib):
-    ok = lib.lla_workspace_bytes(1, 1, 1 << 23, 128, _lib.LLA_DTYPE_BF16, _lib.LLA_KERNEL_MFMA)
-    assert ok > 0
-    assert lib.lla_workspace_bytes(1, 1, (1 << 23) + 1, 128, _lib.LLA_DTYPE_BF16,
-                                   _lib.LLA_KERNEL_MFMA) == 0
+def test_workspace_query_respects_the_sequence_limits(lib):
+    bf16, mfma, auto = _lib.LLA_DTYPE_BF16, _lib.LLA_KERNEL_MFMA, _lib.LLA_KERNEL_AUTO
+    # the matrix-core path takes n <= 2^21; above it the size query reports
+    # nothing, and AUTO resolves to the vector path, which needs no workspace
+    assert lib.lla_workspace_bytes(1, 1, 1 << 21, 128, bf16, mfma) > 0
+    assert lib.lla_workspace_bytes(1, 1, 1 << 21, 128, bf16, auto) > 0
+    assert lib.lla_workspace_bytes(1, 1, (1 << 21) + 32, 128, bf16, mfma) == 0
+    assert lib.lla_workspace_bytes(1, 1, (1 << 21) + 32, 128, bf16, auto) == 0
+    assert lib.lla_workspace_bytes(1, 1, (1 << 23) + 1, 128, bf16, auto) == 0
+
+
+@pytest.mark.parametrize("kernel", [_lib.LLA_KERNEL_MFMA])
+def test_matrix_core_sequence_limit_is_rejected_before_any_device_work(lib, kernel):
+    # fake device pointers: a call that got past validation would fault or fail
+    # in HIP; this one must come back UNSUPPORTED from the host checks alone
+    a = _args(n=(1 << 21) + 32, d=128, B=1, H=1, kernel=kernel)
+    assert _call(lib, a) == _lib.LLA_ERR_UNSUPPORTED
+    assert "2^21" in _lib.last_error()
+    assert _call(lib, _args(n=(1 << 21) + 32, d=64, B=1, H=1, kernel=kernel)) == _lib.LLA_ERR_UNSUPPORTED
+    rho_in = ctypes.c_void_p(BASE + 5 * GAP)
+    assert lib.lla_output_given_rho(ctypes.byref(a), rho_in, None) == _lib.LLA_ERR_UNSUPPORTED
+
+
+def test_library_reports_the_hash_of_this_trees_sources(lib):
+    from local_linear_attention_flashlla_amd import build
+    assert lib.lla_source_hash().decode() == build.source_hash()
+    assert _lib.is_current(lib)
 
 
 @pytest.mark.parametrize("rho_in,kw,status", [
