@@ -237,6 +237,26 @@ int lla_decode_ex(const lla_decode_args* args, hipStream_t stream);
    sizes). Linear in n. */
 size_t lla_decode_workspace_bytes(int B, int H, int n, int d, int dtype);
 
+/* For callers that cannot allocate device memory: code under HIP graph
+   capture, tight serving loops, harnesses that forbid hipMalloc. Same
+   computation, kernels and results as lla_decode_ex, but the scratch comes
+   from a static device array of LLA_DECODE_NOALLOC_SCRATCH_BYTES (64 MiB)
+   that each GPU the library runs on holds until the process ends; the call
+   allocates nothing, frees nothing and only launches kernels on `stream`.
+   args: as for lla_decode_ex, except that workspace must be NULL and
+   workspace_bytes 0 (LLA_ERR_INVALID_ARG otherwise). The inputs and outputs
+   are the caller's, as for lla_decode_ex. A call whose scratch need
+   (lla_decode_workspace_bytes) exceeds the static size returns
+   LLA_ERR_WORKSPACE before any device work. `stream` (NULL = the default
+   stream) must belong to the current device, whose copy of the scratch is
+   used (LLA_ERR_INVALID_ARG otherwise). All calls on one GPU share that GPU's
+   scratch: calls that overlap in time on one GPU (other streams, other host
+   threads) race and give wrong results; calls in one stream are ordered and
+   safe. The scratch keeps the last call's contents; nothing in it needs to
+   start at zero. */
+#define LLA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int lla_decode_noalloc(const lla_decode_args* args, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Backward: the gradient of L = sum_i dout_i . out_i with respect to q, k and
  * v for the causal forward, on either path: the matrix cores (bf16 inputs,

@@ -125,7 +125,7 @@ def decode_workspace_bytes(B: int, H: int, n: int, d: int, dtype: str = "bf16") 
 
 def decode(q, k, v, lam: float, cg_max_iters: int, cg_rel_tol: float, *, out=None, omega=None,
            rho=None, rowmax=None, cg_iters=None, cg_resid=None, workspace=None, stream=None,
-           events=None):
+           events=None, noalloc: bool = False):
     """Decode-shaped LLA forward on the GPU: one new query per (batch, head).
 
     q: [B, H, d]; k, v: [B, H, n, d] key and value caches (the new key and
@@ -133,7 +133,10 @@ def decode(q, k, v, lam: float, cg_max_iters: int, cg_rel_tol: float, *, out=Non
     Returns ``out`` ([B, H, d] float32), the last row of the causal forward
     whose query is q. Optional outputs: omega/rowmax/cg_resid [B, H] float32,
     rho [B, H, d] float32, cg_iters [B, H] int32. ``events``: optional
-    (begin, end) pair recorded around the Gram kernel.
+    (begin, end) pair recorded around the Gram kernel. ``noalloc``: call
+    lla_decode_noalloc (the library's static per-GPU scratch; no workspace,
+    nothing allocated) instead of lla_decode_ex; pass ``out`` to allocate
+    nothing on this side either.
     """
     import ctypes
     import torch
@@ -185,7 +188,12 @@ def decode(q, k, v, lam: float, cg_max_iters: int, cg_rel_tol: float, *, out=Non
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
-    _lib.check(_lib.load().lla_decode_ex(ctypes.byref(a), ctypes.c_void_p(handle)))
+    if noalloc:
+        if workspace is not None:
+            raise ValueError("noalloc decode takes no workspace")
+        _lib.check(_lib.load().lla_decode_noalloc(ctypes.byref(a), ctypes.c_void_p(handle)))
+    else:
+        _lib.check(_lib.load().lla_decode_ex(ctypes.byref(a), ctypes.c_void_p(handle)))
     return out
 
 

@@ -33,8 +33,10 @@ EXPORTED_SYMBOLS = (
     "lla_forward_f32", "lla_forward_bf16", "lla_forward_ex", "lla_output_given_rho",
     "lla_workspace_bytes", "lla_decode_ex", "lla_decode_workspace_bytes",
     "lla_backward_ex", "lla_backward_workspace_bytes", "lla_status_string", "lla_last_error", "lla_version",
-    "lla_source_hash",
+    "lla_source_hash", "lla_decode_noalloc",
 )
+
+LLA_DECODE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class LlaFwdArgs(ctypes.Structure):
@@ -156,6 +158,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.lla_output_given_rho.restype = ci
     lib.lla_decode_ex.argtypes = [ctypes.POINTER(LlaDecodeArgs), vp]
     lib.lla_decode_ex.restype = ci
+    lib.lla_decode_noalloc.argtypes = [ctypes.POINTER(LlaDecodeArgs), vp]
+    lib.lla_decode_noalloc.restype = ci
     lib.lla_decode_workspace_bytes.argtypes = [ci, ci, ci, ci, ci]
     lib.lla_decode_workspace_bytes.restype = cz
     lib.lla_backward_ex.argtypes = [ctypes.POINTER(LlaBwdArgs), vp]

@@ -236,8 +236,8 @@ int lla_output_given_rho(const lla_fwd_args* a, const float* rho_in, hipStream_t
   return forward_impl(a, rho_in, stream);
 }
 
-int lla_decode_ex(const lla_decode_args* a, hipStream_t stream) {
-  g_last_error[0] = '\0';
+// Host checks of a decode call; fills *p (everything but the workspace).
+static int decode_validate(const lla_decode_args* a, lla::DecodeParams* p) {
   if (!a) return fail(LLA_ERR_INVALID_ARG, "args is NULL");
   if (a->dtype != LLA_DTYPE_F32 && a->dtype != LLA_DTYPE_BF16)
     return fail(LLA_ERR_INVALID_ARG, "unknown dtype %d", a->dtype);
@@ -282,14 +282,22 @@ int lla_decode_ex(const lla_decode_args* a, hipStream_t stream) {
   }
   if (a->workspace && !aligned16(a->workspace))
     return fail(LLA_ERR_INVALID_ARG, "workspace pointer not 16-byte aligned");
-  lla::DecodeParams p{};
-  p.q = a->q; p.k = a->k; p.v = a->v; p.out = a->out;
-  p.omega = a->omega; p.rho = a->rho; p.rowmax = a->rowmax;
-  p.cg_iters = a->cg_iters; p.cg_resid = a->cg_resid;
-  p.BH = (int)bh; p.n = a->n; p.d = a->d; p.dtype = a->dtype;
-  p.lambda = a->lambda; p.cg_max_iters = a->cg_max_iters; p.cg_rel_tol = a->cg_rel_tol;
-  p.ev_main_begin = a->ev_main_begin;
-  p.ev_main_end = a->ev_main_end;
+  *p = lla::DecodeParams{};
+  p->q = a->q; p->k = a->k; p->v = a->v; p->out = a->out;
+  p->omega = a->omega; p->rho = a->rho; p->rowmax = a->rowmax;
+  p->cg_iters = a->cg_iters; p->cg_resid = a->cg_resid;
+  p->BH = (int)bh; p->n = a->n; p->d = a->d; p->dtype = a->dtype;
+  p->lambda = a->lambda; p->cg_max_iters = a->cg_max_iters; p->cg_rel_tol = a->cg_rel_tol;
+  p->ev_main_begin = a->ev_main_begin;
+  p->ev_main_end = a->ev_main_end;
+  return LLA_OK;
+}
+
+int lla_decode_ex(const lla_decode_args* a, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  lla::DecodeParams p;
+  const int st = decode_validate(a, &p);
+  if (st != LLA_OK) return st;
   const size_t need = lla::decode_workspace_bytes(p.BH, p.n, p.d);
   void* ws = a->workspace;
   bool owned = false;
@@ -310,6 +318,36 @@ int lla_decode_ex(const lla_decode_args* a, hipStream_t stream) {
     if (e == hipSuccess && f != hipSuccess)
       return fail(LLA_ERR_HIP, "workspace free: %s", hipGetErrorString(f));
   }
+  if (e != hipSuccess) return fail(LLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  return LLA_OK;
+}
+
+int lla_decode_noalloc(const lla_decode_args* a, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  lla::DecodeParams p;
+  const int st = decode_validate(a, &p);
+  if (st != LLA_OK) return st;
+  if (a->workspace || a->workspace_bytes)
+    return fail(LLA_ERR_INVALID_ARG, "lla_decode_noalloc takes no workspace (its scratch is static)");
+  const size_t need = lla::decode_workspace_bytes(p.BH, p.n, p.d);
+  if (need > lla::kDecodeScratchBytes)
+    return fail(LLA_ERR_WORKSPACE, "decode needs %zu bytes of scratch; the static scratch holds %zu "
+                "(use lla_decode_ex with a workspace)", need, lla::kDecodeScratchBytes);
+  // the stream must run on the current device, whose copy of the scratch is used
+  if (stream) {
+    int cur = -1, sdev = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess) e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return fail(LLA_ERR_HIP, "device query: %s", hipGetErrorString(e));
+    if (sdev != cur)
+      return fail(LLA_ERR_INVALID_ARG, "stream belongs to device %d, the current device is %d", sdev, cur);
+  }
+  void* scratch = nullptr;
+  hipError_t e = lla::decode_scratch(&scratch);
+  if (e != hipSuccess) return fail(LLA_ERR_HIP, "static scratch address: %s", hipGetErrorString(e));
+  p.workspace = scratch;
+  p.workspace_bytes = lla::kDecodeScratchBytes;
+  e = lla::launch_decode(p, stream);
   if (e != hipSuccess) return fail(LLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return LLA_OK;
 }

@@ -35,6 +35,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "lla_internal.h"
@@ -790,6 +791,34 @@ hipError_t launch_dec(const DecodeParams& p, hipStream_t stream) {
 }  // namespace
 
 bool decode_supported(int d) { return d == 64 || d == 128; }
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free decode entry point: a file-scope device array
+// of kDecodeScratchBytes that every GPU the library runs on holds until the
+// process ends. Host code must not use `scratch` itself as a device address
+// (in host code it names a host-side stand-in); decode_scratch() looks up the
+// array's address on the current device once and keeps it per device.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 size_t decode_workspace_bytes(int BH, int n, int d) { return dec_layout(BH, n, d).total; }
 

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/lla.h"
+
 namespace lla {
 
 // Everything a forward launch needs, already validated by the host API.
@@ -61,6 +63,10 @@ struct DecodeParams {
 bool decode_supported(int d);
 size_t decode_workspace_bytes(int BH, int n, int d);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+// Static per-device scratch of lla_decode_noalloc: its size, and its device
+// address on the current device (looked up once per device, then cached).
+constexpr size_t kDecodeScratchBytes = LLA_DECODE_NOALLOC_SCRATCH_BYTES;
+hipError_t decode_scratch(void** ptr);
 
 // fp32 vector-ALU kernel (any d in {16,32,64,128}, fp32 or bf16 inputs).
 hipError_t launch_valu(const FwdParams& p, hipStream_t stream);

@@ -307,3 +307,16 @@ def test_struct_layout_matches_c_compiler(tmp_path, cname, mirror):
                                           text=True).stdout.split()]
     want = [getattr(M, f).offset for f in fields] + [ctypes.sizeof(M)]
     assert got == want
+
+
+def test_noalloc_decode_rejects_a_workspace_and_oversized_calls_on_the_host(lib):
+    # fake device pointers: both calls must come back from the host checks
+    a = _dargs(workspace=BASE + 7 * GAP, workspace_bytes=1 << 20)
+    assert lib.lla_decode_noalloc(ctypes.byref(a), None) == _lib.LLA_ERR_INVALID_ARG
+    big = 1 << 40   # room for 64 GiB caches between the fake pointers
+    a = _dargs(B=64, H=64, n=65536, d=128, q=BASE, k=BASE + big, v=BASE + 2 * big, out=BASE + 3 * big)
+    need = lib.lla_decode_workspace_bytes(64, 64, 65536, 128, _lib.LLA_DTYPE_BF16)
+    assert need > _lib.LLA_DECODE_NOALLOC_SCRATCH_BYTES
+    assert lib.lla_decode_noalloc(ctypes.byref(a), None) == _lib.LLA_ERR_WORKSPACE
+    assert "static scratch" in _lib.last_error()
+    assert lib.lla_decode_noalloc(ctypes.byref(_dargs(d=48)), None) == _lib.LLA_ERR_UNSUPPORTED
