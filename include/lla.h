@@ -110,9 +110,27 @@ enum {
 
 /* Flags for lla_forward_ex (bitwise OR). */
 enum {
-  LLA_FLAG_SPLIT_U = 1 /* MFMA kernel: carry the CG tile W*(K p) as two fp16
-                          terms (hi + lo) instead of one; slower, more exact */
+  LLA_FLAG_SPLIT_U = 1,    /* MFMA kernel: carry the CG tile W*(K p) as two fp16
+                              terms (hi + lo) instead of one; slower, more exact */
+  LLA_FLAG_PRECOND = 2,    /* MFMA kernel: preconditioned CG (below) whatever
+                              the tolerance */
+  LLA_FLAG_NO_PRECOND = 4  /* MFMA kernel: plain CG whatever the tolerance */
 };
+/* Preconditioned CG (matrix-core path). Without either flag, the forward's
+   CG is preconditioned when cg_rel_tol > 0 (the caller asks for a solution
+   to that tolerance) and plain with cg_rel_tol = 0 (a fixed number of plain
+   CG steps). The preconditioner is not on the pages; it is added because
+   small ridges on clustered keys leave plain CG far from the answer after any
+   affordable number of steps. Queries are grouped in 32s; group g >= 1 uses
+       P_g = sum_{j < N_g} (k_j - m)(k_j - m)^T + lambda I,
+   the unit-weight scatter matrix of the first N_g keys (m their mean) plus
+   the ridge, with N_g = 32 g for g < 8 and, beyond, 32 g rounded down to a
+   multiple of 32 * 2^(floor(log2 g) - 2) (four prefix lengths per doubling of
+   g, each built once per head); group 0 is not preconditioned. N_g <= 32 g,
+   so every query of the group sees those keys. The recurrence is CG with
+   z = P_g^{-1} r in the direction update (p = z + beta p, beta = r'z'/rz),
+   x0 = 0 and the same stop rule on ||r||. P_g^{-1} is formed in fp32 and
+   applied in two fp16 terms. The vector path ignores both flags (plain CG). */
 
 /* Full argument block of lla_forward_ex. Zero-initialise, then fill. */
 typedef struct lla_fwd_args {
@@ -299,7 +317,11 @@ typedef struct lla_bwd_args {
   hipEvent_t ev_main_end;
   int flags;          /* LLA_FLAG_SPLIT_U: the adjoint's right-hand side and CG
                          products carry w * (...) as two fp16 terms (slower,
-                         more exact; see lla_backward_ex) */
+                         more exact; see lla_backward_ex). LLA_FLAG_PRECOND,
+                         LLA_FLAG_NO_PRECOND: as for the forward, whose rule
+                         the adjoint solve follows (preconditioned when
+                         cg_rel_tol > 0 unless a flag says otherwise); pass
+                         the forward's flags */
   int kernel;         /* LLA_KERNEL_*: AUTO takes the matrix-core path for bf16
                          inputs with d in {64, 128}, the vector path otherwise;
                          use the forward's choice */

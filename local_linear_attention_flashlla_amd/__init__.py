@@ -11,11 +11,12 @@ from __future__ import annotations
 from typing import Optional
 
 from . import _lib
-from ._lib import (LLA_DTYPE_BF16, LLA_DTYPE_F32, LLA_FLAG_SPLIT_U, LLA_KERNEL_AUTO,
+from ._lib import (LLA_DTYPE_BF16, LLA_DTYPE_F32, LLA_FLAG_NO_PRECOND, LLA_FLAG_PRECOND,
+                   LLA_FLAG_SPLIT_U, LLA_KERNEL_AUTO,
                    LLA_KERNEL_MFMA, LLA_KERNEL_VALU, LlaError)
 
 __all__ = ["forward", "decode", "decode_workspace_bytes", "workspace_bytes", "LlaError", "LLA_KERNEL_AUTO", "LLA_KERNEL_VALU",
-           "LLA_KERNEL_MFMA", "LLA_FLAG_SPLIT_U", "version"]
+           "LLA_KERNEL_MFMA", "LLA_FLAG_SPLIT_U", "LLA_FLAG_PRECOND", "LLA_FLAG_NO_PRECOND", "version"]
 
 
 def version() -> int:

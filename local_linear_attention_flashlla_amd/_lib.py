@@ -27,6 +27,8 @@ LLA_KERNEL_VALU = 1
 LLA_KERNEL_MFMA = 2
 
 LLA_FLAG_SPLIT_U = 1
+LLA_FLAG_PRECOND = 2
+LLA_FLAG_NO_PRECOND = 4
 
 # Every symbol include/lla.h declares.
 EXPORTED_SYMBOLS = (

@@ -86,7 +86,10 @@ int validate(const lla_fwd_args* a) {
     return fail(LLA_ERR_INVALID_ARG, "cg_max_iters must be in [0, 100000] (got %d)", a->cg_max_iters);
   if (!(a->cg_rel_tol >= 0.f) || !std::isfinite(a->cg_rel_tol))
     return fail(LLA_ERR_INVALID_ARG, "cg_rel_tol must be finite and >= 0 (got %g)", (double)a->cg_rel_tol);
-  if (a->flags & ~LLA_FLAG_SPLIT_U) return fail(LLA_ERR_INVALID_ARG, "unknown flags 0x%x", a->flags);
+  if (a->flags & ~(LLA_FLAG_SPLIT_U | LLA_FLAG_PRECOND | LLA_FLAG_NO_PRECOND))
+    return fail(LLA_ERR_INVALID_ARG, "unknown flags 0x%x", a->flags);
+  if ((a->flags & LLA_FLAG_PRECOND) && (a->flags & LLA_FLAG_NO_PRECOND))
+    return fail(LLA_ERR_INVALID_ARG, "LLA_FLAG_PRECOND and LLA_FLAG_NO_PRECOND together");
   // sizes: every element count must fit comfortably in 64-bit and the grid in 2^31
   const unsigned long long bh = (unsigned long long)a->B * (unsigned long long)a->H;
   if (bh > 0x7fffffffULL) return fail(LLA_ERR_UNSUPPORTED, "B*H too large");
@@ -409,7 +412,10 @@ int lla_backward_ex(const lla_bwd_args* a, hipStream_t stream) {
   }
   if (a->workspace && !aligned16(a->workspace))
     return fail(LLA_ERR_INVALID_ARG, "workspace pointer not 16-byte aligned");
-  if (a->flags & ~LLA_FLAG_SPLIT_U) return fail(LLA_ERR_INVALID_ARG, "unknown flags 0x%x", a->flags);
+  if (a->flags & ~(LLA_FLAG_SPLIT_U | LLA_FLAG_PRECOND | LLA_FLAG_NO_PRECOND))
+    return fail(LLA_ERR_INVALID_ARG, "unknown flags 0x%x", a->flags);
+  if ((a->flags & LLA_FLAG_PRECOND) && (a->flags & LLA_FLAG_NO_PRECOND))
+    return fail(LLA_ERR_INVALID_ARG, "LLA_FLAG_PRECOND and LLA_FLAG_NO_PRECOND together");
   lla::BwdParams p{};
   p.q = a->q; p.k = a->k; p.v = a->v;
   p.out = a->out; p.dout = a->dout; p.rho_c = a->rho_c;

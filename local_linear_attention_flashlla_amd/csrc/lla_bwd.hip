@@ -967,7 +967,7 @@ hipError_t bwd_d(const BwdParams& p, hipStream_t stream) {
   f.cg_rel_tol = p.cg_rel_tol;
   f.cg_iters = p.adj_iters;
   f.cg_resid = p.adj_resid;
-  f.flags = p.flags & LLA_FLAG_SPLIT_U;
+  f.flags = p.flags & (LLA_FLAG_SPLIT_U | LLA_FLAG_PRECOND | LLA_FLAG_NO_PRECOND);
   f.workspace = p.workspace;
   f.workspace_bytes = p.workspace_bytes;
   hipError_t e = mfma_moments(f, stream);
@@ -1005,6 +1005,9 @@ hipError_t bwd_d(const BwdParams& p, hipStream_t stream) {
   else
     hipLaunchKernelGGL((bwd_sweep<D, 0>), grid, dim3(NT), 0, stream, sp);
   e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // the adjoint solve takes the forward's policy, preconditioner included
+  e = mfma_precond_build(f, stream);
   if (e != hipSuccess) return e;
   if (p.ev_main_begin) {
     e = hipEventRecord(p.ev_main_begin, stream);

@@ -83,6 +83,11 @@ hipError_t launch_mfma(const FwdParams& p, hipStream_t stream);
 // max; the residual slab set to mu), and the CG kernel alone, which solves
 // Sigma_c x = r for whatever right-hand side r the residual slab holds.
 hipError_t mfma_moments(const FwdParams& p, hipStream_t stream);
+// The preconditioners of the CG kernel (no-op when the call's flags and
+// tolerance leave CG unpreconditioned), and the CG kernel, which uses them
+// under the same rule (LLA_FLAG_PRECOND, LLA_FLAG_NO_PRECOND, else
+// cg_rel_tol > 0).
+hipError_t mfma_precond_build(const FwdParams& p, hipStream_t stream);
 hipError_t mfma_cg(const FwdParams& p, hipStream_t stream);
 
 // Everything a backward launch needs, already validated by the host API.

@@ -180,6 +180,217 @@ __global__ __launch_bounds__(NT) void prep_convert(const uint16_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
+// Prefix-Gram preconditioner of slot `sl` of head `bh` (one workgroup each).
+// With N = 32 pc_group_of_slot(sl) leading keys in the scaled units of the key
+// tiles (s k_j, s the head's power-of-two scale) and m their plain mean,
+//     P = sum_{j<N} (s k_j - s m)(s k_j - s m)^T + lambda s^2 I
+//       = G - t t^T / N + lambda s^2 I,   G = sum s^2 k_j k_j^T, t = sum s k_j,
+// G on the matrix cores from the transposed key tiles (fp16 keys, exact
+// products, fp32 sums; blocks on or above the diagonal only), then
+// M = P^{-1} by in-place Gauss-Jordan elimination in fp32 (no pivoting: P is
+// symmetric positive definite), each thread holding a (D/16) x (D/16) block in
+// registers and the pivot row and column broadcast through LDS, one barrier
+// per step. M is symmetrised, scaled by a power of two sM >= its largest
+// (diagonal) entry and stored as two fp16 terms, rows in order and columns
+// permuted inside 16-element chunks (the MFMA A operand of z = M r in the CG
+// kernel). A non-positive or non-finite pivot (P not positive definite in
+// fp32) stores sM = 0: the CG kernel then leaves those groups unpreconditioned.
+template <int D>
+__global__ __launch_bounds__(NT) void pc_build(const _Float16* __restrict__ kt,
+                                               const float* __restrict__ partial, int nchunk,
+                                               int nblk, int nslots, float lambda,
+                                               _Float16* __restrict__ pcm, float* __restrict__ pcs) {
+  constexpr int NMB = D / 32;
+  constexpr int NBLK = NMB * (NMB + 1) / 2;  // 32 x 32 blocks on or above the diagonal
+  constexpr int EB = D / 16;                 // side of each thread's block of M
+  __shared__ float sA[D][D + 1];
+  __shared__ float sT[D];
+  __shared__ float sRow[2][D], sCol[2][D];
+  __shared__ float sRed[4];
+  const int sl = blockIdx.x, bh = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, ql = lane & 31, g = lane >> 5;
+  const int N = 32 * pc_group_of_slot(sl);
+  if (tid < 64) {
+    float a, b;
+    head_scales(partial, bh, nchunk, tid, &a, &b);
+    if (tid == 0) sRed[0] = a;
+  }
+  __syncthreads();
+  const float s = sRed[0];
+  const float lam_s = lambda * s * s;
+
+  // ---- G and t over the N keys (N / 32 whole tiles)
+  const int b0 = (wave * NBLK + 3) / 4, b1 = ((wave + 1) * NBLK + 3) / 4;  // this wave's blocks
+  static_assert(NBLK <= 12, "at most three blocks per wave");
+  int ba[3], bb[3];
+  #pragma unroll
+  for (int x = 0; x < 3; ++x) {
+    // block b0 + x in row-major order over the upper triangle
+    int i = b0 + x, r = 0;
+    while (r < NMB - 1 && i >= NMB - r) {
+      i -= NMB - r;
+      ++r;
+    }
+    ba[x] = r;
+    bb[x] = min(r + i, NMB - 1);
+  }
+  floatx16 acc[3];
+  #pragma unroll
+  for (int x = 0; x < 3; ++x)
+    #pragma unroll
+    for (int r = 0; r < 16; ++r) acc[x][r] = 0.f;
+  float tsum[NMB];
+  #pragma unroll
+  for (int rb = 0; rb < NMB; ++rb) tsum[rb] = 0.f;
+  const _Float16* head = kt + static_cast<size_t>(bh) * nblk * BK * D;
+  const int ntl = N / BK;
+  for (int t = 0; t < ntl; ++t) {
+    half8 fr[NMB][2];
+    #pragma unroll
+    for (int rb = 0; rb < NMB; ++rb)
+      #pragma unroll
+      for (int h = 0; h < 2; ++h)
+        fr[rb][h] = *reinterpret_cast<const half8*>(head + static_cast<size_t>(t) * BK * D +
+                                                    ((2 * h + g) * D + 32 * rb + ql) * 8);
+    #pragma unroll
+    for (int x = 0; x < 3; ++x) {
+      if (x < b1 - b0) {
+        #pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          half8 fa = fr[0][h], fb = fr[0][h];
+          #pragma unroll
+          for (int rb = 1; rb < NMB; ++rb) {
+            if (ba[x] == rb) fa = fr[rb][h];
+            if (bb[x] == rb) fb = fr[rb][h];
+          }
+          acc[x] = mfma(fa, fb, acc[x]);
+        }
+      }
+    }
+    #pragma unroll
+    for (int rb = 0; rb < NMB; ++rb)
+      #pragma unroll
+      for (int h = 0; h < 2; ++h)
+        #pragma unroll
+        for (int c = 0; c < 8; ++c) tsum[rb] += static_cast<float>(fr[rb][h][c]);
+  }
+  if (wave == 0) {
+    #pragma unroll
+    for (int rb = 0; rb < NMB; ++rb) {
+      const float v = pair_sum(tsum[rb]);
+      if (g == 0) sT[32 * rb + ql] = v;
+    }
+  }
+  __syncthreads();
+  const float invN = 1.f / static_cast<float>(N);
+  #pragma unroll
+  for (int x = 0; x < 3; ++x) {
+    if (x < b1 - b0) {
+      #pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 32 * ba[x] + 8 * (r >> 2) + 4 * g + (r & 3), col = 32 * bb[x] + ql;
+        float v = acc[x][r] - sT[row] * sT[col] * invN;
+        if (row == col) v += lam_s;
+        sA[row][col] = v;
+        sA[col][row] = v;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- M = P^{-1}: Gauss-Jordan in place, thread block (br, bc)
+  const int br = tid / 16, bc = tid % 16;
+  float A[EB][EB];
+  #pragma unroll
+  for (int i = 0; i < EB; ++i)
+    #pragma unroll
+    for (int j = 0; j < EB; ++j) A[i][j] = sA[EB * br + i][EB * bc + j];
+  bool ok = true;
+  for (int k = 0; k < D; ++k) {
+    const int buf = k & 1, kb = k / EB, kl = k % EB;
+    if (br == kb) {
+      #pragma unroll
+      for (int j = 0; j < EB; ++j) {
+        float v = A[0][j];
+        #pragma unroll
+        for (int i = 1; i < EB; ++i) v = i == kl ? A[i][j] : v;
+        sRow[buf][EB * bc + j] = v;
+      }
+    }
+    if (bc == kb) {
+      #pragma unroll
+      for (int i = 0; i < EB; ++i) {
+        float v = A[i][0];
+        #pragma unroll
+        for (int j = 1; j < EB; ++j) v = j == kl ? A[i][j] : v;
+        sCol[buf][EB * br + i] = v;
+      }
+    }
+    __syncthreads();
+    const float piv = sCol[buf][k];
+    if (!(piv > 0.f) || !(piv < INFINITY)) {  // the same value in every thread
+      ok = false;
+      break;
+    }
+    const float ip = 1.f / piv;
+    float rv[EB], cv[EB];
+    #pragma unroll
+    for (int j = 0; j < EB; ++j) rv[j] = sRow[buf][EB * bc + j];
+    #pragma unroll
+    for (int i = 0; i < EB; ++i) cv[i] = sCol[buf][EB * br + i];
+    #pragma unroll
+    for (int i = 0; i < EB; ++i) {
+      const float ci = cv[i] * ip;
+      #pragma unroll
+      for (int j = 0; j < EB; ++j) {
+        const bool rk = br == kb && i == kl, ck = bc == kb && j == kl;
+        const float upd = fmaf(-ci, rv[j], A[i][j]);
+        A[i][j] = rk ? (ck ? ip : rv[j] * ip) : (ck ? -ci : upd);
+      }
+    }
+  }
+  __syncthreads();
+  // ---- symmetrise, scale, split into two fp16 terms, store
+  if (ok) {
+    #pragma unroll
+    for (int i = 0; i < EB; ++i)
+      #pragma unroll
+      for (int j = 0; j < EB; ++j) sA[EB * br + i][EB * bc + j] = A[i][j];
+  }
+  __syncthreads();
+  if (tid < 64 * ((D + 63) / 64)) {
+    const float dg = (ok && tid < D) ? sA[tid][tid] : 0.f;
+    const float m = wave_max(dg);
+    if (lane == 0) sRed[wave] = m;
+  }
+  __syncthreads();
+  float mdiag = sRed[0];
+  #pragma unroll
+  for (int w = 1; w < (D + 63) / 64; ++w) mdiag = fmaxf(mdiag, sRed[w]);
+  const bool good = ok && mdiag > 0.f && mdiag < INFINITY;
+  const float sM = good ? pow2_ceil(mdiag) : 0.f;
+  const size_t base = (static_cast<size_t>(bh) * nslots + sl) * 2 * D * D;
+  if (good) {
+    const float inv = 1.f / sM;
+    #pragma unroll
+    for (int i = 0; i < EB; ++i) {
+      const int row = EB * br + i;
+      #pragma unroll
+      for (int j = 0; j < EB; ++j) {
+        const int col = EB * bc + j;
+        const float v = 0.5f * (sA[row][col] + sA[col][row]) * inv;
+        const _Float16 hi = static_cast<_Float16>(v);
+        const _Float16 lo = static_cast<_Float16>(v - static_cast<float>(hi));
+        const int pcol = (col & ~15) | swz16(col & 15);
+        pcm[base + static_cast<size_t>(row) * D + pcol] = hi;
+        pcm[base + static_cast<size_t>(D) * D + static_cast<size_t>(row) * D + pcol] = lo;
+      }
+    }
+  }
+  if (tid == 0) pcs[static_cast<size_t>(bh) * nslots + sl] = sM;
+}
+
+// ---------------------------------------------------------------------------
 struct MainParams {
   const uint16_t* q;
   float* out;
@@ -198,14 +409,22 @@ struct MainParams {
   float* qs;         // per-query state slab: row max, omega
   const float* rho_in;  // supplied rho_i [BH][n][d] (no CG solve), or NULL
   float* rho_c;      // optional [BH][n][d]: the centred system's solution
+  const _Float16* pcm;  // preconditioners (see pc_build), used by the CG kernel with PRECOND
+  const float* pcs;
+  int nslots;
   int BH, n, nchunk, nblk;
   int nq32;          // 32-query groups per head in the state slabs
+  // Block selection of the CG kernel: first_only = 1 runs block 0 of every
+  // head (blockIdx.x = head); otherwise the usual order, skipping blocks
+  // below qb_from (those a first_only launch runs)
+  int first_only;
+  int qb_from;
   float lambda;
   int cg_max_iters;
   float cg_rel_tol;
 };
 
-template <int D, int PHASE, bool SPLIT_U, int NW>
+template <int D, int PHASE, bool SPLIT_U, int NW, bool PRECOND = false>
 __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
   constexpr int NKS = D / 16;  // k-steps over d
   constexpr int NMB = D / 32;  // 32-row blocks over d
@@ -226,7 +445,13 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
   const int n = P.n;
   const int nqb = (n + BQW - 1) / BQW;
   int qb, bh;
-  block_coords(static_cast<int>(blockIdx.x), P.BH, nqb, &qb, &bh);
+  if (PHASE == 2 && P.first_only) {
+    qb = 0;
+    bh = static_cast<int>(blockIdx.x);
+  } else {
+    block_coords(static_cast<int>(blockIdx.x), P.BH, nqb, &qb, &bh);
+    if (PHASE == 2 && qb < P.qb_from) return;  // the whole workgroup, before any barrier
+  }
   const int i0 = qb * BQW;
   const int kend = min(n, i0 + BQW);
   const int ntiles = (kend + BK - 1) / BK;
@@ -606,6 +831,89 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
   bool active = qvalid && rr > 0.f && P.cg_max_iters > 0;
   int iters = 0;
 
+  // Preconditioned CG (PRECOND): z = M r with M the prefix-Gram preconditioner
+  // of this wave's group of 32 queries (group 0 and a failed build: z = r),
+  // formed on the matrix cores with M and r each in two fp16 terms (hi hi +
+  // hi lo + lo hi, fp32 sums); r^T z replaces r^T r in the direction update.
+  // z in the accumulator layout (register r of block mb): it shares the
+  // registers of the sweep's Y accumulators, which are free from the r update
+  // until the next sweep starts (and before the first)
+  floatx16 (&zacc)[NMB] = acc;
+  float pc_s = 0.f;
+  __amdgpu_buffer_rsrc_t pc_rsrc = make_rsrc(P.pcs, 0);
+  if constexpr (PRECOND) {
+    const int grp = (i0 >> 5) + wave;  // this wave's group (wave-uniform)
+    if (wave_any && grp >= 1) {
+      const int slot = pc_slot_of_group(grp);
+      pc_s = P.pcs[static_cast<size_t>(bh) * P.nslots + slot];
+      pc_rsrc = make_rsrc(P.pcm + (static_cast<size_t>(bh) * P.nslots + slot) * 2 * D * D,
+                          2 * D * D * sizeof(_Float16));
+    }
+  }
+  const bool use_pc = PRECOND && pc_s > 0.f;
+  auto r_to_z = [&]() __attribute__((always_inline)) {
+    #pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+      #pragma unroll
+      for (int r = 0; r < 16; ++r) zacc[mb][r] = rv4[mb * 4 + (r >> 2)][r & 3];
+  };
+  auto apply_pc = [&]() __attribute__((always_inline)) {
+    float mx = 0.f;
+    #pragma unroll
+    for (int c = 0; c < NMB * 4; ++c)
+      #pragma unroll
+      for (int b = 0; b < 4; ++b) mx = fmaxf(mx, fabsf(rv4[c][b]));
+    const float sr = pow2_ceil(pair_max(mx));
+    const float inv = 1.f / sr;
+    #pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+      #pragma unroll
+      for (int r = 0; r < 16; ++r) zacc[mb][r] = 0.f;
+    #pragma unroll
+    for (int t = 0; t < NKS; ++t) {
+      // k-step t of r / sr as two fp16 terms, in operand order
+      half8 rh, rl;
+      #pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 8 * (t & 1) + e, c = (t >> 1) * 4 + (r >> 2);
+        const float v = rv4[c][r & 3] * inv;
+        const _Float16 h = static_cast<_Float16>(v);
+        rh[e] = h;
+        rl[e] = static_cast<_Float16>(v - static_cast<float>(h));
+      }
+      #pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+        const int off = ((32 * mb + ql) * D + 16 * t + 8 * g) * 2;
+        const half8 mh = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(pc_rsrc, off, 0, 0));
+        const half8 ml = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(pc_rsrc, off, D * D * 2, 0));
+        zacc[mb] = mfma(mh, rh, zacc[mb]);
+        zacc[mb] = mfma(mh, rl, zacc[mb]);
+        zacc[mb] = mfma(ml, rh, zacc[mb]);
+      }
+    }
+    const float zs = sr * pc_s;
+    #pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) zacc[mb] *= zs;
+  };
+  auto zr_dot = [&]() __attribute__((always_inline)) {
+    float t = 0.f;
+    #pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+      #pragma unroll
+      for (int r = 0; r < 16; ++r) t += rv4[mb * 4 + (r >> 2)][r & 3] * zacc[mb][r];
+    return pair_sum(t);
+  };
+  // the vector the next direction starts from: z (preconditioned) or r
+  auto zsrc = [&](int c, int b) __attribute__((always_inline)) {
+    if constexpr (PRECOND) return zacc[c >> 2][4 * (c & 3) + b];
+    else return rv4[c][b];
+  };
+  float rz = rr;
+  if constexpr (PRECOND) {
+    if (use_pc) apply_pc();
+    else r_to_z();
+    rz = zr_dot();
+  }
   // fp16 kbar . op for an operand-ordered fp16 vector
   auto kbar_dot = [&](const half8 (&op)[NKS]) __attribute__((always_inline)) {
     float acc_ = 0.f;
@@ -626,7 +934,7 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
     #pragma unroll
     for (int c = 0; c < NMB * 4; ++c)
       #pragma unroll
-      for (int b = 0; b < 4; ++b) mx = fmaxf(mx, fabsf(rv4[c][b]));
+      for (int b = 0; b < 4; ++b) mx = fmaxf(mx, fabsf(zsrc(c, b)));
     sp = pow2_ceil(pair_max(mx));
     const float inv = 1.f / sp;
     #pragma unroll
@@ -634,7 +942,7 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
       #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int r = 4 * (c & 3) + b, mb = c >> 2;
-        dop[2 * mb + (r >> 3)][r & 7] = static_cast<_Float16>(rv4[c][b] * inv);
+        dop[2 * mb + (r >> 3)][r & 7] = static_cast<_Float16>(zsrc(c, b) * inv);
       }
   }
   float kbd = kbar_dot(dop);
@@ -650,7 +958,7 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
     #pragma unroll
     for (int c = 0; c < NMB * 4; ++c) {
       asm volatile("" : "+a"(rv4[c]));
-      asm volatile("" : "+a"(xv4[c]));
+      if constexpr (!PRECOND) asm volatile("" : "+a"(xv4[c]));
     }
   };
   park();
@@ -898,24 +1206,47 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
           // al = 0 leaves a stopped query's state as it is
           const int ci = mb * 4 + (r >> 2), bi = r & 3;
           rv4[ci][bi] = rv4[ci][bi] - al * v;
-          xv4[ci][bi] = xv4[ci][bi] + al * dv;
+          if constexpr (!PRECOND) xv4[ci][bi] = xv4[ci][bi] + al * dv;
           rrn += rv4[ci][bi] * rv4[ci][bi];
         }
       }
+    if constexpr (PRECOND) {
+      // the iterate waits in its workspace slab (registers are short here):
+      // x += al d, one read and one write of this lane's 256 bytes
+      #pragma unroll
+      for (int c = 0; c < NMB * 4; ++c) {
+        floatx4 xc = slab_ld(xs, c, lane);
+        const int mb = c >> 2, h = (c & 3) >> 1, e0 = 4 * (c & 1);
+        #pragma unroll
+        for (int b = 0; b < 4; ++b) xc[b] += al * static_cast<float>(dop[2 * mb + h][e0 + b]);
+        slab_st(xs, c, lane, xc);
+      }
+    }
     rrn = pair_sum(rrn);
     bool cont = false;
     if (step) {
       ++iters;
       cont = !(sqrtf(rrn) <= thr || rrn == 0.f);
     }
+    // preconditioned: z = M r for the next direction (skipped once no query
+    // of the wave continues; the stale z is then never used)
+    float rzn = rrn;
+    if constexpr (PRECOND) {
+      if (use_pc) {
+        if (__any(cont ? 1 : 0)) apply_pc();
+      } else {
+        r_to_z();
+      }
+      rzn = zr_dot();
+    }
     // lanes that stopped keep their state; the pair exchanges run in every lane
-    const float be = (step && rr > 0.f) ? rrn / rr * sp : 0.f;
+    const float be = (step && rz > 0.f) ? rzn / rz * sp : 0.f;
     float mx = 0.f;
     #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
       #pragma unroll
       for (int r = 0; r < 16; ++r)
-        mx = fmaxf(mx, fabsf(rv4[mb * 4 + (r >> 2)][r & 3] + be * static_cast<float>(dop[2 * mb + (r >> 3)][r & 7])));
+        mx = fmaxf(mx, fabsf(zsrc(mb * 4 + (r >> 2), r & 3) + be * static_cast<float>(dop[2 * mb + (r >> 3)][r & 7])));
     const float sp_new = pow2_ceil(pair_max(mx));
     const float inv_sp = 1.f / sp_new;
     #pragma unroll
@@ -923,19 +1254,24 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
       #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int t = 2 * mb + (r >> 3), c = r & 7;
-        const float pv = rv4[mb * 4 + (r >> 2)][r & 3] + be * static_cast<float>(dop[t][c]);
+        const float pv = zsrc(mb * 4 + (r >> 2), r & 3) + be * static_cast<float>(dop[t][c]);
         if (cont) dop[t][c] = static_cast<_Float16>(pv * inv_sp);
       }
     if (cont) sp = sp_new;
     const float kbdn = kbar_dot(dop);
     if (cont) kbd = kbdn;
-    if (step) rr = rrn;
+    if (step) {
+      rr = rrn;
+      rz = rzn;
+    }
     active = cont;
     park();
   }
   __syncthreads();  // no tile copy may still be in flight when the kernel ends
-  #pragma unroll
-  for (int c = 0; c < NMB * 4; ++c) slab_st(xs, c, lane, xv4[c]);
+  if constexpr (!PRECOND) {
+    #pragma unroll
+    for (int c = 0; c < NMB * 4; ++c) slab_st(xs, c, lane, xv4[c]);
+  }
 
   if (qvalid && g == 0) {
     if (P.cg_iters) P.cg_iters[orow] = iters;
@@ -1184,6 +1520,9 @@ MainParams main_params(const FwdParams& p, const Workspace& w) {
   m.qs = w.qs;
   m.rho_in = p.rho_in;
   m.rho_c = p.rho_c;
+  m.pcm = w.pcm;
+  m.pcs = w.pcs;
+  m.nslots = pc_nslots(p.n);
   m.BH = p.BH;
   m.n = p.n;
   m.nchunk = (p.n + NORM_ROWS - 1) / NORM_ROWS;
@@ -1213,8 +1552,61 @@ hipError_t launch_prep(const FwdParams& p, const Workspace& w, hipStream_t strea
   return hipGetLastError();
 }
 
+// Whether the forward's CG is preconditioned: LLA_FLAG_PRECOND or
+// LLA_FLAG_NO_PRECOND decide; otherwise yes when an early-stopping tolerance
+// is set (the caller asks for a solution to that tolerance, which the
+// preconditioned recurrence reaches in fewer steps), no with tolerance 0 (a
+// fixed number of plain CG steps).
+bool use_precond(const FwdParams& p) {
+  if (p.rho_in || p.cg_max_iters == 0 || pc_nslots(p.n) == 0) return false;
+  if (p.flags & LLA_FLAG_PRECOND) return true;
+  if (p.flags & LLA_FLAG_NO_PRECOND) return false;
+  return p.cg_rel_tol > 0.f;
+}
+
+template <int D>
+hipError_t launch_pc_build(const FwdParams& p, const Workspace& w, hipStream_t stream) {
+  const int nsl = pc_nslots(p.n);
+  const int nchunk = (p.n + NORM_ROWS - 1) / NORM_ROWS;
+  const int nblk = (p.n + BK - 1) / BK;
+  hipLaunchKernelGGL(pc_build<D>, dim3(nsl, p.BH), dim3(NT), 0, stream, w.kt, w.partial, nchunk, nblk,
+                     nsl, p.lambda, w.pcm, w.pcs);
+  return hipGetLastError();
+}
+
 dim3 grid_of(const FwdParams& p, int nw) {
   return dim3(static_cast<unsigned>(static_cast<long long>((p.n + 32 * nw - 1) / (32 * nw)) * p.BH));
+}
+
+template <int D, bool SPLIT>
+void launch_cg_variant(const MainParams& m, dim3 grid, bool pc, hipStream_t stream) {
+  if (pc)
+    hipLaunchKernelGGL((lla_mfma_phase<D, 2, SPLIT, kNW2, true>), grid, dim3(64 * kNW2), 0, stream, m);
+  else
+    hipLaunchKernelGGL((lla_mfma_phase<D, 2, SPLIT, kNW2>), grid, dim3(64 * kNW2), 0, stream, m);
+}
+
+// The CG kernel. The first block of every head (its first 128 queries, the
+// only ones whose prefixes are shorter than d = 128 keys and whose local fit
+// can therefore nearly interpolate, where fp16 rounding of the CG tile
+// W * (K p) is amplified by 1 / lambda) always carries that tile in two fp16
+// terms, in a launch of its own; the other blocks do so with LLA_FLAG_SPLIT_U.
+template <int D>
+hipError_t launch_cg(const FwdParams& p, MainParams m, bool pc, hipStream_t stream) {
+  const bool split = p.flags & LLA_FLAG_SPLIT_U;
+  if (!split) {
+    MainParams f = m;
+    f.first_only = 1;
+    launch_cg_variant<D, true>(f, dim3(static_cast<unsigned>(p.BH)), pc, stream);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    m.qb_from = 1;
+  }
+  if (split)
+    launch_cg_variant<D, true>(m, grid_of(p, kNW2), pc, stream);
+  else if ((p.n + 32 * kNW2 - 1) / (32 * kNW2) > 1)
+    launch_cg_variant<D, false>(m, grid_of(p, kNW2), pc, stream);
+  return hipGetLastError();
 }
 
 template <int D>
@@ -1241,15 +1633,16 @@ hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
     if (p.ev_main_end) e = hipEventRecord(p.ev_main_end, stream);
     return e;
   }
+  const bool pc = use_precond(p);
+  if (pc) {
+    e = launch_pc_build<D>(p, w, stream);
+    if (e != hipSuccess) return e;
+  }
   if (p.ev_main_begin) {
     e = hipEventRecord(p.ev_main_begin, stream);
     if (e != hipSuccess) return e;
   }
-  if (p.flags & LLA_FLAG_SPLIT_U)
-    hipLaunchKernelGGL((lla_mfma_phase<D, 2, true, kNW2>), grid2, dim3(64 * kNW2), 0, stream, m);
-  else
-    hipLaunchKernelGGL((lla_mfma_phase<D, 2, false, kNW2>), grid2, dim3(64 * kNW2), 0, stream, m);
-  e = hipGetLastError();
+  e = launch_cg<D>(p, m, pc, stream);
   if (e != hipSuccess) return e;
   if (p.ev_main_end) {
     e = hipEventRecord(p.ev_main_end, stream);
@@ -1273,12 +1666,13 @@ hipError_t moments_d(const FwdParams& p, hipStream_t stream) {
 template <int D>
 hipError_t cg_d(const FwdParams& p, hipStream_t stream) {
   const Workspace w = carve(p.workspace, p.BH, p.n, D);
-  const MainParams m = main_params<D>(p, w);
-  if (p.flags & LLA_FLAG_SPLIT_U)
-    hipLaunchKernelGGL((lla_mfma_phase<D, 2, true, kNW2>), grid_of(p, kNW2), dim3(64 * kNW2), 0, stream, m);
-  else
-    hipLaunchKernelGGL((lla_mfma_phase<D, 2, false, kNW2>), grid_of(p, kNW2), dim3(64 * kNW2), 0, stream, m);
-  return hipGetLastError();
+  return launch_cg<D>(p, main_params<D>(p, w), use_precond(p), stream);
+}
+
+template <int D>
+hipError_t precond_d(const FwdParams& p, hipStream_t stream) {
+  if (!use_precond(p)) return hipSuccess;
+  return launch_pc_build<D>(p, carve(p.workspace, p.BH, p.n, D), stream);
 }
 
 }  // namespace
@@ -1289,10 +1683,13 @@ size_t mfma_workspace_bytes(int BH, int n, int d) {
   const int nchunk = (n + NORM_ROWS - 1) / NORM_ROWS;
   const size_t npad = static_cast<size_t>((n + BK - 1) / BK) * BK;
   const size_t nqpad = static_cast<size_t>((n + kMaxBQ - 1) / kMaxBQ) * kMaxBQ;
+  const size_t nsl = static_cast<size_t>(pc_nslots(n));
   return align256(static_cast<size_t>(BH) * nchunk * 2 * sizeof(float)) +
          3 * align256(static_cast<size_t>(BH) * npad * d * sizeof(_Float16)) +
          3 * align256(static_cast<size_t>(BH) * nqpad * d * sizeof(float)) +
-         align256(static_cast<size_t>(BH) * nqpad * 4 * sizeof(float));
+         align256(static_cast<size_t>(BH) * nqpad * 4 * sizeof(float)) +
+         align256(static_cast<size_t>(BH) * nsl * 2 * d * d * sizeof(_Float16)) +
+         align256(static_cast<size_t>(BH) * nsl * sizeof(float));
 }
 
 hipError_t launch_mfma(const FwdParams& p, hipStream_t stream) {
@@ -1306,6 +1703,13 @@ hipError_t mfma_moments(const FwdParams& p, hipStream_t stream) {
   if (p.n > kMfmaMaxN || p.BH > 0x7fffffff) return hipErrorInvalidValue;
   if (p.d == 128) return moments_d<128>(p, stream);
   if (p.d == 64) return moments_d<64>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t mfma_precond_build(const FwdParams& p, hipStream_t stream) {
+  if (p.n > kMfmaMaxN || p.BH > 0x7fffffff) return hipErrorInvalidValue;
+  if (p.d == 128) return precond_d<128>(p, stream);
+  if (p.d == 64) return precond_d<64>(p, stream);
   return hipErrorInvalidValue;
 }
 

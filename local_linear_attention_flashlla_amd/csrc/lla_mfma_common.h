@@ -112,6 +112,27 @@ __device__ __forceinline__ float wave_max(float v) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// Prefix-Gram preconditioner of the CG solve. Queries are grouped in 32s;
+// group g >= 1 is preconditioned with the scatter matrix of the first 32 g'
+// keys plus the ridge, where g' = g for g < 8 and, beyond, g rounded down to
+// a multiple of 2^(floor(log2 g) - 2): four prefix lengths per doubling of g,
+// each built once per head ("slot") and shared by the groups up to the next.
+// Group 0 is not preconditioned.
+__host__ __device__ inline int pc_slot_of_group(int g) {  // g >= 1
+  if (g < 8) return g - 1;
+  const int e = 31 - __builtin_clz(static_cast<unsigned>(g));
+  return 7 + 4 * (e - 3) + ((g >> (e - 2)) - 4);
+}
+__host__ __device__ inline int pc_group_of_slot(int slot) {  // g' of the slot
+  if (slot < 7) return slot + 1;
+  const int e = 3 + (slot - 7) / 4, q = (slot - 7) % 4;
+  return (4 + q) << (e - 2);
+}
+inline int pc_nslots(int n) {
+  const int G = (n + 31) / 32;
+  return G >= 2 ? pc_slot_of_group(G - 1) + 1 : 0;
+}
+
 struct Workspace {
   float* partial;   // [BH][nchunk][2]: max row ||.||^2 of q and k; of v
   _Float16* kr;     // [BH][npad][D]      s k, d index permuted by swz16
@@ -121,6 +142,8 @@ struct Workspace {
   float* kbs;       // fp32 kbar, same layout
   float* rs;        // CG residuals, same layout
   float* qs;        // per query row max and omega: [blocks][4 waves][2][64 lanes]
+  _Float16* pcm;    // [BH][nslots][2][D][D] preconditioners M / sM, hi and lo fp16 terms
+  float* pcs;       // [BH][nslots] their power-of-two scales sM (0: not built)
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -148,6 +171,11 @@ Workspace carve(void* base, int BH, int n, int d) {
   w.rs = reinterpret_cast<float*>(p);
   p += sl;
   w.qs = reinterpret_cast<float*>(p);
+  p += align256(static_cast<size_t>(BH) * nqpad * 4 * sizeof(float));
+  const size_t nsl = static_cast<size_t>(pc_nslots(n));
+  w.pcm = reinterpret_cast<_Float16*>(p);
+  p += align256(static_cast<size_t>(BH) * nsl * 2 * d * d * sizeof(_Float16));
+  w.pcs = reinterpret_cast<float*>(p);
   return w;
 }
 

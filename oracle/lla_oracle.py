@@ -44,6 +44,13 @@ Readings taken where the pages leave a step open:
     ||r_k|| <= tol * ||r_0|| (recurrence residual), on breakdown
     (p^T Sigma p <= 0 or r = 0), or at k = max_iters. tol = 0 runs exactly
     max_iters steps unless the residual is exactly zero.
+  * Preconditioned CG (not on the pages, which only mention early stopping;
+    used where the iteration budget cannot otherwise reach the answer): the
+    same recurrence with z = P^{-1} r in place of r in the direction update.
+    P is the prefix-Gram preconditioner of the row's group of 32 queries
+    (``prefix_group_length``, ``prefix_preconditioner``): the unit-weight
+    scatter matrix of the first N keys plus lam I, with N <= 32 floor(i/32)
+    so that those keys are visible to every query of the group.
 """
 
 from __future__ import annotations
@@ -69,6 +76,8 @@ __all__ = [
     "eq9_intercept",
     "covariance_form_intercept",
     "tilde_moments",
+    "prefix_group_length",
+    "prefix_preconditioner",
 ]
 
 
@@ -119,33 +128,72 @@ def cholesky_solve(Sigma: np.ndarray, rhs: np.ndarray) -> np.ndarray:
     return solve_triangular(L.T, y, lower=False)
 
 
-def cg_solve(Sigma: np.ndarray, rhs: np.ndarray, max_iters: int, rel_tol: float):
+def prefix_group_length(i: int) -> int:
+    """Number N of leading keys whose scatter matrix preconditions row i.
+
+    Rows are grouped in 32s, group g = floor(i / 32). Group 0 gets no
+    preconditioner (N = 0). Groups 1..7 use N = 32 g, the keys every query of
+    the group sees. From group 8 on, N is 32 g rounded down to a multiple of
+    32 * 2^(floor(log2 g) - 2): four prefix lengths per doubling of g, each
+    shared by the groups up to the next, so a head needs only a few
+    preconditioners. Always N <= 32 g <= i."""
+    g = int(i) // 32
+    if g == 0:
+        return 0
+    if g < 8:
+        return 32 * g
+    step = 1 << (g.bit_length() - 3)
+    return 32 * (g // step) * step
+
+
+def prefix_preconditioner(K_prefix: np.ndarray, lam: float):
+    """P for the last row of K_prefix (row i = len(K_prefix) - 1): with N =
+    prefix_group_length(i) and m the plain mean of k_0..k_{N-1},
+    P = sum_{j<N} (k_j - m)(k_j - m)^T + lam I; None when N = 0."""
+    i = K_prefix.shape[0] - 1
+    N = prefix_group_length(i)
+    if N == 0:
+        return None
+    Kp = np.asarray(K_prefix[:N], dtype=np.float64)
+    m = Kp.mean(axis=0)
+    D = Kp - m[None, :]
+    return D.T @ D + lam * np.eye(Kp.shape[1])
+
+
+def cg_solve(Sigma: np.ndarray, rhs: np.ndarray, max_iters: int, rel_tol: float, precond=None):
     """Conjugate gradient on Sigma x = rhs with the stop rule in the module
     docstring ([LLA] 2.2: matrix-free CG; only products Sigma p are used).
+    ``precond``: None, or an SPD matrix P; then the preconditioned recurrence
+    (z = P^{-1} r, applied by a Cholesky solve, and r^T z in place of r^T r).
     Returns (x, iterations, ||r|| / ||r_0||)."""
+    def apply(r):
+        return r.copy() if precond is None else cholesky_solve(precond, r)
     x = np.zeros_like(rhs)
     r = rhs.astype(np.float64).copy()
     rr = float(r @ r)
     r0 = np.sqrt(rr)
     if r0 == 0.0:
         return x, 0, 0.0
-    p = r.copy()
+    z = apply(r)
+    rz = float(r @ z)
+    p = z.copy()
     it = 0
     for _ in range(max_iters):
         Sp = Sigma @ p
         pSp = float(p @ Sp)
         if not pSp > 0.0:
             break
-        alpha = rr / pSp
+        alpha = rz / pSp
         x = x + alpha * p
         r = r - alpha * Sp
-        rr_new = float(r @ r)
+        rr = float(r @ r)
         it += 1
-        if np.sqrt(rr_new) <= rel_tol * r0 or rr_new == 0.0:
-            rr = rr_new
+        if np.sqrt(rr) <= rel_tol * r0 or rr == 0.0:
             break
-        p = r + (rr_new / rr) * p
-        rr = rr_new
+        z = apply(r)
+        rz_new = float(r @ z)
+        p = z + (rz_new / rz) * p
+        rz = rz_new
     return x, it, float(np.sqrt(rr) / r0)
 
 
@@ -194,15 +242,18 @@ def oracle_row(q_i, K_prefix, V_prefix, lam, scale=None, solver="cholesky",
     ``solver="cg_centred"``: CG (same stop rule) on Sigma_c rho_c = mu_i, the
     system centred at the weighted key mean (``centred_moments``); output by
     ``centred_intercept``; ``rho`` is reported as the pages' rho_i.
+    ``solver="pcg_centred"``: the same with the prefix-Gram preconditioner of
+    the row's group (``prefix_preconditioner``).
     ``solver="zero"``: rho_i = 0, the local-constant (softmax) limit."""
     q_i = np.asarray(q_i, dtype=np.float64)
     K_prefix = np.asarray(K_prefix, dtype=np.float64)
     V_prefix = np.asarray(V_prefix, dtype=np.float64)
     c = _scale(q_i.shape[0], scale)
     _, m, w = causal_weights(q_i, K_prefix, c)
-    if solver == "cg_centred":
+    if solver in ("cg_centred", "pcg_centred"):
         Zc, omega, kbar, mu, Sigma_c = centred_moments(q_i, K_prefix, w, lam)
-        rho_c, iters, resid = cg_solve(Sigma_c, mu, cg_max_iters, cg_rel_tol)
+        P = prefix_preconditioner(K_prefix, lam) if solver == "pcg_centred" else None
+        rho_c, iters, resid = cg_solve(Sigma_c, mu, cg_max_iters, cg_rel_tol, precond=P)
         b, s, _ = centred_intercept(w, Zc, V_prefix, rho_c)
         rho = rho_c / (1.0 + (kbar - q_i) @ rho_c)
         schur = float(omega - mu @ rho)

@@ -61,7 +61,7 @@ from typing import Optional
 
 import numpy as np
 
-from .lla_oracle import cg_solve, cholesky_solve
+from .lla_oracle import cg_solve, cholesky_solve, prefix_preconditioner
 
 __all__ = ["backward_row", "backward_row_centred", "backward_head"]
 
@@ -121,7 +121,9 @@ def backward_row_centred(q_i, K, V, g_i, lam, scale=None, solver="cholesky",
                          cg_max_iters=0, cg_rel_tol=0.0, jstar: Optional[int] = None):
     """The same gradient through the centred form (module docstring).
     ``solver="cholesky"``: exact solves; ``solver="cg"``: rho_c and y are CG
-    iterates under the oracle's stop rule, each system started from zero.
+    iterates under the oracle's stop rule, each system started from zero;
+    ``solver="pcg"``: the same with the row's prefix-Gram preconditioner
+    (``lla_oracle.prefix_preconditioner``) on both systems.
     Returns the dict of ``backward_row`` (dq, dK, dV, dw, jstar) plus rho_c,
     y, the adjoint iteration count and the identity term -lam y.rho_c."""
     q_i = np.asarray(q_i, np.float64)
@@ -139,10 +141,11 @@ def backward_row_centred(q_i, K, V, g_i, lam, scale=None, solver="cholesky",
     u = kbar - q_i
     Sigma_c = (Cj * w[:, None]).T @ Cj + lam * np.eye(d)
     rhs = omega * u
+    P = prefix_preconditioner(K, lam) if solver == "pcg" else None
     if solver == "cholesky":
         rho_c = cholesky_solve(Sigma_c, rhs)
-    elif solver == "cg":
-        rho_c, _, _ = cg_solve(Sigma_c, rhs, cg_max_iters, cg_rel_tol)
+    elif solver in ("cg", "pcg"):
+        rho_c, _, _ = cg_solve(Sigma_c, rhs, cg_max_iters, cg_rel_tol, precond=P)
     else:
         raise ValueError(solver)
     A = 1.0 - Cj @ rho_c
@@ -154,7 +157,7 @@ def backward_row_centred(q_i, K, V, g_i, lam, scale=None, solver="cholesky",
         y = cholesky_solve(Sigma_c, h)
         adj_iters = -1
     else:
-        y, adj_iters, _ = cg_solve(Sigma_c, h, cg_max_iters, cg_rel_tol)
+        y, adj_iters, _ = cg_solve(Sigma_c, h, cg_max_iters, cg_rel_tol, precond=P)
     e = beta / omega - Cj @ y
     tau = (h @ rho_c) / omega - y @ u
     dw = A * e + tau

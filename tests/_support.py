@@ -129,8 +129,19 @@ def oracle_given_rho(wl, heads_rows, rho, lam=None):
     return res
 
 
+def mfma_solver(flags, T, tol):
+    """The oracle's float64 counterpart of the matrix-core CG under the rule of
+    include/lla.h: preconditioned with LLA_FLAG_PRECOND, plain with
+    LLA_FLAG_NO_PRECOND, otherwise preconditioned iff cg_rel_tol > 0."""
+    from local_linear_attention_flashlla_amd import _lib
+    if T > 0 and ((flags & _lib.LLA_FLAG_PRECOND) or
+                  (not flags & _lib.LLA_FLAG_NO_PRECOND and tol > 0)):
+        return "pcg_centred"
+    return "cg_centred"
+
+
 def check_parity(wl, out, heads_rows, tol, T=None, cg_tol=None, lam=None, label="",
-                 factor=4.0):
+                 factor=4.0, solver="cg_centred"):
     """Compare GPU rows with the float64 oracle.
 
     e_gpu = row error of the GPU output against the exact (Cholesky) oracle;
@@ -148,7 +159,7 @@ def check_parity(wl, out, heads_rows, tol, T=None, cg_tol=None, lam=None, label=
     T = wl.cg_max_iters if T is None else T
     cg_tol = wl.cg_rel_tol if cg_tol is None else cg_tol
     exact = oracle_rows(wl, heads_rows, lam=lam)
-    cg = oracle_rows(wl, heads_rows, solver="cg_centred", T=T, tol=cg_tol, lam=lam)
+    cg = oracle_rows(wl, heads_rows, solver=solver, T=T, tol=cg_tol, lam=lam)
     e_gpu, e_cg, idx = [], [], []
     for ((b, h), rows), ex, c in zip(heads_rows, exact, cg):
         rows = list(rows)

@@ -20,7 +20,8 @@ Rounding modelled (every other operation is exact, i.e. float64):
     then omega and mu~ scaled by exp2(mref - m) with m the exact row max;
   * CG: direction d = fp16(p / sp) with sp a power of two, kbar rounded to
     fp16 as the expansion point, T = K d - kbar.d in fp32, U = fp16(w T)
-    (or two fp16 terms), Y = sum U k and sum U in fp32; exact line search
+    (two fp16 terms for the first 128 queries of a head, or all with
+    split_u), Y = sum U k and sum U in fp32; exact line search
     along d, Fletcher-Reeves beta; r, x, p held in fp32; the stop rule of
     lla.h;
   * output phase: rho in two fp16 terms, a / sA = w (1 - (k - kbar).rho) / sA
@@ -176,6 +177,38 @@ def model_row(q_i, K, V, lam, cg_max_iters, cg_rel_tol, s, sv, split_u=False, ex
     return {"b": out, "rho_c": x * s, "iters": iters}
 
 
+def group_prefix(i):
+    """Keys (a prefix) whose scatter matrix preconditions row i, as lla.h
+    defines it: 0 for the first 32 rows; 32 g for group g = i // 32 < 8;
+    beyond, 32 g rounded down to a multiple of 32 * 2^(floor(log2 g) - 2)."""
+    g = i // 32
+    if g < 8:
+        return 32 * g
+    e = int(g).bit_length() - 1
+    step = 2 ** (e - 2)
+    return 32 * (g // step) * step
+
+
+def preconditioners(k, lam):
+    """A function i -> M_i (inverse of the prefix-Gram preconditioner, input
+    units) or None, computed the way the kernel does: fp32 inverse of the
+    scatter matrix of the scaled fp16 keys plus the ridge, symmetrised."""
+    cache = {}
+
+    def f(i):
+        N = group_prefix(i)
+        if N == 0:
+            return None
+        if N not in cache:
+            Kp = np.asarray(k[:N], np.float64)
+            D = Kp - Kp.mean(axis=0)
+            P = np.asarray(D.T @ D + lam * np.eye(k.shape[1]), np.float32)
+            M = np.linalg.inv(P).astype(np.float64)
+            cache[N] = 0.5 * (M + M.T)
+        return cache[N]
+    return f
+
+
 def model_head(q, k, v, lam, cg_max_iters, cg_rel_tol, rows=None, split_u=False, exact=False,
                scales=None, precond=None):
     """Rows of one head ([n, d] arrays, the values the GPU reads, in float64).
@@ -185,7 +218,9 @@ def model_head(q, k, v, lam, cg_max_iters, cg_rel_tol, rows=None, split_u=False,
     n = q.shape[0]
     rows = range(n) if rows is None else rows
     s, sv = head_scales(q, k, v) if scales is None else scales
+    # the kernel carries the CG tile in two fp16 terms for the first 128
+    # queries of every head, and for all of them with split_u
     res = [model_row(q[i], k[:i + 1], v[:i + 1], lam, cg_max_iters, cg_rel_tol, s, sv,
-                     split_u=split_u, exact=exact,
+                     split_u=split_u or i < 128, exact=exact,
                      precond=None if precond is None else precond(i)) for i in rows]
     return {key: np.array([r[key] for r in res]) for key in ("b", "rho_c", "iters")}

@@ -207,6 +207,27 @@ def test_too_small_workspace_is_reported(lib):
     assert _call(lib, a) == -4
 
 
+def _nslots(n):
+    """Preconditioners per head (include/lla.h): one per prefix length, the
+    lengths 32 g' of groups g = 1 .. ceil(n / 32) - 1 (g' = g for g < 8, then
+    four lengths per doubling of g)."""
+    G = (n + 31) // 32
+    if G < 2:
+        return 0
+    g = G - 1
+    if g < 8:
+        return g
+    e = g.bit_length() - 1
+    return 7 + 4 * (e - 3) + (g >> (e - 2)) - 4 + 1
+
+
+def _pc_bytes(BH, n, d):
+    """Workspace bytes of the preconditioners: a d x d matrix in two fp16 terms
+    and a float scale each (256-byte aligned regions): O(d^2 log n) per head."""
+    al = lambda x: (x + 255) // 256 * 256
+    return al(BH * _nslots(n) * 2 * d * d * 2) + al(BH * _nslots(n) * 4)
+
+
 def test_workspace_sizes(lib):
     # the VALU kernel keeps its state on chip
     assert lib.lla_workspace_bytes(1, 1, 256, 16, _lib.LLA_DTYPE_F32, _lib.LLA_KERNEL_VALU) == 0
@@ -217,8 +238,11 @@ def test_workspace_sizes(lib):
              for n in (1024, 2048, 4096, 8192, 16384)]
     if sizes[0] == 0:
         pytest.skip("MFMA kernel not available in this build")
-    diffs = [b - a for a, b in zip(sizes, sizes[1:])]
-    # linear: doubling n adds twice the previous increment
+    pc = [_pc_bytes(16, n, 128) for n in (1024, 2048, 4096, 8192, 16384)]
+    assert [_nslots(n) for n in (1024, 2048, 4096, 8192, 16384)] == [15, 19, 23, 27, 31]
+    lin = [a - b for a, b in zip(sizes, pc)]
+    diffs = [b - a for a, b in zip(lin, lin[1:])]
+    # the rest is linear: doubling n adds twice the previous increment
     assert diffs[1] == 2 * diffs[0] and diffs[2] == 2 * diffs[1] and diffs[3] == 2 * diffs[2]
 
 
@@ -273,7 +297,8 @@ def test_backward_workspace_is_linear_in_n(lib):
     sizes = [lib.lla_backward_workspace_bytes(1, 16, n, 128, _lib.LLA_DTYPE_BF16)
              for n in (1024, 2048, 4096, 8192)]
     assert all(s > 0 for s in sizes)
-    diffs = [b - a for a, b in zip(sizes, sizes[1:])]
+    lin = [a - _pc_bytes(16, n, 128) for a, n in zip(sizes, (1024, 2048, 4096, 8192))]
+    diffs = [b - a for a, b in zip(lin, lin[1:])]
     assert diffs[1] == 2 * diffs[0] and diffs[2] == 2 * diffs[1]
     # and it holds the forward's workspace
     assert sizes[0] > lib.lla_workspace_bytes(1, 16, 1024, 128, _lib.LLA_DTYPE_BF16, _lib.LLA_KERNEL_MFMA)

@@ -8,15 +8,7 @@ solves short of the exact answer, the bound is tol + 4 x the error of the
 oracle's own float64 CG gradient (same iteration cap and stop rule on both
 the forward and the adjoint system) -- the same rule as the forward's.
 
-dk carries one more term in its bound. Where a query's local fit nearly
-interpolates (a prefix shorter than d, small lambda), rho_c is of order
-1/lambda while e_ij = beta_ij/omega_i - c_ij.y_i is a difference of O(1)
-terms of order lambda, and dk_j holds w_ij e_ij rho_c,i. The forward's moment
-and product operands round the weights of that fit to fp16, which moves e_ij
-by about 2^-11 |beta_ij / omega_i|; ``interp_sensitivity`` is that shift
-carried into dk_j, S_j = 2^-11 sum_i w_ij |beta_ij / omega_i| |rho_c,i|, and
-the bound adds 4 S_j / |dk_j|. It is negligible unless lambda is small and
-prefixes are short.
+No term of the bound is derived from the kernel's own rounding.
 
 The key attaining a row's max decides where the max's share of the gradient
 goes; where float64 and the kernel's fp16 operands could order two scores
@@ -83,59 +75,38 @@ def kernel_argmax(wl, b, h, rows):
     return js
 
 
-def interp_sensitivity(wl, g, b, h, rows, lam, eps=2.0 ** -11):
-    """S_j = eps sum_i w_ij |beta_ij / omega_i| |rho_c,i| over the listed
-    rows i (exact float64 quantities, from the oracle's own pieces); eps is
-    the rounding of the fit's weights: 2^-11 on the fp16 matrix-core path,
-    2^-24 on the fp32 vector path."""
-    from oracle import lla_oracle as O
-    c = 1.0 / np.sqrt(wl.d)
-    S = np.zeros(wl.n)
-    for i in rows:
-        qi, K, V = wl.q[b, h, i], wl.k[b, h, :i + 1], wl.v[b, h, :i + 1]
-        _, _, w = O.causal_weights(qi, K, c)
-        _, omega, kbar, mu, Sc = O.centred_moments(qi, K, w, lam)
-        rho_c = O.cholesky_solve(Sc, mu)
-        gi = np.asarray(g[b, h, i], np.float64)
-        beta = V @ gi - gi @ ((V.T @ w) / omega)
-        S[:i + 1] += eps * w * np.abs(beta) / omega * np.linalg.norm(rho_c)
-    return S
-
-
 def check_grads(wl, g, res, heads, dq_rows, kv_from, T, tol, lam, label, factor=4.0, bar=None,
-                fp16_scores=True):
+                fp16_scores=True, which=("dq", "dk", "dv")):
     """dq on rows dq_rows, dk/dv on keys kv_from..n-1 (the oracle then runs
     rows kv_from..n-1, which hold every contribution to those keys). The
     maximising key is decided on fp16 operands for the matrix-core path; the
     vector path scores in fp32, where float64's decision is the same (ties
-    at the level of fp32 rounding aside)."""
+    at the level of fp32 rounding aside). The float64 CG gradient takes the
+    recurrence the library runs: on the matrix-core path preconditioned when
+    tol > 0 (include/lla.h), on the vector path plain."""
+    solver = "pcg" if fp16_scores and T > 0 and tol > 0 else "cg"
     n = wl.n
     kv_rows = list(range(kv_from, n))
     rows = sorted(set(dq_rows) | set(kv_rows))
     hr = [((b, h), rows) for b, h in heads]
     jst = {(b, h): kernel_argmax(wl, b, h, rows) for b, h in heads} if fp16_scores else None
     ex = oracle_grads(wl, g, hr, lam=lam, jstar=jst)
-    cg = oracle_grads(wl, g, hr, form="centred", solver="cg", T=T, tol=tol, lam=lam, jstar=jst)
+    cg = oracle_grads(wl, g, hr, form="centred", solver=solver, T=T, tol=tol, lam=lam, jstar=jst)
     worst = 0.0
     for name, idx, sel in (("dq", 0, list(dq_rows)), ("dk", 1, kv_rows), ("dv", 2, kv_rows)):
-        e_gpu, e_cg, e_s = [], [], []
+        if name not in which:
+            continue
+        e_gpu, e_cg = [], []
         for ((b, h), _), x, c in zip(hr, ex, cg):
             e_gpu.append(row_errors(res[name][b, h, sel], x[idx][sel]))
             e_cg.append(row_errors(c[idx][sel], x[idx][sel]))
-            if name == "dk":
-                S = interp_sensitivity(wl, g, b, h, rows, lam,
-                                       eps=2.0 ** -11 if fp16_scores else 2.0 ** -24)[sel]
-                e_s.append(S / np.maximum(np.linalg.norm(x[idx][sel], axis=-1), 1e-30))
-            else:
-                e_s.append(np.zeros(len(sel)))
-        e_gpu, e_cg, e_s = np.concatenate(e_gpu), np.concatenate(e_cg), np.concatenate(e_s)
+        e_gpu, e_cg = np.concatenate(e_gpu), np.concatenate(e_cg)
         base = tol_of(name) if bar is None else bar
-        ratio = float((e_gpu / (base + factor * e_cg + factor * e_s)).max())
+        ratio = float((e_gpu / (base + factor * e_cg)).max())
         worst = max(worst, ratio)
         print(f"[parity] {label} {name}: rows={e_gpu.size} max={e_gpu.max():.3e} "
               f"p50={np.median(e_gpu):.2e} p99={np.quantile(e_gpu, 0.99):.2e} | float64-CG err max "
-              f"{e_cg.max():.2e} | fit-rounding term max {e_s.max():.2e} | worst "
-              f"e/(tol+{factor}(e_cg+e_s)) {ratio:.2f}", flush=True)
+              f"{e_cg.max():.2e} | worst e/(tol+{factor} e_cg) {ratio:.2f}", flush=True)
         assert np.all(np.isfinite(res[name]))
         assert ratio <= 1.0, f"{label} {name}: worst ratio {ratio:.2f}"
     return worst
@@ -187,6 +158,15 @@ def test_backward_without_cg_is_softmax_attention_gradient(torch, d):
     assert worst <= 1e-2
 
 
+# Recipes whose local fits nearly interpolate with a small ridge (prefixes
+# shorter than d, lambda 1e-2 and 1e-3): there the matrix-core backward's dk
+# is 11-19% off the exact gradient (dq and dv stay within 1e-2), and no
+# tolerance below is widened for it; test_backward_dk_small_lambda_matrix_cores
+# records that gap as an expected failure, and the fp32 vector path is checked
+# on the same recipes.
+SMALL_LAMBDA = {("standard", 384), ("recall", 256)}
+
+
 @pytest.mark.parametrize("name,n,T,tol,lam", [
     ("standard", 512, 16, 0.0, None),     # the benchmark's CG policy
     # worse conditioning with a budget that converges: the adjoint compounds
@@ -201,12 +181,39 @@ def test_backward_workload_recipes(torch, name, n, T, tol, lam):
     d = wl.d
     g = make_cotangent(1, 2, n, d, seed=11)
     res = run(torch, wl, g, T=T, tol=tol, lam=lam, adj=True)
-    check_grads(wl, g, res, [(0, 0), (0, 1)], range(n), 0, T, tol, lam, f"{name} n={n} lam={lam}")
+    which = ("dq", "dv") if (name, n) in SMALL_LAMBDA else ("dq", "dk", "dv")
+    check_grads(wl, g, res, [(0, 0), (0, 1)], range(n), 0, T, tol, lam, f"{name} n={n} lam={lam}",
+                which=which)
     it = res["adj_iters"]
     assert it.min() >= 0 and it.max() <= T
     if tol == 0.0:
         # a fixed budget: every query with a nonzero right-hand side runs it
         assert np.mean(it == T) > 0.9
+
+
+@pytest.mark.xfail(strict=True, reason="matrix-core dk is 11-19% off the exact gradient where "
+                   "the local fit nearly interpolates with lambda 1e-2 or 1e-3 (a known gap; the "
+                   "fp32 vector path is within the bar on the same recipes)")
+@pytest.mark.parametrize("name,n,T,tol,lam", [("standard", 384, 128, 1e-5, 1e-2),
+                                              ("recall", 256, 64, 1e-4, None)])
+def test_backward_dk_small_lambda_matrix_cores(torch, name, n, T, tol, lam):
+    wl = make_workload(name, n=n, B=1, H=2)
+    lam = wl.lam if lam is None else lam
+    g = make_cotangent(1, 2, n, wl.d, seed=11)
+    res = run(torch, wl, g, T=T, tol=tol, lam=lam)
+    check_grads(wl, g, res, [(0, 0), (0, 1)], range(n), 0, T, tol, lam,
+                f"{name} n={n} lam={lam} (dk, matrix cores)", which=("dk",))
+
+
+@pytest.mark.parametrize("name,n,T,tol,lam", [("standard", 384, 128, 1e-5, 1e-2),
+                                              ("recall", 256, 64, 1e-4, None)])
+def test_backward_small_lambda_vector_path(torch, name, n, T, tol, lam):
+    wl = make_workload(name, n=n, B=1, H=2)
+    lam = wl.lam if lam is None else lam
+    g = make_cotangent(1, 2, n, wl.d, seed=11)
+    res = run(torch, wl, g, T=T, tol=tol, lam=lam, kernel=lla.LLA_KERNEL_VALU)
+    check_grads(wl, g, res, [(0, 0), (0, 1)], range(n), 0, T, tol, lam,
+                f"{name} n={n} lam={lam} (vector path)", fp16_scores=False)
 
 
 def test_backward_full_size_standard(torch):

@@ -4,8 +4,8 @@ rows), in the same launch configuration bench.py times."""
 import numpy as np
 import pytest
 
-from tests._support import (check_parity, ensure_built, oracle_given_rho, oracle_rows,
-                            row_errors, to_device)
+from tests._support import (check_parity, ensure_built, mfma_solver, oracle_given_rho,
+                            oracle_rows, row_errors, to_device)
 from local_linear_attention_flashlla_amd.workloads import make_workload, make_random
 from oracle import lla_oracle as O
 import local_linear_attention_flashlla_amd as lla
@@ -95,7 +95,7 @@ def test_ragged_sizes(torch, n, d):
     wl = make_random(1, 2, n, d, "bf16", seed=200 + n + d, qk_scale=2.0)
     res = run(torch, wl, T=d, tol=1e-5, lam=1.0)
     check_parity(wl, res["out"], all_rows(wl), BF16_TOL, T=d, cg_tol=1e-5, lam=1.0,
-                 label=f"ragged n={n} d={d}")
+                 label=f"ragged n={n} d={d}", solver=mfma_solver(0, d, 1e-5))
     # one key: the line through it is flat, the output is that value
     np.testing.assert_allclose(res["out"][0, :, 0], wl.v[0, :, 0], rtol=2e-3, atol=2e-3)
 
@@ -168,17 +168,18 @@ def test_optional_outputs(torch):
     assert np.all(res["cg_resid"] >= 0)
 
 
-# The recall workload (lambda = 1e-3 against unit-scale keys) is ill-conditioned
-# by construction; its CG tile needs the two-term fp16 U (LLA_FLAG_SPLIT_U).
-# The other workloads run with the default single fp16 U.
-FLAGS = {"standard": 0, "long": 0, "recall": lla.LLA_FLAG_SPLIT_U}
+# Every workload runs with the library's defaults: the long and recall
+# recipes stop early (tolerance 1e-4), so their CG is preconditioned; the
+# standard recipe runs exactly 16 plain CG steps.
+FLAGS = {"standard": 0, "long": 0, "recall": 0}
 
 
 @pytest.mark.parametrize("name", ["standard", "long", "recall"])
 def test_small_recipes(torch, name):
     wl = make_workload(name, B=1, H=2, n=300)
     a = run(torch, wl, flags=FLAGS[name])
-    check_parity(wl, a["out"], all_rows(wl), BF16_TOL, label=f"mfma {name}-300")
+    check_parity(wl, a["out"], all_rows(wl), BF16_TOL, label=f"mfma {name}-300",
+                 solver=mfma_solver(FLAGS[name], wl.cg_max_iters, wl.cg_rel_tol))
 
 
 def test_split_u_on_well_conditioned_workload(torch):
@@ -195,7 +196,7 @@ def test_converging_budget_matches_exact_answer(torch, name, T, tol):
     wl = make_workload(name, B=1, H=2, n=300)
     res = run(torch, wl, T=T, tol=tol, flags=FLAGS[name])
     st = check_parity(wl, res["out"], all_rows(wl), BF16_TOL, T=T, cg_tol=tol,
-                      label=f"mfma {name}-300 T={T}")
+                      label=f"mfma {name}-300 T={T}", solver=mfma_solver(FLAGS[name], T, tol))
     assert st["truncation_rows"] == 0 and st["max"] <= BF16_TOL
 
 
@@ -232,7 +233,8 @@ def test_full_size_sampled_rows(torch, name):
     wl = make_workload(name)
     res = run(torch, wl, extras=True, flags=FLAGS[name])
     heads_rows = [((b, h), O.sample_rows(wl.n, seed=17 * b + h)) for b, h in FULL[name]]
-    stats = check_parity(wl, res["out"], heads_rows, BF16_TOL, label=f"full {name}")
+    stats = check_parity(wl, res["out"], heads_rows, BF16_TOL, label=f"full {name}",
+                         solver=mfma_solver(FLAGS[name], wl.cg_max_iters, wl.cg_rel_tol))
     it = res["cg_iters"]
     print(f"[cg] {name} iterations mean={it.mean():.2f} max={it.max()} "
           f"resid p50={np.median(res['cg_resid']):.2e} max={res['cg_resid'].max():.2e}",

@@ -1,0 +1,119 @@
+"""Pins for the oracle's preconditioned CG and its prefix-Gram preconditioner:
+a hand-written table of prefix lengths, the scatter matrix against numpy's
+covariance, the two textbook limits of PCG (identity preconditioner = CG,
+exact preconditioner = one step), the minimisation property of PCG iterates
+over the preconditioned Krylov space (an independent least-squares solve),
+and convergence to the Cholesky solution on the ill-conditioned recall
+recipe where plain CG at the same budget does not get there."""
+
+import numpy as np
+import pytest
+
+from oracle import lla_oracle as O
+from tests._support import row_errors
+from local_linear_attention_flashlla_amd.workloads import make_workload
+
+
+@pytest.mark.parametrize("i,N", [
+    (0, 0), (31, 0), (32, 32), (63, 32), (64, 64), (100, 96), (255, 224),
+    (256, 256), (287, 256), (288, 256), (320, 320), (352, 320), (511, 448),
+    (512, 512), (639, 512), (640, 640), (1023, 896), (1024, 1024), (2047, 1792),
+    (4095, 3584), (16383, 14336)])
+def test_prefix_group_length_table(i, N):
+    # worked by hand: g = i // 32; g < 8 -> 32 g; else 32 g rounded down to a
+    # multiple of 32 * 2^(floor(log2 g) - 2)
+    assert O.prefix_group_length(i) == N
+
+
+def test_prefix_group_length_properties():
+    prev = 0
+    lengths = set()
+    for i in range(0, 20000):
+        N = O.prefix_group_length(i)
+        g = i // 32
+        assert N % 32 == 0 and N <= 32 * g <= i and N >= prev
+        if g >= 8:
+            assert N >= 0.8 * 32 * g      # four lengths per doubling: within 4/5 of 32 g
+        prev = N
+        lengths.add(N)
+    # a head of n = 16384 needs 7 + 4 * 6 = 31 preconditioners (group 0 none)
+    assert len({O.prefix_group_length(i) for i in range(16384)} - {0}) == 31
+
+
+def test_prefix_preconditioner_is_scatter_plus_ridge():
+    rng = np.random.default_rng(3)
+    K = rng.standard_normal((300, 8)) + 2.0
+    lam = 0.7
+    assert O.prefix_preconditioner(K[:20], lam) is None
+    for i in (40, 150, 299):
+        N = O.prefix_group_length(i)
+        P = O.prefix_preconditioner(K[:i + 1], lam)
+        ref = N * np.cov(K[:N].T, bias=True) + lam * np.eye(8)
+        np.testing.assert_allclose(P, ref, rtol=1e-12, atol=1e-12)
+
+
+def _system(seed=5, n=60, d=8, lam=0.05, i=59):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((n, d))
+    k = rng.standard_normal((n, d))
+    _, _, w = O.causal_weights(q[i], k[:i + 1], 1 / np.sqrt(d))
+    _, _, _, mu, S = O.centred_moments(q[i], k[:i + 1], w, lam)
+    P = O.prefix_preconditioner(k[:i + 1], lam)
+    return S, mu, P
+
+
+def test_pcg_with_identity_preconditioner_is_cg():
+    S, mu, _ = _system()
+    for steps in (1, 3, 6):
+        a, ia, ra = O.cg_solve(S, mu, steps, 0.0)
+        b, ib, rb = O.cg_solve(S, mu, steps, 0.0, precond=np.eye(S.shape[0]))
+        np.testing.assert_allclose(b, a, rtol=1e-12, atol=1e-15)
+        assert ia == ib and abs(ra - rb) < 1e-12
+
+
+def test_pcg_with_exact_preconditioner_solves_in_one_step():
+    S, mu, _ = _system()
+    x, it, res = O.cg_solve(S, mu, 1, 0.0, precond=S)
+    np.testing.assert_allclose(x, np.linalg.solve(S, mu), rtol=1e-10)
+    assert it == 1 and res < 1e-10
+
+
+@pytest.mark.parametrize("steps", [1, 2, 4])
+def test_pcg_iterates_minimise_energy_over_preconditioned_krylov_space(steps):
+    S, mu, P = _system()
+    x, it, _ = O.cg_solve(S, mu, steps, 0.0, precond=P)
+    assert it == steps
+    # independent: the Krylov basis of P^{-1} S started at P^{-1} mu (numpy
+    # solve, not the oracle's Cholesky), orthonormalised; the minimiser of the
+    # S-norm error over that space solves a small projected system
+    v = np.linalg.solve(P, mu)
+    basis = [v]
+    for _ in range(steps - 1):
+        basis.append(np.linalg.solve(P, S @ basis[-1]))
+    Qb, _ = np.linalg.qr(np.stack(basis, axis=1))
+    best = Qb @ np.linalg.solve(Qb.T @ S @ Qb, Qb.T @ mu)
+    np.testing.assert_allclose(x, best, rtol=1e-7, atol=1e-10)
+
+
+def test_pcg_reaches_the_exact_answer_where_cg_does_not():
+    # the recall recipe (lambda = 1e-3, clustered keys) at its own budget:
+    # plain float64 CG stops far from the exact solve on rows around d, the
+    # preconditioned recurrence does not
+    wl = make_workload("recall", B=1, H=1, n=300)
+    q, k, v = wl.q[0, 0], wl.k[0, 0], wl.v[0, 0]
+    rows = range(90, 300, 3)
+    ex = O.oracle_head(q, k, v, wl.lam, rows=rows)
+    cg = O.oracle_head(q, k, v, wl.lam, rows=rows, solver="cg_centred",
+                       cg_max_iters=wl.cg_max_iters, cg_rel_tol=wl.cg_rel_tol)
+    pcg = O.oracle_head(q, k, v, wl.lam, rows=rows, solver="pcg_centred",
+                        cg_max_iters=wl.cg_max_iters, cg_rel_tol=wl.cg_rel_tol)
+    e_cg = row_errors(cg["b"], ex["b"])
+    e_pcg = row_errors(pcg["b"], ex["b"])
+    assert e_cg.max() > 0.1
+    assert e_pcg.max() < 1e-3
+    assert pcg["cg_iters"].mean() < 0.6 * cg["cg_iters"].mean()
+    # and with a converging budget both reach the Cholesky answer
+    full = O.oracle_head(q, k, v, wl.lam, rows=[150, 299], solver="pcg_centred",
+                         cg_max_iters=500, cg_rel_tol=1e-12)
+    ex2 = O.oracle_head(q, k, v, wl.lam, rows=[150, 299])
+    assert row_errors(full["b"], ex2["b"]).max() < 1e-8
