@@ -800,7 +800,7 @@ __global__ __launch_bounds__(NT) void bwd_keys(KeyParams P) {
   const int n = P.n;
   const int nkb = (n + 32 * NW - 1) / (32 * NW);
   int qb, bh;
-  block_coords(static_cast<int>(blockIdx.x), P.BH, nkb, &qb, &bh);
+  block_coords(static_cast<int>(blockIdx.x), P.BH, nkb, &qb, &bh, false);
   const int kb = nkb - 1 - qb;  // longest query range first
   const int KT = kb * NW + wave; // this wave's key tile
   const int kj = 32 * KT + ql;

@@ -414,11 +414,6 @@ struct MainParams {
   int nslots;
   int BH, n, nchunk, nblk;
   int nq32;          // 32-query groups per head in the state slabs
-  // Block selection of the CG kernel: first_only = 1 runs block 0 of every
-  // head (blockIdx.x = head); otherwise the usual order, skipping blocks
-  // below qb_from (those a first_only launch runs)
-  int first_only;
-  int qb_from;
   float lambda;
   int cg_max_iters;
   float cg_rel_tol;
@@ -445,13 +440,7 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
   const int n = P.n;
   const int nqb = (n + BQW - 1) / BQW;
   int qb, bh;
-  if (PHASE == 2 && P.first_only) {
-    qb = 0;
-    bh = static_cast<int>(blockIdx.x);
-  } else {
-    block_coords(static_cast<int>(blockIdx.x), P.BH, nqb, &qb, &bh);
-    if (PHASE == 2 && qb < P.qb_from) return;  // the whole workgroup, before any barrier
-  }
+  block_coords(static_cast<int>(blockIdx.x), P.BH, nqb, &qb, &bh);
   const int i0 = qb * BQW;
   const int kend = min(n, i0 + BQW);
   const int ntiles = (kend + BK - 1) / BK;
@@ -1586,25 +1575,12 @@ void launch_cg_variant(const MainParams& m, dim3 grid, bool pc, hipStream_t stre
     hipLaunchKernelGGL((lla_mfma_phase<D, 2, SPLIT, kNW2>), grid, dim3(64 * kNW2), 0, stream, m);
 }
 
-// The CG kernel. The first block of every head (its first 128 queries, the
-// only ones whose prefixes are shorter than d = 128 keys and whose local fit
-// can therefore nearly interpolate, where fp16 rounding of the CG tile
-// W * (K p) is amplified by 1 / lambda) always carries that tile in two fp16
-// terms, in a launch of its own; the other blocks do so with LLA_FLAG_SPLIT_U.
+// The CG kernel (the CG tile in two fp16 terms with LLA_FLAG_SPLIT_U).
 template <int D>
-hipError_t launch_cg(const FwdParams& p, MainParams m, bool pc, hipStream_t stream) {
-  const bool split = p.flags & LLA_FLAG_SPLIT_U;
-  if (!split) {
-    MainParams f = m;
-    f.first_only = 1;
-    launch_cg_variant<D, true>(f, dim3(static_cast<unsigned>(p.BH)), pc, stream);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    m.qb_from = 1;
-  }
-  if (split)
+hipError_t launch_cg(const FwdParams& p, const MainParams& m, bool pc, hipStream_t stream) {
+  if (p.flags & LLA_FLAG_SPLIT_U)
     launch_cg_variant<D, true>(m, grid_of(p, kNW2), pc, stream);
-  else if ((p.n + 32 * kNW2 - 1) / (32 * kNW2) > 1)
+  else
     launch_cg_variant<D, false>(m, grid_of(p, kNW2), pc, stream);
   return hipGetLastError();
 }

@@ -281,21 +281,47 @@ __device__ __forceinline__ void step_barrier() {
 }
 
 // Work order. Workgroups are handed to the eight XCDs (each with its own L2)
-// in turn: block b runs on XCD b % 8. When the head count divides by 8, each
-// XCD gets its own heads and walks them one after the other, every head's
+// in turn: block b runs on XCD b % 8. The first block of every head goes
+// first: its sweeps are short, but its queries (prefixes shorter than d, the
+// nearly interpolating fits) can take the most CG steps, which makes it the
+// latest to finish when it starts last. After those, when the head count
+// divides by 8, each XCD walks its own heads one after the other, every head's
 // query blocks longest causal prefix first, so the key tiles that an XCD's
-// workgroups stream are those of about one head at a time and stay in its L2.
-// Otherwise the order is longest prefix first across all heads.
+// workgroups stream are those of about one head at a time and stay in its L2;
+// otherwise the order is longest prefix first across all heads.
+// (first_block_first = false keeps the plain order, for a kernel whose
+// blocks are not query blocks.)
 constexpr int kXcds = 8;
-__device__ __forceinline__ void block_coords(int b, int BH, int nqb, int* qb, int* bh) {
+__device__ __forceinline__ void block_coords(int b, int BH, int nqb, int* qb, int* bh,
+                                             bool first_block_first = true) {
+  if (!first_block_first) {
+    if (BH % kXcds == 0) {
+      const int xcd = b % kXcds, j = b / kXcds;
+      *bh = xcd * (BH / kXcds) + j / nqb;
+      *qb = nqb - 1 - j % nqb;
+    } else {
+      *qb = nqb - 1 - b / BH;
+      *bh = b % BH;
+    }
+    return;
+  }
   if (BH % kXcds == 0) {
     const int xcd = b % kXcds, j = b / kXcds;
     const int heads_per_xcd = BH / kXcds;
-    *bh = xcd * heads_per_xcd + j / nqb;
-    *qb = nqb - 1 - j % nqb;
+    if (j < heads_per_xcd) {
+      *bh = xcd * heads_per_xcd + j;
+      *qb = 0;
+    } else {
+      const int jr = j - heads_per_xcd;  // nqb >= 2 here
+      *bh = xcd * heads_per_xcd + jr / (nqb - 1);
+      *qb = nqb - 1 - jr % (nqb - 1);
+    }
+  } else if (b < BH) {
+    *qb = 0;
+    *bh = b;
   } else {
-    *qb = nqb - 1 - b / BH;
-    *bh = b % BH;
+    *qb = nqb - 1 - (b - BH) / BH;
+    *bh = (b - BH) % BH;
   }
 }
 }  // namespace

@@ -20,8 +20,7 @@ Rounding modelled (every other operation is exact, i.e. float64):
     then omega and mu~ scaled by exp2(mref - m) with m the exact row max;
   * CG: direction d = fp16(p / sp) with sp a power of two, kbar rounded to
     fp16 as the expansion point, T = K d - kbar.d in fp32, U = fp16(w T)
-    (two fp16 terms for the first 128 queries of a head, or all with
-    split_u), Y = sum U k and sum U in fp32; exact line search
+    (or two fp16 terms), Y = sum U k and sum U in fp32; exact line search
     along d, Fletcher-Reeves beta; r, x, p held in fp32; the stop rule of
     lla.h;
   * output phase: rho in two fp16 terms, a / sA = w (1 - (k - kbar).rho) / sA
@@ -218,9 +217,7 @@ def model_head(q, k, v, lam, cg_max_iters, cg_rel_tol, rows=None, split_u=False,
     n = q.shape[0]
     rows = range(n) if rows is None else rows
     s, sv = head_scales(q, k, v) if scales is None else scales
-    # the kernel carries the CG tile in two fp16 terms for the first 128
-    # queries of every head, and for all of them with split_u
     res = [model_row(q[i], k[:i + 1], v[:i + 1], lam, cg_max_iters, cg_rel_tol, s, sv,
-                     split_u=split_u or i < 128, exact=exact,
+                     split_u=split_u, exact=exact,
                      precond=None if precond is None else precond(i)) for i in rows]
     return {key: np.array([r[key] for r in res]) for key in ("b", "rho_c", "iters")}
