@@ -180,46 +180,38 @@ __global__ __launch_bounds__(NT) void prep_convert(const uint16_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// Prefix-Gram preconditioner of slot `sl` of head `bh` (one workgroup each).
-// With N = 32 pc_group_of_slot(sl) leading keys in the scaled units of the key
-// tiles (s k_j, s the head's power-of-two scale) and m their plain mean,
+// Prefix-Gram preconditioners (preconditioned CG, see include/lla.h). Slot sl
+// of head bh holds the preconditioner of the first N = 32 pc_group_of_slot(sl)
+// keys, in the scaled units of the key tiles (s k_j, s the head's power-of-two
+// scale): with m their plain mean,
 //     P = sum_{j<N} (s k_j - s m)(s k_j - s m)^T + lambda s^2 I
-//       = G - t t^T / N + lambda s^2 I,   G = sum s^2 k_j k_j^T, t = sum s k_j,
-// G on the matrix cores from the transposed key tiles (fp16 keys, exact
-// products, fp32 sums; blocks on or above the diagonal only), then
-// M = P^{-1} by in-place Gauss-Jordan elimination in fp32 (no pivoting: P is
-// symmetric positive definite), each thread holding a (D/16) x (D/16) block in
-// registers and the pivot row and column broadcast through LDS, one barrier
-// per step. M is symmetrised, scaled by a power of two sM >= its largest
-// (diagonal) entry and stored as two fp16 terms, rows in order and columns
-// permuted inside 16-element chunks (the MFMA A operand of z = M r in the CG
-// kernel). A non-positive or non-finite pivot (P not positive definite in
-// fp32) stores sM = 0: the CG kernel then leaves those groups unpreconditioned.
+//       = G - t t^T / N + lambda s^2 I,   G = sum_{j<N} s^2 k_j k_j^T, t = sum_{j<N} s k_j.
+// Three kernels, each key tile read once:
+//   pc_gram    per slot: the Gram matrix and key sum of the slot's own keys
+//              (those past the previous slot's prefix), on the matrix cores
+//              (fp16 keys, exact products, fp32 sums; the blocks on or above
+//              the diagonal), into the slot's storage as fp32;
+//   pc_scan    per head: running sums over the slots, in place (each slot then
+//              holds G and t of its whole prefix);
+//   pc_invert  per slot: P, then M = P^{-1} by in-place Gauss-Jordan
+//              elimination in fp32 (no pivoting: P is symmetric positive
+//              definite), each thread holding a (D/16) x (D/16) block in
+//              registers and the pivot row and column broadcast through LDS,
+//              one barrier per step; M symmetrised, scaled by a power of two
+//              sM >= its largest (diagonal) entry and stored over the slot's
+//              Gram as two fp16 terms, rows in order and columns permuted
+//              inside 16-element chunks (the MFMA A operand of z = M r in the
+//              CG kernel). A non-positive or non-finite pivot (P not positive
+//              definite in fp32) stores sM = 0: the CG kernel then leaves
+//              those groups unpreconditioned.
 template <int D>
-__global__ __launch_bounds__(NT) void pc_build(const _Float16* __restrict__ kt,
-                                               const float* __restrict__ partial, int nchunk,
-                                               int nblk, int nslots, float lambda,
-                                               _Float16* __restrict__ pcm, float* __restrict__ pcs) {
+__global__ __launch_bounds__(NT) void pc_gram(const _Float16* __restrict__ kt, int nblk, int nslots,
+                                              float* __restrict__ gram, float* __restrict__ tsum_out) {
   constexpr int NMB = D / 32;
   constexpr int NBLK = NMB * (NMB + 1) / 2;  // 32 x 32 blocks on or above the diagonal
-  constexpr int EB = D / 16;                 // side of each thread's block of M
-  __shared__ float sA[D][D + 1];
-  __shared__ float sT[D];
-  __shared__ float sRow[2][D], sCol[2][D];
-  __shared__ float sRed[4];
   const int sl = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, ql = lane & 31, g = lane >> 5;
-  const int N = 32 * pc_group_of_slot(sl);
-  if (tid < 64) {
-    float a, b;
-    head_scales(partial, bh, nchunk, tid, &a, &b);
-    if (tid == 0) sRed[0] = a;
-  }
-  __syncthreads();
-  const float s = sRed[0];
-  const float lam_s = lambda * s * s;
-
-  // ---- G and t over the N keys (N / 32 whole tiles)
+  const int t0 = sl == 0 ? 0 : pc_group_of_slot(sl - 1), t1 = pc_group_of_slot(sl);  // key tiles
   const int b0 = (wave * NBLK + 3) / 4, b1 = ((wave + 1) * NBLK + 3) / 4;  // this wave's blocks
   static_assert(NBLK <= 12, "at most three blocks per wave");
   int ba[3], bb[3];
@@ -243,15 +235,15 @@ __global__ __launch_bounds__(NT) void pc_build(const _Float16* __restrict__ kt,
   #pragma unroll
   for (int rb = 0; rb < NMB; ++rb) tsum[rb] = 0.f;
   const _Float16* head = kt + static_cast<size_t>(bh) * nblk * BK * D;
-  const int ntl = N / BK;
-  for (int t = 0; t < ntl; ++t) {
-    half8 fr[NMB][2];
+  auto load = [&](int t, half8 (&fr)[NMB][2]) __attribute__((always_inline)) {
     #pragma unroll
     for (int rb = 0; rb < NMB; ++rb)
       #pragma unroll
       for (int h = 0; h < 2; ++h)
         fr[rb][h] = *reinterpret_cast<const half8*>(head + static_cast<size_t>(t) * BK * D +
                                                     ((2 * h + g) * D + 32 * rb + ql) * 8);
+  };
+  auto use = [&](const half8 (&fr)[NMB][2]) __attribute__((always_inline)) {
     #pragma unroll
     for (int x = 0; x < 3; ++x) {
       if (x < b1 - b0) {
@@ -267,63 +259,127 @@ __global__ __launch_bounds__(NT) void pc_build(const _Float16* __restrict__ kt,
         }
       }
     }
-    #pragma unroll
-    for (int rb = 0; rb < NMB; ++rb)
+    if (wave == 0) {
       #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int rb = 0; rb < NMB; ++rb)
         #pragma unroll
-        for (int c = 0; c < 8; ++c) tsum[rb] += static_cast<float>(fr[rb][h][c]);
-  }
-  if (wave == 0) {
-    #pragma unroll
-    for (int rb = 0; rb < NMB; ++rb) {
-      const float v = pair_sum(tsum[rb]);
-      if (g == 0) sT[32 * rb + ql] = v;
+        for (int h = 0; h < 2; ++h)
+          #pragma unroll
+          for (int c = 0; c < 8; ++c) tsum[rb] += static_cast<float>(fr[rb][h][c]);
     }
+  };
+  // tile loads one tile ahead of their products
+  half8 fa_[NMB][2], fb_[NMB][2];
+  if (t0 < t1) load(t0, fa_);
+  int t = t0;
+  for (; t + 1 < t1; t += 2) {
+    load(t + 1, fb_);
+    use(fa_);
+    if (t + 2 < t1) load(t + 2, fa_);
+    use(fb_);
   }
-  __syncthreads();
-  const float invN = 1.f / static_cast<float>(N);
+  if (t < t1) use(fa_);
+  float* G = gram + (static_cast<size_t>(bh) * nslots + sl) * D * D;
   #pragma unroll
   for (int x = 0; x < 3; ++x) {
     if (x < b1 - b0) {
       #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = 32 * ba[x] + 8 * (r >> 2) + 4 * g + (r & 3), col = 32 * bb[x] + ql;
-        float v = acc[x][r] - sT[row] * sT[col] * invN;
-        if (row == col) v += lam_s;
-        sA[row][col] = v;
-        sA[col][row] = v;
+        G[static_cast<size_t>(row) * D + col] = acc[x][r];
+        if (ba[x] != bb[x]) G[static_cast<size_t>(col) * D + row] = acc[x][r];
       }
     }
   }
-  __syncthreads();
+  if (wave == 0) {
+    #pragma unroll
+    for (int rb = 0; rb < NMB; ++rb) {
+      const float v = pair_sum(tsum[rb]);
+      if (g == 0) tsum_out[(static_cast<size_t>(bh) * nslots + sl) * D + 32 * rb + ql] = v;
+    }
+  }
+}
 
-  // ---- M = P^{-1}: Gauss-Jordan in place, thread block (br, bc)
+// Running sums over a head's slots, in place: thread e of block (c, bh)
+// handles element e of every slot's Gram matrix (e < D^2) or key sum.
+template <int D>
+__global__ __launch_bounds__(NT) void pc_scan(int nslots, float* __restrict__ gram,
+                                              float* __restrict__ tsum) {
+  const int bh = blockIdx.y;
+  const int e = blockIdx.x * NT + threadIdx.x;
+  if (e >= D * D + D) return;
+  float* base;
+  size_t stride;
+  if (e < D * D) {
+    base = gram + static_cast<size_t>(bh) * nslots * D * D + e;
+    stride = static_cast<size_t>(D) * D;
+  } else {
+    base = tsum + static_cast<size_t>(bh) * nslots * D + (e - D * D);
+    stride = D;
+  }
+  float a = 0.f;
+  for (int sl = 0; sl < nslots; ++sl) {
+    a += base[sl * stride];
+    base[sl * stride] = a;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(NT) void pc_invert(const float* __restrict__ partial, int nchunk,
+                                                int nslots, float lambda, float* __restrict__ gram,
+                                                const float* __restrict__ tsum,
+                                                float* __restrict__ pcs) {
+  constexpr int EB = D / 16;                 // side of each thread's block of M
+  __shared__ float sA[D][D + 1];
+  __shared__ float sT[D];
+  __shared__ float sRow[2][D], sCol[2][D];
+  __shared__ float sRed[4];
+  const int sl = blockIdx.x, bh = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int N = 32 * pc_group_of_slot(sl);
+  if (tid < 64) {
+    float a, b;
+    head_scales(partial, bh, nchunk, tid, &a, &b);
+    if (tid == 0) sRed[0] = a;
+  }
+  const size_t slot = static_cast<size_t>(bh) * nslots + sl;
+  if (tid < D) sT[tid] = tsum[slot * D + tid];
+  __syncthreads();
+  const float s = sRed[0];
+  const float lam_s = lambda * s * s;
+  const float invN = 1.f / static_cast<float>(N);
+  float* G = gram + slot * D * D;
   const int br = tid / 16, bc = tid % 16;
   float A[EB][EB];
   #pragma unroll
   for (int i = 0; i < EB; ++i)
     #pragma unroll
-    for (int j = 0; j < EB; ++j) A[i][j] = sA[EB * br + i][EB * bc + j];
+    for (int j = 0; j < EB; ++j) {
+      const int row = EB * br + i, col = EB * bc + j;
+      float v = G[static_cast<size_t>(row) * D + col] - sT[row] * sT[col] * invN;
+      if (row == col) v += lam_s;
+      A[i][j] = v;
+    }
+  // ---- M = P^{-1}: Gauss-Jordan in place, thread block (br, bc). Step k
+  // (k uniform over the workgroup, so every branch on kl below is uniform):
+  // the owners of row k and column k publish them; every element takes the
+  // rank-one update A -= A[:,k] A[k,:] / A[k,k], which leaves row k and
+  // column k at zero; their owners then write A[k,j] / p, -A[i,k] / p and
+  // 1 / p there.
   bool ok = true;
   for (int k = 0; k < D; ++k) {
     const int buf = k & 1, kb = k / EB, kl = k % EB;
-    if (br == kb) {
-      #pragma unroll
-      for (int j = 0; j < EB; ++j) {
-        float v = A[0][j];
-        #pragma unroll
-        for (int i = 1; i < EB; ++i) v = i == kl ? A[i][j] : v;
-        sRow[buf][EB * bc + j] = v;
-      }
-    }
-    if (bc == kb) {
-      #pragma unroll
-      for (int i = 0; i < EB; ++i) {
-        float v = A[i][0];
-        #pragma unroll
-        for (int j = 1; j < EB; ++j) v = j == kl ? A[i][j] : v;
-        sCol[buf][EB * br + i] = v;
+    #pragma unroll
+    for (int c = 0; c < EB; ++c) {
+      if (c == kl) {
+        if (br == kb) {
+          #pragma unroll
+          for (int j = 0; j < EB; ++j) sRow[buf][EB * bc + j] = A[c][j];
+        }
+        if (bc == kb) {
+          #pragma unroll
+          for (int i = 0; i < EB; ++i) sCol[buf][EB * br + i] = A[i][c];
+        }
       }
     }
     __syncthreads();
@@ -337,20 +393,28 @@ __global__ __launch_bounds__(NT) void pc_build(const _Float16* __restrict__ kt,
     #pragma unroll
     for (int j = 0; j < EB; ++j) rv[j] = sRow[buf][EB * bc + j];
     #pragma unroll
-    for (int i = 0; i < EB; ++i) cv[i] = sCol[buf][EB * br + i];
+    for (int i = 0; i < EB; ++i) cv[i] = sCol[buf][EB * br + i] * ip;
     #pragma unroll
-    for (int i = 0; i < EB; ++i) {
-      const float ci = cv[i] * ip;
+    for (int i = 0; i < EB; ++i)
       #pragma unroll
-      for (int j = 0; j < EB; ++j) {
-        const bool rk = br == kb && i == kl, ck = bc == kb && j == kl;
-        const float upd = fmaf(-ci, rv[j], A[i][j]);
-        A[i][j] = rk ? (ck ? ip : rv[j] * ip) : (ck ? -ci : upd);
+      for (int j = 0; j < EB; ++j) A[i][j] = fmaf(-cv[i], rv[j], A[i][j]);
+    #pragma unroll
+    for (int c = 0; c < EB; ++c) {
+      if (c == kl) {
+        if (br == kb) {
+          #pragma unroll
+          for (int j = 0; j < EB; ++j) A[c][j] = rv[j] * ip;
+        }
+        if (bc == kb) {
+          #pragma unroll
+          for (int i = 0; i < EB; ++i) A[i][c] = -cv[i];
+        }
+        if (br == kb && bc == kb) A[c][c] = ip;
       }
     }
   }
   __syncthreads();
-  // ---- symmetrise, scale, split into two fp16 terms, store
+  // ---- symmetrise, scale, split into two fp16 terms, store over the Gram
   if (ok) {
     #pragma unroll
     for (int i = 0; i < EB; ++i)
@@ -369,8 +433,10 @@ __global__ __launch_bounds__(NT) void pc_build(const _Float16* __restrict__ kt,
   for (int w = 1; w < (D + 63) / 64; ++w) mdiag = fmaxf(mdiag, sRed[w]);
   const bool good = ok && mdiag > 0.f && mdiag < INFINITY;
   const float sM = good ? pow2_ceil(mdiag) : 0.f;
-  const size_t base = (static_cast<size_t>(bh) * nslots + sl) * 2 * D * D;
   if (good) {
+    // (every thread has read its part of the Gram before the first barrier)
+    _Float16* hiM = reinterpret_cast<_Float16*>(G);
+    _Float16* loM = hiM + D * D;
     const float inv = 1.f / sM;
     #pragma unroll
     for (int i = 0; i < EB; ++i) {
@@ -382,12 +448,12 @@ __global__ __launch_bounds__(NT) void pc_build(const _Float16* __restrict__ kt,
         const _Float16 hi = static_cast<_Float16>(v);
         const _Float16 lo = static_cast<_Float16>(v - static_cast<float>(hi));
         const int pcol = (col & ~15) | swz16(col & 15);
-        pcm[base + static_cast<size_t>(row) * D + pcol] = hi;
-        pcm[base + static_cast<size_t>(D) * D + static_cast<size_t>(row) * D + pcol] = lo;
+        hiM[static_cast<size_t>(row) * D + pcol] = hi;
+        loM[static_cast<size_t>(row) * D + pcol] = lo;
       }
     }
   }
-  if (tid == 0) pcs[static_cast<size_t>(bh) * nslots + sl] = sM;
+  if (tid == 0) pcs[slot] = sM;
 }
 
 // ---------------------------------------------------------------------------
@@ -1558,8 +1624,16 @@ hipError_t launch_pc_build(const FwdParams& p, const Workspace& w, hipStream_t s
   const int nsl = pc_nslots(p.n);
   const int nchunk = (p.n + NORM_ROWS - 1) / NORM_ROWS;
   const int nblk = (p.n + BK - 1) / BK;
-  hipLaunchKernelGGL(pc_build<D>, dim3(nsl, p.BH), dim3(NT), 0, stream, w.kt, w.partial, nchunk, nblk,
-                     nsl, p.lambda, w.pcm, w.pcs);
+  float* gram = reinterpret_cast<float*>(w.pcm);  // each slot's 2 D^2 halfs hold D^2 floats
+  hipLaunchKernelGGL(pc_gram<D>, dim3(nsl, p.BH), dim3(NT), 0, stream, w.kt, nblk, nsl, gram, w.pct);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(pc_scan<D>, dim3((D * D + D + NT - 1) / NT, p.BH), dim3(NT), 0, stream, nsl, gram,
+                     w.pct);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(pc_invert<D>, dim3(nsl, p.BH), dim3(NT), 0, stream, w.partial, nchunk, nsl,
+                     p.lambda, gram, w.pct, w.pcs);
   return hipGetLastError();
 }
 
@@ -1665,7 +1739,8 @@ size_t mfma_workspace_bytes(int BH, int n, int d) {
          3 * align256(static_cast<size_t>(BH) * nqpad * d * sizeof(float)) +
          align256(static_cast<size_t>(BH) * nqpad * 4 * sizeof(float)) +
          align256(static_cast<size_t>(BH) * nsl * 2 * d * d * sizeof(_Float16)) +
-         align256(static_cast<size_t>(BH) * nsl * sizeof(float));
+         align256(static_cast<size_t>(BH) * nsl * sizeof(float)) +
+         align256(static_cast<size_t>(BH) * nsl * d * sizeof(float));
 }
 
 hipError_t launch_mfma(const FwdParams& p, hipStream_t stream) {

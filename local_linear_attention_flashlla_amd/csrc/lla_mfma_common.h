@@ -143,7 +143,9 @@ struct Workspace {
   float* rs;        // CG residuals, same layout
   float* qs;        // per query row max and omega: [blocks][4 waves][2][64 lanes]
   _Float16* pcm;    // [BH][nslots][2][D][D] preconditioners M / sM, hi and lo fp16 terms
+                    // (while they are built: the slots' fp32 Gram matrices, D x D)
   float* pcs;       // [BH][nslots] their power-of-two scales sM (0: not built)
+  float* pct;       // [BH][nslots][D] key sums of the slots' prefixes (build only)
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -176,6 +178,8 @@ Workspace carve(void* base, int BH, int n, int d) {
   w.pcm = reinterpret_cast<_Float16*>(p);
   p += align256(static_cast<size_t>(BH) * nsl * 2 * d * d * sizeof(_Float16));
   w.pcs = reinterpret_cast<float*>(p);
+  p += align256(static_cast<size_t>(BH) * nsl * sizeof(float));
+  w.pct = reinterpret_cast<float*>(p);
   return w;
 }
 

@@ -222,10 +222,11 @@ def _nslots(n):
 
 
 def _pc_bytes(BH, n, d):
-    """Workspace bytes of the preconditioners: a d x d matrix in two fp16 terms
-    and a float scale each (256-byte aligned regions): O(d^2 log n) per head."""
+    """Workspace bytes of the preconditioners: a d x d matrix in two fp16 terms,
+    a float scale and a d-float key sum each (256-byte aligned regions):
+    O(d^2 log n) per head."""
     al = lambda x: (x + 255) // 256 * 256
-    return al(BH * _nslots(n) * 2 * d * d * 2) + al(BH * _nslots(n) * 4)
+    return al(BH * _nslots(n) * 2 * d * d * 2) + al(BH * _nslots(n) * 4) + al(BH * _nslots(n) * d * 4)
 
 
 def test_workspace_sizes(lib):
