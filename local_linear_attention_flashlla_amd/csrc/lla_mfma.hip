@@ -1089,6 +1089,15 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
     const int tlast = ntiles - 1;
     half8 ua[2], ub[2], ula[2], ulb[2];
     floatx16 sa, ta, sb, tb;
+    // In the preconditioned solve, the first block of a head (qb = 0) carries
+    // U in two fp16 terms (hi + lo) whatever LLA_FLAG_SPLIT_U says: its
+    // queries' prefixes are at most 128 keys, near d, so their local fits can
+    // nearly interpolate, and with a small ridge (the regime a tolerance-driven
+    // solve is for) fp16 rounding of U there is amplified by about 1 / lambda.
+    // All its tiles are diagonal ones, so the choice (uniform over the
+    // workgroup) sits in the masked steps only. The fixed-budget plain solve
+    // is left as it is.
+    const bool first_block = PRECOND && qb == 0;
     // One step, written out in issue order: the tile copies, PF fragment
     // reads ahead, then for each of the NF matrix products of the step (the
     // NY of Y alternating with the NKS of [S; T]) its MFMA(s), the fragment
@@ -1146,7 +1155,11 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
           const int p = k >> 1;
           if (doY) {
             acc[p % NMB] = mfma(f, up[p / NMB], acc[p % NMB]);
-            if constexpr (SPLIT_U) acc[p % NMB] = mfma(f, ulp[p / NMB], acc[p % NMB]);
+            if constexpr (SPLIT_U) {
+              acc[p % NMB] = mfma(f, ulp[p / NMB], acc[p % NMB]);
+            } else if constexpr (MASKED) {
+              if (first_block) acc[p % NMB] = mfma(f, ulp[p / NMB], acc[p % NMB]);
+            }
           }
         } else {
           const int t = k >> 1;
@@ -1166,7 +1179,7 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
           }
           wv[r] = w;
           if (r & 1) {
-            if constexpr (SPLIT_U) {
+            if (SPLIT_U || (MASKED && first_block)) {
               const float u0 = wv[r - 1] * tc[r - 1], u1 = w * tc[r];
               const half2v hu = pack_sum(u0, u1, usum);
               const half2v lo = pack_sum(u0 - static_cast<float>(hu[0]), u1 - static_cast<float>(hu[1]), usum);
@@ -1216,7 +1229,7 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
       for (int k = 0; k < NY; ++k) {
         const half8 f = kt_frag_at(sKt3, k >> 1, k & 1);
         acc[k >> 1] = mfma(f, ub[k & 1], acc[k >> 1]);
-        if constexpr (SPLIT_U) acc[k >> 1] = mfma(f, ulb[k & 1], acc[k >> 1]);
+        if (SPLIT_U || first_block) acc[k >> 1] = mfma(f, ulb[k & 1], acc[k >> 1]);
       }
     }
     usum = pair_sum(usum);

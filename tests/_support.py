@@ -141,7 +141,7 @@ def mfma_solver(flags, T, tol):
 
 
 def check_parity(wl, out, heads_rows, tol, T=None, cg_tol=None, lam=None, label="",
-                 factor=4.0, solver="cg_centred"):
+                 factor=3.0, solver="cg_centred"):
     """Compare GPU rows with the float64 oracle.
 
     e_gpu = row error of the GPU output against the exact (Cholesky) oracle;
@@ -151,10 +151,11 @@ def check_parity(wl, out, heads_rows, tol, T=None, cg_tol=None, lam=None, label=
     CG budget reaches the exact answer in float64 (e_cg ~ 0) this is the plain
     tolerance. Where it does not (the CG budget, not the arithmetic, limits
     those rows: no arithmetic can match the exact answer there), the GPU must
-    stay as close as an unconverged CG iterate of another precision does;
-    float32 and fp16 emulations of the kernel's arithmetic running the same
-    algorithm land within 1.5x and 2.4x of the float64 iterate's error on the
-    hardest rows.
+    stay as close as an unconverged CG iterate of another precision does. The
+    numpy model of the kernel's rounding (tests/kernel_model.py) lands within
+    1.33 times the float64 iterate's error on every truncated row of the
+    standard recipe's fixed 16 steps (n = 300, and sampled rows at full size);
+    the factor 3 is over twice that.
     Returns a dict of statistics (also printed)."""
     T = wl.cg_max_iters if T is None else T
     cg_tol = wl.cg_rel_tol if cg_tol is None else cg_tol

@@ -20,7 +20,8 @@ Rounding modelled (every other operation is exact, i.e. float64):
     then omega and mu~ scaled by exp2(mref - m) with m the exact row max;
   * CG: direction d = fp16(p / sp) with sp a power of two, kbar rounded to
     fp16 as the expansion point, T = K d - kbar.d in fp32, U = fp16(w T)
-    (or two fp16 terms), Y = sum U k and sum U in fp32; exact line search
+    (two fp16 terms for the first 128 queries of a head when preconditioned,
+    and everywhere with split_u), Y = sum U k and sum U in fp32; exact line search
     along d, Fletcher-Reeves beta; r, x, p held in fp32; the stop rule of
     lla.h;
   * output phase: rho in two fp16 terms, a / sA = w (1 - (k - kbar).rho) / sA
@@ -84,11 +85,16 @@ def _apply_two_term(R, M, r):
 
 
 def model_row(q_i, K, V, lam, cg_max_iters, cg_rel_tol, s, sv, split_u=False, exact=False,
-              precond=None):
+              precond=None, first_block_split=None):
     """Row i of the causal forward (K, V: the prefix k_0..k_i, v_0..v_i) as
     the kernel computes it. ``precond``: None (plain CG) or the preconditioner
     matrix M (in input units, as the oracle defines it); it is rounded to fp32
-    and applied in two fp16 terms. Returns dict(b, rho_c, iters)."""
+    and applied in two fp16 terms. ``first_block_split``: whether the first
+    128 queries of a head carry U in two terms (the kernel does so in its
+    preconditioned mode, also on rows 0..31, which have no preconditioner;
+    default: whether ``precond`` is given). Returns dict(b, rho_c, iters)."""
+    if first_block_split is None:
+        first_block_split = precond is not None
     R = _R(exact)
     d = q_i.shape[0]
     ks = R.h(s * K)                                    # fp16 scaled keys
@@ -134,10 +140,11 @@ def model_row(q_i, K, V, lam, cg_max_iters, cg_rel_tol, s, sv, split_u=False, ex
         kbd = float(R.f(kb16 @ dv))
         T = R.f(ks @ dv - kbd)
         u = w * T
-        if split_u:
+        if split_u or (first_block_split and K.shape[0] <= 128):
+            # two fp16 terms: with split_u, and in the preconditioned mode in
+            # a head's first block of 128 queries (prefixes of at most 128 keys)
             uh = R.h(u)
-            ul = R.h(u - uh)
-            U = uh + ul
+            U = uh + R.h(u - uh)
         else:
             U = R.h(u)
         Y = R.f(U @ ks)
@@ -219,5 +226,6 @@ def model_head(q, k, v, lam, cg_max_iters, cg_rel_tol, rows=None, split_u=False,
     s, sv = head_scales(q, k, v) if scales is None else scales
     res = [model_row(q[i], k[:i + 1], v[:i + 1], lam, cg_max_iters, cg_rel_tol, s, sv,
                      split_u=split_u, exact=exact,
-                     precond=None if precond is None else precond(i)) for i in rows]
+                     precond=None if precond is None else precond(i),
+                     first_block_split=precond is not None) for i in rows]
     return {key: np.array([r[key] for r in res]) for key in ("b", "rho_c", "iters")}

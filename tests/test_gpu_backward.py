@@ -4,7 +4,7 @@ workload (sampled rows), in the launch configuration bench.py times.
 
 Each gradient row (dq per query; dk, dv per key) is compared by the relative
 row error of the forward's parity tests. Where the CG budget leaves the
-solves short of the exact answer, the bound is tol + 4 x the error of the
+solves short of the exact answer, the bound is tol + 3 x the error of the
 oracle's own float64 CG gradient (same iteration cap and stop rule on both
 the forward and the adjoint system) -- the same rule as the forward's.
 
@@ -75,7 +75,7 @@ def kernel_argmax(wl, b, h, rows):
     return js
 
 
-def check_grads(wl, g, res, heads, dq_rows, kv_from, T, tol, lam, label, factor=4.0, bar=None,
+def check_grads(wl, g, res, heads, dq_rows, kv_from, T, tol, lam, label, factor=3.0, bar=None,
                 fp16_scores=True, which=("dq", "dk", "dv")):
     """dq on rows dq_rows, dk/dv on keys kv_from..n-1 (the oracle then runs
     rows kv_from..n-1, which hold every contribution to those keys). The
