@@ -125,11 +125,17 @@ def cpu_baseline(wl, target_rows: int, seed: int = 0):
     wall = time.perf_counter() - t0
     cpu_s = sum(r[0] for r in res)
     nrows = sum(r[1] for r in res)
+    # rows are drawn uniformly, so rows / rate estimates the whole workload's
+    # time without bias (a row's cost grows with its prefix length)
+    full_s = B * H * n * wall / nrows
     return {
         "value": nrows / wall, "unit": "queries/s", "cores": cores, "kind": "oracle",
         "sample": (f"{nrows} rows drawn uniformly (seed {seed}) from the {B}x{H}x{n} rows of "
                    f"the workload; float64 Cholesky per row; {cpu_s:.1f} CPU-s over "
                    f"{wall:.1f} s wall"),
+        "full_config_s": full_s,
+        "full_config_note": (f"extrapolated, not run: all {B * H * n} rows at the sampled rate "
+                             f"on {cores} cores"),
     }
 
 

@@ -59,6 +59,20 @@
  *    computed for 32 queries at once, and 0 * NaN is NaN). On the
  *    matrix-core path an infinite input changes its head's power-of-two
  *    scale, and with it the whole head.
+ *  - Range on the matrix-core path: a head's keys take one power-of-two
+ *    scale s (largest key row norm to (64, 128]) and its values another;
+ *    both are then fp16. Queries enter the scores as q log2(e) / (sqrt(d) s)
+ *    in fp16. The scales absorb key row norms from about 2^-93 to 2^106 and
+ *    value rows of any bf16 magnitude. Within a head, key and value rows
+ *    down to about 2^-17 of the head's largest keep full fp16 precision;
+ *    smaller ones lose it gradually (fp16 subnormals; at 2^-20 the outputs
+ *    stay within 2e-2). Limits: the query operand
+ *    overflows when a query row norm times a key row norm exceeds about 2^25
+ *    (score differences beyond a million nats); and where the fit
+ *    extrapolates far outside its keys (|(k_j - kbar) . rho| >> 1, outputs
+ *    many times the size of the values) the output scan's single fp16 term
+ *    per weight loses the cancellation. The fp32 vector path has neither
+ *    limit.
  */
 #ifndef LLA_H
 #define LLA_H

@@ -565,14 +565,14 @@ __global__ __launch_bounds__(NT) void bwd_rows(RowsParams P) {
   const int qi = 32 * T + ql;
   const bool qvalid = qi < n;
   if (tid < 64) {
-    float a, b, mqk, mv;
+    float a, b, mk, mv, mq;
     head_scales(P.partial, bh, P.nchunk, tid, &a, &b);
-    head_maxima(P.partial, bh, P.nchunk, tid, &mqk, &mv);
+    head_maxima(P.partial, bh, P.nchunk, tid, &mk, &mv, &mq);
     if (tid == 0) {
       sScale[0] = a;
       sScale[1] = b;
-      sScale[2] = sqrtf(mqk);  // largest row norm of q and k together
-      sScale[3] = sqrtf(mv);   // and of v
+      sScale[2] = fmaxf(mk, mq);  // largest row norm of q and k together
+      sScale[3] = mv;             // and of v
     }
   }
   __syncthreads();
@@ -660,7 +660,7 @@ __global__ __launch_bounds__(NT) void bwd_rows(RowsParams P) {
   const float sy = pow2_ceil(pair_max(mxy));
   const float om = qst[64 + lane], m2 = qst[lane];
   const float tau = qvalid ? kap / om - yu : 0.f;
-  const float msum = -P.lambda * s * s * yx;
+  const float msum = -scaled_ridge(P.lambda, s) * yx;
   const float gvbar = gb + kap;
   // |dL/ds| <= (1 + 2 kmax |rho_c|)(2 |g| vmax / omega + 2 kmax |y|) + |tau|
   // (+ |msum| at the maximising key): the dq product's operand scale

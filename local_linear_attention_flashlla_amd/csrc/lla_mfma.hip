@@ -53,8 +53,10 @@ namespace lla {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Prepass 1: per (head, chunk of 256 rows) the largest squared row norm of q
-// and k together, and of v.
+// Prepass 1: per (head, chunk of 256 rows) the largest row norm of k, of v
+// and of q. A row's norm is formed as 2^e ||x 2^-e|| with 2^e above its
+// largest element, so that no square overflows or underflows fp32 for any
+// bf16 row (a norm past fp32's range comes out infinite).
 template <int D>
 __global__ __launch_bounds__(NT) void prep_norms(const uint16_t* __restrict__ q,
                                                  const uint16_t* __restrict__ k,
@@ -66,57 +68,65 @@ __global__ __launch_bounds__(NT) void prep_norms(const uint16_t* __restrict__ q,
   constexpr int RPI = NT / LPR;            // rows per workgroup pass
   const int bh = blockIdx.x, chunk = blockIdx.y;
   const int sub = threadIdx.x % LPR, rofs = threadIdx.x / LPR;
-  float mqk = 0.f, mv = 0.f;
+  float mx[3] = {0.f, 0.f, 0.f};           // k, v, q
   for (int r0 = 0; r0 < NORM_ROWS; r0 += RPI) {
     const int i = chunk * NORM_ROWS + r0 + rofs;
-    float sq = 0.f, sk = 0.f, sw = 0.f;
+    float x[3][8];
     if (i < n) {
       const size_t off = (static_cast<size_t>(bh) * n + i) * D + sub * 8;
-      const uint4 a = *reinterpret_cast<const uint4*>(q + off);
-      const uint4 b = *reinterpret_cast<const uint4*>(k + off);
-      const uint4 e = *reinterpret_cast<const uint4*>(v + off);
-      const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w},
-                     ev[4] = {e.x, e.y, e.z, e.w};
+      const uint4 a = *reinterpret_cast<const uint4*>(k + off);
+      const uint4 b = *reinterpret_cast<const uint4*>(v + off);
+      const uint4 c = *reinterpret_cast<const uint4*>(q + off);
+      const uint32_t w[3][4] = {{a.x, a.y, a.z, a.w}, {b.x, b.y, b.z, b.w}, {c.x, c.y, c.z, c.w}};
       #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        float x0 = bf16_to_f(av[u] & 0xffffu), x1 = bf16_to_f(av[u] >> 16);
-        sq += x0 * x0 + x1 * x1;
-        x0 = bf16_to_f(bv[u] & 0xffffu); x1 = bf16_to_f(bv[u] >> 16);
-        sk += x0 * x0 + x1 * x1;
-        x0 = bf16_to_f(ev[u] & 0xffffu); x1 = bf16_to_f(ev[u] >> 16);
-        sw += x0 * x0 + x1 * x1;
-      }
+      for (int t = 0; t < 3; ++t)
+        #pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          x[t][2 * u] = bf16_to_f(w[t][u] & 0xffffu);
+          x[t][2 * u + 1] = bf16_to_f(w[t][u] >> 16);
+        }
+    } else {
+      #pragma unroll
+      for (int t = 0; t < 3; ++t)
+        #pragma unroll
+        for (int e = 0; e < 8; ++e) x[t][e] = 0.f;
     }
-    // the row's sums: add across its LPR lanes
     #pragma unroll
-    for (int o = LPR / 2; o > 0; o >>= 1) {
-      sq += __shfl_xor(sq, o);
-      sk += __shfl_xor(sk, o);
-      sw += __shfl_xor(sw, o);
+    for (int t = 0; t < 3; ++t) {
+      float am = 0.f;
+      #pragma unroll
+      for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(x[t][e]));
+      #pragma unroll
+      for (int o = LPR / 2; o > 0; o >>= 1) am = fmaxf(am, __shfl_xor(am, o));
+      int ex = 0;
+      frexpf(am, &ex);                     // am < 2^ex (ex = 0 for a zero row)
+      float ss = 0.f;
+      #pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float y = ldexpf(x[t][e], -ex);
+        ss += y * y;
+      }
+      #pragma unroll
+      for (int o = LPR / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+      mx[t] = fmaxf(mx[t], ldexpf(sqrtf(ss), ex));
     }
-    mqk = fmaxf(mqk, fmaxf(sq, sk));
-    mv = fmaxf(mv, sw);
   }
-  for (int o = 32; o > 0; o >>= 1) {
-    mqk = fmaxf(mqk, __shfl_xor(mqk, o));
-    mv = fmaxf(mv, __shfl_xor(mv, o));
-  }
-  __shared__ float red[2][NT / 64];
+  #pragma unroll
+  for (int t = 0; t < 3; ++t)
+    for (int o = 32; o > 0; o >>= 1) mx[t] = fmaxf(mx[t], __shfl_xor(mx[t], o));
+  __shared__ float red[3][NT / 64];
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
-    red[0][wave] = mqk;
-    red[1][wave] = mv;
+    red[0][wave] = mx[0];
+    red[1][wave] = mx[1];
+    red[2][wave] = mx[2];
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    float a = red[0][0], b = red[1][0];
-    for (int w = 1; w < NT / 64; ++w) {
-      a = fmaxf(a, red[0][w]);
-      b = fmaxf(b, red[1][w]);
-    }
+  if (threadIdx.x < 3) {
+    float a = red[threadIdx.x][0];
+    for (int w = 1; w < NT / 64; ++w) a = fmaxf(a, red[threadIdx.x][w]);
     // a NaN/Inf input makes the scale meaningless but must not make it 0
-    partial[(static_cast<size_t>(bh) * nchunk + chunk) * 2 + 0] = a;
-    partial[(static_cast<size_t>(bh) * nchunk + chunk) * 2 + 1] = b;
+    partial[(static_cast<size_t>(bh) * nchunk + chunk) * 3 + threadIdx.x] = a;
   }
 }
 
@@ -346,7 +356,7 @@ __global__ __launch_bounds__(NT) void pc_invert(const float* __restrict__ partia
   if (tid < D) sT[tid] = tsum[slot * D + tid];
   __syncthreads();
   const float s = sRed[0];
-  const float lam_s = lambda * s * s;
+  const float lam_s = scaled_ridge(lambda, s);
   const float invN = 1.f / static_cast<float>(N);
   float* G = gram + slot * D * D;
   const int br = tid / 16, bc = tid % 16;
@@ -531,7 +541,7 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
   // keys a score tile comes out of the matrix cores in log2 units (no
   // per-element multiply before the exponential)
   const float qsc = kLog2e / sqrtf(static_cast<float>(D)) / s;
-  const float lam_s = P.lambda * s * s;
+  const float lam_s = scaled_ridge(P.lambda, s);
 
   // buffer resources over this head's key tiles (rows, transposed) and value tiles
   const size_t head_elems = static_cast<size_t>(P.nblk) * BK * D;
@@ -1678,7 +1688,7 @@ hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
   hipError_t e = launch_prep<D>(p, w, stream);
   if (e != hipSuccess) return e;
   const MainParams m = main_params<D>(p, w);
-  const dim3 grid1 = grid_of(p, kNW13), grid2 = grid_of(p, kNW2);
+  const dim3 grid1 = grid_of(p, kNW13);
   // three kernels, one per phase, sharing the block order and per-query state
   // slabs: moments, conjugate gradient (timed by the optional events), output
   hipLaunchKernelGGL((lla_mfma_phase<D, 1, false, kNW13>), grid1, dim3(64 * kNW13), 0, stream, m);
@@ -1747,7 +1757,7 @@ size_t mfma_workspace_bytes(int BH, int n, int d) {
   const size_t npad = static_cast<size_t>((n + BK - 1) / BK) * BK;
   const size_t nqpad = static_cast<size_t>((n + kMaxBQ - 1) / kMaxBQ) * kMaxBQ;
   const size_t nsl = static_cast<size_t>(pc_nslots(n));
-  return align256(static_cast<size_t>(BH) * nchunk * 2 * sizeof(float)) +
+  return align256(static_cast<size_t>(BH) * nchunk * 3 * sizeof(float)) +
          3 * align256(static_cast<size_t>(BH) * npad * d * sizeof(_Float16)) +
          3 * align256(static_cast<size_t>(BH) * nqpad * d * sizeof(float)) +
          align256(static_cast<size_t>(BH) * nqpad * 4 * sizeof(float)) +

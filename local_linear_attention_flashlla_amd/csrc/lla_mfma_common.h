@@ -134,7 +134,7 @@ inline int pc_nslots(int n) {
 }
 
 struct Workspace {
-  float* partial;   // [BH][nchunk][2]: max row ||.||^2 of q and k; of v
+  float* partial;   // [BH][nchunk][3]: largest row norm of k, of v, of q
   _Float16* kr;     // [BH][npad][D]      s k, d index permuted by swz16
   _Float16* kt;     // [BH][npad/32][D][32] s k transposed, key index permuted
   _Float16* vt;     // [BH][npad/32][D][32] sv v transposed, key index permuted
@@ -156,7 +156,7 @@ Workspace carve(void* base, int BH, int n, int d) {
   char* p = static_cast<char*>(base);
   Workspace w;
   w.partial = reinterpret_cast<float*>(p);
-  p += align256(static_cast<size_t>(BH) * nchunk * 2 * sizeof(float));
+  p += align256(static_cast<size_t>(BH) * nchunk * 3 * sizeof(float));
   const size_t t = align256(static_cast<size_t>(BH) * npad * d * sizeof(_Float16));
   w.kr = reinterpret_cast<_Float16*>(p);
   p += t;
@@ -183,29 +183,48 @@ Workspace carve(void* base, int BH, int n, int d) {
   return w;
 }
 
-// Largest squared row norms of one head (q and k together, and v) from its
-// chunk partials. Called by every lane of one wave: each lane takes every
-// 64th chunk, then a 64-lane maximum; every lane gets the result.
+// Largest row norms of one head (of k, of v and of q) from its chunk
+// partials. Called by every lane of one wave: each lane takes every 64th
+// chunk, then a 64-lane maximum; every lane gets the results.
 __device__ __forceinline__ void head_maxima(const float* partial, int bh, int nchunk, int lane,
-                                            float* mqk, float* mv) {
-  float a = 0.f, b = 0.f;
-  for (int c = lane; c < nchunk; c += 64) {
-    a = fmaxf(a, partial[(static_cast<size_t>(bh) * nchunk + c) * 2 + 0]);
-    b = fmaxf(b, partial[(static_cast<size_t>(bh) * nchunk + c) * 2 + 1]);
+                                            float* mk, float* mv, float* mq) {
+  float a = 0.f, b = 0.f, c = 0.f;
+  for (int ch = lane; ch < nchunk; ch += 64) {
+    const float* pr = partial + (static_cast<size_t>(bh) * nchunk + ch) * 3;
+    a = fmaxf(a, pr[0]);
+    b = fmaxf(b, pr[1]);
+    c = fmaxf(c, pr[2]);
   }
-  *mqk = wave_max(a);
+  *mk = wave_max(a);
   *mv = wave_max(b);
+  *mq = wave_max(c);
 }
 
-// Per-head power-of-two scales s (q, k) and sv (v) that bring the largest
-// row norm to at most kRowNormCap; called by every lane of one wave.
+// Per-head power-of-two scales s (keys) and sv (values) that bring the
+// largest key row norm and the largest value row norm to (64, 128]. The keys
+// alone set s: the fit's geometry lives in the keys, which then keep fp16's
+// full precision down to rows about 2^-17 of the largest. Queries enter the
+// matrix products only as q log2(e) / (sqrt(d) s), whose fp16 rounding error
+// is absolute and meets keys of norm at most 128, so small query rows cost
+// nothing; the operand overflows fp16 only when a query and a key row norm
+// multiply to more than about 2^25 (scores beyond a million nats). Called
+// by every lane of one wave.
 __device__ __forceinline__ void head_scales(const float* partial, int bh, int nchunk, int lane,
                                             float* s, float* sv) {
-  float mqk, mv;
-  head_maxima(partial, bh, nchunk, lane, &mqk, &mv);
-  const float a = sqrtf(mqk), b = sqrtf(mv);
-  *s = a > 0.f ? fminf(fmaxf(pow2_floor(kRowNormCap / a), 0x1p-60f), 0x1p60f) : 1.f;
-  *sv = b > 0.f ? fminf(fmaxf(pow2_floor(kRowNormCap / b), 0x1p-60f), 0x1p60f) : 1.f;
+  float a, b, mq;
+  head_maxima(partial, bh, nchunk, lane, &a, &b, &mq);
+  // bounds: any bf16 value row fits (sv only ever divides out); s stays
+  // where 1 / s and s^2-scaled sums are finite fp32
+  *s = a > 0.f ? fminf(fmaxf(pow2_floor(kRowNormCap / a), 0x1p-100f), 0x1p100f) : 1.f;
+  *sv = b > 0.f ? fminf(fmaxf(pow2_floor(kRowNormCap / b), 0x1p-120f), 0x1p120f) : 1.f;
+}
+
+// The ridge in key-scaled units, lambda s^2, held below 2^100: keys scaled to
+// norms of at most 128 make the fit's own terms tiny next to that, so
+// clamping changes rho by far less than fp32 resolves (rho ~ 0 either way)
+// while an infinite ridge would turn the CG step into 0 * inf.
+__device__ __forceinline__ float scaled_ridge(float lambda, float s) {
+  return fminf(lambda * s * s, 0x1p100f);
 }
 
 // Buffer resource over `bytes` bytes at `base` (raw, untyped; reads past the

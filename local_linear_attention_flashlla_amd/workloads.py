@@ -44,6 +44,7 @@ __all__ = [
     "Workload",
     "WORKLOADS",
     "make_workload",
+    "make_scaled",
     "f64_to_bf16_bits",
     "bf16_bits_to_f64",
 ]
@@ -220,6 +221,36 @@ def make_random(B: int, H: int, n: int, d: int, dtype: str = "f32",
             if ramp is not None:
                 k[b, h] *= ramp[:, None]
     spec = Spec("random", B, H, n, d, dtype, 1.0, 16, 0.0)
+    if dtype == "f32":
+        dev = [x.astype(np.float32) for x in (q, k, v)]
+        exact = [x.astype(np.float64) for x in dev]
+    else:
+        dev = [f64_to_bf16_bits(x) for x in (q, k, v)]
+        exact = [bf16_bits_to_f64(x) for x in dev]
+    return Workload(spec, B, H, n, d, *exact, *dev)
+
+
+def make_scaled(B: int, H: int, n: int, d: int, dtype: str = "bf16", seed: int = 0,
+                span_log2: float = 0.0, log2_q: int = 0, log2_k: int = 0, log2_v: int = 0,
+                lam: float = 1.0, qk_scale: float = 2.0) -> Workload:
+    """Inputs with widely varying magnitudes, for range tests: Gaussian q,k,v
+    as in ``make_random`` (q,k unit rows times ``qk_scale``); then every row of
+    q, k and v is multiplied by its own 2^u, u ~ U(-span_log2, 0) (drawn per
+    head after its q,k,v, in the order q rows, k rows, v rows), and the whole
+    of q, k, v by 2^log2_q, 2^log2_k, 2^log2_v. ``lam`` is the ridge the
+    workload is run with (scale it by 4^log2_k to keep the fit's balance)."""
+    rng = np.random.default_rng(seed)
+    q = np.empty((B, H, n, d))
+    k = np.empty((B, H, n, d))
+    v = np.empty((B, H, n, d))
+    for b in range(B):
+        for h in range(H):
+            qh, kh, vh = _head_gaussian(rng, n, d, qk_scale)
+            rows = 2.0 ** rng.uniform(-span_log2, 0.0, size=(3, n, 1))
+            q[b, h] = qh * rows[0] * 2.0 ** log2_q
+            k[b, h] = kh * rows[1] * 2.0 ** log2_k
+            v[b, h] = vh * rows[2] * 2.0 ** log2_v
+    spec = Spec("scaled", B, H, n, d, dtype, lam, 16, 0.0)
     if dtype == "f32":
         dev = [x.astype(np.float32) for x in (q, k, v)]
         exact = [x.astype(np.float64) for x in dev]

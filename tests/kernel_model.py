@@ -12,7 +12,8 @@ iterate, so that the GPU parity tests' allowance for unconverged rows and the
 CG-iterate tolerances are derived from data rather than chosen to pass.
 
 Rounding modelled (every other operation is exact, i.e. float64):
-  * keys, values: s k and sv v in fp16 (exact for bf16 inputs in range);
+  * keys, values: s k and sv v in fp16, s and sv powers of two from the
+    head's largest key and value row norms (exact for bf16 inputs in range);
   * the query operand: fp16(q log2(e) / (sqrt(d) s)), so scores come out in
     log2 units; score sums rounded to fp32;
   * moment phase: weights exp2(S - mref) rounded to fp16 against a reference
@@ -61,9 +62,10 @@ class _R:
 
 
 def head_scales(q_head, k_head, v_head):
-    """Power-of-two scales s (q and k) and sv (v) that bring the head's largest
-    row norm to at most 128."""
-    a = max(np.linalg.norm(q_head, axis=-1).max(), np.linalg.norm(k_head, axis=-1).max())
+    """Power-of-two scales s (keys; queries enter as q / s) and sv (values)
+    that bring the head's largest key row norm and largest value row norm to
+    at most 128."""
+    a = np.linalg.norm(k_head, axis=-1).max()
     b = np.linalg.norm(v_head, axis=-1).max()
     s = _pow2_floor(ROW_NORM_CAP / a) if a > 0 else 1.0
     sv = _pow2_floor(ROW_NORM_CAP / b) if b > 0 else 1.0
