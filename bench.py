@@ -141,42 +141,70 @@ def cpu_baseline(wl, target_rows: int, seed: int = 0):
 
 def memory_curve(torch, lla, dev, ns=(1024, 2048, 4096, 8192, 16384), B=1, H=16, d=128):
     """Peak device memory of one forward at the long-sequence shape (B=1, H=16,
-    d=128, bf16) for n = 1k .. 16k: inputs, output and workspace, all allocated
-    here through torch (the library allocates nothing when it is handed a
-    workspace). Working memory linear in n shows as a constant peak per row."""
-    rows = []
-    for n in ns:
-        torch.cuda.synchronize(dev)
-        torch.cuda.empty_cache()
-        base = torch.cuda.memory_allocated(dev)
-        gen = torch.Generator(device=dev)
-        gen.manual_seed(n)
-        qkv = []
-        for _ in range(3):
-            x = torch.randn((B, H, n, d), device=dev, generator=gen, dtype=torch.float32)
-            qkv.append(x.to(torch.bfloat16))
-            del x
-        q, k, v = qkv
-        q /= q.float().norm(dim=-1, keepdim=True).to(torch.bfloat16)
-        k /= k.float().norm(dim=-1, keepdim=True).to(torch.bfloat16)
-        torch.cuda.synchronize(dev)
-        torch.cuda.reset_peak_memory_stats(dev)
-        ws_bytes = lla.workspace_bytes(B, H, n, d, "bf16", lla.LLA_KERNEL_MFMA)
-        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-        out = torch.empty((B, H, n, d), dtype=torch.float32, device=dev)
-        lla.forward(q, k, v, 1.0, 2, 0.0, out=out, workspace=ws, kernel=lla.LLA_KERNEL_MFMA)
-        torch.cuda.synchronize(dev)
-        peak = torch.cuda.max_memory_allocated(dev) - base
-        io = 3 * B * H * n * d * 2 + B * H * n * d * 4
-        rows.append({"n": n, "peak_bytes": int(peak), "workspace_bytes": int(ws_bytes),
-                     "inputs_outputs_bytes": int(io),
-                     "peak_bytes_per_row": peak / (B * H * n),
-                     "workspace_bytes_per_row": ws_bytes / (B * H * n)})
-        del q, k, v, ws, out, qkv
+    d=128, bf16) for n = 1k .. 16k, on two paths: the blocked matrix-core
+    forward and the naive one (pairwise differences z_ij and moment matrices
+    Sigma_i materialised; lla_forward_naive). Inputs, output and workspace are
+    all allocated here through torch (the library allocates nothing when it
+    is handed a workspace). Working memory linear in n shows as a constant
+    peak per row; the naive path's grows with n. A naive size whose workspace
+    does not fit in the device's free memory is reported from the size query
+    alone, not run. Each point also carries the time of that one forward."""
+    free_total = torch.cuda.mem_get_info(dev)
+    curves = {}
+    for path in ("blocked", "naive"):
+        rows = []
+        for n in ns:
+            io = 3 * B * H * n * d * 2 + B * H * n * d * 4
+            if path == "naive":
+                ws_bytes = lla.naive_workspace_bytes(B, H, n, d, "bf16")
+            else:
+                ws_bytes = lla.workspace_bytes(B, H, n, d, "bf16", lla.LLA_KERNEL_MFMA)
+            torch.cuda.synchronize(dev)
+            torch.cuda.empty_cache()
+            if ws_bytes == 0 or ws_bytes + io > 0.9 * torch.cuda.mem_get_info(dev)[0]:
+                rows.append({"n": n, "run": False, "workspace_bytes": int(ws_bytes),
+                             "inputs_outputs_bytes": int(io),
+                             "note": "workspace does not fit in free device memory"})
+                continue
+            base = torch.cuda.memory_allocated(dev)
+            gen = torch.Generator(device=dev)
+            gen.manual_seed(n)
+            qkv = []
+            for _ in range(3):
+                x = torch.randn((B, H, n, d), device=dev, generator=gen, dtype=torch.float32)
+                qkv.append(x.to(torch.bfloat16))
+                del x
+            q, k, v = qkv
+            q /= q.float().norm(dim=-1, keepdim=True).to(torch.bfloat16)
+            k /= k.float().norm(dim=-1, keepdim=True).to(torch.bfloat16)
+            torch.cuda.synchronize(dev)
+            torch.cuda.reset_peak_memory_stats(dev)
+            ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+            out = torch.empty((B, H, n, d), dtype=torch.float32, device=dev)
+            t0 = time.perf_counter()
+            if path == "naive":
+                lla.forward(q, k, v, 1.0, 0, 0.0, out=out, workspace=ws, naive=True)
+            else:
+                lla.forward(q, k, v, 1.0, 2, 0.0, out=out, workspace=ws, kernel=lla.LLA_KERNEL_MFMA)
+            torch.cuda.synchronize(dev)
+            ms = (time.perf_counter() - t0) * 1e3
+            peak = torch.cuda.max_memory_allocated(dev) - base
+            rows.append({"n": n, "run": True, "peak_bytes": int(peak), "workspace_bytes": int(ws_bytes),
+                         "inputs_outputs_bytes": int(io),
+                         "peak_bytes_per_row": peak / (B * H * n),
+                         "workspace_bytes_per_row": ws_bytes / (B * H * n),
+                         "forward_ms": ms})
+            print(f"[memory] {path} n={n} peak {peak / 2**30:.3f} GiB ({ms:.1f} ms)",
+                  file=sys.stderr, flush=True)
+            del q, k, v, ws, out, qkv
+        curves[path] = rows
     return {"metric": "peak device memory of one forward vs n", "unit": "bytes",
             "config": {"workload": "long-sequence shape", "B": B, "H": H, "d": d,
-                       "dtype": "bf16", "kernel": "mfma"},
-            "data": "synthetic", "rows": rows}
+                       "dtype": "bf16",
+                       "blocked": "matrix-core forward, 2 CG steps",
+                       "naive": "lla_forward_naive (exact solve)"},
+            "device_memory_bytes": int(free_total[1]),
+            "data": "synthetic", "curves": curves}
 
 
 def bench_given_rho(args, torch, lla, wl, q, k, v, out, ws, kernel, kernel_used):
@@ -432,7 +460,7 @@ def main(argv=None):
                          "instead of the forward")
     ap.add_argument("--memory-curve", action="store_true",
                     help="instead of timing, print the peak device memory of one forward at "
-                         "n = 1k .. 16k (B=1, H=16, d=128) as one JSON line")
+                         "n = 1k .. 16k (B=1, H=16, d=128), blocked and naive, as one JSON line")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:

@@ -219,6 +219,26 @@ int lla_forward_ex(const lla_fwd_args* args, hipStream_t stream);
    rho far from the solution. */
 int lla_output_given_rho(const lla_fwd_args* args, const float* rho_in, hipStream_t stream);
 
+/* The naive forward: the same out_i (Eqs. (6)-(8) of the reading notes'
+   section 2.1), evaluated the way that page's section 2.2 describes a direct
+   implementation, as the comparison point of its peak-memory figure (Fig. 2,
+   FlashLLA against the naive form at d = 128): every pairwise difference
+   z_ij = k_j - q_i (Theta(n^2 d) per head) and every moment matrix Sigma_i
+   (Theta(n d^2)) are materialised in the workspace, and each
+   Sigma_i rho_i = mu_i is solved exactly by Cholesky. fp32 arithmetic
+   throughout (fp32 or bf16 inputs, d in {16, 32, 64, 128}); no CG, so
+   cg_max_iters and cg_rel_tol are ignored and cg_iters / cg_resid (if
+   requested) are written 0; omega, rho (the pages' rho_i) and rowmax are
+   available. kernel must be LLA_KERNEL_AUTO, flags 0 and rho_c NULL
+   (LLA_ERR_INVALID_ARG otherwise); n <= 2^16 and B*H <= 65535
+   (LLA_ERR_UNSUPPORTED). Workspace: lla_naive_workspace_bytes, about
+   4 B*H*n^2*(d + 1) bytes; NULL = allocated and freed stream-ordered. The
+   events bracket the moment kernel. Returns LLA_OK or a negative status. */
+int lla_forward_naive(const lla_fwd_args* args, hipStream_t stream);
+
+/* Workspace bytes of lla_forward_naive; 0 for sizes it rejects. */
+size_t lla_naive_workspace_bytes(int B, int H, int n, int d, int dtype);
+
 /* Device workspace bytes lla_forward_ex (or lla_output_given_rho) needs for
    these sizes and this kernel choice (LLA_KERNEL_*; the matrix-core path needs
    a workspace linear in B*H*n, the vector path none, and AUTO resolves as in

@@ -15,7 +15,8 @@ from ._lib import (LLA_DTYPE_BF16, LLA_DTYPE_F32, LLA_FLAG_NO_PRECOND, LLA_FLAG_
                    LLA_FLAG_SPLIT_U, LLA_KERNEL_AUTO,
                    LLA_KERNEL_MFMA, LLA_KERNEL_VALU, LlaError)
 
-__all__ = ["forward", "decode", "decode_workspace_bytes", "workspace_bytes", "LlaError", "LLA_KERNEL_AUTO", "LLA_KERNEL_VALU",
+__all__ = ["forward", "decode", "decode_workspace_bytes", "workspace_bytes", "naive_workspace_bytes",
+           "LlaError", "LLA_KERNEL_AUTO", "LLA_KERNEL_VALU",
            "LLA_KERNEL_MFMA", "LLA_FLAG_SPLIT_U", "LLA_FLAG_PRECOND", "LLA_FLAG_NO_PRECOND", "version"]
 
 
@@ -29,6 +30,13 @@ def workspace_bytes(B: int, H: int, n: int, d: int, dtype: str = "bf16",
     return int(_lib.load().lla_workspace_bytes(B, H, n, d, dt, kernel))
 
 
+def naive_workspace_bytes(B: int, H: int, n: int, d: int, dtype: str = "bf16") -> int:
+    """Workspace of the naive forward (``forward(..., naive=True)``): the
+    pairwise differences and moment matrices it materialises."""
+    dt = LLA_DTYPE_BF16 if dtype == "bf16" else LLA_DTYPE_F32
+    return int(_lib.load().lla_naive_workspace_bytes(B, H, n, d, dt))
+
+
 def _ptr(t) -> int:
     return 0 if t is None else int(t.data_ptr())
 
@@ -36,7 +44,7 @@ def _ptr(t) -> int:
 def forward(q, k, v, lam: float, cg_max_iters: int, cg_rel_tol: float, *,
             out=None, omega=None, rho=None, rowmax=None, cg_iters=None, cg_resid=None, rho_c=None,
             workspace=None, kernel: int = LLA_KERNEL_AUTO, flags: int = 0, stream=None,
-            events=None, rho_in=None):
+            events=None, rho_in=None, naive: bool = False):
     """Causal LLA forward on the GPU.
 
     q, k, v: contiguous [B, H, n, d] tensors on a HIP device, all float32 or all
@@ -53,6 +61,9 @@ def forward(q, k, v, lam: float, cg_max_iters: int, cg_rel_tol: float, *,
     solve is skipped and ``out`` is Eq. (8) with this rho_i
     (``lla_output_given_rho``); ``lam``, ``cg_max_iters`` and ``cg_rel_tol``
     are then passed through but do not change the result.
+    ``naive``: run ``lla_forward_naive`` instead (pairwise differences and
+    moment matrices materialised, exact Cholesky solves, fp32; CG settings
+    ignored, ``workspace`` sized by ``naive_workspace_bytes``).
     """
     import torch
 
@@ -107,7 +118,11 @@ def forward(q, k, v, lam: float, cg_max_iters: int, cg_rel_tol: float, *,
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     import ctypes
-    if rho_in is not None:
+    if naive:
+        if rho_in is not None:
+            raise ValueError("naive and rho_in do not combine")
+        st = _lib.load().lla_forward_naive(ctypes.byref(a), ctypes.c_void_p(handle))
+    elif rho_in is not None:
         if (rho_in.dtype != torch.float32 or tuple(rho_in.shape) != (B, H, n, d)
                 or not rho_in.is_contiguous() or not rho_in.is_cuda):
             raise ValueError(f"rho_in must be a contiguous float32 GPU tensor of shape {(B, H, n, d)}")

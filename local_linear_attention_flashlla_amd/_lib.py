@@ -35,7 +35,7 @@ EXPORTED_SYMBOLS = (
     "lla_forward_f32", "lla_forward_bf16", "lla_forward_ex", "lla_output_given_rho",
     "lla_workspace_bytes", "lla_decode_ex", "lla_decode_workspace_bytes",
     "lla_backward_ex", "lla_backward_workspace_bytes", "lla_status_string", "lla_last_error", "lla_version",
-    "lla_source_hash", "lla_decode_noalloc",
+    "lla_source_hash", "lla_decode_noalloc", "lla_forward_naive", "lla_naive_workspace_bytes",
 )
 
 LLA_DECODE_NOALLOC_SCRATCH_BYTES = 64 << 20
@@ -158,6 +158,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.lla_forward_ex.restype = ci
     lib.lla_output_given_rho.argtypes = [ctypes.POINTER(LlaFwdArgs), vp, vp]
     lib.lla_output_given_rho.restype = ci
+    lib.lla_forward_naive.argtypes = [ctypes.POINTER(LlaFwdArgs), vp]
+    lib.lla_forward_naive.restype = ci
+    lib.lla_naive_workspace_bytes.argtypes = [ci, ci, ci, ci, ci]
+    lib.lla_naive_workspace_bytes.restype = cz
     lib.lla_decode_ex.argtypes = [ctypes.POINTER(LlaDecodeArgs), vp]
     lib.lla_decode_ex.restype = ci
     lib.lla_decode_noalloc.argtypes = [ctypes.POINTER(LlaDecodeArgs), vp]

@@ -19,7 +19,8 @@ LIB_NAME = "liblla.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 ARCH = os.environ.get("LLA_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["lla_api.hip", "lla_valu.hip", "lla_mfma.hip", "lla_decode.hip", "lla_bwd.hip"]
+SOURCES = ["lla_api.hip", "lla_valu.hip", "lla_mfma.hip", "lla_decode.hip", "lla_bwd.hip",
+           "lla_naive.hip"]
 # headers the sources include (part of the source hash)
 HEADERS = [os.path.join(CSRC, "lla_internal.h"), os.path.join(CSRC, "lla_mfma_common.h"),
            os.path.join(ROOT, "include", "lla.h")]

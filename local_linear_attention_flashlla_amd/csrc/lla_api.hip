@@ -239,6 +239,70 @@ int lla_output_given_rho(const lla_fwd_args* a, const float* rho_in, hipStream_t
   return forward_impl(a, rho_in, stream);
 }
 
+// Longest sequence and most heads of the naive forward: its grid holds n
+// rows in x and B*H heads in y (at most 65535), and its workspace grows as
+// B*H*n^2*d.
+constexpr int kMaxNaiveN = 1 << 16;
+
+// Checks of a naive call beyond validate(): sizes, and the fields that have
+// no meaning for it.
+static int naive_check(const lla_fwd_args* a) {
+  if (a->n > kMaxNaiveN) return fail(LLA_ERR_UNSUPPORTED, "naive forward: n=%d > 2^16", a->n);
+  if ((unsigned long long)a->B * (unsigned long long)a->H > 65535ULL)
+    return fail(LLA_ERR_UNSUPPORTED, "naive forward: B*H > 65535");
+  if (a->kernel != LLA_KERNEL_AUTO)
+    return fail(LLA_ERR_INVALID_ARG, "naive forward: kernel must be LLA_KERNEL_AUTO (got %d)", a->kernel);
+  if (a->flags != 0) return fail(LLA_ERR_INVALID_ARG, "naive forward: flags must be 0 (got 0x%x)", a->flags);
+  if (a->rho_c) return fail(LLA_ERR_INVALID_ARG, "naive forward: rho_c is not produced (exact solve)");
+  return LLA_OK;
+}
+
+size_t lla_naive_workspace_bytes(int B, int H, int n, int d, int dtype) {
+  if (B < 1 || H < 1 || n < 1 || n > kMaxNaiveN || !d_supported(d)) return 0;
+  if (dtype != LLA_DTYPE_F32 && dtype != LLA_DTYPE_BF16) return 0;
+  const unsigned long long bh = (unsigned long long)B * (unsigned long long)H;
+  if (bh > 65535ULL) return 0;
+  return lla::naive_workspace_bytes(static_cast<int>(bh), n, d);
+}
+
+int lla_forward_naive(const lla_fwd_args* a, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  int st = validate(a);
+  if (st != LLA_OK) return st;
+  st = naive_check(a);
+  if (st != LLA_OK) return st;
+  lla::FwdParams p{};
+  p.q = a->q; p.k = a->k; p.v = a->v; p.out = a->out;
+  p.omega = a->omega; p.rho = a->rho; p.rowmax = a->rowmax;
+  p.cg_iters = a->cg_iters; p.cg_resid = a->cg_resid;
+  p.BH = a->B * a->H; p.n = a->n; p.d = a->d; p.dtype = a->dtype;
+  p.lambda = a->lambda;
+  p.ev_main_begin = a->ev_main_begin;
+  p.ev_main_end = a->ev_main_end;
+  const size_t need = lla::naive_workspace_bytes(p.BH, p.n, p.d);
+  void* ws = a->workspace;
+  bool owned = false;
+  if (ws) {
+    if (a->workspace_bytes < need)
+      return fail(LLA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", a->workspace_bytes, need);
+  } else {
+    const hipError_t e = hipMallocAsync(&ws, need, stream);
+    if (e != hipSuccess) return fail(LLA_ERR_HIP, "workspace allocation of %zu bytes: %s", need,
+                                     hipGetErrorString(e));
+    owned = true;
+  }
+  p.workspace = ws;
+  p.workspace_bytes = owned ? need : a->workspace_bytes;
+  const hipError_t e = lla::launch_naive(p, stream);
+  if (owned) {
+    const hipError_t f = hipFreeAsync(ws, stream);
+    if (e == hipSuccess && f != hipSuccess)
+      return fail(LLA_ERR_HIP, "workspace free: %s", hipGetErrorString(f));
+  }
+  if (e != hipSuccess) return fail(LLA_ERR_HIP, "naive launch: %s", hipGetErrorString(e));
+  return LLA_OK;
+}
+
 // Host checks of a decode call; fills *p (everything but the workspace).
 static int decode_validate(const lla_decode_args* a, lla::DecodeParams* p) {
   if (!a) return fail(LLA_ERR_INVALID_ARG, "args is NULL");

@@ -90,6 +90,11 @@ hipError_t mfma_moments(const FwdParams& p, hipStream_t stream);
 hipError_t mfma_precond_build(const FwdParams& p, hipStream_t stream);
 hipError_t mfma_cg(const FwdParams& p, hipStream_t stream);
 
+// The naive forward (fp32; pairwise differences and moment matrices held in
+// the workspace, exact Cholesky solves): its workspace and launch.
+size_t naive_workspace_bytes(int BH, int n, int d);
+hipError_t launch_naive(const FwdParams& p, hipStream_t stream);
+
 // Everything a backward launch needs, already validated by the host API.
 struct BwdParams {
   const void* q;      // bf16 [BH][n][d]

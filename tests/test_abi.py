@@ -346,3 +346,37 @@ def test_noalloc_decode_rejects_a_workspace_and_oversized_calls_on_the_host(lib)
     assert lib.lla_decode_noalloc(ctypes.byref(a), None) == _lib.LLA_ERR_WORKSPACE
     assert "static scratch" in _lib.last_error()
     assert lib.lla_decode_noalloc(ctypes.byref(_dargs(d=48)), None) == _lib.LLA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kernel=_lib.LLA_KERNEL_VALU), -1), (dict(kernel=_lib.LLA_KERNEL_MFMA), -1),
+    (dict(flags=_lib.LLA_FLAG_SPLIT_U), -1),
+    (dict(rho_c=BASE + 6 * GAP), -1),
+    (dict(n=(1 << 16) + 1), -2),
+    (dict(B=256, H=256), -2),               # B*H = 65536 heads: more than the grid holds
+    (dict(d=48), -2), (dict(lambda_=0.0), -1), (dict(q=0), -1),
+    (dict(out=BASE + GAP + 64), -1),        # overlaps k
+])
+def test_naive_forward_rejects_invalid_arguments_on_the_host(lib, kw, status):
+    a = _args(**kw)
+    assert lib.lla_forward_naive(ctypes.byref(a), None) == status
+    assert _lib.last_error() != ""
+
+
+def test_naive_workspace_holds_the_pairwise_differences_and_moment_matrices(lib):
+    # z_ij (BH n^2 d), w_ij (BH n^2), Sigma_i (BH n d^2), mu_i and rho_i
+    # (BH n d each), omega_i and the row max (BH n each), in fp32, each region
+    # 256-byte aligned
+    al = lambda x: (x + 255) // 256 * 256
+    for B, H, n, d in [(1, 1, 1, 16), (2, 3, 100, 64), (1, 16, 1024, 128), (1, 1, 4096, 128)]:
+        r = B * H * n
+        want = (al(4 * r * n * d) + al(4 * r * n) + al(4 * r * d * d) + 2 * al(4 * r * d)
+                + 2 * al(4 * r))
+        assert lib.lla_naive_workspace_bytes(B, H, n, d, _lib.LLA_DTYPE_BF16) == want
+    # quadratic in n, against the linear workspace of the blocked forward
+    w1 = lib.lla_naive_workspace_bytes(1, 16, 2048, 128, _lib.LLA_DTYPE_BF16)
+    w2 = lib.lla_naive_workspace_bytes(1, 16, 4096, 128, _lib.LLA_DTYPE_BF16)
+    assert 3.8 < w2 / w1 < 4.0   # the n^2 d term dominates; Sigma_i grows as n d^2
+    assert lib.lla_naive_workspace_bytes(1, 1, (1 << 16) + 1, 16, _lib.LLA_DTYPE_F32) == 0
+    assert lib.lla_naive_workspace_bytes(256, 256, 16, 16, _lib.LLA_DTYPE_F32) == 0
+    assert lib.lla_naive_workspace_bytes(1, 1, 16, 48, _lib.LLA_DTYPE_F32) == 0
