@@ -506,7 +506,7 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
   __shared__ __align__(16) _Float16 sKr0[BK * D], sKr1[BK * D], sKr2[BK * D], sKr3[BK * D];
   __shared__ __align__(16) _Float16 sKt0[D * BK], sKt1[D * BK], sKt2[D * BK], sKt3[D * BK];
   __shared__ __align__(16) half8 sKb[NW][NKS][64];  // kbar, fp16, operand order
-  __shared__ float sScale[2];
+  __shared__ float sScale[3];
   __shared__ int sFlag[NW];
 
   const int tid = threadIdx.x;
@@ -528,11 +528,13 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
   const int wlast = wave_any ? min(ntiles - 1, (wfirst + 31) / BK) : -1;  // last tile of the wave
 
   if (tid < 64) {
-    float a, b;
+    float a, b, mk = 0.f, mv, mq;
     head_scales(P.partial, bh, P.nchunk, tid, &a, &b);
+    if constexpr (PHASE >= 4) head_maxima(P.partial, bh, P.nchunk, tid, &mk, &mv, &mq);
     if (tid == 0) {
       sScale[0] = a;
       sScale[1] = b;
+      sScale[2] = mk;  // (output for a supplied rho) the head's largest key row norm
     }
   }
   __syncthreads();
@@ -815,8 +817,6 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
 
   // Per query: kbar = mu~ / omega, r0 = mu = mu~ - omega q, x0 = 0, into the
   // lane-contiguous workspace slabs; the row max and omega into the state slab.
-  // With a supplied rho (no CG solve) the output phase is centred at q
-  // instead, which is Eq. (8) as printed: the slabs then hold s q and rho / s.
   {
     const float inv_om = qvalid ? 1.f / om : 0.f;
     #pragma unroll
@@ -831,14 +831,6 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
           kb[b] = mt * inv_om;
           rc[b] = qvalid ? mt - om * qv[b] : 0.f;
         }
-        if (P.rho_in) {
-          kb = qvalid ? qv : floatx4{0.f, 0.f, 0.f, 0.f};
-          if (qvalid) {
-            const float4 rv = *reinterpret_cast<const float4*>(P.rho_in + orow * D + 32 * mb + 8 * a + 4 * g);
-            const float inv_s = 1.f / s;
-            x0 = floatx4{rv.x * inv_s, rv.y * inv_s, rv.z * inv_s, rv.w * inv_s};
-          }
-        }
         slab_st(kbs, mb * 4 + a, lane, kb);
         slab_st(xs, mb * 4 + a, lane, x0);
         slab_st(rsl, mb * 4 + a, lane, rc);
@@ -848,10 +840,6 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
   qst[64 + lane] = om;
   if (qvalid && g == 0) {
     if (P.omega) P.omega[orow] = om;
-    if (P.rho_in) {  // no CG solve in this mode
-      if (P.cg_iters) P.cg_iters[orow] = 0;
-      if (P.cg_resid) P.cg_resid[orow] = 0.f;
-    }
     if (P.rowmax) P.rowmax[orow] = m2 * kLn2;
   }
   } else if constexpr (PHASE == 2) {
@@ -1356,19 +1344,43 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
     if (P.cg_resid) P.cg_resid[orow] = r0n > 0.f ? sqrtf(rr) / r0n : 0.f;
   }
   } else {
-  // ------------------------------ phase 3 ------------------------------
-  const float m2 = qst[lane];
+  // ------------------------- phase 3 (and 4) ---------------------------
+  // PHASE 4 is the output for a supplied rho in one sweep over the keys and
+  // values (no moment kernel before it): rho comes from P.rho_in, the
+  // expansion point is q itself (Eq. (8) as printed), and the scores are
+  // taken against a running reference instead of the exact row max: the
+  // first tile's max, raised (rescaling what has been accumulated) when a
+  // later tile's scores pass it by more than 15 in log2 units, which keeps
+  // every weight, and with it every A entry, within fp16. The exact row max
+  // and omega are tracked beside it for the optional outputs.
+  // PHASE 5 is PHASE 4 with omega and the row max written (the sum of the
+  // weights and the exact max are tracked only there).
+  constexpr bool GIVEN = PHASE >= 4, STATS = PHASE == 5;
+  const float m2 = GIVEN ? 0.f : qst[lane];
   // rho' = x as two fp16 terms: x = srho (hi + lo)
   half8 rhi[NKS], rlo[NKS];
   float srho, kr_dot, inv_sA;
+  // (PHASE 4, 5) |q| times the head's largest key norm, in log2 units: no
+  // score of this query can pass it (Cauchy-Schwarz)
+  float kbound = 0.f;
   {
     float xv[NMB][16];
     float mx = 0.f, nn = 0.f;
+    const float inv_s = 1.f / s;
     #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
       #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const floatx4 xc = slab_ld(xs, mb * 4 + a, lane);
+        floatx4 xc;
+        if constexpr (GIVEN) {
+          xc = floatx4{0.f, 0.f, 0.f, 0.f};
+          if (qvalid) {
+            const float4 rv = *reinterpret_cast<const float4*>(P.rho_in + orow * D + 32 * mb + 8 * a + 4 * g);
+            xc = floatx4{rv.x * inv_s, rv.y * inv_s, rv.z * inv_s, rv.w * inv_s};
+          }
+        } else {
+          xc = slab_ld(xs, mb * 4 + a, lane);
+        }
         #pragma unroll
         for (int b = 0; b < 4; ++b) {
           xv[mb][4 * a + b] = xc[b];
@@ -1388,22 +1400,32 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
         rhi[2 * mb + (r >> 3)][r & 7] = h;
         rlo[2 * mb + (r >> 3)][r & 7] = static_cast<_Float16>(xsc - static_cast<float>(h));
       }
-    float kd = 0.f;
+    float kd = 0.f, cn = 0.f;
     #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
       #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const floatx4 kb = slab_ld(kbs, mb * 4 + a, lane);
+        // the expansion point c: kbar, or (supplied rho) s q
+        floatx4 kb;
+        if constexpr (GIVEN) {
+          kb = qvalid ? q_acc(mb, a) : floatx4{0.f, 0.f, 0.f, 0.f};
+        } else {
+          kb = slab_ld(kbs, mb * 4 + a, lane);
+        }
         #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const int r = 4 * a + b;
           const int t = 2 * mb + (r >> 3), c = r & 7;
           kd += kb[b] * (static_cast<float>(rhi[t][c]) + static_cast<float>(rlo[t][c]));
+          cn += kb[b] * kb[b];
         }
       }
     kr_dot = pair_sum(kd) * srho;
-    // |(k - kbar).rho'| <= 2 * 128 * ||rho'||, so a / sA stays within [-1, 1]
-    inv_sA = 1.f / pow2_ceil(1.f + 2.f * kRowNormCap * sqrtf(nn));
+    // |(k - c).rho'| <= (128 + ||c||) ||rho'|| (||c|| <= 128 for c = kbar), so
+    // a / sA stays within [-1, 1]
+    const float cmax = GIVEN ? sqrtf(pair_sum(cn)) : kRowNormCap;
+    inv_sA = 1.f / pow2_ceil(1.f + (kRowNormCap + cmax) * sqrtf(nn));
+    if constexpr (GIVEN) kbound = cmax / s * sScale[2] * (kLog2e / sqrtf(static_cast<float>(D)));
   }
   // racc starts at -kbar.rho' / srho (srho is a power of two: exact), so
   // (k - kbar).rho' = srho racc and a / sA = w (inv_sA - srho inv_sA racc)
@@ -1419,6 +1441,10 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
     #pragma unroll
     for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
   float den = 0.f;
+  // PHASE 4: the running score reference, the exact row max (log2 units) and
+  // the sum of the weights against the reference
+  float mref = 0.f, mabs = -INFINITY, wsum = 0.f;
+  bool have_ref = false;
   {
     // Y += Vt(j-1) A(j-1); [S - m2; R](j+1); A(j) = exp2(S(j)) (1 - srho R(j)) / sA
     constexpr int NY = 2 * NMB, NF = NY + NKS, PF = 4, EPS = 16 / NF;
@@ -1444,7 +1470,7 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
     for (int h = 0; h < 2; ++h)
       #pragma unroll
       for (int c = 0; c < 8; ++c) ab[h][c] = static_cast<_Float16>(0.f);
-    auto ostep = [&](auto JM, auto masked, int j, const floatx16& sc, const floatx16& rc, floatx16& sn,
+    auto ostep = [&](auto JM, auto masked, int j, floatx16& sc, const floatx16& rc, floatx16& sn,
                      floatx16& rn, const half8 (&up)[2], half8 (&uc)[2]) __attribute__((always_inline)) {
       constexpr int jm = decltype(JM)::value;
       constexpr bool MASKED = decltype(masked)::value;
@@ -1460,6 +1486,41 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
       half8 fr[PF];
       #pragma unroll
       for (int k = 0; k < PF; ++k) fr[k] = frag(k);
+      // PHASE 4: set (first tile) or raise the score reference before the
+      // tile's weights are formed and before the next tile's scores are
+      // started against it; what has been accumulated is rescaled with it
+      // (den here, acc once this step's products with A(j - 1) are issued)
+      float pend = 1.f;
+      if constexpr (GIVEN) {
+        // the tile max is needed to set the reference (first tile), to write
+        // the row max, or where the bound leaves room for a raise (the
+        // margin covers the fp16 rounding of the score operands)
+        const bool need = STATS || !have_ref || kbound * 1.004f + 1.f - mref > 15.f;
+        if (doV && __any(need ? 1 : 0)) {
+          float tm = -INFINITY;
+          #pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const bool ok = !MASKED || key_of(r) <= lim;
+            tm = fmaxf(tm, ok ? sc[r] : -INFINITY);
+          }
+          tm = pair_max(tm);
+          if (tm > -INFINITY) mabs = fmaxf(mabs, tm + mref);
+          const bool raise = tm > -INFINITY && (!have_ref || tm > 15.f);
+          if (__any(raise ? 1 : 0)) {
+            const float dl = raise ? tm : 0.f;
+            #pragma unroll
+            for (int r = 0; r < 16; ++r) sc[r] -= dl;
+            // (nothing is accumulated before the reference is first set)
+            pend = have_ref ? fast_exp2(-dl) : 1.f;
+            den *= pend;
+            wsum *= pend;
+            mref += dl;
+            #pragma unroll
+            for (int r = 0; r < 16; ++r) sinit[r] = -mref;
+            have_ref = have_ref || raise;
+          }
+        }
+      }
       float wv[16];
       __builtin_amdgcn_sched_barrier(0);
       #pragma unroll
@@ -1487,6 +1548,7 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
             if constexpr (MASKED) {
               if (key_of(r) > lim) w = 0.f;
             }
+            if constexpr (STATS) wsum += w;
             wv[r] = w;
             if (r & 1) {
               const half2v ha = mul_pack_sum(wv[r - 1], fmaf(rc[r - 1], a_slope, inv_sA), w,
@@ -1497,6 +1559,12 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
           }
         }
         __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (GIVEN) {
+        if (__any(pend != 1.f ? 1 : 0)) {
+          #pragma unroll
+          for (int mb = 0; mb < NMB; ++mb) acc[mb] *= pend;
+        }
       }
       step_barrier<D, NW, 2>();
     };
@@ -1520,6 +1588,7 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
     __syncthreads();  // no tile copy may still be in flight when the kernel ends
   }
   den = pair_sum(den);
+  if constexpr (STATS) wsum = pair_sum(wsum);
 
   if (!qvalid) return;
   const float ob = 1.f / (den * sv);
@@ -1535,6 +1604,26 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
       o.w = acc[mb][4 * a + 3] * ob;
       *reinterpret_cast<float4*>(P.out + orow * D + dim) = o;
     }
+  if constexpr (GIVEN) {
+    if (P.rho) {
+      #pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+        #pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const size_t o = orow * D + 32 * mb + 8 * a + 4 * g;
+          *reinterpret_cast<float4*>(P.rho + o) = *reinterpret_cast<const float4*>(P.rho_in + o);
+        }
+    }
+    if (g == 0) {
+      if constexpr (STATS) {
+        if (P.omega) P.omega[orow] = wsum * fast_exp2(mref - mabs);
+        if (P.rowmax) P.rowmax[orow] = mabs * kLn2;
+      }
+      if (P.cg_iters) P.cg_iters[orow] = 0;
+      if (P.cg_resid) P.cg_resid[orow] = 0.f;
+    }
+    return;
+  } else {
   if (P.rho_c) {
     #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
@@ -1574,6 +1663,7 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
         *reinterpret_cast<float4*>(P.rho + orow * D + dim) =
             make_float4(xc[0] * rs, xc[1] * rs, xc[2] * rs, xc[3] * rs);
       }
+  }
   }
   }
 }
@@ -1689,23 +1779,27 @@ hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const MainParams m = main_params<D>(p, w);
   const dim3 grid1 = grid_of(p, kNW13);
-  // three kernels, one per phase, sharing the block order and per-query state
-  // slabs: moments, conjugate gradient (timed by the optional events), output
-  hipLaunchKernelGGL((lla_mfma_phase<D, 1, false, kNW13>), grid1, dim3(64 * kNW13), 0, stream, m);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
   if (p.rho_in) {
-    // rho supplied: no CG kernel; the events bracket the output kernel
+    // rho supplied: one sweep over the keys and values (PHASE 4, or 5 with
+    // omega or the row max wanted), bracketed by the events
     if (p.ev_main_begin) {
       e = hipEventRecord(p.ev_main_begin, stream);
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((lla_mfma_phase<D, 3, false, kNW13>), grid1, dim3(64 * kNW13), 0, stream, m);
+    if (p.omega || p.rowmax)
+      hipLaunchKernelGGL((lla_mfma_phase<D, 5, false, kNW13>), grid1, dim3(64 * kNW13), 0, stream, m);
+    else
+      hipLaunchKernelGGL((lla_mfma_phase<D, 4, false, kNW13>), grid1, dim3(64 * kNW13), 0, stream, m);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (p.ev_main_end) e = hipEventRecord(p.ev_main_end, stream);
     return e;
   }
+  // three kernels, one per phase, sharing the block order and per-query state
+  // slabs: moments, conjugate gradient (timed by the optional events), output
+  hipLaunchKernelGGL((lla_mfma_phase<D, 1, false, kNW13>), grid1, dim3(64 * kNW13), 0, stream, m);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const bool pc = use_precond(p);
   if (pc) {
     e = launch_pc_build<D>(p, w, stream);

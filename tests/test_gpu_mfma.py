@@ -50,12 +50,14 @@ def all_rows(wl):
     return [((b, h), range(wl.n)) for b in range(wl.B) for h in range(wl.H)]
 
 
-def given_rho_cases(torch, wl, kernel, tol_rel, label):
+def given_rho_cases(torch, wl, kernel, tol_rel, label, lam=None):
     """Eq. (8) for supplied rho against the oracle's Eq. (8) with the same rho:
     the exact rho (then also the exact output), rho = 0 (softmax) and a rho
-    halfway to zero with noise (any rho; the denominator stays away from 0)."""
+    halfway to zero with noise (any rho; the denominator stays away from 0).
+    omega and the row max, which the one-sweep kernel forms against its own
+    running reference, against the oracle's."""
     hr = all_rows(wl)
-    lam = wl.lam
+    lam = wl.lam if lam is None else lam
     ex = oracle_rows(wl, hr, lam=lam)
     shape = (wl.B, wl.H, wl.n, wl.d)
     rho_exact = np.zeros(shape, np.float32)
@@ -71,9 +73,18 @@ def given_rho_cases(torch, wl, kernel, tol_rel, label):
         rho_t = torch.from_numpy(rho).cuda()
         rho_o = torch.empty(shape, device="cuda")
         it_o = torch.full(shape[:3], -1, dtype=torch.int32, device="cuda")
+        om_o = torch.empty(shape[:3], device="cuda")
+        rm_o = torch.empty(shape[:3], device="cuda")
         out = lla.forward(q, k, v, lam, 16, 0.0, kernel=kernel, rho_in=rho_t, rho=rho_o,
-                          cg_iters=it_o)
+                          cg_iters=it_o, omega=om_o, rowmax=rm_o)
+        # without omega and the row max (on the matrix cores a variant that
+        # tracks neither): the same raises of the reference, the same output
+        out_plain = lla.forward(q, k, v, lam, 16, 0.0, kernel=kernel, rho_in=rho_t)
         torch.cuda.synchronize()
+        assert torch.equal(out, out_plain)
+        for ((b, h), _), x in zip(hr, ex):
+            np.testing.assert_allclose(rm_o[b, h].cpu().numpy(), x["m"], rtol=1e-3, atol=1e-3)
+            np.testing.assert_allclose(om_o[b, h].cpu().numpy(), x["omega"], rtol=5e-3)
         got = out.cpu().numpy().astype(np.float64)
         ref = oracle_given_rho(wl, hr, rho.astype(np.float64), lam)
         e = np.concatenate([row_errors(got[b, h], r) for ((b, h), _), r in zip(hr, ref)])
@@ -242,6 +253,15 @@ def test_full_size_sampled_rows(torch, name):
     assert it.max() <= wl.cg_max_iters
     assert np.isfinite(res["out"]).all()
     assert stats["rows"] > 0
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_output_given_rho_with_rising_scores(torch, d):
+    # the one-sweep output for a supplied rho starts its score reference at
+    # the first tile's max; key norms growing 10-20 fold along the sequence
+    # make it raise (and rescale) on most rows
+    wl = make_random(1, 2, 512, d, "bf16", seed=40 + d, qk_scale=8.0, key_ramp={64: 9.0, 128: 19.0}[d])
+    given_rho_cases(torch, wl, MFMA, BF16_TOL, f"mfma rising scores d={d}", lam=1e3)
 
 
 @pytest.mark.parametrize("d", [64, 128])
