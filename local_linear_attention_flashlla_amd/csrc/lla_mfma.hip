@@ -1239,6 +1239,7 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
     // (recomputed where needed rather than kept); exact line search along d;
     // then the next direction p = r + beta sp d, renormalised and rounded to
     // fp16.
+    // (Sigma_c d replaces Y in the accumulators: the second pass reads it)
     float dAd = 0.f, rd = 0.f;
     #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
@@ -1250,6 +1251,7 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
           const int r = 8 * h + c;
           const float dv = static_cast<float>(dop[2 * mb + h][c]);
           const float v = acc[mb][r] - usum * static_cast<float>(kb[c]) + lam_s * dv;
+          acc[mb][r] = v;
           dAd += dv * v;
           rd += rv4[mb * 4 + (r >> 2)][r & 3] * dv;
         }
@@ -1263,12 +1265,11 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
     for (int mb = 0; mb < NMB; ++mb)
       #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const half8 kb = sKb[wave][2 * mb + h][lane];
         #pragma unroll
         for (int c = 0; c < 8; ++c) {
           const int r = 8 * h + c;
           const float dv = static_cast<float>(dop[2 * mb + h][c]);
-          const float v = acc[mb][r] - usum * static_cast<float>(kb[c]) + lam_s * dv;
+          const float v = acc[mb][r];
           // al = 0 leaves a stopped query's state as it is
           const int ci = mb * 4 + (r >> 2), bi = r & 3;
           rv4[ci][bi] = rv4[ci][bi] - al * v;
@@ -1307,22 +1308,32 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
     }
     // lanes that stopped keep their state; the pair exchanges run in every lane
     const float be = (step && rz > 0.f) ? rzn / rz * sp : 0.f;
+    // p = z + beta sp d, held in the accumulators (in place of z where z
+    // lives there), then renormalised and rounded
     float mx = 0.f;
     #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
       #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        mx = fmaxf(mx, fabsf(zsrc(mb * 4 + (r >> 2), r & 3) + be * static_cast<float>(dop[2 * mb + (r >> 3)][r & 7])));
+      for (int r = 0; r < 16; ++r) {
+        const float pv = zsrc(mb * 4 + (r >> 2), r & 3) + be * static_cast<float>(dop[2 * mb + (r >> 3)][r & 7]);
+        acc[mb][r] = pv;
+        mx = fmaxf(mx, fabsf(pv));
+      }
     const float sp_new = pow2_ceil(pair_max(mx));
     const float inv_sp = 1.f / sp_new;
+    // the next direction; a query that stopped keeps its own (a select per
+    // register, not a branch per element)
     #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
+    for (int t = 0; t < NKS; ++t) {
+      half8 nd;
       #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = 2 * mb + (r >> 3), c = r & 7;
-        const float pv = zsrc(mb * 4 + (r >> 2), r & 3) + be * static_cast<float>(dop[t][c]);
-        if (cont) dop[t][c] = static_cast<_Float16>(pv * inv_sp);
-      }
+      for (int c = 0; c < 8; ++c) nd[c] = static_cast<_Float16>(acc[t >> 1][8 * (t & 1) + c] * inv_sp);
+      const u32x4 a = __builtin_bit_cast(u32x4, nd), b = __builtin_bit_cast(u32x4, dop[t]);
+      u32x4 sel;
+      #pragma unroll
+      for (int e = 0; e < 4; ++e) sel[e] = cont ? a[e] : b[e];
+      dop[t] = __builtin_bit_cast(half8, sel);
+    }
     if (cont) sp = sp_new;
     const float kbdn = kbar_dot(dop);
     if (cont) kbd = kbdn;
