@@ -457,9 +457,14 @@ __global__ __launch_bounds__(NT) void pc_invert(const float* __restrict__ partia
         const float v = 0.5f * (sA[row][col] + sA[col][row]) * inv;
         const _Float16 hi = static_cast<_Float16>(v);
         const _Float16 lo = static_cast<_Float16>(v - static_cast<float>(hi));
+        // operand order: the A fragment of k-step t, block mb for lane
+        // (ql, g) holds row 32 mb + ql, permuted columns 16 t + 8 g + (0..7);
+        // a wave's fragments of one (t, mb) are 1 KiB contiguous
         const int pcol = (col & ~15) | swz16(col & 15);
-        hiM[static_cast<size_t>(row) * D + pcol] = hi;
-        loM[static_cast<size_t>(row) * D + pcol] = lo;
+        const int t = pcol >> 4, fg = (pcol >> 3) & 1, e = pcol & 7;
+        const int fi = (((t * (D / 32) + (row >> 5)) * 64 + 32 * fg + (row & 31)) * 8) + e;
+        hiM[fi] = hi;
+        loM[fi] = lo;
       }
     }
   }
@@ -922,26 +927,40 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
     for (int mb = 0; mb < NMB; ++mb)
       #pragma unroll
       for (int r = 0; r < 16; ++r) zacc[mb][r] = 0.f;
+    // M's fragments half a matrix at a time (at d = 128, 32 loads of 16
+    // bytes per lane): all of a batch's loads are in flight together, so the
+    // latency is paid twice, not once per fragment
+    constexpr int TB = NKS / 2;
     #pragma unroll
-    for (int t = 0; t < NKS; ++t) {
-      // k-step t of r / sr as two fp16 terms, in operand order
-      half8 rh, rl;
+    for (int t0 = 0; t0 < NKS; t0 += TB) {
+      half8 mh[TB][NMB], ml[TB][NMB];
       #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int r = 8 * (t & 1) + e, c = (t >> 1) * 4 + (r >> 2);
-        const float v = rv4[c][r & 3] * inv;
-        const _Float16 h = static_cast<_Float16>(v);
-        rh[e] = h;
-        rl[e] = static_cast<_Float16>(v - static_cast<float>(h));
-      }
+      for (int tt = 0; tt < TB; ++tt)
+        #pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+          const int off = (((t0 + tt) * NMB + mb) * 64 + lane) * 16;  // operand order (pc_invert)
+          mh[tt][mb] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(pc_rsrc, off, 0, 0));
+          ml[tt][mb] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(pc_rsrc, off, D * D * 2, 0));
+        }
       #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb) {
-        const int off = ((32 * mb + ql) * D + 16 * t + 8 * g) * 2;
-        const half8 mh = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(pc_rsrc, off, 0, 0));
-        const half8 ml = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(pc_rsrc, off, D * D * 2, 0));
-        zacc[mb] = mfma(mh, rh, zacc[mb]);
-        zacc[mb] = mfma(mh, rl, zacc[mb]);
-        zacc[mb] = mfma(ml, rh, zacc[mb]);
+      for (int tt = 0; tt < TB; ++tt) {
+        const int t = t0 + tt;
+        // k-step t of r / sr as two fp16 terms, in operand order
+        half8 rh, rl;
+        #pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * (t & 1) + e, c = (t >> 1) * 4 + (r >> 2);
+          const float v = rv4[c][r & 3] * inv;
+          const _Float16 h = static_cast<_Float16>(v);
+          rh[e] = h;
+          rl[e] = static_cast<_Float16>(v - static_cast<float>(h));
+        }
+        #pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+          zacc[mb] = mfma(mh[tt][mb], rh, zacc[mb]);
+          zacc[mb] = mfma(mh[tt][mb], rl, zacc[mb]);
+          zacc[mb] = mfma(ml[tt][mb], rh, zacc[mb]);
+        }
       }
     }
     const float zs = sr * pc_s;
@@ -1278,16 +1297,20 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
         }
       }
     if constexpr (PRECOND) {
-      // the iterate waits in its workspace slab (registers are short here):
-      // x += al d, one read and one write of this lane's 256 bytes
+      // the iterate waits in its workspace slab (registers are short during
+      // the sweep): x += al d, one read and one write of this lane's 256
+      // bytes, all reads issued before the first write
+      floatx4 xc[NMB * 4];
+      #pragma unroll
+      for (int c = 0; c < NMB * 4; ++c) xc[c] = slab_ld(xs, c, lane);
       #pragma unroll
       for (int c = 0; c < NMB * 4; ++c) {
-        floatx4 xc = slab_ld(xs, c, lane);
         const int mb = c >> 2, h = (c & 3) >> 1, e0 = 4 * (c & 1);
         #pragma unroll
-        for (int b = 0; b < 4; ++b) xc[b] += al * static_cast<float>(dop[2 * mb + h][e0 + b]);
-        slab_st(xs, c, lane, xc);
+        for (int b = 0; b < 4; ++b) xc[c][b] += al * static_cast<float>(dop[2 * mb + h][e0 + b]);
       }
+      #pragma unroll
+      for (int c = 0; c < NMB * 4; ++c) slab_st(xs, c, lane, xc[c]);
     }
     rrn = pair_sum(rrn);
     bool cont = false;

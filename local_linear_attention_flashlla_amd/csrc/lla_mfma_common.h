@@ -142,7 +142,8 @@ struct Workspace {
   float* kbs;       // fp32 kbar, same layout
   float* rs;        // CG residuals, same layout
   float* qs;        // per query row max and omega: [blocks][4 waves][2][64 lanes]
-  _Float16* pcm;    // [BH][nslots][2][D][D] preconditioners M / sM, hi and lo fp16 terms
+  _Float16* pcm;    // [BH][nslots][2][D*D] preconditioners M / sM, hi and lo fp16 terms,
+                    // each in MFMA operand order (see pc_invert)
                     // (while they are built: the slots' fp32 Gram matrices, D x D)
   float* pcs;       // [BH][nslots] their power-of-two scales sM (0: not built)
   float* pct;       // [BH][nslots][D] key sums of the slots' prefixes (build only)
