@@ -510,7 +510,13 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
   // arrays so that every buffer choice is static.
   __shared__ __align__(16) _Float16 sKr0[BK * D], sKr1[BK * D], sKr2[BK * D], sKr3[BK * D];
   __shared__ __align__(16) _Float16 sKt0[D * BK], sKt1[D * BK], sKt2[D * BK], sKt3[D * BK];
-  __shared__ __align__(16) half8 sKb[NW][NKS][64];  // kbar, fp16, operand order
+  // kbar, fp16, operand order, for the CG update; the preconditioned CG reads
+  // kbar from its workspace slab instead and gives this LDS to the block's
+  // preconditioner (sM: both fp16 terms, operand order), held for the whole
+  // kernel when the block's four groups share one
+  constexpr bool PCG = PHASE == 2 && PRECOND;
+  __shared__ __align__(16) half8 sKb[PCG ? 1 : NW][NKS][64];
+  __shared__ __align__(16) half8 sM[PCG ? 2 * D * D / 8 : 1];
   __shared__ float sScale[3];
   __shared__ int sFlag[NW];
 
@@ -869,9 +875,27 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
           kb16[2 * mb + (r >> 3)][r & 7] = static_cast<_Float16>(kb[b]);
         }
       }
-    #pragma unroll
-    for (int t = 0; t < NKS; ++t) sKb[wave][t][lane] = kb16[t];
+    if constexpr (!PCG) {
+      #pragma unroll
+      for (int t = 0; t < NKS; ++t) sKb[wave][t][lane] = kb16[t];
+    }
   }
+  // fragment t of kbar in fp16, operand order (the same values as sKb holds)
+  auto kb_frag = [&](int t) __attribute__((always_inline)) {
+    if constexpr (PCG) {
+      const int c0 = (t >> 1) * 4 + 2 * (t & 1);
+      const floatx4 a = slab_ld(kbs, c0, lane), b = slab_ld(kbs, c0 + 1, lane);
+      half8 h;
+      #pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        h[e] = static_cast<_Float16>(a[e]);
+        h[4 + e] = static_cast<_Float16>(b[e]);
+      }
+      return h;
+    } else {
+      return sKb[wave][t][lane];
+    }
+  };
   // CG state in registers: residual r and iterate x (fp32, accumulator
   // layout); between updates they are parked in the accumulation registers
   floatx4 rv4[NMB * 4], xv4[NMB * 4];
@@ -909,6 +933,25 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
     }
   }
   const bool use_pc = PRECOND && pc_s > 0.f;
+  // the block's four groups share one built preconditioner (uniform over the
+  // workgroup): copy it into LDS once, both terms, for every iteration
+  bool m_lds = false;
+  if constexpr (PCG) {
+    const int g0 = i0 >> 5, g3 = g0 + NW - 1;
+    if (g0 >= 1 && g3 <= (n - 1) >> 5 && pc_slot_of_group(g0) == pc_slot_of_group(g3)) {
+      const int slot = pc_slot_of_group(g0);
+      m_lds = P.pcs[static_cast<size_t>(bh) * P.nslots + slot] > 0.f;
+      if (m_lds) {
+        const __amdgpu_buffer_rsrc_t src = make_rsrc(P.pcm + (static_cast<size_t>(bh) * P.nslots + slot) * 2 * D * D,
+                                                     2 * D * D * sizeof(_Float16));
+        constexpr int NCH = 2 * D * D / 8;  // 16-byte chunks
+        #pragma unroll
+        for (int c = tid; c < NCH; c += 64 * NW)
+          sM[c] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(src, c * 16, 0, 0));
+      }
+    }
+    __syncthreads();
+  }
   auto r_to_z = [&]() __attribute__((always_inline)) {
     #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
@@ -938,9 +981,14 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
       for (int tt = 0; tt < TB; ++tt)
         #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) {
-          const int off = (((t0 + tt) * NMB + mb) * 64 + lane) * 16;  // operand order (pc_invert)
-          mh[tt][mb] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(pc_rsrc, off, 0, 0));
-          ml[tt][mb] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(pc_rsrc, off, D * D * 2, 0));
+          const int fi = ((t0 + tt) * NMB + mb) * 64 + lane;  // operand order (pc_invert)
+          if (m_lds) {
+            mh[tt][mb] = sM[fi];
+            ml[tt][mb] = sM[D * D / 8 + fi];
+          } else {
+            mh[tt][mb] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(pc_rsrc, fi * 16, 0, 0));
+            ml[tt][mb] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(pc_rsrc, fi * 16, D * D * 2, 0));
+          }
         }
       #pragma unroll
       for (int tt = 0; tt < TB; ++tt) {
@@ -991,7 +1039,7 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
     float acc_ = 0.f;
     #pragma unroll
     for (int t = 0; t < NKS; ++t) {
-      const half8 kb = sKb[wave][t][lane];
+      const half8 kb = kb_frag(t);
       #pragma unroll
       for (int c = 0; c < 8; ++c) acc_ += static_cast<float>(kb[c]) * static_cast<float>(op[t][c]);
     }
@@ -1264,7 +1312,7 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
     for (int mb = 0; mb < NMB; ++mb)
       #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const half8 kb = sKb[wave][2 * mb + h][lane];
+        const half8 kb = kb_frag(2 * mb + h);
         #pragma unroll
         for (int c = 0; c < 8; ++c) {
           const int r = 8 * h + c;
