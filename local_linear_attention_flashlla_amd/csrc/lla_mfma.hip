@@ -54,9 +54,9 @@ namespace {
 
 // ---------------------------------------------------------------------------
 // Prepass 1: per (head, chunk of 256 rows) the largest row norm of k, of v
-// and of q. A row's norm is formed as 2^e ||x 2^-e|| with 2^e above its
-// largest element, so that no square overflows or underflows fp32 for any
-// bf16 row (a norm past fp32's range comes out infinite).
+// and of q. Where a row's sum of squares would leave fp32's range, its norm
+// is formed as 2^e ||x 2^-e|| with 2^e above its largest element, so that no
+// bf16 row loses its norm (a norm past fp32's range comes out infinite).
 template <int D>
 __global__ __launch_bounds__(NT) void prep_norms(const uint16_t* __restrict__ q,
                                                  const uint16_t* __restrict__ k,
@@ -93,22 +93,35 @@ __global__ __launch_bounds__(NT) void prep_norms(const uint16_t* __restrict__ q,
     }
     #pragma unroll
     for (int t = 0; t < 3; ++t) {
-      float am = 0.f;
-      #pragma unroll
-      for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(x[t][e]));
-      #pragma unroll
-      for (int o = LPR / 2; o > 0; o >>= 1) am = fmaxf(am, __shfl_xor(am, o));
-      int ex = 0;
-      frexpf(am, &ex);                     // am < 2^ex (ex = 0 for a zero row)
       float ss = 0.f;
       #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float y = ldexpf(x[t][e], -ex);
-        ss += y * y;
-      }
+      for (int e = 0; e < 8; ++e) ss += x[t][e] * x[t][e];
       #pragma unroll
       for (int o = LPR / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
-      mx[t] = fmaxf(mx[t], ldexpf(sqrtf(ss), ex));
+      float nrm = sqrtf(ss);
+      // a sum of squares past fp32's range (or a nonzero one below 2^-100)
+      // is formed again under the row's own power of two (rare: the wave
+      // branches only when one of its rows needs it)
+      const bool rescale = !(ss <= 0x1p100f) || (ss > 0.f && ss < 0x1p-100f);
+      if (__any(rescale ? 1 : 0)) {
+        float am = 0.f;
+        #pragma unroll
+        for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(x[t][e]));
+        #pragma unroll
+        for (int o = LPR / 2; o > 0; o >>= 1) am = fmaxf(am, __shfl_xor(am, o));
+        int ex = 0;
+        frexpf(am, &ex);                   // am < 2^ex (ex = 0 for a zero row)
+        float sy = 0.f;
+        #pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float y = ldexpf(x[t][e], -ex);
+          sy += y * y;
+        }
+        #pragma unroll
+        for (int o = LPR / 2; o > 0; o >>= 1) sy += __shfl_xor(sy, o);
+        if (rescale) nrm = ldexpf(sqrtf(sy), ex);
+      }
+      mx[t] = fmaxf(mx[t], nrm);
     }
   }
   #pragma unroll
