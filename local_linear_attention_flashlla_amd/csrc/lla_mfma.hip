@@ -69,59 +69,67 @@ __global__ __launch_bounds__(NT) void prep_norms(const uint16_t* __restrict__ q,
   const int bh = blockIdx.x, chunk = blockIdx.y;
   const int sub = threadIdx.x % LPR, rofs = threadIdx.x / LPR;
   float mx[3] = {0.f, 0.f, 0.f};           // k, v, q
-  for (int r0 = 0; r0 < NORM_ROWS; r0 += RPI) {
-    const int i = chunk * NORM_ROWS + r0 + rofs;
-    float x[3][8];
-    if (i < n) {
-      const size_t off = (static_cast<size_t>(bh) * n + i) * D + sub * 8;
-      const uint4 a = *reinterpret_cast<const uint4*>(k + off);
-      const uint4 b = *reinterpret_cast<const uint4*>(v + off);
-      const uint4 c = *reinterpret_cast<const uint4*>(q + off);
-      const uint32_t w[3][4] = {{a.x, a.y, a.z, a.w}, {b.x, b.y, b.z, b.w}, {c.x, c.y, c.z, c.w}};
-      #pragma unroll
-      for (int t = 0; t < 3; ++t)
-        #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          x[t][2 * u] = bf16_to_f(w[t][u] & 0xffffu);
-          x[t][2 * u + 1] = bf16_to_f(w[t][u] >> 16);
-        }
-    } else {
-      #pragma unroll
-      for (int t = 0; t < 3; ++t)
-        #pragma unroll
-        for (int e = 0; e < 8; ++e) x[t][e] = 0.f;
+  // four passes' rows are loaded before any is reduced, so that a wave keeps
+  // twelve 1 KiB loads in flight (the kernel is bound by memory latency)
+  constexpr int PB = 4;
+  static_assert((NORM_ROWS / RPI) % PB == 0, "passes must group evenly");
+  for (int r0 = 0; r0 < NORM_ROWS; r0 += PB * RPI) {
+    uint4 raw[PB][3];
+    #pragma unroll
+    for (int pb = 0; pb < PB; ++pb) {
+      const int i = chunk * NORM_ROWS + r0 + pb * RPI + rofs;
+      raw[pb][0] = raw[pb][1] = raw[pb][2] = make_uint4(0u, 0u, 0u, 0u);
+      if (i < n) {
+        const size_t off = (static_cast<size_t>(bh) * n + i) * D + sub * 8;
+        raw[pb][0] = *reinterpret_cast<const uint4*>(k + off);
+        raw[pb][1] = *reinterpret_cast<const uint4*>(v + off);
+        raw[pb][2] = *reinterpret_cast<const uint4*>(q + off);
+      }
     }
     #pragma unroll
-    for (int t = 0; t < 3; ++t) {
-      float ss = 0.f;
+    for (int pb = 0; pb < PB; ++pb) {
+      float x[3][8];
       #pragma unroll
-      for (int e = 0; e < 8; ++e) ss += x[t][e] * x[t][e];
-      #pragma unroll
-      for (int o = LPR / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
-      float nrm = sqrtf(ss);
-      // a sum of squares past fp32's range (or a nonzero one below 2^-100)
-      // is formed again under the row's own power of two (rare: the wave
-      // branches only when one of its rows needs it)
-      const bool rescale = !(ss <= 0x1p100f) || (ss > 0.f && ss < 0x1p-100f);
-      if (__any(rescale ? 1 : 0)) {
-        float am = 0.f;
+      for (int t = 0; t < 3; ++t) {
+        const uint32_t w[4] = {raw[pb][t].x, raw[pb][t].y, raw[pb][t].z, raw[pb][t].w};
         #pragma unroll
-        for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(x[t][e]));
-        #pragma unroll
-        for (int o = LPR / 2; o > 0; o >>= 1) am = fmaxf(am, __shfl_xor(am, o));
-        int ex = 0;
-        frexpf(am, &ex);                   // am < 2^ex (ex = 0 for a zero row)
-        float sy = 0.f;
-        #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float y = ldexpf(x[t][e], -ex);
-          sy += y * y;
+        for (int u = 0; u < 4; ++u) {
+          x[t][2 * u] = bf16_to_f(w[u] & 0xffffu);
+          x[t][2 * u + 1] = bf16_to_f(w[u] >> 16);
         }
-        #pragma unroll
-        for (int o = LPR / 2; o > 0; o >>= 1) sy += __shfl_xor(sy, o);
-        if (rescale) nrm = ldexpf(sqrtf(sy), ex);
       }
-      mx[t] = fmaxf(mx[t], nrm);
+      #pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        float ss = 0.f;
+        #pragma unroll
+        for (int e = 0; e < 8; ++e) ss += x[t][e] * x[t][e];
+        #pragma unroll
+        for (int o = LPR / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+        float nrm = sqrtf(ss);
+        // a sum of squares past fp32's range (or a nonzero one below 2^-100)
+        // is formed again under the row's own power of two (rare: the wave
+        // branches only when one of its rows needs it)
+        const bool rescale = !(ss <= 0x1p100f) || (ss > 0.f && ss < 0x1p-100f);
+        if (__any(rescale ? 1 : 0)) {
+          float am = 0.f;
+          #pragma unroll
+          for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(x[t][e]));
+          #pragma unroll
+          for (int o = LPR / 2; o > 0; o >>= 1) am = fmaxf(am, __shfl_xor(am, o));
+          int ex = 0;
+          frexpf(am, &ex);                 // am < 2^ex (ex = 0 for a zero row)
+          float sy = 0.f;
+          #pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float y = ldexpf(x[t][e], -ex);
+            sy += y * y;
+          }
+          #pragma unroll
+          for (int o = LPR / 2; o > 0; o >>= 1) sy += __shfl_xor(sy, o);
+          if (rescale) nrm = ldexpf(sqrtf(sy), ex);
+        }
+        mx[t] = fmaxf(mx[t], nrm);
+      }
     }
   }
   #pragma unroll
@@ -172,33 +180,52 @@ __global__ __launch_bounds__(NT) void prep_convert(const uint16_t* __restrict__ 
   }
   __syncthreads();
   const float s = sc[0], sv = sc[1];
-  for (int e = threadIdx.x; e < BK * D; e += NT) {
-    const int r = e / D, c = e % D;
+  // 16 bytes (8 elements) per thread and instruction, in and out
+  for (int e8 = threadIdx.x; e8 < BK * D / 8; e8 += NT) {
+    const int r = e8 / (D / 8), c = (e8 % (D / 8)) * 8;
     const int j = kb * BK + r;
-    float a = 0.f, b = 0.f;
+    uint4 a = make_uint4(0u, 0u, 0u, 0u), b = make_uint4(0u, 0u, 0u, 0u);
     if (j < n) {
       const size_t off = (static_cast<size_t>(bh) * n + j) * D + c;
-      a = bf16_to_f(k[off]) * s;
-      b = bf16_to_f(v[off]) * sv;
+      a = *reinterpret_cast<const uint4*>(k + off);
+      b = *reinterpret_cast<const uint4*>(v + off);
     }
-    sK[r][c] = a;
-    sV[r][c] = b;
+    const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+    #pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      sK[r][c + 2 * u] = bf16_to_f(av[u] & 0xffffu) * s;
+      sK[r][c + 2 * u + 1] = bf16_to_f(av[u] >> 16) * s;
+      sV[r][c + 2 * u] = bf16_to_f(bv[u] & 0xffffu) * sv;
+      sV[r][c + 2 * u + 1] = bf16_to_f(bv[u] >> 16) * sv;
+    }
   }
   __syncthreads();
   // both tiles chunk-major: 16-byte chunk c of every row, rows consecutive
   const size_t tb = (static_cast<size_t>(bh) * nblk + kb) * BK * D;
-  for (int e = threadIdx.x; e < BK * D; e += NT) {
+  for (int e8 = threadIdx.x; e8 < BK * D / 8; e8 += NT) {
     // K rows: [chunk c < D/8][row r < 32][8], d positions 8c..8c+7 permuted
-    const int c = e / (8 * BK), r = (e / 8) % BK, pos = 8 * c + e % 8;
-    const int src = (pos & ~15) | swz16(pos & 15);
-    kr[tb + e] = static_cast<_Float16>(sK[r][src]);
+    const int c = e8 / BK, r = e8 % BK;
+    half8 h;
+    #pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int pos = 8 * c + e;
+      h[e] = static_cast<_Float16>(sK[r][(pos & ~15) | swz16(pos & 15)]);
+    }
+    *reinterpret_cast<half8*>(kr + tb + 8 * e8) = h;
   }
-  for (int e = threadIdx.x; e < BK * D; e += NT) {
+  for (int e8 = threadIdx.x; e8 < BK * D / 8; e8 += NT) {
     // transposed: [chunk c < 4][dim < D][8], key positions 8c..8c+7 permuted
-    const int c = e / (8 * D), dim = (e / 8) % D, pos = 8 * c + e % 8;
-    const int key = (pos & 16) | swz16(pos & 15);
-    kt[tb + e] = static_cast<_Float16>(sK[key][dim]);
-    vt[tb + e] = static_cast<_Float16>(sV[key][dim]);
+    const int c = e8 / D, dim = e8 % D;
+    half8 hk, hv;
+    #pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int pos = 8 * c + e;
+      const int key = (pos & 16) | swz16(pos & 15);
+      hk[e] = static_cast<_Float16>(sK[key][dim]);
+      hv[e] = static_cast<_Float16>(sV[key][dim]);
+    }
+    *reinterpret_cast<half8*>(kt + tb + 8 * e8) = hk;
+    *reinterpret_cast<half8*>(vt + tb + 8 * e8) = hv;
   }
 }
 
