@@ -263,11 +263,14 @@ def bench_decode(args, torch, lla, dev):
     of the workload's shape (the workload's generator for one batch element,
     tiled over --decode-batch). Queries/s = heads answered per second. One
     query per head against n keys is bound by reading the cache: the floor is
-    K and V read once. The kernels read K three times (scores, Gram, output)
-    and V once. The roofline line is the Gram kernel, the dominant one,
-    against HBM: its algorithmic bytes are K read once; the whole call's rate
-    against K + V read once is reported beside it, and the Gram kernel's
-    matrix-core rate (n d (d + 1) FLOPs per head) as information."""
+    K and V read once. bf16 caches (the workloads here) take one pass over K
+    and V (moments, Gram matrix and cross moment together), then a small
+    solve per head; the roofline line is that pass against HBM with its
+    algorithmic bytes, K and V read once. fp32 caches take the five-kernel
+    path that reads K three times and V once; there the line is its Gram
+    kernel with K read once. The whole call's rate against K + V read once is
+    reported beside it, and the main kernel's matrix-core rate as
+    information."""
     from local_linear_attention_flashlla_amd.workloads import make_workload
     wl = make_workload(args.workload, B=1)
     B = args.decode_batch if args.decode_batch > 0 else {"standard": 4, "long": 1, "recall": 8}.get(
@@ -308,31 +311,42 @@ def bench_decode(args, torch, lla, dev):
     gram_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     esz = 2 if wl.dtype == "bf16" else 4
     cache = B * H * n * d * esz
-    # G = sum_j u_j u_j^T is symmetric: its d (d + 1) / 2 distinct entries
-    # take d (d + 1) FLOPs per key (a multiply and an add each), n d (d + 1)
-    # per head; the kernel forms only the blocks on or above the diagonal
-    gram_flops = 1.0 * B * H * n * d * (d + 1)
+    one_pass = wl.dtype == "bf16"
+    if one_pass:
+        # per key: G (d^2 multiply-adds), the cross moment (d^2) and the score
+        # (d): 2 (2 d^2 + d) FLOPs; the pass reads K and V once
+        main_flops = 2.0 * B * H * n * (2 * d * d + d)
+        main_bytes = 2 * cache
+        main_name, read_bytes, mdtype = "single pass over K and V", 2 * cache, "bf16"
+    else:
+        # G = sum_j u_j u_j^T is symmetric: its d (d + 1) / 2 distinct entries
+        # take d (d + 1) FLOPs per key (a multiply and an add each), n d (d + 1)
+        # per head; the kernel forms only the blocks on or above the diagonal
+        main_flops = 1.0 * B * H * n * d * (d + 1)
+        main_bytes = cache
+        main_name, read_bytes, mdtype = "Gram kernel", 4 * cache, "fp16"
     rec = {
         "metric": "LLA decode queries/s (one new query per head), 1 MI355X",
         "value": B * H / (ms * 1e-3), "unit": "queries/s", "n_gpus": 1, "steps": steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        # the Gram kernel multiplies fp16 x fp16 into fp32 (operands in two
-        # fp16 terms); scores, CG and output run in fp32 on the vector ALU
-        "vs_baseline": None, "dtype": "fp16", "data": "synthetic",
+        # bf16 caches: bf16 x bf16 products into fp32 (w k and w v in two bf16
+        # terms), CG in fp32; fp32 caches: the Gram kernel's fp16 x fp16
+        # products (two fp16 terms), the rest fp32
+        "vs_baseline": None, "dtype": mdtype, "data": "synthetic",
         "config": {"workload": f"decode over the {wl.name} caches", "B": B, "H": H, "n": n, "d": d,
                    "input_dtype": wl.dtype,
                    "lambda": wl.lam, "cg_max_iters": wl.cg_max_iters, "cg_rel_tol": wl.cg_rel_tol},
         "cg_iters_mean": float(iters.float().mean().item()),
         "cache_bytes_k_plus_v": 2 * cache,
-        "cache_bytes_read_by_the_kernels": 4 * cache,
+        "cache_bytes_read_by_the_kernels": read_bytes,
         "whole_call_vs_hbm": {"bytes": 2 * cache, "GBps": 2 * cache / (ms * 1e-3) / 1e9,
                               "frac": 2 * cache / (ms * 1e-3) / 1e9 / PEAK["hbm"]},
-        "main_kernel": "Gram kernel", "main_kernel_ms": gram_ms,
-        "gram_mfma": {"TFLOPs": gram_flops / (gram_ms * 1e-3) / 1e12,
-                      "frac": gram_flops / (gram_ms * 1e-3) / 1e12 / PEAK["mfma_fp16"]},
-        "roofline": {"bound": "hbm", "achieved": cache / (gram_ms * 1e-3) / 1e9,
+        "main_kernel": main_name, "main_kernel_ms": gram_ms,
+        "main_kernel_mfma": {"TFLOPs": main_flops / (gram_ms * 1e-3) / 1e12,
+                             "frac": main_flops / (gram_ms * 1e-3) / 1e12 / PEAK["mfma_fp16"]},
+        "roofline": {"bound": "hbm", "achieved": main_bytes / (gram_ms * 1e-3) / 1e9,
                      "peak": PEAK["hbm"], "unit": "GB/s",
-                     "frac": cache / (gram_ms * 1e-3) / 1e9 / PEAK["hbm"],
+                     "frac": main_bytes / (gram_ms * 1e-3) / 1e9 / PEAK["hbm"],
                      "traffic": None},
     }
     print(json.dumps(rec), flush=True)

@@ -252,11 +252,18 @@ size_t lla_workspace_bytes(int B, int H, int n, int d, int dtype, int kernel);
  * whose query sits at position n - 1 (q_{n-1} = q). Same estimator, same
  * mean-centred CG system and the same CG policy as lla_forward_ex.
  * The centred Gram matrix sum_j w_j (k_j - kbar)(k_j - kbar)^T of the query
- * (d x d) is formed once on the matrix cores, its operands carried as two
- * fp16 terms each, and CG runs on it plus lambda I in fp32: the cache is read
- * three times whatever the iteration count, and working memory is n + O(d^2)
- * floats per head. In exact arithmetic the iterates are those of the
- * matrix-free CG.
+ * (d x d) is formed once on the matrix cores and CG runs on it plus lambda I
+ * in fp32; in exact arithmetic the iterates are those of the matrix-free CG.
+ * bf16 caches: one pass over K and V yields, per chunk of keys and against
+ * the chunk's max, the moments, the uncentred Gram matrix and the cross
+ * moment sum_j w_j v_j k_j^T (bf16 products, w k and w v in two bf16 terms,
+ * fp32 sums); the head's centred system follows by the parallel-axis
+ * identity and the output in the covariance form
+ * out = (sum w v - C rho_c + (sum w v)(kbar . rho_c)) / omega. The fp32 sums
+ * need |k|^2 and |v||k| times the cache length within fp32's range. fp32
+ * caches: the centred Gram matrix with fp16 operands in two terms each; the
+ * cache is read three times. Working memory is O(d^2) floats per chunk of
+ * keys (bf16) or n + O(d^2) floats per head (fp32).
  * ------------------------------------------------------------------------ */
 typedef struct lla_decode_args {
   int dtype;          /* LLA_DTYPE_F32 or LLA_DTYPE_BF16 */
@@ -276,7 +283,8 @@ typedef struct lla_decode_args {
   float* cg_resid;    /* [B][H]    ||r_k|| / ||r_0|| at exit */
   void* workspace;    /* optional caller workspace (device), as for lla_forward_ex */
   size_t workspace_bytes;
-  hipEvent_t ev_main_begin; /* optional: recorded around the Gram kernel */
+  hipEvent_t ev_main_begin; /* optional: recorded around the main kernel (bf16: the
+                               pass over the cache; fp32: the Gram kernel) */
   hipEvent_t ev_main_end;
 } lla_decode_args;
 

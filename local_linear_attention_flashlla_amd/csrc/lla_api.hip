@@ -365,7 +365,7 @@ int lla_decode_ex(const lla_decode_args* a, hipStream_t stream) {
   lla::DecodeParams p;
   const int st = decode_validate(a, &p);
   if (st != LLA_OK) return st;
-  const size_t need = lla::decode_workspace_bytes(p.BH, p.n, p.d);
+  const size_t need = lla::decode_workspace_bytes(p.BH, p.n, p.d, p.dtype);
   void* ws = a->workspace;
   bool owned = false;
   if (ws) {
@@ -396,7 +396,7 @@ int lla_decode_noalloc(const lla_decode_args* a, hipStream_t stream) {
   if (st != LLA_OK) return st;
   if (a->workspace || a->workspace_bytes)
     return fail(LLA_ERR_INVALID_ARG, "lla_decode_noalloc takes no workspace (its scratch is static)");
-  const size_t need = lla::decode_workspace_bytes(p.BH, p.n, p.d);
+  const size_t need = lla::decode_workspace_bytes(p.BH, p.n, p.d, p.dtype);
   if (need > lla::kDecodeScratchBytes)
     return fail(LLA_ERR_WORKSPACE, "decode needs %zu bytes of scratch; the static scratch holds %zu "
                 "(use lla_decode_ex with a workspace)", need, lla::kDecodeScratchBytes);
@@ -424,7 +424,7 @@ size_t lla_decode_workspace_bytes(int B, int H, int n, int d, int dtype) {
   if (dtype != LLA_DTYPE_F32 && dtype != LLA_DTYPE_BF16) return 0;
   const unsigned long long bh = (unsigned long long)B * (unsigned long long)H;
   if (bh > 65535ULL || bh * (unsigned long long)n > (1ULL << 36)) return 0;
-  return lla::decode_workspace_bytes((int)bh, n, d);
+  return lla::decode_workspace_bytes((int)bh, n, d, dtype);
 }
 
 int lla_backward_ex(const lla_bwd_args* a, hipStream_t stream) {

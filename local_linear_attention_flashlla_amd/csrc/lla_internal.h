@@ -54,14 +54,15 @@ struct DecodeParams {
   float cg_rel_tol;
   void* workspace;
   size_t workspace_bytes;
-  hipEvent_t ev_main_begin;  // optional, recorded around the Gram kernel
+  hipEvent_t ev_main_begin;  // optional, recorded around the main kernel (bf16: the one
+                             // pass over the cache; fp32: the Gram kernel)
   hipEvent_t ev_main_end;
 };
 
 // decode-shaped forward (one query per head against n keys): d in {64,128},
 // fp32 or bf16 inputs
 bool decode_supported(int d);
-size_t decode_workspace_bytes(int BH, int n, int d);
+size_t decode_workspace_bytes(int BH, int n, int d, int dtype);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 // Static per-device scratch of lla_decode_noalloc: its size, and its device
 // address on the current device (looked up once per device, then cached).

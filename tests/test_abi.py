@@ -183,11 +183,20 @@ def test_decode_invalid_arguments_are_rejected_on_the_host(lib, field, value, st
 
 def test_decode_workspace_is_linear_in_n(lib):
     assert lib.lla_decode_workspace_bytes(1, 1, 100, 32, _lib.LLA_DTYPE_BF16) == 0
-    sizes = [lib.lla_decode_workspace_bytes(4, 8, n, 128, _lib.LLA_DTYPE_BF16)
+    # fp32 caches: the score buffer grows with n; the Gram partials do not
+    sizes = [lib.lla_decode_workspace_bytes(4, 8, n, 128, _lib.LLA_DTYPE_F32)
              for n in (4096, 8192, 16384)]
     assert all(s > 0 for s in sizes)
-    # the score buffer grows with n; the Gram partials do not
     assert sizes[1] - sizes[0] >= 4 * 8 * 4096 * 4 and sizes[2] - sizes[1] >= 4 * 8 * 8192 * 4
+    # bf16 caches (one pass over the cache): chunk partials of 4 + 2d + 2d^2
+    # floats, at most one chunk per 512 keys and about 256 chunks in all, and
+    # with several chunks per head one combined partial per head
+    psz = (4 + 2 * 128 + 2 * 128 * 128) * 4
+    for bh, n in ((32, 1), (32, 100), (32, 4096), (32, 16384), (256, 4096), (1, 65536)):
+        got = lib.lla_decode_workspace_bytes(bh, 1, n, 128, _lib.LLA_DTYPE_BF16)
+        per_head = max(1, min(64, 256 // bh, n // 512))
+        want = bh * per_head * psz + (bh * psz if per_head > 1 else 0)
+        assert want <= got < want + 512, (bh, n, got, want)
 
 
 def test_null_args_pointer(lib):
