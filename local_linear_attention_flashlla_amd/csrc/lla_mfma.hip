@@ -531,6 +531,7 @@ struct MainParams {
   const float* rho_in;  // supplied rho_i [BH][n][d] (no CG solve), or NULL
   float* rho_c;      // optional [BH][n][d]: the centred system's solution
   const _Float16* pcm;  // preconditioners (see pc_build), used by the CG kernel with PRECOND
+  _Float16* kb16;    // fp16 kbar fragments (preconditioned CG), per 32-query group
   const float* pcs;
   int nslots;
   int BH, n, nchunk, nblk;
@@ -662,6 +663,7 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
   const __amdgpu_buffer_rsrc_t xs = make_rsrc(P.xs + wslot * (32 * D), 32 * D * 4);
   const __amdgpu_buffer_rsrc_t kbs = make_rsrc(P.kbs + wslot * (32 * D), 32 * D * 4);
   const __amdgpu_buffer_rsrc_t rsl = make_rsrc(P.rs + wslot * (32 * D), 32 * D * 4);
+  const __amdgpu_buffer_rsrc_t kb16r = make_rsrc(P.kb16 + wslot * (32 * D), 32 * D * 2);
   float* qst = P.qs + wslot * 128;  // [0, 64): row max m2; [64, 128): omega
   const size_t orow = static_cast<size_t>(bh) * n + (qvalid ? qi : 0);
 
@@ -918,20 +920,18 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
     if constexpr (!PCG) {
       #pragma unroll
       for (int t = 0; t < NKS; ++t) sKb[wave][t][lane] = kb16[t];
+    } else {
+      // (the preconditioner takes the LDS that sKb would: the fragments wait in
+      // a slab of their own, 16 B per lane each)
+      #pragma unroll
+      for (int t = 0; t < NKS; ++t)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, kb16[t]), kb16r, t * 1024 + lane * 16, 0, 0);
     }
   }
   // fragment t of kbar in fp16, operand order (the same values as sKb holds)
   auto kb_frag = [&](int t) __attribute__((always_inline)) {
     if constexpr (PCG) {
-      const int c0 = (t >> 1) * 4 + 2 * (t & 1);
-      const floatx4 a = slab_ld(kbs, c0, lane), b = slab_ld(kbs, c0 + 1, lane);
-      half8 h;
-      #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        h[e] = static_cast<_Float16>(a[e]);
-        h[4 + e] = static_cast<_Float16>(b[e]);
-      }
-      return h;
+      return __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(kb16r, t * 1024 + lane * 16, 0, 0));
     } else {
       return sKb[wave][t][lane];
     }
@@ -1337,6 +1337,13 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
         if (SPLIT_U || first_block) acc[k >> 1] = mfma(f, ulb[k & 1], acc[k >> 1]);
       }
     }
+    // (preconditioned) kbar's fragments for the correction below, loaded while
+    // the last products, the pair exchange and the barrier complete
+    half8 kbf[PCG ? NKS : 1];
+    if constexpr (PCG) {
+      #pragma unroll
+      for (int t = 0; t < NKS; ++t) kbf[t] = kb_frag(t);
+    }
     usum = pair_sum(usum);
     // every wave is done with the tiles: start the next sweep's first copies
     __syncthreads();
@@ -1352,7 +1359,7 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
     for (int mb = 0; mb < NMB; ++mb)
       #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const half8 kb = kb_frag(2 * mb + h);
+        const half8 kb = PCG ? kbf[(2 * mb + h) % (PCG ? NKS : 1)] : kb_frag(2 * mb + h);
         #pragma unroll
         for (int c = 0; c < 8; ++c) {
           const int r = 8 * h + c;
@@ -1806,6 +1813,7 @@ MainParams main_params(const FwdParams& p, const Workspace& w) {
   m.vt = w.vt;
   m.xs = w.xs;
   m.kbs = w.kbs;
+  m.kb16 = w.kb16;
   m.rs = w.rs;
   m.qs = w.qs;
   m.rho_in = p.rho_in;
@@ -1979,7 +1987,8 @@ size_t mfma_workspace_bytes(int BH, int n, int d) {
          align256(static_cast<size_t>(BH) * nqpad * 4 * sizeof(float)) +
          align256(static_cast<size_t>(BH) * nsl * 2 * d * d * sizeof(_Float16)) +
          align256(static_cast<size_t>(BH) * nsl * sizeof(float)) +
-         align256(static_cast<size_t>(BH) * nsl * d * sizeof(float));
+         align256(static_cast<size_t>(BH) * nsl * d * sizeof(float)) +
+         align256(static_cast<size_t>(BH) * nqpad * d * sizeof(_Float16));
 }
 
 hipError_t launch_mfma(const FwdParams& p, hipStream_t stream) {

@@ -147,6 +147,8 @@ struct Workspace {
                     // (while they are built: the slots' fp32 Gram matrices, D x D)
   float* pcs;       // [BH][nslots] their power-of-two scales sM (0: not built)
   float* pct;       // [BH][nslots][D] key sums of the slots' prefixes (build only)
+  _Float16* kb16;   // fp16 kbar for the preconditioned CG: per 32-query group, the D / 8
+                    // fragments of 8 halfs in MFMA operand order, lane-contiguous (16 B per lane)
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -181,6 +183,8 @@ Workspace carve(void* base, int BH, int n, int d) {
   w.pcs = reinterpret_cast<float*>(p);
   p += align256(static_cast<size_t>(BH) * nsl * sizeof(float));
   w.pct = reinterpret_cast<float*>(p);
+  p += align256(static_cast<size_t>(BH) * nsl * d * sizeof(float));
+  w.kb16 = reinterpret_cast<_Float16*>(p);
   return w;
 }
 
