@@ -1340,9 +1340,12 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
     // (preconditioned) kbar's fragments for the correction below, loaded while
     // the last products, the pair exchange and the barrier complete
     half8 kbf[PCG ? NKS : 1];
+    floatx4 xpre[PCG ? NMB * 4 : 1];  // and the iterate's slab, for the update
     if constexpr (PCG) {
       #pragma unroll
       for (int t = 0; t < NKS; ++t) kbf[t] = kb_frag(t);
+      #pragma unroll
+      for (int c = 0; c < NMB * 4; ++c) xpre[c] = slab_ld(xs, c, lane);
     }
     usum = pair_sum(usum);
     // every wave is done with the tiles: start the next sweep's first copies
@@ -1393,11 +1396,9 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
       }
     if constexpr (PRECOND) {
       // the iterate waits in its workspace slab (registers are short during
-      // the sweep): x += al d, one read and one write of this lane's 256
-      // bytes, all reads issued before the first write
-      floatx4 xc[NMB * 4];
-      #pragma unroll
-      for (int c = 0; c < NMB * 4; ++c) xc[c] = slab_ld(xs, c, lane);
+      // the sweep): x += al d, one read (issued at the end of the sweep) and
+      // one write of this lane's 256 bytes
+      floatx4 (&xc)[NMB * 4] = xpre;
       #pragma unroll
       for (int c = 0; c < NMB * 4; ++c) {
         const int mb = c >> 2, h = (c & 3) >> 1, e0 = 4 * (c & 1);
