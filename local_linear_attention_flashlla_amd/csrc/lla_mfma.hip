@@ -375,12 +375,15 @@ __global__ __launch_bounds__(NT) void pc_scan(int nslots, float* __restrict__ gr
 }
 
 template <int D>
-__global__ __launch_bounds__(NT) void pc_invert(const float* __restrict__ partial, int nchunk,
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void pc_invert(const float* __restrict__ partial, int nchunk,
                                                 int nslots, float lambda, float* __restrict__ gram,
                                                 const float* __restrict__ tsum,
                                                 float* __restrict__ pcs) {
   constexpr int EB = D / 16;                 // side of each thread's block of M
-  __shared__ float sA[D][D + 1];
+  // a quarter of M's rows at a time, for the transposed reads of the
+  // symmetrisation (a whole D x D buffer would cap the kernel at two
+  // workgroups per compute unit)
+  __shared__ float sQ[D / 4][D + 1];
   __shared__ float sT[D];
   __shared__ float sRow[2][D], sCol[2][D];
   __shared__ float sRed[4];
@@ -463,38 +466,47 @@ __global__ __launch_bounds__(NT) void pc_invert(const float* __restrict__ partia
       }
     }
   }
-  __syncthreads();
-  // ---- symmetrise, scale, split into two fp16 terms, store over the Gram
-  if (ok) {
+  // ---- the largest diagonal element (from the diagonal blocks), then
+  // symmetrise, scale, split into two fp16 terms, store over the Gram
+  float dg = 0.f;
+  if (ok && br == bc) {
     #pragma unroll
-    for (int i = 0; i < EB; ++i)
-      #pragma unroll
-      for (int j = 0; j < EB; ++j) sA[EB * br + i][EB * bc + j] = A[i][j];
+    for (int i = 0; i < EB; ++i) dg = fmaxf(dg, A[i][i]);
   }
-  __syncthreads();
-  if (tid < 64 * ((D + 63) / 64)) {
-    const float dg = (ok && tid < D) ? sA[tid][tid] : 0.f;
-    const float m = wave_max(dg);
-    if (lane == 0) sRed[wave] = m;
-  }
+  dg = wave_max(dg);
+  __syncthreads();  // (sRed was read during the set-up)
+  if (lane == 0) sRed[wave] = dg;
   __syncthreads();
   float mdiag = sRed[0];
   #pragma unroll
-  for (int w = 1; w < (D + 63) / 64; ++w) mdiag = fmaxf(mdiag, sRed[w]);
-  const bool good = ok && mdiag > 0.f && mdiag < INFINITY;
+  for (int w = 1; w < NT / 64; ++w) mdiag = fmaxf(mdiag, sRed[w]);
+  const bool good = ok && mdiag > 0.f && mdiag < INFINITY;  // uniform
   const float sM = good ? pow2_ceil(mdiag) : 0.f;
-  if (good) {
-    // (every thread has read its part of the Gram before the first barrier)
-    _Float16* hiM = reinterpret_cast<_Float16*>(G);
-    _Float16* loM = hiM + D * D;
-    const float inv = 1.f / sM;
+  // (every thread has read its part of the Gram before the first barrier)
+  _Float16* hiM = reinterpret_cast<_Float16*>(G);
+  _Float16* loM = hiM + D * D;
+  const float inv = good ? 1.f / sM : 0.f;
+  // quarter qr holds rows [D / 4 qr, D / 4 (qr + 1)): the block rows br with
+  // br / 4 == qr (16 block rows of EB); a thread takes the transposed values
+  // of its block from the quarter that holds its block column's rows
+  #pragma unroll
+  for (int qr = 0; qr < 4; ++qr) {
+    if (!good) break;  // uniform
+    if (br / 4 == qr) {
+      #pragma unroll
+      for (int i = 0; i < EB; ++i)
+        #pragma unroll
+        for (int j = 0; j < EB; ++j) sQ[EB * br + i - D / 4 * qr][EB * bc + j] = A[i][j];
+    }
+    __syncthreads();
+    if (bc / 4 == qr) {
     #pragma unroll
     for (int i = 0; i < EB; ++i) {
       const int row = EB * br + i;
       #pragma unroll
       for (int j = 0; j < EB; ++j) {
         const int col = EB * bc + j;
-        const float v = 0.5f * (sA[row][col] + sA[col][row]) * inv;
+        const float v = 0.5f * (A[i][j] + sQ[col - D / 4 * qr][row]) * inv;
         const _Float16 hi = static_cast<_Float16>(v);
         const _Float16 lo = static_cast<_Float16>(v - static_cast<float>(hi));
         // operand order: the A fragment of k-step t, block mb for lane
@@ -507,6 +519,8 @@ __global__ __launch_bounds__(NT) void pc_invert(const float* __restrict__ partia
         loM[fi] = lo;
       }
     }
+    }
+    __syncthreads();  // the next quarter overwrites sQ
   }
   if (tid == 0) pcs[slot] = sM;
 }
