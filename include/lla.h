@@ -357,9 +357,10 @@ typedef struct lla_bwd_args {
   size_t workspace_bytes;
   hipEvent_t ev_main_begin; /* optional: recorded around the adjoint CG kernel */
   hipEvent_t ev_main_end;
-  int flags;          /* LLA_FLAG_SPLIT_U: the adjoint's right-hand side and CG
-                         products carry w * (...) as two fp16 terms (slower,
-                         more exact; see lla_backward_ex). LLA_FLAG_PRECOND,
+  int flags;          /* LLA_FLAG_SPLIT_U: the adjoint CG's products carry
+                         w * (...) as two fp16 terms (slower, more exact; the
+                         right-hand side and the moments always carry two).
+                         LLA_FLAG_PRECOND,
                          LLA_FLAG_NO_PRECOND: as for the forward, whose rule
                          the adjoint solve follows (preconditioned when
                          cg_rel_tol > 0 unless a flag says otherwise); pass

@@ -106,6 +106,7 @@ struct BwdWorkspace {
   _Float16* vr;   // [BH][nblk][BK*D] sv v, row layout
   char* rec;      // [BH][nblk] per-query-tile records
   int32_t* jstar; // [BH][n] maximising key per query
+  float* gvb;     // [BH][n] g . vbar per query (the weighted mean of g . v_j)
 };
 
 size_t rec_bytes_d(int d) { return d == 128 ? rec_bytes<128>() : rec_bytes<64>(); }
@@ -119,6 +120,8 @@ BwdWorkspace carve_bwd(void* base, int BH, int n, int d) {
   w.rec = p;
   p += align256(static_cast<size_t>(BH) * nblk * rec_bytes_d(d));
   w.jstar = reinterpret_cast<int32_t*>(p);
+  p += align256(static_cast<size_t>(BH) * n * sizeof(int32_t));
+  w.gvb = reinterpret_cast<float*>(p);
   return w;
 }
 
@@ -171,6 +174,7 @@ struct SweepParams {
   float* qs;
   const char* rec;
   int32_t* jstar;
+  float* gvb;
   float* dq;
   int BH, n, nchunk, nblk, nq32;
 };
@@ -180,7 +184,7 @@ struct SweepParams {
 // three LDS buffers with one barrier per tile.
 //   MODE 0: the adjoint right-hand side and the maximising key;
 //   MODE 1: dq.
-template <int D, int MODE, bool SPLIT = false>
+template <int D, int MODE>
 __global__ __launch_bounds__(NT) void bwd_sweep(SweepParams P) {
   constexpr int NKS = D / 16, NMB = D / 32, NW = NT / 64, BQW = 32 * NW;
   // The dq sweep runs a two-stage pipeline over three tile buffers; the
@@ -249,7 +253,7 @@ __global__ __launch_bounds__(NT) void bwd_sweep(SweepParams P) {
   // where the fit nearly interpolates; dk needs two, see bwd_keys)
   half8 rh[MODE == 1 ? NKS : 1], rl[MODE == 1 ? NKS : 1], yop[MODE == 1 ? NKS : 1];
   float sinit_v = 0.f, ginit_v = 0.f;
-  float sg = 1.f, om = 0.f;
+  float sg = 1.f, om = 0.f, gb_row = 0.f;
   float c_rinit = 0.f, c_rslope = 0.f, c_yinit = 0.f, c_eg = 0.f, c_ey = 0.f, c_tau = 0.f,
         c_f = 0.f, c_oms = 0.f, c_dqs = 0.f;
   int jst = -1;
@@ -298,6 +302,7 @@ __global__ __launch_bounds__(NT) void bwd_sweep(SweepParams P) {
     sinit_v = -qst[lane];
     om = qst[64 + lane];
     ginit_v = -sg * sv * gb;
+    gb_row = gb;
   } else {
     // from the query tile's record (written by bwd_rows); a wave past the end
     // of the head has none and takes no part in the products
@@ -344,6 +349,11 @@ __global__ __launch_bounds__(NT) void bwd_sweep(SweepParams P) {
     #pragma unroll
     for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
   float usum = 0.f;
+  // (right-hand side) the row sums of w and of w (G - g.out): g . vbar from
+  // this sweep's own weights. Through the forward's output instead, its error
+  // (small against out, not against the O(lambda) residuals e_j of a nearly
+  // interpolating fit, which it shifts) would reach dk multiplied by 1/lambda.
+  float wsum = 0.f, wgsum = 0.f;
   float bestv = -INFINITY;
   int bestk = qvalid ? qi : 0;  // (stays a visible key even for NaN scores)
 
@@ -406,20 +416,19 @@ __global__ __launch_bounds__(NT) void bwd_sweep(SweepParams P) {
           bestk = kj;
         }
         wv[r] = w;
+        wsum += w;
+        wgsum = fmaf(w, X[1][r], wgsum);
         if (r & 1) {
-          if constexpr (SPLIT) {
-            const float u0 = wv[r - 1] * X[1][r - 1], u1 = w * X[1][r];
-            const half2v hu = pack_sum(u0, u1, usum);
-            const half2v lo = pack_sum(u0 - static_cast<float>(hu[0]), u1 - static_cast<float>(hu[1]), usum);
-            U[r >> 3][(r - 1) & 7] = hu[0];
-            U[r >> 3][r & 7] = hu[1];
-            Ul[r >> 3][(r - 1) & 7] = lo[0];
-            Ul[r >> 3][r & 7] = lo[1];
-          } else {
-            const half2v hu = mul_pack_sum(wv[r - 1], X[1][r - 1], w, X[1][r], usum);
-            U[r >> 3][(r - 1) & 7] = hu[0];
-            U[r >> 3][r & 7] = hu[1];
-          }
+          // U in two fp16 terms (hi + lo): h feeds e_j = beta_j / omega -
+          // c_j . y, a difference of O(1) terms that is O(lambda) where the
+          // fit nearly interpolates
+          const float u0 = wv[r - 1] * X[1][r - 1], u1 = w * X[1][r];
+          const half2v hu = pack_sum(u0, u1, usum);
+          const half2v lo = pack_sum(u0 - static_cast<float>(hu[0]), u1 - static_cast<float>(hu[1]), usum);
+          U[r >> 3][(r - 1) & 7] = hu[0];
+          U[r >> 3][r & 7] = hu[1];
+          Ul[r >> 3][(r - 1) & 7] = lo[0];
+          Ul[r >> 3][r & 7] = lo[1];
         }
       } else {
         const float A = fmaf(c_rslope, X[2][r], 1.f);
@@ -436,7 +445,7 @@ __global__ __launch_bounds__(NT) void bwd_sweep(SweepParams P) {
     for (int h = 0; h < 2; ++h)
       #pragma unroll
       for (int mb = 0; mb < NMB; ++mb) acc[mb] = mfma(kt_frag_at(tb_, mb, h), U[h], acc[mb]);
-    if constexpr (SPLIT)
+    if constexpr (MODE == 0)
       #pragma unroll
       for (int h = 0; h < 2; ++h)
         #pragma unroll
@@ -502,7 +511,13 @@ __global__ __launch_bounds__(NT) void bwd_sweep(SweepParams P) {
         for (int b = 0; b < 4; ++b) rc[b] = (acc[mb][4 * a + b] - usum * kb[b]) * inv;
         slab_st(rsl, mb * 4 + a, lane, rc);
       }
-    if (qvalid && g == 0) P.jstar[orow] = bestk;
+    // g . vbar = g . out + sum_j w_j (g . v_j - g . out) / sum_j w_j
+    wsum = pair_sum(wsum);
+    wgsum = pair_sum(wgsum);
+    if (qvalid && g == 0) {
+      P.jstar[orow] = bestk;
+      P.gvb[orow] = gb_row + (wsum > 0.f ? wgsum / (wsum * sg * sv) : 0.f);
+    }
   } else {
     // The max's share: the row's sum of the operands the products used, taken
     // off at the maximising key, so that dq's row of dL/ds sums to zero as it
@@ -531,7 +546,6 @@ __global__ __launch_bounds__(NT) void bwd_sweep(SweepParams P) {
 // ---------------------------------------------------------------------------
 struct RowsParams {
   const uint16_t* q;
-  const float* out;
   const float* dout;
   const float* rho_c;
   const float* partial;
@@ -540,6 +554,7 @@ struct RowsParams {
   const float* rs;
   const float* qs;
   const int32_t* jstar;
+  const float* gvb;
   char* rec;
   int BH, n, nchunk, nblk, nq32;
   float lambda;
@@ -588,7 +603,7 @@ __global__ __launch_bounds__(NT) void bwd_rows(RowsParams P) {
   // per-query vectors in the accumulator layout: slot (mb, a, b) is dim
   // 32 mb + 8 a + 4 g + b
   float qv[NMB][4][4], rv[NMB][4][4], gv[NMB][4][4], kb[NMB][4][4], ys[NMB][4][4];
-  float gb = 0.f, gn = 0.f;
+  float gn = 0.f;
   #pragma unroll
   for (int mb = 0; mb < NMB; ++mb)
     #pragma unroll
@@ -614,18 +629,6 @@ __global__ __launch_bounds__(NT) void bwd_rows(RowsParams P) {
     }
   gn = pair_sum(gn);
   const float sg = gn > 0.f ? pow2_floor(64.f / sqrtf(gn)) : 1.f;
-  gb = 0.f;
-  #pragma unroll
-  for (int mb = 0; mb < NMB; ++mb)
-    #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int dim = 32 * mb + 8 * a + 4 * g;
-      const float4 b4 = *reinterpret_cast<const float4*>(P.out + orow * D + dim);
-      const float be[4] = {b4.x, b4.y, b4.z, b4.w};
-      #pragma unroll
-      for (int b = 0; b < 4; ++b) gb += gv[mb][a][b] * (qvalid ? be[b] : 0.f);
-    }
-  gb = pair_sum(gb);
   // x_s = rho_c / s is the forward's scaled iterate
   float kbx = 0.f, kby = 0.f, kap = 0.f, yu = 0.f, yx = 0.f, rn = 0.f, yn = 0.f, mxx = 0.f, mxy = 0.f;
   #pragma unroll
@@ -661,7 +664,8 @@ __global__ __launch_bounds__(NT) void bwd_rows(RowsParams P) {
   const float om = qst[64 + lane], m2 = qst[lane];
   const float tau = qvalid ? kap / om - yu : 0.f;
   const float msum = -scaled_ridge(P.lambda, s) * yx;
-  const float gvbar = gb + kap;
+  // g . vbar, formed by the right-hand-side sweep from its weights
+  const float gvbar = qvalid ? P.gvb[orow] : 0.f;
   // |dL/ds| <= (1 + 2 kmax |rho_c|)(2 |g| vmax / omega + 2 kmax |y|) + |tau|
   // (+ |msum| at the maximising key): the dq product's operand scale
   float bound = (1.f + 2.f * kmax * sqrtf(rn)) * (2.f * sqrtf(gn) * vmax / om + 2.f * kmax * sqrtf(yn)) +
@@ -970,7 +974,11 @@ hipError_t bwd_d(const BwdParams& p, hipStream_t stream) {
   f.flags = p.flags & (LLA_FLAG_SPLIT_U | LLA_FLAG_PRECOND | LLA_FLAG_NO_PRECOND);
   f.workspace = p.workspace;
   f.workspace_bytes = p.workspace_bytes;
-  hipError_t e = mfma_moments(f, stream);
+  // (the weights of the moments in two fp16 terms: the right-hand side below
+  // subtracts (sum U) kbar, which is exact only for the kbar of the sweep's own
+  // weights, and a nearly interpolating fit multiplies the difference by
+  // 1/lambda in dk)
+  hipError_t e = mfma_moments(f, true, stream);
   if (e != hipSuccess) return e;
   const Workspace w = carve(p.workspace, p.BH, n, D);
   const BwdWorkspace bw = carve_bwd(p.workspace, p.BH, n, D);
@@ -993,6 +1001,7 @@ hipError_t bwd_d(const BwdParams& p, hipStream_t stream) {
   sp.qs = w.qs;
   sp.rec = bw.rec;
   sp.jstar = bw.jstar;
+  sp.gvb = bw.gvb;
   sp.dq = p.dq;
   sp.BH = p.BH;
   sp.n = n;
@@ -1000,10 +1009,7 @@ hipError_t bwd_d(const BwdParams& p, hipStream_t stream) {
   sp.nblk = nblk;
   sp.nq32 = nq32;
   const dim3 grid(static_cast<unsigned>(static_cast<long long>(nqb) * p.BH));
-  if (p.flags & LLA_FLAG_SPLIT_U)
-    hipLaunchKernelGGL((bwd_sweep<D, 0, true>), grid, dim3(NT), 0, stream, sp);
-  else
-    hipLaunchKernelGGL((bwd_sweep<D, 0>), grid, dim3(NT), 0, stream, sp);
+  hipLaunchKernelGGL((bwd_sweep<D, 0>), grid, dim3(NT), 0, stream, sp);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // the adjoint solve takes the forward's policy, preconditioner included
@@ -1021,7 +1027,6 @@ hipError_t bwd_d(const BwdParams& p, hipStream_t stream) {
   }
   RowsParams rp{};
   rp.q = sp.q;
-  rp.out = p.out;
   rp.dout = p.dout;
   rp.rho_c = p.rho_c;
   rp.partial = w.partial;
@@ -1030,6 +1035,7 @@ hipError_t bwd_d(const BwdParams& p, hipStream_t stream) {
   rp.rs = w.rs;
   rp.qs = w.qs;
   rp.jstar = bw.jstar;
+  rp.gvb = bw.gvb;
   rp.rec = bw.rec;
   rp.BH = p.BH;
   rp.n = n;
@@ -1063,7 +1069,8 @@ size_t bwd_workspace_bytes(int BH, int n, int d) {
   return mfma_workspace_bytes(BH, n, d) +
          align256(static_cast<size_t>(BH) * nblk * BK * d * sizeof(_Float16)) +
          align256(static_cast<size_t>(BH) * nblk * rec_bytes_d(d)) +
-         align256(static_cast<size_t>(BH) * n * sizeof(int32_t));
+         align256(static_cast<size_t>(BH) * n * sizeof(int32_t)) +
+         align256(static_cast<size_t>(BH) * n * sizeof(float));
 }
 
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {

@@ -83,7 +83,7 @@ hipError_t launch_mfma(const FwdParams& p, hipStream_t stream);
 // workspace: the prepasses and the moment kernel (per-query kbar, omega, row
 // max; the residual slab set to mu), and the CG kernel alone, which solves
 // Sigma_c x = r for whatever right-hand side r the residual slab holds.
-hipError_t mfma_moments(const FwdParams& p, hipStream_t stream);
+hipError_t mfma_moments(const FwdParams& p, bool two_term, hipStream_t stream);
 // The preconditioners of the CG kernel (no-op when the call's flags and
 // tolerance leave CG unpreconditioned), and the CG kernel, which uses them
 // under the same rule (LLA_FLAG_PRECOND, LLA_FLAG_NO_PRECOND, else

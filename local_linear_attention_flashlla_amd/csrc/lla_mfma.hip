@@ -766,15 +766,20 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
   floatx16 sinit;  // -mref, the initial value of the score accumulators
   #pragma unroll
   for (int r = 0; r < 16; ++r) sinit[r] = -mref;
-  half8 wa[2], wb[2];
+  // (SPLIT_U: the weights as two fp16 terms, hi + lo, for the backward pass,
+  // whose right-hand side needs kbar to about 2^-22 of the weights)
+  half8 wa[2], wb[2], wal[2], wbl[2];
   #pragma unroll
   for (int h = 0; h < 2; ++h)
     #pragma unroll
-    for (int c = 0; c < 8; ++c) wb[h][c] = static_cast<_Float16>(0.f);
+    for (int c = 0; c < 8; ++c) {
+      wb[h][c] = static_cast<_Float16>(0.f);
+      wbl[h][c] = static_cast<_Float16>(0.f);
+    }
   // step j: Y += Kt(j-1) W(j-1); S(j+1) - mref; the max of S(j) over the first
   // half of the step, then (rarely) a new reference, then W(j) = exp2(S(j) - mref)
   auto wstep = [&](auto JM, auto masked, int j, floatx16& sc, floatx16& sn, const half8 (&up)[2],
-                   half8 (&uc)[2]) __attribute__((always_inline)) {
+                   half8 (&uc)[2], const half8 (&upl)[2], half8 (&ucl)[2]) __attribute__((always_inline)) {
     constexpr int jm = decltype(JM)::value;
     constexpr bool MASKED = decltype(masked)::value;
     const _Float16* kbn = KR(std::integral_constant<int, jm + 1>{});
@@ -818,7 +823,10 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
       }
       const half8 f = fr[k % PF];
       if (k < NY) {
-        if (doY) acc[k % NMB] = mfma(f, up[k / NMB], acc[k % NMB]);
+        if (doY) {
+          acc[k % NMB] = mfma(f, up[k / NMB], acc[k % NMB]);
+          if constexpr (SPLIT_U) acc[k % NMB] = mfma(f, upl[k / NMB], acc[k % NMB]);
+        }
       } else {
         const int t = k - NY;
         if (doF) {
@@ -847,6 +855,11 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
               const half2v hw = pack_sum(wv[r - 1], w, om);
               uc[r >> 3][(r - 1) & 7] = hw[0];
               uc[r >> 3][r & 7] = hw[1];
+              if constexpr (SPLIT_U) {
+                const half2v lw = pack_sum(wv[r - 1] - static_cast<float>(hw[0]), w - static_cast<float>(hw[1]), om);
+                ucl[r >> 3][(r - 1) & 7] = lw[0];
+                ucl[r >> 3][r & 7] = lw[1];
+              }
             }
           }
         }
@@ -856,21 +869,24 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
     step_barrier<D, NW, 2>();
   };
   for (int j0 = 0; j0 < ps_steps - NW; j0 += 4) {
-    wstep(I0{}, std::false_type{}, j0 + 0, sa, sb, wb, wa);
-    wstep(I1{}, std::false_type{}, j0 + 1, sb, sa, wa, wb);
-    wstep(I2{}, std::false_type{}, j0 + 2, sa, sb, wb, wa);
-    wstep(I3{}, std::false_type{}, j0 + 3, sb, sa, wa, wb);
+    wstep(I0{}, std::false_type{}, j0 + 0, sa, sb, wb, wa, wbl, wal);
+    wstep(I1{}, std::false_type{}, j0 + 1, sb, sa, wa, wb, wal, wbl);
+    wstep(I2{}, std::false_type{}, j0 + 2, sa, sb, wb, wa, wbl, wal);
+    wstep(I3{}, std::false_type{}, j0 + 3, sb, sa, wa, wb, wal, wbl);
   }
   for (int j0 = ps_steps - NW; j0 < ps_steps; j0 += 4) {
-    wstep(I0{}, std::true_type{}, j0 + 0, sa, sb, wb, wa);
-    wstep(I1{}, std::true_type{}, j0 + 1, sb, sa, wa, wb);
-    wstep(I2{}, std::true_type{}, j0 + 2, sa, sb, wb, wa);
-    wstep(I3{}, std::true_type{}, j0 + 3, sb, sa, wa, wb);
+    wstep(I0{}, std::true_type{}, j0 + 0, sa, sb, wb, wa, wbl, wal);
+    wstep(I1{}, std::true_type{}, j0 + 1, sb, sa, wa, wb, wal, wbl);
+    wstep(I2{}, std::true_type{}, j0 + 2, sa, sb, wb, wa, wbl, wal);
+    wstep(I3{}, std::true_type{}, j0 + 3, sb, sa, wa, wb, wal, wbl);
   }
   // Y += Kt^T W of the last tile (sKt3)
   if (ps_steps - 1 <= wlast) {
     #pragma unroll
-    for (int k = 0; k < NY; ++k) acc[k % NMB] = mfma(kt_frag_at(sKt3, k % NMB, k / NMB), wb[k / NMB], acc[k % NMB]);
+    for (int k = 0; k < NY; ++k) {
+      acc[k % NMB] = mfma(kt_frag_at(sKt3, k % NMB, k / NMB), wb[k / NMB], acc[k % NMB]);
+      if constexpr (SPLIT_U) acc[k % NMB] = mfma(kt_frag_at(sKt3, k % NMB, k / NMB), wbl[k / NMB], acc[k % NMB]);
+    }
   }
   __syncthreads();  // no tile copy may still be in flight when the kernel ends
   {
@@ -1965,13 +1981,17 @@ hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
 }
 
 template <int D>
-hipError_t moments_d(const FwdParams& p, hipStream_t stream) {
+hipError_t moments_d(const FwdParams& p, bool two_term, hipStream_t stream) {
   const Workspace w = carve(p.workspace, p.BH, p.n, D);
   hipError_t e = launch_prep<D>(p, w, stream);
   if (e != hipSuccess) return e;
   const MainParams m = main_params<D>(p, w);
-  hipLaunchKernelGGL((lla_mfma_phase<D, 1, false, kNW13>), grid_of(p, kNW13), dim3(64 * kNW13), 0,
-                     stream, m);
+  if (two_term)
+    hipLaunchKernelGGL((lla_mfma_phase<D, 1, true, kNW13>), grid_of(p, kNW13), dim3(64 * kNW13), 0,
+                       stream, m);
+  else
+    hipLaunchKernelGGL((lla_mfma_phase<D, 1, false, kNW13>), grid_of(p, kNW13), dim3(64 * kNW13), 0,
+                       stream, m);
   return hipGetLastError();
 }
 
@@ -2013,10 +2033,10 @@ hipError_t launch_mfma(const FwdParams& p, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
-hipError_t mfma_moments(const FwdParams& p, hipStream_t stream) {
+hipError_t mfma_moments(const FwdParams& p, bool two_term, hipStream_t stream) {
   if (p.n > kMfmaMaxN || p.BH > 0x7fffffff) return hipErrorInvalidValue;
-  if (p.d == 128) return moments_d<128>(p, stream);
-  if (p.d == 64) return moments_d<64>(p, stream);
+  if (p.d == 128) return moments_d<128>(p, two_term, stream);
+  if (p.d == 64) return moments_d<64>(p, two_term, stream);
   return hipErrorInvalidValue;
 }
 
