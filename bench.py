@@ -44,6 +44,14 @@ def algorithmic_flops(n: int, d: int, iters: np.ndarray) -> float:
     return float(d * np.sum(pairs[None, None, :] * (10.0 + 6.0 * iters.astype(np.float64))))
 
 
+def min_flops(n: int, d: int, iters: np.ndarray) -> float:
+    """The count without re-forming the scores in every CG sweep: per causal
+    pair 8d (one score product, the moment, rho and output products) plus 4d per
+    iteration (p.k and U k), F_min = d sum_i (i+1)(8 + 4 T_i)."""
+    pairs = np.arange(1, n + 1, dtype=np.float64)
+    return float(d * np.sum(pairs[None, None, :] * (8.0 + 4.0 * iters.astype(np.float64))))
+
+
 def cg_flops(n: int, d: int, iters: np.ndarray) -> float:
     """The conjugate-gradient share of algorithmic_flops: 6d per causal pair per
     iteration (q.k, p.k and U k)."""
@@ -545,19 +553,26 @@ def main(argv=None):
     flops = algorithmic_flops(n, d, iters_np)
     flops_cg = cg_flops(n, d, iters_np)
     flops_nom = algorithmic_flops(n, d, np.full_like(iters_np, wl.cg_max_iters))
+    flops_min = min_flops(n, d, iters_np)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
+    # (and events around each whole step, on the stream the library launches on)
+    sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
+        sev[i][0].record()
         step(events=ev[i])
+        sev[i][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
     kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    step_ev = np.array([a.elapsed_time(b) for a, b in sev])
 
     queries = B * H * n
     value = queries / (ms_step * 1e-3)
@@ -604,6 +619,8 @@ def main(argv=None):
         "tflops": tflops,
         "flops_per_step": flops,
         "flops_nominal": flops_nom,
+        "flops_min": flops_min,
+        "step_ms_events": {"median": float(np.median(step_ev)), "min": float(step_ev.min())},
         "cg_iters_mean": float(iters_np.mean()),
         "cg_iters_max": int(iters_np.max()),
         "main_kernel_ms": kern_ms,

@@ -21,6 +21,8 @@ def test_forward_flops_match_the_closed_form():
     assert bench.algorithmic_flops(n, d, iters) == 3_643_021_459_456
     assert bench.cg_flops(n, d, iters) == d * pairs * 6 * T * heads
     assert bench.backward_flops(n, d, iters) == d * pairs * (36 + 6 * T) * heads
+    # without the score products re-formed in each sweep: 8d + 4d per iteration
+    assert bench.min_flops(n, d, iters) == d * pairs * (8 + 4 * T) * heads
 
 
 def test_flops_count_each_query_with_its_own_iterations():
