@@ -135,16 +135,22 @@ enum {
    to that tolerance) and plain with cg_rel_tol = 0 (a fixed number of plain
    CG steps). The preconditioner is not on the pages; it is added because
    small ridges on clustered keys leave plain CG far from the answer after any
-   affordable number of steps. Queries are grouped in 32s; group g >= 1 uses
-       P_g = sum_{j < N_g} (k_j - m)(k_j - m)^T + lambda I,
-   the unit-weight scatter matrix of the first N_g keys (m their mean) plus
-   the ridge, with N_g = 32 g for g < 8 and, beyond, 32 g rounded down to a
-   multiple of 32 * 2^(floor(log2 g) - 2) (four prefix lengths per doubling of
-   g, each built once per head); group 0 is not preconditioned. N_g <= 32 g,
-   so every query of the group sees those keys. The recurrence is CG with
-   z = P_g^{-1} r in the direction update (p = z + beta p, beta = r'z'/rz),
-   x0 = 0 and the same stop rule on ||r||. P_g^{-1} is formed in fp32 and
-   applied in two fp16 terms. The vector path ignores both flags (plain CG). */
+   affordable number of steps. Queries are grouped in 32s (g = floor(i/32));
+   row i uses a unit-weight scatter matrix plus the ridge:
+     rows i < 256 (g < 8): P_i = sum_{j <= i} (k_j - m_g)(k_j - m_g)^T + lambda I,
+       the row's whole prefix about its group's point m_0 = k_0, m_g = the mean
+       of the first 32 g keys; applied as the group's matrix (the scatter of
+       those 32 g keys, lambda I for g = 0) and a rank-r correction by the
+       group's own keys (r = i - 32 g + 1 <= 32, Woodbury identity);
+     rows i >= 256: P_g = sum_{j < N_g} (k_j - m)(k_j - m)^T + lambda I, the
+       first N_g keys about their mean m, N_g = 32 g rounded down to a
+       multiple of 32 * 2^(floor(log2 g) - 2) (four prefix lengths per
+       doubling of g, each built once per head).
+   Every key used is visible to the row. The recurrence is CG with
+   z = P^{-1} r in the direction update (p = z + beta p, beta = r'z'/rz),
+   x0 = 0 and the same stop rule on ||r||. The group matrices' inverses are
+   formed in fp32 and applied in two fp16 terms. The vector path ignores both
+   flags (plain CG). */
 
 /* Full argument block of lla_forward_ex. Zero-initialise, then fill. */
 typedef struct lla_fwd_args {

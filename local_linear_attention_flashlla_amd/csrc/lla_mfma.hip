@@ -525,6 +525,223 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void pc
   if (tid == 0) pcs[slot] = sM;
 }
 
+// Rows below 256 (groups g < kWoodGroups of 32 queries): row i = 32 g + ql
+// is preconditioned with its whole prefix, P_i = sum_{j<=i} (k_j - m)(k_j - m)^T
+// + lam I about the group's point m (k_0 for g = 0, else the mean of the
+// first N = 32 g keys), scaled units. With P_g the group's matrix (the slot's
+// P for g >= 1, lam I for g = 0), M = P_g^{-1} as the CG kernel applies it,
+// U the group's 32 keys less m (columns past the head's end zero) and
+// A = I + U^T M U = L L^T:
+//     P_i^{-1} x = M x - (M U) mask(V^T mask(V mask(U^T M x))),  V = L^{-1},
+// mask keeping the keys j <= ql (a leading block of the inverse of a
+// triangular matrix is the inverse of its leading block). This kernel builds
+// one group's record: U (two fp16 terms, the row-tile layout of kr, so that
+// U^T z takes z straight from the accumulators), V and V^T, and -M U (two
+// terms each, MFMA operand order with the key index permuted as an
+// accumulator's rows are), each under a power-of-two scale. M U and A are
+// formed in fp32 on the vector ALU (0.5 M and 0.13 M multiply-adds at d = 128)
+// from the M the CG kernel applies (the slot's two fp16 terms); L and V by a
+// left-looking Cholesky and a forward substitution, one column per lane. A
+// pivot that is not positive and finite leaves the record invalid: the CG
+// kernel then preconditions those rows with P_g alone.
+template <int D>
+__global__ __launch_bounds__(NT) void pc_wood(const float* __restrict__ partial, int nchunk, int n,
+                                              int nblk, int nslots, float lambda,
+                                              const _Float16* __restrict__ kr,
+                                              const _Float16* __restrict__ pcm,
+                                              const float* __restrict__ pcs,
+                                              const float* __restrict__ tsum,
+                                              _Float16* __restrict__ pcw, float* __restrict__ pcws) {
+  constexpr int NMB = D / 32;
+  __shared__ float sM[D][D + 1];
+  __shared__ float sU[D][33];
+  __shared__ float sMU[D][33];
+  __shared__ float sA[32][33];
+  __shared__ float sV[32][33];
+  __shared__ float sm[D];
+  __shared__ float sRed[3][NT / 64];
+  __shared__ float sS[2];
+  __shared__ int sBad;
+  const int g = blockIdx.x, bh = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float* sc = pcws + (static_cast<size_t>(bh) * kWoodGroups + g) * 4;
+  _Float16* rec = pcw + (static_cast<size_t>(bh) * kWoodGroups + g) * wood_rec_halfs(D);
+  const size_t slot = static_cast<size_t>(bh) * nslots + (g > 0 ? g - 1 : 0);
+  // g >= 1 needs its slot's matrix (built for every group of the head); a
+  // failed build leaves the rows to P_g alone, as the CG kernel does
+  const bool have_m = g == 0 || pcs[slot] > 0.f;  // uniform
+  if (!have_m) {
+    if (tid == 0) sc[3] = 0.f;
+    return;
+  }
+  if (tid < 64) {
+    float a, b;
+    head_scales(partial, bh, nchunk, tid, &a, &b);
+    if (tid == 0) sS[0] = a;
+  }
+  if (tid == 0) sBad = 0;
+  __syncthreads();
+  const float s = sS[0];
+  const float lam_s = scaled_ridge(lambda, s);
+  // the group's point m (natural dims)
+  const _Float16* tile0 = kr + static_cast<size_t>(bh) * nblk * BK * D;
+  const _Float16* tileg = tile0 + static_cast<size_t>(g) * BK * D;  // keys 32 g .. 32 g + 31
+  for (int p = tid; p < D; p += NT) {
+    const int dim = (p & ~15) | swz16(p & 15);
+    sm[dim] = g == 0 ? static_cast<float>(tile0[(p >> 3) * BK * 8 + (p & 7)])
+                     : tsum[slot * D + dim] / static_cast<float>(32 * g);
+  }
+  __syncthreads();
+  // U (natural dims x 32 keys) and M (natural)
+  for (int e = tid; e < D * 32; e += NT) {
+    const int p = e >> 5, j = e & 31;
+    const int dim = (p & ~15) | swz16(p & 15);
+    const float kv = static_cast<float>(tileg[((p >> 3) * BK + j) * 8 + (p & 7)]);
+    sU[dim][j] = 32 * g + j < n ? kv - sm[dim] : 0.f;
+  }
+  if (g == 0) {
+    const float il = 1.f / lam_s;
+    for (int e = tid; e < D * D; e += NT) sM[e / D][e % D] = (e / D == e % D) ? il : 0.f;
+  } else {
+    const float ms = pcs[slot];
+    const _Float16* hiM = pcm + slot * 2 * D * D;
+    const _Float16* loM = hiM + D * D;
+    for (int e = tid; e < D * D; e += NT) {
+      const int row = e / D, col = e % D;
+      const int pcol = (col & ~15) | swz16(col & 15);
+      const int t = pcol >> 4, fg = (pcol >> 3) & 1, el = pcol & 7;
+      const int fi = (((t * (D / 32) + (row >> 5)) * 64 + 32 * fg + (row & 31)) * 8) + el;
+      sM[row][col] = ms * (static_cast<float>(hiM[fi]) + static_cast<float>(loM[fi]));
+    }
+  }
+  __syncthreads();
+  // M U
+  for (int e = tid; e < D * 32; e += NT) {
+    const int dim = e >> 5, j = e & 31;
+    float a = 0.f;
+    for (int k = 0; k < D; ++k) a = fmaf(sM[dim][k], sU[k][j], a);
+    sMU[dim][j] = a;
+  }
+  __syncthreads();
+  // A = I + U^T M U
+  for (int e = tid; e < 32 * 32; e += NT) {
+    const int i = e >> 5, j = e & 31;
+    float a = i == j ? 1.f : 0.f;
+    for (int k = 0; k < D; ++k) a = fmaf(sU[k][i], sMU[k][j], a);
+    sA[i][j] = a;
+  }
+  __syncthreads();
+  // Cholesky A = L L^T in place (lower triangle), one row per lane of wave 0
+  if (wave == 0) {
+    bool bad = false;
+    for (int k = 0; k < 32; ++k) {
+      // the diagonal (every lane computes it; lanes agree)
+      float a = sA[k][k];
+      for (int j = 0; j < k; ++j) a = fmaf(-sA[k][j], sA[k][j], a);
+      bad = bad || !(a > 0.f) || !(a < INFINITY);
+      const float lkk = sqrtf(fmaxf(a, 0.f));
+      const float il = bad ? 0.f : 1.f / lkk;
+      if (lane > k && lane < 32) {
+        float b = sA[lane][k];
+        for (int j = 0; j < k; ++j) b = fmaf(-sA[lane][j], sA[k][j], b);
+        sA[lane][k] = b * il;
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_wave_barrier();
+      if (lane == k) sA[k][k] = lkk;
+      __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_wave_barrier();
+    }
+    // V = L^{-1}: column c in lane c
+    if (lane < 32 && !bad) {
+      const int c = lane;
+      for (int i = 0; i < 32; ++i) {
+        float v;
+        if (i < c) {
+          v = 0.f;
+        } else if (i == c) {
+          v = 1.f / sA[c][c];
+        } else {
+          float a = 0.f;
+          for (int j = c; j < i; ++j) a = fmaf(sA[i][j], sV[j][c], a);
+          v = -a / sA[i][i];
+        }
+        sV[i][c] = v;
+      }
+    }
+    if (lane == 0) sBad = bad ? 1 : 0;
+  }
+  __syncthreads();
+  if (sBad) {  // uniform
+    if (tid == 0) sc[3] = 0.f;
+    return;
+  }
+  // power-of-two scales of U, V and M U
+  float mu_ = 0.f, mv_ = 0.f, mm_ = 0.f;
+  for (int e = tid; e < D * 32; e += NT) {
+    mu_ = fmaxf(mu_, fabsf(sU[e >> 5][e & 31]));
+    mm_ = fmaxf(mm_, fabsf(sMU[e >> 5][e & 31]));
+  }
+  for (int e = tid; e < 32 * 32; e += NT) mv_ = fmaxf(mv_, fabsf(sV[e >> 5][e & 31]));
+  mu_ = wave_max(mu_);
+  mv_ = wave_max(mv_);
+  mm_ = wave_max(mm_);
+  if (lane == 0) {
+    sRed[0][wave] = mu_;
+    sRed[1][wave] = mv_;
+    sRed[2][wave] = mm_;
+  }
+  __syncthreads();
+  float su = 0.f, sv_ = 0.f, smu = 0.f;
+  #pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    su = fmaxf(su, sRed[0][w]);
+    sv_ = fmaxf(sv_, sRed[1][w]);
+    smu = fmaxf(smu, sRed[2][w]);
+  }
+  const bool finite = su < INFINITY && sv_ < INFINITY && smu < INFINITY;  // uniform
+  su = pow2_ceil(su);
+  sv_ = pow2_ceil(sv_);
+  smu = pow2_ceil(smu);
+  const float iu = 1.f / su, iv = 1.f / sv_, imu = 1.f / smu;
+  auto split = [](float x, _Float16* hi, _Float16* lo, size_t at, size_t off) {
+    const _Float16 h = static_cast<_Float16>(x);
+    hi[at] = h;
+    lo[at + off] = static_cast<_Float16>(x - static_cast<float>(h));
+  };
+  // U: row-tile layout, position p (dims swz16-permuted) of key j at
+  // ((p >> 3) * 32 + j) * 8 + (p & 7)
+  for (int e = tid; e < D * 32; e += NT) {
+    const int p = e >> 5, j = e & 31;
+    const int dim = (p & ~15) | swz16(p & 15);
+    split(sU[dim][j] * iu, rec, rec, ((p >> 3) * 32 + j) * 8 + (p & 7), 32 * D);
+  }
+  // operand fragments over the group's 32 keys as the K index: lane l =
+  // 32 fg + ql, k-step t, slot c holds key kp = swz(16 t + 8 fg + c), the row
+  // of an accumulator that the lane's register 8 t + c holds
+  _Float16* V0 = rec + 64 * D;
+  for (int e = tid; e < 2 * 64 * 8; e += NT) {
+    const int t = e >> 9, l = (e >> 3) & 63, c = e & 7;
+    const int fg = l >> 5, ql = l & 31, p = 16 * t + 8 * fg + c;
+    const int kp = (p & ~15) | swz16(p & 15);
+    split(sV[ql][kp] * iv, V0, V0, e, 1024);           // V: row ql
+    split(sV[kp][ql] * iv, V0 + 2048, V0 + 2048, e, 1024);  // V^T: row ql
+  }
+  _Float16* N0 = rec + 64 * D + 4096;
+  for (int e = tid; e < 2 * NMB * 64 * 8; e += NT) {
+    const int t = e / (NMB * 512), mb = (e / 512) % NMB, l = (e >> 3) & 63, c = e & 7;
+    const int fg = l >> 5, ql = l & 31, p = 16 * t + 8 * fg + c;
+    const int kp = (p & ~15) | swz16(p & 15);
+    split(-sMU[32 * mb + ql][kp] * imu, N0, N0, e, 32 * D);
+  }
+  if (tid == 0) {
+    sc[0] = su;
+    sc[1] = sv_;
+    sc[2] = smu;
+    sc[3] = finite ? 1.f : 0.f;
+  }
+}
+
 // ---------------------------------------------------------------------------
 struct MainParams {
   const uint16_t* q;
@@ -547,6 +764,8 @@ struct MainParams {
   const _Float16* pcm;  // preconditioners (see pc_build), used by the CG kernel with PRECOND
   _Float16* kb16;    // fp16 kbar fragments (preconditioned CG), per 32-query group
   const float* pcs;
+  const _Float16* pcw;  // rank-r corrections of the first groups' preconditioners (pc_wood)
+  const float* pcws;
   int nslots;
   int BH, n, nchunk, nblk;
   int nq32;          // 32-query groups per head in the state slabs
@@ -987,6 +1206,8 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
   // of this wave's group of 32 queries (group 0 and a failed build: z = r),
   // formed on the matrix cores with M and r each in two fp16 terms (hi hi +
   // hi lo + lo hi, fp32 sums); r^T z replaces r^T r in the direction update.
+  // Rows below 256 then take the rank-r correction by their group's own keys
+  // (pc_wood; group 0 with M = I / lambda).
   // z in the accumulator layout (register r of block mb): it shares the
   // registers of the sweep's Y accumulators, which are free from the r update
   // until the next sweep starts (and before the first)
@@ -1003,6 +1224,16 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
     }
   }
   const bool use_pc = PRECOND && pc_s > 0.f;
+  // the correction's record and scales (a valid record for a group g >= 1
+  // implies a built M, so use_pc)
+  // (only the flag lives through the sweeps; the record's address and scales
+  // are formed where the correction runs)
+  bool wood = false;
+  const int wgrp = (i0 >> 5) + wave;
+  if constexpr (PRECOND) {
+    if (wave_any && wgrp < kWoodGroups)
+      wood = P.pcws[(static_cast<size_t>(bh) * kWoodGroups + wgrp) * 4 + 3] > 0.f;
+  }
   // the block's four groups share one built preconditioner (uniform over the
   // workgroup): copy it into LDS once, both terms, for every iteration
   bool m_lds = false;
@@ -1098,10 +1329,141 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
     if constexpr (PRECOND) return zacc[c >> 2][4 * (c & 3) + b];
     else return rv4[c][b];
   };
+  // z -= (M U) mask(V^T mask(V mask(U^T z))) for z = M r in the accumulators,
+  // the query's keys j <= ql of its group (pc_wood). Operands in two fp16
+  // terms under per-query power-of-two scales; the fragments of a product are
+  // loaded before its first matrix instruction.
+  auto wood_load = [&](__amdgpu_buffer_rsrc_t rs, int half_off) __attribute__((always_inline)) {
+    return __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(rs, half_off * 2, 0, 0));
+  };
+  // an accumulator of 32 keys x 32 queries as a B operand: hi and lo terms of
+  // x / sx, register 8 t + c -> k-step t, slot c
+  auto keys_operand = [&](const floatx16& x, half8 (&xh)[2], half8 (&xl)[2]) __attribute__((always_inline)) {
+    float mx = 0.f;
+    #pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fabsf(x[r]));
+    const float sx = pow2_ceil(pair_max(mx));
+    const float ix = 1.f / sx;
+    #pragma unroll
+    for (int t = 0; t < 2; ++t)
+      #pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float v = x[8 * t + c] * ix;
+        xh[t][c] = static_cast<_Float16>(v);
+        xl[t][c] = static_cast<_Float16>(v - static_cast<float>(xh[t][c]));
+      }
+    return sx;
+  };
+  auto wood_fix = [&]() __attribute__((always_inline)) {
+    const size_t wrec = static_cast<size_t>(bh) * kWoodGroups + wgrp;
+    const __amdgpu_buffer_rsrc_t wood_rsrc = make_rsrc(P.pcw + wrec * wood_rec_halfs(D),
+                                                       wood_rec_halfs(D) * sizeof(_Float16));
+    const float w_su = P.pcws[wrec * 4], w_sv = P.pcws[wrec * 4 + 1], w_smu = P.pcws[wrec * 4 + 2];
+    // t = U^T z
+    float mz = 0.f;
+    #pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+      #pragma unroll
+      for (int r = 0; r < 16; ++r) mz = fmaxf(mz, fabsf(zacc[mb][r]));
+    const float sz = pow2_ceil(pair_max(mz));
+    const float izs = 1.f / sz;
+    floatx16 tk;
+    #pragma unroll
+    for (int r = 0; r < 16; ++r) tk[r] = 0.f;
+    // U's fragments half at a time
+    constexpr int TB = NKS / 2;
+    #pragma unroll
+    for (int t0 = 0; t0 < NKS; t0 += TB) {
+      half8 uh[TB], ul[TB];
+      #pragma unroll
+      for (int tt = 0; tt < TB; ++tt) {
+        const int off = ((2 * (t0 + tt) + g) * 32 + ql) * 8;
+        uh[tt] = wood_load(wood_rsrc, off);
+        ul[tt] = wood_load(wood_rsrc, off + 32 * D);
+      }
+      #pragma unroll
+      for (int tt = 0; tt < TB; ++tt) {
+        const int t = t0 + tt;
+        half8 zh, zl;
+        #pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const float v = zacc[t >> 1][8 * (t & 1) + c] * izs;
+          zh[c] = static_cast<_Float16>(v);
+          zl[c] = static_cast<_Float16>(v - static_cast<float>(zh[c]));
+        }
+        tk = mfma(uh[tt], zh, tk);
+        tk = mfma(uh[tt], zl, tk);
+        tk = mfma(ul[tt], zh, tk);
+      }
+    }
+    const float tsc = w_su * sz;
+    #pragma unroll
+    for (int r = 0; r < 16; ++r) tk[r] = key_of(r) <= ql ? tk[r] * tsc : 0.f;
+    // y = V t, then x = V^T y (records at 64 D and 64 D + 2048 halfs)
+    #pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const int vb = 64 * D + 2048 * pass;
+      half8 vh[2], vl[2], xh[2], xl[2];
+      #pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        vh[t] = wood_load(wood_rsrc, vb + (t * 64 + lane) * 8);
+        vl[t] = wood_load(wood_rsrc, vb + 1024 + (t * 64 + lane) * 8);
+      }
+      const float sx = keys_operand(tk, xh, xl);
+      floatx16 y;
+      #pragma unroll
+      for (int r = 0; r < 16; ++r) y[r] = 0.f;
+      #pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        y = mfma(vh[t], xh[t], y);
+        y = mfma(vh[t], xl[t], y);
+        y = mfma(vl[t], xh[t], y);
+      }
+      const float ysc = w_sv * sx;
+      #pragma unroll
+      for (int r = 0; r < 16; ++r) tk[r] = key_of(r) <= ql ? y[r] * ysc : 0.f;
+    }
+    // z += (-M U) x, accumulated onto z / (s_MU sx) (powers of two: exact)
+    {
+      half8 xh[2], xl[2];
+      const float sx = keys_operand(tk, xh, xl);
+      const float nsc = w_smu * sx, insc = 1.f / nsc;
+      #pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) zacc[mb] *= insc;
+      #pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+        half8 nh[2], nl[2];
+        #pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int off = 64 * D + 4096 + ((t * NMB + mb) * 64 + lane) * 8;
+          nh[t] = wood_load(wood_rsrc, off);
+          nl[t] = wood_load(wood_rsrc, off + 32 * D);
+        }
+        #pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          zacc[mb] = mfma(nh[t], xh[t], zacc[mb]);
+          zacc[mb] = mfma(nh[t], xl[t], zacc[mb]);
+          zacc[mb] = mfma(nl[t], xh[t], zacc[mb]);
+        }
+      }
+      #pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) zacc[mb] *= nsc;
+    }
+  };
+  // group 0 has no built M: M = I / lambda (scaled units), z = r / lambda
+  auto wood_apply = [&]() __attribute__((always_inline)) {
+    if (!use_pc) {
+      const float il = 1.f / lam_s;
+      #pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) zacc[mb] *= il;
+    }
+    wood_fix();
+  };
   float rz = rr;
   if constexpr (PRECOND) {
     if (use_pc) apply_pc();
     else r_to_z();
+    if (wood) wood_apply();
     rz = zr_dot();
   }
   // fp16 kbar . op for an operand-ordered fp16 vector
@@ -1453,6 +1815,7 @@ __global__ __launch_bounds__(64 * NW) void lla_mfma_phase(MainParams P) {
       } else {
         r_to_z();
       }
+      if (wood && __any(cont ? 1 : 0)) wood_apply();
       rzn = zr_dot();
     }
     // lanes that stopped keep their state; the pair exchanges run in every lane
@@ -1851,6 +2214,8 @@ MainParams main_params(const FwdParams& p, const Workspace& w) {
   m.rho_c = p.rho_c;
   m.pcm = w.pcm;
   m.pcs = w.pcs;
+  m.pcw = w.pcw;
+  m.pcws = w.pcws;
   m.nslots = pc_nslots(p.n);
   m.BH = p.BH;
   m.n = p.n;
@@ -1887,7 +2252,7 @@ hipError_t launch_prep(const FwdParams& p, const Workspace& w, hipStream_t strea
 // preconditioned recurrence reaches in fewer steps), no with tolerance 0 (a
 // fixed number of plain CG steps).
 bool use_precond(const FwdParams& p) {
-  if (p.rho_in || p.cg_max_iters == 0 || pc_nslots(p.n) == 0) return false;
+  if (p.rho_in || p.cg_max_iters == 0) return false;
   if (p.flags & LLA_FLAG_PRECOND) return true;
   if (p.flags & LLA_FLAG_NO_PRECOND) return false;
   return p.cg_rel_tol > 0.f;
@@ -1899,15 +2264,24 @@ hipError_t launch_pc_build(const FwdParams& p, const Workspace& w, hipStream_t s
   const int nchunk = (p.n + NORM_ROWS - 1) / NORM_ROWS;
   const int nblk = (p.n + BK - 1) / BK;
   float* gram = reinterpret_cast<float*>(w.pcm);  // each slot's 2 D^2 halfs hold D^2 floats
-  hipLaunchKernelGGL(pc_gram<D>, dim3(nsl, p.BH), dim3(NT), 0, stream, w.kt, nblk, nsl, gram, w.pct);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(pc_scan<D>, dim3((D * D + D + NT - 1) / NT, p.BH), dim3(NT), 0, stream, nsl, gram,
-                     w.pct);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(pc_invert<D>, dim3(nsl, p.BH), dim3(NT), 0, stream, w.partial, nchunk, nsl,
-                     p.lambda, gram, w.pct, w.pcs);
+  hipError_t e;
+  if (nsl > 0) {  // (a head of at most 32 rows has only group 0)
+    hipLaunchKernelGGL(pc_gram<D>, dim3(nsl, p.BH), dim3(NT), 0, stream, w.kt, nblk, nsl, gram, w.pct);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(pc_scan<D>, dim3((D * D + D + NT - 1) / NT, p.BH), dim3(NT), 0, stream, nsl, gram,
+                       w.pct);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(pc_invert<D>, dim3(nsl, p.BH), dim3(NT), 0, stream, w.partial, nchunk, nsl,
+                       p.lambda, gram, w.pct, w.pcs);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  // the rank-r corrections of the first groups (one workgroup per group that
+  // has rows: its key tile exists)
+  hipLaunchKernelGGL(pc_wood<D>, dim3(std::min(kWoodGroups, nblk), p.BH), dim3(NT), 0, stream, w.partial,
+                     nchunk, p.n, nblk, nsl, p.lambda, w.kr, w.pcm, w.pcs, w.pct, w.pcw, w.pcws);
   return hipGetLastError();
 }
 
@@ -2023,7 +2397,9 @@ size_t mfma_workspace_bytes(int BH, int n, int d) {
          align256(static_cast<size_t>(BH) * nsl * 2 * d * d * sizeof(_Float16)) +
          align256(static_cast<size_t>(BH) * nsl * sizeof(float)) +
          align256(static_cast<size_t>(BH) * nsl * d * sizeof(float)) +
-         align256(static_cast<size_t>(BH) * nqpad * d * sizeof(_Float16));
+         align256(static_cast<size_t>(BH) * nqpad * d * sizeof(_Float16)) +
+         align256(static_cast<size_t>(BH) * kWoodGroups * wood_rec_halfs(d) * sizeof(_Float16)) +
+         align256(static_cast<size_t>(BH) * kWoodGroups * 4 * sizeof(float));
 }
 
 hipError_t launch_mfma(const FwdParams& p, hipStream_t stream) {

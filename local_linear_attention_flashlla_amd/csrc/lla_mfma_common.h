@@ -128,6 +128,17 @@ __host__ __device__ inline int pc_group_of_slot(int slot) {  // g' of the slot
   const int e = 3 + (slot - 7) / 4, q = (slot - 7) % 4;
   return (4 + q) << (e - 2);
 }
+// The first kWoodGroups groups of 32 queries (rows below 256) precondition
+// each row with its whole prefix: the group's matrix (the scatter of the
+// first 32 g keys, lam I for g = 0) and a rank-r correction by the group's own
+// keys, applied per query in the CG kernel (pc_wood). A group's record, in
+// halfs: U = the group's 32 keys less the group's point, two fp16 terms in
+// the row-tile layout of kr (2 x 32 D); V = L^{-1} for A = I + U^T M U = L L^T
+// and its transpose, two terms each in MFMA operand order (4 x 2 x 64 x 8);
+// -M U in operand order, two terms (2 x 32 D).
+constexpr int kWoodGroups = 8;
+__host__ __device__ constexpr int wood_rec_halfs(int d) { return 128 * d + 4096; }
+
 inline int pc_nslots(int n) {
   const int G = (n + 31) / 32;
   return G >= 2 ? pc_slot_of_group(G - 1) + 1 : 0;
@@ -149,6 +160,9 @@ struct Workspace {
   float* pct;       // [BH][nslots][D] key sums of the slots' prefixes (build only)
   _Float16* kb16;   // fp16 kbar for the preconditioned CG: per 32-query group, the D / 8
                     // fragments of 8 halfs in MFMA operand order, lane-contiguous (16 B per lane)
+  _Float16* pcw;    // [BH][kWoodGroups] records of the rank-r corrections of the first groups'
+                    // preconditioners (see pc_wood), kWoodRec<D> halfs each
+  float* pcws;      // [BH][kWoodGroups][4] their scales (U, V, M U) and a valid flag
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -185,6 +199,10 @@ Workspace carve(void* base, int BH, int n, int d) {
   w.pct = reinterpret_cast<float*>(p);
   p += align256(static_cast<size_t>(BH) * nsl * d * sizeof(float));
   w.kb16 = reinterpret_cast<_Float16*>(p);
+  p += align256(static_cast<size_t>(BH) * nqpad * d * sizeof(_Float16));
+  w.pcw = reinterpret_cast<_Float16*>(p);
+  p += align256(static_cast<size_t>(BH) * kWoodGroups * wood_rec_halfs(d) * sizeof(_Float16));
+  w.pcws = reinterpret_cast<float*>(p);
   return w;
 }
 

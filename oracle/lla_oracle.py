@@ -47,10 +47,11 @@ Readings taken where the pages leave a step open:
   * Preconditioned CG (not on the pages, which only mention early stopping;
     used where the iteration budget cannot otherwise reach the answer): the
     same recurrence with z = P^{-1} r in place of r in the direction update.
-    P is the prefix-Gram preconditioner of the row's group of 32 queries
-    (``prefix_group_length``, ``prefix_preconditioner``): the unit-weight
-    scatter matrix of the first N keys plus lam I, with N <= 32 floor(i/32)
-    so that those keys are visible to every query of the group.
+    P is the prefix-Gram preconditioner (``prefix_group_length``,
+    ``prefix_preconditioner``): a unit-weight scatter matrix plus lam I. For
+    rows i < 256 it scatters the row's whole prefix about a point shared by
+    its group of 32 queries; from row 256 on, the first N keys of the
+    prefix about their mean, N <= 32 floor(i/32) shared by groups of rows.
 """
 
 from __future__ import annotations
@@ -147,17 +148,33 @@ def prefix_group_length(i: int) -> int:
 
 
 def prefix_preconditioner(K_prefix: np.ndarray, lam: float):
-    """P for the last row of K_prefix (row i = len(K_prefix) - 1): with N =
-    prefix_group_length(i) and m the plain mean of k_0..k_{N-1},
-    P = sum_{j<N} (k_j - m)(k_j - m)^T + lam I; None when N = 0."""
+    """P for the last row of K_prefix (row i = len(K_prefix) - 1), with
+    g = floor(i / 32) and N = prefix_group_length(i):
+
+      g < 8:  P = sum_{j<=i} (k_j - m)(k_j - m)^T + lam I, the whole prefix
+              scattered about m = k_0 (g = 0) or the plain mean of
+              k_0..k_{N-1} (g >= 1). Below 256 keys a prefix spans a part of
+              the key space that its first N keys can miss (up to 31
+              directions, each a near-zero eigenvalue of the system at a small
+              lam), so the row's own keys are kept; the point m is shared by
+              the group, so the rows of a group differ by a rank-r update
+              (r <= 32) of one matrix;
+      g >= 8: P = sum_{j<N} (k_j - m)(k_j - m)^T + lam I with m the mean of
+              those N keys (the prefix is long enough that its first N keys
+              span what the rest does).
+
+    Every key used is visible to row i."""
     i = K_prefix.shape[0] - 1
+    g = i // 32
     N = prefix_group_length(i)
-    if N == 0:
-        return None
-    Kp = np.asarray(K_prefix[:N], dtype=np.float64)
-    m = Kp.mean(axis=0)
-    D = Kp - m[None, :]
-    return D.T @ D + lam * np.eye(Kp.shape[1])
+    if g < 8:
+        K = np.asarray(K_prefix, dtype=np.float64)
+        m = K[0] if g == 0 else K[:N].mean(axis=0)
+    else:
+        K = np.asarray(K_prefix[:N], dtype=np.float64)
+        m = K.mean(axis=0)
+    D = K - m[None, :]
+    return D.T @ D + lam * np.eye(K.shape[1])
 
 
 def cg_solve(Sigma: np.ndarray, rhs: np.ndarray, max_iters: int, rel_tol: float, precond=None):

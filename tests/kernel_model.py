@@ -86,6 +86,72 @@ def _apply_two_term(R, M, r):
     return R.f((mh @ rh + mh @ rl + ml @ rh) * (sm * sr))
 
 
+def _two(R, x):
+    """x as two fp16 terms (hi, lo) under a power-of-two scale: (hi, lo, scale)."""
+    sc = _pow2_ceil(np.abs(x).max()) if np.any(x) else 1.0
+    hi = R.h(x / sc)
+    return hi, R.h(x / sc - hi), sc
+
+
+class WoodGroup:
+    """Group g < 8 of 32 rows as the kernel preconditions it (lla.h): the
+    group's matrix M_g (the fp32 inverse of the scatter of its first 32 g keys
+    about the group's point m, plus lam I; None for g = 0, where M = I / lam)
+    and its 32 keys less m, U (d x 32, input units; columns past the head's
+    end zero). The kernel's precomputation in fp32 (M U from M_g as applied,
+    in two fp16 terms; A = I + U^T M U; its Cholesky factor L; V = L^{-1}) and
+    its per-query products in two fp16 terms are modelled in ``apply``."""
+
+    def __init__(self, Mg, U, lam):
+        self.Mg, self.U, self.lam = Mg, U, lam
+        self._cache = {}
+
+    def _pre(self, R, s):
+        key = (R.exact, s)
+        if key not in self._cache:
+            d = self.U.shape[0]
+            lam_s = self.lam * s * s
+            Us = self.U * s
+            if self.Mg is None:
+                M2 = np.eye(d) / lam_s
+                Ms = None
+            else:
+                Ms = R.f(self.Mg / (s * s))
+                if R.exact:
+                    M2 = Ms
+                else:
+                    mh, ml, sm = _two(R, Ms)
+                    M2 = (mh + ml) * sm
+            MU = R.f(M2 @ Us)
+            A = R.f(np.eye(32) + Us.T @ MU)
+            if R.exact:
+                V = np.linalg.inv(np.linalg.cholesky(A))
+            else:
+                L = np.linalg.cholesky(A.astype(np.float32))
+                V = np.linalg.inv(L).astype(np.float32).astype(np.float64)
+            self._cache[key] = (Ms, lam_s, _two(R, Us), _two(R, V), _two(R, -MU))
+        return self._cache[key]
+
+    def apply(self, R, r, s, nk):
+        """z = P_i^{-1} r in scaled units for the row whose own keys are the
+        group's first nk."""
+        Ms, lam_s, (uh, ul, su), (vh, vl, sv), (nh, nl, smu) = self._pre(R, s)
+        z = r / lam_s if Ms is None else _apply_two_term(R, Ms, r)
+        keep = (np.arange(32) < nk).astype(float)
+        zh, zl, sz = _two(R, z)
+        t = R.f(uh.T @ zh + uh.T @ zl + ul.T @ zh) * (su * sz) * keep
+        for vhh, vll in ((vh, vl), (vh.T, vl.T)):
+            th, tl, st = _two(R, t)
+            t = R.f(vhh @ th + vhh @ tl + vll @ th) * (sv * st) * keep
+        xh, xl, sx = _two(R, t)
+        return R.f(z + R.f(nh @ xh + nh @ xl + nl @ xh) * (smu * sx))
+
+
+class WoodRow:
+    def __init__(self, group, nk):
+        self.group, self.nk = group, nk
+
+
 def model_row(q_i, K, V, lam, cg_max_iters, cg_rel_tol, s, sv, split_u=False, exact=False,
               precond=None, first_block_split=None):
     """Row i of the causal forward (K, V: the prefix k_0..k_i, v_0..v_i) as
@@ -93,7 +159,7 @@ def model_row(q_i, K, V, lam, cg_max_iters, cg_rel_tol, s, sv, split_u=False, ex
     matrix M (in input units, as the oracle defines it); it is rounded to fp32
     and applied in two fp16 terms. ``first_block_split``: whether the first
     128 queries of a head carry U in two terms (the kernel does so in its
-    preconditioned mode, also on rows 0..31, which have no preconditioner;
+    preconditioned mode;
     default: whether ``precond`` is given). Returns dict(b, rho_c, iters)."""
     if first_block_split is None:
         first_block_split = precond is not None
@@ -131,8 +197,15 @@ def model_row(q_i, K, V, lam, cg_max_iters, cg_rel_tol, s, sv, split_u=False, ex
     thr = cg_rel_tol * r0
     active = rr > 0.0 and cg_max_iters > 0
     iters = 0
-    Ms = None if precond is None else R.f(np.asarray(precond) / (s * s))   # scaled units
-    z = r if Ms is None else _apply_two_term(R, Ms, r)
+    if isinstance(precond, WoodRow):
+        def pz(rv):
+            return precond.group.apply(R, rv, s, precond.nk)
+    else:
+        Ms = None if precond is None else R.f(np.asarray(precond) / (s * s))   # scaled units
+
+        def pz(rv):
+            return rv if Ms is None else _apply_two_term(R, Ms, rv)
+    z = pz(r)
     rz = float(r @ z)
     sp = _pow2_ceil(np.abs(z).max()) if rr > 0 else 1.0
     dv = R.h(z / sp)
@@ -164,7 +237,7 @@ def model_row(q_i, K, V, lam, cg_max_iters, cg_rel_tol, s, sv, split_u=False, ex
         if np.sqrt(rrn) <= thr or rrn == 0.0:
             rr = rrn
             break
-        z = r if Ms is None else _apply_two_term(R, Ms, r)
+        z = pz(r)
         rzn = float(r @ z)
         be = rzn / rz * sp
         p = R.f(z + be * dv)
@@ -197,23 +270,41 @@ def group_prefix(i):
     return 32 * (g // step) * step
 
 
+def _group_inverse(Kp, m, lam, d):
+    D = np.asarray(Kp, np.float64) - m
+    P = np.asarray(D.T @ D + lam * np.eye(d), np.float32)
+    M = np.linalg.inv(P).astype(np.float64)
+    return 0.5 * (M + M.T)
+
+
 def preconditioners(k, lam):
-    """A function i -> M_i (inverse of the prefix-Gram preconditioner, input
-    units) or None, computed the way the kernel does: fp32 inverse of the
-    scatter matrix of the scaled fp16 keys plus the ridge, symmetrised."""
+    """A function i -> the preconditioner of row i as lla.h defines it. From
+    row 256 on, M = the fp32 inverse (symmetrised) of the scatter of the first
+    N keys about their mean plus the ridge, one matrix per N as the kernel
+    builds it. Below row 256, a WoodRow: the row's whole prefix about its
+    group's point (k_0 for rows 0..31, else the mean of the first 32 g keys),
+    applied as the kernel does, the group's matrix and the rank-r correction
+    by the group's own keys (WoodGroup)."""
+    k = np.asarray(k, np.float64)
+    n, d = k.shape
     cache = {}
 
     def f(i):
-        N = group_prefix(i)
-        if N == 0:
-            return None
-        if N not in cache:
-            Kp = np.asarray(k[:N], np.float64)
-            D = Kp - Kp.mean(axis=0)
-            P = np.asarray(D.T @ D + lam * np.eye(k.shape[1]), np.float32)
-            M = np.linalg.inv(P).astype(np.float64)
-            cache[N] = 0.5 * (M + M.T)
-        return cache[N]
+        g = i // 32
+        if g >= 8:
+            N = group_prefix(i)
+            if N not in cache:
+                Kp = k[:N]
+                cache[N] = _group_inverse(Kp, Kp.mean(axis=0), lam, d)
+            return cache[N]
+        if ("g", g) not in cache:
+            m = k[0] if g == 0 else k[:32 * g].mean(axis=0)
+            Mg = None if g == 0 else _group_inverse(k[:32 * g], m, lam, d)
+            U = np.zeros((d, 32))
+            top = min(32 * g + 32, n)
+            U[:, :top - 32 * g] = (k[32 * g:top] - m).T
+            cache[("g", g)] = WoodGroup(Mg, U, lam)
+        return WoodRow(cache[("g", g)], i - 32 * g + 1)
     return f
 
 

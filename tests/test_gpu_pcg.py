@@ -1,11 +1,14 @@
 """GPU parity of the preconditioned CG (include/lla.h: prefix-Gram
-preconditioner per group of 32 queries; the default whenever an
-early-stopping tolerance is set) against the float64 oracle.
+preconditioner per group of 32 queries, rows below 256 with their whole
+prefix through a rank-r correction; the default whenever an early-stopping
+tolerance is set) against the float64 oracle.
 
   * the PCG iterate itself after T = 1, 2, 4 steps against the oracle's
-    float64 PCG iterate (tolerance 1e-3: three times the most the numpy model
+    float64 PCG iterate (tolerance 4e-3: three times the most the numpy model
     of the kernel's rounding, tests/kernel_model.py, gives on the same inputs,
-    3.05e-4 over both cases and all three T);
+    1.27e-3 over both cases and all three T; the model lands on the GPU's
+    figures to three digits, e.g. 2.76e-4 at T = 1 and 1.03e-3 at T = 2 on
+    the d = 64 case);
   * the recall recipe (lambda = 1e-3, clustered keys, tol 1e-4, at most 64
     steps) on the default path: every row within 2e-2 of the exact
     (Cholesky) answer, with no allowance for CG truncation, at n = 300 and at
@@ -26,7 +29,7 @@ pytestmark = pytest.mark.gpu
 
 BF16_TOL = 2e-2
 MFMA = lla.LLA_KERNEL_MFMA
-ITER_TOL = {1: 1e-3, 2: 1e-3, 4: 1e-3}
+ITER_TOL = {1: 4e-3, 2: 4e-3, 4: 4e-3}
 
 
 @pytest.fixture(scope="module")

@@ -127,8 +127,9 @@ def test_backward_matrix_cores_past_2_31_elements(torch):
     ne = elements(B, wl)
     ws_f = lla.workspace_bytes(B, wl.H, wl.n, wl.d, "bf16", lla.LLA_KERNEL_MFMA)
     ws_b = lla.backward_workspace_bytes(B, wl.H, wl.n, wl.d, "bf16")
-    # q, k, v (bf16); out, rho_c, dout, dq, dk, dv (fp32); the backward's
-    # workspace, which contains the forward's (freed before it is taken)
+    # q, k, v (bf16); out, rho_c, dout, dq, dk, dv (fp32); one workspace for
+    # both calls (the backward's contains the forward's), passed in so that
+    # no stream-ordered pool holds a freed forward workspace beside it
     need_free(torch, ne * (3 * 2 + 6 * 4) + max(ws_f, ws_b))
     print(f"\n[case] backward matrix cores B={B} H={wl.H} n={wl.n} d={wl.d} bf16: "
           f"{ne / 2**31:.4f} x 2^31 elements per tensor, workspaces {ws_f / GiB:.1f} + "
@@ -140,10 +141,12 @@ def test_backward_matrix_cores_past_2_31_elements(torch):
     dout = replicate(torch, torch.from_numpy(np.ascontiguousarray(g)).cuda(), B)
     del q1, k1, v1
     rho_c = torch.empty((B, wl.H, wl.n, wl.d), device="cuda")
-    out = lla.forward(q, k, v, lam, T, tol, kernel=lla.LLA_KERNEL_MFMA, rho_c=rho_c)
-    dq, dk, dv = lla.backward(q, k, v, out, dout, rho_c, lam, T, tol, kernel=lla.LLA_KERNEL_MFMA)
+    ws = torch.empty(max(ws_f, ws_b), dtype=torch.uint8, device="cuda")
+    out = lla.forward(q, k, v, lam, T, tol, kernel=lla.LLA_KERNEL_MFMA, rho_c=rho_c, workspace=ws)
+    dq, dk, dv = lla.backward(q, k, v, out, dout, rho_c, lam, T, tol, kernel=lla.LLA_KERNEL_MFMA,
+                              workspace=ws)
     torch.cuda.synchronize()
-    del q, k, v, out, dout, rho_c
+    del q, k, v, out, dout, rho_c, ws
     res = {}
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
         bad = first_mismatch(torch, t)

@@ -47,3 +47,21 @@ def test_exact_model_runs_the_oracle_pcg(name, T, tol):
         # which a residual crosses it by one; both have then converged
         assert np.abs(m["iters"] - ref["cg_iters"]).max() <= 1
         assert row_errors(m["b"], ref["b"]).max() < 1e-4
+
+
+@pytest.mark.parametrize("name,T,tol", [("standard", 16, 0.0), ("recall", 64, 1e-4)])
+def test_exact_model_of_the_kernels_preconditioning_runs_the_oracle_pcg(name, T, tol):
+    """With rounding off, the model's preconditioning as the kernel applies it
+    (rows below 256: the group's matrix and the masked rank-r correction by the
+    group's own keys; beyond: the group matrix) is the oracle's PCG."""
+    wl = make_workload(name, B=1, H=1, n=300)
+    q, k, v = wl.q[0, 0], wl.k[0, 0], wl.v[0, 0]
+    rows = list(range(0, 300, 7))
+    ref = O.oracle_head(q, k, v, wl.lam, rows=rows, solver="pcg_centred", cg_max_iters=T, cg_rel_tol=tol)
+    m = KM.model_head(q, k, v, wl.lam, T, tol, rows=rows, exact=True, precond=KM.preconditioners(k, wl.lam))
+    if tol == 0.0:
+        assert np.array_equal(m["iters"], ref["cg_iters"])
+        assert row_errors(m["b"], ref["b"]).max() < 1e-7
+    else:
+        assert np.abs(m["iters"] - ref["cg_iters"]).max() <= 1
+        assert row_errors(m["b"], ref["b"]).max() < 1e-4

@@ -41,15 +41,61 @@ def test_prefix_group_length_properties():
 
 
 def test_prefix_preconditioner_is_scatter_plus_ridge():
+    # independent route: the scatter about a point m of L keys is
+    # L cov + L (mean - m)(mean - m)^T (parallel-axis identity, numpy's cov)
     rng = np.random.default_rng(3)
     K = rng.standard_normal((300, 8)) + 2.0
     lam = 0.7
-    assert O.prefix_preconditioner(K[:20], lam) is None
-    for i in (40, 150, 299):
+
+    def about(X, m):
+        L = X.shape[0]
+        dm = X.mean(axis=0) - m
+        return L * np.cov(X.T, bias=True) + L * np.outer(dm, dm) + lam * np.eye(8)
+
+    # row 0: one key, scattered about itself: lam I
+    np.testing.assert_allclose(O.prefix_preconditioner(K[:1], lam), lam * np.eye(8), atol=0)
+    for i in (19, 31):      # group 0: the whole prefix about k_0
+        np.testing.assert_allclose(O.prefix_preconditioner(K[:i + 1], lam), about(K[:i + 1], K[0]),
+                                   rtol=1e-12, atol=1e-12)
+    for i in (32, 40, 150, 255):   # groups 1..7: the whole prefix about the mean of the first 32 g
+        m = K[:32 * (i // 32)].mean(axis=0)
+        np.testing.assert_allclose(O.prefix_preconditioner(K[:i + 1], lam), about(K[:i + 1], m),
+                                   rtol=1e-12, atol=1e-12)
+    for i in (256, 299):    # from row 256: the first N keys about their mean
         N = O.prefix_group_length(i)
         P = O.prefix_preconditioner(K[:i + 1], lam)
         ref = N * np.cov(K[:N].T, bias=True) + lam * np.eye(8)
         np.testing.assert_allclose(P, ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("g", [0, 1, 5, 7])
+def test_rows_of_a_group_differ_by_a_masked_low_rank_update(g):
+    """Below row 256, row i = 32 g + r - 1 of group g has P_i = P_g + U_r U_r^T
+    with P_g the scatter of the first 32 g keys about the group's point m (lam I
+    for g = 0), U the group's 32 keys less m, U_r its first r columns. The
+    inverse the matrix-core kernel applies, with one Cholesky factor A = L L^T
+    of A = I + U^T P_g^{-1} U shared by the group and V = L^{-1}:
+        P_i^{-1} x = M x - (M U) mask(V^T mask(V mask(U^T M x))),
+    M = P_g^{-1}, mask keeping the first r entries (a leading block of a
+    triangular matrix's inverse is the inverse of its leading block). Checked
+    against numpy's inverse of the oracle's P_i for every row of the group."""
+    rng = np.random.default_rng(11 + g)
+    d, lam = 16, 1e-2
+    K = rng.standard_normal((32 * g + 32, d)) / np.sqrt(d) + 0.3
+    m = K[0] if g == 0 else K[:32 * g].mean(axis=0)
+    D0 = K[:32 * g] - m
+    Pg = D0.T @ D0 + lam * np.eye(d)
+    M = np.linalg.inv(Pg)
+    U = (K[32 * g:32 * g + 32] - m).T
+    A = np.eye(32) + U.T @ M @ U
+    V = np.linalg.inv(np.linalg.cholesky(A))
+    x = rng.standard_normal(d)
+    for r in range(1, 33):
+        i = 32 * g + r - 1
+        mask = (np.arange(32) < r).astype(float)
+        z = M @ x - (M @ U) @ (mask * (V.T @ (mask * (V @ (mask * (U.T @ (M @ x)))))))
+        ref = np.linalg.solve(O.prefix_preconditioner(K[:i + 1], lam), x)
+        np.testing.assert_allclose(z, ref, rtol=1e-9, atol=1e-12)
 
 
 def _system(seed=5, n=60, d=8, lam=0.05, i=59):
@@ -81,6 +127,7 @@ def test_pcg_with_exact_preconditioner_solves_in_one_step():
 @pytest.mark.parametrize("steps", [1, 2, 4])
 def test_pcg_iterates_minimise_energy_over_preconditioned_krylov_space(steps):
     S, mu, P = _system()
+    assert P is not None
     x, it, _ = O.cg_solve(S, mu, steps, 0.0, precond=P)
     assert it == steps
     # independent: the Krylov basis of P^{-1} S started at P^{-1} mu (numpy
