@@ -525,6 +525,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void pc
   if (tid == 0) pcs[slot] = sM;
 }
 
+// Value of lane `l` (a constant) of a wave-wide float.
+__device__ __forceinline__ float lane_value(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
 // Rows below 256 (groups g < kWoodGroups of 32 queries): row i = 32 g + ql
 // is preconditioned with its whole prefix, P_i = sum_{j<=i} (k_j - m)(k_j - m)^T
 // + lam I about the group's point m (k_0 for g = 0, else the mean of the
@@ -539,11 +544,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void pc
 // U^T z takes z straight from the accumulators), V and V^T, and -M U (two
 // terms each, MFMA operand order with the key index permuted as an
 // accumulator's rows are), each under a power-of-two scale. M U and A are
-// formed in fp32 on the vector ALU (0.5 M and 0.13 M multiply-adds at d = 128)
-// from the M the CG kernel applies (the slot's two fp16 terms); L and V by a
-// left-looking Cholesky and a forward substitution, one column per lane. A
-// pivot that is not positive and finite leaves the record invalid: the CG
-// kernel then preconditions those rows with P_g alone.
+// formed in fp32 on the vector ALU (0.5 M and 0.13 M multiply-adds at d = 128,
+// 4 x 4 register blocks) from the M the CG kernel applies (the slot's two fp16
+// terms); L and V by a right-looking Cholesky and a forward substitution in one
+// wave's registers (lane i: row i of L, column i of V). A pivot that is not
+// positive and finite leaves the record invalid: the CG kernel then
+// preconditions those rows with P_g alone.
 template <int D>
 __global__ __launch_bounds__(NT) void pc_wood(const float* __restrict__ partial, int nchunk, int n,
                                               int nblk, int nslots, float lambda,
@@ -553,11 +559,13 @@ __global__ __launch_bounds__(NT) void pc_wood(const float* __restrict__ partial,
                                               const float* __restrict__ tsum,
                                               _Float16* __restrict__ pcw, float* __restrict__ pcws) {
   constexpr int NMB = D / 32;
-  __shared__ float sM[D][D + 1];
-  __shared__ float sU[D][33];
-  __shared__ float sMU[D][33];
-  __shared__ float sA[32][33];
-  __shared__ float sV[32][33];
+  constexpr int LM = D + 4;  // row stride of sMt (floats)
+  constexpr int LU = 36;     // row stride of sU, sMU, sA (floats)
+  __shared__ __align__(16) float sMt[D * LM];  // sMt[k][dim] = M[dim][k]
+  __shared__ __align__(16) float sU[D * LU];   // U[dim][j]
+  __shared__ __align__(16) float sMU[D * LU];  // (M U)[dim][j]
+  __shared__ __align__(16) float sA[32 * LU];  // A[i][j]
+  __shared__ float sV[32][33];                 // V[i][j]
   __shared__ float sm[D];
   __shared__ float sRed[3][NT / 64];
   __shared__ float sS[2];
@@ -591,82 +599,117 @@ __global__ __launch_bounds__(NT) void pc_wood(const float* __restrict__ partial,
     sm[dim] = g == 0 ? static_cast<float>(tile0[(p >> 3) * BK * 8 + (p & 7)])
                      : tsum[slot * D + dim] / static_cast<float>(32 * g);
   }
-  __syncthreads();
-  // U (natural dims x 32 keys) and M (natural)
-  for (int e = tid; e < D * 32; e += NT) {
-    const int p = e >> 5, j = e & 31;
-    const int dim = (p & ~15) | swz16(p & 15);
-    const float kv = static_cast<float>(tileg[((p >> 3) * BK + j) * 8 + (p & 7)]);
-    sU[dim][j] = 32 * g + j < n ? kv - sm[dim] : 0.f;
-  }
+  // M, transposed (natural dims), from the slot's two terms or I / lambda
   if (g == 0) {
     const float il = 1.f / lam_s;
-    for (int e = tid; e < D * D; e += NT) sM[e / D][e % D] = (e / D == e % D) ? il : 0.f;
+    for (int e = tid; e < D * D; e += NT) sMt[(e / D) * LM + e % D] = (e / D == e % D) ? il : 0.f;
   } else {
     const float ms = pcs[slot];
-    const _Float16* hiM = pcm + slot * 2 * D * D;
-    const _Float16* loM = hiM + D * D;
-    for (int e = tid; e < D * D; e += NT) {
-      const int row = e / D, col = e % D;
-      const int pcol = (col & ~15) | swz16(col & 15);
-      const int t = pcol >> 4, fg = (pcol >> 3) & 1, el = pcol & 7;
-      const int fi = (((t * (D / 32) + (row >> 5)) * 64 + 32 * fg + (row & 31)) * 8) + el;
-      sM[row][col] = ms * (static_cast<float>(hiM[fi]) + static_cast<float>(loM[fi]));
-    }
-  }
-  __syncthreads();
-  // M U
-  for (int e = tid; e < D * 32; e += NT) {
-    const int dim = e >> 5, j = e & 31;
-    float a = 0.f;
-    for (int k = 0; k < D; ++k) a = fmaf(sM[dim][k], sU[k][j], a);
-    sMU[dim][j] = a;
-  }
-  __syncthreads();
-  // A = I + U^T M U
-  for (int e = tid; e < 32 * 32; e += NT) {
-    const int i = e >> 5, j = e & 31;
-    float a = i == j ? 1.f : 0.f;
-    for (int k = 0; k < D; ++k) a = fmaf(sU[k][i], sMU[k][j], a);
-    sA[i][j] = a;
-  }
-  __syncthreads();
-  // Cholesky A = L L^T in place (lower triangle), one row per lane of wave 0
-  if (wave == 0) {
-    bool bad = false;
-    for (int k = 0; k < 32; ++k) {
-      // the diagonal (every lane computes it; lanes agree)
-      float a = sA[k][k];
-      for (int j = 0; j < k; ++j) a = fmaf(-sA[k][j], sA[k][j], a);
-      bad = bad || !(a > 0.f) || !(a < INFINITY);
-      const float lkk = sqrtf(fmaxf(a, 0.f));
-      const float il = bad ? 0.f : 1.f / lkk;
-      if (lane > k && lane < 32) {
-        float b = sA[lane][k];
-        for (int j = 0; j < k; ++j) b = fmaf(-sA[lane][j], sA[k][j], b);
-        sA[lane][k] = b * il;
+    const half8* hiM = reinterpret_cast<const half8*>(pcm + slot * 2 * D * D);
+    const half8* loM = hiM + D * D / 8;
+    // fragment f: row 32 rb + r, permuted columns 16 t + 8 fg + (0..7)
+    for (int f = tid; f < D * D / 8; f += NT) {
+      const int r = f & 31, fg = (f >> 5) & 1, rb = (f >> 6) % NMB, t = (f >> 6) / NMB;
+      const int row = 32 * rb + r;
+      const half8 h = hiM[f], l = loM[f];
+      #pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int pcol = 16 * t + 8 * fg + c;
+        const int col = (pcol & ~15) | swz16(pcol & 15);
+        sMt[col * LM + row] = ms * (static_cast<float>(h[c]) + static_cast<float>(l[c]));
       }
-      __builtin_amdgcn_s_waitcnt(0);
-      __builtin_amdgcn_wave_barrier();
-      if (lane == k) sA[k][k] = lkk;
-      __builtin_amdgcn_s_waitcnt(0);
-      __builtin_amdgcn_wave_barrier();
     }
-    // V = L^{-1}: column c in lane c
-    if (lane < 32 && !bad) {
-      const int c = lane;
+  }
+  __syncthreads();
+  // U (natural dims x 32 keys): chunk f holds positions 8 (f >> 5) .. + 7 of key f & 31
+  for (int f = tid; f < D * 4; f += NT) {
+    const int pb = f >> 5, j = f & 31;
+    const half8 kv = reinterpret_cast<const half8*>(tileg)[f];
+    #pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int p = 8 * pb + c;
+      const int dim = (p & ~15) | swz16(p & 15);
+      sU[dim * LU + j] = 32 * g + j < n ? static_cast<float>(kv[c]) - sm[dim] : 0.f;
+    }
+  }
+  __syncthreads();
+  // M U: a 4 x 4 block (dims d0.., keys j0..) per item
+  for (int e = tid; e < D * 2; e += NT) {
+    const int d0 = 4 * (e >> 3), j0 = 4 * (e & 7);
+    float4 acc[4];
+    #pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    #pragma unroll 4
+    for (int k = 0; k < D; ++k) {
+      const float4 m = *reinterpret_cast<const float4*>(sMt + k * LM + d0);
+      const float4 u = *reinterpret_cast<const float4*>(sU + k * LU + j0);
+      const float mv[4] = {m.x, m.y, m.z, m.w};
+      #pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[i].x = fmaf(mv[i], u.x, acc[i].x);
+        acc[i].y = fmaf(mv[i], u.y, acc[i].y);
+        acc[i].z = fmaf(mv[i], u.z, acc[i].z);
+        acc[i].w = fmaf(mv[i], u.w, acc[i].w);
+      }
+    }
+    #pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<float4*>(sMU + (d0 + i) * LU + j0) = acc[i];
+  }
+  __syncthreads();
+  // A = I + U^T M U: keys (i, j0..j0+3) per item
+  for (int e = tid; e < 32 * 8; e += NT) {
+    const int i = e >> 3, j0 = 4 * (e & 7);
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    #pragma unroll 8
+    for (int k = 0; k < D; ++k) {
+      const float u = sU[k * LU + i];
+      const float4 m = *reinterpret_cast<const float4*>(sMU + k * LU + j0);
+      a.x = fmaf(u, m.x, a.x);
+      a.y = fmaf(u, m.y, a.y);
+      a.z = fmaf(u, m.z, a.z);
+      a.w = fmaf(u, m.w, a.w);
+    }
+    if (i == j0) a.x += 1.f;
+    if (i == j0 + 1) a.y += 1.f;
+    if (i == j0 + 2) a.z += 1.f;
+    if (i == j0 + 3) a.w += 1.f;
+    *reinterpret_cast<float4*>(sA + i * LU + j0) = a;
+  }
+  __syncthreads();
+  // Cholesky A = L L^T and V = L^{-1} in wave 0's registers: lane i holds row
+  // i of A (then of L) and column i of V; other lanes' values by readlane
+  if (wave == 0) {
+    const int li = lane & 31;
+    float a[32];
+    #pragma unroll
+    for (int j = 0; j < 32; ++j) a[j] = sA[li * LU + j];
+    bool bad = false;
+    #pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const float piv = lane_value(a[k], k);  // A[k][k] less the first k columns' share
+      bad = bad || !(piv > 0.f) || !(piv < INFINITY);
+      const float lkk = sqrtf(fmaxf(piv, 0.f));
+      const float il = bad ? 0.f : 1.f / lkk;
+      const float lk = li == k ? lkk : (li > k ? a[k] * il : 0.f);  // L[li][k]
+      a[k] = lk;
+      #pragma unroll
+      for (int j = k + 1; j < 32; ++j) a[j] = fmaf(-lk, lane_value(lk, j), a[j]);
+    }
+    if (!bad) {
+      // column li of V: V[i][li] = 0 above the diagonal, 1 / L[i][i] on it,
+      // -(sum_{j<i} L[i][j] V[j][li]) / L[i][i] below
+      float v[32];
+      #pragma unroll
       for (int i = 0; i < 32; ++i) {
-        float v;
-        if (i < c) {
-          v = 0.f;
-        } else if (i == c) {
-          v = 1.f / sA[c][c];
-        } else {
-          float a = 0.f;
-          for (int j = c; j < i; ++j) a = fmaf(sA[i][j], sV[j][c], a);
-          v = -a / sA[i][i];
-        }
-        sV[i][c] = v;
+        float acc = 0.f;
+        #pragma unroll
+        for (int j = 0; j < i; ++j) acc = fmaf(lane_value(a[j], i), v[j], acc);
+        const float lii = lane_value(a[i], i);
+        v[i] = li > i ? 0.f : (li == i ? 1.f / lii : -acc / lii);
+      }
+      if (lane < 32) {
+        #pragma unroll
+        for (int i = 0; i < 32; ++i) sV[i][lane] = v[i];
       }
     }
     if (lane == 0) sBad = bad ? 1 : 0;
@@ -679,8 +722,8 @@ __global__ __launch_bounds__(NT) void pc_wood(const float* __restrict__ partial,
   // power-of-two scales of U, V and M U
   float mu_ = 0.f, mv_ = 0.f, mm_ = 0.f;
   for (int e = tid; e < D * 32; e += NT) {
-    mu_ = fmaxf(mu_, fabsf(sU[e >> 5][e & 31]));
-    mm_ = fmaxf(mm_, fabsf(sMU[e >> 5][e & 31]));
+    mu_ = fmaxf(mu_, fabsf(sU[(e >> 5) * LU + (e & 31)]));
+    mm_ = fmaxf(mm_, fabsf(sMU[(e >> 5) * LU + (e & 31)]));
   }
   for (int e = tid; e < 32 * 32; e += NT) mv_ = fmaxf(mv_, fabsf(sV[e >> 5][e & 31]));
   mu_ = wave_max(mu_);
@@ -704,35 +747,59 @@ __global__ __launch_bounds__(NT) void pc_wood(const float* __restrict__ partial,
   sv_ = pow2_ceil(sv_);
   smu = pow2_ceil(smu);
   const float iu = 1.f / su, iv = 1.f / sv_, imu = 1.f / smu;
-  auto split = [](float x, _Float16* hi, _Float16* lo, size_t at, size_t off) {
-    const _Float16 h = static_cast<_Float16>(x);
-    hi[at] = h;
-    lo[at + off] = static_cast<_Float16>(x - static_cast<float>(h));
+  // x in two fp16 terms, stored as the 8-half chunks f of hi and hi + off
+  auto put8 = [](const float (&x)[8], _Float16* base, int f, int off) {
+    half8 h, l;
+    #pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      h[c] = static_cast<_Float16>(x[c]);
+      l[c] = static_cast<_Float16>(x[c] - static_cast<float>(h[c]));
+    }
+    reinterpret_cast<half8*>(base)[f] = h;
+    reinterpret_cast<half8*>(base + off)[f] = l;
   };
   // U: row-tile layout, position p (dims swz16-permuted) of key j at
   // ((p >> 3) * 32 + j) * 8 + (p & 7)
-  for (int e = tid; e < D * 32; e += NT) {
-    const int p = e >> 5, j = e & 31;
-    const int dim = (p & ~15) | swz16(p & 15);
-    split(sU[dim][j] * iu, rec, rec, ((p >> 3) * 32 + j) * 8 + (p & 7), 32 * D);
+  for (int f = tid; f < D * 4; f += NT) {
+    const int pb = f >> 5, j = f & 31;
+    float x[8];
+    #pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int p = 8 * pb + c;
+      x[c] = sU[((p & ~15) | swz16(p & 15)) * LU + j] * iu;
+    }
+    put8(x, rec, f, 32 * D);
   }
   // operand fragments over the group's 32 keys as the K index: lane l =
   // 32 fg + ql, k-step t, slot c holds key kp = swz(16 t + 8 fg + c), the row
   // of an accumulator that the lane's register 8 t + c holds
   _Float16* V0 = rec + 64 * D;
-  for (int e = tid; e < 2 * 64 * 8; e += NT) {
-    const int t = e >> 9, l = (e >> 3) & 63, c = e & 7;
-    const int fg = l >> 5, ql = l & 31, p = 16 * t + 8 * fg + c;
-    const int kp = (p & ~15) | swz16(p & 15);
-    split(sV[ql][kp] * iv, V0, V0, e, 1024);           // V: row ql
-    split(sV[kp][ql] * iv, V0 + 2048, V0 + 2048, e, 1024);  // V^T: row ql
+  for (int f = tid; f < 2 * 64; f += NT) {
+    const int t = f >> 6, l = f & 63;
+    const int fg = l >> 5, ql = l & 31;
+    float xv[8], xt[8];
+    #pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int p = 16 * t + 8 * fg + c;
+      const int kp = (p & ~15) | swz16(p & 15);
+      xv[c] = sV[ql][kp] * iv;  // V: row ql
+      xt[c] = sV[kp][ql] * iv;  // V^T: row ql
+    }
+    put8(xv, V0, f, 1024);
+    put8(xt, V0 + 2048, f, 1024);
   }
   _Float16* N0 = rec + 64 * D + 4096;
-  for (int e = tid; e < 2 * NMB * 64 * 8; e += NT) {
-    const int t = e / (NMB * 512), mb = (e / 512) % NMB, l = (e >> 3) & 63, c = e & 7;
-    const int fg = l >> 5, ql = l & 31, p = 16 * t + 8 * fg + c;
-    const int kp = (p & ~15) | swz16(p & 15);
-    split(-sMU[32 * mb + ql][kp] * imu, N0, N0, e, 32 * D);
+  for (int f = tid; f < 2 * NMB * 64; f += NT) {
+    const int t = f / (NMB * 64), mb = (f / 64) % NMB, l = f & 63;
+    const int fg = l >> 5, ql = l & 31;
+    float x[8];
+    #pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int p = 16 * t + 8 * fg + c;
+      const int kp = (p & ~15) | swz16(p & 15);
+      x[c] = -sMU[(32 * mb + ql) * LU + kp] * imu;
+    }
+    put8(x, N0, f, 32 * D);
   }
   if (tid == 0) {
     sc[0] = su;
