@@ -1,22 +1,25 @@
-// fp32 vector-ALU kernel for the causal LLA forward pass.
+// fp32 vector-ALU kernels for the causal LLA forward and backward passes.
 //
-// One workgroup of 256 threads owns a block of VQ = 32 consecutive query rows
-// of one (batch, head) and runs all three phases of the blocked forward of
-// "Local Linear Attention: reading notes" (section 2.2, Algorithm 1) for it:
+// In the forward, one workgroup of 256 threads owns a block of 8, 16 or 32
+// consecutive query rows of one (batch, head) and runs all three phases of the
+// blocked forward of "Local Linear Attention: reading notes" (section 2.2,
+// Algorithm 1) for it:
 //   1. scan key tiles with an online row max -> omega_i, mu~_i (Eqs. (10)-(11))
 //   2. matrix-free CG, one key-tile sweep per iteration for the Gram product
 //      (Eq. (12), centred at kbar_i = mu~_i / omega_i; see include/lla.h)
 //   3. scan key/value tiles -> out_i = sum_j w_ij (1 - (k_j - kbar_i)^T rho) v_j
 //      / sum_j w_ij (1 - (k_j - kbar_i)^T rho)
 // Per-query CG state lives in registers (x, r, kbar, accumulators) and LDS
-// (q, p); the weights exist only as a VQ x VK tile in LDS.
+// (q, p); the weights exist only as a rows x tile-keys tile in LDS. The next
+// key (and value) tile is loaded into registers while the current one is used.
 //
-// Thread roles: thread t serves query row t >> 3 together with the 7 other
-// threads of its group of 8 lanes (row reductions are 3 xor-shuffles). For
-// score tiles it computes keys (t & 7) and (t & 7) + 8 of the tile; for
-// d-vectors it owns the float4 chunks (t & 7) + 8 u of the row.
+// Thread roles (forward): the LPR = 8, 16 or 32 lanes of a row group serve one
+// query row (row reductions are xor-shuffles within the group). For score
+// tiles a lane computes keys l and l + LPR of a 2 LPR-key tile; for d-vectors
+// it owns float4 chunks and a slice of the tile's keys (struct Lanes below).
+// The backward keeps 32 rows per workgroup and 8 lanes per row.
 //
-// This kernel is the fp32 path (fp32 inputs must not be rounded to a 16-bit
+// These kernels are the fp32 path (fp32 inputs must not be rounded to a 16-bit
 // matrix type) and the reference GPU path for bf16 inputs.
 
 #include <hip/hip_runtime.h>
@@ -30,8 +33,8 @@
 namespace lla {
 namespace {
 
-constexpr int VQ = 32;   // queries per workgroup
-constexpr int VK = 16;   // keys per tile
+constexpr int VQ = 32;   // queries per workgroup (backward)
+constexpr int VK = 16;   // keys per tile (backward)
 constexpr int VT = 256;  // threads per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -83,27 +86,107 @@ __device__ __forceinline__ void stage_rows(float* dst, const Tin* src, int r0, i
   }
 }
 
-template <int D, typename Tin>
-__global__ __launch_bounds__(VT) void lla_valu_kernel(FwdParams P) {
-  constexpr int LD = D + 4;           // padded LDS row stride (floats)
-  constexpr int NC = D / 4;           // float4 chunks per row
-  constexpr int YC = (NC + 7) / 8;    // chunks owned per thread
-  __shared__ __align__(16) float sQ[VQ * LD];  // q rows of the block
-  __shared__ __align__(16) float sP[VQ * LD];  // p (phase 2) / rho (phase 3)
-  __shared__ __align__(16) float sK[VK * LD];  // key tile
-  __shared__ __align__(16) float sV[VK * LD];  // value tile (phase 3)
-  __shared__ float sW[VQ * (VK + 1)];          // weight-derived tile
+// Lane layout of the forward. LPR lanes serve one query row, so a workgroup
+// holds VQ = VT / LPR rows and a key tile VK = 2 LPR keys (two scores per
+// lane). A d-vector is split into CL = min(d / 4, LPR) float4 columns and
+// S = LPR / CL key slices: lane l of a row owns chunks (l % CL) + CL u and
+// adds up keys l / CL + S m of each tile; the slices are summed once per
+// sweep. Small problems take more lanes per row (more workgroups, fewer and
+// wider tiles per sweep); large ones fewer (keys re-read by fewer blocks).
+template <int D, int LPR>
+struct Lanes {
+  static constexpr int VQ = VT / LPR;
+  static constexpr int VK = 2 * LPR;
+  static constexpr int NC = D / 4;
+  static constexpr int CL = NC < LPR ? NC : LPR;
+  static constexpr int S = LPR / CL;
+  static constexpr int YC = NC / CL;
+};
+
+// sum / max over the W lanes of a row group (W a power of two <= 64)
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+  #pragma unroll
+  for (int o = 1; o < W; o <<= 1) v += __shfl_xor(v, o);
+  return v;
+}
+template <int W>
+__device__ __forceinline__ float group_max(float v) {
+  #pragma unroll
+  for (int o = 1; o < W; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+// sum of a chunk over the key slices (lanes CL, 2 CL, ... apart)
+template <int CL, int LPR>
+__device__ __forceinline__ float4 slice_sum(float4 a) {
+  #pragma unroll
+  for (int o = CL; o < LPR; o <<= 1) {
+    a.x += __shfl_xor(a.x, o);
+    a.y += __shfl_xor(a.y, o);
+    a.z += __shfl_xor(a.z, o);
+    a.w += __shfl_xor(a.w, o);
+  }
+  return a;
+}
+
+// A tile of ROWS rows of a [n][D] matrix held in registers between its global
+// loads and its LDS store, so that the next tile's loads are in flight while
+// the current one is used (float4 e = threadIdx.x + VT u of the tile).
+template <int D, int ROWS>
+struct TileRegs {
+  static constexpr int NC = D / 4;
+  static constexpr int NU = ROWS > 0 ? (ROWS * NC + VT - 1) / VT : 1;  // (1: unused)
+  float4 v[NU];
+  // rows [r0, r0 + ROWS), zero at or beyond rend
+  template <typename Tin>
+  __device__ __forceinline__ void load(const Tin* src, int r0, int rend) {
+    #pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int e = static_cast<int>(threadIdx.x) + VT * u;
+      const int r = e / NC, c = (e % NC) * 4;
+      v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (e < ROWS * NC && r0 + r < rend) v[u] = load4(src, static_cast<size_t>(r0 + r) * D + c);
+    }
+  }
+  template <int LD>
+  __device__ __forceinline__ void store(float* dst) const {
+    #pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int e = static_cast<int>(threadIdx.x) + VT * u;
+      if (e < ROWS * NC) *reinterpret_cast<float4*>(dst + (e / NC) * LD + (e % NC) * 4) = v[u];
+    }
+  }
+};
+
+// ls > 0: the block's score weights are kept in dynamic LDS (row r, key j at
+// r ls + j), written in phase 1 and read by every later sweep in place of the
+// q . k products and exponentials (the same weights up to the rounding of the
+// score's scaling, which the recomputing form may fuse into the exponent's
+// subtraction).
+template <int D, typename Tin, int LPR>
+__global__ __launch_bounds__(VT) void lla_valu_kernel(FwdParams P, int ls) {
+  using L = Lanes<D, LPR>;
+  constexpr int BQ = L::VQ, BKV = L::VK, CL = L::CL, S = L::S, YC = L::YC;
+  constexpr int LD = D + 4;   // padded LDS row stride (floats)
+  constexpr int LW = BKV + 1;  // row stride of the weight tile
+  __shared__ __align__(16) float sQ[BQ * LD];   // q rows of the block
+  __shared__ __align__(16) float sP[BQ * LD];   // p (phase 2) / rho (phase 3)
+  __shared__ __align__(16) float sK[BKV * LD];  // key tile
+  __shared__ __align__(16) float sV[BKV * LD];  // value tile (phase 3)
+  __shared__ float sW[BQ * LW];                 // weight-derived tile
   __shared__ int sAny;
+  extern __shared__ float sS[];                 // cached weights (ls > 0)
 
   const int tid = threadIdx.x;
-  const int row = tid >> 3;
-  const int l8 = tid & 7;
-  const int nqb = (P.n + VQ - 1) / VQ;
+  const int row = tid / LPR;
+  const int ln = tid % LPR;
+  const int cl = ln % CL, sl = ln / CL;
+  const int nqb = (P.n + BQ - 1) / BQ;
   const int blk = blockIdx.x;
   const int qb = nqb - 1 - blk / P.BH;  // longest causal prefix first
   const int bh = blk % P.BH;
-  const int i0 = qb * VQ;
-  const int nq = min(VQ, P.n - i0);
+  const int i0 = qb * BQ;
+  const int nq = min(BQ, P.n - i0);
   const int kend = i0 + nq;           // keys 0 .. kend-1 are visible to the block
   const int qi = i0 + row;            // this thread's query row
   const bool valid = row < nq;
@@ -113,8 +196,45 @@ __global__ __launch_bounds__(VT) void lla_valu_kernel(FwdParams P) {
   const Tin* V = static_cast<const Tin*>(P.v) + base;
   const float sc2 = kLog2e / sqrtf(static_cast<float>(D));  // scores in log2 units
   const float lam = P.lambda;
+  const float* qrow = sQ + row * LD;
+  const float* prow = sP + row * LD;
+  const bool cached = ls > 0;  // uniform
+  float* srow = sS + row * ls;
 
-  stage_rows<D, LD>(sQ, Q, i0, VQ, kend);
+  // Small blocks (more lanes per row) are latency-bound: they load the next
+  // tile into registers while the current one is used. With 32 rows per
+  // block the registers are better spent on the block's own state.
+  constexpr bool PREFETCH = LPR > 8;
+  stage_rows<D, LD>(sQ, Q, i0, BQ, kend);
+  TileRegs<D, PREFETCH ? BKV : 0> kpre;
+  auto first_keys = [&]() __attribute__((always_inline)) {
+    if constexpr (PREFETCH) kpre.load(K, 0, kend);
+  };
+  // key tile kt into sK (between two barriers)
+  auto next_keys = [&](int kt) __attribute__((always_inline)) {
+    __syncthreads();
+    if constexpr (PREFETCH) {
+      kpre.template store<LD>(sK);
+      if (kt + BKV < kend) kpre.load(K, kt + BKV, kend);
+    } else {
+      stage_rows<D, LD>(sK, K, kt, BKV, kend);
+    }
+    __syncthreads();
+  };
+  // acc[u] += sum over this lane's slice of the tile's keys of sW[row][kk] X[kk][chunk u]
+  auto tile_product = [&](float4 (&a)[YC], const float* X) __attribute__((always_inline)) {
+    #pragma unroll
+    for (int u = 0; u < YC; ++u) {
+      const int c = (cl + CL * u) * 4;
+      float4 t = a[u];
+      #pragma unroll
+      for (int m = 0; m < BKV / S; ++m) {
+        const int kk = sl + S * m;
+        t = fma4(sW[row * LW + kk], *reinterpret_cast<const float4*>(X + kk * LD + c), t);
+      }
+      a[u] = t;
+    }
+  };
 
   // ---------------- phase 1: online max, omega, mu~ ----------------
   float m2 = -INFINITY;  // running row max (log2 units)
@@ -122,58 +242,59 @@ __global__ __launch_bounds__(VT) void lla_valu_kernel(FwdParams P) {
   float4 acc[YC];
   for (int u = 0; u < YC; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
 
-  for (int kt = 0; kt < kend; kt += VK) {
-    __syncthreads();
-    stage_rows<D, LD>(sK, K, kt, VK, kend);
-    __syncthreads();
+  first_keys();
+  for (int kt = 0; kt < kend; kt += BKV) {
+    next_keys(kt);
     float s[2];
     float tmax = -INFINITY;
     for (int u = 0; u < 2; ++u) {
-      const int kc = l8 + 8 * u;
+      const int kc = ln + LPR * u;
       const int j = kt + kc;
       float dsum = 0.f;
       for (int c = 0; c < D; c += 4)
-        dsum += dot4(*reinterpret_cast<const float4*>(sQ + row * LD + c),
+        dsum += dot4(*reinterpret_cast<const float4*>(qrow + c),
                      *reinterpret_cast<const float4*>(sK + kc * LD + c));
       s[u] = (valid && j <= qi) ? dsum * sc2 : -INFINITY;
       tmax = fmaxf(tmax, s[u]);
+      if (cached) srow[j] = s[u];
     }
-    tmax = row_max8(tmax);
+    tmax = group_max<LPR>(tmax);
     const float mnew = fmaxf(m2, tmax);
     const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(m2 - mnew);
     float psum = 0.f;
     for (int u = 0; u < 2; ++u) {
       const float w = (s[u] == -INFINITY) ? 0.f : exp2f(s[u] - mnew);
-      sW[row * (VK + 1) + l8 + 8 * u] = w;
+      sW[row * LW + ln + LPR * u] = w;
       psum += w;
     }
-    om = om * alpha + row_sum8(psum);
+    om = om * alpha + group_sum<LPR>(psum);
     m2 = mnew;
     for (int u = 0; u < YC; ++u) {
       acc[u].x *= alpha; acc[u].y *= alpha; acc[u].z *= alpha; acc[u].w *= alpha;
     }
     __syncthreads();
-    for (int u = 0; u < YC; ++u) {
-      const int c = (l8 + 8 * u) * 4;
-      if (c < D) {
-        float4 a = acc[u];
-        for (int kk = 0; kk < VK; ++kk)
-          a = fma4(sW[row * (VK + 1) + kk], *reinterpret_cast<const float4*>(sK + kk * LD + c), a);
-        acc[u] = a;
-      }
+    tile_product(acc, sK);
+  }
+  for (int u = 0; u < YC; ++u) acc[u] = slice_sum<CL, LPR>(acc[u]);
+  // scores -> weights against the final row max (each lane its own keys)
+  if (cached) {
+    for (int j = ln; j < kend; j += LPR) {
+      const float sj = srow[j];
+      srow[j] = (sj == -INFINITY) ? 0.f : exp2f(sj - m2);
     }
   }
 
   // ------------- CG set-up on the mean-centred system ----------------
   // kbar = mu~ / omega; mu = mu~ - omega q = omega (kbar - q); x0 = 0, r0 = p0 = mu.
+  // Every slice holds the row's chunks; dot products sum over the CL chunk lanes.
   float4 kb[YC], x[YC], r[YC];
   float rr = 0.f, kp = 0.f;
   const float inv_om = valid ? 1.f / om : 0.f;
   for (int u = 0; u < YC; ++u) {
-    const int c = (l8 + 8 * u) * 4;
+    const int c = (cl + CL * u) * 4;
     kb[u] = x[u] = r[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (c < D && valid) {
-      const float4 qv = *reinterpret_cast<const float4*>(sQ + row * LD + c);
+    if (valid) {
+      const float4 qv = *reinterpret_cast<const float4*>(qrow + c);
       const float4 a = acc[u];
       if (P.rho_in) {
         // rho supplied: no solve; the output scan is centred at q, which is
@@ -189,12 +310,12 @@ __global__ __launch_bounds__(VT) void lla_valu_kernel(FwdParams P) {
     }
   }
   __syncthreads();  // sP is free (phase 1 never touched it) but keep LDS phases apart
-  for (int u = 0; u < YC; ++u) {
-    const int c = (l8 + 8 * u) * 4;
-    if (c < D) *reinterpret_cast<float4*>(sP + row * LD + c) = r[u];
+  if (sl == 0) {
+    for (int u = 0; u < YC; ++u)
+      *reinterpret_cast<float4*>(sP + row * LD + (cl + CL * u) * 4) = r[u];
   }
-  rr = row_sum8(rr);
-  kp = row_sum8(kp);
+  rr = group_sum<CL>(rr);
+  kp = group_sum<CL>(kp);
   const float r0 = sqrtf(rr);
   const float stop_at = P.cg_rel_tol * r0;
   bool active = valid && rr > 0.f && P.cg_max_iters > 0;
@@ -204,57 +325,52 @@ __global__ __launch_bounds__(VT) void lla_valu_kernel(FwdParams P) {
   for (int it = 0; it < P.cg_max_iters; ++it) {
     if (tid == 0) sAny = 0;
     __syncthreads();
-    if (active && l8 == 0) sAny = 1;
+    if (active && ln == 0) sAny = 1;
     __syncthreads();
     if (!sAny) break;
     // Y = sum_j w_ij k_j ((k_j - kbar) . p) over the causal prefix
     float usum = 0.f;
     for (int u = 0; u < YC; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int kt = 0; kt < kend; kt += VK) {
-      __syncthreads();
-      stage_rows<D, LD>(sK, K, kt, VK, kend);
-      __syncthreads();
+    first_keys();
+    for (int kt = 0; kt < kend; kt += BKV) {
+      next_keys(kt);
       for (int u = 0; u < 2; ++u) {
-        const int kc = l8 + 8 * u;
+        const int kc = ln + LPR * u;
         const int j = kt + kc;
         float ds = 0.f, dt = 0.f;
-        for (int c = 0; c < D; c += 4) {
-          const float4 kv = *reinterpret_cast<const float4*>(sK + kc * LD + c);
-          ds += dot4(*reinterpret_cast<const float4*>(sQ + row * LD + c), kv);
-          dt += dot4(*reinterpret_cast<const float4*>(sP + row * LD + c), kv);
+        if (cached) {
+          for (int c = 0; c < D; c += 4)
+            dt += dot4(*reinterpret_cast<const float4*>(prow + c),
+                       *reinterpret_cast<const float4*>(sK + kc * LD + c));
+        } else {
+          for (int c = 0; c < D; c += 4) {
+            const float4 kv = *reinterpret_cast<const float4*>(sK + kc * LD + c);
+            ds += dot4(*reinterpret_cast<const float4*>(qrow + c), kv);
+            dt += dot4(*reinterpret_cast<const float4*>(prow + c), kv);
+          }
         }
         float U = 0.f;
-        if (valid && j <= qi) U = exp2f(ds * sc2 - m2) * (dt - kp);
-        sW[row * (VK + 1) + kc] = U;
+        if (valid && j <= qi) U = (cached ? srow[j] : exp2f(ds * sc2 - m2)) * (dt - kp);
+        sW[row * LW + kc] = U;
         usum += U;
       }
       __syncthreads();
-      for (int u = 0; u < YC; ++u) {
-        const int c = (l8 + 8 * u) * 4;
-        if (c < D) {
-          float4 a = acc[u];
-          for (int kk = 0; kk < VK; ++kk)
-            a = fma4(sW[row * (VK + 1) + kk], *reinterpret_cast<const float4*>(sK + kk * LD + c), a);
-          acc[u] = a;
-        }
-      }
+      tile_product(acc, sK);
     }
-    usum = row_sum8(usum);
+    usum = group_sum<LPR>(usum);
+    for (int u = 0; u < YC; ++u) acc[u] = slice_sum<CL, LPR>(acc[u]);
     // Sigma_c p = Y - (sum_j U_ij) kbar + lambda p; then the CG step.
     float pAp = 0.f;
     float4 Ap[YC], pv[YC];
     for (int u = 0; u < YC; ++u) {
-      const int c = (l8 + 8 * u) * 4;
-      pv[u] = Ap[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (c < D) {
-        pv[u] = *reinterpret_cast<const float4*>(sP + row * LD + c);
-        const float4 a = acc[u];
-        Ap[u] = make_float4(a.x - usum * kb[u].x + lam * pv[u].x, a.y - usum * kb[u].y + lam * pv[u].y,
-                            a.z - usum * kb[u].z + lam * pv[u].z, a.w - usum * kb[u].w + lam * pv[u].w);
-        pAp += dot4(pv[u], Ap[u]);
-      }
+      const int c = (cl + CL * u) * 4;
+      pv[u] = *reinterpret_cast<const float4*>(prow + c);
+      const float4 a = acc[u];
+      Ap[u] = make_float4(a.x - usum * kb[u].x + lam * pv[u].x, a.y - usum * kb[u].y + lam * pv[u].y,
+                          a.z - usum * kb[u].z + lam * pv[u].z, a.w - usum * kb[u].w + lam * pv[u].w);
+      pAp += dot4(pv[u], Ap[u]);
     }
-    pAp = row_sum8(pAp);
+    pAp = group_sum<CL>(pAp);
     bool step = active && pAp > 0.f;
     if (active && !step) active = false;  // breakdown
     float rrn = 0.f;
@@ -266,7 +382,7 @@ __global__ __launch_bounds__(VT) void lla_valu_kernel(FwdParams P) {
       }
       rrn += dot4(r[u], r[u]);
     }
-    rrn = row_sum8(rrn);
+    rrn = group_sum<CL>(rrn);
     float kpn = 0.f;
     if (step) {
       ++iters;
@@ -275,15 +391,15 @@ __global__ __launch_bounds__(VT) void lla_valu_kernel(FwdParams P) {
       } else {
         const float be = rrn / rr;
         for (int u = 0; u < YC; ++u) {
-          const int c = (l8 + 8 * u) * 4;
           pv[u] = fma4(be, pv[u], r[u]);
-          if (c < D) *reinterpret_cast<float4*>(sP + row * LD + c) = pv[u];
+          // (every lane of the row has read p above: one wave holds the row)
+          if (sl == 0) *reinterpret_cast<float4*>(sP + row * LD + (cl + CL * u) * 4) = pv[u];
           kpn += dot4(kb[u], pv[u]);
         }
       }
       rr = rrn;
     }
-    kpn = row_sum8(kpn);
+    kpn = group_sum<CL>(kpn);
     if (active) kp = kpn;
     __syncthreads();
   }
@@ -293,56 +409,67 @@ __global__ __launch_bounds__(VT) void lla_valu_kernel(FwdParams P) {
   __syncthreads();
   float kr = 0.f, qr = 0.f;
   for (int u = 0; u < YC; ++u) {
-    const int c = (l8 + 8 * u) * 4;
-    if (c < D) {
-      *reinterpret_cast<float4*>(sP + row * LD + c) = x[u];
-      kr += dot4(kb[u], x[u]);
-      qr += dot4(*reinterpret_cast<const float4*>(sQ + row * LD + c), x[u]);
-    }
+    const int c = (cl + CL * u) * 4;
+    if (sl == 0) *reinterpret_cast<float4*>(sP + row * LD + c) = x[u];
+    kr += dot4(kb[u], x[u]);
+    qr += dot4(*reinterpret_cast<const float4*>(qrow + c), x[u]);
     acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  kr = row_sum8(kr);
-  qr = row_sum8(qr);
+  kr = group_sum<CL>(kr);
+  qr = group_sum<CL>(qr);
   float den = 0.f;
-  for (int kt = 0; kt < kend; kt += VK) {
+  TileRegs<D, PREFETCH ? BKV : 0> vpre;
+  if constexpr (PREFETCH) {
+    kpre.load(K, 0, kend);
+    vpre.load(V, 0, kend);
+  }
+  for (int kt = 0; kt < kend; kt += BKV) {
     __syncthreads();
-    stage_rows<D, LD>(sK, K, kt, VK, kend);
-    stage_rows<D, LD>(sV, V, kt, VK, kend);
+    if constexpr (PREFETCH) {
+      kpre.template store<LD>(sK);
+      vpre.template store<LD>(sV);
+      if (kt + BKV < kend) {
+        kpre.load(K, kt + BKV, kend);
+        vpre.load(V, kt + BKV, kend);
+      }
+    } else {
+      stage_rows<D, LD>(sK, K, kt, BKV, kend);
+      stage_rows<D, LD>(sV, V, kt, BKV, kend);
+    }
     __syncthreads();
     for (int u = 0; u < 2; ++u) {
-      const int kc = l8 + 8 * u;
+      const int kc = ln + LPR * u;
       const int j = kt + kc;
       float ds = 0.f, dr = 0.f;
-      for (int c = 0; c < D; c += 4) {
-        const float4 kv = *reinterpret_cast<const float4*>(sK + kc * LD + c);
-        ds += dot4(*reinterpret_cast<const float4*>(sQ + row * LD + c), kv);
-        dr += dot4(*reinterpret_cast<const float4*>(sP + row * LD + c), kv);
+      if (cached) {
+        for (int c = 0; c < D; c += 4)
+          dr += dot4(*reinterpret_cast<const float4*>(prow + c),
+                     *reinterpret_cast<const float4*>(sK + kc * LD + c));
+      } else {
+        for (int c = 0; c < D; c += 4) {
+          const float4 kv = *reinterpret_cast<const float4*>(sK + kc * LD + c);
+          ds += dot4(*reinterpret_cast<const float4*>(qrow + c), kv);
+          dr += dot4(*reinterpret_cast<const float4*>(prow + c), kv);
+        }
       }
       float a = 0.f;
-      if (valid && j <= qi) a = exp2f(ds * sc2 - m2) * (1.f - (dr - kr));
-      sW[row * (VK + 1) + kc] = a;
+      if (valid && j <= qi) a = (cached ? srow[j] : exp2f(ds * sc2 - m2)) * (1.f - (dr - kr));
+      sW[row * LW + kc] = a;
       den += a;
     }
     __syncthreads();
-    for (int u = 0; u < YC; ++u) {
-      const int c = (l8 + 8 * u) * 4;
-      if (c < D) {
-        float4 o = acc[u];
-        for (int kk = 0; kk < VK; ++kk)
-          o = fma4(sW[row * (VK + 1) + kk], *reinterpret_cast<const float4*>(sV + kk * LD + c), o);
-        acc[u] = o;
-      }
-    }
+    tile_product(acc, sV);
   }
-  den = row_sum8(den);
+  den = group_sum<LPR>(den);
+  for (int u = 0; u < YC; ++u) acc[u] = slice_sum<CL, LPR>(acc[u]);
   if (!valid) return;
   const size_t orow = static_cast<size_t>(bh) * P.n + qi;
   const float inv_den = 1.f / den;
   // the pages' rho_i = Sigma_i^{-1} mu_i = rho_c / (1 + (kbar - q) . rho_c)
   const float rs = 1.f / (1.f + (kr - qr));
-  for (int u = 0; u < YC; ++u) {
-    const int c = (l8 + 8 * u) * 4;
-    if (c < D) {
+  if (sl == 0) {
+    for (int u = 0; u < YC; ++u) {
+      const int c = (cl + CL * u) * 4;
       const float4 o = acc[u];
       *reinterpret_cast<float4*>(P.out + orow * D + c) =
           make_float4(o.x * inv_den, o.y * inv_den, o.z * inv_den, o.w * inv_den);
@@ -352,7 +479,7 @@ __global__ __launch_bounds__(VT) void lla_valu_kernel(FwdParams P) {
       if (P.rho_c) *reinterpret_cast<float4*>(P.rho_c + orow * D + c) = x[u];
     }
   }
-  if (l8 == 0) {
+  if (ln == 0) {
     if (P.omega) P.omega[orow] = om;
     if (P.rowmax) P.rowmax[orow] = m2 * kLn2;
     if (P.cg_iters) P.cg_iters[orow] = iters;
@@ -793,21 +920,42 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   }
 }
 
-template <int D, typename Tin>
-hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
-  const int nqb = (p.n + VQ - 1) / VQ;
+template <int D, typename Tin, int LPR>
+hipError_t launch_lanes(const FwdParams& p, hipStream_t stream) {
+  constexpr int BQ = Lanes<D, LPR>::VQ;
+  const int nqb = (p.n + BQ - 1) / BQ;
   const long long blocks = static_cast<long long>(nqb) * p.BH;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (p.ev_main_begin) {
     const hipError_t e = hipEventRecord(p.ev_main_begin, stream);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((lla_valu_kernel<D, Tin>), dim3(static_cast<unsigned>(blocks)), dim3(VT), 0,
-                     stream, p);
+  // the weight cache: rows of n keys rounded up to the tile, plus LPR floats so
+  // that a wave's rows start on different banks; only when it adds <= 64 KiB
+  const long long ls = (static_cast<long long>(p.n) + 2 * LPR - 1) / (2 * LPR) * (2 * LPR) + LPR;
+  const bool cache = ls * BQ * 4 <= 65536;
+  hipLaunchKernelGGL((lla_valu_kernel<D, Tin, LPR>), dim3(static_cast<unsigned>(blocks)), dim3(VT),
+                     cache ? static_cast<unsigned>(ls * BQ * 4) : 0u, stream, p, cache ? static_cast<int>(ls) : 0);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.ev_main_end) return hipEventRecord(p.ev_main_end, stream);
   return hipSuccess;
+}
+
+// The fewest lanes per row (most queries per workgroup) that still give
+// every compute unit two workgroups; at most 32.
+template <int D, typename Tin>
+hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const long long fill = 2LL * cus;
+  auto blocks = [&](int bq) { return static_cast<long long>((p.n + bq - 1) / bq) * p.BH; };
+  if (blocks(Lanes<D, 8>::VQ) >= fill) return launch_lanes<D, Tin, 8>(p, stream);
+  if (blocks(Lanes<D, 16>::VQ) >= fill) return launch_lanes<D, Tin, 16>(p, stream);
+  return launch_lanes<D, Tin, 32>(p, stream);
 }
 
 template <typename Tin>

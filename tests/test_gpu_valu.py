@@ -152,6 +152,31 @@ def test_ragged_sizes_f32(torch, n, d):
     np.testing.assert_allclose(res["out"][0, 0, 0], wl.v[0, 0, 0], rtol=1e-6, atol=1e-6)
 
 
+# The forward serves 32, 16 or 8 query rows per workgroup (8, 16 or 32 lanes
+# per row: the fewest that give each of the device's compute units two
+# workgroups; 256 on this device) and keeps a block's weights in LDS when n is
+# short enough (n <= 496, 992, 1984 for 32, 16, 8 rows). One shape per layout
+# and form of the sweeps, against the oracle on sampled rows of two heads.
+LAYOUTS = [
+    (1, 64, 256, 16, "32 rows, weights cached"),
+    (2, 8, 512, 32, "16 rows, cached"),
+    (1, 4, 2048, 64, "16 rows, recomputed"),
+    (1, 2, 1001, 128, "8 rows, cached, ragged tail"),
+    (1, 1, 4096, 16, "8 rows, recomputed"),
+]
+
+
+@pytest.mark.parametrize("B,H,n,d,layout", LAYOUTS, ids=[x[-1] for x in LAYOUTS])
+def test_lane_layouts_f32(torch, B, H, n, d, layout):
+    wl = make_random(B, H, n, d, "f32", seed=300 + n + d, qk_scale=2.0)
+    res = run(torch, wl, T=2 * d, tol=1e-7, lam=0.5)
+    rng = np.random.default_rng(n + d)
+    rows = sorted(set(range(40)) | set(range(n - 40, n)) | set(rng.integers(0, n, 40).tolist()))
+    heads = [(0, 0), (B - 1, H - 1)]
+    hr = [(bh, rows) for bh in heads]
+    compare(wl, res, F32_TOL, hr, 2 * d, 1e-7, lam=0.5, label=f"valu layout {layout} n={n} d={d}")
+
+
 @pytest.mark.parametrize("name", ["standard", "long", "recall"])
 def test_bf16_recipes_small_valu(torch, name):
     """The bf16 workloads' recipes at a size the oracle checks row by row."""
