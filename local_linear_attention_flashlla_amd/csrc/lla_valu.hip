@@ -17,7 +17,7 @@
 // query row (row reductions are xor-shuffles within the group). For score
 // tiles a lane computes keys l and l + LPR of a 2 LPR-key tile; for d-vectors
 // it owns float4 chunks and a slice of the tile's keys (struct Lanes below).
-// The backward keeps 32 rows per workgroup and 8 lanes per row.
+// The backward uses the same layouts.
 //
 // These kernels are the fp32 path (fp32 inputs must not be rounded to a 16-bit
 // matrix type) and the reference GPU path for bf16 inputs.
@@ -33,8 +33,6 @@
 namespace lla {
 namespace {
 
-constexpr int VQ = 32;   // queries per workgroup (backward)
-constexpr int VK = 16;   // keys per tile (backward)
 constexpr int VT = 256;  // threads per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -490,7 +488,8 @@ __global__ __launch_bounds__(VT) void lla_valu_kernel(FwdParams P, int ls) {
 // ---------------------------------------------------------------------------
 // Gradient of the forward above (fp32 arithmetic, any d in {16,32,64,128},
 // fp32 or bf16 inputs): dq, dk, dv of sum(dout * out). One workgroup per block
-// of VQ queries, the thread roles of the forward. The gradient is implicit
+// of 32, 16 or 8 queries, the lane layouts and the weight cache of the forward
+// (the same choice per launch). The gradient is implicit
 // differentiation of Eqs. (6)-(8) of "Local Linear Attention: reading notes"
 // (section 2.1) in the form centred at kbar, as in the matrix-core backward:
 //   h = C^T g,  adjoint CG  Sigma_c y = h  (the forward's CG loop on h),
@@ -503,33 +502,38 @@ __global__ __launch_bounds__(VT) void lla_valu_kernel(FwdParams P, int ls) {
 // (and with them the forward's rho_c) are reproduced exactly. dk and dv are
 // reduced over the block's queries in LDS per key tile and added to the
 // zero-filled outputs with fp32 atomics.
-template <int D, typename Tin>
-__global__ __launch_bounds__(VT) void lla_valu_bwd_kernel(BwdParams P) {
+template <int D, typename Tin, int LPR>
+__global__ __launch_bounds__(VT) void lla_valu_bwd_kernel(BwdParams P, int ls) {
+  using L = Lanes<D, LPR>;
+  constexpr int BQ = L::VQ, BKV = L::VK, NC = L::NC, CL = L::CL, S = L::S, YC = L::YC;
   constexpr int LD = D + 4;
-  constexpr int NC = D / 4;
-  constexpr int YC = (NC + 7) / 8;
-  __shared__ __align__(16) float sQ[VQ * LD];   // q rows
-  __shared__ __align__(16) float sG[VQ * LD];   // dout rows
-  __shared__ __align__(16) float sP[VQ * LD];   // CG direction, then rho_c
-  __shared__ __align__(16) float sY[VQ * LD];   // y
-  __shared__ __align__(16) float sK[VK * LD];
-  __shared__ __align__(16) float sV[VK * LD];
-  __shared__ float sW[VQ * (VK + 1)];           // weight tile / dL/ds
-  __shared__ float sA[VQ * (VK + 1)];           // c dL/ds with the max's share (dk)
-  __shared__ float sB[VQ * (VK + 1)];           // -w A
-  __shared__ float sE[VQ * (VK + 1)];           // -w e
-  __shared__ float sOm[VQ];
+  constexpr int LW = BKV + 1;
+  // as in the forward; at d = 128 the two tiles' registers would spill
+  constexpr bool PREFETCH = LPR > 8 && D <= 64;
+  __shared__ __align__(16) float sQ[BQ * LD];   // q rows
+  __shared__ __align__(16) float sG[BQ * LD];   // dout rows
+  __shared__ __align__(16) float sP[BQ * LD];   // CG direction, then rho_c
+  __shared__ __align__(16) float sY[BQ * LD];   // y
+  __shared__ __align__(16) float sK[BKV * LD];
+  __shared__ __align__(16) float sV[BKV * LD];
+  __shared__ float sW[BQ * LW];                 // weight tile / dL/ds
+  __shared__ float sA[BQ * LW];                 // c dL/ds with the max's share (dk)
+  __shared__ float sB[BQ * LW];                 // -w A
+  __shared__ float sE[BQ * LW];                 // -w e
+  __shared__ float sOm[BQ];
   __shared__ int sAny;
+  extern __shared__ float sS[];                 // cached weights (ls > 0), as in the forward
 
   const int tid = threadIdx.x;
-  const int row = tid >> 3;
-  const int l8 = tid & 7;
-  const int nqb = (P.n + VQ - 1) / VQ;
+  const int row = tid / LPR;
+  const int ln = tid % LPR;
+  const int cl = ln % CL, sl = ln / CL;
+  const int nqb = (P.n + BQ - 1) / BQ;
   const int blk = blockIdx.x;
   const int qb = nqb - 1 - blk / P.BH;
   const int bh = blk % P.BH;
-  const int i0 = qb * VQ;
-  const int nq = min(VQ, P.n - i0);
+  const int i0 = qb * BQ;
+  const int nq = min(BQ, P.n - i0);
   const int kend = i0 + nq;
   const int qi = i0 + row;
   const bool valid = row < nq;
@@ -541,14 +545,57 @@ __global__ __launch_bounds__(VT) void lla_valu_bwd_kernel(BwdParams P) {
   const float cs = 1.f / sqrtf(static_cast<float>(D));
   const float lam = P.lambda;
   const size_t orow = base + static_cast<size_t>(valid ? qi : i0) * D;
+  const float* qrow = sQ + row * LD;
+  const float* grow = sG + row * LD;
+  const float* prow = sP + row * LD;
+  const float* yrow = sY + row * LD;
+  const bool cached = ls > 0;  // uniform
+  float* srow = sS + row * ls;
 
-  stage_rows<D, LD>(sQ, Q, i0, VQ, kend);
-  for (int e = tid; e < VQ * NC; e += VT) {
+  stage_rows<D, LD>(sQ, Q, i0, BQ, kend);
+  for (int e = tid; e < BQ * NC; e += VT) {
     const int r = e / NC, c = (e % NC) * 4;
     float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
     if (r < nq) val = *reinterpret_cast<const float4*>(P.dout + base + static_cast<size_t>(i0 + r) * D + c);
     *reinterpret_cast<float4*>(sG + r * LD + c) = val;
   }
+  TileRegs<D, PREFETCH ? BKV : 0> kpre, vpre;
+  // the first tile of a sweep over K (and V)
+  auto first = [&](bool with_v) __attribute__((always_inline)) {
+    if constexpr (PREFETCH) {
+      kpre.load(K, 0, kend);
+      if (with_v) vpre.load(V, 0, kend);
+    }
+  };
+  // tile kt into sK (and sV) between two barriers, the next tile's loads issued
+  auto next = [&](int kt, bool with_v) __attribute__((always_inline)) {
+    __syncthreads();
+    if constexpr (PREFETCH) {
+      kpre.template store<LD>(sK);
+      if (with_v) vpre.template store<LD>(sV);
+      if (kt + BKV < kend) {
+        kpre.load(K, kt + BKV, kend);
+        if (with_v) vpre.load(V, kt + BKV, kend);
+      }
+    } else {
+      stage_rows<D, LD>(sK, K, kt, BKV, kend);
+      if (with_v) stage_rows<D, LD>(sV, V, kt, BKV, kend);
+    }
+    __syncthreads();
+  };
+  // acc[u] += sum over this lane's slice of the tile's keys of sW[row][kk] sK[kk][chunk u]
+  auto tile_product = [&](float4 (&a)[YC]) __attribute__((always_inline)) {
+    #pragma unroll
+    for (int u = 0; u < YC; ++u) {
+      const int c = (cl + CL * u) * 4;
+      float4 t = a[u];
+      for (int m = 0; m < BKV / S; ++m) {
+        const int kk = sl + S * m;
+        t = fma4(sW[row * LW + kk], *reinterpret_cast<const float4*>(sK + kk * LD + c), t);
+      }
+      a[u] = t;
+    }
+  };
 
   // ---------------- phase 1 (the forward's): row max, omega, mu~ ----------------
   float m2 = -INFINITY;
@@ -557,53 +604,53 @@ __global__ __launch_bounds__(VT) void lla_valu_bwd_kernel(BwdParams P) {
   for (int u = 0; u < YC; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
   float bestv = -INFINITY;
   int bestj = valid ? qi : 0;  // the maximising key (ties: the smaller index)
-  for (int kt = 0; kt < kend; kt += VK) {
-    __syncthreads();
-    stage_rows<D, LD>(sK, K, kt, VK, kend);
-    __syncthreads();
+  first(false);
+  for (int kt = 0; kt < kend; kt += BKV) {
+    next(kt, false);
     float s[2];
     float tmax = -INFINITY;
     for (int u = 0; u < 2; ++u) {
-      const int kc = l8 + 8 * u;
+      const int kc = ln + LPR * u;
       const int j = kt + kc;
       float dsum = 0.f;
       for (int c = 0; c < D; c += 4)
-        dsum += dot4(*reinterpret_cast<const float4*>(sQ + row * LD + c),
+        dsum += dot4(*reinterpret_cast<const float4*>(qrow + c),
                      *reinterpret_cast<const float4*>(sK + kc * LD + c));
       s[u] = (valid && j <= qi) ? dsum * sc2 : -INFINITY;
       tmax = fmaxf(tmax, s[u]);
+      if (cached) srow[j] = s[u];
       if (s[u] > bestv || (s[u] == bestv && s[u] != -INFINITY && j < bestj)) {
         bestv = s[u];
         bestj = j;
       }
     }
-    tmax = row_max8(tmax);
+    tmax = group_max<LPR>(tmax);
     const float mnew = fmaxf(m2, tmax);
     const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(m2 - mnew);
     float psum = 0.f;
     for (int u = 0; u < 2; ++u) {
       const float w = (s[u] == -INFINITY) ? 0.f : exp2f(s[u] - mnew);
-      sW[row * (VK + 1) + l8 + 8 * u] = w;
+      sW[row * LW + ln + LPR * u] = w;
       psum += w;
     }
-    om = om * alpha + row_sum8(psum);
+    om = om * alpha + group_sum<LPR>(psum);
     m2 = mnew;
     for (int u = 0; u < YC; ++u) {
       acc[u].x *= alpha; acc[u].y *= alpha; acc[u].z *= alpha; acc[u].w *= alpha;
     }
     __syncthreads();
-    for (int u = 0; u < YC; ++u) {
-      const int c = (l8 + 8 * u) * 4;
-      if (c < D) {
-        float4 a = acc[u];
-        for (int kk = 0; kk < VK; ++kk)
-          a = fma4(sW[row * (VK + 1) + kk], *reinterpret_cast<const float4*>(sK + kk * LD + c), a);
-        acc[u] = a;
-      }
+    tile_product(acc);
+  }
+  for (int u = 0; u < YC; ++u) acc[u] = slice_sum<CL, LPR>(acc[u]);
+  if (cached) {
+    for (int j = ln; j < kend; j += LPR) {
+      const float sj = srow[j];
+      srow[j] = (sj == -INFINITY) ? 0.f : exp2f(sj - m2);
     }
   }
-  // the row's maximising key: larger score, then smaller index, over the 8 lanes
-  for (int o = 1; o < 8; o <<= 1) {
+  // the row's maximising key: larger score, then smaller index, over the row's lanes
+  #pragma unroll
+  for (int o = 1; o < LPR; o <<= 1) {
     const float ov = __shfl_xor(bestv, o);
     const int oj = __shfl_xor(bestj, o);
     if (ov > bestv || (ov == bestv && oj < bestj)) {
@@ -612,58 +659,80 @@ __global__ __launch_bounds__(VT) void lla_valu_bwd_kernel(BwdParams P) {
     }
   }
   const float inv_om = valid ? 1.f / om : 0.f;
-  float4 kb[YC], qv[YC], gv4[YC];
+  float4 kb[YC], qv[YC];
   float gb = 0.f;
   for (int u = 0; u < YC; ++u) {
-    const int c = (l8 + 8 * u) * 4;
-    kb[u] = qv[u] = gv4[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (c < D && valid) {
+    const int c = (cl + CL * u) * 4;
+    kb[u] = qv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (valid) {
       const float4 a = acc[u];
       kb[u] = make_float4(a.x * inv_om, a.y * inv_om, a.z * inv_om, a.w * inv_om);
-      qv[u] = *reinterpret_cast<const float4*>(sQ + row * LD + c);
-      gv4[u] = *reinterpret_cast<const float4*>(sG + row * LD + c);
-      gb += dot4(gv4[u], *reinterpret_cast<const float4*>(P.out + orow + c));
+      qv[u] = *reinterpret_cast<const float4*>(qrow + c);
+      gb += dot4(*reinterpret_cast<const float4*>(grow + c), *reinterpret_cast<const float4*>(P.out + orow + c));
     }
   }
-  gb = row_sum8(gb);
+  gb = group_sum<CL>(gb);
+
+  // w_ij (final row max) of key j of the tile (lane's key kc): cached, or from q . k
+  auto weight = [&](int kc, int j) __attribute__((always_inline)) -> float {
+    if (!(valid && j <= qi)) return 0.f;
+    if (cached) return srow[j];
+    float ds = 0.f;
+    for (int c = 0; c < D; c += 4)
+      ds += dot4(*reinterpret_cast<const float4*>(qrow + c),
+                 *reinterpret_cast<const float4*>(sK + kc * LD + c));
+    return exp2f(ds * sc2 - m2);
+  };
+  // the same weight, with the key's products with rows a and b (nb of them)
+  // formed in the one pass over the key that also forms q . k if needed
+  auto weight_dots = [&](int kc, int j, int nb, const float* a, float& da, const float* b,
+                         float& db) __attribute__((always_inline)) -> float {
+    float ds = 0.f;
+    da = db = 0.f;
+    // (two loops, so that neither carries a branch: one inside the loop keeps
+    // the compiler from batching the loads across its iterations)
+    if (cached) {
+      for (int c = 0; c < D; c += 4) {
+        const float4 kv = *reinterpret_cast<const float4*>(sK + kc * LD + c);
+        da += dot4(*reinterpret_cast<const float4*>(a + c), kv);
+        if (nb > 1) db += dot4(*reinterpret_cast<const float4*>(b + c), kv);
+      }
+    } else {
+      for (int c = 0; c < D; c += 4) {
+        const float4 kv = *reinterpret_cast<const float4*>(sK + kc * LD + c);
+        ds += dot4(*reinterpret_cast<const float4*>(qrow + c), kv);
+        da += dot4(*reinterpret_cast<const float4*>(a + c), kv);
+        if (nb > 1) db += dot4(*reinterpret_cast<const float4*>(b + c), kv);
+      }
+    }
+    if (!(valid && j <= qi)) return 0.f;
+    return cached ? srow[j] : exp2f(ds * sc2 - m2);
+  };
 
   // ---------------- right-hand side h = C^T g ----------------
   // U_j = w_j (g.v_j - g.out); h = (sum_j U_j k_j - (sum_j U_j) kbar) / omega
   // (any constant in place of g.out gives the same h: sum_j w_j (k_j - kbar) = 0)
   float usum = 0.f;
   for (int u = 0; u < YC; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int kt = 0; kt < kend; kt += VK) {
-    __syncthreads();
-    stage_rows<D, LD>(sK, K, kt, VK, kend);
-    stage_rows<D, LD>(sV, V, kt, VK, kend);
-    __syncthreads();
+  first(true);
+  for (int kt = 0; kt < kend; kt += BKV) {
+    next(kt, true);
     for (int u = 0; u < 2; ++u) {
-      const int kc = l8 + 8 * u;
+      const int kc = ln + LPR * u;
       const int j = kt + kc;
-      float ds = 0.f, dg = 0.f;
-      for (int c = 0; c < D; c += 4) {
-        ds += dot4(*reinterpret_cast<const float4*>(sQ + row * LD + c),
-                   *reinterpret_cast<const float4*>(sK + kc * LD + c));
-        dg += dot4(*reinterpret_cast<const float4*>(sG + row * LD + c),
+      float dg = 0.f;
+      for (int c = 0; c < D; c += 4)
+        dg += dot4(*reinterpret_cast<const float4*>(grow + c),
                    *reinterpret_cast<const float4*>(sV + kc * LD + c));
-      }
-      float U = 0.f;
-      if (valid && j <= qi) U = exp2f(ds * sc2 - m2) * (dg - gb);
-      sW[row * (VK + 1) + kc] = U;
+      const float U = weight(kc, j) * (dg - gb);
+      sW[row * LW + kc] = U;
       usum += U;
     }
     __syncthreads();
-    for (int u = 0; u < YC; ++u) {
-      const int c = (l8 + 8 * u) * 4;
-      if (c < D) {
-        float4 a = acc[u];
-        for (int kk = 0; kk < VK; ++kk)
-          a = fma4(sW[row * (VK + 1) + kk], *reinterpret_cast<const float4*>(sK + kk * LD + c), a);
-        acc[u] = a;
-      }
-    }
+    tile_product(acc);
   }
-  usum = row_sum8(usum);
+  usum = group_sum<LPR>(usum);
+  for (int u = 0; u < YC; ++u) acc[u] = slice_sum<CL, LPR>(acc[u]);
   float4 hv[YC], x[YC], r[YC];
   float rr = 0.f, kp = 0.f;
   for (int u = 0; u < YC; ++u) {
@@ -676,12 +745,12 @@ __global__ __launch_bounds__(VT) void lla_valu_bwd_kernel(BwdParams P) {
     kp += dot4(kb[u], r[u]);
   }
   __syncthreads();
-  for (int u = 0; u < YC; ++u) {
-    const int c = (l8 + 8 * u) * 4;
-    if (c < D) *reinterpret_cast<float4*>(sP + row * LD + c) = r[u];
+  if (sl == 0) {
+    for (int u = 0; u < YC; ++u)
+      *reinterpret_cast<float4*>(sP + row * LD + (cl + CL * u) * 4) = r[u];
   }
-  rr = row_sum8(rr);
-  kp = row_sum8(kp);
+  rr = group_sum<CL>(rr);
+  kp = group_sum<CL>(kp);
   const float r0 = sqrtf(rr);
   const float stop_at = P.cg_rel_tol * r0;
   bool active = valid && rr > 0.f && P.cg_max_iters > 0;
@@ -691,55 +760,37 @@ __global__ __launch_bounds__(VT) void lla_valu_bwd_kernel(BwdParams P) {
   for (int it = 0; it < P.cg_max_iters; ++it) {
     if (tid == 0) sAny = 0;
     __syncthreads();
-    if (active && l8 == 0) sAny = 1;
+    if (active && ln == 0) sAny = 1;
     __syncthreads();
     if (!sAny) break;
     float us = 0.f;
     for (int u = 0; u < YC; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int kt = 0; kt < kend; kt += VK) {
-      __syncthreads();
-      stage_rows<D, LD>(sK, K, kt, VK, kend);
-      __syncthreads();
+    first(false);
+    for (int kt = 0; kt < kend; kt += BKV) {
+      next(kt, false);
       for (int u = 0; u < 2; ++u) {
-        const int kc = l8 + 8 * u;
+        const int kc = ln + LPR * u;
         const int j = kt + kc;
-        float ds = 0.f, dt = 0.f;
-        for (int c = 0; c < D; c += 4) {
-          const float4 kv = *reinterpret_cast<const float4*>(sK + kc * LD + c);
-          ds += dot4(*reinterpret_cast<const float4*>(sQ + row * LD + c), kv);
-          dt += dot4(*reinterpret_cast<const float4*>(sP + row * LD + c), kv);
-        }
-        float U = 0.f;
-        if (valid && j <= qi) U = exp2f(ds * sc2 - m2) * (dt - kp);
-        sW[row * (VK + 1) + kc] = U;
+        float dt, unused;
+        const float U = weight_dots(kc, j, 1, prow, dt, prow, unused) * (dt - kp);
+        sW[row * LW + kc] = U;
         us += U;
       }
       __syncthreads();
-      for (int u = 0; u < YC; ++u) {
-        const int c = (l8 + 8 * u) * 4;
-        if (c < D) {
-          float4 a = acc[u];
-          for (int kk = 0; kk < VK; ++kk)
-            a = fma4(sW[row * (VK + 1) + kk], *reinterpret_cast<const float4*>(sK + kk * LD + c), a);
-          acc[u] = a;
-        }
-      }
+      tile_product(acc);
     }
-    us = row_sum8(us);
+    us = group_sum<LPR>(us);
+    for (int u = 0; u < YC; ++u) acc[u] = slice_sum<CL, LPR>(acc[u]);
     float pAp = 0.f;
     float4 Ap[YC], pv[YC];
     for (int u = 0; u < YC; ++u) {
-      const int c = (l8 + 8 * u) * 4;
-      pv[u] = Ap[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (c < D) {
-        pv[u] = *reinterpret_cast<const float4*>(sP + row * LD + c);
-        const float4 a = acc[u];
-        Ap[u] = make_float4(a.x - us * kb[u].x + lam * pv[u].x, a.y - us * kb[u].y + lam * pv[u].y,
-                            a.z - us * kb[u].z + lam * pv[u].z, a.w - us * kb[u].w + lam * pv[u].w);
-        pAp += dot4(pv[u], Ap[u]);
-      }
+      pv[u] = *reinterpret_cast<const float4*>(prow + (cl + CL * u) * 4);
+      const float4 a = acc[u];
+      Ap[u] = make_float4(a.x - us * kb[u].x + lam * pv[u].x, a.y - us * kb[u].y + lam * pv[u].y,
+                          a.z - us * kb[u].z + lam * pv[u].z, a.w - us * kb[u].w + lam * pv[u].w);
+      pAp += dot4(pv[u], Ap[u]);
     }
-    pAp = row_sum8(pAp);
+    pAp = group_sum<CL>(pAp);
     bool step = active && pAp > 0.f;
     if (active && !step) active = false;
     float rrn = 0.f;
@@ -751,7 +802,7 @@ __global__ __launch_bounds__(VT) void lla_valu_bwd_kernel(BwdParams P) {
       }
       rrn += dot4(r[u], r[u]);
     }
-    rrn = row_sum8(rrn);
+    rrn = group_sum<CL>(rrn);
     float kpn = 0.f;
     if (step) {
       ++iters;
@@ -760,19 +811,19 @@ __global__ __launch_bounds__(VT) void lla_valu_bwd_kernel(BwdParams P) {
       } else {
         const float be = rrn / rr;
         for (int u = 0; u < YC; ++u) {
-          const int c = (l8 + 8 * u) * 4;
           pv[u] = fma4(be, pv[u], r[u]);
-          if (c < D) *reinterpret_cast<float4*>(sP + row * LD + c) = pv[u];
+          // (every lane of the row has read p above: one wave holds the row)
+          if (sl == 0) *reinterpret_cast<float4*>(sP + row * LD + (cl + CL * u) * 4) = pv[u];
           kpn += dot4(kb[u], pv[u]);
         }
       }
       rr = rrn;
     }
-    kpn = row_sum8(kpn);
+    kpn = group_sum<CL>(kpn);
     if (active) kp = kpn;
     __syncthreads();
   }
-  if (valid && l8 == 0) {
+  if (valid && ln == 0) {
     if (P.adj_iters) P.adj_iters[orow / D] = iters;
     if (P.adj_resid) P.adj_resid[orow / D] = r0 > 0.f ? sqrtf(rr) / r0 : 0.f;
   }
@@ -782,10 +833,10 @@ __global__ __launch_bounds__(VT) void lla_valu_bwd_kernel(BwdParams P) {
   float4 rc[YC];
   float kbx = 0.f, kby = 0.f, kap = 0.f, yu = 0.f, yr = 0.f;
   for (int u = 0; u < YC; ++u) {
-    const int c = (l8 + 8 * u) * 4;
+    const int c = (cl + CL * u) * 4;
     rc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (c < D && valid) rc[u] = *reinterpret_cast<const float4*>(P.rho_c + orow + c);
-    if (c < D) {
+    if (valid) rc[u] = *reinterpret_cast<const float4*>(P.rho_c + orow + c);
+    if (sl == 0) {
       *reinterpret_cast<float4*>(sP + row * LD + c) = rc[u];
       *reinterpret_cast<float4*>(sY + row * LD + c) = x[u];
     }
@@ -795,65 +846,50 @@ __global__ __launch_bounds__(VT) void lla_valu_bwd_kernel(BwdParams P) {
     yu += dot4(x[u], make_float4(kb[u].x - qv[u].x, kb[u].y - qv[u].y, kb[u].z - qv[u].z, kb[u].w - qv[u].w));
     yr += dot4(x[u], rc[u]);
   }
-  kbx = row_sum8(kbx);
-  kby = row_sum8(kby);
-  kap = row_sum8(kap);
-  yu = row_sum8(yu);
-  yr = row_sum8(yr);
+  kbx = group_sum<CL>(kbx);
+  kby = group_sum<CL>(kby);
+  kap = group_sum<CL>(kap);
+  yu = group_sum<CL>(yu);
+  yr = group_sum<CL>(yr);
   const float tau = valid ? kap * inv_om - yu : 0.f;
   const float msum = -lam * yr;
   const float gvbar = gb + kap;
-  if (l8 == 0) sOm[row] = inv_om;
+  if (ln == 0) sOm[row] = inv_om;
 
   // ---------------- final sweep: dq, and dk, dv per key tile ----------------
   float rsum = 0.f;
   for (int u = 0; u < YC; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int kt = 0; kt < kend; kt += VK) {
-    __syncthreads();
-    stage_rows<D, LD>(sK, K, kt, VK, kend);
-    stage_rows<D, LD>(sV, V, kt, VK, kend);
-    __syncthreads();
+  first(true);
+  for (int kt = 0; kt < kend; kt += BKV) {
+    next(kt, true);
     for (int u = 0; u < 2; ++u) {
-      const int kc = l8 + 8 * u;
+      const int kc = ln + LPR * u;
       const int j = kt + kc;
-      float ds = 0.f, dr = 0.f, dy = 0.f, dg = 0.f;
-      for (int c = 0; c < D; c += 4) {
-        const float4 kv = *reinterpret_cast<const float4*>(sK + kc * LD + c);
-        ds += dot4(*reinterpret_cast<const float4*>(sQ + row * LD + c), kv);
-        dr += dot4(*reinterpret_cast<const float4*>(sP + row * LD + c), kv);
-        dy += dot4(*reinterpret_cast<const float4*>(sY + row * LD + c), kv);
-        dg += dot4(*reinterpret_cast<const float4*>(sG + row * LD + c),
+      float dr, dy, dg = 0.f;
+      const float w = weight_dots(kc, j, 2, prow, dr, yrow, dy);
+      for (int c = 0; c < D; c += 4)
+        dg += dot4(*reinterpret_cast<const float4*>(grow + c),
                    *reinterpret_cast<const float4*>(sV + kc * LD + c));
-      }
       const bool vis = valid && j <= qi;
-      const float w = vis ? exp2f(ds * sc2 - m2) : 0.f;
       const float A = 1.f - (dr - kbx);
       const float ev = (dg - gvbar) * inv_om - (dy - kby);
       const float sig = w * fmaf(A, ev, tau);
       rsum += sig;
-      sW[row * (VK + 1) + kc] = sig;
-      sA[row * (VK + 1) + kc] = cs * ((vis && j == bestj) ? sig - msum : sig);
-      sB[row * (VK + 1) + kc] = -w * A;
-      sE[row * (VK + 1) + kc] = -w * ev;
+      sW[row * LW + kc] = sig;
+      sA[row * LW + kc] = cs * ((vis && j == bestj) ? sig - msum : sig);
+      sB[row * LW + kc] = -w * A;
+      sE[row * LW + kc] = -w * ev;
     }
     __syncthreads();
-    for (int u = 0; u < YC; ++u) {
-      const int c = (l8 + 8 * u) * 4;
-      if (c < D) {
-        float4 a = acc[u];
-        for (int kk = 0; kk < VK; ++kk)
-          a = fma4(sW[row * (VK + 1) + kk], *reinterpret_cast<const float4*>(sK + kk * LD + c), a);
-        acc[u] = a;
-      }
-    }
+    tile_product(acc);
     // dk_j = sum_i [c dL/ds q_i - w A y_i - w e rho_c,i], dv_j = sum_i (w A / omega_i) g_i
-    for (int e = tid; e < VK * NC; e += VT) {
+    for (int e = tid; e < BKV * NC; e += VT) {
       const int kk = e / NC, c = (e % NC) * 4;
       const int j = kt + kk;
       if (j >= kend) continue;
       float4 dk = make_float4(0.f, 0.f, 0.f, 0.f), dv = dk;
       for (int i = 0; i < nq; ++i) {
-        const float a1 = sA[i * (VK + 1) + kk], a2 = sB[i * (VK + 1) + kk], a3 = sE[i * (VK + 1) + kk];
+        const float a1 = sA[i * LW + kk], a2 = sB[i * LW + kk], a3 = sE[i * LW + kk];
         dk = fma4(a1, *reinterpret_cast<const float4*>(sQ + i * LD + c), dk);
         dk = fma4(a2, *reinterpret_cast<const float4*>(sY + i * LD + c), dk);
         dk = fma4(a3, *reinterpret_cast<const float4*>(sP + i * LD + c), dk);
@@ -865,18 +901,17 @@ __global__ __launch_bounds__(VT) void lla_valu_bwd_kernel(BwdParams P) {
       atomicAdd(pvv + 0, dv.x); atomicAdd(pvv + 1, dv.y); atomicAdd(pvv + 2, dv.z); atomicAdd(pvv + 3, dv.w);
     }
   }
-  rsum = row_sum8(rsum);
-  if (!valid) return;
+  rsum = group_sum<LPR>(rsum);
+  for (int u = 0; u < YC; ++u) acc[u] = slice_sum<CL, LPR>(acc[u]);
+  if (!valid || sl != 0) return;
   // dq = c (sum_j dL/ds_j k_j - (sum_j dL/ds_j) k_j*) + omega y
   for (int u = 0; u < YC; ++u) {
-    const int c = (l8 + 8 * u) * 4;
-    if (c < D) {
-      const float4 ks = load4(K, static_cast<size_t>(bestj) * D + c);
-      const float4 a = acc[u];
-      const float4 o = make_float4(cs * (a.x - rsum * ks.x) + om * x[u].x, cs * (a.y - rsum * ks.y) + om * x[u].y,
-                                   cs * (a.z - rsum * ks.z) + om * x[u].z, cs * (a.w - rsum * ks.w) + om * x[u].w);
-      *reinterpret_cast<float4*>(P.dq + orow + c) = o;
-    }
+    const int c = (cl + CL * u) * 4;
+    const float4 ks = load4(K, static_cast<size_t>(bestj) * D + c);
+    const float4 a = acc[u];
+    const float4 o = make_float4(cs * (a.x - rsum * ks.x) + om * x[u].x, cs * (a.y - rsum * ks.y) + om * x[u].y,
+                                 cs * (a.z - rsum * ks.z) + om * x[u].z, cs * (a.w - rsum * ks.w) + om * x[u].w);
+    *reinterpret_cast<float4*>(P.dq + orow + c) = o;
   }
 }
 
@@ -888,9 +923,34 @@ __global__ void zero_fill(float* __restrict__ a, float* __restrict__ b, size_t n
   }
 }
 
-template <int D, typename Tin>
-hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
-  const int nqb = (p.n + VQ - 1) / VQ;
+// Lanes per query row for a launch: the fewest that still give every compute
+// unit two workgroups; at most 32.
+template <int D>
+hipError_t lanes_per_row(int n, int BH, int* lpr) {
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const long long fill = 2LL * cus;
+  auto blocks = [&](int bq) { return static_cast<long long>((n + bq - 1) / bq) * BH; };
+  *lpr = blocks(Lanes<D, 8>::VQ) >= fill ? 8 : blocks(Lanes<D, 16>::VQ) >= fill ? 16 : 32;
+  return hipSuccess;
+}
+
+// Row stride of the weight cache (rows of n keys rounded up to the tile, plus
+// LPR floats so that a wave's rows start on different banks), or 0 where the
+// cache would take more than 64 KiB of dynamic LDS.
+template <int D, int LPR>
+int cache_stride(int n) {
+  const long long ls = (static_cast<long long>(n) + 2 * LPR - 1) / (2 * LPR) * (2 * LPR) + LPR;
+  return ls * Lanes<D, LPR>::VQ * 4 <= 65536 ? static_cast<int>(ls) : 0;
+}
+
+template <int D, typename Tin, int LPR>
+hipError_t launch_bwd_lanes(const BwdParams& p, hipStream_t stream) {
+  constexpr int BQ = Lanes<D, LPR>::VQ;
+  const int nqb = (p.n + BQ - 1) / BQ;
   const long long blocks = static_cast<long long>(nqb) * p.BH;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const size_t n4 = static_cast<size_t>(p.BH) * p.n * D / 4;
@@ -902,11 +962,23 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
     e = hipEventRecord(p.ev_main_begin, stream);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((lla_valu_bwd_kernel<D, Tin>), dim3(static_cast<unsigned>(blocks)), dim3(VT), 0, stream, p);
+  const int ls = cache_stride<D, LPR>(p.n);
+  hipLaunchKernelGGL((lla_valu_bwd_kernel<D, Tin, LPR>), dim3(static_cast<unsigned>(blocks)), dim3(VT),
+                     static_cast<unsigned>(ls) * BQ * 4u, stream, p, ls);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.ev_main_end) return hipEventRecord(p.ev_main_end, stream);
   return hipSuccess;
+}
+
+template <int D, typename Tin>
+hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
+  int lpr = 8;
+  const hipError_t e = lanes_per_row<D>(p.n, p.BH, &lpr);
+  if (e != hipSuccess) return e;
+  if (lpr == 8) return launch_bwd_lanes<D, Tin, 8>(p, stream);
+  if (lpr == 16) return launch_bwd_lanes<D, Tin, 16>(p, stream);
+  return launch_bwd_lanes<D, Tin, 32>(p, stream);
 }
 
 template <typename Tin>
@@ -930,31 +1002,22 @@ hipError_t launch_lanes(const FwdParams& p, hipStream_t stream) {
     const hipError_t e = hipEventRecord(p.ev_main_begin, stream);
     if (e != hipSuccess) return e;
   }
-  // the weight cache: rows of n keys rounded up to the tile, plus LPR floats so
-  // that a wave's rows start on different banks; only when it adds <= 64 KiB
-  const long long ls = (static_cast<long long>(p.n) + 2 * LPR - 1) / (2 * LPR) * (2 * LPR) + LPR;
-  const bool cache = ls * BQ * 4 <= 65536;
+  const int ls = cache_stride<D, LPR>(p.n);
   hipLaunchKernelGGL((lla_valu_kernel<D, Tin, LPR>), dim3(static_cast<unsigned>(blocks)), dim3(VT),
-                     cache ? static_cast<unsigned>(ls * BQ * 4) : 0u, stream, p, cache ? static_cast<int>(ls) : 0);
+                     static_cast<unsigned>(ls) * BQ * 4u, stream, p, ls);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.ev_main_end) return hipEventRecord(p.ev_main_end, stream);
   return hipSuccess;
 }
 
-// The fewest lanes per row (most queries per workgroup) that still give
-// every compute unit two workgroups; at most 32.
 template <int D, typename Tin>
 hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
-  int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
+  int lpr = 8;
+  const hipError_t e = lanes_per_row<D>(p.n, p.BH, &lpr);
   if (e != hipSuccess) return e;
-  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return e;
-  const long long fill = 2LL * cus;
-  auto blocks = [&](int bq) { return static_cast<long long>((p.n + bq - 1) / bq) * p.BH; };
-  if (blocks(Lanes<D, 8>::VQ) >= fill) return launch_lanes<D, Tin, 8>(p, stream);
-  if (blocks(Lanes<D, 16>::VQ) >= fill) return launch_lanes<D, Tin, 16>(p, stream);
+  if (lpr == 8) return launch_lanes<D, Tin, 8>(p, stream);
+  if (lpr == 16) return launch_lanes<D, Tin, 16>(p, stream);
   return launch_lanes<D, Tin, 32>(p, stream);
 }
 

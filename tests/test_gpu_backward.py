@@ -280,6 +280,30 @@ def test_backward_valu_fp32_ragged(torch, n, d):
                 f"valu f32 n={n} d={d}", bar=F32_TOL, fp16_scores=False)
 
 
+# The vector backward takes the forward's lane layouts (32, 16 or 8 query rows
+# per workgroup, chosen from the launch size for a device of 256 compute
+# units) and its weight cache (n <= 496, 992, 1984): one shape per layout and
+# form, dq on sampled rows and dk, dv on the last 48 keys of two heads.
+BWD_LAYOUTS = [
+    (1, 64, 256, 16, "32 rows, weights cached"),
+    (2, 8, 512, 32, "16 rows, cached"),
+    (1, 4, 2048, 64, "16 rows, recomputed"),
+    (1, 2, 1001, 128, "8 rows, cached, ragged tail"),
+    (1, 1, 4096, 16, "8 rows, recomputed"),
+]
+
+
+@pytest.mark.parametrize("B,H,n,d,layout", BWD_LAYOUTS, ids=[x[-1] for x in BWD_LAYOUTS])
+def test_backward_valu_lane_layouts(torch, B, H, n, d, layout):
+    wl = make_random(B, H, n, d, "f32", seed=700 + n + d, qk_scale=2.0)
+    g = make_cotangent(B, H, n, d, seed=n + d)
+    res = run(torch, wl, g, T=2 * d, tol=1e-7, lam=1.0, kernel=VALU)
+    rng = np.random.default_rng(n)
+    dq_rows = sorted(set(range(32)) | set(rng.integers(0, n, 32).tolist()))
+    check_grads(wl, g, res, [(0, 0), (B - 1, H - 1)], dq_rows, n - 48, 2 * d, 1e-7, 1.0,
+                f"valu layout {layout} n={n} d={d}", bar=F32_TOL, fp16_scores=False)
+
+
 @pytest.mark.parametrize("name", ["tiny", "piecewise"])
 def test_backward_valu_fp32_workloads(torch, name):
     """The fp32 workloads with their own CG policy (tiny: lambda 0.1, tol 1e-8,
