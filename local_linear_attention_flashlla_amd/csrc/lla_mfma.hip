@@ -380,12 +380,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void pc
                                                 const float* __restrict__ tsum,
                                                 float* __restrict__ pcs) {
   constexpr int EB = D / 16;                 // side of each thread's block of M
+  static_assert(EB % 2 == 0, "a pivot pair lies in one thread block");
   // a quarter of M's rows at a time, for the transposed reads of the
   // symmetrisation (a whole D x D buffer would cap the kernel at two
   // workgroups per compute unit)
   __shared__ float sQ[D / 4][D + 1];
   __shared__ float sT[D];
-  __shared__ float sRow[2][D], sCol[2][D];
+  __shared__ float sRow[2][2][D], sCol[2][2][D];  // [step parity][pivot of the pair]
   __shared__ float sRed[4];
   const int sl = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -413,56 +414,92 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void pc
       if (row == col) v += lam_s;
       A[i][j] = v;
     }
-  // ---- M = P^{-1}: Gauss-Jordan in place, thread block (br, bc). Step k
-  // (k uniform over the workgroup, so every branch on kl below is uniform):
-  // the owners of row k and column k publish them; every element takes the
-  // rank-one update A -= A[:,k] A[k,:] / A[k,k], which leaves row k and
-  // column k at zero; their owners then write A[k,j] / p, -A[i,k] / p and
-  // 1 / p there.
+  // ---- M = P^{-1}: Gauss-Jordan in place, thread block (br, bc), two pivots
+  // K = {k, k + 1} per step (k even; one barrier per pair). Step k (uniform
+  // over the workgroup, so every branch on kl below is uniform): the owners
+  // of rows K and columns K publish them; with B the inverse of the 2 x 2
+  // block A[K][K], formed as the two single pivots would (pivot a, then the
+  // Schur complement), every element takes A -= A[:,K] B A[K,:], and then
+  // A[K][j] = B A[K][j], A[i][K] = -A[i][K] B and A[K][K] = B: the two
+  // single-pivot steps in one.
   bool ok = true;
-  for (int k = 0; k < D; ++k) {
-    const int buf = k & 1, kb = k / EB, kl = k % EB;
+  for (int k = 0; k < D; k += 2) {
+    const int buf = (k >> 1) & 1, kb = k / EB, kl = k % EB;
     #pragma unroll
-    for (int c = 0; c < EB; ++c) {
+    for (int c = 0; c < EB; c += 2) {
       if (c == kl) {
         if (br == kb) {
           #pragma unroll
-          for (int j = 0; j < EB; ++j) sRow[buf][EB * bc + j] = A[c][j];
+          for (int j = 0; j < EB; ++j) {
+            sRow[buf][0][EB * bc + j] = A[c][j];
+            sRow[buf][1][EB * bc + j] = A[c + 1][j];
+          }
         }
         if (bc == kb) {
           #pragma unroll
-          for (int i = 0; i < EB; ++i) sCol[buf][EB * br + i] = A[i][c];
+          for (int i = 0; i < EB; ++i) {
+            sCol[buf][0][EB * br + i] = A[i][c];
+            sCol[buf][1][EB * br + i] = A[i][c + 1];
+          }
         }
       }
     }
     __syncthreads();
-    const float piv = sCol[buf][k];
-    if (!(piv > 0.f) || !(piv < INFINITY)) {  // the same value in every thread
+    // the same values in every thread
+    const float a = sCol[buf][0][k], b = sCol[buf][1][k];       // A[k][k], A[k][k+1]
+    const float b2 = sCol[buf][0][k + 1], c2 = sCol[buf][1][k + 1];  // A[k+1][k], A[k+1][k+1]
+    if (!(a > 0.f) || !(a < INFINITY)) {
       ok = false;
       break;
     }
-    const float ip = 1.f / piv;
-    float rv[EB], cv[EB];
+    const float ia = 1.f / a;
+    const float sch = c2 - b2 * ia * b;  // the second pivot
+    if (!(sch > 0.f) || !(sch < INFINITY)) {
+      ok = false;
+      break;
+    }
+    const float is = 1.f / sch;
+    const float u = ia * b, w = b2 * ia;  // A[k][k+1] / a, A[k+1][k] / a
+    const float B00 = ia + u * is * w, B01 = -u * is, B10 = -w * is, B11 = is;
+    float r0[EB], r1[EB], t0[EB], t1[EB];
     #pragma unroll
-    for (int j = 0; j < EB; ++j) rv[j] = sRow[buf][EB * bc + j];
+    for (int j = 0; j < EB; ++j) {
+      r0[j] = sRow[buf][0][EB * bc + j];
+      r1[j] = sRow[buf][1][EB * bc + j];
+    }
     #pragma unroll
-    for (int i = 0; i < EB; ++i) cv[i] = sCol[buf][EB * br + i] * ip;
+    for (int i = 0; i < EB; ++i) {
+      const float c0 = sCol[buf][0][EB * br + i], c1 = sCol[buf][1][EB * br + i];
+      t0[i] = c0 * B00 + c1 * B10;  // (A[i][K] B)_0
+      t1[i] = c0 * B01 + c1 * B11;
+    }
     #pragma unroll
     for (int i = 0; i < EB; ++i)
       #pragma unroll
-      for (int j = 0; j < EB; ++j) A[i][j] = fmaf(-cv[i], rv[j], A[i][j]);
+      for (int j = 0; j < EB; ++j) A[i][j] = fmaf(-t0[i], r0[j], fmaf(-t1[i], r1[j], A[i][j]));
     #pragma unroll
-    for (int c = 0; c < EB; ++c) {
+    for (int c = 0; c < EB; c += 2) {
       if (c == kl) {
         if (br == kb) {
           #pragma unroll
-          for (int j = 0; j < EB; ++j) A[c][j] = rv[j] * ip;
+          for (int j = 0; j < EB; ++j) {
+            A[c][j] = B00 * r0[j] + B01 * r1[j];
+            A[c + 1][j] = B10 * r0[j] + B11 * r1[j];
+          }
         }
         if (bc == kb) {
           #pragma unroll
-          for (int i = 0; i < EB; ++i) A[i][c] = -cv[i];
+          for (int i = 0; i < EB; ++i) {
+            A[i][c] = -t0[i];
+            A[i][c + 1] = -t1[i];
+          }
         }
-        if (br == kb && bc == kb) A[c][c] = ip;
+        if (br == kb && bc == kb) {
+          A[c][c] = B00;
+          A[c][c + 1] = B01;
+          A[c + 1][c] = B10;
+          A[c + 1][c + 1] = B11;
+        }
       }
     }
   }
