@@ -1,6 +1,6 @@
 // fp32 vector-ALU kernels for the causal LLA forward and backward passes.
 //
-// In the forward, one workgroup of 256 threads owns a block of 8, 16 or 32
+// In the forward, one workgroup of 256 threads owns a block of 4, 8, 16 or 32
 // consecutive query rows of one (batch, head) and runs all three phases of the
 // blocked forward of "Local Linear Attention: reading notes" (section 2.2,
 // Algorithm 1) for it:
@@ -13,7 +13,7 @@
 // (q, p); the weights exist only as a rows x tile-keys tile in LDS. The next
 // key (and value) tile is loaded into registers while the current one is used.
 //
-// Thread roles (forward): the LPR = 8, 16 or 32 lanes of a row group serve one
+// Thread roles (forward): the LPR = 8, 16, 32 or 64 lanes of a row group serve one
 // query row (row reductions are xor-shuffles within the group). For score
 // tiles a lane computes keys l and l + LPR of a 2 LPR-key tile; for d-vectors
 // it owns float4 chunks and a slice of the tile's keys (struct Lanes below).
@@ -924,9 +924,9 @@ __global__ void zero_fill(float* __restrict__ a, float* __restrict__ b, size_t n
 }
 
 // Lanes per query row for a launch: the fewest that still give every compute
-// unit two workgroups; at most 32.
+// unit two workgroups; at most max_lpr.
 template <int D>
-hipError_t lanes_per_row(int n, int BH, int* lpr) {
+hipError_t lanes_per_row(int n, int BH, int max_lpr, int* lpr) {
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -934,7 +934,8 @@ hipError_t lanes_per_row(int n, int BH, int* lpr) {
   if (e != hipSuccess) return e;
   const long long fill = 2LL * cus;
   auto blocks = [&](int bq) { return static_cast<long long>((n + bq - 1) / bq) * BH; };
-  *lpr = blocks(Lanes<D, 8>::VQ) >= fill ? 8 : blocks(Lanes<D, 16>::VQ) >= fill ? 16 : 32;
+  *lpr = 8;
+  while (*lpr < max_lpr && blocks(VT / *lpr) < fill) *lpr *= 2;
   return hipSuccess;
 }
 
@@ -974,7 +975,7 @@ hipError_t launch_bwd_lanes(const BwdParams& p, hipStream_t stream) {
 template <int D, typename Tin>
 hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
   int lpr = 8;
-  const hipError_t e = lanes_per_row<D>(p.n, p.BH, &lpr);
+  const hipError_t e = lanes_per_row<D>(p.n, p.BH, 32, &lpr);
   if (e != hipSuccess) return e;
   if (lpr == 8) return launch_bwd_lanes<D, Tin, 8>(p, stream);
   if (lpr == 16) return launch_bwd_lanes<D, Tin, 16>(p, stream);
@@ -1013,11 +1014,16 @@ hipError_t launch_lanes(const FwdParams& p, hipStream_t stream) {
 
 template <int D, typename Tin>
 hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
+  // one row per wave (64 lanes) for d <= 64: at d = 128 the 128-key tiles
+  // of K and V would not leave LDS for the weight cache
   int lpr = 8;
-  const hipError_t e = lanes_per_row<D>(p.n, p.BH, &lpr);
+  const hipError_t e = lanes_per_row<D>(p.n, p.BH, D <= 64 ? 64 : 32, &lpr);
   if (e != hipSuccess) return e;
   if (lpr == 8) return launch_lanes<D, Tin, 8>(p, stream);
   if (lpr == 16) return launch_lanes<D, Tin, 16>(p, stream);
+  if constexpr (D <= 64) {
+    if (lpr == 64) return launch_lanes<D, Tin, 64>(p, stream);
+  }
   return launch_lanes<D, Tin, 32>(p, stream);
 }
 

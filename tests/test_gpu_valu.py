@@ -152,17 +152,20 @@ def test_ragged_sizes_f32(torch, n, d):
     np.testing.assert_allclose(res["out"][0, 0, 0], wl.v[0, 0, 0], rtol=1e-6, atol=1e-6)
 
 
-# The forward serves 32, 16 or 8 query rows per workgroup (8, 16 or 32 lanes
-# per row: the fewest that give each of the device's compute units two
-# workgroups; 256 on this device) and keeps a block's weights in LDS when n is
-# short enough (n <= 496, 992, 1984 for 32, 16, 8 rows). One shape per layout
-# and form of the sweeps, against the oracle on sampled rows of two heads.
+# The forward serves 32, 16, 8 or (d <= 64) 4 query rows per workgroup (8, 16,
+# 32 or 64 lanes per row: the fewest that give each of the device's compute
+# units two workgroups; 256 on this device) and keeps a block's weights in LDS
+# when n is short enough (n <= 496, 992, 1984, 3968 for 32, 16, 8, 4 rows).
+# One shape per layout and form of the sweeps, against the oracle on sampled
+# rows of two heads.
 LAYOUTS = [
     (1, 64, 256, 16, "32 rows, weights cached"),
     (2, 8, 512, 32, "16 rows, cached"),
     (1, 4, 2048, 64, "16 rows, recomputed"),
     (1, 2, 1001, 128, "8 rows, cached, ragged tail"),
     (1, 1, 4096, 16, "8 rows, recomputed"),
+    (1, 1, 1023, 64, "4 rows, cached, ragged tail"),
+    (1, 1, 4000, 32, "4 rows, recomputed"),
 ]
 
 
