@@ -974,11 +974,16 @@ hipError_t launch_bwd_lanes(const BwdParams& p, hipStream_t stream) {
 
 template <int D, typename Tin>
 hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
+  // one row per wave only for d <= 32: beyond, the two prefetched 128-key
+  // tiles would not fit the registers the backward's state leaves
   int lpr = 8;
-  const hipError_t e = lanes_per_row<D>(p.n, p.BH, 32, &lpr);
+  const hipError_t e = lanes_per_row<D>(p.n, p.BH, D <= 32 ? 64 : 32, &lpr);
   if (e != hipSuccess) return e;
   if (lpr == 8) return launch_bwd_lanes<D, Tin, 8>(p, stream);
   if (lpr == 16) return launch_bwd_lanes<D, Tin, 16>(p, stream);
+  if constexpr (D <= 32) {
+    if (lpr == 64) return launch_bwd_lanes<D, Tin, 64>(p, stream);
+  }
   return launch_bwd_lanes<D, Tin, 32>(p, stream);
 }
 

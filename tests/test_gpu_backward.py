@@ -280,16 +280,19 @@ def test_backward_valu_fp32_ragged(torch, n, d):
                 f"valu f32 n={n} d={d}", bar=F32_TOL, fp16_scores=False)
 
 
-# The vector backward takes the forward's lane layouts (32, 16 or 8 query rows
-# per workgroup, chosen from the launch size for a device of 256 compute
-# units) and its weight cache (n <= 496, 992, 1984): one shape per layout and
-# form, dq on sampled rows and dk, dv on the last 48 keys of two heads.
+# The vector backward takes the forward's lane layouts (32, 16, 8 or, for
+# d <= 32, 4 query rows per workgroup, chosen from the launch size for a
+# device of 256 compute units) and its weight cache (n <= 496, 992, 1984,
+# 3968): one shape per layout and form, dq on sampled rows and dk, dv on the
+# last 48 keys of two heads.
 BWD_LAYOUTS = [
     (1, 64, 256, 16, "32 rows, weights cached"),
     (2, 8, 512, 32, "16 rows, cached"),
     (1, 4, 2048, 64, "16 rows, recomputed"),
     (1, 2, 1001, 128, "8 rows, cached, ragged tail"),
-    (1, 1, 4096, 16, "8 rows, recomputed"),
+    (1, 1, 4096, 64, "8 rows, recomputed"),
+    (1, 1, 1023, 32, "4 rows, cached, ragged tail"),
+    (1, 1, 4000, 16, "4 rows, recomputed"),
 ]
 
 
